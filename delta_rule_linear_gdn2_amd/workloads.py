@@ -1,0 +1,209 @@
+"""Seeded synthetic inputs for the Gated DeltaNet-2 forward pass.
+
+This module only draws random numbers and rounds them to the device dtype; it
+holds none of the method's arithmetic, and both the HIP path and the FP64
+oracle consume its output.  Everything is generated on the CPU with numpy's
+PCG64 (``numpy.random.default_rng(seed)``), so inputs do not depend on the
+device.
+
+Value distributions follow the setting of the pages: 16 heads with a 128 x 128
+state per head, 4K training length and 64-token chunks ("Gated DeltaNet-2"
+analysis at iplexlaw.co.kr, "What was compared" and "Token processing and
+parallel training"); gates are sigmoid outputs, q and k are L2-normalised per
+head and token (same page, "Token processing and parallel training"), and the
+decay sits close to one.  The pages train on FineWeb-Edu; no dataset is used
+here: Gaussian / sigmoid tensors of the same shapes stand in for the
+activations.
+
+Recipes (seed = 1000 + workload index):
+  q, k  ~ N(0, 1), then L2-normalised over dk per (token, head)
+  v     ~ N(0, 1)
+  alpha = sigmoid(N(3, 1)) per key channel           (FP32 always)
+  b, w  = sigmoid(N(0, 1)) per key / value channel
+  initial state ~ N(0, 0.1^2) where the workload has one, else zeros
+  bf16 workloads round q, k, v, b, w to bfloat16 (round-to-nearest-even)
+  once, at generation: the oracle receives the same rounded values in FP32.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+GEN_NAME = "numpy.random.PCG64"
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    index: int
+    kind: str          # "chunk" | "decode" | "varlen"
+    dtype: str         # "f32" | "bf16"  (q, k, v, b, w, o); alpha and state are FP32
+    B: int = 1
+    T: int = 0
+    H: int = 16
+    dk: int = 128
+    dv: int = 128
+    init_state: bool = False
+    steps: int = 0               # decode: consecutive in-place steps
+    num_seqs: int = 0            # varlen
+    min_len: int = 0
+    max_len: int = 0
+    gate_modes: tuple = field(default_factory=tuple)
+
+    @property
+    def seed(self) -> int:
+        return 1000 + self.index
+
+
+WORKLOADS = {
+    "tiny_f32": Workload("tiny_f32", 0, "chunk", "f32", B=1, T=256, H=2, dk=32, dv=32),
+    "layer_bf16": Workload("layer_bf16", 1, "chunk", "bf16", B=1, T=4096, H=16),
+    "batched_bf16": Workload("batched_bf16", 2, "chunk", "bf16", B=8, T=4096, H=16, init_state=True),
+    "decode_b256": Workload("decode_b256", 3, "decode", "bf16", B=256, H=16, init_state=True, steps=64),
+    "varlen32_bf16": Workload("varlen32_bf16", 4, "varlen", "bf16", B=1, H=16, init_state=True,
+                              num_seqs=32, min_len=256, max_len=8192,
+                              gate_modes=("gdn2", "kda", "gdn")),
+}
+
+
+# ---------------------------------------------------------------------------
+# dtype helpers
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round-to-nearest-even); return the bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """float32 -> nearest bfloat16 value, returned as float32 (exact)."""
+    return bf16_to_f32(bf16_bits(x))
+
+
+def _sigmoid(x: np.ndarray) -> np.ndarray:
+    return (1.0 / (1.0 + np.exp(-x.astype(np.float64)))).astype(np.float32)
+
+
+def _l2norm(x: np.ndarray) -> np.ndarray:
+    n = np.sqrt(np.sum(x.astype(np.float64) ** 2, axis=-1, keepdims=True))
+    return (x / np.maximum(n, 1e-12)).astype(np.float32)
+
+
+def _normal(rng, shape, mean=0.0, std=1.0) -> np.ndarray:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    if mean != 0.0:
+        x += np.float32(mean)
+    return x
+
+
+# ---------------------------------------------------------------------------
+# generators
+
+
+def token_tensors(rng, lead: tuple, H: int, dk: int, dv: int, dtype: str,
+                  gate_mode: str = "gdn2", alpha_mean: float = 3.0, alpha_std: float = 1.0) -> dict:
+    """q, k, v, alpha, b, w with leading shape ``lead`` (e.g. (B, T)).
+
+    Returned arrays are float32 holding values exactly representable in
+    ``dtype``.  ``gate_mode``:
+      "gdn2" - channel-wise alpha, b, w (full method)
+      "kda"  - b = w = beta broadcast, beta = sigmoid(N(0,1)) per (token, head)
+      "gdn"  - as "kda" and a scalar alpha per (token, head) broadcast over dk
+    """
+    q = _l2norm(_normal(rng, lead + (H, dk)))
+    k = _l2norm(_normal(rng, lead + (H, dk)))
+    v = _normal(rng, lead + (H, dv))
+    if gate_mode == "gdn2":
+        alpha = _sigmoid(_normal(rng, lead + (H, dk), alpha_mean, alpha_std))
+        b = _sigmoid(_normal(rng, lead + (H, dk)))
+        w = _sigmoid(_normal(rng, lead + (H, dv)))
+    elif gate_mode in ("kda", "gdn"):
+        if gate_mode == "kda":
+            alpha = _sigmoid(_normal(rng, lead + (H, dk), alpha_mean, alpha_std))
+        else:
+            a1 = _sigmoid(_normal(rng, lead + (H, 1), alpha_mean, alpha_std))
+            alpha = np.ascontiguousarray(np.broadcast_to(a1, lead + (H, dk)))
+        beta = _sigmoid(_normal(rng, lead + (H, 1)))
+        if dtype == "bf16":
+            beta = round_bf16(beta)
+        b = np.ascontiguousarray(np.broadcast_to(beta, lead + (H, dk)))
+        w = np.ascontiguousarray(np.broadcast_to(beta, lead + (H, dv)))
+    else:
+        raise ValueError(gate_mode)
+    out = dict(q=q, k=k, v=v, alpha=alpha, b=b, w=w)
+    if dtype == "bf16":
+        for name in ("q", "k", "v", "b", "w"):
+            out[name] = round_bf16(out[name])
+    return out
+
+
+def initial_state(rng, N: int, H: int, dk: int, dv: int, std: float = 0.1) -> np.ndarray:
+    return _normal(rng, (N, H, dk, dv), 0.0, std)
+
+
+def varlen_lengths(rng, num_seqs: int, lo: int, hi: int) -> np.ndarray:
+    return rng.integers(lo, hi + 1, size=num_seqs).astype(np.int64)
+
+
+def cu_from_lengths(lengths) -> np.ndarray:
+    cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(np.asarray(lengths, dtype=np.int64))
+    return cu
+
+
+def make(name: str, gate_mode: str = "gdn2", seed: int | None = None, **overrides) -> dict:
+    """Generate the inputs of a named workload.
+
+    Returns a dict with the workload, the tensors (float32, values exact in the
+    workload dtype), ``initial_state`` (or None) and, for varlen, ``cu_seqlens``.
+    ``overrides`` replace shape fields (e.g. T=300 for a reduced-size case).
+    """
+    wl = WORKLOADS[name]
+    if overrides:
+        wl = Workload(**{**wl.__dict__, **overrides})
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    out: dict = {"workload": wl, "gate_mode": gate_mode, "generator": GEN_NAME,
+                 "numpy": np.__version__}
+    if wl.kind == "chunk":
+        out.update(token_tensors(rng, (wl.B, wl.T), wl.H, wl.dk, wl.dv, wl.dtype, gate_mode))
+        out["initial_state"] = initial_state(rng, wl.B, wl.H, wl.dk, wl.dv) if wl.init_state else None
+        out["cu_seqlens"] = None
+    elif wl.kind == "varlen":
+        lengths = varlen_lengths(rng, wl.num_seqs, wl.min_len, wl.max_len)
+        cu = cu_from_lengths(lengths)
+        total = int(cu[-1])
+        out.update(token_tensors(rng, (1, total), wl.H, wl.dk, wl.dv, wl.dtype, gate_mode))
+        out["initial_state"] = (initial_state(rng, wl.num_seqs, wl.H, wl.dk, wl.dv)
+                                if wl.init_state else None)
+        out["cu_seqlens"] = cu
+    elif wl.kind == "decode":
+        # `steps` pre-generated token slices [steps, N, H, d]; state [N, H, dk, dv]
+        out.update(token_tensors(rng, (wl.steps, wl.B), wl.H, wl.dk, wl.dv, wl.dtype, gate_mode))
+        out["initial_state"] = initial_state(rng, wl.B, wl.H, wl.dk, wl.dv)
+        out["cu_seqlens"] = None
+    else:
+        raise ValueError(wl.kind)
+    return out
+
+
+def to_torch(arr: np.ndarray, dtype: str, device="cpu"):
+    """float32 numpy array (values exact in ``dtype``) -> torch tensor on ``device``."""
+    import torch
+
+    if dtype == "bf16":
+        bits = bf16_bits(arr).view(np.int16)
+        t = torch.from_numpy(bits).view(torch.bfloat16)
+    elif dtype == "f32":
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    else:
+        raise ValueError(dtype)
+    return t.to(device)

@@ -1,0 +1,467 @@
+/*
+ * Gated DeltaNet-2 forward recurrence: plain FP64 CPU oracle.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the HIP library; it is slow on purpose and
+ * written so that each step can be checked against the pages by eye.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [IPX]  "Gated DeltaNet-2: Decoupling Erase and Write in Linear Attention",
+ *          analysis at iplexlaw.co.kr -- sections "Independent decisions on two
+ *          axes" (the update equations) and "Token processing and parallel
+ *          training" (64-token chunkwise WY form, FP32 decay / solve).
+ *   [MP]   "DeltaNet" entity trail at mindpattern.ai -- finding "You Could Have
+ *          Come Up With Kimi Delta Attention": per-key-channel decay with
+ *          diagonal-plus-low-rank transitions; fused recurrent and chunkwise
+ *          modes compute identical mathematics.
+ *
+ * The method, per head, per token t, with state S in R^{dk x dv} (keys index
+ * rows) [IPX, "Independent decisions on two axes"]:
+ *     e_t  = b_t (.) k_t                 erase vector on key channels
+ *     z_t  = w_t (.) v_t                 write vector on value channels
+ *     Sbar = Diag(alpha_t) S_{t-1}       channel-wise decay on key channels
+ *     r_t  = Sbar^T e_t                  old read
+ *     S_t  = Sbar + k_t (z_t - r_t)^T    delta update
+ *     o_t  = S_t^T q_t                   query reads the UPDATED state
+ *
+ * Functions:
+ *   gdn2_oracle_recurrent   O1  the definition, token by token  (THE oracle)
+ *   gdn2_oracle_chunked     O2  chunkwise WY form, any chunk size C (pin)
+ *   gdn2_oracle_transition  O3  explicit dk x dk transition products (pin)
+ *   gdn2_oracle_kda         O4a Kimi-Delta-Attention form (pin for b=w=beta)
+ *   gdn2_oracle_gdn         O4b Gated DeltaNet form (pin for scalar alpha)
+ *
+ * Layouts (row-major, contiguous, FP64):
+ *   q, k, b, alpha : [B, T, H, dk]        v, w, o : [B, T, H, dv]
+ *   initial / final state : [N, H, dk, dv]
+ *   With cu_seqlens (int32 [N+1], host memory) B must be 1 and sequence n
+ *   occupies packed tokens [cu_seqlens[n], cu_seqlens[n+1]); otherwise N = B
+ *   and sequence n is batch row n with T tokens.
+ *   chains (optional, int32 [num_chains]) selects which (n*H + h) chains are
+ *   evaluated; outputs of the other chains are left untouched.  NULL = all.
+ *   initial_state NULL = zeros; final_state NULL = not written.
+ * Return value: 0 on success, -1 on a bad argument.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+typedef struct {
+    int32_t B, T, H, dk, dv, N;
+    const int32_t* cu;
+} shape_t;
+
+/* Token range and batch row of sequence n. */
+static void seq_bounds(const shape_t* s, int32_t n, int64_t* bos, int64_t* eos, int64_t* brow)
+{
+    if (s->cu) {
+        *bos = s->cu[n];
+        *eos = s->cu[n + 1];
+        *brow = 0;
+    } else {
+        *bos = 0;
+        *eos = s->T;
+        *brow = n;
+    }
+}
+
+/* Offset of element 0 of token t (within batch row brow) for head h. */
+static int64_t tok_off(const shape_t* s, int64_t brow, int64_t t, int32_t h, int32_t width)
+{
+    return ((brow * s->T + t) * s->H + h) * (int64_t)width;
+}
+
+static int check_shape(const shape_t* s)
+{
+    if (s->B <= 0 || s->T < 0 || s->H <= 0 || s->dk <= 0 || s->dv <= 0 || s->N <= 0) return -1;
+    if (s->cu) {
+        if (s->B != 1) return -1;
+        if (s->cu[0] != 0) return -1;
+        for (int32_t n = 0; n < s->N; ++n)
+            if (s->cu[n + 1] < s->cu[n]) return -1;
+        if (s->cu[s->N] > s->T) return -1;
+    } else if (s->N != s->B) {
+        return -1;
+    }
+    return 0;
+}
+
+static int pick_threads(int32_t nthreads)
+{
+#ifdef _OPENMP
+    return nthreads > 0 ? nthreads : omp_get_max_threads();
+#else
+    (void)nthreads;
+    return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------------
+ * O1: the recurrence exactly as defined [IPX, "Independent decisions on two
+ * axes"], one token at a time.  S is dk x dv, row c = key channel c.
+ * ---------------------------------------------------------------------- */
+static void recurrent_chain(const shape_t* s, int32_t n, int32_t h,
+                            const double* q, const double* k, const double* v,
+                            const double* alpha, const double* b, const double* w,
+                            const double* S0, double* Sf, double* o)
+{
+    const int32_t dk = s->dk, dv = s->dv;
+    double* S = (double*)calloc((size_t)dk * dv, sizeof(double));
+    double* e = (double*)malloc(sizeof(double) * dk);
+    double* z = (double*)malloc(sizeof(double) * dv);
+    double* r = (double*)malloc(sizeof(double) * dv);
+    const int64_t soff = ((int64_t)n * s->H + h) * dk * dv;
+    if (S0) memcpy(S, S0 + soff, sizeof(double) * dk * dv);
+
+    int64_t bos, eos, brow;
+    seq_bounds(s, n, &bos, &eos, &brow);
+    for (int64_t t = bos; t < eos; ++t) {
+        const double* qt = q + tok_off(s, brow, t, h, dk);
+        const double* kt = k + tok_off(s, brow, t, h, dk);
+        const double* bt = b + tok_off(s, brow, t, h, dk);
+        const double* at = alpha + tok_off(s, brow, t, h, dk);
+        const double* vt = v + tok_off(s, brow, t, h, dv);
+        const double* wt = w + tok_off(s, brow, t, h, dv);
+        double* ot = o + tok_off(s, brow, t, h, dv);
+
+        for (int32_t c = 0; c < dk; ++c) e[c] = bt[c] * kt[c];          /* e = b (.) k */
+        for (int32_t j = 0; j < dv; ++j) z[j] = wt[j] * vt[j];          /* z = w (.) v */
+        for (int32_t c = 0; c < dk; ++c)                                /* Sbar = Diag(alpha) S */
+            for (int32_t j = 0; j < dv; ++j) S[c * dv + j] *= at[c];
+        for (int32_t j = 0; j < dv; ++j) {                              /* r = Sbar^T e */
+            double acc = 0.0;
+            for (int32_t c = 0; c < dk; ++c) acc += S[c * dv + j] * e[c];
+            r[j] = acc;
+        }
+        for (int32_t c = 0; c < dk; ++c)                                /* S = Sbar + k (z - r)^T */
+            for (int32_t j = 0; j < dv; ++j) S[c * dv + j] += kt[c] * (z[j] - r[j]);
+        for (int32_t j = 0; j < dv; ++j) {                              /* o = S^T q */
+            double acc = 0.0;
+            for (int32_t c = 0; c < dk; ++c) acc += S[c * dv + j] * qt[c];
+            ot[j] = acc;
+        }
+    }
+    if (Sf) memcpy(Sf + soff, S, sizeof(double) * dk * dv);
+    free(S);
+    free(e);
+    free(z);
+    free(r);
+}
+
+/* ------------------------------------------------------------------------
+ * O2: the chunkwise form [IPX, "Token processing and parallel training"]:
+ * within a chunk the cumulative channel-wise decay is absorbed into
+ * asymmetric factors (row side e * exp(+G), column side k * exp(-G)), which
+ * leaves a unit-lower-triangular solve and dense products:
+ *   G_i  = sum_{m<=i} log alpha_m                 (per key channel)
+ *   Et_i = e_i exp(G_i),  Kh_j = k_j exp(-G_j),  Qt_i = q_i exp(G_i),
+ *   Kb_j = k_j exp(G_last - G_j)
+ *   A    = strict_lower(Et Kh^T),  P = lower_incl_diag(Qt Kh^T)
+ *   Tm   = (I + A)^{-1}           (forward substitution)
+ *   W    = Tm Et,   Ut = Tm Z,    U = Ut - W S0
+ *   O    = Qt S0 + P U,           S_last = Diag(exp(G_last)) S0 + Kb^T U
+ * Chunks restart at every sequence start; the last chunk may be short.
+ * Requires alpha > 0 (log).  FP64; meant for small inputs.
+ * ---------------------------------------------------------------------- */
+static void chunked_chain(const shape_t* s, int32_t n, int32_t h, int32_t C,
+                          const double* q, const double* k, const double* v,
+                          const double* alpha, const double* b, const double* w,
+                          const double* S0, double* Sf, double* o)
+{
+    const int32_t dk = s->dk, dv = s->dv;
+    const size_t LK = (size_t)C * dk, LV = (size_t)C * dv, LL = (size_t)C * C;
+    double* S  = (double*)calloc((size_t)dk * dv, sizeof(double));
+    double* G  = (double*)malloc(sizeof(double) * LK);
+    double* Et = (double*)malloc(sizeof(double) * LK);
+    double* Kh = (double*)malloc(sizeof(double) * LK);
+    double* Qt = (double*)malloc(sizeof(double) * LK);
+    double* Kb = (double*)malloc(sizeof(double) * LK);
+    double* Z  = (double*)malloc(sizeof(double) * LV);
+    double* A  = (double*)malloc(sizeof(double) * LL);
+    double* P  = (double*)malloc(sizeof(double) * LL);
+    double* Tm = (double*)malloc(sizeof(double) * LL);
+    double* W  = (double*)malloc(sizeof(double) * LK);
+    double* U  = (double*)malloc(sizeof(double) * LV);
+    double* Sn = (double*)malloc(sizeof(double) * (size_t)dk * dv);
+    const int64_t soff = ((int64_t)n * s->H + h) * dk * dv;
+    if (S0) memcpy(S, S0 + soff, sizeof(double) * dk * dv);
+
+    int64_t bos, eos, brow;
+    seq_bounds(s, n, &bos, &eos, &brow);
+    for (int64_t t0 = bos; t0 < eos; t0 += C) {
+        const int32_t L = (int32_t)((eos - t0) < C ? (eos - t0) : C);
+        /* cumulative log decay and absorbed factors */
+        for (int32_t i = 0; i < L; ++i) {
+            const int64_t ok = tok_off(s, brow, t0 + i, h, dk);
+            const int64_t ov = tok_off(s, brow, t0 + i, h, dv);
+            for (int32_t c = 0; c < dk; ++c) {
+                const double prev = i ? G[(size_t)(i - 1) * dk + c] : 0.0;
+                G[(size_t)i * dk + c] = prev + log(alpha[ok + c]);
+            }
+            for (int32_t c = 0; c < dk; ++c) {
+                const double g = G[(size_t)i * dk + c];
+                Et[(size_t)i * dk + c] = b[ok + c] * k[ok + c] * exp(g);
+                Kh[(size_t)i * dk + c] = k[ok + c] * exp(-g);
+                Qt[(size_t)i * dk + c] = q[ok + c] * exp(g);
+            }
+            for (int32_t j = 0; j < dv; ++j) Z[(size_t)i * dv + j] = w[ov + j] * v[ov + j];
+        }
+        for (int32_t i = 0; i < L; ++i)
+            for (int32_t c = 0; c < dk; ++c)
+                Kb[(size_t)i * dk + c] = Kh[(size_t)i * dk + c] * exp(G[(size_t)(L - 1) * dk + c]);
+        /* A (strictly lower) and P (lower including the diagonal) */
+        for (int32_t i = 0; i < L; ++i)
+            for (int32_t j = 0; j < L; ++j) {
+                double a = 0.0, p = 0.0;
+                for (int32_t c = 0; c < dk; ++c) {
+                    a += Et[(size_t)i * dk + c] * Kh[(size_t)j * dk + c];
+                    p += Qt[(size_t)i * dk + c] * Kh[(size_t)j * dk + c];
+                }
+                A[(size_t)i * C + j] = j < i ? a : 0.0;
+                P[(size_t)i * C + j] = j <= i ? p : 0.0;
+            }
+        /* Tm = (I + A)^{-1}, unit lower triangular, column by column */
+        for (int32_t j = 0; j < L; ++j)
+            for (int32_t i = 0; i < L; ++i) {
+                if (i < j) { Tm[(size_t)i * C + j] = 0.0; continue; }
+                if (i == j) { Tm[(size_t)i * C + j] = 1.0; continue; }
+                double acc = 0.0;
+                for (int32_t m = j; m < i; ++m) acc += A[(size_t)i * C + m] * Tm[(size_t)m * C + j];
+                Tm[(size_t)i * C + j] = -acc;
+            }
+        /* W = Tm Et ; U = Tm Z - W S */
+        for (int32_t i = 0; i < L; ++i) {
+            for (int32_t c = 0; c < dk; ++c) {
+                double acc = 0.0;
+                for (int32_t m = 0; m <= i; ++m) acc += Tm[(size_t)i * C + m] * Et[(size_t)m * dk + c];
+                W[(size_t)i * dk + c] = acc;
+            }
+            for (int32_t j = 0; j < dv; ++j) {
+                double ut = 0.0, ws = 0.0;
+                for (int32_t m = 0; m <= i; ++m) ut += Tm[(size_t)i * C + m] * Z[(size_t)m * dv + j];
+                for (int32_t c = 0; c < dk; ++c) ws += W[(size_t)i * dk + c] * S[(size_t)c * dv + j];
+                U[(size_t)i * dv + j] = ut - ws;
+            }
+        }
+        /* O = Qt S + P U */
+        for (int32_t i = 0; i < L; ++i) {
+            double* ot = o + tok_off(s, brow, t0 + i, h, dv);
+            for (int32_t j = 0; j < dv; ++j) {
+                double acc = 0.0;
+                for (int32_t c = 0; c < dk; ++c) acc += Qt[(size_t)i * dk + c] * S[(size_t)c * dv + j];
+                for (int32_t m = 0; m <= i; ++m) acc += P[(size_t)i * C + m] * U[(size_t)m * dv + j];
+                ot[j] = acc;
+            }
+        }
+        /* S <- Diag(exp(G_last)) S + Kb^T U */
+        for (int32_t c = 0; c < dk; ++c) {
+            const double gl = exp(G[(size_t)(L - 1) * dk + c]);
+            for (int32_t j = 0; j < dv; ++j) {
+                double acc = gl * S[(size_t)c * dv + j];
+                for (int32_t m = 0; m < L; ++m) acc += Kb[(size_t)m * dk + c] * U[(size_t)m * dv + j];
+                Sn[(size_t)c * dv + j] = acc;
+            }
+        }
+        memcpy(S, Sn, sizeof(double) * dk * dv);
+    }
+    if (Sf) memcpy(Sf + soff, S, sizeof(double) * dk * dv);
+    free(S); free(G); free(Et); free(Kh); free(Qt); free(Kb); free(Z);
+    free(A); free(P); free(Tm); free(W); free(U); free(Sn);
+}
+
+/* ------------------------------------------------------------------------
+ * O3: the same recurrence written with explicit transition matrices
+ * [MP, "diagonal-plus-low-rank transitions"]:
+ *     M_t = (I - k_t e_t^T) Diag(alpha_t)      (dk x dk)
+ *     S_t = M_t S_{t-1} + k_t z_t^T,   o_t = S_t^T q_t
+ * ---------------------------------------------------------------------- */
+static void transition_chain(const shape_t* s, int32_t n, int32_t h,
+                             const double* q, const double* k, const double* v,
+                             const double* alpha, const double* b, const double* w,
+                             const double* S0, double* Sf, double* o)
+{
+    const int32_t dk = s->dk, dv = s->dv;
+    double* S  = (double*)calloc((size_t)dk * dv, sizeof(double));
+    double* Sn = (double*)malloc(sizeof(double) * (size_t)dk * dv);
+    double* M  = (double*)malloc(sizeof(double) * (size_t)dk * dk);
+    const int64_t soff = ((int64_t)n * s->H + h) * dk * dv;
+    if (S0) memcpy(S, S0 + soff, sizeof(double) * dk * dv);
+
+    int64_t bos, eos, brow;
+    seq_bounds(s, n, &bos, &eos, &brow);
+    for (int64_t t = bos; t < eos; ++t) {
+        const int64_t ok = tok_off(s, brow, t, h, dk);
+        const int64_t ov = tok_off(s, brow, t, h, dv);
+        for (int32_t r = 0; r < dk; ++r)
+            for (int32_t c = 0; c < dk; ++c) {
+                const double id = r == c ? 1.0 : 0.0;
+                M[(size_t)r * dk + c] = (id - k[ok + r] * b[ok + c] * k[ok + c]) * alpha[ok + c];
+            }
+        for (int32_t r = 0; r < dk; ++r)
+            for (int32_t j = 0; j < dv; ++j) {
+                double acc = k[ok + r] * w[ov + j] * v[ov + j];
+                for (int32_t c = 0; c < dk; ++c) acc += M[(size_t)r * dk + c] * S[(size_t)c * dv + j];
+                Sn[(size_t)r * dv + j] = acc;
+            }
+        memcpy(S, Sn, sizeof(double) * dk * dv);
+        for (int32_t j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int32_t r = 0; r < dk; ++r) acc += S[(size_t)r * dv + j] * q[ok + r];
+            o[ov + j] = acc;
+        }
+    }
+    if (Sf) memcpy(Sf + soff, S, sizeof(double) * dk * dv);
+    free(S);
+    free(Sn);
+    free(M);
+}
+
+/* ------------------------------------------------------------------------
+ * O4: the two published relatives the method reduces to [IPX, "Independent
+ * decisions on two axes": tying both gates to one scalar beta gives KDA, and
+ * also making the decay scalar gives Gated DeltaNet; "From a growing cache to
+ * a fixed state" for the roles of the gates].  Written in their own matrix
+ * form with a scalar beta per token-head:
+ *   KDA: S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *   GDN: S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T
+ *   both: o_t = S_t^T q_t
+ * beta: [B, T, H];  KDA alpha: [B, T, H, dk];  GDN alpha: [B, T, H].
+ * ---------------------------------------------------------------------- */
+static void relative_chain(const shape_t* s, int32_t n, int32_t h, int scalar_alpha,
+                           const double* q, const double* k, const double* v,
+                           const double* alpha, const double* beta,
+                           const double* S0, double* Sf, double* o)
+{
+    const int32_t dk = s->dk, dv = s->dv;
+    double* S  = (double*)calloc((size_t)dk * dv, sizeof(double));
+    double* D  = (double*)malloc(sizeof(double) * (size_t)dk * dv);
+    double* M  = (double*)malloc(sizeof(double) * (size_t)dk * dk);
+    const int64_t soff = ((int64_t)n * s->H + h) * dk * dv;
+    if (S0) memcpy(S, S0 + soff, sizeof(double) * dk * dv);
+
+    int64_t bos, eos, brow;
+    seq_bounds(s, n, &bos, &eos, &brow);
+    for (int64_t t = bos; t < eos; ++t) {
+        const int64_t ok = tok_off(s, brow, t, h, dk);
+        const int64_t ov = tok_off(s, brow, t, h, dv);
+        const int64_t os = tok_off(s, brow, t, h, 1);
+        const double bt = beta[os];
+        for (int32_t r = 0; r < dk; ++r)        /* D = decayed state */
+            for (int32_t j = 0; j < dv; ++j)
+                D[(size_t)r * dv + j] = (scalar_alpha ? alpha[os] : alpha[ok + r]) * S[(size_t)r * dv + j];
+        for (int32_t r = 0; r < dk; ++r)        /* M = I - beta k k^T */
+            for (int32_t c = 0; c < dk; ++c)
+                M[(size_t)r * dk + c] = (r == c ? 1.0 : 0.0) - bt * k[ok + r] * k[ok + c];
+        for (int32_t r = 0; r < dk; ++r)
+            for (int32_t j = 0; j < dv; ++j) {
+                double acc = bt * k[ok + r] * v[ov + j];
+                for (int32_t c = 0; c < dk; ++c) acc += M[(size_t)r * dk + c] * D[(size_t)c * dv + j];
+                S[(size_t)r * dv + j] = acc;
+            }
+        for (int32_t j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int32_t r = 0; r < dk; ++r) acc += S[(size_t)r * dv + j] * q[ok + r];
+            o[ov + j] = acc;
+        }
+    }
+    if (Sf) memcpy(Sf + soff, S, sizeof(double) * dk * dv);
+    free(S);
+    free(D);
+    free(M);
+}
+
+/* ---------------------------------------------------------------------- */
+
+#define CHAIN_LOOP(BODY)                                                              \
+    do {                                                                              \
+        const int64_t total = chains ? (int64_t)num_chains : (int64_t)s.N * s.H;      \
+        if (chains)                                                                   \
+            for (int64_t i = 0; i < total; ++i)                                       \
+                if (chains[i] < 0 || chains[i] >= s.N * s.H) return -1;               \
+        _Pragma("omp parallel for schedule(dynamic, 1) num_threads(nt)")              \
+        for (int64_t i = 0; i < total; ++i) {                                         \
+            const int32_t id = chains ? chains[i] : (int32_t)i;                       \
+            const int32_t n = id / s.H, h = id % s.H;                                 \
+            BODY;                                                                     \
+        }                                                                             \
+    } while (0)
+
+int gdn2_oracle_recurrent(const double* q, const double* k, const double* v,
+                          const double* alpha, const double* b, const double* w,
+                          const double* initial_state, double* final_state, double* o,
+                          const int32_t* cu_seqlens, int32_t B, int32_t T, int32_t H,
+                          int32_t dk, int32_t dv, int32_t num_seqs,
+                          const int32_t* chains, int32_t num_chains, int32_t nthreads)
+{
+    const shape_t s = {B, T, H, dk, dv, cu_seqlens ? num_seqs : B, cu_seqlens};
+    if (check_shape(&s) || !q || !k || !v || !alpha || !b || !w || !o) return -1;
+    const int nt = pick_threads(nthreads);
+    CHAIN_LOOP(recurrent_chain(&s, n, h, q, k, v, alpha, b, w, initial_state, final_state, o));
+    return 0;
+}
+
+int gdn2_oracle_chunked(const double* q, const double* k, const double* v,
+                        const double* alpha, const double* b, const double* w,
+                        const double* initial_state, double* final_state, double* o,
+                        const int32_t* cu_seqlens, int32_t B, int32_t T, int32_t H,
+                        int32_t dk, int32_t dv, int32_t num_seqs, int32_t chunk,
+                        const int32_t* chains, int32_t num_chains, int32_t nthreads)
+{
+    const shape_t s = {B, T, H, dk, dv, cu_seqlens ? num_seqs : B, cu_seqlens};
+    if (check_shape(&s) || chunk <= 0 || !q || !k || !v || !alpha || !b || !w || !o) return -1;
+    const int nt = pick_threads(nthreads);
+    CHAIN_LOOP(chunked_chain(&s, n, h, chunk, q, k, v, alpha, b, w, initial_state, final_state, o));
+    return 0;
+}
+
+int gdn2_oracle_transition(const double* q, const double* k, const double* v,
+                           const double* alpha, const double* b, const double* w,
+                           const double* initial_state, double* final_state, double* o,
+                           const int32_t* cu_seqlens, int32_t B, int32_t T, int32_t H,
+                           int32_t dk, int32_t dv, int32_t num_seqs,
+                           const int32_t* chains, int32_t num_chains, int32_t nthreads)
+{
+    const shape_t s = {B, T, H, dk, dv, cu_seqlens ? num_seqs : B, cu_seqlens};
+    if (check_shape(&s) || !q || !k || !v || !alpha || !b || !w || !o) return -1;
+    const int nt = pick_threads(nthreads);
+    CHAIN_LOOP(transition_chain(&s, n, h, q, k, v, alpha, b, w, initial_state, final_state, o));
+    return 0;
+}
+
+int gdn2_oracle_kda(const double* q, const double* k, const double* v,
+                    const double* alpha, const double* beta,
+                    const double* initial_state, double* final_state, double* o,
+                    const int32_t* cu_seqlens, int32_t B, int32_t T, int32_t H,
+                    int32_t dk, int32_t dv, int32_t num_seqs,
+                    const int32_t* chains, int32_t num_chains, int32_t nthreads)
+{
+    const shape_t s = {B, T, H, dk, dv, cu_seqlens ? num_seqs : B, cu_seqlens};
+    if (check_shape(&s) || !q || !k || !v || !alpha || !beta || !o) return -1;
+    const int nt = pick_threads(nthreads);
+    CHAIN_LOOP(relative_chain(&s, n, h, 0, q, k, v, alpha, beta, initial_state, final_state, o));
+    return 0;
+}
+
+int gdn2_oracle_gdn(const double* q, const double* k, const double* v,
+                    const double* alpha, const double* beta,
+                    const double* initial_state, double* final_state, double* o,
+                    const int32_t* cu_seqlens, int32_t B, int32_t T, int32_t H,
+                    int32_t dk, int32_t dv, int32_t num_seqs,
+                    const int32_t* chains, int32_t num_chains, int32_t nthreads)
+{
+    const shape_t s = {B, T, H, dk, dv, cu_seqlens ? num_seqs : B, cu_seqlens};
+    if (check_shape(&s) || !q || !k || !v || !alpha || !beta || !o) return -1;
+    const int nt = pick_threads(nthreads);
+    CHAIN_LOOP(relative_chain(&s, n, h, 1, q, k, v, alpha, beta, initial_state, final_state, o));
+    return 0;
+}
+
+int gdn2_oracle_max_threads(void)
+{
+    return pick_threads(0);
+}
