@@ -1,0 +1,228 @@
+"""Benchmark of the GDN-2 forward hot path on one MI355X.
+
+A step is one chunkwise forward (gdn2_chunk_fwd) over the batched training
+shape B=8, T=4096, H=16, dk=dv=128 (bf16 q/k/v/b/w, FP32 alpha and state,
+N(0, 0.1^2) initial state).  ``value`` is its throughput in tokens/s (B*T
+tokens per call), inputs resident in HBM.  The decode half of the metric --
+gdn2_recurrent_step over N=256 sequences x 16 heads with 128 x 128 FP32
+states, 64 consecutive in-place steps -- is timed right after and reported as
+state GB/s under "decode".  Both carry their roofline; the FP64 CPU oracle is
+timed on a bounded sample of the same chunkwise workload as ``cpu_baseline``.
+
+Prints exactly one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GDN-2 fwd tokens/s (H16,d128,T4K,B8) + decode state GB/s; % of roofline"
+HBM_PEAK_GBPS = 8000.0
+NAMES = ("q", "k", "v", "alpha", "b", "w")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def chunk_bytes(B, T, H, dk, dv, N, eb=2):
+    """Algorithmic HBM bytes of one chunkwise forward: q, k, b, v, w read and
+    o written in the input dtype, alpha read in FP32, the state read once and
+    written once in FP32."""
+    tok = B * T * H
+    return tok * (3 * dk * eb + 2 * dv * eb + dk * 4 + dv * eb) + 2 * N * H * dk * dv * 4
+
+
+def step_bytes(N, H, dk, dv, eb=2):
+    """Algorithmic HBM bytes of one decode step: the FP32 state read and
+    written once, the token vectors read, o written."""
+    return N * H * (2 * dk * dv * 4 + 3 * dk * eb + 2 * dv * eb + dk * 4 + dv * eb)
+
+
+def to_dev(x, dtype):
+    from delta_rule_linear_gdn2_amd import workloads as W
+
+    return {n: W.to_torch(x[n], "f32" if n == "alpha" else dtype, "cuda") for n in NAMES}
+
+
+def time_events(fn, warmup, steps):
+    """Per-call HIP-event durations (ms) on the current stream, plus total."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_all0.record()
+    for e0, e1 in ev:
+        e0.record()
+        fn()
+        e1.record()
+    t_all1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per = [e0.elapsed_time(e1) for e0, e1 in ev]
+    return per, t_all0.elapsed_time(t_all1), wall
+
+
+def bench_chunk(args):
+    import torch
+
+    from delta_rule_linear_gdn2_amd import binding
+    from delta_rule_linear_gdn2_amd import workloads as W
+
+    t0 = time.time()
+    x = W.make(args.workload)
+    wl = x["workload"]
+    log(f"generated {wl.name} in {time.time() - t0:.1f}s")
+    d = to_dev(x, wl.dtype)
+    s0 = None if x["initial_state"] is None else torch.from_numpy(x["initial_state"]).cuda()
+    cu = None if x["cu_seqlens"] is None else torch.from_numpy(x["cu_seqlens"]).cuda()
+    B, T, H, dk = x["q"].shape
+    dv = x["v"].shape[-1]
+    N = B if cu is None else int(cu.shape[0]) - 1
+    o = torch.empty((B, T, H, dv), dtype=d["q"].dtype, device="cuda")
+    sf = torch.empty((N, H, dk, dv), dtype=torch.float32, device="cuda")
+
+    def call():
+        binding.gdn2_chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["b"], d["w"], s0,
+                               final_state=sf, out=o, cu_seqlens=cu)
+
+    per, total_ms, wall = time_events(call, args.warmup, args.steps)
+    ms = total_ms / args.steps
+    kern_ms = float(np.mean(per))
+    eb = 2 if wl.dtype == "bf16" else 4
+    nbytes = chunk_bytes(B, T, H, dk, dv, N, eb)
+    tokens = B * T
+    log(f"chunk: {ms * 1e3:.1f} us/step (event avg {kern_ms * 1e3:.1f} us), "
+        f"{tokens / (ms / 1e3) / 1e6:.2f} M tokens/s, {nbytes / (kern_ms / 1e3) / 1e9:.0f} GB/s")
+    return dict(x=x, wl=wl, tokens=tokens, ms=ms, kern_ms=kern_ms, wall=wall, bytes=nbytes,
+                per=per, dims=(B, T, H, dk, dv, N))
+
+
+def bench_decode(args):
+    import torch
+
+    from delta_rule_linear_gdn2_amd import binding
+    from delta_rule_linear_gdn2_amd import workloads as W
+
+    x = W.make("decode_b256")
+    wl = x["workload"]
+    steps_in = x["q"].shape[0]
+    N, H, dk = x["q"].shape[1:]
+    dv = x["v"].shape[-1]
+    slices = [to_dev({n: x[n][t] for n in NAMES}, wl.dtype) for t in range(steps_in)]
+    state = torch.from_numpy(x["initial_state"]).cuda()
+    outs = [torch.empty((N, H, dv), dtype=slices[0]["q"].dtype, device="cuda") for _ in range(steps_in)]
+
+    def call():  # the 64 consecutive in-place steps
+        for t in range(steps_in):
+            s = slices[t]
+            binding.gdn2_recurrent_step(s["q"], s["k"], s["v"], s["alpha"], s["b"], s["w"], state,
+                                        out=outs[t])
+
+    per, total_ms, _ = time_events(call, max(1, args.warmup), max(1, args.steps // 4))
+    step_ms = total_ms / max(1, args.steps // 4) / steps_in
+    state_bytes = 2 * N * H * dk * dv * 4
+    nbytes = step_bytes(N, H, dk, dv)
+    log(f"decode: {step_ms * 1e3:.1f} us/step, state {state_bytes / (step_ms / 1e3) / 1e9:.0f} GB/s")
+    return dict(step_ms=step_ms, state_gbps=state_bytes / (step_ms / 1e3) / 1e9,
+                achieved=nbytes / (step_ms / 1e3) / 1e9, bytes=nbytes)
+
+
+def cpu_baseline(x, wl, chains_rows=4):
+    """The FP64 oracle on the first ``chains_rows`` batch rows (all heads, full length)."""
+    import oracle
+
+    sub = {n: np.ascontiguousarray(x[n][:chains_rows]) for n in NAMES}
+    s0 = None if x["initial_state"] is None else np.ascontiguousarray(x["initial_state"][:chains_rows])
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    oracle.recurrent(sub["q"], sub["k"], sub["v"], sub["alpha"], sub["b"], sub["w"], s0, threads=threads)
+    wall = time.perf_counter() - t0
+    tokens = chains_rows * wl.T
+    return {"value": tokens / wall, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{chains_rows} of {wl.B} sequences x all {wl.H} heads x {wl.T} tokens "
+                      f"({chains_rows * wl.H} (sequence, head) chains) of the same workload, FP64, "
+                      f"{wall:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="batched_bf16",
+                    choices=["batched_bf16", "layer_bf16", "varlen32_bf16", "tiny_f32"])
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode half")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from delta_rule_linear_gdn2_amd import binding
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    binding.load()
+    ch = bench_chunk(args)
+    dec = None if args.no_decode else bench_decode(args)
+    cpu = None
+    if not args.no_cpu and ch["wl"].kind == "chunk":
+        cpu = cpu_baseline(ch["x"], ch["wl"], chains_rows=min(4, ch["wl"].B))
+        log(f"cpu oracle: {cpu['value']:.0f} tokens/s on {cpu['cores']} threads")
+    B, T, H, dk, dv, N = ch["dims"]
+    wl = ch["wl"]
+    achieved = ch["bytes"] / (ch["kern_ms"] / 1e3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": ch["tokens"] / (ch["ms"] / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ch["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded numpy PCG64; Gaussian/sigmoid inputs, L2-normalised q,k)",
+        "config": {"workload": f"{wl.name}: chunkwise forward B={B} T={T} H={H} dk={dk} dv={dv}, "
+                               f"64-token chunks, FP32 alpha/state",
+                   "B": B, "T": T, "H": H, "dk": dk, "dv": dv, "num_seqs": N},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "gdn2 chunk forward", "algorithmic_bytes": ch["bytes"],
+                     "avg_launch_ms": ch["kern_ms"]},
+        "cpu_baseline": cpu,
+    }
+    if dec is not None:
+        out["decode"] = {
+            "workload": "decode_b256: N=256 H=16 dk=dv=128, bf16 tokens, FP32 state, 64 in-place steps",
+            "state_GBps": dec["state_gbps"], "us_per_step": dec["step_ms"] * 1e3,
+            "roofline": {"bound": "hbm", "achieved": dec["achieved"], "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": dec["achieved"] / HBM_PEAK_GBPS, "traffic": None,
+                         "algorithmic_bytes": dec["bytes"]},
+        }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,27 @@
+"""Gated DeltaNet-2 forward pass for AMD Instinct MI355X (gfx950).
+
+Two entry points, both hand-written HIP behind the C ABI in include/gdn2.h:
+
+* ``gdn2_chunk_fwd``      chunkwise WY forward over whole sequences (64-token
+                          chunks; varlen via ``cu_seqlens``)
+* ``gdn2_recurrent_step`` fused single-token decode step, state updated in place
+
+Importing the package does not load the library; the first call does.
+"""
+from .binding import (  # noqa: F401
+    Gdn2Error,
+    gdn2_chunk_fwd,
+    gdn2_chunk_fwd_workspace_bytes,
+    gdn2_recurrent_step,
+    load,
+    status_string,
+)
+
+__all__ = [
+    "Gdn2Error",
+    "gdn2_chunk_fwd",
+    "gdn2_chunk_fwd_workspace_bytes",
+    "gdn2_recurrent_step",
+    "load",
+    "status_string",
+]

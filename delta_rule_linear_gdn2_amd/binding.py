@@ -1,0 +1,189 @@
+"""ctypes binding of ``libgdn2.so`` (the C ABI declared in include/gdn2.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  PyTorch supplies device memory and the current
+stream.  There is no fallback: if the library is missing or cannot bind to the
+HIP runtime torch uses, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgdn2.so")
+
+GDN2_OK = 0
+STATUS_NAMES = {
+    0: "GDN2_OK", 1: "GDN2_ERR_NULL_POINTER", 2: "GDN2_ERR_BAD_SHAPE", 3: "GDN2_ERR_UNSUPPORTED",
+    4: "GDN2_ERR_BAD_DTYPE", 5: "GDN2_ERR_MISALIGNED", 6: "GDN2_ERR_ALIAS", 7: "GDN2_ERR_WORKSPACE",
+    8: "GDN2_ERR_HIP",
+}
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+
+EXPORTS = ("gdn2_chunk_fwd", "gdn2_chunk_fwd_workspace_bytes", "gdn2_recurrent_step",
+           "gdn2_status_string", "gdn2_version")
+
+
+class Gdn2Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = int(status)
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+_LIB = None
+
+
+def _hip_runtimes_loaded() -> set[str]:
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    paths.add(os.path.realpath(line.split()[-1]))
+    except OSError:
+        pass
+    return paths
+
+
+def load(path: str = LIB_PATH):
+    """Load ``libgdn2.so`` (after torch, so it binds to torch's HIP runtime)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    import torch  # noqa: F401  -- loads torch's libamdhip64 first (same SONAME)
+
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built; build it with `python -m delta_rule_linear_gdn2_amd.build` "
+            "(the GDN-2 ops have no non-HIP implementation)")
+    lib = ctypes.CDLL(path)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.gdn2_chunk_fwd.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, Z, P]
+    lib.gdn2_chunk_fwd.restype = ctypes.c_int
+    lib.gdn2_chunk_fwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+    lib.gdn2_chunk_fwd_workspace_bytes.restype = Z
+    lib.gdn2_recurrent_step.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, P]
+    lib.gdn2_recurrent_step.restype = ctypes.c_int
+    lib.gdn2_status_string.argtypes = [ctypes.c_int]
+    lib.gdn2_status_string.restype = ctypes.c_char_p
+    lib.gdn2_version.argtypes = []
+    lib.gdn2_version.restype = ctypes.c_int32
+    runtimes = _hip_runtimes_loaded()
+    if len(runtimes) > 1:
+        raise RuntimeError(f"two HIP runtimes are mapped in this process: {sorted(runtimes)}")
+    _LIB = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().gdn2_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(dt) -> int:
+    import torch
+
+    if dt == torch.bfloat16:
+        return DTYPE_BF16
+    if dt == torch.float32:
+        return DTYPE_F32
+    raise TypeError(f"unsupported dtype {dt} (float32 or bfloat16)")
+
+
+def _check(name, t, shape, dtype, device):
+    if t.shape != shape:
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {shape}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype} != {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, num_seqs, dtype_code) -> int:
+    return int(load().gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, num_seqs, dtype_code))
+
+
+def gdn2_chunk_fwd(q, k, v, alpha, b, w, initial_state=None, *, output_final_state=True,
+                   final_state=None, out=None, cu_seqlens=None, stream=None):
+    """Chunkwise GDN-2 forward.  Returns ``(o, final_state)`` (final_state may be None).
+
+    q, k, b: [B, T, H, dk]; v, w: [B, T, H, dv] (float32 or bfloat16, all the
+    same); alpha: [B, T, H, dk] float32; initial_state: [N, H, dk, dv] float32
+    or None; cu_seqlens: int32 [N + 1] on the device or None (then B must be 1).
+    ``final_state`` may be passed (e.g. the initial_state tensor itself for an
+    in-place update); otherwise it is allocated when ``output_final_state``.
+    """
+    import torch
+
+    lib = load()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(dt)
+    N = B if cu_seqlens is None else int(cu_seqlens.shape[0]) - 1
+    for name, t, width in (("q", q, dk), ("k", k, dk), ("b", b, dk), ("v", v, dv), ("w", w, dv)):
+        _check(name, t, (B, T, H, width), dt, dev)
+    _check("alpha", alpha, (B, T, H, dk), torch.float32, dev)
+    if initial_state is not None:
+        _check("initial_state", initial_state, (N, H, dk, dv), torch.float32, dev)
+    if cu_seqlens is not None:
+        _check("cu_seqlens", cu_seqlens, (N + 1,), torch.int32, dev)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    else:
+        _check("out", out, (B, T, H, dv), dt, dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _check("final_state", final_state, (N, H, dk, dv), torch.float32, dev)
+    ws_bytes = gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, code)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    rc = lib.gdn2_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w),
+                            _ptr(initial_state), _ptr(final_state), _ptr(out), _ptr(cu_seqlens),
+                            B, T, H, dk, dv, N, code, _ptr(ws), ws_bytes, _stream(stream))
+    if rc != GDN2_OK:
+        raise Gdn2Error(rc, "gdn2_chunk_fwd")
+    return out, final_state
+
+
+def gdn2_recurrent_step(q, k, v, alpha, b, w, state, *, out=None, stream=None):
+    """One fused recurrent (decode) step; updates ``state`` in place, returns o.
+
+    q, k, b: [N, H, dk]; v, w: [N, H, dv]; alpha: [N, H, dk] float32;
+    state: [N, H, dk, dv] float32.
+    """
+    import torch
+
+    lib = load()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(dt)
+    for name, t, width in (("q", q, dk), ("k", k, dk), ("b", b, dk), ("v", v, dv), ("w", w, dv)):
+        _check(name, t, (N, H, width), dt, dev)
+    _check("alpha", alpha, (N, H, dk), torch.float32, dev)
+    _check("state", state, (N, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=dt, device=dev)
+    else:
+        _check("out", out, (N, H, dv), dt, dev)
+    rc = lib.gdn2_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w),
+                                 _ptr(state), _ptr(out), N, H, dk, dv, code, _stream(stream))
+    if rc != GDN2_OK:
+        raise Gdn2Error(rc, "gdn2_recurrent_step")
+    return out

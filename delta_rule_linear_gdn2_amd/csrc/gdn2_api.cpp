@@ -1,0 +1,147 @@
+// C ABI of the GDN-2 library: argument validation and kernel dispatch.
+//
+// Every check runs on the host before anything is enqueued, so argument
+// errors come back synchronously and never reach the device.
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
+#include <cstdint>
+
+#include "../../include/gdn2.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int32_t kVersion = 10000;  // 1.0.0
+
+bool supported_head(int32_t d) { return d == 32 || d == 64 || d == 128; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Span span(const void* p, int64_t bytes)
+{
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return {lo, lo + uintptr_t(bytes)};
+}
+
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+int element_bytes(gdn2_dtype dt) { return dt == GDN2_DTYPE_BF16 ? 2 : 4; }
+
+// Compute units of the current device, cached per device id.
+int32_t device_cus()
+{
+    static std::atomic<int32_t> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64) {
+        const int32_t c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn2_status_string(gdn2_status s)
+{
+    switch (s) {
+        case GDN2_OK: return "GDN2_OK";
+        case GDN2_ERR_NULL_POINTER: return "GDN2_ERR_NULL_POINTER: a required pointer is NULL";
+        case GDN2_ERR_BAD_SHAPE: return "GDN2_ERR_BAD_SHAPE: invalid or inconsistent sizes";
+        case GDN2_ERR_UNSUPPORTED: return "GDN2_ERR_UNSUPPORTED: head size not supported (dk, dv in {32, 64, 128})";
+        case GDN2_ERR_BAD_DTYPE: return "GDN2_ERR_BAD_DTYPE: unknown dtype";
+        case GDN2_ERR_MISALIGNED: return "GDN2_ERR_MISALIGNED: tensor pointer not 16-byte aligned";
+        case GDN2_ERR_ALIAS: return "GDN2_ERR_ALIAS: an output overlaps an input";
+        case GDN2_ERR_WORKSPACE: return "GDN2_ERR_WORKSPACE: workspace too small";
+        case GDN2_ERR_HIP: return "GDN2_ERR_HIP: the HIP runtime reported an error";
+    }
+    return "GDN2: unknown status";
+}
+
+int32_t gdn2_version(void) { return kVersion; }
+
+size_t gdn2_chunk_fwd_workspace_bytes(int32_t, int32_t, int32_t, int32_t, int32_t, int32_t, gdn2_dtype)
+{
+    return 0;
+}
+
+gdn2_status gdn2_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                           const void* b, const void* w, const float* initial_state,
+                           float* final_state, void* o, const int32_t* cu_seqlens, int32_t B,
+                           int32_t T, int32_t H, int32_t dk, int32_t dv, int32_t num_seqs,
+                           gdn2_dtype dtype, void* workspace, size_t workspace_bytes, void* stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    if (dtype != GDN2_DTYPE_F32 && dtype != GDN2_DTYPE_BF16) return GDN2_ERR_BAD_DTYPE;
+    if (B <= 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return GDN2_ERR_BAD_SHAPE;
+    if (cu_seqlens && (B != 1 || num_seqs <= 0)) return GDN2_ERR_BAD_SHAPE;
+    if (!supported_head(dk) || !supported_head(dv)) return GDN2_ERR_UNSUPPORTED;
+    const int32_t N = cu_seqlens ? num_seqs : B;
+    if (T > 0 && (!q || !k || !v || !alpha || !b || !w || !o)) return GDN2_ERR_NULL_POINTER;
+    const void* ptrs[] = {q, k, v, alpha, b, w, o, initial_state, final_state};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDN2_ERR_MISALIGNED;
+    if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return GDN2_ERR_MISALIGNED;
+
+    const int64_t tokens = int64_t(B) * T * H;
+    const int eb = element_bytes(dtype);
+    const Span sq = span(q, tokens * dk * eb), sk = span(k, tokens * dk * eb), sb = span(b, tokens * dk * eb);
+    const Span sv = span(v, tokens * dv * eb), sw = span(w, tokens * dv * eb), so = span(o, tokens * dv * eb);
+    const Span sa = span(alpha, tokens * dk * 4);
+    const int64_t state_bytes = int64_t(N) * H * dk * dv * 4;
+    const Span si = span(initial_state, initial_state ? state_bytes : 0);
+    const Span sf = span(final_state, final_state ? state_bytes : 0);
+    const Span sc = span(cu_seqlens, cu_seqlens ? int64_t(N + 1) * 4 : 0);
+    for (Span in : {sq, sk, sv, sa, sb, sw, si, sc})
+        if (overlap(so, in)) return GDN2_ERR_ALIAS;
+    for (Span in : {sq, sk, sv, sa, sb, sw, sc, so})
+        if (overlap(sf, in)) return GDN2_ERR_ALIAS;
+    if (overlap(sf, si) && final_state != initial_state) return GDN2_ERR_ALIAS;
+
+    gdn2::ChunkArgs a{q, k, v, alpha, b, w, initial_state, final_state, o, cu_seqlens,
+                      B, T, H, dk, dv, N, device_cus()};
+    const hipError_t e = gdn2::launch_chunk_fwd_simple(a, dtype == GDN2_DTYPE_BF16,
+                                                       static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
+gdn2_status gdn2_recurrent_step(const void* q, const void* k, const void* v, const float* alpha,
+                                const void* b, const void* w, float* state, void* o, int32_t N,
+                                int32_t H, int32_t dk, int32_t dv, gdn2_dtype dtype, void* stream)
+{
+    if (dtype != GDN2_DTYPE_F32 && dtype != GDN2_DTYPE_BF16) return GDN2_ERR_BAD_DTYPE;
+    if (N <= 0 || H <= 0 || dk <= 0 || dv <= 0) return GDN2_ERR_BAD_SHAPE;
+    if (!supported_head(dk) || !supported_head(dv)) return GDN2_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !alpha || !b || !w || !state || !o) return GDN2_ERR_NULL_POINTER;
+    const void* ptrs[] = {q, k, v, alpha, b, w, state, o};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return GDN2_ERR_MISALIGNED;
+    const int64_t heads = int64_t(N) * H;
+    const int eb = element_bytes(dtype);
+    const Span sq = span(q, heads * dk * eb), sk = span(k, heads * dk * eb), sb = span(b, heads * dk * eb);
+    const Span sv = span(v, heads * dv * eb), sw = span(w, heads * dv * eb), so = span(o, heads * dv * eb);
+    const Span sa = span(alpha, heads * dk * 4), ss = span(state, heads * dk * dv * 4);
+    for (Span in : {sq, sk, sv, sa, sb, sw, ss})
+        if (overlap(so, in)) return GDN2_ERR_ALIAS;
+    for (Span in : {sq, sk, sv, sa, sb, sw})
+        if (overlap(ss, in)) return GDN2_ERR_ALIAS;
+
+    gdn2::StepArgs a{q, k, v, alpha, b, w, state, o, N, H, dk, dv};
+    const hipError_t e = gdn2::launch_recurrent_step(a, dtype == GDN2_DTYPE_BF16,
+                                                     static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// Device-side helpers shared by the gfx950 kernels of the GDN-2 library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn2 {
+
+// bf16 values are carried as raw 16-bit patterns.
+using bf16raw = uint16_t;
+
+// Per token and key channel, log2(alpha) is clamped to [kLog2AlphaFloor, 0].
+// The chunk kernels split the decay factor exp2(G_i - G_j) of the intra-chunk
+// products into a row factor and a column factor around a reference token at
+// most 8 tokens away; with the floor the larger factor stays below 2^120, which
+// FP32 and bf16 both represent.
+constexpr float kLog2AlphaFloor = -15.0f;
+
+__device__ __forceinline__ float bf16_to_f32(bf16raw x) { return __uint_as_float(uint32_t(x) << 16); }
+
+// Round to nearest even; NaN stays NaN.
+__device__ __forceinline__ bf16raw f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return bf16raw((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return bf16raw(u >> 16);
+}
+
+__device__ __forceinline__ float load_as_f32(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float load_as_f32(const bf16raw* p, int64_t i) { return bf16_to_f32(p[i]); }
+__device__ __forceinline__ void store_from_f32(float* p, int64_t i, float x) { p[i] = x; }
+__device__ __forceinline__ void store_from_f32(bf16raw* p, int64_t i, float x) { p[i] = f32_to_bf16(x); }
+
+__device__ __forceinline__ float log2_decay(float alpha)
+{
+    return fminf(fmaxf(__log2f(alpha), kLog2AlphaFloor), 0.0f);
+}
+
+// Token range [bos, eos) and batch row of sequence n.  Packed offsets are
+// clamped to [0, T] so a malformed array cannot cause out-of-bounds access.
+__device__ __forceinline__ void sequence_bounds(const int32_t* cu_seqlens, int32_t n, int32_t T,
+                                                int64_t& bos, int64_t& eos, int64_t& brow)
+{
+    if (cu_seqlens) {
+        int64_t a = cu_seqlens[n], b = cu_seqlens[n + 1];
+        a = a < 0 ? 0 : (a > T ? T : a);
+        b = b < a ? a : (b > T ? T : b);
+        bos = a;
+        eos = b;
+        brow = 0;
+    } else {
+        bos = 0;
+        eos = T;
+        brow = n;
+    }
+}
+
+}  // namespace gdn2

@@ -1,0 +1,40 @@
+// Host-visible launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn2 {
+
+struct ChunkArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const void* b;
+    const void* w;
+    const float* initial_state;
+    float* final_state;
+    void* o;
+    const int32_t* cu_seqlens;
+    int32_t B, T, H, dk, dv, N;
+    int32_t cus;  // compute units of the device
+};
+
+struct StepArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const void* b;
+    const void* w;
+    float* state;
+    void* o;
+    int32_t N, H, dk, dv;
+};
+
+// Each returns hipSuccess or the launch error; bf16 selects the input dtype.
+hipError_t launch_recurrent_step(const StepArgs& a, bool bf16, hipStream_t stream);
+hipError_t launch_chunk_fwd_simple(const ChunkArgs& a, bool bf16, hipStream_t stream);
+
+}  // namespace gdn2

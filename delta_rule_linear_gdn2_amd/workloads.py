@@ -15,7 +15,7 @@ decay sits close to one.  The pages train on FineWeb-Edu; no dataset is used
 here: Gaussian / sigmoid tensors of the same shapes stand in for the
 activations.
 
-Recipes (seed = 1000 + workload index):
+Recipes (seed = 1000 + workload index; see ``make`` for how it is split):
   q, k  ~ N(0, 1), then L2-normalised over dk per (token, head)
   v     ~ N(0, 1)
   alpha = sigmoid(N(3, 1)) per key channel           (FP32 always)
@@ -26,6 +26,8 @@ Recipes (seed = 1000 + workload index):
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -88,12 +90,20 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
 
 
 def _sigmoid(x: np.ndarray) -> np.ndarray:
-    return (1.0 / (1.0 + np.exp(-x.astype(np.float64)))).astype(np.float32)
+    """float32 sigmoid, in place on ``x``."""
+    np.negative(x, out=x)
+    np.exp(x, out=x)
+    x += np.float32(1.0)
+    np.reciprocal(x, out=x)
+    return x
 
 
 def _l2norm(x: np.ndarray) -> np.ndarray:
-    n = np.sqrt(np.sum(x.astype(np.float64) ** 2, axis=-1, keepdims=True))
-    return (x / np.maximum(n, 1e-12)).astype(np.float32)
+    """float32 L2 normalisation over the last axis, in place on ``x``."""
+    n = np.sqrt(np.einsum("...c,...c->...", x, x))[..., None]
+    np.maximum(n, np.float32(1e-12), out=n)
+    x /= n
+    return x
 
 
 def _normal(rng, shape, mean=0.0, std=1.0) -> np.ndarray:
@@ -109,16 +119,13 @@ def _normal(rng, shape, mean=0.0, std=1.0) -> np.ndarray:
 # generators
 
 
-def token_tensors(rng, lead: tuple, H: int, dk: int, dv: int, dtype: str,
-                  gate_mode: str = "gdn2", alpha_mean: float = 3.0, alpha_std: float = 1.0) -> dict:
-    """q, k, v, alpha, b, w with leading shape ``lead`` (e.g. (B, T)).
+TOKEN_BLOCK = 2048  # tokens per independently seeded generation block
 
-    Returned arrays are float32 holding values exactly representable in
-    ``dtype``.  ``gate_mode``:
-      "gdn2" - channel-wise alpha, b, w (full method)
-      "kda"  - b = w = beta broadcast, beta = sigmoid(N(0,1)) per (token, head)
-      "gdn"  - as "kda" and a scalar alpha per (token, head) broadcast over dk
-    """
+
+def _token_block(seed_seq, ntok: int, H: int, dk: int, dv: int, dtype: str, gate_mode: str,
+                 alpha_mean: float, alpha_std: float) -> dict:
+    rng = np.random.default_rng(seed_seq)
+    lead = (ntok,)
     q = _l2norm(_normal(rng, lead + (H, dk)))
     k = _l2norm(_normal(rng, lead + (H, dk)))
     v = _normal(rng, lead + (H, dv))
@@ -130,13 +137,13 @@ def token_tensors(rng, lead: tuple, H: int, dk: int, dv: int, dtype: str,
         if gate_mode == "kda":
             alpha = _sigmoid(_normal(rng, lead + (H, dk), alpha_mean, alpha_std))
         else:
-            a1 = _sigmoid(_normal(rng, lead + (H, 1), alpha_mean, alpha_std))
-            alpha = np.ascontiguousarray(np.broadcast_to(a1, lead + (H, dk)))
+            alpha = np.broadcast_to(_sigmoid(_normal(rng, lead + (H, 1), alpha_mean, alpha_std)),
+                                    lead + (H, dk))
         beta = _sigmoid(_normal(rng, lead + (H, 1)))
         if dtype == "bf16":
             beta = round_bf16(beta)
-        b = np.ascontiguousarray(np.broadcast_to(beta, lead + (H, dk)))
-        w = np.ascontiguousarray(np.broadcast_to(beta, lead + (H, dv)))
+        b = np.broadcast_to(beta, lead + (H, dk))
+        w = np.broadcast_to(beta, lead + (H, dv))
     else:
         raise ValueError(gate_mode)
     out = dict(q=q, k=k, v=v, alpha=alpha, b=b, w=w)
@@ -144,6 +151,42 @@ def token_tensors(rng, lead: tuple, H: int, dk: int, dv: int, dtype: str,
         for name in ("q", "k", "v", "b", "w"):
             out[name] = round_bf16(out[name])
     return out
+
+
+def token_tensors(seed_seq, lead: tuple, H: int, dk: int, dv: int, dtype: str,
+                  gate_mode: str = "gdn2", alpha_mean: float = 3.0, alpha_std: float = 1.0,
+                  workers: int | None = None) -> dict:
+    """q, k, v, alpha, b, w with leading shape ``lead`` (e.g. (B, T)).
+
+    Returned arrays are float32 holding values exactly representable in
+    ``dtype``.  The flattened token axis is cut into blocks of TOKEN_BLOCK
+    tokens, each drawn from its own child of ``seed_seq`` (so the values do not
+    depend on the number of worker threads).  ``gate_mode``:
+      "gdn2" - channel-wise alpha, b, w (full method)
+      "kda"  - b = w = beta broadcast, beta = sigmoid(N(0,1)) per (token, head)
+      "gdn"  - as "kda" and a scalar alpha per (token, head) broadcast over dk
+    """
+    ntok = int(np.prod(lead)) if lead else 1
+    widths = dict(q=dk, k=dk, v=dv, alpha=dk, b=dk, w=dv)
+    out = {n: np.empty((ntok, H, d), dtype=np.float32) for n, d in widths.items()}
+    nblocks = max(1, -(-ntok // TOKEN_BLOCK))
+    children = seed_seq.spawn(nblocks)
+
+    def fill(i):
+        lo = i * TOKEN_BLOCK
+        hi = min(ntok, lo + TOKEN_BLOCK)
+        blk = _token_block(children[i], hi - lo, H, dk, dv, dtype, gate_mode, alpha_mean, alpha_std)
+        for n in widths:
+            out[n][lo:hi] = blk[n]
+
+    workers = workers or min(16, os.cpu_count() or 1)
+    if nblocks == 1 or workers == 1:
+        for i in range(nblocks):
+            fill(i)
+    else:
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(fill, range(nblocks)))
+    return {n: a.reshape(tuple(lead) + (H, widths[n])) for n, a in out.items()}
 
 
 def initial_state(rng, N: int, H: int, dk: int, dv: int, std: float = 0.1) -> np.ndarray:
@@ -166,29 +209,33 @@ def make(name: str, gate_mode: str = "gdn2", seed: int | None = None, **override
     Returns a dict with the workload, the tensors (float32, values exact in the
     workload dtype), ``initial_state`` (or None) and, for varlen, ``cu_seqlens``.
     ``overrides`` replace shape fields (e.g. T=300 for a reduced-size case).
+    Seeding: SeedSequence(seed) spawns three children, for the varlen lengths,
+    the token tensors and the initial state, in that order.
     """
     wl = WORKLOADS[name]
     if overrides:
         wl = Workload(**{**wl.__dict__, **overrides})
-    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    ss_len, ss_tok, ss_state = np.random.SeedSequence(wl.seed if seed is None else seed).spawn(3)
     out: dict = {"workload": wl, "gate_mode": gate_mode, "generator": GEN_NAME,
                  "numpy": np.__version__}
+    state_rng = np.random.default_rng(ss_state)
     if wl.kind == "chunk":
-        out.update(token_tensors(rng, (wl.B, wl.T), wl.H, wl.dk, wl.dv, wl.dtype, gate_mode))
-        out["initial_state"] = initial_state(rng, wl.B, wl.H, wl.dk, wl.dv) if wl.init_state else None
+        out.update(token_tensors(ss_tok, (wl.B, wl.T), wl.H, wl.dk, wl.dv, wl.dtype, gate_mode))
+        out["initial_state"] = (initial_state(state_rng, wl.B, wl.H, wl.dk, wl.dv)
+                                if wl.init_state else None)
         out["cu_seqlens"] = None
     elif wl.kind == "varlen":
-        lengths = varlen_lengths(rng, wl.num_seqs, wl.min_len, wl.max_len)
+        lengths = varlen_lengths(np.random.default_rng(ss_len), wl.num_seqs, wl.min_len, wl.max_len)
         cu = cu_from_lengths(lengths)
         total = int(cu[-1])
-        out.update(token_tensors(rng, (1, total), wl.H, wl.dk, wl.dv, wl.dtype, gate_mode))
-        out["initial_state"] = (initial_state(rng, wl.num_seqs, wl.H, wl.dk, wl.dv)
+        out.update(token_tensors(ss_tok, (1, total), wl.H, wl.dk, wl.dv, wl.dtype, gate_mode))
+        out["initial_state"] = (initial_state(state_rng, wl.num_seqs, wl.H, wl.dk, wl.dv)
                                 if wl.init_state else None)
         out["cu_seqlens"] = cu
     elif wl.kind == "decode":
         # `steps` pre-generated token slices [steps, N, H, d]; state [N, H, dk, dv]
-        out.update(token_tensors(rng, (wl.steps, wl.B), wl.H, wl.dk, wl.dv, wl.dtype, gate_mode))
-        out["initial_state"] = initial_state(rng, wl.B, wl.H, wl.dk, wl.dv)
+        out.update(token_tensors(ss_tok, (wl.steps, wl.B), wl.H, wl.dk, wl.dv, wl.dtype, gate_mode))
+        out["initial_state"] = initial_state(state_rng, wl.B, wl.H, wl.dk, wl.dv)
         out["cu_seqlens"] = None
     else:
         raise ValueError(wl.kind)

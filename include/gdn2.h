@@ -1,0 +1,131 @@
+/*
+ * gdn2.h -- C ABI of the Gated DeltaNet-2 forward-pass library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation.  Per head, per token t, with a state S in R^{dk x dv} whose
+ * rows are key channels ("Gated DeltaNet-2: Decoupling Erase and Write in
+ * Linear Attention" analysis at iplexlaw.co.kr, section "Independent
+ * decisions on two axes"):
+ *     e_t = b_t (.) k_t           z_t = w_t (.) v_t
+ *     Sbar = Diag(alpha_t) S_{t-1}          (decay on key channels)
+ *     r_t = Sbar^T e_t                      (old read through the erase key)
+ *     S_t = Sbar + k_t (z_t - r_t)^T        (delta update)
+ *     o_t = S_t^T q_t                       (query reads the UPDATED state)
+ * The same page, section "Token processing and parallel training", gives the
+ * chunkwise WY form with 64-token chunks used for long inputs
+ * (gdn2_chunk_fwd); the "DeltaNet" entity trail at mindpattern.ai (finding
+ * "You Could Have Come Up With Kimi Delta Attention") states that the fused
+ * recurrent decode form (gdn2_recurrent_step) computes identical mathematics.
+ *
+ * Conventions shared by every entry point.
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    allocates no memory, keeps no state between calls and is thread-safe.
+ *  - Tensors are contiguous, row-major, with the innermost index last.
+ *  - dtype (gdn2_dtype) applies to q, k, v, b, w and o.  alpha and the
+ *    recurrent state are always FP32.  bf16 outputs are rounded to nearest
+ *    even.  Arithmetic is FP32 (decay, cumulative decay, solve and state);
+ *    bf16 inputs feed bf16 matrix-core products with FP32 accumulation.
+ *  - Inputs are gate VALUES, not logits: 0 <= alpha <= 1; b, w are used as
+ *    given (no clamp, so an erase gate in [0, 2] works).  There is no query
+ *    scale: callers pre-scale q.  Per token and key channel, log2(alpha) is
+ *    clamped to [-15, 0]: alpha below 2^-15 acts as 2^-15 and alpha above 1
+ *    acts as 1.
+ *  - Pointers to q, k, v, b, w, o, alpha and states must be 16-byte aligned.
+ *  - Calls enqueue work on `stream` (a hipStream_t; NULL = the null stream)
+ *    and return without synchronising.  Argument errors are reported
+ *    synchronously, before anything is enqueued; device faults surface at the
+ *    caller's next synchronisation.  Results are bitwise reproducible from
+ *    run to run (no atomics, fixed reduction order).
+ *  - Supported head sizes: dk in {32, 64, 128}, dv in {32, 64, 128}.
+ */
+#ifndef GDN2_H
+#define GDN2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdn2_status {
+    GDN2_OK = 0,
+    GDN2_ERR_NULL_POINTER = 1, /* a required pointer is NULL                         */
+    GDN2_ERR_BAD_SHAPE = 2,    /* a size is <= 0 (or < 0 for T), or inconsistent     */
+    GDN2_ERR_UNSUPPORTED = 3,  /* head size not instantiated                         */
+    GDN2_ERR_BAD_DTYPE = 4,    /* dtype is not a gdn2_dtype value                    */
+    GDN2_ERR_MISALIGNED = 5,   /* a tensor pointer is not 16-byte aligned            */
+    GDN2_ERR_ALIAS = 6,        /* an output overlaps an input it may not overlap     */
+    GDN2_ERR_WORKSPACE = 7,    /* workspace smaller than the query function's answer */
+    GDN2_ERR_HIP = 8           /* the HIP runtime reported an error at launch        */
+} gdn2_status;
+
+typedef enum gdn2_dtype {
+    GDN2_DTYPE_F32 = 0,
+    GDN2_DTYPE_BF16 = 1
+} gdn2_dtype;
+
+/*
+ * Chunkwise forward over whole sequences ("Token processing and parallel
+ * training": 64-token chunks, cumulative channel-wise decay in FP32 absorbed
+ * into asymmetric erase factors, a per-chunk lower-triangular solve and dense
+ * products; the state is carried between chunks in FP32).
+ *
+ *   q, k, b : [B, T, H, dk]  dtype          v, w, o : [B, T, H, dv]  dtype
+ *   alpha   : [B, T, H, dk]  FP32
+ *   initial_state : [N, H, dk, dv] FP32, or NULL for zeros.
+ *   final_state   : [N, H, dk, dv] FP32, or NULL if not wanted.  May be the
+ *                   same pointer as initial_state (updated in place); any
+ *                   other overlap with an input is GDN2_ERR_ALIAS.
+ *   cu_seqlens    : NULL, or DEVICE int32 [num_seqs + 1] with cu_seqlens[0] = 0,
+ *                   non-decreasing, cu_seqlens[num_seqs] = T.  Then B must be
+ *                   1, the batch row holds num_seqs packed sequences, sequence
+ *                   n owns tokens [cu_seqlens[n], cu_seqlens[n+1]) and state
+ *                   row n (N = num_seqs).  Without it N = B and num_seqs is
+ *                   ignored.  Offsets are clamped to [0, T] on the device, so
+ *                   a malformed array cannot make the kernel read or write
+ *                   outside the tensors; it only gives meaningless results.
+ *   T may be 0 (then only final_state = initial_state is written).
+ *   workspace / workspace_bytes: device scratch of at least
+ *                   gdn2_chunk_fwd_workspace_bytes(...) bytes (may be NULL when
+ *                   that is 0).
+ * o must not overlap any input.
+ */
+gdn2_status gdn2_chunk_fwd(const void* q, const void* k, const void* v,
+                           const float* alpha, const void* b, const void* w,
+                           const float* initial_state, float* final_state, void* o,
+                           const int32_t* cu_seqlens,
+                           int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                           int32_t num_seqs, gdn2_dtype dtype,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace needed by gdn2_chunk_fwd for these sizes (currently always 0). */
+size_t gdn2_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                                      int32_t num_seqs, gdn2_dtype dtype);
+
+/*
+ * One fused recurrent step (decode) for N independent sequences: each
+ * (sequence, head) state is read once and written once, in place.
+ *
+ *   q, k, b : [N, H, dk] dtype     v, w, o : [N, H, dv] dtype
+ *   alpha   : [N, H, dk] FP32
+ *   state   : [N, H, dk, dv] FP32, read and overwritten with the new state.
+ * o must not overlap any input or the state.
+ */
+gdn2_status gdn2_recurrent_step(const void* q, const void* k, const void* v,
+                                const float* alpha, const void* b, const void* w,
+                                float* state, void* o,
+                                int32_t N, int32_t H, int32_t dk, int32_t dv,
+                                gdn2_dtype dtype, void* stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* gdn2_status_string(gdn2_status status);
+
+/* Library version as MAJOR * 10000 + MINOR * 100 + PATCH. */
+int32_t gdn2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN2_H */

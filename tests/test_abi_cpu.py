@@ -1,0 +1,121 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every
+function include/gdn2.h declares, and rejects bad arguments synchronously,
+before any HIP call (so no device is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from delta_rule_linear_gdn2_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn2.h")
+
+OK, NULLP, SHAPE, UNSUP, DTYPE, MISAL, ALIAS, WS, HIP = range(9)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn2_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail(f"{binding.LIB_PATH} is not built (run __graft_entry__.build())")
+    return binding.load()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) == set(binding.EXPORTS)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in range(9):
+        s = binding.status_string(code)
+        assert s.startswith(binding.STATUS_NAMES[code])
+    assert "unknown" in binding.status_string(99)
+    assert lib.gdn2_version() == 10000
+
+
+def test_workspace_query(lib):
+    assert binding.gdn2_chunk_fwd_workspace_bytes(8, 4096, 16, 128, 128, 8, 1) == 0
+
+
+# Fake, well-separated, 256-byte aligned device addresses: validation must
+# reject every case below before touching them.
+BASE = 1 << 40
+GAP = 1 << 32
+
+
+def fake(i, off=0):
+    return ctypes.c_void_p(BASE + i * GAP + off)
+
+
+def chunk_call(lib, **kw):
+    args = dict(q=fake(0), k=fake(1), v=fake(2), alpha=fake(3), b=fake(4), w=fake(5),
+                s0=fake(6), sf=fake(7), o=fake(8), cu=None,
+                B=2, T=64, H=4, dk=64, dv=64, num_seqs=0, dtype=1, ws=None, ws_bytes=0)
+    args.update(kw)
+    a = args
+    return lib.gdn2_chunk_fwd(a["q"], a["k"], a["v"], a["alpha"], a["b"], a["w"], a["s0"], a["sf"],
+                              a["o"], a["cu"], a["B"], a["T"], a["H"], a["dk"], a["dv"],
+                              a["num_seqs"], a["dtype"], a["ws"], a["ws_bytes"], None)
+
+
+def step_call(lib, **kw):
+    args = dict(q=fake(0), k=fake(1), v=fake(2), alpha=fake(3), b=fake(4), w=fake(5),
+                state=fake(6), o=fake(8), N=4, H=2, dk=128, dv=128, dtype=1)
+    args.update(kw)
+    a = args
+    return lib.gdn2_recurrent_step(a["q"], a["k"], a["v"], a["alpha"], a["b"], a["w"], a["state"],
+                                   a["o"], a["N"], a["H"], a["dk"], a["dv"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,expected", [
+    (dict(dtype=2), DTYPE),
+    (dict(dtype=-1), DTYPE),
+    (dict(B=0), SHAPE),
+    (dict(T=-1), SHAPE),
+    (dict(H=0), SHAPE),
+    (dict(dk=0), SHAPE),
+    (dict(cu=fake(9), B=2, num_seqs=3), SHAPE),
+    (dict(cu=fake(9), B=1, num_seqs=0), SHAPE),
+    (dict(dk=48), UNSUP),
+    (dict(dv=256), UNSUP),
+    (dict(dk=16), UNSUP),
+    (dict(q=None), NULLP),
+    (dict(alpha=None), NULLP),
+    (dict(o=None), NULLP),
+    (dict(q=fake(0, 8)), MISAL),
+    (dict(alpha=fake(3, 4)), MISAL),
+    (dict(sf=fake(7, 2)), MISAL),
+    (dict(cu=fake(9, 2), B=1, num_seqs=2), MISAL),
+    (dict(o=fake(0, 256)), ALIAS),                    # o inside q
+    (dict(o=fake(6, 16)), ALIAS),                     # o inside the initial state
+    (dict(sf=fake(3, 64)), ALIAS),                    # final state inside alpha
+    (dict(sf=fake(8)), ALIAS),                        # final state == o
+    (dict(sf=fake(6, 1024)), ALIAS),                  # partial overlap with initial state
+])
+def test_chunk_fwd_rejects(lib, kw, expected):
+    assert chunk_call(lib, **kw) == expected
+
+
+@pytest.mark.parametrize("kw,expected", [
+    (dict(dtype=5), DTYPE),
+    (dict(N=0), SHAPE),
+    (dict(H=-2), SHAPE),
+    (dict(dv=96), UNSUP),
+    (dict(state=None), NULLP),
+    (dict(w=None), NULLP),
+    (dict(v=fake(2, 4)), MISAL),
+    (dict(o=fake(6, 512)), ALIAS),                    # o inside the state
+    (dict(state=fake(1, 64)), ALIAS),                 # state overlaps k
+])
+def test_recurrent_step_rejects(lib, kw, expected):
+    assert step_call(lib, **kw) == expected
