@@ -186,7 +186,7 @@ def main():
     dec = None if args.no_decode else bench_decode(args)
     cpu = None
     if not args.no_cpu and ch["wl"].kind == "chunk":
-        cpu = cpu_baseline(ch["x"], ch["wl"], chains_rows=min(4, ch["wl"].B))
+        cpu = cpu_baseline(ch["x"], ch["wl"], chains_rows=ch["wl"].B)
         log(f"cpu oracle: {cpu['value']:.0f} tokens/s on {cpu['cores']} threads")
     B, T, H, dk, dv, N = ch["dims"]
     wl = ch["wl"]
