@@ -161,6 +161,28 @@ def cpu_baseline(x, wl, chains_rows=4):
                       f"{wall:.1f} s wall"}
 
 
+def run_only(args):
+    """One part alone (for rocprofv3 runs); prints one JSON line."""
+    import torch
+
+    if args.only == "chunk":
+        ch = bench_chunk(args)
+        res = {"part": "chunk", "workload": ch["wl"].name, "avg_launch_ms": ch["kern_ms"],
+               "algorithmic_bytes": ch["bytes"], "launches": args.steps + args.warmup}
+    elif args.only == "decode":
+        dec = bench_decode(args)
+        res = {"part": "decode", "us_per_step": dec["step_ms"] * 1e3, "algorithmic_bytes": dec["bytes"]}
+    else:
+        nbytes = 1 << 30
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        per, total, _ = time_events(lambda: dst.copy_(src), args.warmup, args.steps)
+        ms = float(np.mean(per))
+        res = {"part": "copy", "bytes_read": nbytes, "bytes_written": nbytes, "avg_launch_ms": ms,
+               "GBps": 2 * nbytes / (ms / 1e3) / 1e9, "launches": args.steps + args.warmup}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -169,6 +191,9 @@ def main():
     ap.add_argument("--workload", default="batched_bf16",
                     choices=["batched_bf16", "layer_bf16", "varlen32_bf16", "tiny_f32"])
     ap.add_argument("--no-decode", action="store_true", help="skip the decode half")
+    ap.add_argument("--only", choices=["chunk", "decode", "copy"], default=None,
+                    help="profiling aid: run one part only and print its timing line "
+                         "(copy = a plain 1 GiB device copy, the reference for HBM byte counters)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -182,6 +207,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     binding.load()
+    if args.only:
+        return run_only(args)
     ch = bench_chunk(args)
     dec = None if args.no_decode else bench_decode(args)
     cpu = None

@@ -22,6 +22,7 @@ SOURCES = [
     "gdn2_api.cpp",
     "recurrent_step.hip",
     "chunk_fwd_simple.hip",
+    "chunk_fwd_mfma.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

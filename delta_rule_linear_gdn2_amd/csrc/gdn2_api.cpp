@@ -112,8 +112,10 @@ gdn2_status gdn2_chunk_fwd(const void* q, const void* k, const void* v, const fl
 
     gdn2::ChunkArgs a{q, k, v, alpha, b, w, initial_state, final_state, o, cu_seqlens,
                       B, T, H, dk, dv, N, device_cus()};
-    const hipError_t e = gdn2::launch_chunk_fwd_simple(a, dtype == GDN2_DTYPE_BF16,
-                                                       static_cast<hipStream_t>(stream));
+    const bool bf16 = dtype == GDN2_DTYPE_BF16;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const hipError_t e = gdn2::chunk_fwd_mfma_supported(a, bf16) ? gdn2::launch_chunk_fwd_mfma(a, st)
+                                                                 : gdn2::launch_chunk_fwd_simple(a, bf16, st);
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 

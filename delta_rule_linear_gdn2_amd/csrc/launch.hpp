@@ -37,4 +37,8 @@ struct StepArgs {
 hipError_t launch_recurrent_step(const StepArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_chunk_fwd_simple(const ChunkArgs& a, bool bf16, hipStream_t stream);
 
+// Matrix-core chunk kernel: bf16 inputs, dk = 128, dv a multiple of 64.
+bool chunk_fwd_mfma_supported(const ChunkArgs& a, bool bf16);
+hipError_t launch_chunk_fwd_mfma(const ChunkArgs& a, hipStream_t stream);
+
 }  // namespace gdn2

@@ -83,14 +83,15 @@ def test_varlen_sampled(mode):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_varlen_edges(dtype):
+@pytest.mark.parametrize("d", [64, 128])
+def test_varlen_edges(dtype, d):
     """Zero-length, one-token, chunk-boundary and ragged sequences packed together."""
     lens = [0, 1, 63, 64, 65, 130, 0, 7, 200]
     cu = W.cu_from_lengths(lens)
-    x = W.make("batched_bf16", seed=92, B=1, T=int(cu[-1]), H=2, dk=64, dv=64, dtype=dtype)
+    x = W.make("batched_bf16", seed=92, B=1, T=int(cu[-1]), H=2, dk=d, dv=d, dtype=dtype)
     x["cu_seqlens"] = cu
-    x["initial_state"] = 0.1 * np.random.default_rng(93).standard_normal((len(lens), 2, 64, 64)).astype(np.float32)
-    o, sf = _full_parity(x, dtype, f"varlen edges {dtype}")
+    x["initial_state"] = 0.1 * np.random.default_rng(93).standard_normal((len(lens), 2, d, d)).astype(np.float32)
+    o, sf = _full_parity(x, dtype, f"varlen edges {dtype} d={d}")
     # zero-length sequences pass their state through unchanged
     np.testing.assert_array_equal(G.f64(sf)[0], x["initial_state"][0])
     np.testing.assert_array_equal(G.f64(sf)[6], x["initial_state"][6])
