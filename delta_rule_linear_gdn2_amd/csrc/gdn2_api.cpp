@@ -7,7 +7,7 @@
 #include <atomic>
 #include <cstdint>
 
-#include "../../include/gdn2.h"
+#include "gdn2.h"
 #include "launch.hpp"
 
 namespace {
