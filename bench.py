@@ -27,6 +27,7 @@ if ROOT not in sys.path:
 
 METRIC = "GDN-2 fwd tokens/s (H16,d128,T4K,B8) + decode state GB/s; % of roofline"
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak
 NAMES = ("q", "k", "v", "alpha", "b", "w")
 
 
@@ -42,10 +43,43 @@ def chunk_bytes(B, T, H, dk, dv, N, eb=2):
     return tok * (3 * dk * eb + 2 * dv * eb + dk * 4 + dv * eb) + 2 * N * H * dk * dv * 4
 
 
+def chunk_flops(lengths, H, dk, dv, C=64):
+    """Triangle-aware FLOPs of the chunkwise form, summed over chunks of every
+    sequence: A (strict lower) and P (lower incl. diagonal) over dk channels,
+    T = (I + A)^-1 (~L^3/3), T [Et | Z], W S, Qt S, P U and Kb^T U."""
+    total = 0
+    for n in lengths:
+        full, tail = divmod(int(n), C)
+        for L, cnt in ((C, full), (tail, 1 if tail else 0)):
+            per = (dk * L * (L - 1) + dk * L * (L + 1) + L ** 3 / 3 + (dk + dv) * L * (L + 1)
+                   + 3 * 2 * L * dk * dv + dv * L * (L + 1))
+            total += cnt * per
+    return total * H
+
+
 def step_bytes(N, H, dk, dv, eb=2):
     """Algorithmic HBM bytes of one decode step: the FP32 state read and
     written once, the token vectors read, o written."""
     return N * H * (2 * dk * dv * 4 + 3 * dk * eb + 2 * dv * eb + dk * 4 + dv * eb)
+
+
+def pmc_traffic(part):
+    """HBM bytes per launch measured by rocprofv3 FETCH_SIZE + WRITE_SIZE
+    (scaled by the copy-kernel factors) as recorded in profiles/pmc_traffic.json,
+    or None when the kernel's sources have changed since the counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)["kernels"][part]
+    except (OSError, KeyError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for name in rec["sources"]:
+        with open(os.path.join(ROOT, "delta_rule_linear_gdn2_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return rec["traffic_bytes"] if h.hexdigest() == rec["source_sha256"] else None
 
 
 def to_dev(x, dtype):
@@ -218,6 +252,12 @@ def main():
     B, T, H, dk, dv, N = ch["dims"]
     wl = ch["wl"]
     achieved = ch["bytes"] / (ch["kern_ms"] / 1e3) / 1e9
+    if N == B and ch["x"]["cu_seqlens"] is None:
+        lengths = [T] * B
+    else:
+        lengths = np.diff(ch["x"]["cu_seqlens"]).tolist()
+    flops = chunk_flops(lengths, H, dk, dv)
+    mfma_tflops = flops / (ch["kern_ms"] / 1e3) / 1e12
     out = {
         "metric": METRIC,
         "value": ch["tokens"] / (ch["ms"] / 1e3),
@@ -235,9 +275,14 @@ def main():
                                f"64-token chunks, FP32 alpha/state",
                    "B": B, "T": T, "H": H, "dk": dk, "dv": dv, "num_seqs": N},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": pmc_traffic("chunk") if wl.name == "batched_bf16" else None,
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE)",
                      "kernel": "gdn2 chunk forward", "algorithmic_bytes": ch["bytes"],
-                     "avg_launch_ms": ch["kern_ms"]},
+                     "avg_launch_ms": ch["kern_ms"],
+                     "mfma": {"achieved": mfma_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                              "unit": "TFLOP/s", "frac": mfma_tflops / MFMA_BF16_PEAK_TFLOPS,
+                              "flops": flops, "counting": "triangle-aware algorithmic FLOPs"}},
         "cpu_baseline": cpu,
     }
     if dec is not None:
@@ -245,7 +290,9 @@ def main():
             "workload": "decode_b256: N=256 H=16 dk=dv=128, bf16 tokens, FP32 state, 64 in-place steps",
             "state_GBps": dec["state_gbps"], "us_per_step": dec["step_ms"] * 1e3,
             "roofline": {"bound": "hbm", "achieved": dec["achieved"], "peak": HBM_PEAK_GBPS,
-                         "unit": "GB/s", "frac": dec["achieved"] / HBM_PEAK_GBPS, "traffic": None,
+                         "unit": "GB/s", "frac": dec["achieved"] / HBM_PEAK_GBPS,
+                         "traffic": pmc_traffic("decode"),
+                         "traffic_unit": "HBM bytes per step (rocprofv3 FETCH_SIZE+WRITE_SIZE)",
                          "algorithmic_bytes": dec["bytes"]},
         }
     print(json.dumps(out), flush=True)
