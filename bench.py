@@ -220,8 +220,8 @@ def run_only(args):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="batched_bf16",
                     choices=["batched_bf16", "layer_bf16", "varlen32_bf16", "tiny_f32"])
     ap.add_argument("--no-decode", action="store_true", help="skip the decode half")

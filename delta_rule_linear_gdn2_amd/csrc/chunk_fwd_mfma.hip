@@ -1,50 +1,52 @@
-// Chunkwise forward on gfx950 matrix cores (bf16 inputs, dk = 128).
+// Chunkwise forward on gfx950 matrix cores (bf16 inputs, dk = 128, value
+// tiles of 64 columns).
 //
 // The chunkwise WY form (Gated DeltaNet-2 analysis, iplexlaw.co.kr, "Token
-// processing and parallel training"): per 64-token chunk the cumulative
-// channel-wise decay is absorbed into asymmetric erase factors, leaving a
-// lower-triangular solve and dense products; FP32 is kept for the decay, the
-// solve and the carried state.  With incoming state S, per key channel
-// G_i = sum_{m<=i} log2 alpha_m and e = b k, z = w v:
-//     A_ij = sum_c e_ic k_jc 2^(G_ic - G_jc)  (j < i)     P_ij = same with q, j <= i
-//     U    = (I + A)^-1 (Z - Et S)                          Et_i = e_i 2^G_i
-//     O    = Qt S + P U                                      Qt_i = q_i 2^G_i
-//     S   <- Diag(2^G_last) S + Kb^T U                       Kb_j = k_j 2^(G_last - G_j)
+// processing and parallel training"): per chunk the cumulative channel-wise
+// decay is absorbed into asymmetric factors, leaving a lower-triangular solve
+// and dense products; FP32 is kept for the decay, the solve and the carried
+// state.  With incoming state S, per key channel the running decay
+// c_i = prod_{m<=i} alpha_m inside the chunk, e = b k and z = w v:
+//     Et_i = e_i c_i     Qt_i = q_i c_i     Kt_j = k_j / c_j     Kb_j = Kt_j c_last
+//     A = strict_lower(Et Kt^T)     P = lower(Qt Kt^T)
+//     U = (I + A)^-1 (Z - Et S)     O = Qt S + P U     S <- Diag(c_last) S + Kb^T U
 //
-// Decay factors.  The chunk is cut into four 16-token blocks.  For a row
-// token i in block I and a column token j <= i, 2^(G_i - G_j) is split around
-// the block's reference token m_I (its 8th token):
-//     2^(G_i - G_j) = [2^(G_i - m_I)] * [2^(m_I - G_j)]
-// Both factors are at most 2^(8 * 15) because log2 alpha >= -15 and i, j lie
-// within 8 tokens of m_I on the side where a factor exceeds one; for j in an
-// earlier block the column factor is <= 1.  All factors are FP32 products of
-// alpha: forward and backward running products inside each 8-token half
-// block, and per-half products combined across the chunk.  Underflow of a
-// factor that is <= 1 only drops terms below 2^-126 of their neighbours.
+// Range.  alpha is clamped to [2^-15, 1].  A chunk is cut short when some
+// channel decays below 2^-120 across it: it then covers 32, 16 or 8 tokens,
+// the longest prefix whose decay stays at or above 2^-120 in every channel (8
+// tokens always do).  Hence every factor c_i and 1 / c_j lies in
+// [2^-120, 2^120], which FP32 and bf16 represent, and all factors are plain
+// products of alpha (one reciprocal per element).  All waves take the decision
+// from the same exchanged products, so it is uniform across the workgroup.
 //
-// Matrix products (v_mfma_f32_16x16x32_bf16, FP32 accumulate):
-//     A, P blocks (K = 128 channels), Et S, (Qt S)^T, the off-diagonal part of
-//     the blocked solve, (P U)^T and Kb^T U (K = tokens);
-// in FP32 (v_mfma_f32_16x16x4_f32) the diagonal-block solve U_I = T_II R_I,
-// with T_II = (I + A_II)^-1 formed by FP32 forward substitution.
+// Pipeline.  One workgroup of eight wavefronts (two per SIMD) per (sequence,
+// head, 64-column value tile).  Waves 0..3 (value waves) own 16 value columns
+// each and keep that 128 x 16 slice of the FP32 state in MFMA accumulators for
+// the whole sequence; waves 4..7 (key waves) prepare the chunks.  Each period
+// of three barriers B0, B1, B2 advances two chunks: the value waves form
+// X = Z - Et S and (Qt S)^T of chunk c before B1, and its blocked solve,
+// output rows and state update between B1 and B2; meanwhile the key waves
+// compute the decay products of chunk c + 1 before B1 and its operand tiles
+// between B1 and B2.  After B2, wave 3 forms the diagonal blocks of A of
+// chunk c + 1 and their inverses, waves 0..2 its other A and P blocks, and the
+// key waves issue the loads of chunk c + 2.  Tiles the value
+// waves read between B1 and B2 are double-buffered; Et, Qt, Kt, the products
+// and z are consumed before their next write and stay single.  Each wave loads
+// its next inputs with 16-byte loads as soon as it has consumed the current
+// ones.  Workgroups of one chain share an XCD, so the second value tile
+// re-reads the key-side inputs from L2.
 //
-// Work split.  One workgroup of eight wavefronts (two per SIMD) per (sequence,
-// head, value tile).  VW of them are value wavefronts: wavefront w < VW owns
-// value columns 16w..16w+15 and keeps that 128 x 16 slice of the FP32 state in
-// its accumulators for the whole sequence.  All eight share the key-side work
-// of a chunk (decay factors, operand tiles, A, P, T) through LDS.  Workgroups
-// of the same chain are placed on the same XCD so that every tile after the
-// first re-reads the key-side inputs from L2.
-//
-// Operand layouts (16x16x32 bf16): lane l = 16 g + r provides row/column r and
-// a group of eight K indices chosen by g; the accumulator holds rows 4g..4g+3
-// of column r.  A and B only need to agree on the K order, so for a K-step over
-// 32 channels or tokens group g takes {4g..4g+3} U {16+4g..16+4g+3}: exactly
-// the rows a lane already holds in two adjacent accumulator blocks.  An
-// accumulator tile therefore serves directly as a B operand, and also as an A
-// operand of the transposed product (X Y)^T = Y^T X^T; transposed products
-// give each lane four consecutive columns of one row, which makes the stores
-// of A, P and O contiguous.
+// Matrix products (v_mfma_f32_16x16x32_bf16, FP32 accumulate): lane
+// l = 16 g + r provides row/column r and a group of eight K indices chosen by
+// g; the accumulator holds rows 4g..4g+3 of column r.  A and B only need to
+// agree on the K order, so for a K-step over 32 channels or tokens group g may
+// take {4g..4g+3} U {16+4g..16+4g+3}: exactly the rows a lane holds in two
+// adjacent accumulator blocks.  An accumulator tile therefore serves directly
+// as a B operand, and as an A operand of the transposed product
+// (X Y)^T = Y^T X^T; transposed products leave four consecutive columns of one
+// row in each lane, so the stores of A, P and O are contiguous.  The diagonal
+// blocks of the solve apply T_II = (I + A_II)^-1 in FP32
+// (v_mfma_f32_16x16x4_f32).
 #include "gdn2_device.hpp"
 #include "launch.hpp"
 
@@ -56,43 +58,75 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kDK = 128;         // key head size
-constexpr int kC = 64;           // chunk
-constexpr int kWaves = 8;        // wavefronts per workgroup
+constexpr int kDK = 128;          // key head size
+constexpr int kC = 64;            // chunk
+constexpr int kDVT = 64;          // value columns per workgroup
+constexpr int kWaves = 8;         // wavefronts per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kTWave = kWaves - 1;  // wavefront that forms T
-constexpr float kAlphaMin = 3.0517578125e-05f;  // 2^-15
+constexpr int kValueWaves = 4;    // waves 0..3: 16 value columns each
+constexpr int kTWave = 3;         // diagonal blocks of A and their inverses (a value wave)
+constexpr float kAlphaMin = 0x1p-15f;
+constexpr float kRangeMin = 0x1p-120f;
 
 // ---- LDS map (bytes) -------------------------------------------------------
-// Region 1, prep -> A/P:  Eh, Qh, Kh [64][128] bf16, Ko [6][16][128] bf16
-// Region 1, A/P -> end:   Aneg, P [64][64] bf16, AdT, T [4][16][16] f32
-// Region 2, prep -> end:  Et, Qt [64][128] bf16, KbT [128][64] bf16
-// then Zs [DVT][68] f32 (z = w v, column major), per-half alpha products, gamma.
-constexpr int kOffEh = 0, kOffQh = 16384, kOffKh = 32768, kOffKo = 49152;  // .. 73728
-constexpr int kOffAneg = 0, kOffP = 8192, kOffAdT = 16384, kOffT = 20480;  // .. 24576
-constexpr int kOffEt = 73728, kOffQt = 90112, kOffKbT = 106496, kOffZs = 122880;
-constexpr int kZsStride = 68;  // floats per value column in Zs
-template <int DVT>
-struct Lds {
-    static constexpr int kOffPh = kOffZs + DVT * kZsStride * 4;  // [8 halves][128] f32
-    static constexpr int kOffGam = kOffPh + 8 * 128 * 4;         // [128] f32
-    static constexpr int kBytes = kOffGam + 128 * 4;
-    static_assert(kBytes <= 160 * 1024, "LDS budget");
-};
+constexpr int kOffEt = 0;          // [64][128] bf16, single
+constexpr int kOffQt = 16384;      // [64][128] bf16, single
+constexpr int kOffKt = 32768;      // [64][128] bf16, single
+constexpr int kOffKbT = 49152;     // [2][128][64] bf16
+constexpr int kOffAneg = 81920;    // [2][64][64] bf16 (-A below the diagonal blocks)
+constexpr int kOffP = 98304;       // [2][64][64] bf16
+constexpr int kT16 = 20;            // floats per row of a 16 x 16 FP32 block (padded)
+constexpr int kTBlk = 16 * kT16 + 16;  // floats per padded block (the next block shifts by 16 banks)
+constexpr int kOffT = 114688;      // [2][4][kTBlk] f32, T_II row major
+constexpr int kOffGam = kOffT + 2 * 4 * kTBlk * 4;  // [2][128] f32 (chunk decay per channel)
+constexpr int kOffPh = kOffGam + 1024;  // [8][128] f32: decay over tokens 16 j .. 16 j + 15 (rows j < 4),
+                                        // over 0..7 (row 4), per-block channel minima (row 5)
+constexpr int kOffAd = kOffPh + 4096;   // [4][kTBlk] f32, diagonal blocks of A, column major
+constexpr int kOffZs = kOffAd + 4 * kTBlk * 4;  // [64 columns][kZsStride] f32, z = w v
+constexpr int kZsStride = 68;
+constexpr int kLdsBytes = kOffZs + kDVT * kZsStride * 4;
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+static_assert(kOffP == kOffAneg + 2 * 8192 && kOffT == kOffP + 2 * 8192, "Aneg and P are cleared as one range");
 
-// Byte offset of (row, ch) in a [rows][128] bf16 tile; 16-byte granules are
-// XOR-swizzled by the row so that 16 rows read at one granule column hit
-// different banks.
-__device__ __forceinline__ int off_rc128(int row, int ch)
+// [64][128] bf16 tiles Et, Qt, Kt.  Channels are stored permuted within each
+// group of 32 so that the split K groups of the matrix products, channels
+// {32 s + 4 g .. + 3} U {32 s + 16 + 4 g .. + 3}, occupy the 16 contiguous bytes
+// at position 32 s + 8 g; the 16-byte granules are XOR-swizzled by a linear
+// map of the low four row bits, under which the prep stores (two 8-byte
+// pieces per lane) and the operand reads (16 rows at one granule column) are
+// free of bank conflicts.
+__device__ __forceinline__ int chan_pos(int ch)
 {
-    return row * 256 + ((((ch >> 3) ^ row) & 15) << 4) + ((ch & 7) << 1);
+    return (ch & ~31) | ((ch & 12) << 1) | ((ch & 16) >> 2) | (ch & 3);
 }
-// Byte offset of (row, col) in a [rows][64] bf16 tile (granule XOR by row/2;
-// the row parity picks the bank half).
+__device__ __forceinline__ int parity(int x) { return __builtin_popcount(x) & 1; }
+__device__ __forceinline__ int tile_swz(int row)
+{
+    return parity(row & 11) | (parity(row & 9) << 1) | (parity(row & 7) << 2) | (parity(row & 13) << 3);
+}
+__device__ __forceinline__ int off_t128(int row, int pos)  // pos: permuted position
+{
+    return row * 256 + ((((pos >> 3) ^ tile_swz(row)) & 15) << 4) + ((pos & 7) << 1);
+}
+// [64][64] bf16 tiles Aneg, P: 8-byte pieces XOR-swizzled by the low row bits.
 __device__ __forceinline__ int off_rc64(int row, int col)
 {
-    return row * 128 + ((((col >> 3) ^ (row >> 1)) & 7) << 4) + ((col & 7) << 1);
+    return row * 128 + ((((col >> 2) ^ row) & 15) << 3) + ((col & 3) << 1);
 }
+// [128][64] bf16 tile Kb^T (channel rows, token columns): 8-byte pieces
+// XOR-swizzled by a linear map of the row bits (prep stores hit 16 channels
+// eight apart, reads 16 consecutive channels).
+__device__ __forceinline__ int kbt_swz(int row)
+{
+    return parity(row & 40) | (parity(row & 6) << 1) | (parity(row & 20) << 2) | (parity(row & 9) << 3);
+}
+__device__ __forceinline__ int off_kbt(int row, int col)
+{
+    return row * 128 + ((((col >> 2) ^ kbt_swz(row)) & 15) << 3) + ((col & 3) << 1);
+}
+// Float index of (column, token) in Zs: tokens rotated by 16 per group of 16
+// columns so that the column-wise stores of z spread over the banks.
+__device__ __forceinline__ int zs_index(int col, int tok) { return col * kZsStride + ((tok + 16 * (col >> 4)) & 63); }
 
 __device__ __forceinline__ uint32_t pack2(float a, float b)
 {
@@ -124,49 +158,52 @@ __device__ __forceinline__ void lds_st(unsigned char* lds, int off, V v)
     *reinterpret_cast<V*>(lds + off) = v;
 }
 
-// Per-lane byte offsets of the operand reads, computed once.  For a tile row
-// 16 k + r the swizzle term depends on r only, so every read below is one of
-// these offsets plus a compile-time constant (the tile base and 16 k rows).
+// Per-lane byte offsets of the operand reads.  For a tile row 16 k + r the
+// swizzle terms depend on r only, so every read is one of these plus a
+// compile-time constant (tile base and 16 k rows) -- except in Kb^T, whose
+// swizzle also takes the block index (a constant XOR, see ld_kbt).
 struct LaneOffs {
-    int c128[4];     // [.][128] tile, channels 32 s + 8 g .. + 7 (16 bytes)
-    int s128[4][2];  // [.][128] tile, channels 32 s + 4 g .. + 3 and 32 s + 16 + 4 g .. + 3
-    int s64[2][2];   // [.][64] tile, columns 32 s + 4 g .. + 3 and 32 s + 16 + 4 g .. + 3
+    int c128[4];     // [64][128] tile, positions 32 s + 8 g .. + 7 (16 bytes)
+    int s64[2][2];   // [64][64] tile, columns 32 s + 16 h + 4 g .. + 3 (8 bytes)
+    int kbt_row;     // Kb^T: r * 128
+    int kbt_sl;      // Kb^T: 8-byte slot g ^ swizzle(r)
 };
 
 __device__ __forceinline__ LaneOffs lane_offsets(int r, int g)
 {
     LaneOffs o;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        o.c128[s] = off_rc128(r, 32 * s + 8 * g);
-        o.s128[s][0] = off_rc128(r, 32 * s + 4 * g);
-        o.s128[s][1] = off_rc128(r, 32 * s + 16 + 4 * g);
-    }
+    for (int s = 0; s < 4; ++s) o.c128[s] = off_t128(r, 32 * s + 8 * g);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
         o.s64[s][0] = off_rc64(r, 32 * s + 4 * g);
         o.s64[s][1] = off_rc64(r, 32 * s + 16 + 4 * g);
     }
+    o.kbt_row = r * 128;
+    o.kbt_sl = (g ^ kbt_swz(r)) & 15;
     return o;
 }
 
-// Operand of row 16 k + r of a [.][128] tile, contiguous K groups.
+// Row 16 k + r of a [64][128] tile: the split K group of K-step s.
 __device__ __forceinline__ bf16x8 ld_c128(const unsigned char* lds, const LaneOffs& o, int base, int k, int s)
 {
     return as_bf16x8(lds_ld<uint4>(lds, base + 16 * k * 256 + o.c128[s]));
 }
-// Same tile with split K groups {32s+4g..+3} U {32s+16+4g..+3}.
-__device__ __forceinline__ bf16x8 ld_s128(const unsigned char* lds, const LaneOffs& o, int base, int k, int s)
-{
-    const uint2 lo = lds_ld<uint2>(lds, base + 16 * k * 256 + o.s128[s][0]);
-    const uint2 hi = lds_ld<uint2>(lds, base + 16 * k * 256 + o.s128[s][1]);
-    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-}
-// Split K groups, row 16 k + r of a [.][64] tile.
+// Split K groups, row 16 k + r of a [64][64] tile.
 __device__ __forceinline__ bf16x8 ld_s64(const unsigned char* lds, const LaneOffs& o, int base, int k, int s)
 {
     const uint2 lo = lds_ld<uint2>(lds, base + 16 * k * 128 + o.s64[s][0]);
     const uint2 hi = lds_ld<uint2>(lds, base + 16 * k * 128 + o.s64[s][1]);
+    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+// Split K groups, channel row 16 cb + r of Kb^T (tokens 32 s + 4 g .. + 3 and
+// 32 s + 16 + 4 g .. + 3): slot (8 s + 4 h + g) ^ swizzle(16 cb + r), and the
+// swizzle is linear, so the block part is a constant.
+__device__ __forceinline__ bf16x8 ld_kbt(const unsigned char* lds, const LaneOffs& o, int base, int cb, int s)
+{
+    const int c0 = ((8 * s) ^ kbt_swz(16 * cb)) & 15, c1 = ((8 * s + 4) ^ kbt_swz(16 * cb)) & 15;
+    const uint2 lo = lds_ld<uint2>(lds, base + 16 * cb * 128 + o.kbt_row + ((o.kbt_sl ^ c0) << 3));
+    const uint2 hi = lds_ld<uint2>(lds, base + 16 * cb * 128 + o.kbt_row + ((o.kbt_sl ^ c1) << 3));
     return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 // Operand from two accumulator blocks held by this lane (rows 4g..4g+3 of
@@ -179,12 +216,59 @@ __device__ __forceinline__ bf16x8 pack_acc_pair(f32x4 lo, f32x4 hi)
 
 __device__ __forceinline__ float lo_f(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float hi_f(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
-__device__ __forceinline__ float clamp_alpha(float x) { return __builtin_amdgcn_fmed3f(x, kAlphaMin, 1.0f); }
+__device__ __forceinline__ void unpack8(const uint4 x, float* f)
+{
+    f[0] = lo_f(x.x);
+    f[1] = hi_f(x.x);
+    f[2] = lo_f(x.y);
+    f[3] = hi_f(x.y);
+    f[4] = lo_f(x.z);
+    f[5] = hi_f(x.z);
+    f[6] = lo_f(x.w);
+    f[7] = hi_f(x.w);
+}
+
+// DPP moves on 32-bit values (all lanes read valid sources).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+constexpr int kQuadPrev = 0x90;   // quad_perm(0, 0, 1, 2): lane i <- lane i - 1 (lane 0 <- itself)
+constexpr int kQuadPrev2 = 0x40;  // quad_perm(0, 0, 0, 1): lanes 2, 3 <- lanes 0, 1
+constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128;
+
+// Minimum over the wavefront, returned as a wave-uniform value.
+__device__ __forceinline__ float wave_min(float x)
+{
+    x = fminf(x, dpp<kRowRor8>(x));
+    x = fminf(x, dpp<kRowRor4>(x));
+    x = fminf(x, dpp<kRowRor2>(x));
+    x = fminf(x, dpp<kRowRor1>(x));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    return fminf(fminf(r0, r1), fminf(r2, r3));
+}
+
+// Workgroup barrier for LDS traffic only.  The waves exchange data through
+// LDS alone, so a wave waits for its own LDS accesses (lgkmcnt = 0) and meets
+// the others at s_barrier; its global loads stay in flight across the barrier
+// (a full __syncthreads() fence would also wait for them, draining the
+// prefetch of the next chunk at every barrier).  The empty asm statements keep
+// the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier()
+{
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63, expcnt 7, lgkmcnt 0
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
 
 // Raw buffer resources: one descriptor per tensor window, 32-bit per-lane
-// offsets and per-token offsets in scalar registers.  Every access is guarded
-// by an explicit token test, so the descriptor's own range check is not relied
-// upon (its num_records is the window size).
+// offsets.  Reads past the window return zero and stores past it are dropped;
+// the windows end at the last valid token of the chunk.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcFlags = 0x00020000;  // 32-bit raw buffer, gfx9 family
 
@@ -192,298 +276,493 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), kRsrcFlags);
 }
+__device__ __forceinline__ uint4 ld_b128(rsrc_t r, uint32_t off)
+{
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 0);
+    return make_uint4(x[0], x[1], x[2], x[3]);
+}
 
-template <int DVT>
-struct Raw {  // one thread's share of a chunk's global inputs
-    static constexpr int kVW = DVT / 64;  // 16-byte value words per thread
-    uint32_t q[8], k[8], b[8];            // 2 bf16 channels x 8 tokens
-    float2 a[8];                          // alpha, 2 channels x 8 tokens
-    uint4 v[kVW], w[kVW];                 // DVT / 8 value columns of one token
+// One key wavefront's share of a chunk's inputs: key wavefront kw prepares
+// tokens 16 kw .. 16 kw + 15; lane l takes tokens 16 kw + 4 (l & 3) + {0..3}
+// and channels 8 (l >> 2) .. + 7 (a quad holds the wavefront's 16 tokens).
+struct RawK {
+    uint4 q[4], k[4], b[4];  // 8 bf16 channels per token
+    uint4 a[4][2];           // alpha, 8 FP32 channels per token
+};
+// A value wavefront's share of v and w: wavefront w loads tokens 16 w + (l & 15),
+// columns 16 (l >> 4) .. + 15 of the tile.
+struct RawV {
+    uint4 v[2], w[2];
 };
 
-// Loads chunk [t0, t0 + L) of head h.  Key side: wavefront w reads tokens
-// 8 w .. 8 w + 7, lane l the channel pair 2 l, 2 l + 1 (whole rows per
-// instruction).  Value side: thread t reads DVT / 8 columns of token t / 8.
-template <int DVT>
-__device__ __forceinline__ void load_raw(Raw<DVT>& R, const ChunkArgs& a, int64_t brow, int64_t t0, int L,
-                                         int h, int j0, int tid, int wave)
+// Global row of (token t0, head h) in [B*T, H] order.
+__device__ __forceinline__ int64_t token_row(const ChunkArgs& a, int64_t brow, int64_t t0, int h)
 {
-    const int lane = tid & 63;
-    const int64_t row0 = (brow * a.T + t0) * a.H + h;  // (token t0, head h)
-    const uint32_t kstride = uint32_t(a.H) * kDK * 2;  // bytes per token, bf16 key rows
-    const uint32_t win = uint32_t(kC) * kstride;
-    const rsrc_t rq = make_rsrc(static_cast<const bf16raw*>(a.q) + row0 * kDK, win);
-    const rsrc_t rk = make_rsrc(static_cast<const bf16raw*>(a.k) + row0 * kDK, win);
-    const rsrc_t rb = make_rsrc(static_cast<const bf16raw*>(a.b) + row0 * kDK, win);
-    const rsrc_t ra = make_rsrc(a.alpha + row0 * kDK, 2 * win);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int tok = 8 * wave + i;
-        if (tok < L) {
-            const int so = tok * int(kstride);
-            R.q[i] = __builtin_amdgcn_raw_buffer_load_b32(rq, 4 * lane, so, 0);
-            R.k[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, 4 * lane, so, 0);
-            R.b[i] = __builtin_amdgcn_raw_buffer_load_b32(rb, 4 * lane, so, 0);
-            const u32x2 av = __builtin_amdgcn_raw_buffer_load_b64(ra, 8 * lane, 2 * so, 0);
-            R.a[i] = make_float2(__uint_as_float(av[0]), __uint_as_float(av[1]));
-        } else {
-            R.q[i] = R.k[i] = R.b[i] = 0u;
-            R.a[i] = make_float2(1.f, 1.f);
-        }
-    }
-    constexpr int kVW = Raw<DVT>::kVW;
-    const int vtok = tid >> 3, cz = tid & 7;
+    return (brow * a.T + t0) * a.H + h;
+}
+
+// Buffer windows of a chunk's key-side inputs (L valid tokens from row0).
+struct RawSrc {
+    rsrc_t q, k, b, a;
+    uint32_t kstride;  // bytes per token, bf16 key rows
+};
+__device__ __forceinline__ RawSrc raw_src(const ChunkArgs& a, int64_t row0, int L)
+{
+    RawSrc s;
+    s.kstride = uint32_t(a.H) * kDK * 2;
+    const uint32_t win = uint32_t(L - 1) * s.kstride + kDK * 2;
+    s.q = make_rsrc(static_cast<const bf16raw*>(a.q) + row0 * kDK, win);
+    s.k = make_rsrc(static_cast<const bf16raw*>(a.k) + row0 * kDK, win);
+    s.b = make_rsrc(static_cast<const bf16raw*>(a.b) + row0 * kDK, win);
+    s.a = make_rsrc(a.alpha + row0 * kDK, 2 * win);
+    return s;
+}
+// Loads this lane's token t (of four) of a chunk.
+__device__ __forceinline__ void load_token(RawK& R, const RawSrc& s, int t, int kw, int lane)
+{
+    const int tp = lane & 3, cg = lane >> 2;
+    const uint32_t tok = uint32_t(16 * kw + 4 * tp + t);
+    const uint32_t off = tok * s.kstride + 16 * cg;
+    R.q[t] = ld_b128(s.q, off);
+    R.k[t] = ld_b128(s.k, off);
+    R.b[t] = ld_b128(s.b, off);
+    R.a[t][0] = ld_b128(s.a, 2 * tok * s.kstride + 32 * cg);
+    R.a[t][1] = ld_b128(s.a, 2 * tok * s.kstride + 32 * cg + 16);
+}
+
+__device__ __forceinline__ void load_rawv(RawV& V, const ChunkArgs& a, int64_t row0, int L, int j0, int wave,
+                                          int lane)
+{
     const uint32_t vstride = uint32_t(a.H) * uint32_t(a.dv) * 2;
-    const int64_t vrow0 = row0 * a.dv + j0;
-    const rsrc_t rv = make_rsrc(static_cast<const bf16raw*>(a.v) + vrow0, uint32_t(kC) * vstride);
-    const rsrc_t rw = make_rsrc(static_cast<const bf16raw*>(a.w) + vrow0, uint32_t(kC) * vstride);
-    if (vtok < L) {
-        const int vo = vtok * int(vstride) + 16 * kVW * cz;
+    const uint32_t win = uint32_t(L - 1) * vstride + kDVT * 2;
+    const int64_t base = row0 * a.dv + j0;
+    const rsrc_t rv = make_rsrc(static_cast<const bf16raw*>(a.v) + base, win);
+    const rsrc_t rw = make_rsrc(static_cast<const bf16raw*>(a.w) + base, win);
+    const uint32_t off = uint32_t(16 * wave + (lane & 15)) * vstride + 32 * (lane >> 4);
 #pragma unroll
-        for (int u = 0; u < kVW; ++u) {
-            const auto x = __builtin_amdgcn_raw_buffer_load_b128(rv, vo + 16 * u, 0, 0);
-            const auto y = __builtin_amdgcn_raw_buffer_load_b128(rw, vo + 16 * u, 0, 0);
-            R.v[u] = make_uint4(x[0], x[1], x[2], x[3]);
-            R.w[u] = make_uint4(y[0], y[1], y[2], y[3]);
+    for (int u = 0; u < 2; ++u) {
+        V.v[u] = ld_b128(rv, off + 16 * u);
+        V.w[u] = ld_b128(rw, off + 16 * u);
+    }
+}
+
+// Alpha of channel c of token t of this lane (as prepared by decay_pass1).
+__device__ __forceinline__ float alpha_at(const RawK& R, int t, int c)
+{
+    const uint4 x = R.a[t][c >> 2];
+    return __uint_as_float((c & 3) == 0 ? x.x : (c & 3) == 1 ? x.y : (c & 3) == 2 ? x.z : x.w);
+}
+
+// First half of the key prep: decay products along the wavefront's 16 tokens
+// (in lane, then a quad scan).  Writes the product over the 16 tokens to
+// Ph[kw] (and wavefront 0 the product over tokens 0..7 to Ph[4]); returns in
+// ex the product over the wavefront's tokens before this lane's four.
+__device__ __forceinline__ void decay_pass1(unsigned char* lds, RawK& R, float* ex, int L, int kw, int lane)
+{
+    const int tp = lane & 3, cg = lane >> 2;
+    // alpha clamped to [2^-15, 1], and 1 past the sequence end, written back
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const bool live = 16 * kw + 4 * tp + t < L;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint4& x = R.a[t][h];
+            x.x = __float_as_uint(live ? __builtin_amdgcn_fmed3f(__uint_as_float(x.x), kAlphaMin, 1.0f) : 1.0f);
+            x.y = __float_as_uint(live ? __builtin_amdgcn_fmed3f(__uint_as_float(x.y), kAlphaMin, 1.0f) : 1.0f);
+            x.z = __float_as_uint(live ? __builtin_amdgcn_fmed3f(__uint_as_float(x.z), kAlphaMin, 1.0f) : 1.0f);
+            x.w = __float_as_uint(live ? __builtin_amdgcn_fmed3f(__uint_as_float(x.w), kAlphaMin, 1.0f) : 1.0f);
         }
+    }
+    float inc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        float p = 1.0f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) p *= alpha_at(R, t, c);
+        const float y = dpp<kQuadPrev>(p);
+        const float x1 = tp >= 1 ? p * y : p;
+        const float z = dpp<kQuadPrev2>(x1);
+        inc[c] = tp >= 2 ? x1 * z : x1;  // tokens 16 kw .. 16 kw + 4 tp + 3
+        const float e = dpp<kQuadPrev>(inc[c]);
+        ex[c] = tp >= 1 ? e : 1.0f;      // tokens 16 kw .. 16 kw + 4 tp - 1
+    }
+    float* ph = reinterpret_cast<float*>(lds + kOffPh);
+    if (tp == 3 || (kw == 0 && tp == 1)) {
+        float* dst = ph + (tp == 3 ? kw : 4) * 128 + 8 * cg;
+        *reinterpret_cast<float4*>(dst) = make_float4(inc[0], inc[1], inc[2], inc[3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(inc[4], inc[5], inc[6], inc[7]);
+    }
+    // smallest decay over the 16 tokens among all channels (products are <= 1)
+    float m = 1.0f;
+    if (tp == 3) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) m = fminf(m, inc[c]);
+    }
+    m = wave_min(m);
+    if (lane == 0) ph[5 * 128 + kw] = m;
+}
+
+// Chunk length (identical in every wavefront: the same four values in the
+// same order): with m_j the smallest decay over block j (tokens 16 j ..
+// 16 j + 15) among all channels, the longest of 64, 32, 16 tokens for which
+// m_0 m_1 ... stays >= 2^-120, else 8; at most L.  The product of the minima
+// bounds every channel's decay from below, so all factors of the chunk stay
+// within [2^-120, 2^120].
+__device__ __forceinline__ int chunk_step(const unsigned char* lds, int L)
+{
+    const float* pm = reinterpret_cast<const float*>(lds + kOffPh) + 5 * 128;
+    const float g16 = pm[0], g32 = g16 * pm[1], g64 = g32 * pm[2] * pm[3];
+    const int leff = g64 >= kRangeMin ? 64 : g32 >= kRangeMin ? 32 : g16 >= kRangeMin ? 16 : 8;
+    return leff < L ? leff : L;
+}
+
+// Stores channels 8 cg .. 8 cg + 7 of one row of a [64][128] tile: two
+// 8-byte pieces at their permuted positions.
+__device__ __forceinline__ void st_row8(unsigned char* lds, int base, int row, int cg, uint4 v)
+{
+    lds_st<uint2>(lds, base + off_t128(row, chan_pos(8 * cg)), make_uint2(v.x, v.y));
+    lds_st<uint2>(lds, base + off_t128(row, chan_pos(8 * cg + 4)), make_uint2(v.z, v.w));
+}
+
+// Zero rows of Et, Qt, Kt and zero columns of Kb^T for the four tokens from tok0.
+__device__ __forceinline__ void zero_rows(unsigned char* lds, int kbt, int tok0, int cg)
+{
+    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        st_row8(lds, kOffEt, tok0 + t, cg, zero);
+        st_row8(lds, kOffQt, tok0 + t, cg, zero);
+        st_row8(lds, kOffKt, tok0 + t, cg, zero);
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) lds_st<uint2>(lds, kbt + off_kbt(8 * cg + c, tok0), make_uint2(0u, 0u));
+}
+
+// Rows of Et, Qt, Kt and columns of Kb^T for this lane's four tokens, given
+// the decay before them (cum) and the chunk decay (gam).
+__device__ __forceinline__ void prep_rows(unsigned char* lds, const RawK& R, float* cum, const float* gam, int kbt,
+                                          int tok0, int cg)
+{
+    uint32_t kbp[2][8];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        float q[8], k[8], b[8];
+        unpack8(R.q[t], q);
+        unpack8(R.k[t], k);
+        unpack8(R.b[t], b);
+        float et[8], qt[8], kt[8], kb[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            cum[c] *= alpha_at(R, t, c);  // 1 past the sequence end (decay_pass1)
+            const float rc = __builtin_amdgcn_rcpf(cum[c]);
+            et[c] = b[c] * k[c] * cum[c];
+            qt[c] = q[c] * cum[c];
+            kt[c] = k[c] * rc;
+            kb[c] = kt[c] * gam[c];
+        }
+        st_row8(lds, kOffEt, tok0 + t, cg, make_uint4(pack2(et[0], et[1]), pack2(et[2], et[3]),
+                                                         pack2(et[4], et[5]), pack2(et[6], et[7])));
+        st_row8(lds, kOffQt, tok0 + t, cg, make_uint4(pack2(qt[0], qt[1]), pack2(qt[2], qt[3]),
+                                                         pack2(qt[4], qt[5]), pack2(qt[6], qt[7])));
+        st_row8(lds, kOffKt, tok0 + t, cg, make_uint4(pack2(kt[0], kt[1]), pack2(kt[2], kt[3]),
+                                                         pack2(kt[4], kt[5]), pack2(kt[6], kt[7])));
+        if (t & 1) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) kbp[t >> 1][c] = pack2(__uint_as_float(kbp[t >> 1][c]), kb[c]);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) kbp[t >> 1][c] = __float_as_uint(kb[c]);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // one token's temporaries at a time
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) lds_st<uint2>(lds, kbt + off_kbt(8 * cg + c, tok0), make_uint2(kbp[0][c], kbp[1][c]));
+}
+
+// Decay factors and operand rows of this lane's four tokens (wavefront not
+// entirely past the chunk); the chunk decay gamma (wavefront 4 writes it).
+__device__ __forceinline__ void prep_factors_rows(unsigned char* lds, const RawK& R, const float* ex, int step,
+                                                  int kbuf, int kw, int lane)
+{
+    const int tp = lane & 3, cg = lane >> 2;
+    const float* ph = reinterpret_cast<const float*>(lds + kOffPh) + 8 * cg;
+    const int tok0 = 16 * kw + 4 * tp;
+    const int kbt = kOffKbT + kbuf * 16384;
+    // gamma over the tokens the chunk covers; cum: decay before this lane's tokens
+    // products of blocks 0 .. nw - 1 (gamma) and 0 .. kw - 1 (prefix), as
+    // multiplications by 1 past the bound (no data-dependent loads)
+    const int nw = step <= 8 ? 0 : (step + 15) >> 4;  // 0: the chunk ends inside tokens 0..7
+    float gam[8], cum[8];
+    const float4* p4 = reinterpret_cast<const float4*>(ph);  // row j, channels 8 cg ..: p4[32 j], p4[32 j + 1]
+    const auto block = [&](int j, float* v) {
+        const float4 a = p4[32 * j], b = p4[32 * j + 1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    };
+#pragma unroll
+    for (int c = 0; c < 8; ++c) gam[c] = cum[c] = 1.0f;
+    if (nw == 0) block(4, gam);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (j < nw || j < kw) {  // uniform
+            float v[8];
+            block(j, v);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                if (j < nw) gam[c] *= v[c];
+                if (j < kw) cum[c] *= v[c];
+            }
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) cum[c] *= ex[c];
+    if (kw == 0 && tp == 0) {
+        float* gp = reinterpret_cast<float*>(lds + kOffGam) + kbuf * 128 + 8 * cg;
+        *reinterpret_cast<float4*>(gp) = make_float4(gam[0], gam[1], gam[2], gam[3]);
+        *reinterpret_cast<float4*>(gp + 4) = make_float4(gam[4], gam[5], gam[6], gam[7]);
+    }
+    // A chunk cut short (step < L) ends at a multiple of 8, so each lane's four
+    // tokens are either all in it or all past it; the lanes past it write
+    // zero rows (their decay factors are not formed).  Past the sequence end
+    // (step = L) the inputs read as zero and alpha as 1, which gives zero rows.
+    if (tok0 >= step)
+        zero_rows(lds, kbt, tok0, cg);
+    else
+        prep_rows(lds, R, cum, gam, kbt, tok0, cg);
+}
+
+// Second half of the key prep: decay factors and the operand tiles of this
+// lane's four tokens; the chunk decay gamma (wavefront 4 writes it).
+__device__ __forceinline__ void prep_tiles(unsigned char* lds, const RawK& R, const float* ex, int step, int kbuf,
+                                           int kw, int lane)
+{
+    const int tp = lane & 3, cg = lane >> 2;
+    const int tok0 = 16 * kw + 4 * tp;
+    const int kbt = kOffKbT + kbuf * 16384;
+    if (16 * kw >= step)  // the whole wavefront lies past the chunk
+        zero_rows(lds, kbt, tok0, cg);
+    else
+        prep_factors_rows(lds, R, ex, step, kbuf, kw, lane);
+}
+
+// z = w v of the chunk into Zs (rows past the chunk are masked when read).
+__device__ __forceinline__ void prep_z(unsigned char* lds, const RawV& V, int wave, int lane)
+{
+    const int tok = 16 * wave + (lane & 15), cq = lane >> 4;
+    float* zs = reinterpret_cast<float*>(lds + kOffZs);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        float v[8], w[8];
+        unpack8(V.v[u], v);
+        unpack8(V.w[u], w);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) zs[zs_index(16 * cq + 8 * u + m, tok)] = v[m] * w[m];
+    }
+}
+
+// One block of A or P (16 x 16 over K = 128 channels), formed transposed:
+// D = Kt_J Row_I^T, which leaves row 16 I + r, columns 16 J + 4 g .. + 3 in
+// each lane.
+template <int KIND, int I, int J>  // KIND 0: A (rows Et), 1: P (rows Qt)
+__device__ __forceinline__ void ap_block(unsigned char* lds, const LaneOffs& o, int buf, int r, int g)
+{
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        acc = mfma_bf16(ld_c128(lds, o, kOffKt, J, s), ld_c128(lds, o, KIND == 0 ? kOffEt : kOffQt, I, s), acc);
+    const int row = 16 * I + r, col = 16 * J + 4 * g;
+    if (KIND == 0) {
+        lds_st<uint2>(lds, kOffAneg + buf * 8192 + off_rc64(row, col),
+                      make_uint2(pack2(-acc[0], -acc[1]), pack2(-acc[2], -acc[3])));
     } else {
+        float p[4] = {acc[0], acc[1], acc[2], acc[3]};
+        if (I == J) {
 #pragma unroll
-        for (int u = 0; u < kVW; ++u) R.v[u] = R.w[u] = make_uint4(0u, 0u, 0u, 0u);
+            for (int i = 0; i < 4; ++i) p[i] = col + i <= row ? p[i] : 0.f;
+        }
+        lds_st<uint2>(lds, kOffP + buf * 8192 + off_rc64(row, col), make_uint2(pack2(p[0], p[1]), pack2(p[2], p[3])));
+    }
+    __builtin_amdgcn_sched_barrier(0);  // one block's operands in flight at a time
+}
+
+// The six A blocks below the diagonal blocks and the ten P blocks on and below
+// them, over value wavefronts 0..2 (grouped by shared operands).
+__device__ __forceinline__ void ap_work(unsigned char* lds, const LaneOffs& o, int buf, int slot, int r, int g)
+{
+    switch (slot) {
+        case 0:
+            ap_block<1, 3, 3>(lds, o, buf, r, g);
+            ap_block<1, 3, 2>(lds, o, buf, r, g);
+            ap_block<1, 3, 1>(lds, o, buf, r, g);
+            ap_block<1, 3, 0>(lds, o, buf, r, g);
+            ap_block<0, 3, 2>(lds, o, buf, r, g);
+            break;
+        case 1:
+            ap_block<1, 2, 2>(lds, o, buf, r, g);
+            ap_block<1, 2, 1>(lds, o, buf, r, g);
+            ap_block<1, 2, 0>(lds, o, buf, r, g);
+            ap_block<0, 3, 1>(lds, o, buf, r, g);
+            ap_block<0, 3, 0>(lds, o, buf, r, g);
+            break;
+        default:
+            ap_block<1, 1, 1>(lds, o, buf, r, g);
+            ap_block<1, 1, 0>(lds, o, buf, r, g);
+            ap_block<1, 0, 0>(lds, o, buf, r, g);
+            ap_block<0, 2, 1>(lds, o, buf, r, g);
+            ap_block<0, 2, 0>(lds, o, buf, r, g);
+            ap_block<0, 1, 0>(lds, o, buf, r, g);
+            break;
     }
 }
 
-// Key-side elementwise work of one chunk (all threads): decay factors, the
-// bf16 operand tiles Eh, Qh, Kh, Ko, Et, Qt, KbT, the value tile z = w v and
-// the chunk decay gamma.  Ends with the tiles visible to every wavefront.
-// Thread (wavefront hb, lane cp) handles tokens 8 hb .. 8 hb + 7 (half hb & 1
-// of block hb >> 1) for channels 2 cp, 2 cp + 1.
-template <int DVT>
-__device__ __forceinline__ void prep_chunk(unsigned char* lds, const Raw<DVT>& R, int tid, int hb)
+// Wavefront kTWave: the diagonal blocks A_II (strictly lower, FP32) and
+// T_II = (I + A_II)^-1 by forward substitution; lane group g takes block g,
+// lane r its column r.
+__device__ __forceinline__ void t_work(unsigned char* lds, const LaneOffs& o, int buf, int r, int g)
 {
-    const int cp = tid & 63;
-    const int blk = hb >> 1, half = hb & 1;
-    const float* ph = reinterpret_cast<const float*>(lds + Lds<DVT>::kOffPh);
-
-    // pass 1: products of the clamped decay over this half block
-    float al0[8], al1[8];
-    float p0 = 1.f, p1 = 1.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        al0[i] = clamp_alpha(R.a[i].x);
-        al1[i] = clamp_alpha(R.a[i].y);
-        p0 *= al0[i];
-        p1 *= al1[i];
-    }
-    lds_st<float2>(lds, Lds<DVT>::kOffPh + (hb * 128 + 2 * cp) * 4, make_float2(p0, p1));
-    __syncthreads();
-
-    // pass 2: factors between the block references, for this thread's channels
-    float s1[2], s2[2], dsc[2][4];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        const int ch = 2 * cp + c;
-        float lo[4], hi[4];
-#pragma unroll
-        for (int J = 0; J < 4; ++J) {
-            lo[J] = ph[(2 * J) * 128 + ch];      // block start -> reference token
-            hi[J] = ph[(2 * J + 1) * 128 + ch];  // reference token -> block end
-        }
-        float pre = 1.f;
-#pragma unroll
-        for (int J = 0; J < 4; ++J)
-            if (J < blk) pre *= lo[J] * hi[J];
-        s1[c] = pre * lo[blk];  // 2^(m_blk): chunk start -> reference of blk
-        float post = hi[blk];
-#pragma unroll
-        for (int J = 0; J < 4; ++J)
-            if (J > blk) post *= lo[J] * hi[J];
-        s2[c] = post;  // 2^(G_last - m_blk)
-        float run = hi[blk];
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-            if (I > blk) {
-                dsc[c][I] = run * lo[I];  // 2^(m_I - m_blk)
-                run *= lo[I] * hi[I];
-            } else {
-                dsc[c][I] = 0.f;
-            }
-        }
-        if (hb == 0) {
-            float gam = 1.f;
-#pragma unroll
-            for (int J = 0; J < 4; ++J) gam *= lo[J] * hi[J];
-            reinterpret_cast<float*>(lds + Lds<DVT>::kOffGam)[ch] = gam;
-        }
-    }
-
-    // per-token factors r = 2^(G_i - m), ri = 2^(m - G_i) around the block's
-    // reference m (the last token of half 0):
-    //   half 0: r_i = prod alpha[0..i] / p,   ri_i = prod alpha[i+1..7]
-    //   half 1: r_i = prod alpha[0..i],       ri_i = prod alpha[i+1..7] / p
-    // with p the product over the whole half.
-    const float inv0 = __builtin_amdgcn_rcpf(p0), inv1 = __builtin_amdgcn_rcpf(p1);
-    float suf0[8], suf1[8];
-    suf0[7] = 1.f;
-    suf1[7] = 1.f;
-#pragma unroll
-    for (int i = 6; i >= 0; --i) {
-        suf0[i] = suf0[i + 1] * al0[i + 1];
-        suf1[i] = suf1[i + 1] * al1[i + 1];
-    }
-    float cum0 = 1.f, cum1 = 1.f;
-    uint32_t kb0[4], kb1[4];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        cum0 *= al0[i];
-        cum1 *= al1[i];
-        float r0, r1, ri0, ri1;
-        if (half == 0) {
-            r0 = i == 7 ? 1.f : cum0 * inv0;
-            r1 = i == 7 ? 1.f : cum1 * inv1;
-            ri0 = suf0[i];
-            ri1 = suf1[i];
-        } else {
-            r0 = cum0;
-            r1 = cum1;
-            ri0 = suf0[i] * inv0;
-            ri1 = suf1[i] * inv1;
-        }
-        const int row = 8 * hb + i;
-        const float q0 = lo_f(R.q[i]), q1 = hi_f(R.q[i]);
-        const float k0 = lo_f(R.k[i]), k1 = hi_f(R.k[i]);
-        const float e0 = lo_f(R.b[i]) * k0, e1 = hi_f(R.b[i]) * k1;
-        const float eh0 = e0 * r0, eh1 = e1 * r1;
-        const float qh0 = q0 * r0, qh1 = q1 * r1;
-        const float kh0 = k0 * ri0, kh1 = k1 * ri1;
-        const int off = off_rc128(row, 2 * cp);
-        lds_st<uint32_t>(lds, kOffEh + off, pack2(eh0, eh1));
-        lds_st<uint32_t>(lds, kOffQh + off, pack2(qh0, qh1));
-        lds_st<uint32_t>(lds, kOffKh + off, pack2(kh0, kh1));
-        lds_st<uint32_t>(lds, kOffEt + off, pack2(eh0 * s1[0], eh1 * s1[1]));
-        lds_st<uint32_t>(lds, kOffQt + off, pack2(qh0 * s1[0], qh1 * s1[1]));
-#pragma unroll
-        for (int I = 1; I < 4; ++I)
-            if (I > blk) {
-                const int pair = I * (I - 1) / 2 + blk;
-                lds_st<uint32_t>(lds, kOffKo + pair * 4096 + off_rc128(8 * half + i, 2 * cp),
-                                 pack2(kh0 * dsc[0][I], kh1 * dsc[1][I]));
-            }
-        const uint32_t kbp = pack2(kh0 * s2[0], kh1 * s2[1]);  // (channel 0, channel 1)
-        if (i & 1) {
-            kb0[i >> 1] |= kbp << 16;
-            kb1[i >> 1] |= kbp & 0xffff0000u;
-        } else {
-            kb0[i >> 1] = kbp & 0xffffu;
-            kb1[i >> 1] = kbp >> 16;
-        }
-    }
-    lds_st<uint4>(lds, kOffKbT + off_rc64(2 * cp, 8 * hb), make_uint4(kb0[0], kb0[1], kb0[2], kb0[3]));
-    lds_st<uint4>(lds, kOffKbT + off_rc64(2 * cp + 1, 8 * hb), make_uint4(kb1[0], kb1[1], kb1[2], kb1[3]));
-
-    // z = w (.) v, column major for the accumulator-layout reads
-    {
-        constexpr int kVW = Raw<DVT>::kVW;
-        const int tok = tid >> 3, cz = tid & 7;
-        float* zs = reinterpret_cast<float*>(lds + kOffZs);
-#pragma unroll
-        for (int u = 0; u < kVW; ++u) {
-            const uint32_t vv[4] = {R.v[u].x, R.v[u].y, R.v[u].z, R.v[u].w};
-            const uint32_t ww[4] = {R.w[u].x, R.w[u].y, R.w[u].z, R.w[u].w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int col = 8 * kVW * cz + 8 * u + 2 * j;
-                zs[col * kZsStride + tok] = lo_f(ww[j]) * lo_f(vv[j]);
-                zs[(col + 1) * kZsStride + tok] = hi_f(ww[j]) * hi_f(vv[j]);
-            }
-        }
-    }
-    __syncthreads();
-}
-
-// One A or P block product.  Off-diagonal blocks and all P blocks are formed
-// transposed (K rows as the A operand), which leaves row 16 I + r, columns
-// 16 J + 4 g .. + 3 in each lane; the diagonal A block is formed directly and
-// stored column major in FP32 for the forward substitution.
-struct Item {
-    int kind;  // 0: A block, 1: P block
-    int I, J;
-};
-
-__device__ __forceinline__ void ap_block(const unsigned char* lds, const LaneOffs& o, const Item it, f32x4& acc)
-{
-    const int rowbase = it.kind == 0 ? kOffEh : kOffQh;
-    const bool diag = it.J == it.I;
-    const int kbase = diag ? kOffKh : kOffKo + (it.I * (it.I - 1) / 2 + it.J) * 4096;
-    const int kblk = diag ? it.J : 0;
-    acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (it.kind == 0 && diag) {
+    for (int I = 0; I < 4; ++I) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-            acc = mfma_bf16(ld_c128(lds, o, rowbase, it.I, s), ld_c128(lds, o, kbase, kblk, s), acc);
-    } else {
+            acc = mfma_bf16(ld_c128(lds, o, kOffEt, I, s), ld_c128(lds, o, kOffKt, I, s), acc);
+        // acc[i] = A_II[4g + i][r]: column r, rows 4g..4g+3, strictly lower part
+        float4 v;
+        v.x = 4 * g + 0 > r ? acc[0] : 0.f;
+        v.y = 4 * g + 1 > r ? acc[1] : 0.f;
+        v.z = 4 * g + 2 > r ? acc[2] : 0.f;
+        v.w = 4 * g + 3 > r ? acc[3] : 0.f;
+        lds_st<float4>(lds, kOffAd + (I * kTBlk + r * kT16 + 4 * g) * 4, v);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // Other lanes of this wavefront read the columns back: LDS accesses of one
+    // wavefront complete in order; this keeps the compiler from reordering.
+    __asm__ volatile("" ::: "memory");
+    const float* adc = reinterpret_cast<const float*>(lds + kOffAd) + g * kTBlk;  // column j at adc + j * kT16
+    const auto adt = [&](int j, int q4) { return *reinterpret_cast<const float4*>(adc + j * kT16 + 4 * q4); };
+    float t[16];
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-            acc = mfma_bf16(ld_c128(lds, o, kbase, kblk, s), ld_c128(lds, o, rowbase, it.I, s), acc);
+    for (int i = 0; i < 16; ++i) t[i] = i == r ? 1.f : 0.f;
+    float4 c0[4], c1[4];  // columns j and j + 1; column j + 2 is read during step j
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+        c0[q4] = adt(0, q4);
+        c1[q4] = adt(1, q4);
     }
-}
-
-__device__ __forceinline__ void ap_store(unsigned char* lds, const Item it, int r, int g, const f32x4 acc)
-{
-    const int row = 16 * it.I + r;      // transposed blocks: this lane's row
-    const int col = 16 * it.J + 4 * g;  // .. and its four columns
-    if (it.kind == 0) {
-        if (it.J < it.I) {
-            lds_st<uint2>(lds, kOffAneg + off_rc64(row, col),
-                          make_uint2(pack2(-acc[0], -acc[1]), pack2(-acc[2], -acc[3])));
-        } else {
-            // direct block: column r, rows 4g..4g+3; strictly lower part only
-            float4 v;
-            v.x = 4 * g + 0 > r ? acc[0] : 0.f;
-            v.y = 4 * g + 1 > r ? acc[1] : 0.f;
-            v.z = 4 * g + 2 > r ? acc[2] : 0.f;
-            v.w = 4 * g + 3 > r ? acc[3] : 0.f;
-            lds_st<float4>(lds, kOffAdT + ((it.I * 16 + r) * 16 + 4 * g) * 4, v);
-            if (it.I == 1 || it.I == 3)  // diagonal blocks the blocked solve reads as zero
-                lds_st<uint2>(lds, kOffAneg + off_rc64(row, col), make_uint2(0u, 0u));
+#pragma unroll
+    for (int j = 0; j < 15; ++j) {
+        float4 c2[4];
+        if (j < 13)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) c2[q4] = adt(j + 2, q4);
+        const float col[16] = {c0[0].x, c0[0].y, c0[0].z, c0[0].w, c0[1].x, c0[1].y, c0[1].z, c0[1].w,
+                               c0[2].x, c0[2].y, c0[2].z, c0[2].w, c0[3].x, c0[3].y, c0[3].z, c0[3].w};
+#pragma unroll
+        for (int i = j + 1; i < 16; ++i) t[i] -= col[i] * t[j];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            c0[q4] = c1[q4];
+            if (j < 13) c1[q4] = c2[q4];
         }
-    } else {
-        if (it.J < it.I) {
-            lds_st<uint2>(lds, kOffP + off_rc64(row, col), make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3])));
-        } else {
-            const float p0 = col + 0 <= row ? acc[0] : 0.f, p1 = col + 1 <= row ? acc[1] : 0.f;
-            const float p2 = col + 2 <= row ? acc[2] : 0.f, p3 = col + 3 <= row ? acc[3] : 0.f;
-            lds_st<uint2>(lds, kOffP + off_rc64(row, col), make_uint2(pack2(p0, p1), pack2(p2, p3)));
-            if (it.I == 0 || it.I == 2)  // block right of the diagonal, read by P U as zero
-                lds_st<uint2>(lds, kOffP + off_rc64(row, col + 16), make_uint2(0u, 0u));
-        }
+        __asm__ volatile("" ::: "memory");  // two columns ahead, no further
     }
+    float* T = reinterpret_cast<float*>(lds + kOffT) + (buf * 4 + g) * kTBlk;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) T[i * kT16 + r] = t[i];
 }
 
-// A/P work items of wavefront w (20 blocks over 8 wavefronts).
-__device__ __forceinline__ int ap_items(int w, Item* out)
+// Value wavefront, chunk of lv tokens: X = Z - Et S (direct, rows past the
+// chunk zero) and OT = (Qt S)^T.
+__device__ __forceinline__ void value_xo(const unsigned char* lds, const LaneOffs& o, const f32x4* S, f32x4* X,
+                                         f32x4* OT, int lv, int wave, int r, int g)
 {
-    switch (w) {
-        case 0: out[0] = {0, 3, 0}; out[1] = {0, 3, 1}; return 2;
-        case 1: out[0] = {0, 3, 2}; out[1] = {0, 3, 3}; return 2;
-        case 2: out[0] = {1, 3, 0}; out[1] = {1, 3, 1}; return 2;
-        case 3: out[0] = {1, 3, 2}; out[1] = {1, 3, 3}; return 2;
-        case 4: out[0] = {0, 2, 0}; out[1] = {0, 2, 1}; out[2] = {0, 2, 2}; return 3;
-        case 5: out[0] = {1, 2, 0}; out[1] = {1, 2, 1}; out[2] = {1, 2, 2}; return 3;
-        case 6: out[0] = {0, 1, 0}; out[1] = {0, 1, 1}; out[2] = {0, 0, 0}; return 3;
-        default: out[0] = {1, 1, 0}; out[1] = {1, 1, 1}; out[2] = {1, 0, 0}; return 3;
+    bf16x8 sb[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) sb[s] = pack_acc_pair(S[2 * s], S[2 * s + 1]);
+    const float* zs = reinterpret_cast<const float*>(lds + kOffZs);
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        f32x4 xe = f32x4{0.f, 0.f, 0.f, 0.f}, xq = xe;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            xe = mfma_bf16(ld_c128(lds, o, kOffEt, I, s), sb[s], xe);
+            xq = mfma_bf16(sb[s], ld_c128(lds, o, kOffQt, I, s), xq);
+        }
+        const float4 z = *reinterpret_cast<const float4*>(zs + zs_index(16 * wave + r, 16 * I + 4 * g));
+        const int t0 = 16 * I + 4 * g;
+        X[I] = f32x4{t0 + 0 < lv ? z.x - xe[0] : 0.f, t0 + 1 < lv ? z.y - xe[1] : 0.f,
+                     t0 + 2 < lv ? z.z - xe[2] : 0.f, t0 + 3 < lv ? z.w - xe[3] : 0.f};
+        OT[I] = xq;
+        __builtin_amdgcn_sched_barrier(0);  // one row block's operands in flight at a time
     }
 }
 
-template <int VW>
+// Value wavefront, rest of the chunk: blocked solve, output rows and state
+// update, from the tiles of buffer vbuf.
+__device__ __forceinline__ void value_solve(const unsigned char* lds, const LaneOffs& o, f32x4* S, const f32x4* X,
+                                            const f32x4* OT, int vbuf, rsrc_t ro, int ostride, int lv, int wave, int r,
+                                            int g)
+{
+    const int aneg = kOffAneg + vbuf * 8192, pb = kOffP + vbuf * 8192;
+    const int tb = kOffT + vbuf * 4 * kTBlk * 4, kbt = kOffKbT + vbuf * 16384;
+    // ---- blocked solve: R_I = X_I - sum_J A_IJ U_J ; U_I = T_II R_I
+    f32x4 U[4];
+    bf16x8 ub[2];
+    const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        f32x4 R_ = X[I];
+        if (I >= 1) R_ = mfma_bf16(ld_s64(lds, o, aneg, I, 0), ub[0], R_);
+        if (I >= 3) R_ = mfma_bf16(ld_s64(lds, o, aneg, I, 1), ub[1], R_);
+        const float4 tr = lds_ld<float4>(lds, tb + (I * kTBlk + r * kT16 + 4 * g) * 4);
+        f32x4 u = zero4;
+        u = mfma_f32(tr.x, R_[0], u);
+        u = mfma_f32(tr.y, R_[1], u);
+        u = mfma_f32(tr.z, R_[2], u);
+        u = mfma_f32(tr.w, R_[3], u);
+        U[I] = u;
+        // operands over tokens 0..31 and 32..63; blocks not solved yet stay zero
+        if (I == 0) ub[0] = pack_acc_pair(U[0], zero4);
+        if (I == 1) ub[0] = pack_acc_pair(U[0], U[1]);
+        if (I == 2) ub[1] = pack_acc_pair(U[2], zero4);
+        if (I == 3) ub[1] = pack_acc_pair(U[2], U[3]);
+    }
+    // ---- O^T = (Qt S)^T + U^T P^T; lane holds token 16 I + r, columns 4g..4g+3
+    const int o_vo = r * ostride + (16 * wave + 4 * g) * 2;
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        f32x4 acc2 = OT[I];
+        acc2 = mfma_bf16(ub[0], ld_s64(lds, o, pb, I, 0), acc2);
+        if (I >= 2) acc2 = mfma_bf16(ub[1], ld_s64(lds, o, pb, I, 1), acc2);
+        if (16 * I + r < lv) {
+            u32x2 pk;
+            pk[0] = pack2(acc2[0], acc2[1]);
+            pk[1] = pack2(acc2[2], acc2[3]);
+            __builtin_amdgcn_raw_buffer_store_b64(pk, ro, o_vo, 16 * I * ostride, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // ---- S <- Diag(gamma) S + Kb^T U
+    const float* gam = reinterpret_cast<const float*>(lds + kOffGam) + vbuf * 128;
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+        const float4 gm = *reinterpret_cast<const float4*>(gam + 16 * cb + 4 * g);
+        f32x4 acc3 = f32x4{S[cb][0] * gm.x, S[cb][1] * gm.y, S[cb][2] * gm.z, S[cb][3] * gm.w};
+        acc3 = mfma_bf16(ld_kbt(lds, o, kbt, cb, 0), ub[0], acc3);
+        acc3 = mfma_bf16(ld_kbt(lds, o, kbt, cb, 1), ub[1], acc3);
+        S[cb] = acc3;
+        if (cb & 1) __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, int ntiles, int nchains)
 {
-    constexpr int DVT = 16 * VW;
     extern __shared__ __align__(16) unsigned char lds[];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63;
-    const int g = lane >> 4, r = lane & 15;
-    const bool vwave = wave < VW;
+    const int lane0 = tid & 63;
+    const int g0 = lane0 >> 4, r0 = lane0 & 15;
+    const bool vwave = wave < kValueWaves;
+    const int kw = wave - kValueWaves;
 
     // XCD-aware mapping: all tiles of a chain share blockIdx.x % 8.
     const int bid = blockIdx.x;
@@ -492,207 +771,155 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
     const int chain = (slot / ntiles) * 8 + xcd;
     if (chain >= nchains) return;
     const int n = chain / a.H, h = chain % a.H;
-    const int j0 = tile * DVT;
+    const int j0 = tile * kDVT;
     const int64_t dv = a.dv;
 
     int64_t bos, eos, brow;
     sequence_bounds(a.cu_seqlens, n, a.T, bos, eos, brow);
 
-    // state slice of a value wavefront: channels 16 cb + 4 g + i, column j0 + 16 wave + r
-    f32x4 S[8];
-    const int64_t sbase = (int64_t(n) * a.H + h) * kDK * dv + j0;
-    const uint32_t sbytes = uint32_t(kDK * dv * 4);
-    const int s_vo = ((4 * g) * int(dv) + 16 * wave + r) * 4;
+    // The blocks the solve and the output read as zero (A on the diagonal, P
+    // right of it) are never written: clear Aneg and P, both buffers, once.
+    {
+        uint4* z = reinterpret_cast<uint4*>(lds + kOffAneg);
+        const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb) S[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (vwave && a.initial_state) {
-        const rsrc_t rs = make_rsrc(a.initial_state + sbase, sbytes);
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                S[cb][i] = __uint_as_float(
-                    __builtin_amdgcn_raw_buffer_load_b32(rs, s_vo, (16 * cb + i) * int(dv) * 4, 0));
+        for (int i = 0; i < 4; ++i) z[tid + i * kThreads] = zero;  // 4 x 512 x 16 = 32768 bytes
     }
 
-    Raw<DVT> R;
-    if (bos < eos) load_raw(R, a, brow, bos, int(eos - bos < kC ? eos - bos : kC), h, j0, tid, wave);
-
-    bf16raw* o = static_cast<bf16raw*>(a.o);
-    const float* gam = reinterpret_cast<const float*>(lds + Lds<DVT>::kOffGam);
-    const float* zcol = reinterpret_cast<const float*>(lds + kOffZs) + (16 * wave + r) * kZsStride;
-    Item items[3];
-    const int nitems = ap_items(wave, items);
-    const LaneOffs lo_ = lane_offsets(r, g);
-
-    for (int64_t t0 = bos; t0 < eos; t0 += kC) {
-        const int L = int(eos - t0 < kC ? eos - t0 : kC);
-        prep_chunk<DVT>(lds, R, tid, wave);
-        if (t0 + kC < eos) {
-            const int64_t tn = t0 + kC;
-            load_raw(R, a, brow, tn, int(eos - tn < kC ? eos - tn : kC), h, j0, tid, wave);
+    // Both roles run the same sequence of periods (the loop control is
+    // computed identically) and meet at the same three barriers per period;
+    // separate loops keep each role's registers apart.
+    int64_t tk = bos;  // chunk the key side prepares this period
+    int64_t tv = -1;   // chunk the value side finishes this period (< 0: none)
+    int kbuf = 0;      // buffer the key side writes this period; the value side reads kbuf ^ 1
+    if (vwave) {
+        // state slice of a value wavefront: channels 16 cb + 4 g + i, column j0 + 16 wave + r
+        f32x4 S[8];
+        const int64_t sbase = (int64_t(n) * a.H + h) * kDK * dv + j0;
+        const uint32_t sbytes = uint32_t(kDK * dv * 4);
+        const int s_vo = ((4 * g0) * int(dv) + 16 * wave + r0) * 4;
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) S[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (a.initial_state) {
+            const rsrc_t rs = make_rsrc(a.initial_state + sbase, sbytes);
+#pragma unroll
+            for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    S[cb][i] = __uint_as_float(
+                        __builtin_amdgcn_raw_buffer_load_b32(rs, s_vo, (16 * cb + i) * int(dv) * 4, 0));
         }
 
-        // ---- A and P blocks
-        f32x4 acc[3];
-#pragma unroll
-        for (int k = 0; k < 3; ++k) {
-            if (k < nitems) ap_block(lds, lo_, items[k], acc[k]);
-            __builtin_amdgcn_sched_barrier(0);
+        bf16raw* o = static_cast<bf16raw*>(a.o);
+        const int ostride = a.H * int(dv) * 2;
+        RawV V;
+        int lv = 0;  // length of chunk tv
+        if (tk < eos) load_rawv(V, a, token_row(a, brow, tk, h), int(eos - tk < kC ? eos - tk : kC), j0, wave, lane0);
+        while (tk < eos || tv >= 0) {
+            const bool has_k = tk < eos, has_v = tv >= 0;
+            const int L = has_k ? int(eos - tk < kC ? eos - tk : kC) : 0;
+            lds_barrier();  // B0: z and all tiles of chunk tv visible
+            // Lane indices made opaque per period, so that the LDS addresses
+            // derived from them are recomputed here rather than held in
+            // registers across the whole loop.
+            int r = r0, g = g0, lane = lane0;
+            __asm__ volatile("" : "+v"(r), "+v"(g), "+v"(lane));
+            f32x4 X[4], OT[4];  // per period (not carried across periods)
+            if (has_v) value_xo(lds, lane_offsets(r, g), S, X, OT, lv, wave, r, g);
+            lds_barrier();  // B1: decay products visible; Et, Qt and z of chunk tv consumed
+            int step = 0;
+            if (has_k) step = chunk_step(lds, L);
+            if (has_v) {
+                const rsrc_t ro = make_rsrc(o + token_row(a, brow, tv, h) * dv + j0,
+                                            uint32_t(lv - 1) * uint32_t(ostride) + kDVT * 2);
+                value_solve(lds, lane_offsets(r, g), S, X, OT, kbuf ^ 1, ro, ostride, lv, wave, r, g);
+            }
+            if (has_k) {
+                prep_z(lds, V, wave, lane);
+                const int64_t tn = tk + step;  // v, w of the next chunk
+                if (tn < eos)
+                    load_rawv(V, a, token_row(a, brow, tn, h), int(eos - tn < kC ? eos - tn : kC), j0, wave, lane);
+            }
+            lds_barrier();  // B2: tiles of chunk tk visible
+            if (has_k) {
+                const LaneOffs lk = lane_offsets(r, g);
+                if (wave == kTWave)
+                    t_work(lds, lk, kbuf, r, g);
+                else
+                    ap_work(lds, lk, kbuf, wave, r, g);
+            }
+            tv = has_k ? tk : -1;
+            lv = step;
+            tk = has_k ? tk + step : eos;
+            kbuf ^= 1;
         }
-        __syncthreads();  // region 1 operands consumed
+        if (a.final_state) {
+            const rsrc_t rs = make_rsrc(a.final_state + sbase, sbytes);
 #pragma unroll
-        for (int k = 0; k < 3; ++k)
-            if (k < nitems) ap_store(lds, items[k], r, g, acc[k]);
-        __syncthreads();  // Aneg, P, AdT visible
-
-        // ---- T_II = (I + A_II)^-1, FP32 right-looking substitution; lane group
-        // g takes diagonal block g, lane r its column r
-        if (wave == kTWave) {
-            const float4* adt = reinterpret_cast<const float4*>(lds + kOffAdT) + g * 64;  // column j: adt[4 j ..]
-            float t[16];
+            for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) t[i] = i == r ? 1.f : 0.f;
-            float4 cur[4], nxt[4];
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) cur[q4] = adt[q4];
-#pragma unroll
-            for (int j = 0; j < 15; ++j) {
-                if (j < 14)
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) nxt[q4] = adt[4 * (j + 1) + q4];
-                const float col[16] = {cur[0].x, cur[0].y, cur[0].z, cur[0].w, cur[1].x, cur[1].y, cur[1].z, cur[1].w,
-                                       cur[2].x, cur[2].y, cur[2].z, cur[2].w, cur[3].x, cur[3].y, cur[3].z, cur[3].w};
-#pragma unroll
-                for (int i = j + 1; i < 16; ++i) t[i] -= col[i] * t[j];
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) cur[q4] = nxt[q4];
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            float* T = reinterpret_cast<float*>(lds + kOffT) + g * 256;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) T[i * 16 + r] = t[i];
+                for (int i = 0; i < 4; ++i)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(S[cb][i]), rs, s_vo,
+                                                          (16 * cb + i) * int(dv) * 4, 0);
         }
-
-        // ---- X = Z - Et S (direct) and (Qt S)^T
-        f32x4 X[4], OT[4];
-        bf16x8 sb[4];
-        if (vwave) {
+    } else {
+        RawK R;
+        if (tk < eos) {
+            const RawSrc src = raw_src(a, token_row(a, brow, tk, h), int(eos - tk < kC ? eos - tk : kC));
 #pragma unroll
-            for (int s = 0; s < 4; ++s) sb[s] = pack_acc_pair(S[2 * s], S[2 * s + 1]);
-#pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                f32x4 xe = f32x4{0.f, 0.f, 0.f, 0.f}, xq = xe;
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    xe = mfma_bf16(ld_s128(lds, lo_, kOffEt, I, s), sb[s], xe);
-                    xq = mfma_bf16(sb[s], ld_s128(lds, lo_, kOffQt, I, s), xq);
-                }
-                const float4 z = *reinterpret_cast<const float4*>(zcol + 16 * I + 4 * g);
-                X[I] = f32x4{z.x - xe[0], z.y - xe[1], z.z - xe[2], z.w - xe[3]};
-                OT[I] = xq;
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            for (int t = 0; t < 4; ++t) load_token(R, src, t, kw, lane0);
         }
-        __syncthreads();  // T visible
-
-        if (vwave) {
-            // ---- blocked solve: R_I = X_I - sum_J A_IJ U_J ; U_I = T_II R_I
-            f32x4 U[4];
-            bf16x8 ub[2];
-            const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                f32x4 R_ = X[I];
-                if (I >= 1) R_ = mfma_bf16(ld_s64(lds, lo_, kOffAneg, I, 0), ub[0], R_);
-                if (I >= 3) R_ = mfma_bf16(ld_s64(lds, lo_, kOffAneg, I, 1), ub[1], R_);
-                const float4 tr = *reinterpret_cast<const float4*>(lds + kOffT + ((I * 16 + r) * 16 + 4 * g) * 4);
-                f32x4 u = zero4;
-                u = mfma_f32(tr.x, R_[0], u);
-                u = mfma_f32(tr.y, R_[1], u);
-                u = mfma_f32(tr.z, R_[2], u);
-                u = mfma_f32(tr.w, R_[3], u);
-                U[I] = u;
-                // operands over tokens 0..31 and 32..63; blocks not solved yet stay zero
-                if (I == 0) ub[0] = pack_acc_pair(U[0], zero4);
-                if (I == 1) ub[0] = pack_acc_pair(U[0], U[1]);
-                if (I == 2) ub[1] = pack_acc_pair(U[2], zero4);
-                if (I == 3) ub[1] = pack_acc_pair(U[2], U[3]);
+        while (tk < eos || tv >= 0) {
+            const bool has_k = tk < eos;
+            const int L = has_k ? int(eos - tk < kC ? eos - tk : kC) : 0;
+            lds_barrier();  // B0
+            int r = r0, g = g0, lane = lane0;  // opaque per period (see the value loop)
+            __asm__ volatile("" : "+v"(r), "+v"(g), "+v"(lane));
+            float ex[8];  // per period
+            if (has_k) decay_pass1(lds, R, ex, L, kw, lane);
+            lds_barrier();  // B1
+            int step = 0;
+            if (has_k) {
+                step = chunk_step(lds, L);
+                prep_tiles(lds, R, ex, step, kbuf, kw, lane);
             }
-
-            // ---- O^T = (Qt S)^T + U^T P^T; lane holds token 16 I + r, columns 4g..4g+3
-            const uint32_t ostride = uint32_t(a.H) * uint32_t(dv) * 2;
-            const rsrc_t ro = make_rsrc(o + ((brow * a.T + t0) * a.H + h) * dv + j0, uint32_t(kC) * ostride);
-            const int o_vo = r * int(ostride) + (16 * wave + 4 * g) * 2;
+            lds_barrier();  // B2
+            // The next chunk's inputs, issued while the value waves form its
+            // matrix blocks; they stay in flight until decay_pass1.
+            const int64_t tn = tk + step;
+            if (has_k && tn < eos) {
+                const RawSrc nxt = raw_src(a, token_row(a, brow, tn, h), int(eos - tn < kC ? eos - tn : kC));
 #pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                f32x4 acc2 = OT[I];
-                acc2 = mfma_bf16(ub[0], ld_s64(lds, lo_, kOffP, I, 0), acc2);
-                if (I >= 2) acc2 = mfma_bf16(ub[1], ld_s64(lds, lo_, kOffP, I, 1), acc2);
-                if (16 * I + r < L) {
-                    u32x2 pk;
-                    pk[0] = pack2(acc2[0], acc2[1]);
-                    pk[1] = pack2(acc2[2], acc2[3]);
-                    __builtin_amdgcn_raw_buffer_store_b64(pk, ro, o_vo, 16 * I * int(ostride), 0);
-                }
+                for (int t = 0; t < 4; ++t) load_token(R, nxt, t, kw, lane);
             }
-
-            // ---- S <- Diag(gamma) S + Kb^T U
-#pragma unroll
-            for (int cb = 0; cb < 8; ++cb) {
-                const float4 gm = *reinterpret_cast<const float4*>(gam + 16 * cb + 4 * g);
-                f32x4 acc3 = f32x4{S[cb][0] * gm.x, S[cb][1] * gm.y, S[cb][2] * gm.z, S[cb][3] * gm.w};
-                acc3 = mfma_bf16(ld_s64(lds, lo_, kOffKbT, cb, 0), ub[0], acc3);
-                acc3 = mfma_bf16(ld_s64(lds, lo_, kOffKbT, cb, 1), ub[1], acc3);
-                S[cb] = acc3;
-            }
+            tv = has_k ? tk : -1;
+            tk = has_k ? tk + step : eos;
+            kbuf ^= 1;
         }
-        __syncthreads();  // all reads of this chunk's tiles done
     }
 
-    if (vwave && a.final_state) {
-        const rsrc_t rs = make_rsrc(a.final_state + sbase, sbytes);
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(S[cb][i]), rs, s_vo,
-                                                      (16 * cb + i) * int(dv) * 4, 0);
-    }
-}
-
-template <int VW>
-hipError_t launch_vw(const ChunkArgs& a, hipStream_t stream)
-{
-    constexpr int DVT = 16 * VW;
-    constexpr int kBytes = Lds<DVT>::kBytes;
-    // Allow the kernel its > 64 KiB of dynamic LDS (thread-safe one-time call).
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fwd_mfma_kernel<VW>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kBytes);
-    if (attr != hipSuccess) return attr;
-    const int ntiles = a.dv / DVT;
-    const int64_t chains = int64_t(a.N) * a.H;
-    const int64_t blocks = (chains + 7) / 8 * 8 * ntiles;
-    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(chunk_fwd_mfma_kernel<VW>, dim3(unsigned(blocks)), dim3(kThreads), kBytes, stream, a, ntiles,
-                       int(chains));
-    return hipGetLastError();
 }
 
 }  // namespace
 
 bool chunk_fwd_mfma_supported(const ChunkArgs& a, bool bf16)
 {
-    return bf16 && a.dk == kDK && a.dv % 64 == 0;
+    return bf16 && a.dk == kDK && a.dv % kDVT == 0;
 }
 
 hipError_t launch_chunk_fwd_mfma(const ChunkArgs& a, hipStream_t stream)
 {
-    // 128-column tiles carry the key-side work once per chain; 64-column tiles
-    // spread a chain over two workgroups when chains alone do not fill the chip.
+    // Allow the kernel its > 64 KiB of dynamic LDS (thread-safe one-time call).
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fwd_mfma_kernel),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (attr != hipSuccess) return attr;
+    const int ntiles = a.dv / kDVT;
     const int64_t chains = int64_t(a.N) * a.H;
-    if (a.dv % 128 == 0 && chains >= a.cus) return launch_vw<8>(a, stream);
-    return launch_vw<4>(a, stream);
+    const int64_t blocks = (chains + 7) / 8 * 8 * ntiles;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(chunk_fwd_mfma_kernel, dim3(unsigned(blocks)), dim3(kThreads), kLdsBytes, stream, a, ntiles,
+                       int(chains));
+    return hipGetLastError();
 }
 
 }  // namespace gdn2

@@ -140,11 +140,13 @@ def test_bitwise_deterministic():
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("case", ["no_decay", "slow_decay", "zero_alpha", "erase_0_2"])
+@pytest.mark.parametrize("case", ["no_decay", "slow_decay", "zero_alpha", "steep_3", "steep_4", "erase_0_2"])
 def test_gate_edges(dtype, d, case):
     """alpha = 1 (state carried across every chunk), slow decay sigmoid(N(6, 0.5)),
-    alpha = 0 in some channels (acts as 2^-15), erase gate widened to [0, 2].
-    d = 128 with bf16 runs the matrix-core kernel, the rest the generic one."""
+    alpha = 0 in some channels (acts as 2^-15), one channel decaying by 2^-3 or
+    2^-4 per token (a 64-token chunk would span more than 2^-120 there), erase
+    gate widened to [0, 2].  d = 128 with bf16 runs the matrix-core kernel, the
+    rest the generic one."""
     x = W.make("batched_bf16", seed=11, B=1, T=257, H=2, dk=d, dv=d, dtype=dtype)
     rng = np.random.default_rng(12)
     if case == "no_decay":
@@ -153,6 +155,8 @@ def test_gate_edges(dtype, d, case):
         x["alpha"][:] = (1.0 / (1.0 + np.exp(-rng.normal(6.0, 0.5, x["alpha"].shape)))).astype(np.float32)
     elif case == "zero_alpha":
         x["alpha"][..., ::7] = 0.0
+    elif case in ("steep_3", "steep_4"):
+        x["alpha"][..., 5] = 2.0 ** -int(case[-1])
     elif case == "erase_0_2":
         b = 2.0 / (1.0 + np.exp(-rng.standard_normal(x["b"].shape)))
         x["b"] = W.round_bf16(b.astype(np.float32)) if dtype == "bf16" else b.astype(np.float32)
