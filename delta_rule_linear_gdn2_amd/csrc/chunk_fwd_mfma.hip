@@ -692,7 +692,6 @@ __device__ __forceinline__ void value_xo(const unsigned char* lds, const LaneOff
         X[I] = f32x4{t0 + 0 < lv ? z.x - xe[0] : 0.f, t0 + 1 < lv ? z.y - xe[1] : 0.f,
                      t0 + 2 < lv ? z.z - xe[2] : 0.f, t0 + 3 < lv ? z.w - xe[3] : 0.f};
         OT[I] = xq;
-        __builtin_amdgcn_sched_barrier(0);  // one row block's operands in flight at a time
     }
 }
 
