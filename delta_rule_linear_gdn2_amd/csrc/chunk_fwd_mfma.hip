@@ -66,35 +66,40 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kValueWaves = 4;    // waves 0..3: 16 value columns each
 constexpr int kTWave = 3;         // diagonal blocks of A and their inverses (a value wave)
 constexpr float kAlphaMin = 0x1p-15f;
-constexpr float kRangeMin = 0x1p-120f;
+constexpr float kRangeMin = 0x1p-64f;
 
 // ---- LDS map (bytes) -------------------------------------------------------
-constexpr int kOffEt = 0;          // [64][128] bf16, single
-constexpr int kOffQt = 16384;      // [64][128] bf16, single
-constexpr int kOffKt = 32768;      // [64][128] bf16, single
-constexpr int kOffKbT = 49152;     // [2][128][64] bf16
-constexpr int kOffAneg = 81920;    // [2][64][64] bf16 (-A below the diagonal blocks)
-constexpr int kOffP = 98304;       // [2][64][64] bf16
+constexpr int kOffEt = 0;          // [2][64][128] bf16
+constexpr int kOffQt = 32768;      // [2][64][128] bf16
+constexpr int kOffKt = 65536;      // [64][128] bf16
+constexpr int kOffKbT = 81920;     // [128][64] bf16
+constexpr int kOffAneg = 98304;    // [64][64] bf16 (-A below the diagonal blocks)
+constexpr int kOffP = 106496;      // [64][64] bf16
 constexpr int kT16 = 20;            // floats per row of a 16 x 16 FP32 block (padded)
 constexpr int kTBlk = 16 * kT16 + 16;  // floats per padded block (the next block shifts by 16 banks)
-constexpr int kOffT = 114688;      // [2][4][kTBlk] f32, T_II row major
-constexpr int kOffGam = kOffT + 2 * 4 * kTBlk * 4;  // [2][128] f32 (chunk decay per channel)
-constexpr int kOffPh = kOffGam + 1024;  // [8][128] f32: decay over tokens 16 j .. 16 j + 15 (rows j < 4),
-                                        // over 0..7 (row 4), per-block channel minima (row 5)
-constexpr int kOffAd = kOffPh + 4096;   // [4][kTBlk] f32, diagonal blocks of A, column major
-constexpr int kOffZs = kOffAd + 4 * kTBlk * 4;  // [64 columns][kZsStride] f32, z = w v
-constexpr int kZsStride = 68;
-constexpr int kLdsBytes = kOffZs + kDVT * kZsStride * 4;
+constexpr int kOffT = 114688;      // [4][kTBlk] f32, T_II row major
+constexpr int kOffAd = kOffT + 4 * kTBlk * 4;   // [4][kTBlk] f32, diagonal blocks of A, column major
+constexpr int kOffGam = kOffAd + 4 * kTBlk * 4; // [2][128] f32 (chunk decay per channel)
+constexpr int kOffPh = kOffGam + 1024;  // [7][128] f32: decay over tokens 16 j .. 16 j + 15 (rows j < 4),
+                                        // over 0..7 (row 4), per-block channel minima (row 5), ones (row 6)
+constexpr int kPhOnes = 6;
+constexpr int kOffZs = kOffPh + 3584;   // per value wavefront [16 columns][64 tokens] f32 (zs_off), z = w v
+constexpr int kZsWave = 16 * 64 * 4;
+constexpr int kLdsBytes = kOffZs + kValueWaves * kZsWave;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
-static_assert(kOffP == kOffAneg + 2 * 8192 && kOffT == kOffP + 2 * 8192, "Aneg and P are cleared as one range");
+static_assert(kOffP == kOffAneg + 8192 && kOffT == kOffP + 8192, "Aneg and P are cleared as one range");
+static_assert(kOffZs % 16 == 0 && kZsWave % 16 == 0, "16-byte aligned z rows");
 
 // [64][128] bf16 tiles Et, Qt, Kt.  Channels are stored permuted within each
 // group of 32 so that the split K groups of the matrix products, channels
 // {32 s + 4 g .. + 3} U {32 s + 16 + 4 g .. + 3}, occupy the 16 contiguous bytes
 // at position 32 s + 8 g; the 16-byte granules are XOR-swizzled by a linear
-// map of the low four row bits, under which the prep stores (two 8-byte
-// pieces per lane) and the operand reads (16 rows at one granule column) are
-// free of bank conflicts.
+// map of the low four row bits.  Measured on gfx950: 16-byte reads of 16 rows
+// at one granule column stay free of bank conflicts only when neighbouring
+// lanes (rows 2j, 2j + 1) land on granules that differ in bit 0 alone, and the
+// prep stores (two 8-byte pieces per lane, rows 4 apart across a quad) need
+// the images of rows 4 and 8 to stay apart; the map row ^ (bit 2 ^ bit 3)
+// meets both.
 __device__ __forceinline__ int chan_pos(int ch)
 {
     return (ch & ~31) | ((ch & 12) << 1) | ((ch & 16) >> 2) | (ch & 3);
@@ -102,7 +107,7 @@ __device__ __forceinline__ int chan_pos(int ch)
 __device__ __forceinline__ int parity(int x) { return __builtin_popcount(x) & 1; }
 __device__ __forceinline__ int tile_swz(int row)
 {
-    return parity(row & 11) | (parity(row & 9) << 1) | (parity(row & 7) << 2) | (parity(row & 13) << 3);
+    return (row ^ (((row >> 2) ^ (row >> 3)) & 1)) & 15;
 }
 __device__ __forceinline__ int off_t128(int row, int pos)  // pos: permuted position
 {
@@ -124,9 +129,15 @@ __device__ __forceinline__ int off_kbt(int row, int col)
 {
     return row * 128 + ((((col >> 2) ^ kbt_swz(row)) & 15) << 3) + ((col & 3) << 1);
 }
-// Float index of (column, token) in Zs: tokens rotated by 16 per group of 16
-// columns so that the column-wise stores of z spread over the banks.
-__device__ __forceinline__ int zs_index(int col, int tok) { return col * kZsStride + ((tok + 16 * (col >> 4)) & 63); }
+
+// Byte offset of (column, token) in a value wavefront's z: the 16-byte token
+// granules XOR-swizzled by the column, so that the token-wise stores (b32, one
+// column) and the column-wise operand reads (16 columns at one granule, b128)
+// are free of bank conflicts.
+__device__ __forceinline__ int zs_off(int col, int tok)
+{
+    return col * 256 + ((((tok >> 2) ^ col) & 15) << 4) + ((tok & 3) << 2);
+}
 
 __device__ __forceinline__ uint32_t pack2(float a, float b)
 {
@@ -289,8 +300,8 @@ struct RawK {
     uint4 q[4], k[4], b[4];  // 8 bf16 channels per token
     uint4 a[4][2];           // alpha, 8 FP32 channels per token
 };
-// A value wavefront's share of v and w: wavefront w loads tokens 16 w + (l & 15),
-// columns 16 (l >> 4) .. + 15 of the tile.
+// A value wavefront's share of v and w: its own 16 columns of the tile for all
+// 64 tokens of the chunk; lane l takes token l.
 struct RawV {
     uint4 v[2], w[2];
 };
@@ -310,35 +321,39 @@ __device__ __forceinline__ RawSrc raw_src(const ChunkArgs& a, int64_t row0, int 
 {
     RawSrc s;
     s.kstride = uint32_t(a.H) * kDK * 2;
-    const uint32_t win = uint32_t(L - 1) * s.kstride + kDK * 2;
+    const uint32_t win = L > 0 ? uint32_t(L - 1) * s.kstride + kDK * 2 : 0u;  // 0: every load reads zero
     s.q = make_rsrc(static_cast<const bf16raw*>(a.q) + row0 * kDK, win);
     s.k = make_rsrc(static_cast<const bf16raw*>(a.k) + row0 * kDK, win);
     s.b = make_rsrc(static_cast<const bf16raw*>(a.b) + row0 * kDK, win);
     s.a = make_rsrc(a.alpha + row0 * kDK, 2 * win);
     return s;
 }
-// Loads this lane's token t (of four) of a chunk.
-__device__ __forceinline__ void load_token(RawK& R, const RawSrc& s, int t, int kw, int lane)
+// Loads this lane's token t (of four) of a chunk: q, k, b, and alpha.
+__device__ __forceinline__ void load_qkb(RawK& R, const RawSrc& s, int t, int kw, int lane)
 {
     const int tp = lane & 3, cg = lane >> 2;
-    const uint32_t tok = uint32_t(16 * kw + 4 * tp + t);
-    const uint32_t off = tok * s.kstride + 16 * cg;
+    const uint32_t off = uint32_t(16 * kw + 4 * tp + t) * s.kstride + 16 * cg;
     R.q[t] = ld_b128(s.q, off);
     R.k[t] = ld_b128(s.k, off);
     R.b[t] = ld_b128(s.b, off);
-    R.a[t][0] = ld_b128(s.a, 2 * tok * s.kstride + 32 * cg);
-    R.a[t][1] = ld_b128(s.a, 2 * tok * s.kstride + 32 * cg + 16);
+}
+__device__ __forceinline__ void load_alpha(RawK& R, const RawSrc& s, int t, int kw, int lane)
+{
+    const int tp = lane & 3, cg = lane >> 2;
+    const uint32_t off = 2 * uint32_t(16 * kw + 4 * tp + t) * s.kstride + 32 * cg;
+    R.a[t][0] = ld_b128(s.a, off);
+    R.a[t][1] = ld_b128(s.a, off + 16);
 }
 
 __device__ __forceinline__ void load_rawv(RawV& V, const ChunkArgs& a, int64_t row0, int L, int j0, int wave,
                                           int lane)
 {
     const uint32_t vstride = uint32_t(a.H) * uint32_t(a.dv) * 2;
-    const uint32_t win = uint32_t(L - 1) * vstride + kDVT * 2;
-    const int64_t base = row0 * a.dv + j0;
+    const uint32_t win = L > 0 ? uint32_t(L - 1) * vstride + 32u : 0u;
+    const int64_t base = row0 * a.dv + j0 + 16 * wave;
     const rsrc_t rv = make_rsrc(static_cast<const bf16raw*>(a.v) + base, win);
     const rsrc_t rw = make_rsrc(static_cast<const bf16raw*>(a.w) + base, win);
-    const uint32_t off = uint32_t(16 * wave + (lane & 15)) * vstride + 32 * (lane >> 4);
+    const uint32_t off = uint32_t(lane) * vstride;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         V.v[u] = ld_b128(rv, off + 16 * u);
@@ -346,8 +361,8 @@ __device__ __forceinline__ void load_rawv(RawV& V, const ChunkArgs& a, int64_t r
     }
 }
 
-// Alpha of channel c of token t of this lane (as prepared by decay_pass1).
-__device__ __forceinline__ float alpha_at(const RawK& R, int t, int c)
+// Alpha of channel c of token t of this lane, as loaded.
+__device__ __forceinline__ float raw_alpha(const RawK& R, int t, int c)
 {
     const uint4 x = R.a[t][c >> 2];
     return __uint_as_float((c & 3) == 0 ? x.x : (c & 3) == 1 ? x.y : (c & 3) == 2 ? x.z : x.w);
@@ -355,22 +370,25 @@ __device__ __forceinline__ float alpha_at(const RawK& R, int t, int c)
 
 // First half of the key prep: decay products along the wavefront's 16 tokens
 // (in lane, then a quad scan).  Writes the product over the 16 tokens to
-// Ph[kw] (and wavefront 0 the product over tokens 0..7 to Ph[4]); returns in
-// ex the product over the wavefront's tokens before this lane's four.
-__device__ __forceinline__ void decay_pass1(unsigned char* lds, RawK& R, float* ex, int L, int kw, int lane)
+// Ph[kw] (and wavefront 0 the product over tokens 0..7 to Ph[4]); returns the
+// clamped alpha in al and in ex the product over the wavefront's tokens before this lane's four.
+__device__ __forceinline__ void decay_pass1(unsigned char* lds, const RawK& R, float (*al)[8], float* ex, int L,
+                                            int kw, int lane)
 {
     const int tp = lane & 3, cg = lane >> 2;
-    // alpha clamped to [2^-15, 1], and 1 past the sequence end, written back
+    // alpha clamped to [2^-15, 1], and 1 past the sequence end
+    if (L == kC) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const bool live = 16 * kw + 4 * tp + t < L;
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            uint4& x = R.a[t][h];
-            x.x = __float_as_uint(live ? __builtin_amdgcn_fmed3f(__uint_as_float(x.x), kAlphaMin, 1.0f) : 1.0f);
-            x.y = __float_as_uint(live ? __builtin_amdgcn_fmed3f(__uint_as_float(x.y), kAlphaMin, 1.0f) : 1.0f);
-            x.z = __float_as_uint(live ? __builtin_amdgcn_fmed3f(__uint_as_float(x.z), kAlphaMin, 1.0f) : 1.0f);
-            x.w = __float_as_uint(live ? __builtin_amdgcn_fmed3f(__uint_as_float(x.w), kAlphaMin, 1.0f) : 1.0f);
+            for (int c = 0; c < 8; ++c) al[t][c] = __builtin_amdgcn_fmed3f(raw_alpha(R, t, c), kAlphaMin, 1.0f);
+    } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const bool live = 16 * kw + 4 * tp + t < L;
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                al[t][c] = live ? __builtin_amdgcn_fmed3f(raw_alpha(R, t, c), kAlphaMin, 1.0f) : 1.0f;
         }
     }
     float inc[8];
@@ -378,7 +396,7 @@ __device__ __forceinline__ void decay_pass1(unsigned char* lds, RawK& R, float* 
     for (int c = 0; c < 8; ++c) {
         float p = 1.0f;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) p *= alpha_at(R, t, c);
+        for (int t = 0; t < 4; ++t) p *= al[t][c];
         const float y = dpp<kQuadPrev>(p);
         const float x1 = tp >= 1 ? p * y : p;
         const float z = dpp<kQuadPrev2>(x1);
@@ -405,9 +423,9 @@ __device__ __forceinline__ void decay_pass1(unsigned char* lds, RawK& R, float* 
 // Chunk length (identical in every wavefront: the same four values in the
 // same order): with m_j the smallest decay over block j (tokens 16 j ..
 // 16 j + 15) among all channels, the longest of 64, 32, 16 tokens for which
-// m_0 m_1 ... stays >= 2^-120, else 8; at most L.  The product of the minima
+// m_0 m_1 ... stays >= 2^-64, else 8; at most L.  The product of the minima
 // bounds every channel's decay from below, so all factors of the chunk stay
-// within [2^-120, 2^120].
+// within [2^-64, 2^64].
 __device__ __forceinline__ int chunk_step(const unsigned char* lds, int L)
 {
     const float* pm = reinterpret_cast<const float*>(lds + kOffPh) + 5 * 128;
@@ -416,146 +434,134 @@ __device__ __forceinline__ int chunk_step(const unsigned char* lds, int L)
     return leff < L ? leff : L;
 }
 
-// Stores channels 8 cg .. 8 cg + 7 of one row of a [64][128] tile: two
-// 8-byte pieces at their permuted positions.
-__device__ __forceinline__ void st_row8(unsigned char* lds, int base, int row, int cg, uint4 v)
+// Store offsets of the key prep for one lane (tokens tok0 .. tok0 + 3 with
+// tok0 a multiple of 4, channels 8 cg .. 8 cg + 7).  Both swizzles are linear
+// in the row bits over GF(2), so row tok0 + t of a [64][128] tile lies at
+// (base ^ (tile_swz(t) << 4)) + 256 t and channel row 8 cg + c of Kb^T at
+// (base ^ (kbt_swz(c) << 3)) + 128 c: the XOR only touches the granule bits.
+struct PrepOffs {
+    int t128[2];  // row tok0 of a [64][128] tile, channels 8 cg .. + 3 and 8 cg + 4 .. + 7
+    int kbt;      // Kb^T buffer kbuf, channel row 8 cg, tokens tok0 .. + 3
+};
+__device__ __forceinline__ PrepOffs prep_offsets(int tok0, int cg, int kbuf)
 {
-    lds_st<uint2>(lds, base + off_t128(row, chan_pos(8 * cg)), make_uint2(v.x, v.y));
-    lds_st<uint2>(lds, base + off_t128(row, chan_pos(8 * cg + 4)), make_uint2(v.z, v.w));
+    PrepOffs o;
+    o.t128[0] = off_t128(tok0, chan_pos(8 * cg));
+    o.t128[1] = off_t128(tok0, chan_pos(8 * cg + 4));
+    o.kbt = kOffKbT + kbuf * 16384 + off_kbt(8 * cg, tok0);  // kbuf: 0 (one Kb^T buffer)
+    return o;
+}
+// Channels 8 cg .. 8 cg + 7 of row tok0 + t of the tile at byte offset tile.
+__device__ __forceinline__ void st_tok(unsigned char* lds, const PrepOffs& o, int tile, int t, uint4 v)
+{
+    const int x = tile_swz(t) << 4;
+    lds_st<uint2>(lds, tile + ((o.t128[0] ^ x) + 256 * t), make_uint2(v.x, v.y));
+    lds_st<uint2>(lds, tile + ((o.t128[1] ^ x) + 256 * t), make_uint2(v.z, v.w));
 }
 
-// Zero rows of Et, Qt, Kt and zero columns of Kb^T for the four tokens from tok0.
-__device__ __forceinline__ void zero_rows(unsigned char* lds, int kbt, int tok0, int cg)
+// Key prep of a chunk, after its decay products (decay_pass1) and length
+// (chunk_step) are known: the rows of Et, Qt (buffer ebuf) and Kt, and in kbp
+// this lane's columns of Kt^T (stored after B1, see store_kbt).  Token by
+// token, as their registers are consumed, the inputs of the next chunk are
+// loaded into R.
+//
+// A chunk cut short (step < L) ends at a multiple of 8, so each lane's four
+// tokens are all in it or all past it; lanes past it (kAllLive false) form
+// zero rows from zeroed q and k with a running decay of 1 (their own decay
+// factors are never formed).  Past the sequence end (step = L) the inputs
+// read as zero and alpha as 1, which gives zero rows as well.
+template <bool kAllLive>
+__device__ __forceinline__ void prep_tiles(unsigned char* lds, RawK& R, const RawSrc& nxt, const float (*al)[8],
+                                           const float* ex, uint32_t (*kbp)[8], int step, int ebuf, int kw, int lane)
 {
+    const int tp = lane & 3, cg = lane >> 2;
+    const int tok0 = 16 * kw + 4 * tp;
+    const bool live = kAllLive || tok0 < step;
+    // decay before this lane's tokens: blocks 0 .. kw - 1 (the row of ones
+    // stands in for the others), then the part of its own block before it
+    float cum[8];
+    {
+        const float4* p4 = reinterpret_cast<const float4*>(lds + kOffPh) + 2 * cg;  // row j: p4[32 j], p4[32 j + 1]
+        const int j0 = kw > 0 ? 0 : kPhOnes, j1 = kw > 1 ? 1 : kPhOnes, j2 = kw > 2 ? 2 : kPhOnes;
+        const float4 a0 = p4[32 * j0], b0 = p4[32 * j0 + 1], a1 = p4[32 * j1], b1 = p4[32 * j1 + 1];
+        const float4 a2 = p4[32 * j2], b2 = p4[32 * j2 + 1];
+        const float x0[8] = {a0.x, a0.y, a0.z, a0.w, b0.x, b0.y, b0.z, b0.w};
+        const float x1[8] = {a1.x, a1.y, a1.z, a1.w, b1.x, b1.y, b1.z, b1.w};
+        const float x2[8] = {a2.x, a2.y, a2.z, a2.w, b2.x, b2.y, b2.z, b2.w};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            cum[c] = x0[c] * x1[c] * x2[c] * ex[c];
+            if (!kAllLive) cum[c] = live ? cum[c] : 1.0f;
+        }
+    }
+    // 1 / (decay through token t): one reciprocal of the decay through the
+    // lane's last token, then back through alpha
+    float rc[4][8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        rc[3][c] = __builtin_amdgcn_rcpf(cum[c] * al[0][c] * al[1][c] * al[2][c] * al[3][c]);
+        rc[2][c] = rc[3][c] * al[3][c];
+        rc[1][c] = rc[2][c] * al[2][c];
+        rc[0][c] = rc[1][c] * al[1][c];
+    }
+    const PrepOffs po = prep_offsets(tok0, cg, 0);
+    const int et_base = kOffEt + ebuf * 16384, qt_base = kOffQt + ebuf * 16384;
     const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        st_row8(lds, kOffEt, tok0 + t, cg, zero);
-        st_row8(lds, kOffQt, tok0 + t, cg, zero);
-        st_row8(lds, kOffKt, tok0 + t, cg, zero);
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) lds_st<uint2>(lds, kbt + off_kbt(8 * cg + c, tok0), make_uint2(0u, 0u));
-}
-
-// Rows of Et, Qt, Kt and columns of Kb^T for this lane's four tokens, given
-// the decay before them (cum) and the chunk decay (gam).
-__device__ __forceinline__ void prep_rows(unsigned char* lds, const RawK& R, float* cum, const float* gam, int kbt,
-                                          int tok0, int cg)
-{
-    uint32_t kbp[2][8];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
+        load_alpha(R, nxt, t, kw, lane);  // alpha of token t of the next chunk (clamped copy in al)
         float q[8], k[8], b[8];
-        unpack8(R.q[t], q);
-        unpack8(R.k[t], k);
+        unpack8(kAllLive || live ? R.q[t] : zero, q);
+        unpack8(kAllLive || live ? R.k[t] : zero, k);
         unpack8(R.b[t], b);
-        float et[8], qt[8], kt[8], kb[8];
+        float et[8], qt[8], kt[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            cum[c] *= alpha_at(R, t, c);  // 1 past the sequence end (decay_pass1)
-            const float rc = __builtin_amdgcn_rcpf(cum[c]);
+            cum[c] *= al[t][c];  // 1 past the sequence end
             et[c] = b[c] * k[c] * cum[c];
             qt[c] = q[c] * cum[c];
-            kt[c] = k[c] * rc;
-            kb[c] = kt[c] * gam[c];
+            kt[c] = k[c] * rc[t][c];
         }
-        st_row8(lds, kOffEt, tok0 + t, cg, make_uint4(pack2(et[0], et[1]), pack2(et[2], et[3]),
-                                                         pack2(et[4], et[5]), pack2(et[6], et[7])));
-        st_row8(lds, kOffQt, tok0 + t, cg, make_uint4(pack2(qt[0], qt[1]), pack2(qt[2], qt[3]),
-                                                         pack2(qt[4], qt[5]), pack2(qt[6], qt[7])));
-        st_row8(lds, kOffKt, tok0 + t, cg, make_uint4(pack2(kt[0], kt[1]), pack2(kt[2], kt[3]),
-                                                         pack2(kt[4], kt[5]), pack2(kt[6], kt[7])));
+        st_tok(lds, po, et_base, t, make_uint4(pack2(et[0], et[1]), pack2(et[2], et[3]), pack2(et[4], et[5]),
+                                               pack2(et[6], et[7])));
+        st_tok(lds, po, qt_base, t, make_uint4(pack2(qt[0], qt[1]), pack2(qt[2], qt[3]), pack2(qt[4], qt[5]),
+                                               pack2(qt[6], qt[7])));
+        st_tok(lds, po, kOffKt, t, make_uint4(pack2(kt[0], kt[1]), pack2(kt[2], kt[3]), pack2(kt[4], kt[5]),
+                                              pack2(kt[6], kt[7])));
         if (t & 1) {
 #pragma unroll
-            for (int c = 0; c < 8; ++c) kbp[t >> 1][c] = pack2(__uint_as_float(kbp[t >> 1][c]), kb[c]);
+            for (int c = 0; c < 8; ++c) kbp[t >> 1][c] = pack2(__uint_as_float(kbp[t >> 1][c]), kt[c]);
         } else {
 #pragma unroll
-            for (int c = 0; c < 8; ++c) kbp[t >> 1][c] = __float_as_uint(kb[c]);
+            for (int c = 0; c < 8; ++c) kbp[t >> 1][c] = __float_as_uint(kt[c]);
         }
+        load_qkb(R, nxt, t, kw, lane);  // token t of the next chunk into the registers just consumed
         __builtin_amdgcn_sched_barrier(0);  // one token's temporaries at a time
     }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) lds_st<uint2>(lds, kbt + off_kbt(8 * cg + c, tok0), make_uint2(kbp[0][c], kbp[1][c]));
 }
 
-// Decay factors and operand rows of this lane's four tokens (wavefront not
-// entirely past the chunk); the chunk decay gamma (wavefront 4 writes it).
-__device__ __forceinline__ void prep_factors_rows(unsigned char* lds, const RawK& R, const float* ex, int step,
-                                                  int kbuf, int kw, int lane)
+// Columns of Kb^T for this lane's tokens, after B1 (the value side reads the
+// previous chunk's until then).
+__device__ __forceinline__ void store_kbt(unsigned char* lds, const uint32_t (*kbp)[8], int kw, int lane)
 {
-    const int tp = lane & 3, cg = lane >> 2;
-    const float* ph = reinterpret_cast<const float*>(lds + kOffPh) + 8 * cg;
-    const int tok0 = 16 * kw + 4 * tp;
-    const int kbt = kOffKbT + kbuf * 16384;
-    // gamma over the tokens the chunk covers; cum: decay before this lane's tokens
-    // products of blocks 0 .. nw - 1 (gamma) and 0 .. kw - 1 (prefix), as
-    // multiplications by 1 past the bound (no data-dependent loads)
-    const int nw = step <= 8 ? 0 : (step + 15) >> 4;  // 0: the chunk ends inside tokens 0..7
-    float gam[8], cum[8];
-    const float4* p4 = reinterpret_cast<const float4*>(ph);  // row j, channels 8 cg ..: p4[32 j], p4[32 j + 1]
-    const auto block = [&](int j, float* v) {
-        const float4 a = p4[32 * j], b = p4[32 * j + 1];
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    };
+    const PrepOffs po = prep_offsets(16 * kw + 4 * (lane & 3), lane >> 2, 0);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) gam[c] = cum[c] = 1.0f;
-    if (nw == 0) block(4, gam);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        if (j < nw || j < kw) {  // uniform
-            float v[8];
-            block(j, v);
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                if (j < nw) gam[c] *= v[c];
-                if (j < kw) cum[c] *= v[c];
-            }
-        }
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) cum[c] *= ex[c];
-    if (kw == 0 && tp == 0) {
-        float* gp = reinterpret_cast<float*>(lds + kOffGam) + kbuf * 128 + 8 * cg;
-        *reinterpret_cast<float4*>(gp) = make_float4(gam[0], gam[1], gam[2], gam[3]);
-        *reinterpret_cast<float4*>(gp + 4) = make_float4(gam[4], gam[5], gam[6], gam[7]);
-    }
-    // A chunk cut short (step < L) ends at a multiple of 8, so each lane's four
-    // tokens are either all in it or all past it; the lanes past it write
-    // zero rows (their decay factors are not formed).  Past the sequence end
-    // (step = L) the inputs read as zero and alpha as 1, which gives zero rows.
-    if (tok0 >= step)
-        zero_rows(lds, kbt, tok0, cg);
-    else
-        prep_rows(lds, R, cum, gam, kbt, tok0, cg);
+    for (int c = 0; c < 8; ++c)
+        lds_st<uint2>(lds, (po.kbt ^ (kbt_swz(c) << 3)) + 128 * c, make_uint2(kbp[0][c], kbp[1][c]));
 }
 
-// Second half of the key prep: decay factors and the operand tiles of this
-// lane's four tokens; the chunk decay gamma (wavefront 4 writes it).
-__device__ __forceinline__ void prep_tiles(unsigned char* lds, const RawK& R, const float* ex, int step, int kbuf,
-                                           int kw, int lane)
-{
-    const int tp = lane & 3, cg = lane >> 2;
-    const int tok0 = 16 * kw + 4 * tp;
-    const int kbt = kOffKbT + kbuf * 16384;
-    if (16 * kw >= step)  // the whole wavefront lies past the chunk
-        zero_rows(lds, kbt, tok0, cg);
-    else
-        prep_factors_rows(lds, R, ex, step, kbuf, kw, lane);
-}
-
-// z = w v of the chunk into Zs (rows past the chunk are masked when read).
+// z = w v of the chunk into this wavefront's Zs: columns 16 wave .. + 15 of
+// the tile, token lane (rows past the chunk are masked when read).
 __device__ __forceinline__ void prep_z(unsigned char* lds, const RawV& V, int wave, int lane)
 {
-    const int tok = 16 * wave + (lane & 15), cq = lane >> 4;
-    float* zs = reinterpret_cast<float*>(lds + kOffZs);
+    unsigned char* zs = lds + kOffZs + wave * kZsWave;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         float v[8], w[8];
         unpack8(V.v[u], v);
         unpack8(V.w[u], w);
 #pragma unroll
-        for (int m = 0; m < 8; ++m) zs[zs_index(16 * cq + 8 * u + m, tok)] = v[m] * w[m];
+        for (int m = 0; m < 8; ++m) lds_st<float>(zs, zs_off(8 * u + m, lane), v[m] * w[m]);
     }
 }
 
@@ -563,15 +569,15 @@ __device__ __forceinline__ void prep_z(unsigned char* lds, const RawV& V, int wa
 // D = Kt_J Row_I^T, which leaves row 16 I + r, columns 16 J + 4 g .. + 3 in
 // each lane.
 template <int KIND, int I, int J>  // KIND 0: A (rows Et), 1: P (rows Qt)
-__device__ __forceinline__ void ap_block(unsigned char* lds, const LaneOffs& o, int buf, int r, int g)
+__device__ __forceinline__ void ap_block(unsigned char* lds, const LaneOffs& o, int ebuf, int r, int g)
 {
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int rows = (KIND == 0 ? kOffEt : kOffQt) + ebuf * 16384;
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-        acc = mfma_bf16(ld_c128(lds, o, kOffKt, J, s), ld_c128(lds, o, KIND == 0 ? kOffEt : kOffQt, I, s), acc);
+    for (int s = 0; s < 4; ++s) acc = mfma_bf16(ld_c128(lds, o, kOffKt, J, s), ld_c128(lds, o, rows, I, s), acc);
     const int row = 16 * I + r, col = 16 * J + 4 * g;
     if (KIND == 0) {
-        lds_st<uint2>(lds, kOffAneg + buf * 8192 + off_rc64(row, col),
+        lds_st<uint2>(lds, kOffAneg + off_rc64(row, col),
                       make_uint2(pack2(-acc[0], -acc[1]), pack2(-acc[2], -acc[3])));
     } else {
         float p[4] = {acc[0], acc[1], acc[2], acc[3]};
@@ -579,37 +585,37 @@ __device__ __forceinline__ void ap_block(unsigned char* lds, const LaneOffs& o, 
 #pragma unroll
             for (int i = 0; i < 4; ++i) p[i] = col + i <= row ? p[i] : 0.f;
         }
-        lds_st<uint2>(lds, kOffP + buf * 8192 + off_rc64(row, col), make_uint2(pack2(p[0], p[1]), pack2(p[2], p[3])));
+        lds_st<uint2>(lds, kOffP + off_rc64(row, col), make_uint2(pack2(p[0], p[1]), pack2(p[2], p[3])));
     }
     __builtin_amdgcn_sched_barrier(0);  // one block's operands in flight at a time
 }
 
 // The six A blocks below the diagonal blocks and the ten P blocks on and below
 // them, over value wavefronts 0..2 (grouped by shared operands).
-__device__ __forceinline__ void ap_work(unsigned char* lds, const LaneOffs& o, int buf, int slot, int r, int g)
+__device__ __forceinline__ void ap_work(unsigned char* lds, const LaneOffs& o, int ebuf, int slot, int r, int g)
 {
     switch (slot) {
         case 0:
-            ap_block<1, 3, 3>(lds, o, buf, r, g);
-            ap_block<1, 3, 2>(lds, o, buf, r, g);
-            ap_block<1, 3, 1>(lds, o, buf, r, g);
-            ap_block<1, 3, 0>(lds, o, buf, r, g);
-            ap_block<0, 3, 2>(lds, o, buf, r, g);
+            ap_block<1, 3, 3>(lds, o, ebuf, r, g);
+            ap_block<1, 3, 2>(lds, o, ebuf, r, g);
+            ap_block<1, 3, 1>(lds, o, ebuf, r, g);
+            ap_block<1, 3, 0>(lds, o, ebuf, r, g);
+            ap_block<0, 3, 2>(lds, o, ebuf, r, g);
             break;
         case 1:
-            ap_block<1, 2, 2>(lds, o, buf, r, g);
-            ap_block<1, 2, 1>(lds, o, buf, r, g);
-            ap_block<1, 2, 0>(lds, o, buf, r, g);
-            ap_block<0, 3, 1>(lds, o, buf, r, g);
-            ap_block<0, 3, 0>(lds, o, buf, r, g);
+            ap_block<1, 2, 2>(lds, o, ebuf, r, g);
+            ap_block<1, 2, 1>(lds, o, ebuf, r, g);
+            ap_block<1, 2, 0>(lds, o, ebuf, r, g);
+            ap_block<0, 3, 1>(lds, o, ebuf, r, g);
+            ap_block<0, 3, 0>(lds, o, ebuf, r, g);
             break;
         default:
-            ap_block<1, 1, 1>(lds, o, buf, r, g);
-            ap_block<1, 1, 0>(lds, o, buf, r, g);
-            ap_block<1, 0, 0>(lds, o, buf, r, g);
-            ap_block<0, 2, 1>(lds, o, buf, r, g);
-            ap_block<0, 2, 0>(lds, o, buf, r, g);
-            ap_block<0, 1, 0>(lds, o, buf, r, g);
+            ap_block<1, 1, 1>(lds, o, ebuf, r, g);
+            ap_block<1, 1, 0>(lds, o, ebuf, r, g);
+            ap_block<1, 0, 0>(lds, o, ebuf, r, g);
+            ap_block<0, 2, 1>(lds, o, ebuf, r, g);
+            ap_block<0, 2, 0>(lds, o, ebuf, r, g);
+            ap_block<0, 1, 0>(lds, o, ebuf, r, g);
             break;
     }
 }
@@ -617,14 +623,14 @@ __device__ __forceinline__ void ap_work(unsigned char* lds, const LaneOffs& o, i
 // Wavefront kTWave: the diagonal blocks A_II (strictly lower, FP32) and
 // T_II = (I + A_II)^-1 by forward substitution; lane group g takes block g,
 // lane r its column r.
-__device__ __forceinline__ void t_work(unsigned char* lds, const LaneOffs& o, int buf, int r, int g)
+__device__ __forceinline__ void t_work(unsigned char* lds, const LaneOffs& o, int ebuf, int r, int g)
 {
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-            acc = mfma_bf16(ld_c128(lds, o, kOffEt, I, s), ld_c128(lds, o, kOffKt, I, s), acc);
+            acc = mfma_bf16(ld_c128(lds, o, kOffEt + ebuf * 16384, I, s), ld_c128(lds, o, kOffKt, I, s), acc);
         // acc[i] = A_II[4g + i][r]: column r, rows 4g..4g+3, strictly lower part
         float4 v;
         v.x = 4 * g + 0 > r ? acc[0] : 0.f;
@@ -665,29 +671,44 @@ __device__ __forceinline__ void t_work(unsigned char* lds, const LaneOffs& o, in
         }
         __asm__ volatile("" ::: "memory");  // two columns ahead, no further
     }
-    float* T = reinterpret_cast<float*>(lds + kOffT) + (buf * 4 + g) * kTBlk;
+    float* T = reinterpret_cast<float*>(lds + kOffT) + g * kTBlk;
 #pragma unroll
     for (int i = 0; i < 16; ++i) T[i * kT16 + r] = t[i];
+}
+
+// Chunk decay gamma per channel (the decay through the chunk's last token)
+// into buffer buf, from the decay products: blocks 0 .. nw - 1, or tokens
+// 0..7 (row 4) when the chunk ends inside them.  One wavefront, two channels
+// per lane.
+__device__ __forceinline__ void value_gamma(unsigned char* lds, int step, int buf, int lane)
+{
+    const float2* ph = reinterpret_cast<const float2*>(lds + kOffPh) + lane;  // row j: ph[64 j]
+    const int nw = step <= 8 ? 0 : (step + 15) >> 4;
+    const int j1 = nw > 1 ? 1 : kPhOnes, j2 = nw > 2 ? 2 : kPhOnes, j3 = nw > 3 ? 3 : kPhOnes;
+    const float2 x0 = ph[64 * (nw == 0 ? 4 : 0)], x1 = ph[64 * j1], x2 = ph[64 * j2], x3 = ph[64 * j3];
+    reinterpret_cast<float2*>(lds + kOffGam)[buf * 64 + lane] =
+        make_float2(x0.x * x1.x * x2.x * x3.x, x0.y * x1.y * x2.y * x3.y);
 }
 
 // Value wavefront, chunk of lv tokens: X = Z - Et S (direct, rows past the
 // chunk zero) and OT = (Qt S)^T.
 __device__ __forceinline__ void value_xo(const unsigned char* lds, const LaneOffs& o, const f32x4* S, f32x4* X,
-                                         f32x4* OT, int lv, int wave, int r, int g)
+                                         f32x4* OT, int lv, int ebuf, int wave, int r, int g)
 {
     bf16x8 sb[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) sb[s] = pack_acc_pair(S[2 * s], S[2 * s + 1]);
-    const float* zs = reinterpret_cast<const float*>(lds + kOffZs);
+    const unsigned char* zs = lds + kOffZs + wave * kZsWave;
+    const int et = kOffEt + ebuf * 16384, qt = kOffQt + ebuf * 16384;
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
         f32x4 xe = f32x4{0.f, 0.f, 0.f, 0.f}, xq = xe;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            xe = mfma_bf16(ld_c128(lds, o, kOffEt, I, s), sb[s], xe);
-            xq = mfma_bf16(sb[s], ld_c128(lds, o, kOffQt, I, s), xq);
+            xe = mfma_bf16(ld_c128(lds, o, et, I, s), sb[s], xe);
+            xq = mfma_bf16(sb[s], ld_c128(lds, o, qt, I, s), xq);
         }
-        const float4 z = *reinterpret_cast<const float4*>(zs + zs_index(16 * wave + r, 16 * I + 4 * g));
+        const float4 z = lds_ld<float4>(zs, zs_off(r, 16 * I + 4 * g));
         const int t0 = 16 * I + 4 * g;
         X[I] = f32x4{t0 + 0 < lv ? z.x - xe[0] : 0.f, t0 + 1 < lv ? z.y - xe[1] : 0.f,
                      t0 + 2 < lv ? z.z - xe[2] : 0.f, t0 + 3 < lv ? z.w - xe[3] : 0.f};
@@ -696,13 +717,12 @@ __device__ __forceinline__ void value_xo(const unsigned char* lds, const LaneOff
 }
 
 // Value wavefront, rest of the chunk: blocked solve, output rows and state
-// update, from the tiles of buffer vbuf.
+// update (chunk decay from buffer vbuf).
 __device__ __forceinline__ void value_solve(const unsigned char* lds, const LaneOffs& o, f32x4* S, const f32x4* X,
                                             const f32x4* OT, int vbuf, rsrc_t ro, int ostride, int lv, int wave, int r,
                                             int g)
 {
-    const int aneg = kOffAneg + vbuf * 8192, pb = kOffP + vbuf * 8192;
-    const int tb = kOffT + vbuf * 4 * kTBlk * 4, kbt = kOffKbT + vbuf * 16384;
+    const int aneg = kOffAneg, pb = kOffP, tb = kOffT, kbt = kOffKbT;
     // ---- blocked solve: R_I = X_I - sum_J A_IJ U_J ; U_I = T_II R_I
     f32x4 U[4];
     bf16x8 ub[2];
@@ -740,15 +760,15 @@ __device__ __forceinline__ void value_solve(const unsigned char* lds, const Lane
         }
         __builtin_amdgcn_sched_barrier(0);
     }
-    // ---- S <- Diag(gamma) S + Kb^T U
+    // ---- S <- Diag(gamma) (S + Kt^T U)  (= Diag(gamma) S + Kb^T U with Kb = Kt gamma)
     const float* gam = reinterpret_cast<const float*>(lds + kOffGam) + vbuf * 128;
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) {
         const float4 gm = *reinterpret_cast<const float4*>(gam + 16 * cb + 4 * g);
-        f32x4 acc3 = f32x4{S[cb][0] * gm.x, S[cb][1] * gm.y, S[cb][2] * gm.z, S[cb][3] * gm.w};
+        f32x4 acc3 = S[cb];
         acc3 = mfma_bf16(ld_kbt(lds, o, kbt, cb, 0), ub[0], acc3);
         acc3 = mfma_bf16(ld_kbt(lds, o, kbt, cb, 1), ub[1], acc3);
-        S[cb] = acc3;
+        S[cb] = f32x4{acc3[0] * gm.x, acc3[1] * gm.y, acc3[2] * gm.z, acc3[3] * gm.w};
         if (cb & 1) __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -777,20 +797,20 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
     sequence_bounds(a.cu_seqlens, n, a.T, bos, eos, brow);
 
     // The blocks the solve and the output read as zero (A on the diagonal, P
-    // right of it) are never written: clear Aneg and P, both buffers, once.
+    // right of it) are never written: clear Aneg and P once.
     {
         uint4* z = reinterpret_cast<uint4*>(lds + kOffAneg);
         const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) z[tid + i * kThreads] = zero;  // 4 x 512 x 16 = 32768 bytes
+        for (int i = 0; i < 2; ++i) z[tid + i * kThreads] = zero;  // 2 x 512 x 16 = 16384 bytes
     }
 
     // Both roles run the same sequence of periods (the loop control is
-    // computed identically) and meet at the same three barriers per period;
+    // computed identically) and meet at the same two barriers per period;
     // separate loops keep each role's registers apart.
     int64_t tk = bos;  // chunk the key side prepares this period
     int64_t tv = -1;   // chunk the value side finishes this period (< 0: none)
-    int kbuf = 0;      // buffer the key side writes this period; the value side reads kbuf ^ 1
+    int kbuf = 0;      // Et, Qt, gamma buffer the key side writes this period; the value side reads kbuf ^ 1
     if (vwave) {
         // state slice of a value wavefront: channels 16 cb + 4 g + i, column j0 + 16 wave + r
         f32x4 S[8];
@@ -817,29 +837,28 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
         while (tk < eos || tv >= 0) {
             const bool has_k = tk < eos, has_v = tv >= 0;
             const int L = has_k ? int(eos - tk < kC ? eos - tk : kC) : 0;
-            lds_barrier();  // B0: z and all tiles of chunk tv visible
+            lds_barrier();  // B0: tiles of chunk tv, decay products of chunk tk visible
             // Lane indices made opaque per period, so that the LDS addresses
             // derived from them are recomputed here rather than held in
             // registers across the whole loop.
             int r = r0, g = g0, lane = lane0;
             __asm__ volatile("" : "+v"(r), "+v"(g), "+v"(lane));
-            f32x4 X[4], OT[4];  // per period (not carried across periods)
-            if (has_v) value_xo(lds, lane_offsets(r, g), S, X, OT, lv, wave, r, g);
-            lds_barrier();  // B1: decay products visible; Et, Qt and z of chunk tv consumed
-            int step = 0;
-            if (has_k) step = chunk_step(lds, L);
+            const int step = has_k ? chunk_step(lds, L) : 0;
+            if (has_k && wave == 0) value_gamma(lds, step, kbuf, lane);  // read by the next period's update
             if (has_v) {
+                f32x4 X[4], OT[4];
+                value_xo(lds, lane_offsets(r, g), S, X, OT, lv, kbuf ^ 1, wave, r, g);
                 const rsrc_t ro = make_rsrc(o + token_row(a, brow, tv, h) * dv + j0,
                                             uint32_t(lv - 1) * uint32_t(ostride) + kDVT * 2);
                 value_solve(lds, lane_offsets(r, g), S, X, OT, kbuf ^ 1, ro, ostride, lv, wave, r, g);
             }
+            const int64_t tn = tk + step;
             if (has_k) {
-                prep_z(lds, V, wave, lane);
-                const int64_t tn = tk + step;  // v, w of the next chunk
+                prep_z(lds, V, wave, lane);  // after value_xo has read this wavefront's z of chunk tv
                 if (tn < eos)
                     load_rawv(V, a, token_row(a, brow, tn, h), int(eos - tn < kC ? eos - tn : kC), j0, wave, lane);
             }
-            lds_barrier();  // B2: tiles of chunk tk visible
+            lds_barrier();  // B1: tiles of chunk tk visible; A, P, T and Kb^T of chunk tv consumed
             if (has_k) {
                 const LaneOffs lk = lane_offsets(r, g);
                 if (wave == kTWave)
@@ -849,7 +868,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
             }
             tv = has_k ? tk : -1;
             lv = step;
-            tk = has_k ? tk + step : eos;
+            tk = has_k ? tn : eos;
             kbuf ^= 1;
         }
         if (a.final_state) {
@@ -862,11 +881,26 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
                                                           (16 * cb + i) * int(dv) * 4, 0);
         }
     } else {
+        // Key side.  The decay products of a chunk are formed after B1 of the
+        // period before the one that prepares it, so its length is known at
+        // B0; its tiles are formed between B0 and B1 (Et and Qt into the
+        // buffer the value side does not read this period) and its Kb^T
+        // columns after B1.  The next chunk's inputs are loaded during the
+        // prep and stay in flight until its decay products and prep.
+        if (kw == 0) {  // the row of ones of the decay products
+            const float4 one = make_float4(1.f, 1.f, 1.f, 1.f);
+            if (lane0 < 32) reinterpret_cast<float4*>(lds + kOffPh)[kPhOnes * 32 + lane0] = one;
+        }
         RawK R;
+        float al[4][8], ex[8];  // clamped alpha and decay products of chunk tk
         if (tk < eos) {
-            const RawSrc src = raw_src(a, token_row(a, brow, tk, h), int(eos - tk < kC ? eos - tk : kC));
+            const int L = int(eos - tk < kC ? eos - tk : kC);
+            const RawSrc src = raw_src(a, token_row(a, brow, tk, h), L);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) load_token(R, src, t, kw, lane0);
+            for (int t = 0; t < 4; ++t) load_alpha(R, src, t, kw, lane0);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) load_qkb(R, src, t, kw, lane0);
+            decay_pass1(lds, R, al, ex, L, kw, lane0);
         }
         while (tk < eos || tv >= 0) {
             const bool has_k = tk < eos;
@@ -874,25 +908,25 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
             lds_barrier();  // B0
             int r = r0, g = g0, lane = lane0;  // opaque per period (see the value loop)
             __asm__ volatile("" : "+v"(r), "+v"(g), "+v"(lane));
-            float ex[8];  // per period
-            if (has_k) decay_pass1(lds, R, ex, L, kw, lane);
-            lds_barrier();  // B1
-            int step = 0;
-            if (has_k) {
-                step = chunk_step(lds, L);
-                prep_tiles(lds, R, ex, step, kbuf, kw, lane);
-            }
-            lds_barrier();  // B2
-            // The next chunk's inputs, issued while the value waves form its
-            // matrix blocks; they stay in flight until decay_pass1.
+            (void)r;
+            (void)g;
+            const int step = has_k ? chunk_step(lds, L) : 0;
             const int64_t tn = tk + step;
-            if (has_k && tn < eos) {
-                const RawSrc nxt = raw_src(a, token_row(a, brow, tn, h), int(eos - tn < kC ? eos - tn : kC));
-#pragma unroll
-                for (int t = 0; t < 4; ++t) load_token(R, nxt, t, kw, lane);
+            const int Ln = has_k && tn < eos ? int(eos - tn < kC ? eos - tn : kC) : 0;
+            // the next chunk's window (empty past the sequence end: loads read zero)
+            const RawSrc nxt = raw_src(a, token_row(a, brow, Ln > 0 ? tn : tk, h), Ln);
+            uint32_t kbp[2][8];
+            if (has_k) {
+                if (16 * kw + 16 <= step)
+                    prep_tiles<true>(lds, R, nxt, al, ex, kbp, step, kbuf, kw, lane);
+                else
+                    prep_tiles<false>(lds, R, nxt, al, ex, kbp, step, kbuf, kw, lane);
             }
+            lds_barrier();  // B1
+            if (has_k) store_kbt(lds, kbp, kw, lane);
+            if (Ln > 0) decay_pass1(lds, R, al, ex, Ln, kw, lane);
             tv = has_k ? tk : -1;
-            tk = has_k ? tk + step : eos;
+            tk = has_k ? tn : eos;
             kbuf ^= 1;
         }
     }
