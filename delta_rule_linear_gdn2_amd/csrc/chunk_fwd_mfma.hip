@@ -7,34 +7,37 @@
 // and dense products; FP32 is kept for the decay, the solve and the carried
 // state.  With incoming state S, per key channel the running decay
 // c_i = prod_{m<=i} alpha_m inside the chunk, e = b k and z = w v:
-//     Et_i = e_i c_i     Qt_i = q_i c_i     Kt_j = k_j / c_j     Kb_j = Kt_j c_last
+//     Et_i = e_i c_i     Qt_i = q_i c_i     Kt_j = k_j / c_j     gamma = c_last
 //     A = strict_lower(Et Kt^T)     P = lower(Qt Kt^T)
-//     U = (I + A)^-1 (Z - Et S)     O = Qt S + P U     S <- Diag(c_last) S + Kb^T U
+//     U = (I + A)^-1 (Z - Et S)     O = Qt S + P U     S <- Diag(gamma) (S + Kt^T U)
+// (the last is Diag(gamma) S + Kb^T U with Kb_j = Kt_j gamma, the form the
+// pages' decayed keys take).
 //
 // Range.  alpha is clamped to [2^-15, 1].  A chunk is cut short when some
-// channel decays below 2^-120 across it: it then covers 32, 16 or 8 tokens,
-// the longest prefix whose decay stays at or above 2^-120 in every channel (8
+// channel decays below 2^-64 across it: it then covers 32, 16 or 8 tokens,
+// the longest prefix whose decay stays at or above 2^-64 in every channel (8
 // tokens always do).  Hence every factor c_i and 1 / c_j lies in
-// [2^-120, 2^120], which FP32 and bf16 represent, and all factors are plain
-// products of alpha (one reciprocal per element).  All waves take the decision
-// from the same exchanged products, so it is uniform across the workgroup.
+// [2^-64, 2^64], which FP32 and bf16 represent, S + Kt^T U stays far below the
+// FP32 range, and all factors are plain products of alpha (one reciprocal per
+// channel and lane).  All waves take the decision from the same exchanged
+// products, so it is uniform across the workgroup.
 //
 // Pipeline.  One workgroup of eight wavefronts (two per SIMD) per (sequence,
 // head, 64-column value tile).  Waves 0..3 (value waves) own 16 value columns
 // each and keep that 128 x 16 slice of the FP32 state in MFMA accumulators for
 // the whole sequence; waves 4..7 (key waves) prepare the chunks.  Each period
-// of three barriers B0, B1, B2 advances two chunks: the value waves form
-// X = Z - Et S and (Qt S)^T of chunk c before B1, and its blocked solve,
-// output rows and state update between B1 and B2; meanwhile the key waves
-// compute the decay products of chunk c + 1 before B1 and its operand tiles
-// between B1 and B2.  After B2, wave 3 forms the diagonal blocks of A of
-// chunk c + 1 and their inverses, waves 0..2 its other A and P blocks, and the
-// key waves issue the loads of chunk c + 2.  Tiles the value
-// waves read between B1 and B2 are double-buffered; Et, Qt, Kt, the products
-// and z are consumed before their next write and stay single.  Each wave loads
-// its next inputs with 16-byte loads as soon as it has consumed the current
-// ones.  Workgroups of one chain share an XCD, so the second value tile
-// re-reads the key-side inputs from L2.
+// of two barriers B0, B1 advances two chunks.  Between B0 and B1 the value
+// waves finish chunk c - 1 (X = Z - Et S, (Qt S)^T, the blocked solve, the
+// output rows, the state update) while the key waves form the tiles Et, Qt, Kt
+// of chunk c; after B1 the value waves form the A and P blocks of chunk c and
+// the inverses of its diagonal blocks while the key waves store its Kt^T and
+// form the decay products of chunk c + 1, so that its length is known at the
+// next B0.  Et, Qt and gamma are double-buffered; z is private to each value
+// wave; A, P, T, Kt and Kt^T are written and read in different halves of the
+// period and stay single.  The key waves load the next chunk token by token as
+// the prep frees its registers, so the loads are in flight for a whole period.
+// Workgroups of one chain share an XCD, so the second value tile re-reads the
+// key-side inputs from L2.
 //
 // Matrix products (v_mfma_f32_16x16x32_bf16, FP32 accumulate): lane
 // l = 16 g + r provides row/column r and a group of eight K indices chosen by
@@ -118,7 +121,7 @@ __device__ __forceinline__ int off_rc64(int row, int col)
 {
     return row * 128 + ((((col >> 2) ^ row) & 15) << 3) + ((col & 3) << 1);
 }
-// [128][64] bf16 tile Kb^T (channel rows, token columns): 8-byte pieces
+// [128][64] bf16 tile Kt^T (channel rows, token columns): 8-byte pieces
 // XOR-swizzled by a linear map of the row bits (prep stores hit 16 channels
 // eight apart, reads 16 consecutive channels).
 __device__ __forceinline__ int kbt_swz(int row)
@@ -171,13 +174,13 @@ __device__ __forceinline__ void lds_st(unsigned char* lds, int off, V v)
 
 // Per-lane byte offsets of the operand reads.  For a tile row 16 k + r the
 // swizzle terms depend on r only, so every read is one of these plus a
-// compile-time constant (tile base and 16 k rows) -- except in Kb^T, whose
+// compile-time constant (tile base and 16 k rows) -- except in Kt^T, whose
 // swizzle also takes the block index (a constant XOR, see ld_kbt).
 struct LaneOffs {
     int c128[4];     // [64][128] tile, positions 32 s + 8 g .. + 7 (16 bytes)
     int s64[2][2];   // [64][64] tile, columns 32 s + 16 h + 4 g .. + 3 (8 bytes)
-    int kbt_row;     // Kb^T: r * 128
-    int kbt_sl;      // Kb^T: 8-byte slot g ^ swizzle(r)
+    int kbt_row;     // Kt^T: r * 128
+    int kbt_sl;      // Kt^T: 8-byte slot g ^ swizzle(r)
 };
 
 __device__ __forceinline__ LaneOffs lane_offsets(int r, int g)
@@ -207,7 +210,7 @@ __device__ __forceinline__ bf16x8 ld_s64(const unsigned char* lds, const LaneOff
     const uint2 hi = lds_ld<uint2>(lds, base + 16 * k * 128 + o.s64[s][1]);
     return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
-// Split K groups, channel row 16 cb + r of Kb^T (tokens 32 s + 4 g .. + 3 and
+// Split K groups, channel row 16 cb + r of Kt^T (tokens 32 s + 4 g .. + 3 and
 // 32 s + 16 + 4 g .. + 3): slot (8 s + 4 h + g) ^ swizzle(16 cb + r), and the
 // swizzle is linear, so the block part is a constant.
 __device__ __forceinline__ bf16x8 ld_kbt(const unsigned char* lds, const LaneOffs& o, int base, int cb, int s)
@@ -437,18 +440,18 @@ __device__ __forceinline__ int chunk_step(const unsigned char* lds, int L)
 // Store offsets of the key prep for one lane (tokens tok0 .. tok0 + 3 with
 // tok0 a multiple of 4, channels 8 cg .. 8 cg + 7).  Both swizzles are linear
 // in the row bits over GF(2), so row tok0 + t of a [64][128] tile lies at
-// (base ^ (tile_swz(t) << 4)) + 256 t and channel row 8 cg + c of Kb^T at
+// (base ^ (tile_swz(t) << 4)) + 256 t and channel row 8 cg + c of Kt^T at
 // (base ^ (kbt_swz(c) << 3)) + 128 c: the XOR only touches the granule bits.
 struct PrepOffs {
     int t128[2];  // row tok0 of a [64][128] tile, channels 8 cg .. + 3 and 8 cg + 4 .. + 7
-    int kbt;      // Kb^T buffer kbuf, channel row 8 cg, tokens tok0 .. + 3
+    int kbt;      // Kt^T, channel row 8 cg, tokens tok0 .. + 3
 };
-__device__ __forceinline__ PrepOffs prep_offsets(int tok0, int cg, int kbuf)
+__device__ __forceinline__ PrepOffs prep_offsets(int tok0, int cg)
 {
     PrepOffs o;
     o.t128[0] = off_t128(tok0, chan_pos(8 * cg));
     o.t128[1] = off_t128(tok0, chan_pos(8 * cg + 4));
-    o.kbt = kOffKbT + kbuf * 16384 + off_kbt(8 * cg, tok0);  // kbuf: 0 (one Kb^T buffer)
+    o.kbt = kOffKbT + off_kbt(8 * cg, tok0);
     return o;
 }
 // Channels 8 cg .. 8 cg + 7 of row tok0 + t of the tile at byte offset tile.
@@ -504,7 +507,7 @@ __device__ __forceinline__ void prep_tiles(unsigned char* lds, RawK& R, const Ra
         rc[1][c] = rc[2][c] * al[2][c];
         rc[0][c] = rc[1][c] * al[1][c];
     }
-    const PrepOffs po = prep_offsets(tok0, cg, 0);
+    const PrepOffs po = prep_offsets(tok0, cg);
     const int et_base = kOffEt + ebuf * 16384, qt_base = kOffQt + ebuf * 16384;
     const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
@@ -540,11 +543,11 @@ __device__ __forceinline__ void prep_tiles(unsigned char* lds, RawK& R, const Ra
     }
 }
 
-// Columns of Kb^T for this lane's tokens, after B1 (the value side reads the
+// Columns of Kt^T for this lane's tokens, after B1 (the value side reads the
 // previous chunk's until then).
 __device__ __forceinline__ void store_kbt(unsigned char* lds, const uint32_t (*kbp)[8], int kw, int lane)
 {
-    const PrepOffs po = prep_offsets(16 * kw + 4 * (lane & 3), lane >> 2, 0);
+    const PrepOffs po = prep_offsets(16 * kw + 4 * (lane & 3), lane >> 2);
 #pragma unroll
     for (int c = 0; c < 8; ++c)
         lds_st<uint2>(lds, (po.kbt ^ (kbt_swz(c) << 3)) + 128 * c, make_uint2(kbp[0][c], kbp[1][c]));
@@ -858,7 +861,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
                 if (tn < eos)
                     load_rawv(V, a, token_row(a, brow, tn, h), int(eos - tn < kC ? eos - tn : kC), j0, wave, lane);
             }
-            lds_barrier();  // B1: tiles of chunk tk visible; A, P, T and Kb^T of chunk tv consumed
+            lds_barrier();  // B1: tiles of chunk tk visible; A, P, T and Kt^T of chunk tv consumed
             if (has_k) {
                 const LaneOffs lk = lane_offsets(r, g);
                 if (wave == kTWave)
@@ -884,7 +887,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
         // Key side.  The decay products of a chunk are formed after B1 of the
         // period before the one that prepares it, so its length is known at
         // B0; its tiles are formed between B0 and B1 (Et and Qt into the
-        // buffer the value side does not read this period) and its Kb^T
+        // buffer the value side does not read this period) and its Kt^T
         // columns after B1.  The next chunk's inputs are loaded during the
         // prep and stay in flight until its decay products and prep.
         if (kw == 0) {  // the row of ones of the decay products

@@ -9,11 +9,9 @@ namespace gdn2 {
 // bf16 values are carried as raw 16-bit patterns.
 using bf16raw = uint16_t;
 
-// Per token and key channel, log2(alpha) is clamped to [kLog2AlphaFloor, 0].
-// The chunk kernels split the decay factor exp2(G_i - G_j) of the intra-chunk
-// products into a row factor and a column factor around a reference token at
-// most 8 tokens away; with the floor the larger factor stays below 2^120, which
-// FP32 and bf16 both represent.
+// Per token and key channel, the chunk kernels clamp log2(alpha) to
+// [kLog2AlphaFloor, 0] (alpha to [2^-15, 1]); the bound on the decay per token
+// keeps the decay factors of a chunk representable (see the chunk kernels).
 constexpr float kLog2AlphaFloor = -15.0f;
 
 __device__ __forceinline__ float bf16_to_f32(bf16raw x) { return __uint_as_float(uint32_t(x) << 16); }
