@@ -276,7 +276,8 @@ static void chunked_chain(const shape_t* s, int32_t n, int32_t h, int32_t C,
 
 /* ------------------------------------------------------------------------
  * O3: the same recurrence written with explicit transition matrices
- * [MP, "diagonal-plus-low-rank transitions"]:
+ * [MP: with per-channel gating each step's transition is a diagonal matrix
+ * plus a rank-one term]:
  *     M_t = (I - k_t e_t^T) Diag(alpha_t)      (dk x dk)
  *     S_t = M_t S_{t-1} + k_t z_t^T,   o_t = S_t^T q_t
  * ---------------------------------------------------------------------- */

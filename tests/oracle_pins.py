@@ -128,8 +128,8 @@ def pin_pure_decay(orc):
 
 
 # --------------------------------------------------------------------------
-# P4: "write the error, not the value" [MP; IPX "From a growing cache to a
-# fixed state"]: with b = w = 1 and a unit key the update makes the state
+# P4: the delta rule stores the prediction error, not the raw value [MP; IPX
+# "From a growing cache to a fixed state"]: with b = w = 1 and a unit key the update makes the state
 # return exactly v_t for key k_t, whatever the decay and the prior state.
 # Reading with q_t = k_t, the output must be v_t at every token.
 
@@ -189,7 +189,8 @@ def pin_gdn_reduction(orc):
 
 # --------------------------------------------------------------------------
 # P6: the chunkwise WY form computes the same mathematics as the token loop
-# [MP: "identical mathematics"; IPX "Token processing and parallel training"],
+# [MP: the recurrent and chunkwise modes compute the same result; IPX "Token
+# processing and parallel training"],
 # for any chunk size, with a short last chunk, with and without packing.
 
 
