@@ -22,22 +22,23 @@
 // channel and lane).  All waves take the decision from the same exchanged
 // products, so it is uniform across the workgroup.
 //
-// Pipeline.  One workgroup of eight wavefronts (two per SIMD) per (sequence,
-// head, 64-column value tile).  Waves 0..3 (value waves) own 16 value columns
-// each and keep that 128 x 16 slice of the FP32 state in MFMA accumulators for
-// the whole sequence; waves 4..7 (key waves) prepare the chunks.  Each period
-// of two barriers B0, B1 advances two chunks.  Between B0 and B1 the value
-// waves finish chunk c - 1 (X = Z - Et S, (Qt S)^T, the blocked solve, the
-// output rows, the state update) while the key waves form the tiles Et, Qt, Kt
-// of chunk c; after B1 the value waves form the A and P blocks of chunk c and
-// the inverses of its diagonal blocks while the key waves store its Kt^T and
-// form the decay products of chunk c + 1, so that its length is known at the
-// next B0.  Et, Qt and gamma are double-buffered; z is private to each value
-// wave; A, P, T, Kt and Kt^T are written and read in different halves of the
-// period and stay single.  The key waves load the next chunk token by token as
-// the prep frees its registers, so the loads are in flight for a whole period.
-// Workgroups of one chain share an XCD, so the second value tile re-reads the
-// key-side inputs from L2.
+// Pipeline.  One workgroup of twelve wavefronts (three per SIMD) per
+// (sequence, head, 64-column value tile).  Waves 0..3 (value waves) own 16
+// value columns each and keep that 128 x 16 slice of the FP32 state in MFMA
+// accumulators for the whole sequence; waves 4..11 (key waves) prepare the
+// chunks, each 16 tokens x 64 channels.  Each period of two barriers B0, B1
+// advances two chunks.  Between B0 and B1 the value waves finish chunk c - 1
+// block by block (X = Z - Et S, the blocked solve, the output rows, (Qt S)^T)
+// and update the state, while the key waves form the tiles Et, Qt, Kt of chunk
+// c; after B1 the value waves form the A and P blocks of chunk c and the
+// inverses of its diagonal blocks, while the key waves store its Kt^T and its
+// z = w v and form the decay products of chunk c + 1, so that its length is
+// known at the next B0.  Et, Qt, z and gamma are double-buffered; A, P, T, Kt
+// and Kt^T are written and read in different halves of the period and stay
+// single.  Global loads go out in both halves so that the memory pipe stays
+// busy: alpha and q of the next chunk during the prep, as registers free up,
+// and its k, b, v and w after B1.  Workgroups of one chain share an XCD, so
+// the second value tile re-reads the key-side inputs from L2.
 //
 // Matrix products (v_mfma_f32_16x16x32_bf16, FP32 accumulate): lane
 // l = 16 g + r provides row/column r and a group of eight K indices chosen by
@@ -64,9 +65,10 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kDK = 128;          // key head size
 constexpr int kC = 64;            // chunk
 constexpr int kDVT = 64;          // value columns per workgroup
-constexpr int kWaves = 8;         // wavefronts per workgroup
+constexpr int kWaves = 12;        // wavefronts per workgroup (three per SIMD)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kValueWaves = 4;    // waves 0..3: 16 value columns each
+constexpr int kKeyWaves = 8;      // waves 4..11: 16 tokens x 64 channels each
 constexpr int kTWave = 3;         // diagonal blocks of A and their inverses (a value wave)
 constexpr float kAlphaMin = 0x1p-15f;
 constexpr float kRangeMin = 0x1p-64f;
@@ -81,14 +83,16 @@ constexpr int kOffP = 106496;      // [64][64] bf16
 constexpr int kT16 = 20;            // floats per row of a 16 x 16 FP32 block (padded)
 constexpr int kTBlk = 16 * kT16 + 16;  // floats per padded block (the next block shifts by 16 banks)
 constexpr int kOffT = 114688;      // [4][kTBlk] f32, T_II row major
-constexpr int kOffAd = kOffT + 4 * kTBlk * 4;   // [4][kTBlk] f32, diagonal blocks of A, column major
-constexpr int kOffGam = kOffAd + 4 * kTBlk * 4; // [2][128] f32 (chunk decay per channel)
+constexpr int kOffAd = kOffT;   // [4][kTBlk] f32, diagonal blocks of A, column major; the same wave
+                                // reads them all before it overwrites them with T
+constexpr int kOffGam = kOffT + 4 * kTBlk * 4;  // [2][128] f32 (chunk decay per channel)
 constexpr int kOffPh = kOffGam + 1024;  // [7][128] f32: decay over tokens 16 j .. 16 j + 15 (rows j < 4),
                                         // over 0..7 (row 4), per-block channel minima (row 5), ones (row 6)
 constexpr int kPhOnes = 6;
-constexpr int kOffZs = kOffPh + 3584;   // per value wavefront [16 columns][64 tokens] f32 (zs_off), z = w v
+constexpr int kOffZs = kOffPh + 3584;   // [2][value wavefront][16 columns][64 tokens] f32 (zs_off), z = w v
 constexpr int kZsWave = 16 * 64 * 4;
-constexpr int kLdsBytes = kOffZs + kValueWaves * kZsWave;
+constexpr int kZsBuf = kValueWaves * kZsWave;
+constexpr int kLdsBytes = kOffZs + 2 * kZsBuf;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 static_assert(kOffP == kOffAneg + 8192 && kOffT == kOffP + 8192, "Aneg and P are cleared as one range");
 static_assert(kOffZs % 16 == 0 && kZsWave % 16 == 0, "16-byte aligned z rows");
@@ -227,6 +231,13 @@ __device__ __forceinline__ bf16x8 pack_acc_pair(f32x4 lo, f32x4 hi)
     return as_bf16x8(make_uint4(pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(hi[0], hi[1]),
                                 pack2(hi[2], hi[3])));
 }
+// The same, keeping the lower block of an existing operand (its first four
+// elements) and replacing the upper block.
+__device__ __forceinline__ bf16x8 pack_acc_pair_hi(bf16x8 keep, f32x4 hi)
+{
+    const uint4 k = __builtin_bit_cast(uint4, keep);
+    return as_bf16x8(make_uint4(k.x, k.y, pack2(hi[0], hi[1]), pack2(hi[2], hi[3])));
+}
 
 __device__ __forceinline__ float lo_f(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float hi_f(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
@@ -251,6 +262,7 @@ __device__ __forceinline__ float dpp(float x)
 constexpr int kQuadPrev = 0x90;   // quad_perm(0, 0, 1, 2): lane i <- lane i - 1 (lane 0 <- itself)
 constexpr int kQuadPrev2 = 0x40;  // quad_perm(0, 0, 0, 1): lanes 2, 3 <- lanes 0, 1
 constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128;
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114;  // lane i <- lane i - k of its row of 16
 
 // Minimum over the wavefront, returned as a wave-uniform value.
 __device__ __forceinline__ float wave_min(float x)
@@ -297,12 +309,34 @@ __device__ __forceinline__ uint4 ld_b128(rsrc_t r, uint32_t off)
 }
 
 // One key wavefront's share of a chunk's inputs: key wavefront kw prepares
-// tokens 16 kw .. 16 kw + 15; lane l takes tokens 16 kw + 4 (l & 3) + {0..3}
-// and channels 8 (l >> 2) .. + 7 (a quad holds the wavefront's 16 tokens).
+// tokens 16 tb .. 16 tb + 15 (tb = kw & 3) in channels 64 ch .. 64 ch + 63
+// (ch = kw >> 2); lane l takes tokens 16 tb + 2 (l & 7) + {0, 1} and channels
+// 64 ch + 8 (l >> 3) .. + 7 (eight consecutive lanes hold the block's 16 tokens).
 struct RawK {
-    uint4 q[4], k[4], b[4];  // 8 bf16 channels per token
-    uint4 a[4][2];           // alpha, 8 FP32 channels per token
+    uint4 q[2], k[2], b[2];  // 8 bf16 channels per token
+    uint4 a[2][2];           // alpha, 8 FP32 channels per token
 };
+// A key wavefront's share of v and w (the workgroup's 64 value columns):
+// tokens 16 tb + (l & 15), columns 32 ch + 8 (l >> 4) .. + 7 of the tile.
+struct RawVK {
+    uint4 v, w;
+};
+struct KeyLane {
+    int tb, ch, tp, cg;
+    int tok0;  // 16 tb + 2 tp
+    int c0;    // first channel: 64 ch + 8 cg
+};
+__device__ __forceinline__ KeyLane key_lane(int kw, int lane)
+{
+    KeyLane k;
+    k.tb = kw & 3;
+    k.ch = kw >> 2;
+    k.tp = lane & 7;
+    k.cg = lane >> 3;
+    k.tok0 = 16 * k.tb + 2 * k.tp;
+    k.c0 = 64 * k.ch + 8 * k.cg;
+    return k;
+}
 // A value wavefront's share of v and w: its own 16 columns of the tile for all
 // 64 tokens of the chunk; lane l takes token l.
 struct RawV {
@@ -331,23 +365,47 @@ __device__ __forceinline__ RawSrc raw_src(const ChunkArgs& a, int64_t row0, int 
     s.a = make_rsrc(a.alpha + row0 * kDK, 2 * win);
     return s;
 }
-// Loads this lane's token t (of four) of a chunk: q, k, b, and alpha.
-__device__ __forceinline__ void load_qkb(RawK& R, const RawSrc& s, int t, int kw, int lane)
+// Loads token t (of two) of this lane: q, k, b, and alpha.
+__device__ __forceinline__ void load_q(RawK& R, const RawSrc& s, int t, const KeyLane& K)
 {
-    const int tp = lane & 3, cg = lane >> 2;
-    const uint32_t off = uint32_t(16 * kw + 4 * tp + t) * s.kstride + 16 * cg;
-    R.q[t] = ld_b128(s.q, off);
+    R.q[t] = ld_b128(s.q, uint32_t(K.tok0 + t) * s.kstride + 2 * K.c0);
+}
+__device__ __forceinline__ void load_kb(RawK& R, const RawSrc& s, int t, const KeyLane& K)
+{
+    const uint32_t off = uint32_t(K.tok0 + t) * s.kstride + 2 * K.c0;
     R.k[t] = ld_b128(s.k, off);
     R.b[t] = ld_b128(s.b, off);
 }
-__device__ __forceinline__ void load_alpha(RawK& R, const RawSrc& s, int t, int kw, int lane)
+__device__ __forceinline__ void load_alpha(RawK& R, const RawSrc& s, int t, const KeyLane& K)
 {
-    const int tp = lane & 3, cg = lane >> 2;
-    const uint32_t off = 2 * uint32_t(16 * kw + 4 * tp + t) * s.kstride + 32 * cg;
+    const uint32_t off = 2 * uint32_t(K.tok0 + t) * s.kstride + 4 * K.c0;
     R.a[t][0] = ld_b128(s.a, off);
     R.a[t][1] = ld_b128(s.a, off + 16);
 }
 
+__device__ __forceinline__ void load_vk(RawVK& V, const ChunkArgs& a, int64_t row0, int L, int j0, int kw, int lane)
+{
+    const uint32_t vstride = uint32_t(a.H) * uint32_t(a.dv) * 2;
+    const uint32_t win = L > 0 ? uint32_t(L - 1) * vstride + kDVT * 2 : 0u;
+    const int64_t base = row0 * a.dv + j0;
+    const rsrc_t rv = make_rsrc(static_cast<const bf16raw*>(a.v) + base, win);
+    const rsrc_t rw = make_rsrc(static_cast<const bf16raw*>(a.w) + base, win);
+    const uint32_t off = uint32_t(16 * (kw & 3) + (lane & 15)) * vstride + 2 * (32 * (kw >> 2) + 8 * (lane >> 4));
+    V.v = ld_b128(rv, off);
+    V.w = ld_b128(rw, off);
+}
+// z = w v of this key lane's eight columns into buffer buf of the z of the
+// value wavefront that owns them (rows past the chunk are masked when read).
+__device__ __forceinline__ void store_z(unsigned char* lds, const RawVK& V, int buf, int kw, int lane)
+{
+    const int tok = 16 * (kw & 3) + (lane & 15), col = 32 * (kw >> 2) + 8 * (lane >> 4);
+    unsigned char* zs = lds + kOffZs + buf * kZsBuf + (col >> 4) * kZsWave;
+    float v[8], w[8];
+    unpack8(V.v, v);
+    unpack8(V.w, w);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) lds_st<float>(zs, zs_off((col & 15) + m, tok), v[m] * w[m]);
+}
 __device__ __forceinline__ void load_rawv(RawV& V, const ChunkArgs& a, int64_t row0, int L, int j0, int wave,
                                           int lane)
 {
@@ -371,87 +429,92 @@ __device__ __forceinline__ float raw_alpha(const RawK& R, int t, int c)
     return __uint_as_float((c & 3) == 0 ? x.x : (c & 3) == 1 ? x.y : (c & 3) == 2 ? x.z : x.w);
 }
 
-// First half of the key prep: decay products along the wavefront's 16 tokens
-// (in lane, then a quad scan).  Writes the product over the 16 tokens to
-// Ph[kw] (and wavefront 0 the product over tokens 0..7 to Ph[4]); returns the
-// clamped alpha in al and in ex the product over the wavefront's tokens before this lane's four.
+// Decay products of a chunk along the key wavefront's 16 tokens (in lane,
+// then a scan over the eight lanes of a channel group).  Writes the product
+// over the block to Ph[tb] (and, for block 0, the product over tokens 0..7 to
+// Ph[4]) for this wavefront's channels and its smallest block product to
+// Ph[5][2 tb + ch]; returns the clamped alpha in al and in ex the product over
+// the block's tokens before this lane's two.
 __device__ __forceinline__ void decay_pass1(unsigned char* lds, const RawK& R, float (*al)[8], float* ex, int L,
-                                            int kw, int lane)
+                                            const KeyLane& K, int lane)
 {
-    const int tp = lane & 3, cg = lane >> 2;
     // alpha clamped to [2^-15, 1], and 1 past the sequence end
     if (L == kC) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int c = 0; c < 8; ++c) al[t][c] = __builtin_amdgcn_fmed3f(raw_alpha(R, t, c), kAlphaMin, 1.0f);
     } else {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const bool live = 16 * kw + 4 * tp + t < L;
+        for (int t = 0; t < 2; ++t) {
+            const bool live = K.tok0 + t < L;
 #pragma unroll
             for (int c = 0; c < 8; ++c)
                 al[t][c] = live ? __builtin_amdgcn_fmed3f(raw_alpha(R, t, c), kAlphaMin, 1.0f) : 1.0f;
         }
     }
+    const int tp = K.tp;
     float inc[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-        float p = 1.0f;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) p *= al[t][c];
-        const float y = dpp<kQuadPrev>(p);
-        const float x1 = tp >= 1 ? p * y : p;
-        const float z = dpp<kQuadPrev2>(x1);
-        inc[c] = tp >= 2 ? x1 * z : x1;  // tokens 16 kw .. 16 kw + 4 tp + 3
-        const float e = dpp<kQuadPrev>(inc[c]);
-        ex[c] = tp >= 1 ? e : 1.0f;      // tokens 16 kw .. 16 kw + 4 tp - 1
+        float x = al[0][c] * al[1][c];
+        float y = dpp<kRowShr1>(x);
+        x = tp >= 1 ? x * y : x;
+        y = dpp<kRowShr2>(x);
+        x = tp >= 2 ? x * y : x;
+        y = dpp<kRowShr4>(x);
+        x = tp >= 4 ? x * y : x;
+        inc[c] = x;  // tokens 16 tb .. 16 tb + 2 tp + 1
+        const float e = dpp<kRowShr1>(x);
+        ex[c] = tp >= 1 ? e : 1.0f;  // tokens 16 tb .. 16 tb + 2 tp - 1
     }
     float* ph = reinterpret_cast<float*>(lds + kOffPh);
-    if (tp == 3 || (kw == 0 && tp == 1)) {
-        float* dst = ph + (tp == 3 ? kw : 4) * 128 + 8 * cg;
+    if (tp == 7 || (K.tb == 0 && tp == 3)) {
+        float* dst = ph + (tp == 7 ? K.tb : 4) * 128 + K.c0;
         *reinterpret_cast<float4*>(dst) = make_float4(inc[0], inc[1], inc[2], inc[3]);
         *reinterpret_cast<float4*>(dst + 4) = make_float4(inc[4], inc[5], inc[6], inc[7]);
     }
-    // smallest decay over the 16 tokens among all channels (products are <= 1)
+    // smallest decay over the 16 tokens among this wavefront's channels
     float m = 1.0f;
-    if (tp == 3) {
+    if (tp == 7) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) m = fminf(m, inc[c]);
     }
     m = wave_min(m);
-    if (lane == 0) ph[5 * 128 + kw] = m;
+    if (lane == 0) ph[5 * 128 + 2 * K.tb + K.ch] = m;
 }
 
-// Chunk length (identical in every wavefront: the same four values in the
+// Chunk length (identical in every wavefront: the same eight values in the
 // same order): with m_j the smallest decay over block j (tokens 16 j ..
-// 16 j + 15) among all channels, the longest of 64, 32, 16 tokens for which
+// 16 j + 15) among all channels (the smaller of its two channel halves), the longest of 64, 32, 16 tokens for which
 // m_0 m_1 ... stays >= 2^-64, else 8; at most L.  The product of the minima
 // bounds every channel's decay from below, so all factors of the chunk stay
 // within [2^-64, 2^64].
 __device__ __forceinline__ int chunk_step(const unsigned char* lds, int L)
 {
     const float* pm = reinterpret_cast<const float*>(lds + kOffPh) + 5 * 128;
-    const float g16 = pm[0], g32 = g16 * pm[1], g64 = g32 * pm[2] * pm[3];
+    const float m0 = fminf(pm[0], pm[1]), m1 = fminf(pm[2], pm[3]), m2 = fminf(pm[4], pm[5]),
+                m3 = fminf(pm[6], pm[7]);
+    const float g16 = m0, g32 = g16 * m1, g64 = g32 * m2 * m3;
     const int leff = g64 >= kRangeMin ? 64 : g32 >= kRangeMin ? 32 : g16 >= kRangeMin ? 16 : 8;
     return leff < L ? leff : L;
 }
 
-// Store offsets of the key prep for one lane (tokens tok0 .. tok0 + 3 with
-// tok0 a multiple of 4, channels 8 cg .. 8 cg + 7).  Both swizzles are linear
-// in the row bits over GF(2), so row tok0 + t of a [64][128] tile lies at
-// (base ^ (tile_swz(t) << 4)) + 256 t and channel row 8 cg + c of Kt^T at
+// Store offsets of the key prep for one lane (tokens tok0, tok0 + 1 with tok0
+// even, channels c0 .. c0 + 7 with c0 a multiple of 8).  Both swizzles are
+// linear in the row bits over GF(2), so row tok0 + t of a [64][128] tile lies
+// at (base ^ (tile_swz(t) << 4)) + 256 t and channel row c0 + c of Kt^T at
 // (base ^ (kbt_swz(c) << 3)) + 128 c: the XOR only touches the granule bits.
 struct PrepOffs {
-    int t128[2];  // row tok0 of a [64][128] tile, channels 8 cg .. + 3 and 8 cg + 4 .. + 7
-    int kbt;      // Kt^T, channel row 8 cg, tokens tok0 .. + 3
+    int t128[2];  // row tok0 of a [64][128] tile, channels c0 .. + 3 and c0 + 4 .. + 7
+    int kbt;      // Kt^T, channel row c0, tokens tok0, tok0 + 1
 };
-__device__ __forceinline__ PrepOffs prep_offsets(int tok0, int cg)
+__device__ __forceinline__ PrepOffs prep_offsets(int tok0, int c0)
 {
     PrepOffs o;
-    o.t128[0] = off_t128(tok0, chan_pos(8 * cg));
-    o.t128[1] = off_t128(tok0, chan_pos(8 * cg + 4));
-    o.kbt = kOffKbT + off_kbt(8 * cg, tok0);
+    o.t128[0] = off_t128(tok0, chan_pos(c0));
+    o.t128[1] = off_t128(tok0, chan_pos(c0 + 4));
+    o.kbt = kOffKbT + off_kbt(c0, tok0);
     return o;
 }
 // Channels 8 cg .. 8 cg + 7 of row tok0 + t of the tile at byte offset tile.
@@ -468,24 +531,22 @@ __device__ __forceinline__ void st_tok(unsigned char* lds, const PrepOffs& o, in
 // token, as their registers are consumed, the inputs of the next chunk are
 // loaded into R.
 //
-// A chunk cut short (step < L) ends at a multiple of 8, so each lane's four
-// tokens are all in it or all past it; lanes past it (kAllLive false) form
+// A chunk cut short (step < L) ends at a multiple of 8, so each lane's two
+// tokens are both in it or both past it; lanes past it (kAllLive false) form
 // zero rows from zeroed q and k with a running decay of 1 (their own decay
 // factors are never formed).  Past the sequence end (step = L) the inputs
 // read as zero and alpha as 1, which gives zero rows as well.
 template <bool kAllLive>
 __device__ __forceinline__ void prep_tiles(unsigned char* lds, RawK& R, const RawSrc& nxt, const float (*al)[8],
-                                           const float* ex, uint32_t (*kbp)[8], int step, int ebuf, int kw, int lane)
+                                           const float* ex, uint32_t* kbp, int step, int ebuf, const KeyLane& K)
 {
-    const int tp = lane & 3, cg = lane >> 2;
-    const int tok0 = 16 * kw + 4 * tp;
-    const bool live = kAllLive || tok0 < step;
-    // decay before this lane's tokens: blocks 0 .. kw - 1 (the row of ones
+    const bool live = kAllLive || K.tok0 < step;
+    // decay before this lane's tokens: blocks 0 .. tb - 1 (the row of ones
     // stands in for the others), then the part of its own block before it
     float cum[8];
     {
-        const float4* p4 = reinterpret_cast<const float4*>(lds + kOffPh) + 2 * cg;  // row j: p4[32 j], p4[32 j + 1]
-        const int j0 = kw > 0 ? 0 : kPhOnes, j1 = kw > 1 ? 1 : kPhOnes, j2 = kw > 2 ? 2 : kPhOnes;
+        const float4* p4 = reinterpret_cast<const float4*>(lds + kOffPh) + (K.c0 >> 2);  // row j: p4[32 j], p4[32 j + 1]
+        const int j0 = K.tb > 0 ? 0 : kPhOnes, j1 = K.tb > 1 ? 1 : kPhOnes, j2 = K.tb > 2 ? 2 : kPhOnes;
         const float4 a0 = p4[32 * j0], b0 = p4[32 * j0 + 1], a1 = p4[32 * j1], b1 = p4[32 * j1 + 1];
         const float4 a2 = p4[32 * j2], b2 = p4[32 * j2 + 1];
         const float x0[8] = {a0.x, a0.y, a0.z, a0.w, b0.x, b0.y, b0.z, b0.w};
@@ -498,21 +559,19 @@ __device__ __forceinline__ void prep_tiles(unsigned char* lds, RawK& R, const Ra
         }
     }
     // 1 / (decay through token t): one reciprocal of the decay through the
-    // lane's last token, then back through alpha
-    float rc[4][8];
+    // lane's second token, then back through alpha
+    float rc[2][8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-        rc[3][c] = __builtin_amdgcn_rcpf(cum[c] * al[0][c] * al[1][c] * al[2][c] * al[3][c]);
-        rc[2][c] = rc[3][c] * al[3][c];
-        rc[1][c] = rc[2][c] * al[2][c];
+        rc[1][c] = __builtin_amdgcn_rcpf(cum[c] * al[0][c] * al[1][c]);
         rc[0][c] = rc[1][c] * al[1][c];
     }
-    const PrepOffs po = prep_offsets(tok0, cg);
+    const PrepOffs po = prep_offsets(K.tok0, K.c0);
     const int et_base = kOffEt + ebuf * 16384, qt_base = kOffQt + ebuf * 16384;
     const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        load_alpha(R, nxt, t, kw, lane);  // alpha of token t of the next chunk (clamped copy in al)
+    for (int t = 0; t < 2; ++t) {
+        load_alpha(R, nxt, t, K);  // alpha of token t of the next chunk (clamped copy in al)
         float q[8], k[8], b[8];
         unpack8(kAllLive || live ? R.q[t] : zero, q);
         unpack8(kAllLive || live ? R.k[t] : zero, k);
@@ -531,26 +590,25 @@ __device__ __forceinline__ void prep_tiles(unsigned char* lds, RawK& R, const Ra
                                                pack2(qt[6], qt[7])));
         st_tok(lds, po, kOffKt, t, make_uint4(pack2(kt[0], kt[1]), pack2(kt[2], kt[3]), pack2(kt[4], kt[5]),
                                               pack2(kt[6], kt[7])));
-        if (t & 1) {
+        if (t == 1) {
 #pragma unroll
-            for (int c = 0; c < 8; ++c) kbp[t >> 1][c] = pack2(__uint_as_float(kbp[t >> 1][c]), kt[c]);
+            for (int c = 0; c < 8; ++c) kbp[c] = pack2(__uint_as_float(kbp[c]), kt[c]);
         } else {
 #pragma unroll
-            for (int c = 0; c < 8; ++c) kbp[t >> 1][c] = __float_as_uint(kt[c]);
+            for (int c = 0; c < 8; ++c) kbp[c] = __float_as_uint(kt[c]);
         }
-        load_qkb(R, nxt, t, kw, lane);  // token t of the next chunk into the registers just consumed
+        load_q(R, nxt, t, K);  // q of token t of the next chunk (k and b follow after B1)
         __builtin_amdgcn_sched_barrier(0);  // one token's temporaries at a time
     }
 }
 
-// Columns of Kt^T for this lane's tokens, after B1 (the value side reads the
-// previous chunk's until then).
-__device__ __forceinline__ void store_kbt(unsigned char* lds, const uint32_t (*kbp)[8], int kw, int lane)
+// Columns of Kt^T for this lane's two tokens, after B1 (the value side reads
+// the previous chunk's until then).
+__device__ __forceinline__ void store_kbt(unsigned char* lds, const uint32_t* kbp, const KeyLane& K)
 {
-    const PrepOffs po = prep_offsets(16 * kw + 4 * (lane & 3), lane >> 2);
+    const PrepOffs po = prep_offsets(K.tok0, K.c0);
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-        lds_st<uint2>(lds, (po.kbt ^ (kbt_swz(c) << 3)) + 128 * c, make_uint2(kbp[0][c], kbp[1][c]));
+    for (int c = 0; c < 8; ++c) lds_st<uint32_t>(lds, (po.kbt ^ (kbt_swz(c) << 3)) + 128 * c, kbp[c]);
 }
 
 // z = w v of the chunk into this wavefront's Zs: columns 16 wave .. + 15 of
@@ -628,6 +686,7 @@ __device__ __forceinline__ void ap_work(unsigned char* lds, const LaneOffs& o, i
 // lane r its column r.
 __device__ __forceinline__ void t_work(unsigned char* lds, const LaneOffs& o, int ebuf, int r, int g)
 {
+    __asm__ volatile("" : "+v"(r), "+v"(g));  // no part of this work moves above the barrier before it
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -646,33 +705,31 @@ __device__ __forceinline__ void t_work(unsigned char* lds, const LaneOffs& o, in
     // Other lanes of this wavefront read the columns back: LDS accesses of one
     // wavefront complete in order; this keeps the compiler from reordering.
     __asm__ volatile("" ::: "memory");
-    const float* adc = reinterpret_cast<const float*>(lds + kOffAd) + g * kTBlk;  // column j at adc + j * kT16
-    const auto adt = [&](int j, int q4) { return *reinterpret_cast<const float4*>(adc + j * kT16 + 4 * q4); };
+    const unsigned char* adc = lds + kOffAd + g * kTBlk * 4;  // column j at byte j * kT16 * 4
     float t[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) t[i] = i == r ? 1.f : 0.f;
-    float4 c0[4], c1[4];  // columns j and j + 1; column j + 2 is read during step j
+    // Column j + 1 is read during step j; its byte offset is made opaque per
+    // step so that no read moves further ahead (register budget).
+    float4 c0[4];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-        c0[q4] = adt(0, q4);
-        c1[q4] = adt(1, q4);
-    }
+    for (int q4 = 0; q4 < 4; ++q4) c0[q4] = lds_ld<float4>(adc, 16 * q4);
 #pragma unroll
     for (int j = 0; j < 15; ++j) {
-        float4 c2[4];
-        if (j < 13)
+        float4 c1[4];
+        if (j < 14) {
+            int off = (j + 1) * kT16 * 4;
+            __asm__ volatile("" : "+v"(off) : "v"(t[j]) : "memory");  // after t[j] is final
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) c2[q4] = adt(j + 2, q4);
+            for (int q4 = 0; q4 < 4; ++q4) c1[q4] = lds_ld<float4>(adc, off + 16 * q4);
+        }
         const float col[16] = {c0[0].x, c0[0].y, c0[0].z, c0[0].w, c0[1].x, c0[1].y, c0[1].z, c0[1].w,
                                c0[2].x, c0[2].y, c0[2].z, c0[2].w, c0[3].x, c0[3].y, c0[3].z, c0[3].w};
 #pragma unroll
         for (int i = j + 1; i < 16; ++i) t[i] -= col[i] * t[j];
+        if (j < 14)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            c0[q4] = c1[q4];
-            if (j < 13) c1[q4] = c2[q4];
-        }
-        __asm__ volatile("" ::: "memory");  // two columns ahead, no further
+            for (int q4 = 0; q4 < 4; ++q4) c0[q4] = c1[q4];
     }
     float* T = reinterpret_cast<float*>(lds + kOffT) + g * kTBlk;
 #pragma unroll
@@ -693,84 +750,64 @@ __device__ __forceinline__ void value_gamma(unsigned char* lds, int step, int bu
         make_float2(x0.x * x1.x * x2.x * x3.x, x0.y * x1.y * x2.y * x3.y);
 }
 
-// Value wavefront, chunk of lv tokens: X = Z - Et S (direct, rows past the
-// chunk zero) and OT = (Qt S)^T.
-__device__ __forceinline__ void value_xo(const unsigned char* lds, const LaneOffs& o, const f32x4* S, f32x4* X,
-                                         f32x4* OT, int lv, int ebuf, int wave, int r, int g)
+// Value wavefront, one chunk of lv tokens (tiles of buffer ebuf, chunk decay
+// of buffer ebuf), block by block: X_I = Z_I - Et_I S (rows past the chunk
+// zero), the blocked solve R_I = X_I - sum_{J<I} A_IJ U_J, U_I = T_II R_I, and
+// the output rows O_I^T = (Qt_I S)^T + U^T P_I^T (P is lower triangular, so
+// only U_0 .. U_I enter); then the state update.  Every product reads the
+// state as it was at the chunk start.
+__device__ __forceinline__ void value_chunk(const unsigned char* lds, const LaneOffs& o, f32x4* S, int lv, int ebuf,
+                                            rsrc_t ro, int ostride, int wave, int r, int g)
 {
     bf16x8 sb[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) sb[s] = pack_acc_pair(S[2 * s], S[2 * s + 1]);
-    const unsigned char* zs = lds + kOffZs + wave * kZsWave;
+    const unsigned char* zs = lds + kOffZs + ebuf * kZsBuf + wave * kZsWave;
     const int et = kOffEt + ebuf * 16384, qt = kOffQt + ebuf * 16384;
+    const int o_vo = r * ostride + (16 * wave + 4 * g) * 2;
+    const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 ub[2];  // U as an operand over tokens 0..31 and 32..63; blocks not solved yet are zero
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-        f32x4 xe = f32x4{0.f, 0.f, 0.f, 0.f}, xq = xe;
+        f32x4 xe = zero4;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            xe = mfma_bf16(ld_c128(lds, o, et, I, s), sb[s], xe);
-            xq = mfma_bf16(sb[s], ld_c128(lds, o, qt, I, s), xq);
-        }
+        for (int s = 0; s < 4; ++s) xe = mfma_bf16(ld_c128(lds, o, et, I, s), sb[s], xe);
         const float4 z = lds_ld<float4>(zs, zs_off(r, 16 * I + 4 * g));
         const int t0 = 16 * I + 4 * g;
-        X[I] = f32x4{t0 + 0 < lv ? z.x - xe[0] : 0.f, t0 + 1 < lv ? z.y - xe[1] : 0.f,
-                     t0 + 2 < lv ? z.z - xe[2] : 0.f, t0 + 3 < lv ? z.w - xe[3] : 0.f};
-        OT[I] = xq;
-    }
-}
-
-// Value wavefront, rest of the chunk: blocked solve, output rows and state
-// update (chunk decay from buffer vbuf).
-__device__ __forceinline__ void value_solve(const unsigned char* lds, const LaneOffs& o, f32x4* S, const f32x4* X,
-                                            const f32x4* OT, int vbuf, rsrc_t ro, int ostride, int lv, int wave, int r,
-                                            int g)
-{
-    const int aneg = kOffAneg, pb = kOffP, tb = kOffT, kbt = kOffKbT;
-    // ---- blocked solve: R_I = X_I - sum_J A_IJ U_J ; U_I = T_II R_I
-    f32x4 U[4];
-    bf16x8 ub[2];
-    const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
-        f32x4 R_ = X[I];
-        if (I >= 1) R_ = mfma_bf16(ld_s64(lds, o, aneg, I, 0), ub[0], R_);
-        if (I >= 3) R_ = mfma_bf16(ld_s64(lds, o, aneg, I, 1), ub[1], R_);
-        const float4 tr = lds_ld<float4>(lds, tb + (I * kTBlk + r * kT16 + 4 * g) * 4);
+        f32x4 R_ = f32x4{t0 + 0 < lv ? z.x - xe[0] : 0.f, t0 + 1 < lv ? z.y - xe[1] : 0.f,
+                         t0 + 2 < lv ? z.z - xe[2] : 0.f, t0 + 3 < lv ? z.w - xe[3] : 0.f};
+        if (I >= 1) R_ = mfma_bf16(ld_s64(lds, o, kOffAneg, I, 0), ub[0], R_);
+        if (I >= 3) R_ = mfma_bf16(ld_s64(lds, o, kOffAneg, I, 1), ub[1], R_);
+        const float4 tr = lds_ld<float4>(lds, kOffT + (I * kTBlk + r * kT16 + 4 * g) * 4);
         f32x4 u = zero4;
         u = mfma_f32(tr.x, R_[0], u);
         u = mfma_f32(tr.y, R_[1], u);
         u = mfma_f32(tr.z, R_[2], u);
         u = mfma_f32(tr.w, R_[3], u);
-        U[I] = u;
-        // operands over tokens 0..31 and 32..63; blocks not solved yet stay zero
-        if (I == 0) ub[0] = pack_acc_pair(U[0], zero4);
-        if (I == 1) ub[0] = pack_acc_pair(U[0], U[1]);
-        if (I == 2) ub[1] = pack_acc_pair(U[2], zero4);
-        if (I == 3) ub[1] = pack_acc_pair(U[2], U[3]);
-    }
-    // ---- O^T = (Qt S)^T + U^T P^T; lane holds token 16 I + r, columns 4g..4g+3
-    const int o_vo = r * ostride + (16 * wave + 4 * g) * 2;
+        if (I == 0) ub[0] = pack_acc_pair(u, zero4);
+        if (I == 1) ub[0] = pack_acc_pair_hi(ub[0], u);
+        if (I == 2) ub[1] = pack_acc_pair(u, zero4);
+        if (I == 3) ub[1] = pack_acc_pair_hi(ub[1], u);
+        f32x4 acc2 = zero4;
 #pragma unroll
-    for (int I = 0; I < 4; ++I) {
-        f32x4 acc2 = OT[I];
-        acc2 = mfma_bf16(ub[0], ld_s64(lds, o, pb, I, 0), acc2);
-        if (I >= 2) acc2 = mfma_bf16(ub[1], ld_s64(lds, o, pb, I, 1), acc2);
-        if (16 * I + r < lv) {
+        for (int s = 0; s < 4; ++s) acc2 = mfma_bf16(sb[s], ld_c128(lds, o, qt, I, s), acc2);
+        acc2 = mfma_bf16(ub[0], ld_s64(lds, o, kOffP, I, 0), acc2);
+        if (I >= 2) acc2 = mfma_bf16(ub[1], ld_s64(lds, o, kOffP, I, 1), acc2);
+        if (16 * I + r < lv) {  // lane holds token 16 I + r, columns 4g..4g+3
             u32x2 pk;
             pk[0] = pack2(acc2[0], acc2[1]);
             pk[1] = pack2(acc2[2], acc2[3]);
             __builtin_amdgcn_raw_buffer_store_b64(pk, ro, o_vo, 16 * I * ostride, 0);
         }
-        __builtin_amdgcn_sched_barrier(0);
     }
     // ---- S <- Diag(gamma) (S + Kt^T U)  (= Diag(gamma) S + Kb^T U with Kb = Kt gamma)
-    const float* gam = reinterpret_cast<const float*>(lds + kOffGam) + vbuf * 128;
+    const float* gam = reinterpret_cast<const float*>(lds + kOffGam) + ebuf * 128;
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) {
         const float4 gm = *reinterpret_cast<const float4*>(gam + 16 * cb + 4 * g);
         f32x4 acc3 = S[cb];
-        acc3 = mfma_bf16(ld_kbt(lds, o, kbt, cb, 0), ub[0], acc3);
-        acc3 = mfma_bf16(ld_kbt(lds, o, kbt, cb, 1), ub[1], acc3);
+        acc3 = mfma_bf16(ld_kbt(lds, o, kOffKbT, cb, 0), ub[0], acc3);
+        acc3 = mfma_bf16(ld_kbt(lds, o, kOffKbT, cb, 1), ub[1], acc3);
         S[cb] = f32x4{acc3[0] * gm.x, acc3[1] * gm.y, acc3[2] * gm.z, acc3[3] * gm.w};
         if (cb & 1) __builtin_amdgcn_sched_barrier(0);
     }
@@ -805,7 +842,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
         uint4* z = reinterpret_cast<uint4*>(lds + kOffAneg);
         const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) z[tid + i * kThreads] = zero;  // 2 x 512 x 16 = 16384 bytes
+        for (int i = tid; i < 1024; i += kThreads) z[i] = zero;  // 1024 x 16 = 16384 bytes
     }
 
     // Both roles run the same sequence of periods (the loop control is
@@ -834,9 +871,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
 
         bf16raw* o = static_cast<bf16raw*>(a.o);
         const int ostride = a.H * int(dv) * 2;
-        RawV V;
         int lv = 0;  // length of chunk tv
-        if (tk < eos) load_rawv(V, a, token_row(a, brow, tk, h), int(eos - tk < kC ? eos - tk : kC), j0, wave, lane0);
         while (tk < eos || tv >= 0) {
             const bool has_k = tk < eos, has_v = tv >= 0;
             const int L = has_k ? int(eos - tk < kC ? eos - tk : kC) : 0;
@@ -848,21 +883,17 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
             __asm__ volatile("" : "+v"(r), "+v"(g), "+v"(lane));
             const int step = has_k ? chunk_step(lds, L) : 0;
             if (has_k && wave == 0) value_gamma(lds, step, kbuf, lane);  // read by the next period's update
+
             if (has_v) {
-                f32x4 X[4], OT[4];
-                value_xo(lds, lane_offsets(r, g), S, X, OT, lv, kbuf ^ 1, wave, r, g);
                 const rsrc_t ro = make_rsrc(o + token_row(a, brow, tv, h) * dv + j0,
                                             uint32_t(lv - 1) * uint32_t(ostride) + kDVT * 2);
-                value_solve(lds, lane_offsets(r, g), S, X, OT, kbuf ^ 1, ro, ostride, lv, wave, r, g);
+                value_chunk(lds, lane_offsets(r, g), S, lv, kbuf ^ 1, ro, ostride, wave, r, g);
             }
             const int64_t tn = tk + step;
-            if (has_k) {
-                prep_z(lds, V, wave, lane);  // after value_xo has read this wavefront's z of chunk tv
-                if (tn < eos)
-                    load_rawv(V, a, token_row(a, brow, tn, h), int(eos - tn < kC ? eos - tn : kC), j0, wave, lane);
-            }
+
             lds_barrier();  // B1: tiles of chunk tk visible; A, P, T and Kt^T of chunk tv consumed
             if (has_k) {
+
                 const LaneOffs lk = lane_offsets(r, g);
                 if (wave == kTWave)
                     t_work(lds, lk, kbuf, r, g);
@@ -895,39 +926,53 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
             if (lane0 < 32) reinterpret_cast<float4*>(lds + kOffPh)[kPhOnes * 32 + lane0] = one;
         }
         RawK R;
-        float al[4][8], ex[8];  // clamped alpha and decay products of chunk tk
+        RawVK V;                // v, w of chunk tk, loaded in the period before
+        float al[2][8], ex[8];  // clamped alpha and decay products of chunk tk
         if (tk < eos) {
             const int L = int(eos - tk < kC ? eos - tk : kC);
             const RawSrc src = raw_src(a, token_row(a, brow, tk, h), L);
+            const KeyLane K = key_lane(kw, lane0);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) load_alpha(R, src, t, kw, lane0);
+            for (int t = 0; t < 2; ++t) load_alpha(R, src, t, K);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) load_qkb(R, src, t, kw, lane0);
-            decay_pass1(lds, R, al, ex, L, kw, lane0);
+            for (int t = 0; t < 2; ++t) {
+                load_q(R, src, t, K);
+                load_kb(R, src, t, K);
+            }
+            load_vk(V, a, token_row(a, brow, tk, h), L, j0, kw, lane0);
+            decay_pass1(lds, R, al, ex, L, K, lane0);
         }
         while (tk < eos || tv >= 0) {
             const bool has_k = tk < eos;
             const int L = has_k ? int(eos - tk < kC ? eos - tk : kC) : 0;
             lds_barrier();  // B0
-            int r = r0, g = g0, lane = lane0;  // opaque per period (see the value loop)
-            __asm__ volatile("" : "+v"(r), "+v"(g), "+v"(lane));
-            (void)r;
-            (void)g;
+            int lane = lane0;  // opaque per period (see the value loop)
+            __asm__ volatile("" : "+v"(lane));
+            const KeyLane K = key_lane(kw, lane);
             const int step = has_k ? chunk_step(lds, L) : 0;
             const int64_t tn = tk + step;
             const int Ln = has_k && tn < eos ? int(eos - tn < kC ? eos - tn : kC) : 0;
             // the next chunk's window (empty past the sequence end: loads read zero)
             const RawSrc nxt = raw_src(a, token_row(a, brow, Ln > 0 ? tn : tk, h), Ln);
-            uint32_t kbp[2][8];
+            uint32_t kbp[8];
             if (has_k) {
-                if (16 * kw + 16 <= step)
-                    prep_tiles<true>(lds, R, nxt, al, ex, kbp, step, kbuf, kw, lane);
+                if (16 * K.tb + 16 <= step)
+                    prep_tiles<true>(lds, R, nxt, al, ex, kbp, step, kbuf, K);
                 else
-                    prep_tiles<false>(lds, R, nxt, al, ex, kbp, step, kbuf, kw, lane);
+                    prep_tiles<false>(lds, R, nxt, al, ex, kbp, step, kbuf, K);
             }
             lds_barrier();  // B1
-            if (has_k) store_kbt(lds, kbp, kw, lane);
-            if (Ln > 0) decay_pass1(lds, R, al, ex, Ln, kw, lane);
+            if (has_k) {
+                // k and b of the next chunk: issued here so that the memory pipe
+                // stays busy in this half of the period as well
+#pragma unroll
+                for (int t = 0; t < 2; ++t) load_kb(R, nxt, t, K);
+                store_kbt(lds, kbp, K);
+                // z of chunk tk (read by the value side next period), then v, w of the next chunk
+                store_z(lds, V, kbuf, kw, lane);
+                load_vk(V, a, token_row(a, brow, Ln > 0 ? tn : tk, h), Ln, j0, kw, lane);
+            }
+            if (Ln > 0) decay_pass1(lds, R, al, ex, Ln, K, lane);
             tv = has_k ? tk : -1;
             tk = has_k ? tn : eos;
             kbuf ^= 1;
