@@ -259,8 +259,6 @@ __device__ __forceinline__ float dpp(float x)
 {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
-constexpr int kQuadPrev = 0x90;   // quad_perm(0, 0, 1, 2): lane i <- lane i - 1 (lane 0 <- itself)
-constexpr int kQuadPrev2 = 0x40;  // quad_perm(0, 0, 0, 1): lanes 2, 3 <- lanes 0, 1
 constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128;
 constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114;  // lane i <- lane i - k of its row of 16
 
@@ -337,11 +335,6 @@ __device__ __forceinline__ KeyLane key_lane(int kw, int lane)
     k.c0 = 64 * k.ch + 8 * k.cg;
     return k;
 }
-// A value wavefront's share of v and w: its own 16 columns of the tile for all
-// 64 tokens of the chunk; lane l takes token l.
-struct RawV {
-    uint4 v[2], w[2];
-};
 
 // Global row of (token t0, head h) in [B*T, H] order.
 __device__ __forceinline__ int64_t token_row(const ChunkArgs& a, int64_t brow, int64_t t0, int h)
@@ -405,21 +398,6 @@ __device__ __forceinline__ void store_z(unsigned char* lds, const RawVK& V, int 
     unpack8(V.w, w);
 #pragma unroll
     for (int m = 0; m < 8; ++m) lds_st<float>(zs, zs_off((col & 15) + m, tok), v[m] * w[m]);
-}
-__device__ __forceinline__ void load_rawv(RawV& V, const ChunkArgs& a, int64_t row0, int L, int j0, int wave,
-                                          int lane)
-{
-    const uint32_t vstride = uint32_t(a.H) * uint32_t(a.dv) * 2;
-    const uint32_t win = L > 0 ? uint32_t(L - 1) * vstride + 32u : 0u;
-    const int64_t base = row0 * a.dv + j0 + 16 * wave;
-    const rsrc_t rv = make_rsrc(static_cast<const bf16raw*>(a.v) + base, win);
-    const rsrc_t rw = make_rsrc(static_cast<const bf16raw*>(a.w) + base, win);
-    const uint32_t off = uint32_t(lane) * vstride;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        V.v[u] = ld_b128(rv, off + 16 * u);
-        V.w[u] = ld_b128(rw, off + 16 * u);
-    }
 }
 
 // Alpha of channel c of token t of this lane, as loaded.
@@ -609,21 +587,6 @@ __device__ __forceinline__ void store_kbt(unsigned char* lds, const uint32_t* kb
     const PrepOffs po = prep_offsets(K.tok0, K.c0);
 #pragma unroll
     for (int c = 0; c < 8; ++c) lds_st<uint32_t>(lds, (po.kbt ^ (kbt_swz(c) << 3)) + 128 * c, kbp[c]);
-}
-
-// z = w v of the chunk into this wavefront's Zs: columns 16 wave .. + 15 of
-// the tile, token lane (rows past the chunk are masked when read).
-__device__ __forceinline__ void prep_z(unsigned char* lds, const RawV& V, int wave, int lane)
-{
-    unsigned char* zs = lds + kOffZs + wave * kZsWave;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        float v[8], w[8];
-        unpack8(V.v[u], v);
-        unpack8(V.w[u], w);
-#pragma unroll
-        for (int m = 0; m < 8; ++m) lds_st<float>(zs, zs_off(8 * u + m, lane), v[m] * w[m]);
-    }
 }
 
 // One block of A or P (16 x 16 over K = 128 channels), formed transposed:
