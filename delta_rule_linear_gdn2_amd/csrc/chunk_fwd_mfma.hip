@@ -314,10 +314,11 @@ struct RawK {
     uint4 q[2], k[2], b[2];  // 8 bf16 channels per token
     uint4 a[2][2];           // alpha, 8 FP32 channels per token
 };
-// A key wavefront's share of v and w (the workgroup's 64 value columns):
-// tokens 16 tb + (l & 15), columns 32 ch + 8 (l >> 4) .. + 7 of the tile.
+// v and w of the workgroup's 64 value columns, loaded by the key wavefronts of
+// channel half 0 (the others run behind them on their SIMDs): tokens
+// 16 tb + (l & 15), columns 8 (l >> 4) + 32 u .. + 7 of the tile.
 struct RawVK {
-    uint4 v, w;
+    uint4 v[2], w[2];
 };
 struct KeyLane {
     int tb, ch, tp, cg;
@@ -383,21 +384,28 @@ __device__ __forceinline__ void load_vk(RawVK& V, const ChunkArgs& a, int64_t ro
     const int64_t base = row0 * a.dv + j0;
     const rsrc_t rv = make_rsrc(static_cast<const bf16raw*>(a.v) + base, win);
     const rsrc_t rw = make_rsrc(static_cast<const bf16raw*>(a.w) + base, win);
-    const uint32_t off = uint32_t(16 * (kw & 3) + (lane & 15)) * vstride + 2 * (32 * (kw >> 2) + 8 * (lane >> 4));
-    V.v = ld_b128(rv, off);
-    V.w = ld_b128(rw, off);
+    const uint32_t off = uint32_t(16 * (kw & 3) + (lane & 15)) * vstride + 2 * (8 * (lane >> 4));
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        V.v[u] = ld_b128(rv, off + 64 * u);
+        V.w[u] = ld_b128(rw, off + 64 * u);
+    }
 }
 // z = w v of this key lane's eight columns into buffer buf of the z of the
 // value wavefront that owns them (rows past the chunk are masked when read).
 __device__ __forceinline__ void store_z(unsigned char* lds, const RawVK& V, int buf, int kw, int lane)
 {
-    const int tok = 16 * (kw & 3) + (lane & 15), col = 32 * (kw >> 2) + 8 * (lane >> 4);
-    unsigned char* zs = lds + kOffZs + buf * kZsBuf + (col >> 4) * kZsWave;
-    float v[8], w[8];
-    unpack8(V.v, v);
-    unpack8(V.w, w);
+    const int tok = 16 * (kw & 3) + (lane & 15);
 #pragma unroll
-    for (int m = 0; m < 8; ++m) lds_st<float>(zs, zs_off((col & 15) + m, tok), v[m] * w[m]);
+    for (int u = 0; u < 2; ++u) {
+        const int col = 32 * u + 8 * (lane >> 4);
+        unsigned char* zs = lds + kOffZs + buf * kZsBuf + (col >> 4) * kZsWave;
+        float v[8], w[8];
+        unpack8(V.v[u], v);
+        unpack8(V.w[u], w);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) lds_st<float>(zs, zs_off((col & 15) + m, tok), v[m] * w[m]);
+    }
 }
 
 // Alpha of channel c of token t of this lane, as loaded.
@@ -597,8 +605,14 @@ __device__ __forceinline__ void ap_block(unsigned char* lds, const LaneOffs& o, 
 {
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     const int rows = (KIND == 0 ? kOffEt : kOffQt) + ebuf * 16384;
+    bf16x8 ka[4], ra[4];  // operands issued together so that their latency overlaps
 #pragma unroll
-    for (int s = 0; s < 4; ++s) acc = mfma_bf16(ld_c128(lds, o, kOffKt, J, s), ld_c128(lds, o, rows, I, s), acc);
+    for (int s = 0; s < 4; ++s) {
+        ka[s] = ld_c128(lds, o, kOffKt, J, s);
+        ra[s] = ld_c128(lds, o, rows, I, s);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = mfma_bf16(ka[s], ra[s], acc);
     const int row = 16 * I + r, col = 16 * J + 4 * g;
     if (KIND == 0) {
         lds_st<uint2>(lds, kOffAneg + off_rc64(row, col),
@@ -653,9 +667,14 @@ __device__ __forceinline__ void t_work(unsigned char* lds, const LaneOffs& o, in
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        bf16x8 ea[4], ka[4];  // operands issued together so that their latency overlaps
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-            acc = mfma_bf16(ld_c128(lds, o, kOffEt + ebuf * 16384, I, s), ld_c128(lds, o, kOffKt, I, s), acc);
+        for (int s = 0; s < 4; ++s) {
+            ea[s] = ld_c128(lds, o, kOffEt + ebuf * 16384, I, s);
+            ka[s] = ld_c128(lds, o, kOffKt, I, s);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = mfma_bf16(ea[s], ka[s], acc);
         // acc[i] = A_II[4g + i][r]: column r, rows 4g..4g+3, strictly lower part
         float4 v;
         v.x = 4 * g + 0 > r ? acc[0] : 0.f;
@@ -732,16 +751,29 @@ __device__ __forceinline__ void value_chunk(const unsigned char* lds, const Lane
     bf16x8 ub[2];  // U as an operand over tokens 0..31 and 32..63; blocks not solved yet are zero
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-        f32x4 xe = zero4;
+        // this block's operands, issued together so that their latency overlaps
+        bf16x8 ea[4], qa[4], an[2], pa[2];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) xe = mfma_bf16(ld_c128(lds, o, et, I, s), sb[s], xe);
+        for (int s = 0; s < 4; ++s) ea[s] = ld_c128(lds, o, et, I, s);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) qa[s] = ld_c128(lds, o, qt, I, s);
+        if (I >= 1) an[0] = ld_s64(lds, o, kOffAneg, I, 0);
+        if (I >= 3) an[1] = ld_s64(lds, o, kOffAneg, I, 1);
+        pa[0] = ld_s64(lds, o, kOffP, I, 0);
+        if (I >= 2) pa[1] = ld_s64(lds, o, kOffP, I, 1);
         const float4 z = lds_ld<float4>(zs, zs_off(r, 16 * I + 4 * g));
+        const float4 tr = lds_ld<float4>(lds, kOffT + (I * kTBlk + r * kT16 + 4 * g) * 4);
+        f32x4 xe = zero4, xq = zero4;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            xe = mfma_bf16(ea[s], sb[s], xe);
+            xq = mfma_bf16(sb[s], qa[s], xq);
+        }
         const int t0 = 16 * I + 4 * g;
         f32x4 R_ = f32x4{t0 + 0 < lv ? z.x - xe[0] : 0.f, t0 + 1 < lv ? z.y - xe[1] : 0.f,
                          t0 + 2 < lv ? z.z - xe[2] : 0.f, t0 + 3 < lv ? z.w - xe[3] : 0.f};
-        if (I >= 1) R_ = mfma_bf16(ld_s64(lds, o, kOffAneg, I, 0), ub[0], R_);
-        if (I >= 3) R_ = mfma_bf16(ld_s64(lds, o, kOffAneg, I, 1), ub[1], R_);
-        const float4 tr = lds_ld<float4>(lds, kOffT + (I * kTBlk + r * kT16 + 4 * g) * 4);
+        if (I >= 1) R_ = mfma_bf16(an[0], ub[0], R_);
+        if (I >= 3) R_ = mfma_bf16(an[1], ub[1], R_);
         f32x4 u = zero4;
         u = mfma_f32(tr.x, R_[0], u);
         u = mfma_f32(tr.y, R_[1], u);
@@ -751,11 +783,8 @@ __device__ __forceinline__ void value_chunk(const unsigned char* lds, const Lane
         if (I == 1) ub[0] = pack_acc_pair_hi(ub[0], u);
         if (I == 2) ub[1] = pack_acc_pair(u, zero4);
         if (I == 3) ub[1] = pack_acc_pair_hi(ub[1], u);
-        f32x4 acc2 = zero4;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc2 = mfma_bf16(sb[s], ld_c128(lds, o, qt, I, s), acc2);
-        acc2 = mfma_bf16(ub[0], ld_s64(lds, o, kOffP, I, 0), acc2);
-        if (I >= 2) acc2 = mfma_bf16(ub[1], ld_s64(lds, o, kOffP, I, 1), acc2);
+        f32x4 acc2 = mfma_bf16(ub[0], pa[0], xq);
+        if (I >= 2) acc2 = mfma_bf16(ub[1], pa[1], acc2);
         if (16 * I + r < lv) {  // lane holds token 16 I + r, columns 4g..4g+3
             u32x2 pk;
             pk[0] = pack2(acc2[0], acc2[1]);
@@ -839,11 +868,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
             const bool has_k = tk < eos, has_v = tv >= 0;
             const int L = has_k ? int(eos - tk < kC ? eos - tk : kC) : 0;
             lds_barrier();  // B0: tiles of chunk tv, decay products of chunk tk visible
-            // Lane indices made opaque per period, so that the LDS addresses
-            // derived from them are recomputed here rather than held in
-            // registers across the whole loop.
-            int r = r0, g = g0, lane = lane0;
-            __asm__ volatile("" : "+v"(r), "+v"(g), "+v"(lane));
+            const int r = r0, g = g0, lane = lane0;
             const int step = has_k ? chunk_step(lds, L) : 0;
             if (has_k && wave == 0) value_gamma(lds, step, kbuf, lane);  // read by the next period's update
 
@@ -902,13 +927,14 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
                 load_q(R, src, t, K);
                 load_kb(R, src, t, K);
             }
-            load_vk(V, a, token_row(a, brow, tk, h), L, j0, kw, lane0);
+            if (K.ch == 0) load_vk(V, a, token_row(a, brow, tk, h), L, j0, kw, lane0);
             decay_pass1(lds, R, al, ex, L, K, lane0);
         }
         while (tk < eos || tv >= 0) {
             const bool has_k = tk < eos;
             const int L = has_k ? int(eos - tk < kC ? eos - tk : kC) : 0;
             lds_barrier();  // B0
+            if (kw >= 4) __builtin_amdgcn_s_setprio(1);
             int lane = lane0;  // opaque per period (see the value loop)
             __asm__ volatile("" : "+v"(lane));
             const KeyLane K = key_lane(kw, lane);
@@ -925,6 +951,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
                     prep_tiles<false>(lds, R, nxt, al, ex, kbp, step, kbuf, K);
             }
             lds_barrier();  // B1
+            if (kw >= 4) __builtin_amdgcn_s_setprio(0);
             if (has_k) {
                 // k and b of the next chunk: issued here so that the memory pipe
                 // stays busy in this half of the period as well
@@ -932,8 +959,10 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
                 for (int t = 0; t < 2; ++t) load_kb(R, nxt, t, K);
                 store_kbt(lds, kbp, K);
                 // z of chunk tk (read by the value side next period), then v, w of the next chunk
-                store_z(lds, V, kbuf, kw, lane);
-                load_vk(V, a, token_row(a, brow, Ln > 0 ? tn : tk, h), Ln, j0, kw, lane);
+                if (K.ch == 0) {
+                    store_z(lds, V, kbuf, kw, lane);
+                    load_vk(V, a, token_row(a, brow, Ln > 0 ? tn : tk, h), Ln, j0, kw, lane);
+                }
             }
             if (Ln > 0) decay_pass1(lds, R, al, ex, Ln, K, lane);
             tv = has_k ? tk : -1;
