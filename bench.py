@@ -217,6 +217,86 @@ def run_only(args):
     print(json.dumps(res), flush=True)
 
 
+def run_configs(args):
+    """Per-configuration report (not the headline line): one JSON line per
+    chunkwise workload and gate mode, one for decode and one for the oracle on
+    all host cores and on one.  The single-head-batch workload is timed over
+    three input sets in rotation so that repeats cannot be served from the
+    Infinity Cache."""
+    import torch
+
+    import oracle
+    from delta_rule_linear_gdn2_amd import binding
+    from delta_rule_linear_gdn2_amd import workloads as W
+
+    for name, modes, rotate in (("layer_bf16", ("gdn2",), 3), ("batched_bf16", ("gdn2",), 1),
+                                ("varlen32_bf16", ("gdn2", "kda", "gdn"), 1)):
+        for mode in modes:
+            sets = []
+            for i in range(rotate):
+                seed = None if i == 0 else W.WORKLOADS[name].seed + 100 * i
+                x = W.make(name, gate_mode=mode, seed=seed)
+                wl = x["workload"]
+                d = to_dev(x, wl.dtype)
+                d["s0"] = None if x["initial_state"] is None else torch.from_numpy(x["initial_state"]).cuda()
+                d["cu"] = None if x["cu_seqlens"] is None else torch.from_numpy(x["cu_seqlens"]).cuda()
+                sets.append(d)
+            B, T, H, dk = x["q"].shape
+            dv = x["v"].shape[-1]
+            N = B if x["cu_seqlens"] is None else len(x["cu_seqlens"]) - 1
+            o = torch.empty((B, T, H, dv), dtype=sets[0]["q"].dtype, device="cuda")
+            sf = torch.empty((N, H, dk, dv), dtype=torch.float32, device="cuda")
+            idx = [0]
+
+            def call():
+                d = sets[idx[0] % rotate]
+                idx[0] += 1
+                binding.gdn2_chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["b"], d["w"], d["s0"],
+                                       final_state=sf, out=o, cu_seqlens=d["cu"])
+
+            per, _, _ = time_events(call, args.warmup, args.steps)
+            kern_ms = float(np.median(per))
+            nbytes = chunk_bytes(B, T, H, dk, dv, N, 2 if wl.dtype == "bf16" else 4)
+            if x["initial_state"] is None:  # no state to read
+                nbytes -= N * H * dk * dv * 4
+            row = {"report": "config", "workload": name, "gate_mode": mode, "tokens": B * T,
+                   "sequences": N, "us_per_call": kern_ms * 1e3, "tokens_per_s": B * T / (kern_ms / 1e3),
+                   "GBps": nbytes / (kern_ms / 1e3) / 1e9,
+                   "hbm_frac": nbytes / (kern_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
+                   "input_sets": rotate, "timing": f"median of {args.steps} launches after {args.warmup}"}
+            log(f"{name}/{mode}: {row['us_per_call']:.1f} us, {row['tokens_per_s'] / 1e6:.1f} M tokens/s, "
+                f"{row['hbm_frac'] * 100:.1f}% HBM")
+            print(json.dumps(row), flush=True)
+            del sets
+    dec = bench_decode(args)
+    print(json.dumps({"report": "config", "workload": "decode_b256", "us_per_step": dec["step_ms"] * 1e3,
+                      "state_GBps": dec["state_gbps"], "hbm_frac": dec["achieved"] / HBM_PEAK_GBPS}),
+          flush=True)
+    # the oracle: all cores on four sequences of the headline workload, one core on one (sequence, head)
+    x = W.make("batched_bf16")
+    wl = x["workload"]
+    cpu_all = cpu_baseline(x, wl, chains_rows=4)
+    sub = {n: np.ascontiguousarray(x[n][:1, :, :1]) for n in NAMES}
+    s0 = np.ascontiguousarray(x["initial_state"][:1, :1])
+    t0 = time.perf_counter()
+    oracle.recurrent(sub["q"], sub["k"], sub["v"], sub["alpha"], sub["b"], sub["w"], s0, threads=1)
+    one = time.perf_counter() - t0
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    print(json.dumps({"report": "oracle", "cpu_model": model, "nproc": os.cpu_count(),
+                      "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS"),
+                      "all_cores": cpu_all,
+                      "one_core": {"value": wl.T / one, "unit": "token-heads/s", "cores": 1,
+                                   "sample": f"1 sequence x 1 head x {wl.T} tokens, {one:.2f} s"}}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -229,6 +309,9 @@ def main():
                     help="profiling aid: run one part only and print its timing line "
                          "(copy = a plain 1 GiB device copy, the reference for HBM byte counters)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--configs", action="store_true",
+                    help="report every configuration (chunkwise workloads, gate modes, decode, oracle) "
+                         "as separate JSON lines instead of the headline line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -243,6 +326,8 @@ def main():
     binding.load()
     if args.only:
         return run_only(args)
+    if args.configs:
+        return run_configs(args)
     ch = bench_chunk(args)
     dec = None if args.no_decode else bench_decode(args)
     cpu = None
