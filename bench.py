@@ -35,12 +35,18 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def chunk_bytes(B, T, H, dk, dv, N, eb=2):
+def chunk_bytes(B, T, H, dk, dv, N, eb=2, gates=0):
     """Algorithmic HBM bytes of one chunkwise forward: q, k, b, v, w read and
     o written in the input dtype, alpha read in FP32, the state read once and
-    written once in FP32."""
+    written once in FP32.  A scalar gate (gate layout flags 1 erase, 2 write,
+    8 decay) is one value per token and head; a tied write gate (4) is not
+    read."""
     tok = B * T * H
-    return tok * (3 * dk * eb + 2 * dv * eb + dk * 4 + dv * eb) + 2 * N * H * dk * dv * 4
+    erase = eb if gates & 1 else dk * eb
+    write = 0 if gates & 4 else eb if gates & 2 else dv * eb
+    gate = erase + write
+    decay = 4 if gates & 8 else dk * 4
+    return tok * (2 * dk * eb + dv * eb + gate + decay + dv * eb) + 2 * N * H * dk * dv * 4
 
 
 def chunk_flops(lengths, H, dk, dv, C=64):
@@ -229,9 +235,14 @@ def run_configs(args):
     from delta_rule_linear_gdn2_amd import binding
     from delta_rule_linear_gdn2_amd import workloads as W
 
-    for name, modes, rotate in (("layer_bf16", ("gdn2",), 3), ("batched_bf16", ("gdn2",), 1),
-                                ("varlen32_bf16", ("gdn2", "kda", "gdn"), 1)):
-        for mode in modes:
+    full, tied, scalar = binding.GATES_FULL, binding.GATES_KDA, binding.GATES_GDN
+    # (gate mode of the inputs, layout passed): the reduced-gate inputs run once
+    # broadcast through the full layout and once in their compact layout
+    for name, modes, rotate in (("layer_bf16", (("gdn2", full),), 3),
+                                ("batched_bf16", (("gdn2", full), ("kda", tied), ("gdn", scalar)), 1),
+                                ("varlen32_bf16", (("gdn2", full), ("kda", full), ("kda", tied), ("gdn", full),
+                                                   ("gdn", scalar)), 1)):
+        for mode, gates in modes:
             sets = []
             for i in range(rotate):
                 seed = None if i == 0 else W.WORKLOADS[name].seed + 100 * i
@@ -240,6 +251,12 @@ def run_configs(args):
                 d = to_dev(x, wl.dtype)
                 d["s0"] = None if x["initial_state"] is None else torch.from_numpy(x["initial_state"]).cuda()
                 d["cu"] = None if x["cu_seqlens"] is None else torch.from_numpy(x["cu_seqlens"]).cuda()
+                if gates != full:  # compact gates: beta [..], alpha [..] for scalar decay
+                    d["b"] = d["b"][..., 0].contiguous()
+                    d["w"] = None
+                    if gates == scalar:
+                        d["alpha"] = d["alpha"][..., 0].contiguous()
+                    torch.cuda.synchronize()
                 sets.append(d)
             B, T, H, dk = x["q"].shape
             dv = x["v"].shape[-1]
@@ -251,20 +268,21 @@ def run_configs(args):
             def call():
                 d = sets[idx[0] % rotate]
                 idx[0] += 1
-                binding.gdn2_chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["b"], d["w"], d["s0"],
-                                       final_state=sf, out=o, cu_seqlens=d["cu"])
+                binding.gdn2_chunk_fwd_gates(d["q"], d["k"], d["v"], d["alpha"], d["b"], d["w"], gates, d["s0"],
+                                             final_state=sf, out=o, cu_seqlens=d["cu"])
 
             per, _, _ = time_events(call, args.warmup, args.steps)
             kern_ms = float(np.median(per))
-            nbytes = chunk_bytes(B, T, H, dk, dv, N, 2 if wl.dtype == "bf16" else 4)
+            nbytes = chunk_bytes(B, T, H, dk, dv, N, 2 if wl.dtype == "bf16" else 4, gates)
             if x["initial_state"] is None:  # no state to read
                 nbytes -= N * H * dk * dv * 4
-            row = {"report": "config", "workload": name, "gate_mode": mode, "tokens": B * T,
+            layout = {full: "full", tied: "kda (flags 5)", scalar: "gdn (flags 13)"}[gates]
+            row = {"report": "config", "workload": name, "gate_mode": mode, "gate_layout": layout, "tokens": B * T,
                    "sequences": N, "us_per_call": kern_ms * 1e3, "tokens_per_s": B * T / (kern_ms / 1e3),
                    "GBps": nbytes / (kern_ms / 1e3) / 1e9,
                    "hbm_frac": nbytes / (kern_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
                    "input_sets": rotate, "timing": f"median of {args.steps} launches after {args.warmup}"}
-            log(f"{name}/{mode}: {row['us_per_call']:.1f} us, {row['tokens_per_s'] / 1e6:.1f} M tokens/s, "
+            log(f"{name}/{mode}/{layout}: {row['us_per_call']:.1f} us, {row['tokens_per_s'] / 1e6:.1f} M tokens/s, "
                 f"{row['hbm_frac'] * 100:.1f}% HBM")
             print(json.dumps(row), flush=True)
             del sets

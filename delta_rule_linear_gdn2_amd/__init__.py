@@ -5,23 +5,43 @@ Two entry points, both hand-written HIP behind the C ABI in include/gdn2.h:
 * ``gdn2_chunk_fwd``      chunkwise WY forward over whole sequences (64-token
                           chunks; varlen via ``cu_seqlens``)
 * ``gdn2_recurrent_step`` fused single-token decode step, state updated in place
+* ``gdn2_chunk_fwd_gates`` / ``gdn2_recurrent_step_gates``: the same with a gate
+  layout (``GATES_*`` flags: scalar erase, write or decay gates, tied write gate)
 
 Importing the package does not load the library; the first call does.
 """
 from .binding import (  # noqa: F401
+    GATES_FULL,
+    GATES_GDN,
+    GATES_KDA,
+    GATES_SCALAR_DECAY,
+    GATES_SCALAR_ERASE,
+    GATES_SCALAR_WRITE,
+    GATES_TIED,
     Gdn2Error,
     gdn2_chunk_fwd,
+    gdn2_chunk_fwd_gates,
     gdn2_chunk_fwd_workspace_bytes,
     gdn2_recurrent_step,
+    gdn2_recurrent_step_gates,
     load,
     status_string,
 )
 
 __all__ = [
+    "GATES_FULL",
+    "GATES_GDN",
+    "GATES_KDA",
+    "GATES_SCALAR_DECAY",
+    "GATES_SCALAR_ERASE",
+    "GATES_SCALAR_WRITE",
+    "GATES_TIED",
     "Gdn2Error",
     "gdn2_chunk_fwd",
+    "gdn2_chunk_fwd_gates",
     "gdn2_chunk_fwd_workspace_bytes",
     "gdn2_recurrent_step",
+    "gdn2_recurrent_step_gates",
     "load",
     "status_string",
 ]

@@ -22,8 +22,14 @@ STATUS_NAMES = {
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 
-EXPORTS = ("gdn2_chunk_fwd", "gdn2_chunk_fwd_workspace_bytes", "gdn2_recurrent_step",
-           "gdn2_status_string", "gdn2_version")
+EXPORTS = ("gdn2_chunk_fwd", "gdn2_chunk_fwd_gates", "gdn2_chunk_fwd_workspace_bytes",
+           "gdn2_recurrent_step", "gdn2_recurrent_step_gates", "gdn2_status_string", "gdn2_version")
+
+# gdn2_gate_flags: layout of the gates (b, w, alpha), OR-ed together
+GATES_FULL, GATES_SCALAR_ERASE, GATES_SCALAR_WRITE, GATES_TIED, GATES_SCALAR_DECAY = 0, 1, 2, 4, 8
+GATES_KDA = GATES_SCALAR_ERASE | GATES_TIED
+GATES_GDN = GATES_KDA | GATES_SCALAR_DECAY
+VALID_GATES = (0, 1, 2, 3, 5, 8, 9, 10, 11, 13)
 
 
 class Gdn2Error(RuntimeError):
@@ -62,10 +68,14 @@ def load(path: str = LIB_PATH):
     P, I, Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     lib.gdn2_chunk_fwd.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, Z, P]
     lib.gdn2_chunk_fwd.restype = ctypes.c_int
+    lib.gdn2_chunk_fwd_gates.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P, Z, P]
+    lib.gdn2_chunk_fwd_gates.restype = ctypes.c_int
     lib.gdn2_chunk_fwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     lib.gdn2_chunk_fwd_workspace_bytes.restype = Z
     lib.gdn2_recurrent_step.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, P]
     lib.gdn2_recurrent_step.restype = ctypes.c_int
+    lib.gdn2_recurrent_step_gates.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, P]
+    lib.gdn2_recurrent_step_gates.restype = ctypes.c_int
     lib.gdn2_status_string.argtypes = [ctypes.c_int]
     lib.gdn2_status_string.restype = ctypes.c_char_p
     lib.gdn2_version.argtypes = []
@@ -118,16 +128,18 @@ def gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, num_seqs, dtype_code) -> int
     return int(load().gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, num_seqs, dtype_code))
 
 
-def gdn2_chunk_fwd(q, k, v, alpha, b, w, initial_state=None, *, output_final_state=True,
-                   final_state=None, out=None, cu_seqlens=None, stream=None):
-    """Chunkwise GDN-2 forward.  Returns ``(o, final_state)`` (final_state may be None).
+def _gate_widths(gates, dk, dv):
+    """Trailing sizes of (b, w, alpha) for a gate layout (w None: not used)."""
+    if gates not in VALID_GATES:
+        raise ValueError(f"gates must be one of {VALID_GATES} (got {gates})")
+    bw = () if gates & GATES_SCALAR_ERASE else (dk,)
+    ww = None if gates & GATES_TIED else () if gates & GATES_SCALAR_WRITE else (dv,)
+    aw = () if gates & GATES_SCALAR_DECAY else (dk,)
+    return bw, ww, aw
 
-    q, k, b: [B, T, H, dk]; v, w: [B, T, H, dv] (float32 or bfloat16, all the
-    same); alpha: [B, T, H, dk] float32; initial_state: [N, H, dk, dv] float32
-    or None; cu_seqlens: int32 [N + 1] on the device or None (then B must be 1).
-    ``final_state`` may be passed (e.g. the initial_state tensor itself for an
-    in-place update); otherwise it is allocated when ``output_final_state``.
-    """
+
+def _chunk_fwd(q, k, v, alpha, b, w, gates, initial_state, output_final_state, final_state, out,
+               cu_seqlens, stream):
     import torch
 
     lib = load()
@@ -136,9 +148,15 @@ def gdn2_chunk_fwd(q, k, v, alpha, b, w, initial_state=None, *, output_final_sta
     dev, dt = q.device, q.dtype
     code = _dtype_code(dt)
     N = B if cu_seqlens is None else int(cu_seqlens.shape[0]) - 1
-    for name, t, width in (("q", q, dk), ("k", k, dk), ("b", b, dk), ("v", v, dv), ("w", w, dv)):
+    bw, ww, aw = _gate_widths(gates, dk, dv)
+    for name, t, width in (("q", q, dk), ("k", k, dk), ("v", v, dv)):
         _check(name, t, (B, T, H, width), dt, dev)
-    _check("alpha", alpha, (B, T, H, dk), torch.float32, dev)
+    _check("b", b, (B, T, H) + bw, dt, dev)
+    if ww is not None:
+        _check("w", w, (B, T, H) + ww, dt, dev)
+    else:
+        w = None
+    _check("alpha", alpha, (B, T, H) + aw, torch.float32, dev)
     if initial_state is not None:
         _check("initial_state", initial_state, (N, H, dk, dv), torch.float32, dev)
     if cu_seqlens is not None:
@@ -153,12 +171,73 @@ def gdn2_chunk_fwd(q, k, v, alpha, b, w, initial_state=None, *, output_final_sta
         _check("final_state", final_state, (N, H, dk, dv), torch.float32, dev)
     ws_bytes = gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, code)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
-    rc = lib.gdn2_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w),
-                            _ptr(initial_state), _ptr(final_state), _ptr(out), _ptr(cu_seqlens),
-                            B, T, H, dk, dv, N, code, _ptr(ws), ws_bytes, _stream(stream))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(initial_state), _ptr(final_state),
+            _ptr(out), _ptr(cu_seqlens), B, T, H, dk, dv, N, code)
+    tail = (_ptr(ws), ws_bytes, _stream(stream))
+    if gates == GATES_FULL:
+        rc, name = lib.gdn2_chunk_fwd(*args, *tail), "gdn2_chunk_fwd"
+    else:
+        rc, name = lib.gdn2_chunk_fwd_gates(*args, gates, *tail), "gdn2_chunk_fwd_gates"
     if rc != GDN2_OK:
-        raise Gdn2Error(rc, "gdn2_chunk_fwd")
+        raise Gdn2Error(rc, name)
     return out, final_state
+
+
+def gdn2_chunk_fwd(q, k, v, alpha, b, w, initial_state=None, *, output_final_state=True,
+                   final_state=None, out=None, cu_seqlens=None, stream=None):
+    """Chunkwise GDN-2 forward.  Returns ``(o, final_state)`` (final_state may be None).
+
+    q, k, b: [B, T, H, dk]; v, w: [B, T, H, dv] (float32 or bfloat16, all the
+    same); alpha: [B, T, H, dk] float32; initial_state: [N, H, dk, dv] float32
+    or None; cu_seqlens: int32 [N + 1] on the device or None (then B must be 1).
+    ``final_state`` may be passed (e.g. the initial_state tensor itself for an
+    in-place update); otherwise it is allocated when ``output_final_state``.
+    """
+    return _chunk_fwd(q, k, v, alpha, b, w, GATES_FULL, initial_state, output_final_state, final_state, out,
+                      cu_seqlens, stream)
+
+
+def gdn2_chunk_fwd_gates(q, k, v, alpha, b, w, gates, initial_state=None, *, output_final_state=True,
+                         final_state=None, out=None, cu_seqlens=None, stream=None):
+    """gdn2_chunk_fwd with a gate layout, an OR of the GATES_* flags:
+    SCALAR_ERASE takes b as [B, T, H]; SCALAR_WRITE takes w as [B, T, H];
+    TIED (with SCALAR_ERASE) uses b as the write gate too (w ignored, may be
+    None); SCALAR_DECAY takes alpha as [B, T, H] float32.  GATES_FULL is
+    gdn2_chunk_fwd; GATES_KDA and GATES_GDN are the two reductions."""
+    return _chunk_fwd(q, k, v, alpha, b, w, gates, initial_state, output_final_state, final_state, out,
+                      cu_seqlens, stream)
+
+
+def _recurrent_step(q, k, v, alpha, b, w, gates, state, out, stream):
+    import torch
+
+    lib = load()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(dt)
+    bw, ww, aw = _gate_widths(gates, dk, dv)
+    for name, t, width in (("q", q, dk), ("k", k, dk), ("v", v, dv)):
+        _check(name, t, (N, H, width), dt, dev)
+    _check("b", b, (N, H) + bw, dt, dev)
+    if ww is not None:
+        _check("w", w, (N, H) + ww, dt, dev)
+    else:
+        w = None
+    _check("alpha", alpha, (N, H) + aw, torch.float32, dev)
+    _check("state", state, (N, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=dt, device=dev)
+    else:
+        _check("out", out, (N, H, dv), dt, dev)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(state), _ptr(out), N, H, dk, dv, code)
+    if gates == GATES_FULL:
+        rc, name = lib.gdn2_recurrent_step(*args, _stream(stream)), "gdn2_recurrent_step"
+    else:
+        rc, name = lib.gdn2_recurrent_step_gates(*args, gates, _stream(stream)), "gdn2_recurrent_step_gates"
+    if rc != GDN2_OK:
+        raise Gdn2Error(rc, name)
+    return out
 
 
 def gdn2_recurrent_step(q, k, v, alpha, b, w, state, *, out=None, stream=None):
@@ -167,23 +246,10 @@ def gdn2_recurrent_step(q, k, v, alpha, b, w, state, *, out=None, stream=None):
     q, k, b: [N, H, dk]; v, w: [N, H, dv]; alpha: [N, H, dk] float32;
     state: [N, H, dk, dv] float32.
     """
-    import torch
+    return _recurrent_step(q, k, v, alpha, b, w, GATES_FULL, state, out, stream)
 
-    lib = load()
-    N, H, dk = q.shape
-    dv = v.shape[-1]
-    dev, dt = q.device, q.dtype
-    code = _dtype_code(dt)
-    for name, t, width in (("q", q, dk), ("k", k, dk), ("b", b, dk), ("v", v, dv), ("w", w, dv)):
-        _check(name, t, (N, H, width), dt, dev)
-    _check("alpha", alpha, (N, H, dk), torch.float32, dev)
-    _check("state", state, (N, H, dk, dv), torch.float32, dev)
-    if out is None:
-        out = torch.empty((N, H, dv), dtype=dt, device=dev)
-    else:
-        _check("out", out, (N, H, dv), dt, dev)
-    rc = lib.gdn2_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w),
-                                 _ptr(state), _ptr(out), N, H, dk, dv, code, _stream(stream))
-    if rc != GDN2_OK:
-        raise Gdn2Error(rc, "gdn2_recurrent_step")
-    return out
+
+def gdn2_recurrent_step_gates(q, k, v, alpha, b, w, gates, state, *, out=None, stream=None):
+    """gdn2_recurrent_step with a gate layout (see gdn2_chunk_fwd_gates); a
+    scalar gate is [N, H]."""
+    return _recurrent_step(q, k, v, alpha, b, w, gates, state, out, stream)

@@ -310,6 +310,11 @@ __device__ __forceinline__ uint4 ld_b128(rsrc_t r, uint32_t off)
 // tokens 16 tb .. 16 tb + 15 (tb = kw & 3) in channels 64 ch .. 64 ch + 63
 // (ch = kw >> 2); lane l takes tokens 16 tb + 2 (l & 7) + {0, 1} and channels
 // 64 ch + 8 (l >> 3) .. + 7 (eight consecutive lanes hold the block's 16 tokens).
+//
+// Gate layouts (template parameter G, gdn2_gate_flags): a scalar gate is one
+// value per token and head, read once per token and applied to every channel
+// of its axis.  A scalar erase gate sits in b[t].x (bf16 bits), a scalar or
+// tied write gate in w[0].x of RawVK, a scalar decay in a[t][0].x.
 struct RawK {
     uint4 q[2], k[2], b[2];  // 8 bf16 channels per token
     uint4 a[2][2];           // alpha, 8 FP32 channels per token
@@ -348,15 +353,23 @@ struct RawSrc {
     rsrc_t q, k, b, a;
     uint32_t kstride;  // bytes per token, bf16 key rows
 };
+template <int G>
 __device__ __forceinline__ RawSrc raw_src(const ChunkArgs& a, int64_t row0, int L)
 {
     RawSrc s;
     s.kstride = uint32_t(a.H) * kDK * 2;
     const uint32_t win = L > 0 ? uint32_t(L - 1) * s.kstride + kDK * 2 : 0u;  // 0: every load reads zero
+    const uint32_t rows = L > 0 ? uint32_t(L - 1) * uint32_t(a.H) + 1 : 0u;   // per-token scalars
     s.q = make_rsrc(static_cast<const bf16raw*>(a.q) + row0 * kDK, win);
     s.k = make_rsrc(static_cast<const bf16raw*>(a.k) + row0 * kDK, win);
-    s.b = make_rsrc(static_cast<const bf16raw*>(a.b) + row0 * kDK, win);
-    s.a = make_rsrc(a.alpha + row0 * kDK, 2 * win);
+    if (G & kScalarErase)
+        s.b = make_rsrc(static_cast<const bf16raw*>(a.b) + row0, 2 * rows);
+    else
+        s.b = make_rsrc(static_cast<const bf16raw*>(a.b) + row0 * kDK, win);
+    if (G & kScalarDecay)
+        s.a = make_rsrc(a.alpha + row0, 4 * rows);
+    else
+        s.a = make_rsrc(a.alpha + row0 * kDK, 2 * win);
     return s;
 }
 // Loads token t (of two) of this lane: q, k, b, and alpha.
@@ -364,35 +377,55 @@ __device__ __forceinline__ void load_q(RawK& R, const RawSrc& s, int t, const Ke
 {
     R.q[t] = ld_b128(s.q, uint32_t(K.tok0 + t) * s.kstride + 2 * K.c0);
 }
+template <int G>
 __device__ __forceinline__ void load_kb(RawK& R, const RawSrc& s, int t, const KeyLane& K)
 {
     const uint32_t off = uint32_t(K.tok0 + t) * s.kstride + 2 * K.c0;
     R.k[t] = ld_b128(s.k, off);
-    R.b[t] = ld_b128(s.b, off);
+    if (G & kScalarErase)  // one bf16 per token (the token stride of a scalar row is kstride / 128)
+        R.b[t].x = __builtin_amdgcn_raw_buffer_load_b16(s.b, int(uint32_t(K.tok0 + t) * (s.kstride >> 7)), 0, 0);
+    else
+        R.b[t] = ld_b128(s.b, off);
 }
+template <int G>
 __device__ __forceinline__ void load_alpha(RawK& R, const RawSrc& s, int t, const KeyLane& K)
 {
+    if (G & kScalarDecay) {  // one FP32 decay per token
+        R.a[t][0].x = __builtin_amdgcn_raw_buffer_load_b32(s.a, int(uint32_t(K.tok0 + t) * (s.kstride >> 6)), 0, 0);
+        return;
+    }
     const uint32_t off = 2 * uint32_t(K.tok0 + t) * s.kstride + 4 * K.c0;
     R.a[t][0] = ld_b128(s.a, off);
     R.a[t][1] = ld_b128(s.a, off + 16);
 }
 
+template <int G>
 __device__ __forceinline__ void load_vk(RawVK& V, const ChunkArgs& a, int64_t row0, int L, int j0, int kw, int lane)
 {
     const uint32_t vstride = uint32_t(a.H) * uint32_t(a.dv) * 2;
     const uint32_t win = L > 0 ? uint32_t(L - 1) * vstride + kDVT * 2 : 0u;
     const int64_t base = row0 * a.dv + j0;
+    const uint32_t tok = uint32_t(16 * (kw & 3) + (lane & 15));
     const rsrc_t rv = make_rsrc(static_cast<const bf16raw*>(a.v) + base, win);
-    const rsrc_t rw = make_rsrc(static_cast<const bf16raw*>(a.w) + base, win);
-    const uint32_t off = uint32_t(16 * (kw & 3) + (lane & 15)) * vstride + 2 * (8 * (lane >> 4));
+    const uint32_t off = tok * vstride + 2 * (8 * (lane >> 4));
+    if (G & (kTied | kScalarWrite)) {  // the token's scalar write gate (tied: its erase gate)
+        const uint32_t rows = L > 0 ? uint32_t(L - 1) * uint32_t(a.H) + 1 : 0u;
+        const rsrc_t rg = make_rsrc(static_cast<const bf16raw*>(G & kTied ? a.b : a.w) + row0, 2 * rows);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        V.v[u] = ld_b128(rv, off + 64 * u);
-        V.w[u] = ld_b128(rw, off + 64 * u);
+        for (int u = 0; u < 2; ++u) V.v[u] = ld_b128(rv, off + 64 * u);
+        V.w[0].x = __builtin_amdgcn_raw_buffer_load_b16(rg, int(tok * uint32_t(a.H) * 2), 0, 0);
+    } else {
+        const rsrc_t rw = make_rsrc(static_cast<const bf16raw*>(a.w) + base, win);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            V.v[u] = ld_b128(rv, off + 64 * u);
+            V.w[u] = ld_b128(rw, off + 64 * u);
+        }
     }
 }
 // z = w v of this key lane's eight columns into buffer buf of the z of the
 // value wavefront that owns them (rows past the chunk are masked when read).
+template <int G>
 __device__ __forceinline__ void store_z(unsigned char* lds, const RawVK& V, int buf, int kw, int lane)
 {
     const int tok = 16 * (kw & 3) + (lane & 15);
@@ -402,15 +435,22 @@ __device__ __forceinline__ void store_z(unsigned char* lds, const RawVK& V, int 
         unsigned char* zs = lds + kOffZs + buf * kZsBuf + (col >> 4) * kZsWave;
         float v[8], w[8];
         unpack8(V.v[u], v);
-        unpack8(V.w[u], w);
+        if (G & (kTied | kScalarWrite)) {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) w[m] = lo_f(V.w[0].x);
+        } else {
+            unpack8(V.w[u], w);
+        }
 #pragma unroll
         for (int m = 0; m < 8; ++m) lds_st<float>(zs, zs_off((col & 15) + m, tok), v[m] * w[m]);
     }
 }
 
 // Alpha of channel c of token t of this lane, as loaded.
+template <int G>
 __device__ __forceinline__ float raw_alpha(const RawK& R, int t, int c)
 {
+    if (G & kScalarDecay) return __uint_as_float(R.a[t][0].x);
     const uint4 x = R.a[t][c >> 2];
     return __uint_as_float((c & 3) == 0 ? x.x : (c & 3) == 1 ? x.y : (c & 3) == 2 ? x.z : x.w);
 }
@@ -421,6 +461,7 @@ __device__ __forceinline__ float raw_alpha(const RawK& R, int t, int c)
 // Ph[4]) for this wavefront's channels and its smallest block product to
 // Ph[5][2 tb + ch]; returns the clamped alpha in al and in ex the product over
 // the block's tokens before this lane's two.
+template <int G>
 __device__ __forceinline__ void decay_pass1(unsigned char* lds, const RawK& R, float (*al)[8], float* ex, int L,
                                             const KeyLane& K, int lane)
 {
@@ -429,14 +470,14 @@ __device__ __forceinline__ void decay_pass1(unsigned char* lds, const RawK& R, f
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int c = 0; c < 8; ++c) al[t][c] = __builtin_amdgcn_fmed3f(raw_alpha(R, t, c), kAlphaMin, 1.0f);
+            for (int c = 0; c < 8; ++c) al[t][c] = __builtin_amdgcn_fmed3f(raw_alpha<G>(R, t, c), kAlphaMin, 1.0f);
     } else {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const bool live = K.tok0 + t < L;
 #pragma unroll
             for (int c = 0; c < 8; ++c)
-                al[t][c] = live ? __builtin_amdgcn_fmed3f(raw_alpha(R, t, c), kAlphaMin, 1.0f) : 1.0f;
+                al[t][c] = live ? __builtin_amdgcn_fmed3f(raw_alpha<G>(R, t, c), kAlphaMin, 1.0f) : 1.0f;
         }
     }
     const int tp = K.tp;
@@ -522,7 +563,7 @@ __device__ __forceinline__ void st_tok(unsigned char* lds, const PrepOffs& o, in
 // zero rows from zeroed q and k with a running decay of 1 (their own decay
 // factors are never formed).  Past the sequence end (step = L) the inputs
 // read as zero and alpha as 1, which gives zero rows as well.
-template <bool kAllLive>
+template <int G, bool kAllLive>
 __device__ __forceinline__ void prep_tiles(unsigned char* lds, RawK& R, const RawSrc& nxt, const float (*al)[8],
                                            const float* ex, uint32_t* kbp, int step, int ebuf, const KeyLane& K)
 {
@@ -557,11 +598,16 @@ __device__ __forceinline__ void prep_tiles(unsigned char* lds, RawK& R, const Ra
     const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-        load_alpha(R, nxt, t, K);  // alpha of token t of the next chunk (clamped copy in al)
+        load_alpha<G>(R, nxt, t, K);  // alpha of token t of the next chunk (clamped copy in al)
         float q[8], k[8], b[8];
         unpack8(kAllLive || live ? R.q[t] : zero, q);
         unpack8(kAllLive || live ? R.k[t] : zero, k);
-        unpack8(R.b[t], b);
+        if (G & kScalarErase) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) b[c] = lo_f(R.b[t].x);
+        } else {
+            unpack8(R.b[t], b);
+        }
         float et[8], qt[8], kt[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
@@ -805,6 +851,7 @@ __device__ __forceinline__ void value_chunk(const unsigned char* lds, const Lane
     }
 }
 
+template <int G>
 __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, int ntiles, int nchains)
 {
     extern __shared__ __align__(16) unsigned char lds[];
@@ -918,17 +965,17 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
         float al[2][8], ex[8];  // clamped alpha and decay products of chunk tk
         if (tk < eos) {
             const int L = int(eos - tk < kC ? eos - tk : kC);
-            const RawSrc src = raw_src(a, token_row(a, brow, tk, h), L);
+            const RawSrc src = raw_src<G>(a, token_row(a, brow, tk, h), L);
             const KeyLane K = key_lane(kw, lane0);
 #pragma unroll
-            for (int t = 0; t < 2; ++t) load_alpha(R, src, t, K);
+            for (int t = 0; t < 2; ++t) load_alpha<G>(R, src, t, K);
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 load_q(R, src, t, K);
-                load_kb(R, src, t, K);
+                load_kb<G>(R, src, t, K);
             }
-            if (K.ch == 0) load_vk(V, a, token_row(a, brow, tk, h), L, j0, kw, lane0);
-            decay_pass1(lds, R, al, ex, L, K, lane0);
+            if (K.ch == 0) load_vk<G>(V, a, token_row(a, brow, tk, h), L, j0, kw, lane0);
+            decay_pass1<G>(lds, R, al, ex, L, K, lane0);
         }
         while (tk < eos || tv >= 0) {
             const bool has_k = tk < eos;
@@ -942,13 +989,13 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
             const int64_t tn = tk + step;
             const int Ln = has_k && tn < eos ? int(eos - tn < kC ? eos - tn : kC) : 0;
             // the next chunk's window (empty past the sequence end: loads read zero)
-            const RawSrc nxt = raw_src(a, token_row(a, brow, Ln > 0 ? tn : tk, h), Ln);
+            const RawSrc nxt = raw_src<G>(a, token_row(a, brow, Ln > 0 ? tn : tk, h), Ln);
             uint32_t kbp[8];
             if (has_k) {
                 if (16 * K.tb + 16 <= step)
-                    prep_tiles<true>(lds, R, nxt, al, ex, kbp, step, kbuf, K);
+                    prep_tiles<G, true>(lds, R, nxt, al, ex, kbp, step, kbuf, K);
                 else
-                    prep_tiles<false>(lds, R, nxt, al, ex, kbp, step, kbuf, K);
+                    prep_tiles<G, false>(lds, R, nxt, al, ex, kbp, step, kbuf, K);
             }
             lds_barrier();  // B1
             if (kw >= 4) __builtin_amdgcn_s_setprio(0);
@@ -956,15 +1003,15 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
                 // k and b of the next chunk: issued here so that the memory pipe
                 // stays busy in this half of the period as well
 #pragma unroll
-                for (int t = 0; t < 2; ++t) load_kb(R, nxt, t, K);
+                for (int t = 0; t < 2; ++t) load_kb<G>(R, nxt, t, K);
                 store_kbt(lds, kbp, K);
                 // z of chunk tk (read by the value side next period), then v, w of the next chunk
                 if (K.ch == 0) {
-                    store_z(lds, V, kbuf, kw, lane);
-                    load_vk(V, a, token_row(a, brow, Ln > 0 ? tn : tk, h), Ln, j0, kw, lane);
+                    store_z<G>(lds, V, kbuf, kw, lane);
+                    load_vk<G>(V, a, token_row(a, brow, Ln > 0 ? tn : tk, h), Ln, j0, kw, lane);
                 }
             }
-            if (Ln > 0) decay_pass1(lds, R, al, ex, Ln, K, lane);
+            if (Ln > 0) decay_pass1<G>(lds, R, al, ex, Ln, K, lane);
             tv = has_k ? tk : -1;
             tk = has_k ? tn : eos;
             kbuf ^= 1;
@@ -980,19 +1027,42 @@ bool chunk_fwd_mfma_supported(const ChunkArgs& a, bool bf16)
     return bf16 && a.dk == kDK && a.dv % kDVT == 0;
 }
 
-hipError_t launch_chunk_fwd_mfma(const ChunkArgs& a, hipStream_t stream)
+namespace {
+
+template <int G>
+hipError_t launch_gates(const ChunkArgs& a, hipStream_t stream)
 {
     // Allow the kernel its > 64 KiB of dynamic LDS (thread-safe one-time call).
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fwd_mfma_kernel),
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fwd_mfma_kernel<G>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (attr != hipSuccess) return attr;
     const int ntiles = a.dv / kDVT;
     const int64_t chains = int64_t(a.N) * a.H;
     const int64_t blocks = (chains + 7) / 8 * 8 * ntiles;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(chunk_fwd_mfma_kernel, dim3(unsigned(blocks)), dim3(kThreads), kLdsBytes, stream, a, ntiles,
-                       int(chains));
+    hipLaunchKernelGGL(chunk_fwd_mfma_kernel<G>, dim3(unsigned(blocks)), dim3(kThreads), kLdsBytes, stream, a,
+                       ntiles, int(chains));
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_chunk_fwd_mfma(const ChunkArgs& a, hipStream_t stream)
+{
+    // every valid gdn2_gate_flags combination
+    switch (a.gates) {
+        case 0: return launch_gates<0>(a, stream);
+        case 1: return launch_gates<1>(a, stream);
+        case 2: return launch_gates<2>(a, stream);
+        case 3: return launch_gates<3>(a, stream);
+        case 5: return launch_gates<5>(a, stream);
+        case 8: return launch_gates<8>(a, stream);
+        case 9: return launch_gates<9>(a, stream);
+        case 10: return launch_gates<10>(a, stream);
+        case 11: return launch_gates<11>(a, stream);
+        case 13: return launch_gates<13>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace gdn2

@@ -71,12 +71,12 @@ __global__ __launch_bounds__(kSimpleThreads) void chunk_fwd_simple_kernel(ChunkA
         for (int idx = tid; idx < CH * DK; idx += kSimpleThreads) {
             const int i = idx / DK, c = idx % DK;
             if (i < L) {
-                const int64_t off = ((brow * a.T + t0 + i) * H + h) * DK + c;
+                const int64_t row = (brow * a.T + t0 + i) * H + h, off = row * DK + c;
                 const float kk = load_as_f32(k, off);
                 Qs[i][c] = load_as_f32(q, off);
                 Ks[i][c] = kk;
-                Es[i][c] = load_as_f32(b, off) * kk;
-                Gs[i][c] = log2_decay(a.alpha[off]);
+                Es[i][c] = load_as_f32(b, a.gates & kScalarErase ? row : off) * kk;
+                Gs[i][c] = log2_decay(a.alpha[a.gates & kScalarDecay ? row : off]);
             } else {
                 Qs[i][c] = 0.f;
                 Ks[i][c] = 0.f;
@@ -123,8 +123,11 @@ __global__ __launch_bounds__(kSimpleThreads) void chunk_fwd_simple_kernel(ChunkA
             const int i = idx / DVT, jj = idx % DVT;
             float acc = 0.f;
             for (int c = 0; c < DK; ++c) acc += Es[i][c] * Ss[c][jj];
-            const int64_t off = ((brow * a.T + t0 + i) * H + h) * dv + j0 + jj;
-            Us[i][jj] = load_as_f32(w, off) * load_as_f32(v, off) - acc;
+            const int64_t row = (brow * a.T + t0 + i) * H + h, off = row * dv + j0 + jj;
+            const float ww = a.gates & kTied          ? load_as_f32(b, row)
+                             : a.gates & kScalarWrite ? load_as_f32(w, row)
+                                                      : load_as_f32(w, off);
+            Us[i][jj] = ww * load_as_f32(v, off) - acc;
         }
         __syncthreads();
         // U = (I + A)^-1 X: column-oriented forward substitution

@@ -76,20 +76,34 @@ size_t gdn2_chunk_fwd_workspace_bytes(int32_t, int32_t, int32_t, int32_t, int32_
     return 0;
 }
 
-gdn2_status gdn2_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
-                           const void* b, const void* w, const float* initial_state,
-                           float* final_state, void* o, const int32_t* cu_seqlens, int32_t B,
-                           int32_t T, int32_t H, int32_t dk, int32_t dv, int32_t num_seqs,
-                           gdn2_dtype dtype, void* workspace, size_t workspace_bytes, void* stream)
+}  // extern "C"
+
+namespace {
+
+// A gate layout: flags only, and the tie only between a scalar erase gate and
+// the (then absent) write gate.
+bool valid_gates(int32_t g)
 {
-    (void)workspace;
-    (void)workspace_bytes;
+    const int32_t all = GDN2_GATES_SCALAR_ERASE | GDN2_GATES_SCALAR_WRITE | GDN2_GATES_TIED | GDN2_GATES_SCALAR_DECAY;
+    if (g & ~all) return false;
+    if (g & GDN2_GATES_TIED) return (g & GDN2_GATES_SCALAR_ERASE) && !(g & GDN2_GATES_SCALAR_WRITE);
+    return true;
+}
+
+gdn2_status chunk_fwd(const void* q, const void* k, const void* v, const float* alpha, const void* b, const void* w,
+                      const float* initial_state, float* final_state, void* o, const int32_t* cu_seqlens, int32_t B,
+                      int32_t T, int32_t H, int32_t dk, int32_t dv, int32_t num_seqs, gdn2_dtype dtype,
+                      int32_t gates, void* stream)
+{
     if (dtype != GDN2_DTYPE_F32 && dtype != GDN2_DTYPE_BF16) return GDN2_ERR_BAD_DTYPE;
+    if (!valid_gates(gates)) return GDN2_ERR_BAD_SHAPE;
     if (B <= 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return GDN2_ERR_BAD_SHAPE;
     if (cu_seqlens && (B != 1 || num_seqs <= 0)) return GDN2_ERR_BAD_SHAPE;
     if (!supported_head(dk) || !supported_head(dv)) return GDN2_ERR_UNSUPPORTED;
+    const bool tied = gates & GDN2_GATES_TIED;
+    if (tied) w = nullptr;  // ignored
     const int32_t N = cu_seqlens ? num_seqs : B;
-    if (T > 0 && (!q || !k || !v || !alpha || !b || !w || !o)) return GDN2_ERR_NULL_POINTER;
+    if (T > 0 && (!q || !k || !v || !alpha || !b || (!tied && !w) || !o)) return GDN2_ERR_NULL_POINTER;
     const void* ptrs[] = {q, k, v, alpha, b, w, o, initial_state, final_state};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return GDN2_ERR_MISALIGNED;
@@ -97,9 +111,11 @@ gdn2_status gdn2_chunk_fwd(const void* q, const void* k, const void* v, const fl
 
     const int64_t tokens = int64_t(B) * T * H;
     const int eb = element_bytes(dtype);
-    const Span sq = span(q, tokens * dk * eb), sk = span(k, tokens * dk * eb), sb = span(b, tokens * dk * eb);
-    const Span sv = span(v, tokens * dv * eb), sw = span(w, tokens * dv * eb), so = span(o, tokens * dv * eb);
-    const Span sa = span(alpha, tokens * dk * 4);
+    const Span sq = span(q, tokens * dk * eb), sk = span(k, tokens * dk * eb);
+    const Span sb = span(b, gates & GDN2_GATES_SCALAR_ERASE ? tokens * eb : tokens * dk * eb);
+    const Span sv = span(v, tokens * dv * eb), so = span(o, tokens * dv * eb);
+    const Span sw = span(w, tied ? 0 : gates & GDN2_GATES_SCALAR_WRITE ? tokens * eb : tokens * dv * eb);
+    const Span sa = span(alpha, gates & GDN2_GATES_SCALAR_DECAY ? tokens * 4 : tokens * dk * 4);
     const int64_t state_bytes = int64_t(N) * H * dk * dv * 4;
     const Span si = span(initial_state, initial_state ? state_bytes : 0);
     const Span sf = span(final_state, final_state ? state_bytes : 0);
@@ -111,7 +127,7 @@ gdn2_status gdn2_chunk_fwd(const void* q, const void* k, const void* v, const fl
     if (overlap(sf, si) && final_state != initial_state) return GDN2_ERR_ALIAS;
 
     gdn2::ChunkArgs a{q, k, v, alpha, b, w, initial_state, final_state, o, cu_seqlens,
-                      B, T, H, dk, dv, N, device_cus()};
+                      B, T, H, dk, dv, N, device_cus(), gates};
     const bool bf16 = dtype == GDN2_DTYPE_BF16;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const hipError_t e = gdn2::chunk_fwd_mfma_supported(a, bf16) ? gdn2::launch_chunk_fwd_mfma(a, st)
@@ -119,31 +135,80 @@ gdn2_status gdn2_chunk_fwd(const void* q, const void* k, const void* v, const fl
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 
-gdn2_status gdn2_recurrent_step(const void* q, const void* k, const void* v, const float* alpha,
-                                const void* b, const void* w, float* state, void* o, int32_t N,
-                                int32_t H, int32_t dk, int32_t dv, gdn2_dtype dtype, void* stream)
+gdn2_status recurrent_step(const void* q, const void* k, const void* v, const float* alpha, const void* b,
+                           const void* w, float* state, void* o, int32_t N, int32_t H, int32_t dk, int32_t dv,
+                           gdn2_dtype dtype, int32_t gates, void* stream)
 {
     if (dtype != GDN2_DTYPE_F32 && dtype != GDN2_DTYPE_BF16) return GDN2_ERR_BAD_DTYPE;
+    if (!valid_gates(gates)) return GDN2_ERR_BAD_SHAPE;
     if (N <= 0 || H <= 0 || dk <= 0 || dv <= 0) return GDN2_ERR_BAD_SHAPE;
     if (!supported_head(dk) || !supported_head(dv)) return GDN2_ERR_UNSUPPORTED;
-    if (!q || !k || !v || !alpha || !b || !w || !state || !o) return GDN2_ERR_NULL_POINTER;
+    const bool tied = gates & GDN2_GATES_TIED;
+    if (tied) w = nullptr;  // ignored
+    if (!q || !k || !v || !alpha || !b || (!tied && !w) || !state || !o) return GDN2_ERR_NULL_POINTER;
     const void* ptrs[] = {q, k, v, alpha, b, w, state, o};
     for (const void* p : ptrs)
-        if (!aligned16(p)) return GDN2_ERR_MISALIGNED;
+        if (p && !aligned16(p)) return GDN2_ERR_MISALIGNED;
     const int64_t heads = int64_t(N) * H;
     const int eb = element_bytes(dtype);
-    const Span sq = span(q, heads * dk * eb), sk = span(k, heads * dk * eb), sb = span(b, heads * dk * eb);
-    const Span sv = span(v, heads * dv * eb), sw = span(w, heads * dv * eb), so = span(o, heads * dv * eb);
-    const Span sa = span(alpha, heads * dk * 4), ss = span(state, heads * dk * dv * 4);
+    const Span sq = span(q, heads * dk * eb), sk = span(k, heads * dk * eb);
+    const Span sb = span(b, gates & GDN2_GATES_SCALAR_ERASE ? heads * eb : heads * dk * eb);
+    const Span sv = span(v, heads * dv * eb), so = span(o, heads * dv * eb);
+    const Span sw = span(w, tied ? 0 : gates & GDN2_GATES_SCALAR_WRITE ? heads * eb : heads * dv * eb);
+    const Span sa = span(alpha, gates & GDN2_GATES_SCALAR_DECAY ? heads * 4 : heads * dk * 4);
+    const Span ss = span(state, heads * dk * dv * 4);
     for (Span in : {sq, sk, sv, sa, sb, sw, ss})
         if (overlap(so, in)) return GDN2_ERR_ALIAS;
     for (Span in : {sq, sk, sv, sa, sb, sw})
         if (overlap(ss, in)) return GDN2_ERR_ALIAS;
 
-    gdn2::StepArgs a{q, k, v, alpha, b, w, state, o, N, H, dk, dv};
-    const hipError_t e = gdn2::launch_recurrent_step(a, dtype == GDN2_DTYPE_BF16,
-                                                     static_cast<hipStream_t>(stream));
+    gdn2::StepArgs a{q, k, v, alpha, b, w, state, o, N, H, dk, dv, gates};
+    const hipError_t e = gdn2::launch_recurrent_step(a, dtype == GDN2_DTYPE_BF16, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn2_status gdn2_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                           const void* b, const void* w, const float* initial_state,
+                           float* final_state, void* o, const int32_t* cu_seqlens, int32_t B,
+                           int32_t T, int32_t H, int32_t dk, int32_t dv, int32_t num_seqs,
+                           gdn2_dtype dtype, void* workspace, size_t workspace_bytes, void* stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    return chunk_fwd(q, k, v, alpha, b, w, initial_state, final_state, o, cu_seqlens, B, T, H, dk, dv, num_seqs,
+                     dtype, GDN2_GATES_FULL, stream);
+}
+
+gdn2_status gdn2_chunk_fwd_gates(const void* q, const void* k, const void* v, const float* alpha,
+                                 const void* b, const void* w, const float* initial_state,
+                                 float* final_state, void* o, const int32_t* cu_seqlens, int32_t B,
+                                 int32_t T, int32_t H, int32_t dk, int32_t dv, int32_t num_seqs,
+                                 gdn2_dtype dtype, int32_t gates, void* workspace,
+                                 size_t workspace_bytes, void* stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    return chunk_fwd(q, k, v, alpha, b, w, initial_state, final_state, o, cu_seqlens, B, T, H, dk, dv, num_seqs,
+                     dtype, gates, stream);
+}
+
+gdn2_status gdn2_recurrent_step(const void* q, const void* k, const void* v, const float* alpha,
+                                const void* b, const void* w, float* state, void* o, int32_t N,
+                                int32_t H, int32_t dk, int32_t dv, gdn2_dtype dtype, void* stream)
+{
+    return recurrent_step(q, k, v, alpha, b, w, state, o, N, H, dk, dv, dtype, GDN2_GATES_FULL, stream);
+}
+
+gdn2_status gdn2_recurrent_step_gates(const void* q, const void* k, const void* v, const float* alpha,
+                                      const void* b, const void* w, float* state, void* o, int32_t N,
+                                      int32_t H, int32_t dk, int32_t dv, gdn2_dtype dtype,
+                                      int32_t gates, void* stream)
+{
+    return recurrent_step(q, k, v, alpha, b, w, state, o, N, H, dk, dv, dtype, gates, stream);
 }
 
 }  // extern "C"

@@ -6,6 +6,9 @@
 
 namespace gdn2 {
 
+// Gate layout flags (the values of gdn2_gate_flags).
+constexpr int32_t kScalarErase = 1, kScalarWrite = 2, kTied = 4, kScalarDecay = 8;
+
 struct ChunkArgs {
     const void* q;
     const void* k;
@@ -18,7 +21,8 @@ struct ChunkArgs {
     void* o;
     const int32_t* cu_seqlens;
     int32_t B, T, H, dk, dv, N;
-    int32_t cus;  // compute units of the device
+    int32_t cus;    // compute units of the device
+    int32_t gates;  // gdn2_gate_flags, validated: 1 scalar erase, 2 scalar write, 4 write tied to erase, 8 scalar decay
 };
 
 struct StepArgs {
@@ -31,6 +35,7 @@ struct StepArgs {
     float* state;
     void* o;
     int32_t N, H, dk, dv;
+    int32_t gates;  // as in ChunkArgs
 };
 
 // Each returns hipSuccess or the launch error; bf16 selects the input dtype.

@@ -48,19 +48,23 @@ __global__ __launch_bounds__(kStepThreads) void recurrent_step_kernel(StepArgs a
 
     const T* q = static_cast<const T*>(a.q) + int64_t(head) * DK;
     const T* k = static_cast<const T*>(a.k) + int64_t(head) * DK;
-    const T* b = static_cast<const T*>(a.b) + int64_t(head) * DK;
+    // A scalar gate (one value per head) is read with stride 0 over its
+    // channels; a tied write gate is the scalar erase gate.
+    const int bst = a.gates & kScalarErase ? 0 : 1, ast = a.gates & kScalarDecay ? 0 : 1;
+    const int wst = a.gates & (kScalarWrite | kTied) ? 0 : 1;
+    const T* b = static_cast<const T*>(a.b) + int64_t(head) * (bst ? DK : 1);
     const T* v = static_cast<const T*>(a.v) + int64_t(head) * DV;
-    const T* w = static_cast<const T*>(a.w) + int64_t(head) * DV;
-    const float* al = a.alpha + int64_t(head) * DK;
+    const T* w = a.gates & kTied ? b : static_cast<const T*>(a.w) + int64_t(head) * (wst ? DV : 1);
+    const float* al = a.alpha + int64_t(head) * (ast ? DK : 1);
     for (int c = tid; c < DK; c += kStepThreads) {
-        const float kk = load_as_f32(k, c), qq = load_as_f32(q, c), aa = al[c];
+        const float kk = load_as_f32(k, c), qq = load_as_f32(q, c), aa = al[c * ast];
         s_alpha[c] = aa;
-        s_ae[c] = aa * (load_as_f32(b, c) * kk);
+        s_ae[c] = aa * (load_as_f32(b, c * bst) * kk);
         s_aq[c] = aa * qq;
         s_k[c] = kk;
         s_q[c] = qq;
     }
-    for (int j = tid; j < DV; j += kStepThreads) s_z[j] = load_as_f32(w, j) * load_as_f32(v, j);
+    for (int j = tid; j < DV; j += kStepThreads) s_z[j] = load_as_f32(w, j * wst) * load_as_f32(v, j);
     __syncthreads();
 
     // k . q, computed redundantly by every wavefront

@@ -27,9 +27,9 @@
  *    bf16 inputs feed bf16 matrix-core products with FP32 accumulation.
  *  - Inputs are gate VALUES, not logits: 0 <= alpha <= 1; b, w are used as
  *    given (no clamp, so an erase gate in [0, 2] works).  There is no query
- *    scale: callers pre-scale q.  Per token and key channel, log2(alpha) is
- *    clamped to [-15, 0]: alpha below 2^-15 acts as 2^-15 and alpha above 1
- *    acts as 1.
+ *    scale: callers pre-scale q.  The chunkwise entry points clamp alpha per
+ *    token and key channel to [2^-15, 1] (alpha below 2^-15 acts as 2^-15);
+ *    the recurrent step uses alpha as given.
  *  - Pointers to q, k, v, b, w, o, alpha and states must be 16-byte aligned.
  *  - Calls enqueue work on `stream` (a hipStream_t; NULL = the null stream)
  *    and return without synchronising.  Argument errors are reported
@@ -66,6 +66,37 @@ typedef enum gdn2_dtype {
 } gdn2_dtype;
 
 /*
+ * Gate layouts, a bitwise OR of gdn2_gate_flags ("gates" below).  The same
+ * analysis (section "Independent decisions on two axes") obtains Kimi Delta
+ * Attention by tying the erase and write gates to one scalar per token and
+ * head, and Gated DeltaNet by also making the decay one scalar per token and
+ * head; its ablations (section "Ablations and training throughput") average
+ * one of the two gates over its channels.  A scalar gate is passed compactly,
+ * one value per token and head ([..] below: the tensor's leading dimensions,
+ * [B, T, H] or [N, H]), which saves its memory traffic, and acts on every
+ * channel of its axis:
+ *   GDN2_GATES_SCALAR_ERASE  b is [..] (dtype) in place of [.., dk]
+ *   GDN2_GATES_SCALAR_WRITE  w is [..] (dtype) in place of [.., dv]
+ *   GDN2_GATES_TIED          w is ignored (may be NULL); b also serves as the
+ *                            write gate.  Requires SCALAR_ERASE and excludes
+ *                            SCALAR_WRITE.
+ *   GDN2_GATES_SCALAR_DECAY  alpha is [..] (FP32) in place of [.., dk]
+ * GDN2_GATES_FULL (0) is the Gated DeltaNet-2 layout of gdn2_chunk_fwd and
+ * gdn2_recurrent_step.  GDN2_GATES_KDA and GDN2_GATES_GDN name the two
+ * reductions.  Averaging a channel-wise gate is the caller's (it belongs with
+ * the gate projection); the result is passed as the scalar gate.
+ */
+typedef enum gdn2_gate_flags {
+    GDN2_GATES_FULL = 0,
+    GDN2_GATES_SCALAR_ERASE = 1,
+    GDN2_GATES_SCALAR_WRITE = 2,
+    GDN2_GATES_TIED = 4,
+    GDN2_GATES_SCALAR_DECAY = 8,
+    GDN2_GATES_KDA = 5,  /* SCALAR_ERASE | TIED                 */
+    GDN2_GATES_GDN = 13  /* SCALAR_ERASE | TIED | SCALAR_DECAY  */
+} gdn2_gate_flags;
+
+/*
  * Chunkwise forward over whole sequences ("Token processing and parallel
  * training": 64-token chunks, cumulative channel-wise decay in FP32 absorbed
  * into asymmetric erase factors, a per-chunk lower-triangular solve and dense
@@ -99,6 +130,20 @@ gdn2_status gdn2_chunk_fwd(const void* q, const void* k, const void* v,
                            int32_t num_seqs, gdn2_dtype dtype,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * gdn2_chunk_fwd with the gate layout `gates` (a bitwise OR of
+ * gdn2_gate_flags, shapes as listed there; GDN2_GATES_FULL is identical to
+ * gdn2_chunk_fwd).  Other bits, or TIED without SCALAR_ERASE or with
+ * SCALAR_WRITE, give GDN2_ERR_BAD_SHAPE.
+ */
+gdn2_status gdn2_chunk_fwd_gates(const void* q, const void* k, const void* v,
+                                 const float* alpha, const void* b, const void* w,
+                                 const float* initial_state, float* final_state, void* o,
+                                 const int32_t* cu_seqlens,
+                                 int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                                 int32_t num_seqs, gdn2_dtype dtype, int32_t gates,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace needed by gdn2_chunk_fwd for these sizes (currently always 0). */
 size_t gdn2_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
                                       int32_t num_seqs, gdn2_dtype dtype);
@@ -117,6 +162,16 @@ gdn2_status gdn2_recurrent_step(const void* q, const void* k, const void* v,
                                 float* state, void* o,
                                 int32_t N, int32_t H, int32_t dk, int32_t dv,
                                 gdn2_dtype dtype, void* stream);
+
+/*
+ * gdn2_recurrent_step with the gate layout `gates` (as for
+ * gdn2_chunk_fwd_gates; [..] is [N, H]).
+ */
+gdn2_status gdn2_recurrent_step_gates(const void* q, const void* k, const void* v,
+                                      const float* alpha, const void* b, const void* w,
+                                      float* state, void* o,
+                                      int32_t N, int32_t H, int32_t dk, int32_t dv,
+                                      gdn2_dtype dtype, int32_t gates, void* stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* gdn2_status_string(gdn2_status status);

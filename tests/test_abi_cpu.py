@@ -119,3 +119,63 @@ def test_chunk_fwd_rejects(lib, kw, expected):
 ])
 def test_recurrent_step_rejects(lib, kw, expected):
     assert step_call(lib, **kw) == expected
+
+
+def chunk_gates_call(lib, gates, **kw):
+    args = dict(q=fake(0), k=fake(1), v=fake(2), alpha=fake(3), b=fake(4), w=None,
+                s0=fake(6), sf=fake(7), o=fake(8), cu=None,
+                B=2, T=64, H=4, dk=64, dv=64, num_seqs=0, dtype=1, ws=None, ws_bytes=0)
+    args.update(kw)
+    a = args
+    return lib.gdn2_chunk_fwd_gates(a["q"], a["k"], a["v"], a["alpha"], a["b"], a["w"], a["s0"], a["sf"],
+                                    a["o"], a["cu"], a["B"], a["T"], a["H"], a["dk"], a["dv"],
+                                    a["num_seqs"], a["dtype"], gates, a["ws"], a["ws_bytes"], None)
+
+
+def step_gates_call(lib, gates, **kw):
+    args = dict(q=fake(0), k=fake(1), v=fake(2), alpha=fake(3), b=fake(4), w=None,
+                state=fake(6), o=fake(8), N=8, H=4, dk=128, dv=128, dtype=1)
+    args.update(kw)
+    a = args
+    return lib.gdn2_recurrent_step_gates(a["q"], a["k"], a["v"], a["alpha"], a["b"], a["w"], a["state"],
+                                         a["o"], a["N"], a["H"], a["dk"], a["dv"], a["dtype"], gates, None)
+
+
+# 2 x 64 x 4 = 512 (token, head) rows: a scalar gate takes 1024 bytes in
+# bf16, a scalar alpha 2048 bytes.  Every case must be rejected before launch.
+@pytest.mark.parametrize("gates,kw,expected", [
+    (16, {}, SHAPE),                                  # an unknown flag
+    (-1, {}, SHAPE),
+    (4, {}, SHAPE),                                   # tied without a scalar erase gate
+    (7, {}, SHAPE),                                   # tied and a scalar write gate
+    (0, {}, NULLP),                                   # the full layout needs w
+    (1, {}, NULLP),                                   # an untied layout needs w
+    (5, dict(b=None), NULLP),
+    (13, dict(alpha=None), NULLP),
+    (5, dict(b=fake(4, 2)), MISAL),
+    (2, dict(w=fake(5, 8)), MISAL),
+    (5, dict(o=fake(4, 512)), ALIAS),                 # o inside the compact beta
+    (13, dict(o=fake(3, 1024)), ALIAS),               # o inside the compact alpha
+    (13, dict(sf=fake(4, 992)), ALIAS),               # final state over the end of beta
+    (3, dict(w=fake(5), o=fake(5, 512)), ALIAS),      # o inside the compact write gate
+    (5, dict(dk=96), UNSUP),
+    (5, dict(dtype=3), DTYPE),
+])
+def test_chunk_fwd_gates_rejects(lib, gates, kw, expected):
+    assert chunk_gates_call(lib, gates, **kw) == expected
+
+
+# 8 x 4 = 32 (sequence, head) rows: a scalar gate takes 64 bytes in bf16, a
+# scalar alpha 128 bytes.
+@pytest.mark.parametrize("gates,kw,expected", [
+    (16, {}, SHAPE),
+    (6, {}, SHAPE),                                   # tied and a scalar write gate, no scalar erase
+    (0, {}, NULLP),
+    (13, dict(b=None), NULLP),
+    (13, dict(alpha=fake(3, 8)), MISAL),
+    (5, dict(o=fake(4, 32)), ALIAS),                  # o inside beta
+    (13, dict(state=fake(3, 96)), ALIAS),             # state over the compact alpha
+    (10, dict(w=fake(5), o=fake(5, 32)), ALIAS),      # o inside the compact write gate
+])
+def test_recurrent_step_gates_rejects(lib, gates, kw, expected):
+    assert step_gates_call(lib, gates, **kw) == expected
