@@ -290,6 +290,28 @@ def run_configs(args):
     print(json.dumps({"report": "config", "workload": "decode_b256", "us_per_step": dec["step_ms"] * 1e3,
                       "state_GBps": dec["state_gbps"], "hbm_frac": dec["achieved"] / HBM_PEAK_GBPS}),
           flush=True)
+    # several tokens per sequence in one recurrent call (verification steps, short prompts)
+    for T in (4, 16, 64):
+        N, H, dk, dv = 256, 16, 128, 128
+        x = W.make("batched_bf16", seed=2000 + T, B=N, T=T, H=H)
+        d = to_dev(x, "bf16")
+        state = torch.from_numpy(x["initial_state"]).cuda()  # [N, H, dk, dv], N(0, 0.1^2)
+        o = torch.empty((N, T, H, dv), dtype=torch.bfloat16, device="cuda")
+
+        def call_multi():
+            binding.gdn2_recurrent_fwd(d["q"], d["k"], d["v"], d["alpha"], d["b"], d["w"], state, out=o)
+
+        per, _, _ = time_events(call_multi, args.warmup, args.steps)
+        kern_ms = float(np.median(per))
+        nbytes = N * H * (2 * dk * dv * 4 + T * (3 * dk * 2 + 2 * dv * 2 + dk * 4 + dv * 2))
+        row = {"report": "config", "workload": f"recurrent_fwd N={N} H={H} d=128 bf16 T={T}",
+               "us_per_call": kern_ms * 1e3, "tokens_per_s": N * T / (kern_ms / 1e3),
+               "GBps": nbytes / (kern_ms / 1e3) / 1e9, "hbm_frac": nbytes / (kern_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
+               "timing": f"median of {args.steps} launches after {args.warmup}"}
+        log(f"recurrent_fwd T={T}: {row['us_per_call']:.1f} us, {row['tokens_per_s'] / 1e6:.2f} M tokens/s, "
+            f"{row['hbm_frac'] * 100:.1f}% HBM")
+        print(json.dumps(row), flush=True)
+        del d, x
     # the oracle: all cores on four sequences of the headline workload, one core on one (sequence, head)
     x = W.make("batched_bf16")
     wl = x["workload"]

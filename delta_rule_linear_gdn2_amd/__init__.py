@@ -5,6 +5,7 @@ Two entry points, both hand-written HIP behind the C ABI in include/gdn2.h:
 * ``gdn2_chunk_fwd``      chunkwise WY forward over whole sequences (64-token
                           chunks; varlen via ``cu_seqlens``)
 * ``gdn2_recurrent_step`` fused single-token decode step, state updated in place
+* ``gdn2_recurrent_fwd``  the fused recurrent form over T tokens per sequence
 * ``gdn2_chunk_fwd_gates`` / ``gdn2_recurrent_step_gates``: the same with a gate
   layout (``GATES_*`` flags: scalar erase, write or decay gates, tied write gate)
 
@@ -22,6 +23,7 @@ from .binding import (  # noqa: F401
     gdn2_chunk_fwd,
     gdn2_chunk_fwd_gates,
     gdn2_chunk_fwd_workspace_bytes,
+    gdn2_recurrent_fwd,
     gdn2_recurrent_step,
     gdn2_recurrent_step_gates,
     load,
@@ -40,6 +42,7 @@ __all__ = [
     "gdn2_chunk_fwd",
     "gdn2_chunk_fwd_gates",
     "gdn2_chunk_fwd_workspace_bytes",
+    "gdn2_recurrent_fwd",
     "gdn2_recurrent_step",
     "gdn2_recurrent_step_gates",
     "load",

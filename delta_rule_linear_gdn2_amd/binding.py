@@ -23,7 +23,8 @@ DTYPE_F32 = 0
 DTYPE_BF16 = 1
 
 EXPORTS = ("gdn2_chunk_fwd", "gdn2_chunk_fwd_gates", "gdn2_chunk_fwd_workspace_bytes",
-           "gdn2_recurrent_step", "gdn2_recurrent_step_gates", "gdn2_status_string", "gdn2_version")
+           "gdn2_recurrent_fwd", "gdn2_recurrent_step", "gdn2_recurrent_step_gates", "gdn2_status_string",
+           "gdn2_version")
 
 # gdn2_gate_flags: layout of the gates (b, w, alpha), OR-ed together
 GATES_FULL, GATES_SCALAR_ERASE, GATES_SCALAR_WRITE, GATES_TIED, GATES_SCALAR_DECAY = 0, 1, 2, 4, 8
@@ -76,6 +77,8 @@ def load(path: str = LIB_PATH):
     lib.gdn2_recurrent_step.restype = ctypes.c_int
     lib.gdn2_recurrent_step_gates.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, P]
     lib.gdn2_recurrent_step_gates.restype = ctypes.c_int
+    lib.gdn2_recurrent_fwd.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]
+    lib.gdn2_recurrent_fwd.restype = ctypes.c_int
     lib.gdn2_status_string.argtypes = [ctypes.c_int]
     lib.gdn2_status_string.restype = ctypes.c_char_p
     lib.gdn2_version.argtypes = []
@@ -253,3 +256,39 @@ def gdn2_recurrent_step_gates(q, k, v, alpha, b, w, gates, state, *, out=None, s
     """gdn2_recurrent_step with a gate layout (see gdn2_chunk_fwd_gates); a
     scalar gate is [N, H]."""
     return _recurrent_step(q, k, v, alpha, b, w, gates, state, out, stream)
+
+
+def gdn2_recurrent_fwd(q, k, v, alpha, b, w, state, *, gates=GATES_FULL, out=None, stream=None):
+    """The fused recurrent form over T tokens per sequence in one call; updates
+    ``state`` in place and returns o.
+
+    q, k, b: [N, T, H, dk]; v, w: [N, T, H, dv]; alpha: [N, T, H, dk] float32
+    (scalar gates [N, T, H] as the ``gates`` layout says); state:
+    [N, H, dk, dv] float32.
+    """
+    import torch
+
+    lib = load()
+    N, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(dt)
+    bw, ww, aw = _gate_widths(gates, dk, dv)
+    for name, t, width in (("q", q, dk), ("k", k, dk), ("v", v, dv)):
+        _check(name, t, (N, T, H, width), dt, dev)
+    _check("b", b, (N, T, H) + bw, dt, dev)
+    if ww is not None:
+        _check("w", w, (N, T, H) + ww, dt, dev)
+    else:
+        w = None
+    _check("alpha", alpha, (N, T, H) + aw, torch.float32, dev)
+    _check("state", state, (N, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((N, T, H, dv), dtype=dt, device=dev)
+    else:
+        _check("out", out, (N, T, H, dv), dt, dev)
+    rc = lib.gdn2_recurrent_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(state), _ptr(out),
+                                N, T, H, dk, dv, code, gates, _stream(stream))
+    if rc != GDN2_OK:
+        raise Gdn2Error(rc, "gdn2_recurrent_fwd")
+    return out

@@ -135,35 +135,36 @@ gdn2_status chunk_fwd(const void* q, const void* k, const void* v, const float* 
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 
-gdn2_status recurrent_step(const void* q, const void* k, const void* v, const float* alpha, const void* b,
-                           const void* w, float* state, void* o, int32_t N, int32_t H, int32_t dk, int32_t dv,
-                           gdn2_dtype dtype, int32_t gates, void* stream)
+gdn2_status recurrent(const void* q, const void* k, const void* v, const float* alpha, const void* b, const void* w,
+                      float* state, void* o, int32_t N, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                      gdn2_dtype dtype, int32_t gates, void* stream)
 {
     if (dtype != GDN2_DTYPE_F32 && dtype != GDN2_DTYPE_BF16) return GDN2_ERR_BAD_DTYPE;
     if (!valid_gates(gates)) return GDN2_ERR_BAD_SHAPE;
-    if (N <= 0 || H <= 0 || dk <= 0 || dv <= 0) return GDN2_ERR_BAD_SHAPE;
+    if (N <= 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return GDN2_ERR_BAD_SHAPE;
     if (!supported_head(dk) || !supported_head(dv)) return GDN2_ERR_UNSUPPORTED;
     const bool tied = gates & GDN2_GATES_TIED;
     if (tied) w = nullptr;  // ignored
-    if (!q || !k || !v || !alpha || !b || (!tied && !w) || !state || !o) return GDN2_ERR_NULL_POINTER;
+    if (!state || (T > 0 && (!q || !k || !v || !alpha || !b || (!tied && !w) || !o))) return GDN2_ERR_NULL_POINTER;
     const void* ptrs[] = {q, k, v, alpha, b, w, state, o};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return GDN2_ERR_MISALIGNED;
-    const int64_t heads = int64_t(N) * H;
+    const int64_t tokens = int64_t(N) * T * H;
     const int eb = element_bytes(dtype);
-    const Span sq = span(q, heads * dk * eb), sk = span(k, heads * dk * eb);
-    const Span sb = span(b, gates & GDN2_GATES_SCALAR_ERASE ? heads * eb : heads * dk * eb);
-    const Span sv = span(v, heads * dv * eb), so = span(o, heads * dv * eb);
-    const Span sw = span(w, tied ? 0 : gates & GDN2_GATES_SCALAR_WRITE ? heads * eb : heads * dv * eb);
-    const Span sa = span(alpha, gates & GDN2_GATES_SCALAR_DECAY ? heads * 4 : heads * dk * 4);
-    const Span ss = span(state, heads * dk * dv * 4);
+    const Span sq = span(q, tokens * dk * eb), sk = span(k, tokens * dk * eb);
+    const Span sb = span(b, gates & GDN2_GATES_SCALAR_ERASE ? tokens * eb : tokens * dk * eb);
+    const Span sv = span(v, tokens * dv * eb), so = span(o, tokens * dv * eb);
+    const Span sw = span(w, tied ? 0 : gates & GDN2_GATES_SCALAR_WRITE ? tokens * eb : tokens * dv * eb);
+    const Span sa = span(alpha, gates & GDN2_GATES_SCALAR_DECAY ? tokens * 4 : tokens * dk * 4);
+    const Span ss = span(state, int64_t(N) * H * dk * dv * 4);
     for (Span in : {sq, sk, sv, sa, sb, sw, ss})
         if (overlap(so, in)) return GDN2_ERR_ALIAS;
     for (Span in : {sq, sk, sv, sa, sb, sw})
         if (overlap(ss, in)) return GDN2_ERR_ALIAS;
+    if (T == 0) return GDN2_OK;  // nothing to do: the state is unchanged
 
-    gdn2::StepArgs a{q, k, v, alpha, b, w, state, o, N, H, dk, dv, gates};
-    const hipError_t e = gdn2::launch_recurrent_step(a, dtype == GDN2_DTYPE_BF16, static_cast<hipStream_t>(stream));
+    gdn2::StepArgs a{q, k, v, alpha, b, w, state, o, N, H, dk, dv, gates, T};
+    const hipError_t e = gdn2::launch_recurrent(a, dtype == GDN2_DTYPE_BF16, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 
@@ -200,7 +201,7 @@ gdn2_status gdn2_recurrent_step(const void* q, const void* k, const void* v, con
                                 const void* b, const void* w, float* state, void* o, int32_t N,
                                 int32_t H, int32_t dk, int32_t dv, gdn2_dtype dtype, void* stream)
 {
-    return recurrent_step(q, k, v, alpha, b, w, state, o, N, H, dk, dv, dtype, GDN2_GATES_FULL, stream);
+    return recurrent(q, k, v, alpha, b, w, state, o, N, 1, H, dk, dv, dtype, GDN2_GATES_FULL, stream);
 }
 
 gdn2_status gdn2_recurrent_step_gates(const void* q, const void* k, const void* v, const float* alpha,
@@ -208,7 +209,14 @@ gdn2_status gdn2_recurrent_step_gates(const void* q, const void* k, const void* 
                                       int32_t H, int32_t dk, int32_t dv, gdn2_dtype dtype,
                                       int32_t gates, void* stream)
 {
-    return recurrent_step(q, k, v, alpha, b, w, state, o, N, H, dk, dv, dtype, gates, stream);
+    return recurrent(q, k, v, alpha, b, w, state, o, N, 1, H, dk, dv, dtype, gates, stream);
+}
+
+gdn2_status gdn2_recurrent_fwd(const void* q, const void* k, const void* v, const float* alpha, const void* b,
+                               const void* w, float* state, void* o, int32_t N, int32_t T, int32_t H, int32_t dk,
+                               int32_t dv, gdn2_dtype dtype, int32_t gates, void* stream)
+{
+    return recurrent(q, k, v, alpha, b, w, state, o, N, T, H, dk, dv, dtype, gates, stream);
 }
 
 }  // extern "C"

@@ -36,10 +36,11 @@ struct StepArgs {
     void* o;
     int32_t N, H, dk, dv;
     int32_t gates;  // as in ChunkArgs
+    int32_t T;      // tokens per sequence: inputs [N, T, H, .], o [N, T, H, dv]
 };
 
 // Each returns hipSuccess or the launch error; bf16 selects the input dtype.
-hipError_t launch_recurrent_step(const StepArgs& a, bool bf16, hipStream_t stream);
+hipError_t launch_recurrent(const StepArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_chunk_fwd_simple(const ChunkArgs& a, bool bf16, hipStream_t stream);
 
 // Matrix-core chunk kernel: bf16 inputs, dk = 128, dv a multiple of 64.

@@ -173,6 +173,31 @@ gdn2_status gdn2_recurrent_step_gates(const void* q, const void* k, const void* 
                                       int32_t N, int32_t H, int32_t dk, int32_t dv,
                                       gdn2_dtype dtype, int32_t gates, void* stream);
 
+/*
+ * The fused recurrent form over T tokens per sequence in one call (short
+ * prompts, several tokens to verify, decode after a chunkwise prefill): the
+ * recurrence token by token, each (sequence, head) state read once and
+ * written once, in place.  The same mathematics as gdn2_chunk_fwd ("DeltaNet"
+ * entity trail at mindpattern.ai, finding "You Could Have Come Up With Kimi
+ * Delta Attention"), so a final state of gdn2_chunk_fwd continues here; alpha
+ * is used as given (no clamp).  Cost grows with T (one token at a time):
+ * meant for T up to a few chunks, with gdn2_chunk_fwd for long inputs.
+ *
+ *   q, k, b : [N, T, H, dk] dtype     v, w, o : [N, T, H, dv] dtype
+ *   alpha   : [N, T, H, dk] FP32
+ *   gates   : a gate layout as for gdn2_chunk_fwd_gates ([..] is [N, T, H]);
+ *             GDN2_GATES_FULL for the layout above
+ *   state   : [N, H, dk, dv] FP32, read and overwritten with the state after
+ *             token T - 1.  T = 0 leaves it unchanged and launches nothing.
+ * gdn2_recurrent_step is this call with T = 1.  o must not overlap any input
+ * or the state; the state must not overlap an input.
+ */
+gdn2_status gdn2_recurrent_fwd(const void* q, const void* k, const void* v,
+                               const float* alpha, const void* b, const void* w,
+                               float* state, void* o,
+                               int32_t N, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                               gdn2_dtype dtype, int32_t gates, void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* gdn2_status_string(gdn2_status status);
 

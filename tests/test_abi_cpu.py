@@ -179,3 +179,33 @@ def test_chunk_fwd_gates_rejects(lib, gates, kw, expected):
 ])
 def test_recurrent_step_gates_rejects(lib, gates, kw, expected):
     assert step_gates_call(lib, gates, **kw) == expected
+
+
+def recurrent_fwd_call(lib, gates=0, **kw):
+    args = dict(q=fake(0), k=fake(1), v=fake(2), alpha=fake(3), b=fake(4), w=fake(5),
+                state=fake(6), o=fake(8), N=4, T=8, H=2, dk=128, dv=128, dtype=1)
+    args.update(kw)
+    a = args
+    return lib.gdn2_recurrent_fwd(a["q"], a["k"], a["v"], a["alpha"], a["b"], a["w"], a["state"], a["o"],
+                                  a["N"], a["T"], a["H"], a["dk"], a["dv"], a["dtype"], gates, None)
+
+
+# 4 x 8 x 2 = 64 (token, head) rows.  Every case must be rejected before launch;
+# T = 0 succeeds without launching.
+@pytest.mark.parametrize("gates,kw,expected", [
+    (0, dict(T=0), OK),
+    (0, dict(T=-1), SHAPE),
+    (0, dict(N=0), SHAPE),
+    (12, {}, SHAPE),
+    (0, dict(dtype=2), DTYPE),
+    (0, dict(dk=256), UNSUP),
+    (0, dict(w=None), NULLP),
+    (0, dict(state=None, T=0), NULLP),
+    (0, dict(o=fake(1, 16)), ALIAS),                  # o inside k
+    (0, dict(state=fake(8, 4096)), ALIAS),            # state over o ([4, 8, 2, 128] bf16 = 16 KiB)
+    (0, dict(o=fake(0, 12288)), ALIAS),               # o over the end of q (16 KiB; o starts in its last quarter)
+    (5, dict(w=None, o=fake(4, 96)), ALIAS),          # o inside the compact beta (128 bytes)
+    (0, dict(alpha=fake(3, 4)), MISAL),
+])
+def test_recurrent_fwd_rejects(lib, gates, kw, expected):
+    assert recurrent_fwd_call(lib, gates, **kw) == expected
