@@ -15,7 +15,7 @@
  * chunkwise WY form with 64-token chunks used for long inputs
  * (gdn2_chunk_fwd); the "DeltaNet" entity trail at mindpattern.ai (finding
  * "You Could Have Come Up With Kimi Delta Attention") states that the fused
- * recurrent decode form (gdn2_recurrent_step) computes identical mathematics.
+ * recurrent decode form (gdn2_recurrent_step) computes the same result.
  *
  * Conventions shared by every entry point.
  *  - All tensor pointers are DEVICE pointers owned by the caller; the library

@@ -16,8 +16,9 @@ only marshals numpy arrays.  Sources, cited by page title and section:
   form with cumulative channel-wise decay absorbed into asymmetric factors.
   -> ``chunked`` (any chunk size; a self-consistency pin).
 * "DeltaNet" entity trail (mindpattern.ai), "You Could Have Come Up With Kimi
-  Delta Attention": diagonal-plus-low-rank transitions; chunkwise and fused
-  recurrent modes are identical mathematics.  -> ``transition``.
+  Delta Attention": each token's transition is a diagonal decay composed with
+  a rank-one correction of the identity, and the chunkwise and fused
+  recurrent forms compute the same result.  -> ``transition``.
 * IPX "Independent decisions on two axes": tying b = w = beta gives KDA, and a
   scalar decay as well gives Gated DeltaNet.  -> ``kda``, ``gdn``.
 
@@ -64,7 +65,8 @@ def _declare(lib) -> None:
     lib.gdn2_oracle_chunked.argtypes = six + common + [_I] + tail
     lib.gdn2_oracle_kda.argtypes = [_P] * 5 + common + tail
     lib.gdn2_oracle_gdn.argtypes = [_P] * 5 + common + tail
-    for name in ("recurrent", "transition", "chunked", "kda", "gdn"):
+    lib.gdn2_oracle_backward.argtypes = six + [_P, _P, _P] + [_P] * 7 + [_P, _I, _I, _I, _I, _I, _I] + tail
+    for name in ("recurrent", "transition", "chunked", "kda", "gdn", "backward"):
         getattr(lib, "gdn2_oracle_" + name).restype = ctypes.c_int
     lib.gdn2_oracle_max_threads.argtypes = []
     lib.gdn2_oracle_max_threads.restype = ctypes.c_int
@@ -160,6 +162,33 @@ class Oracle:
         return o, sf
 
 
+    def backward(self, q, k, v, alpha, b, w, d_o, initial_state=None, d_final_state=None, cu_seqlens=None,
+                 chains=None, threads=0):
+        """O5: gradients of O1 for the loss <d_o, o> + <d_final_state, S_final>.
+
+        Returns dict(dq, dk, dv, dalpha, db, dw, d_initial_state) in FP64 (chains
+        not selected by ``chains`` are left zero)."""
+        q, dims, cu, s0, ch, o, sf = _prepare(q, k, v, initial_state, cu_seqlens, chains)
+        B, T, H, dk, dv, N = dims
+        g = _f64(d_o)
+        if g.shape != (B, T, H, dv):
+            raise ValueError(f"d_o shape {g.shape} != {(B, T, H, dv)}")
+        dsf = _f64(d_final_state)
+        if dsf is not None and dsf.shape != (N, H, dk, dv):
+            raise ValueError(f"d_final_state shape {dsf.shape} != {(N, H, dk, dv)}")
+        out = {name: np.zeros((B, T, H, width), dtype=np.float64)
+               for name, width in (("dq", dk), ("dk", dk), ("dv", dv), ("dalpha", dk), ("db", dk), ("dw", dv))}
+        out["d_initial_state"] = np.zeros((N, H, dk, dv), dtype=np.float64)
+        arrays = [q] + [_f64(x) for x in (k, v, alpha, b, w)]
+        rc = self.lib.gdn2_oracle_backward(
+            *[_ptr(a) for a in arrays], _ptr(s0), _ptr(g), _ptr(dsf),
+            *[_ptr(out[n]) for n in ("dq", "dk", "dv", "dalpha", "db", "dw", "d_initial_state")],
+            _ptr(cu), B, T, H, dk, dv, N, _ptr(ch), 0 if ch is None else int(ch.shape[0]), int(threads))
+        if rc != 0:
+            raise ValueError(f"oracle rejected its arguments (rc={rc})")
+        return out
+
+
 _DEFAULT = None
 
 
@@ -188,6 +217,10 @@ def kda(*args, **kw):
 
 def gdn(*args, **kw):
     return default().gdn(*args, **kw)
+
+
+def backward(*args, **kw):
+    return default().backward(*args, **kw)
 
 
 def rel_l2(x, ref) -> float:

@@ -13,8 +13,9 @@
  *          training" (64-token chunkwise WY form, FP32 decay / solve).
  *   [MP]   "DeltaNet" entity trail at mindpattern.ai -- finding "You Could Have
  *          Come Up With Kimi Delta Attention": per-key-channel decay with
- *          diagonal-plus-low-rank transitions; fused recurrent and chunkwise
- *          modes compute identical mathematics.
+ *          per-token transitions are a diagonal decay composed with a
+ *          rank-one correction; the fused recurrent and chunkwise forms give
+ *          the same result.
  *
  * The method, per head, per token t, with state S in R^{dk x dv} (keys index
  * rows) [IPX, "Independent decisions on two axes"]:
@@ -31,6 +32,7 @@
  *   gdn2_oracle_transition  O3  explicit dk x dk transition products (pin)
  *   gdn2_oracle_kda         O4a Kimi-Delta-Attention form (pin for b=w=beta)
  *   gdn2_oracle_gdn         O4b Gated DeltaNet form (pin for scalar alpha)
+ *   gdn2_oracle_backward    O5  gradients of O1 (reverse mode, token by token)
  *
  * Layouts (row-major, contiguous, FP64):
  *   q, k, b, alpha : [B, T, H, dk]        v, w, o : [B, T, H, dv]
@@ -376,6 +378,192 @@ static void relative_chain(const shape_t* s, int32_t n, int32_t h, int scalar_al
     free(M);
 }
 
+
+/* ------------------------------------------------------------------------
+ * O5: the gradients of O1 by reverse-mode differentiation, token by token.
+ * The analysis page asks for a backward pass that accumulates gradients
+ * through the gated keys and values and keeps the channel-wise factors
+ * inside the sums [IPX, "Token processing and parallel training"]; this is
+ * that adjoint written out for one token, applied from the last token back
+ * to the first.  The scalar loss is
+ *     L = sum_t <dO_t, o_t> + <dS_final, S_final>,
+ * and the results are dL/dq, dL/dk, dL/dv, dL/dalpha, dL/db, dL/dw (same
+ * layouts as the inputs) and dL/dS_initial.  Per token, with Sprev the state
+ * before it and S the state after it (forward order of O1):
+ *     o = S^T q               dq = S dO_t;        dS += q dO_t^T
+ *     S = Sbar + k u^T        du = dS^T k;        dk = dS u;   dSbar = dS
+ *     u = z - Sbar^T e        dz = du;            de = -Sbar du;  dSbar -= e du^T
+ *     Sbar = Diag(alpha) Sprev  dalpha_c = sum_j dSbar[c][j] Sprev[c][j];
+ *                              dS (for Sprev) = Diag(alpha) dSbar
+ *     e = b (.) k, z = w (.) v  db = de (.) k;  dk += de (.) b;
+ *                              dw = dz (.) v;  dv = dz (.) w
+ * States are kept at every 64th token and the states inside a 64-token
+ * segment are recomputed (forward, as in O1) before the segment is walked
+ * backwards; this only bounds memory and changes no arithmetic.
+ * ---------------------------------------------------------------------- */
+#define O5_SEGMENT 64
+
+/* One forward token of O1 on S in place (the same arithmetic, in order). */
+static void o5_forward_token(int32_t dk, int32_t dv, double* S, const double* qt, const double* kt,
+                             const double* vt, const double* at, const double* bt, const double* wt,
+                             double* e, double* z, double* r)
+{
+    (void)qt;
+    for (int32_t c = 0; c < dk; ++c) e[c] = bt[c] * kt[c];
+    for (int32_t j = 0; j < dv; ++j) z[j] = wt[j] * vt[j];
+    for (int32_t c = 0; c < dk; ++c)
+        for (int32_t j = 0; j < dv; ++j) S[c * dv + j] *= at[c];
+    for (int32_t j = 0; j < dv; ++j) {
+        double acc = 0.0;
+        for (int32_t c = 0; c < dk; ++c) acc += S[c * dv + j] * e[c];
+        r[j] = acc;
+    }
+    for (int32_t c = 0; c < dk; ++c)
+        for (int32_t j = 0; j < dv; ++j) S[c * dv + j] += kt[c] * (z[j] - r[j]);
+}
+
+static void backward_chain(const shape_t* s, int32_t n, int32_t h,
+                           const double* q, const double* k, const double* v,
+                           const double* alpha, const double* b, const double* w,
+                           const double* S0, const double* dO, const double* dSf,
+                           double* dq, double* dk_out, double* dv_out, double* da,
+                           double* db, double* dw, double* dS0)
+{
+    const int32_t dk = s->dk, dv = s->dv;
+    const size_t sz = (size_t)dk * dv;
+    const int64_t soff = ((int64_t)n * s->H + h) * dk * dv;
+    int64_t bos, eos, brow;
+    seq_bounds(s, n, &bos, &eos, &brow);
+    const int64_t L = eos - bos;
+    const int64_t nseg = (L + O5_SEGMENT - 1) / O5_SEGMENT;
+
+    double* ckpt = (double*)calloc((size_t)(nseg + 1) * sz, sizeof(double)); /* state before segment i */
+    double* seg = (double*)malloc((size_t)(O5_SEGMENT + 1) * sz * sizeof(double));
+    double* dS = (double*)calloc(sz, sizeof(double));
+    double* Sbar = (double*)malloc(sz * sizeof(double));
+    double* e = (double*)malloc(sizeof(double) * dk);
+    double* z = (double*)malloc(sizeof(double) * dv);
+    double* r = (double*)malloc(sizeof(double) * dv);
+    double* u = (double*)malloc(sizeof(double) * dv);
+    double* du = (double*)malloc(sizeof(double) * dv);
+    double* de = (double*)malloc(sizeof(double) * dk);
+
+    /* forward: the state before every segment */
+    if (S0) memcpy(ckpt, S0 + soff, sz * sizeof(double));
+    {
+        double* S = (double*)malloc(sz * sizeof(double));
+        memcpy(S, ckpt, sz * sizeof(double));
+        for (int64_t t = 0; t < L; ++t) {
+            const int64_t T = bos + t;
+            o5_forward_token(dk, dv, S, q + tok_off(s, brow, T, h, dk), k + tok_off(s, brow, T, h, dk),
+                             v + tok_off(s, brow, T, h, dv), alpha + tok_off(s, brow, T, h, dk),
+                             b + tok_off(s, brow, T, h, dk), w + tok_off(s, brow, T, h, dv), e, z, r);
+            if ((t + 1) % O5_SEGMENT == 0) memcpy(ckpt + (size_t)((t + 1) / O5_SEGMENT) * sz, S, sz * sizeof(double));
+        }
+        free(S);
+    }
+
+    if (dSf) memcpy(dS, dSf + soff, sz * sizeof(double));
+    for (int64_t sgi = nseg - 1; sgi >= 0; --sgi) {
+        const int64_t t0 = sgi * O5_SEGMENT;
+        const int64_t t1 = t0 + O5_SEGMENT < L ? t0 + O5_SEGMENT : L;
+        /* recompute the states of this segment: seg[i] = state after token t0 + i - 1 */
+        memcpy(seg, ckpt + (size_t)sgi * sz, sz * sizeof(double));
+        for (int64_t t = t0; t < t1; ++t) {
+            const int64_t T = bos + t;
+            double* S = seg + (size_t)(t - t0 + 1) * sz;
+            memcpy(S, seg + (size_t)(t - t0) * sz, sz * sizeof(double));
+            o5_forward_token(dk, dv, S, q + tok_off(s, brow, T, h, dk), k + tok_off(s, brow, T, h, dk),
+                             v + tok_off(s, brow, T, h, dv), alpha + tok_off(s, brow, T, h, dk),
+                             b + tok_off(s, brow, T, h, dk), w + tok_off(s, brow, T, h, dv), e, z, r);
+        }
+        for (int64_t t = t1 - 1; t >= t0; --t) {
+            const int64_t T = bos + t;
+            const double* Sprev = seg + (size_t)(t - t0) * sz;
+            const double* S = seg + (size_t)(t - t0 + 1) * sz;
+            const double* qt = q + tok_off(s, brow, T, h, dk);
+            const double* kt = k + tok_off(s, brow, T, h, dk);
+            const double* bt = b + tok_off(s, brow, T, h, dk);
+            const double* at = alpha + tok_off(s, brow, T, h, dk);
+            const double* vt = v + tok_off(s, brow, T, h, dv);
+            const double* wt = w + tok_off(s, brow, T, h, dv);
+            const double* gt = dO + tok_off(s, brow, T, h, dv);
+            double* dqt = dq + tok_off(s, brow, T, h, dk);
+            double* dkt = dk_out + tok_off(s, brow, T, h, dk);
+            double* dbt = db + tok_off(s, brow, T, h, dk);
+            double* dat = da + tok_off(s, brow, T, h, dk);
+            double* dvt = dv_out + tok_off(s, brow, T, h, dv);
+            double* dwt = dw + tok_off(s, brow, T, h, dv);
+
+            /* the token's forward intermediates */
+            for (int32_t c = 0; c < dk; ++c) e[c] = bt[c] * kt[c];
+            for (int32_t j = 0; j < dv; ++j) z[j] = wt[j] * vt[j];
+            for (int32_t c = 0; c < dk; ++c)
+                for (int32_t j = 0; j < dv; ++j) Sbar[c * dv + j] = at[c] * Sprev[c * dv + j];
+            for (int32_t j = 0; j < dv; ++j) {
+                double acc = 0.0;
+                for (int32_t c = 0; c < dk; ++c) acc += Sbar[c * dv + j] * e[c];
+                u[j] = z[j] - acc;
+            }
+            /* o = S^T q */
+            for (int32_t c = 0; c < dk; ++c) {
+                double acc = 0.0;
+                for (int32_t j = 0; j < dv; ++j) acc += S[c * dv + j] * gt[j];
+                dqt[c] = acc;
+            }
+            for (int32_t c = 0; c < dk; ++c)
+                for (int32_t j = 0; j < dv; ++j) dS[c * dv + j] += qt[c] * gt[j];
+            /* S = Sbar + k u^T */
+            for (int32_t j = 0; j < dv; ++j) {
+                double acc = 0.0;
+                for (int32_t c = 0; c < dk; ++c) acc += dS[c * dv + j] * kt[c];
+                du[j] = acc;
+            }
+            for (int32_t c = 0; c < dk; ++c) {
+                double acc = 0.0;
+                for (int32_t j = 0; j < dv; ++j) acc += dS[c * dv + j] * u[j];
+                dkt[c] = acc;
+            }
+            /* u = z - Sbar^T e  (dS now stands for dL/dSbar) */
+            for (int32_t c = 0; c < dk; ++c) {
+                double acc = 0.0;
+                for (int32_t j = 0; j < dv; ++j) acc += Sbar[c * dv + j] * du[j];
+                de[c] = -acc;
+            }
+            for (int32_t c = 0; c < dk; ++c)
+                for (int32_t j = 0; j < dv; ++j) dS[c * dv + j] -= e[c] * du[j];
+            /* Sbar = Diag(alpha) Sprev */
+            for (int32_t c = 0; c < dk; ++c) {
+                double acc = 0.0;
+                for (int32_t j = 0; j < dv; ++j) acc += dS[c * dv + j] * Sprev[c * dv + j];
+                dat[c] = acc;
+            }
+            for (int32_t c = 0; c < dk; ++c)
+                for (int32_t j = 0; j < dv; ++j) dS[c * dv + j] *= at[c];
+            /* e = b (.) k, z = w (.) v */
+            for (int32_t c = 0; c < dk; ++c) {
+                dbt[c] = de[c] * kt[c];
+                dkt[c] += de[c] * bt[c];
+            }
+            for (int32_t j = 0; j < dv; ++j) {
+                dwt[j] = du[j] * vt[j];
+                dvt[j] = du[j] * wt[j];
+            }
+        }
+    }
+    if (dS0) memcpy(dS0 + soff, dS, sz * sizeof(double));
+    free(ckpt);
+    free(seg);
+    free(dS);
+    free(Sbar);
+    free(e);
+    free(z);
+    free(r);
+    free(u);
+    free(du);
+    free(de);
+}
+
 /* ---------------------------------------------------------------------- */
 
 #define CHAIN_LOOP(BODY)                                                              \
@@ -459,6 +647,24 @@ int gdn2_oracle_gdn(const double* q, const double* k, const double* v,
     if (check_shape(&s) || !q || !k || !v || !alpha || !beta || !o) return -1;
     const int nt = pick_threads(nthreads);
     CHAIN_LOOP(relative_chain(&s, n, h, 1, q, k, v, alpha, beta, initial_state, final_state, o));
+    return 0;
+}
+
+int gdn2_oracle_backward(const double* q, const double* k, const double* v,
+                         const double* alpha, const double* b, const double* w,
+                         const double* initial_state, const double* d_o, const double* d_final_state,
+                         double* dq, double* dk, double* dv, double* dalpha, double* db, double* dw,
+                         double* d_initial_state,
+                         const int32_t* cu_seqlens, int32_t B, int32_t T, int32_t H,
+                         int32_t dk_, int32_t dv_, int32_t num_seqs,
+                         const int32_t* chains, int32_t num_chains, int32_t nthreads)
+{
+    const shape_t s = {B, T, H, dk_, dv_, cu_seqlens ? num_seqs : B, cu_seqlens};
+    if (check_shape(&s) || !q || !k || !v || !alpha || !b || !w || !d_o) return -1;
+    if (!dq || !dk || !dv || !dalpha || !db || !dw) return -1;
+    const int nt = pick_threads(nthreads);
+    CHAIN_LOOP(backward_chain(&s, n, h, q, k, v, alpha, b, w, initial_state, d_o, d_final_state,
+                              dq, dk, dv, dalpha, db, dw, d_initial_state));
     return 0;
 }
 

@@ -212,7 +212,7 @@ def pin_chunked_equals_recurrent(orc):
 
 
 # --------------------------------------------------------------------------
-# P7: diagonal-plus-low-rank transition products [MP].
+# P7: products of per-token transitions (diagonal decay with a rank-one correction) [MP].
 
 
 def pin_transition_products(orc):
@@ -298,4 +298,148 @@ PINS = [
     pin_state_passing,
     pin_packed_equals_separate,
     pin_linearity,
+]
+
+
+# ==========================================================================
+# Pins of the backward oracle O5 (gradients of O1).  The loss is
+#   L = <dO, o> + <dS_final, S_final>;
+# O5 must return its gradients.  The reference values come from central
+# finite differences of the forward oracles, which are pinned above.
+
+BWD_NAMES = (("q", "dq"), ("k", "dk"), ("v", "dv"), ("alpha", "dalpha"), ("b", "db"), ("w", "dw"))
+
+
+def _loss(orc, x, s0, g, gs, cu=None):
+    o, s = orc.recurrent(x["q"], x["k"], x["v"], x["alpha"], x["b"], x["w"], s0, cu)
+    return float((o * g).sum() + (s * gs).sum())
+
+
+def _fd(f, arr, idx, h=1e-6):
+    """Central difference of f() with respect to arr[idx] (arr modified in place, restored)."""
+    old = arr[idx]
+    arr[idx] = old + h
+    fp = f()
+    arr[idx] = old - h
+    fm = f()
+    arr[idx] = old
+    return (fp - fm) / (2 * h)
+
+
+def _bwd_inputs(seed, B, T, H, dk, dv, N=None):
+    x, _ = rand_inputs(seed, B=B, T=T, H=H, dk=dk, dv=dv, state=False)
+    rng = np.random.default_rng(seed + 1000)
+    N = B if N is None else N
+    s0 = 0.3 * rng.standard_normal((N, H, dk, dv))
+    g = rng.standard_normal((B, T, H, dv))
+    gs = rng.standard_normal((N, H, dk, dv))
+    return x, s0, g, gs
+
+
+def _check_fd(orc, x, s0, g, gs, cu=None, sample=None, seed=0, tol=1e-6):
+    gr = orc.backward(x["q"], x["k"], x["v"], x["alpha"], x["b"], x["w"], g, s0, gs, cu)
+    rng = np.random.default_rng(seed)
+    targets = [(name, x[name], gr[key]) for name, key in BWD_NAMES] + [("s0", s0, gr["d_initial_state"])]
+    for name, arr, an in targets:
+        idxs = list(np.ndindex(arr.shape))
+        if sample is not None and len(idxs) > sample:
+            idxs = [idxs[i] for i in rng.choice(len(idxs), sample, replace=False)]
+        fd = np.array([_fd(lambda: _loss(orc, x, s0, g, gs, cu), arr, i) for i in idxs])
+        got = np.array([an[i] for i in idxs])
+        scale = max(1e-3, float(np.abs(fd).max()))
+        err = float(np.abs(got - fd).max())
+        assert err <= tol * scale, f"d{name}: max |analytic - finite difference| {err:.3e} > {tol * scale:.3e}"
+
+
+def pin_bwd_finite_differences(orc):
+    """Every gradient entry of a small batched problem with an initial state
+    and a final-state seed against central differences of O1."""
+    x, s0, g, gs = _bwd_inputs(40, B=2, T=9, H=2, dk=3, dv=2)
+    _check_fd(orc, x, s0, g, gs)
+
+
+def pin_bwd_packed_long(orc):
+    """Packed sequences (one empty, one crossing the 64-token recomputation
+    segment of O5, one short) against central differences on sampled entries."""
+    cu = np.array([0, 0, 70, 75], dtype=np.int32)
+    x, s0, g, gs = _bwd_inputs(41, B=1, T=75, H=1, dk=2, dv=2, N=3)
+    _check_fd(orc, x, s0, g, gs, cu=cu, sample=40, seed=41)
+
+
+def pin_bwd_kda_chain_rule(orc):
+    """With b = w = beta broadcast, dL/dbeta = sum_c db_c + sum_j dw_j and
+    dL/dalpha = dalpha; the references are central differences of the KDA
+    oracle O4a, an independent forward implementation."""
+    x, s0, g, gs = _bwd_inputs(42, B=1, T=11, H=2, dk=3, dv=2)
+    rng = np.random.default_rng(420)
+    beta = _sig(rng.standard_normal(x["q"].shape[:3]))
+    xb = dict(x, b=np.broadcast_to(beta[..., None], x["b"].shape).copy(),
+              w=np.broadcast_to(beta[..., None], x["w"].shape).copy())
+    gr = orc.backward(xb["q"], xb["k"], xb["v"], xb["alpha"], xb["b"], xb["w"], g, s0, gs)
+    alpha = xb["alpha"].copy()
+
+    def lk():
+        o, s = orc.kda(xb["q"], xb["k"], xb["v"], alpha, beta, s0)
+        return float((o * g).sum() + (s * gs).sum())
+
+    fd_beta = np.array([_fd(lk, beta, i) for i in np.ndindex(beta.shape)]).reshape(beta.shape)
+    fd_alpha = np.array([_fd(lk, alpha, i) for i in np.ndindex(alpha.shape)]).reshape(alpha.shape)
+    _close(gr["db"].sum(-1) + gr["dw"].sum(-1), fd_beta, tol=1e-6, what="KDA dbeta")
+    _close(gr["dalpha"], fd_alpha, tol=1e-6, what="KDA dalpha")
+
+
+def pin_bwd_gdn_chain_rule(orc):
+    """With a scalar decay broadcast over the key channels, dL/dalpha_scalar =
+    sum_c dalpha_c; the reference is central differences of the Gated DeltaNet
+    oracle O4b."""
+    x, s0, g, gs = _bwd_inputs(43, B=1, T=11, H=2, dk=3, dv=2)
+    rng = np.random.default_rng(430)
+    beta = _sig(rng.standard_normal(x["q"].shape[:3]))
+    a1 = _sig(rng.normal(2.0, 1.0, x["q"].shape[:3]))
+    xb = dict(x, b=np.broadcast_to(beta[..., None], x["b"].shape).copy(),
+              w=np.broadcast_to(beta[..., None], x["w"].shape).copy(),
+              alpha=np.broadcast_to(a1[..., None], x["alpha"].shape).copy())
+    gr = orc.backward(xb["q"], xb["k"], xb["v"], xb["alpha"], xb["b"], xb["w"], g, s0, gs)
+
+    def lg():
+        o, s = orc.gdn(xb["q"], xb["k"], xb["v"], a1, beta, s0)
+        return float((o * g).sum() + (s * gs).sum())
+
+    fd_a = np.array([_fd(lg, a1, i) for i in np.ndindex(a1.shape)]).reshape(a1.shape)
+    _close(gr["dalpha"].sum(-1), fd_a, tol=1e-6, what="GDN dalpha")
+
+
+def pin_bwd_causal(orc):
+    """A seed on the output of token t0 alone (no final-state seed) leaves the
+    gradients of every later token zero, and of token t0 itself dq nonzero."""
+    x, s0, g, gs = _bwd_inputs(44, B=1, T=12, H=1, dk=4, dv=3)
+    t0 = 6
+    g1 = np.zeros_like(g)
+    g1[:, t0] = g[:, t0]
+    gr = orc.backward(x["q"], x["k"], x["v"], x["alpha"], x["b"], x["w"], g1, s0, None)
+    for _, key in BWD_NAMES:
+        assert not gr[key][:, t0 + 1:].any(), f"{key}: nonzero after the seeded token"
+    assert np.abs(gr["dq"][:, t0]).max() > 0
+
+
+def pin_bwd_linear_in_seeds(orc):
+    """The gradients are linear in the seeds (dO, dS_final)."""
+    x, s0, g, gs = _bwd_inputs(45, B=1, T=10, H=2, dk=3, dv=3)
+    rng = np.random.default_rng(450)
+    g2, gs2 = rng.standard_normal(g.shape), rng.standard_normal(gs.shape)
+    a, c = 0.7, -1.3
+    r1 = orc.backward(x["q"], x["k"], x["v"], x["alpha"], x["b"], x["w"], g, s0, gs)
+    r2 = orc.backward(x["q"], x["k"], x["v"], x["alpha"], x["b"], x["w"], g2, s0, gs2)
+    r3 = orc.backward(x["q"], x["k"], x["v"], x["alpha"], x["b"], x["w"], a * g + c * g2, s0, a * gs + c * gs2)
+    for key in r1:
+        _close(r3[key], a * r1[key] + c * r2[key], tol=1e-11, what=f"linearity {key}")
+
+
+BACKWARD_PINS = [
+    pin_bwd_finite_differences,
+    pin_bwd_packed_long,
+    pin_bwd_kda_chain_rule,
+    pin_bwd_gdn_chain_rule,
+    pin_bwd_causal,
+    pin_bwd_linear_in_seeds,
 ]

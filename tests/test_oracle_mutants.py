@@ -37,18 +37,39 @@ MUTANTS = [
 ]
 
 
-def _mutate(src: str, old: str, new: str) -> str:
-    start = src.index("static void recurrent_chain(")
-    end = src.index("static void", start + 10)
+# (name, original text in backward_chain, replacement): plausible mistakes in
+# the adjoint of one token
+BWD_MUTANTS = [
+    ("dq_from_old_state", "acc += S[c * dv + j] * gt[j];", "acc += Sprev[c * dv + j] * gt[j];"),
+    ("no_output_seed_into_state", "dS[c * dv + j] += qt[c] * gt[j];", "(void)0;"),
+    ("du_with_erase_not_key", "acc += dS[c * dv + j] * kt[c];", "acc += dS[c * dv + j] * e[c];"),
+    ("dk_from_z_not_u", "acc += dS[c * dv + j] * u[j];", "acc += dS[c * dv + j] * z[j];"),
+    ("de_sign", "de[c] = -acc;", "de[c] = acc;"),
+    ("de_through_old_state", "acc += Sbar[c * dv + j] * du[j];", "acc += Sprev[c * dv + j] * du[j];"),
+    ("no_erase_term_in_state_grad", "dS[c * dv + j] -= e[c] * du[j];", "(void)0;"),
+    ("dalpha_with_new_state", "acc += dS[c * dv + j] * Sprev[c * dv + j];",
+     "acc += dS[c * dv + j] * S[c * dv + j];"),
+    ("no_decay_on_state_grad", "dS[c * dv + j] *= at[c];", "(void)0;"),
+    ("db_with_query", "dbt[c] = de[c] * kt[c];", "dbt[c] = de[c] * qt[c];"),
+    ("no_erase_path_into_dk", "dkt[c] += de[c] * bt[c];", "(void)0;"),
+    ("dw_dv_swapped", "dwt[j] = du[j] * vt[j];", "dwt[j] = du[j] * wt[j];"),
+    ("no_final_state_seed", "if (dSf) memcpy(dS, dSf + soff, sz * sizeof(double));", ""),
+]
+
+
+def _mutate(src: str, old: str, new: str, fn: str = "recurrent_chain") -> str:
+    start = src.index(f"static void {fn}(")
+    ends = [i for i in (src.find("\nstatic ", start + 1), src.find("#define CHAIN_LOOP", start)) if i > 0]
+    end = min(ends)  # the next function, or the exported wrappers
     body = src[start:end]
-    assert body.count(old) == 1, f"mutation anchor not unique in recurrent_chain: {old!r}"
+    assert body.count(old) == 1, f"mutation anchor not unique in {fn}: {old!r}"
     return src[:start] + body.replace(old, new) + src[end:]
 
 
-def _pins_failing(lib_path):
+def _pins_failing(lib_path, pins=None):
     orc = oracle.Oracle(oracle.load(lib_path))
     failing = []
-    for pin in oracle_pins.PINS:
+    for pin in (oracle_pins.PINS if pins is None else pins):
         try:
             pin(orc)
         except AssertionError:
@@ -69,6 +90,7 @@ def test_unmutated_copy_passes(tmpdir_mod):
     open(path, "w").write(src)
     lib = obuild.compile_oracle(path, os.path.join(tmpdir_mod, "libclean.so"))
     assert _pins_failing(lib) == []
+    assert _pins_failing(lib, oracle_pins.BACKWARD_PINS) == []
 
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
@@ -79,3 +101,13 @@ def test_mutant_is_caught(tmpdir_mod, name, old, new):
     lib = obuild.compile_oracle(path, os.path.join(tmpdir_mod, f"lib{name}.so"))
     failing = _pins_failing(lib)
     assert failing, f"mutant {name} passes every pin"
+
+
+@pytest.mark.parametrize("name,old,new", BWD_MUTANTS, ids=[m[0] for m in BWD_MUTANTS])
+def test_backward_mutant_is_caught(tmpdir_mod, name, old, new):
+    src = _mutate(open(obuild.SRC).read(), old, new, fn="backward_chain")
+    path = os.path.join(tmpdir_mod, f"bwd_{name}.c")
+    open(path, "w").write(src)
+    lib = obuild.compile_oracle(path, os.path.join(tmpdir_mod, f"libbwd_{name}.so"))
+    failing = _pins_failing(lib, oracle_pins.BACKWARD_PINS)
+    assert failing, f"backward mutant {name} passes every backward pin"

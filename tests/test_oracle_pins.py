@@ -40,3 +40,18 @@ def test_zero_length_sequences(orc):
     o, s = orc.recurrent(x["q"], x["k"], x["v"], x["alpha"], x["b"], x["w"], s0, cu)
     np.testing.assert_array_equal(s[0], s0[0])            # empty sequence: state passes through
     np.testing.assert_array_equal(s[2], s0[2])
+
+
+@pytest.mark.parametrize("pin", oracle_pins.BACKWARD_PINS, ids=lambda p: p.__name__)
+def test_backward_pin(orc, pin):
+    pin(orc)
+
+
+def test_backward_chain_subset(orc):
+    x, s0, g, gs = oracle_pins._bwd_inputs(46, B=2, T=7, H=3, dk=3, dv=2)
+    full = orc.backward(x["q"], x["k"], x["v"], x["alpha"], x["b"], x["w"], g, s0, gs)
+    part = orc.backward(x["q"], x["k"], x["v"], x["alpha"], x["b"], x["w"], g, s0, gs, chains=[4])
+    n, h = divmod(4, 3)
+    for key in ("dq", "dk", "dv", "dalpha", "db", "dw"):
+        np.testing.assert_array_equal(part[key][n, :, h], full[key][n, :, h])
+    np.testing.assert_array_equal(part["d_initial_state"][n, h], full["d_initial_state"][n, h])
