@@ -6,6 +6,7 @@ Two entry points, both hand-written HIP behind the C ABI in include/gdn2.h:
                           chunks; varlen via ``cu_seqlens``)
 * ``gdn2_recurrent_step`` fused single-token decode step, state updated in place
 * ``gdn2_recurrent_fwd``  the fused recurrent form over T tokens per sequence
+* ``gdn2_chunk_bwd``      gradients of the chunkwise forward (gate-aware backward)
 * ``gdn2_chunk_fwd_gates`` / ``gdn2_recurrent_step_gates``: the same with a gate
   layout (``GATES_*`` flags: scalar erase, write or decay gates, tied write gate)
 
@@ -20,6 +21,8 @@ from .binding import (  # noqa: F401
     GATES_SCALAR_WRITE,
     GATES_TIED,
     Gdn2Error,
+    gdn2_chunk_bwd,
+    gdn2_chunk_bwd_workspace_bytes,
     gdn2_chunk_fwd,
     gdn2_chunk_fwd_gates,
     gdn2_chunk_fwd_workspace_bytes,
@@ -39,6 +42,8 @@ __all__ = [
     "GATES_SCALAR_WRITE",
     "GATES_TIED",
     "Gdn2Error",
+    "gdn2_chunk_bwd",
+    "gdn2_chunk_bwd_workspace_bytes",
     "gdn2_chunk_fwd",
     "gdn2_chunk_fwd_gates",
     "gdn2_chunk_fwd_workspace_bytes",

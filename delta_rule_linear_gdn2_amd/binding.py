@@ -22,7 +22,8 @@ STATUS_NAMES = {
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 
-EXPORTS = ("gdn2_chunk_fwd", "gdn2_chunk_fwd_gates", "gdn2_chunk_fwd_workspace_bytes",
+EXPORTS = ("gdn2_chunk_bwd", "gdn2_chunk_bwd_workspace_bytes", "gdn2_chunk_fwd", "gdn2_chunk_fwd_gates",
+           "gdn2_chunk_fwd_workspace_bytes",
            "gdn2_recurrent_fwd", "gdn2_recurrent_step", "gdn2_recurrent_step_gates", "gdn2_status_string",
            "gdn2_version")
 
@@ -79,6 +80,10 @@ def load(path: str = LIB_PATH):
     lib.gdn2_recurrent_step_gates.restype = ctypes.c_int
     lib.gdn2_recurrent_fwd.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]
     lib.gdn2_recurrent_fwd.restype = ctypes.c_int
+    lib.gdn2_chunk_bwd.argtypes = [P] * 17 + [I, I, I, I, I, I, I, P, Z, P]
+    lib.gdn2_chunk_bwd.restype = ctypes.c_int
+    lib.gdn2_chunk_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+    lib.gdn2_chunk_bwd_workspace_bytes.restype = Z
     lib.gdn2_status_string.argtypes = [ctypes.c_int]
     lib.gdn2_status_string.restype = ctypes.c_char_p
     lib.gdn2_version.argtypes = []
@@ -291,4 +296,58 @@ def gdn2_recurrent_fwd(q, k, v, alpha, b, w, state, *, gates=GATES_FULL, out=Non
                                 N, T, H, dk, dv, code, gates, _stream(stream))
     if rc != GDN2_OK:
         raise Gdn2Error(rc, "gdn2_recurrent_fwd")
+    return out
+
+
+def gdn2_chunk_bwd_workspace_bytes(B, T, H, dk, dv, num_seqs, dtype_code) -> int:
+    return int(load().gdn2_chunk_bwd_workspace_bytes(B, T, H, dk, dv, num_seqs, dtype_code))
+
+
+def gdn2_chunk_bwd(q, k, v, alpha, b, w, d_o, initial_state=None, d_final_state=None, *, cu_seqlens=None,
+                   output_d_initial_state=True, d_initial_state=None, workspace=None, stream=None):
+    """Gradients of gdn2_chunk_fwd for the loss <d_o, o> + <d_final_state, S_final>.
+
+    Inputs as for gdn2_chunk_fwd, plus d_o [B, T, H, dv] (input dtype) and
+    d_final_state [N, H, dk, dv] float32 or None.  Returns a dict with dq, dk,
+    db [B, T, H, dk] and dv, dw [B, T, H, dv] (input dtype), dalpha [B, T, H, dk]
+    float32 and d_initial_state [N, H, dk, dv] float32 (None if not wanted).
+    ``workspace`` (uint8 device tensor) is allocated when not given.
+    """
+    import torch
+
+    lib = load()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(dt)
+    N = B if cu_seqlens is None else int(cu_seqlens.shape[0]) - 1
+    for name, t, width in (("q", q, dk), ("k", k, dk), ("b", b, dk), ("v", v, dv), ("w", w, dv),
+                           ("d_o", d_o, dv)):
+        _check(name, t, (B, T, H, width), dt, dev)
+    _check("alpha", alpha, (B, T, H, dk), torch.float32, dev)
+    for name, t in (("initial_state", initial_state), ("d_final_state", d_final_state)):
+        if t is not None:
+            _check(name, t, (N, H, dk, dv), torch.float32, dev)
+    if cu_seqlens is not None:
+        _check("cu_seqlens", cu_seqlens, (N + 1,), torch.int32, dev)
+    out = {name: torch.empty((B, T, H, width), dtype=dt, device=dev)
+           for name, width in (("dq", dk), ("dk", dk), ("db", dk), ("dv", dv), ("dw", dv))}
+    out["dalpha"] = torch.empty((B, T, H, dk), dtype=torch.float32, device=dev)
+    if d_initial_state is not None:
+        _check("d_initial_state", d_initial_state, (N, H, dk, dv), torch.float32, dev)
+    elif output_d_initial_state:
+        d_initial_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    out["d_initial_state"] = d_initial_state
+    ws_bytes = gdn2_chunk_bwd_workspace_bytes(B, T, H, dk, dv, N if cu_seqlens is not None else 0, code)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    elif workspace.numel() < ws_bytes:
+        raise ValueError(f"workspace of {workspace.numel()} bytes < {ws_bytes}")
+    rc = lib.gdn2_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(initial_state),
+                            _ptr(d_o), _ptr(d_final_state), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                            _ptr(out["dalpha"]), _ptr(out["db"]), _ptr(out["dw"]), _ptr(d_initial_state),
+                            _ptr(cu_seqlens), B, T, H, dk, dv, N, code, _ptr(workspace),
+                            0 if workspace is None else workspace.numel(), _stream(stream))
+    if rc != GDN2_OK:
+        raise Gdn2Error(rc, "gdn2_chunk_bwd")
     return out

@@ -23,6 +23,7 @@ SOURCES = [
     "recurrent_step.hip",
     "chunk_fwd_simple.hip",
     "chunk_fwd_mfma.hip",
+    "chunk_bwd.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -168,6 +168,87 @@ gdn2_status recurrent(const void* q, const void* k, const void* v, const float* 
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 
+// Workspace regions of the backward pass: chunk-start states, chunk-end
+// state gradients (slots x H x dk x dv FP32 each, per batch row), U and dX
+// rows (B x T x H x dv FP32 each), each region 256-byte aligned.
+struct BwdWorkspace {
+    int64_t slots;
+    size_t states, rows, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+BwdWorkspace bwd_workspace(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv, bool varlen, int32_t N)
+{
+    BwdWorkspace w;
+    w.slots = T == 0 ? 0 : (int64_t(T) + gdn2::kBwdChunk - 1) / gdn2::kBwdChunk + (varlen ? N : 0);
+    w.states = align256(size_t(B) * size_t(w.slots) * size_t(H) * size_t(dk) * size_t(dv) * 4);
+    w.rows = align256(size_t(B) * size_t(T) * size_t(H) * size_t(dv) * 4);
+    w.total = 2 * w.states + 2 * w.rows;
+    return w;
+}
+
+gdn2_status chunk_bwd(const void* q, const void* k, const void* v, const float* alpha, const void* b, const void* w,
+                      const float* initial_state, const void* d_o, const float* d_final_state, void* dq, void* dk_,
+                      void* dv_, float* dalpha, void* db, void* dw, float* d_initial_state,
+                      const int32_t* cu_seqlens, int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                      int32_t num_seqs, gdn2_dtype dtype, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (dtype != GDN2_DTYPE_F32 && dtype != GDN2_DTYPE_BF16) return GDN2_ERR_BAD_DTYPE;
+    if (B <= 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return GDN2_ERR_BAD_SHAPE;
+    if (cu_seqlens && (B != 1 || num_seqs <= 0)) return GDN2_ERR_BAD_SHAPE;
+    if (!supported_head(dk) || !supported_head(dv)) return GDN2_ERR_UNSUPPORTED;
+    const int32_t N = cu_seqlens ? num_seqs : B;
+    if (T > 0 && (!q || !k || !v || !alpha || !b || !w || !d_o || !dq || !dk_ || !dv_ || !dalpha || !db || !dw))
+        return GDN2_ERR_NULL_POINTER;
+    const void* ptrs[] = {q, k, v, alpha, b, w, initial_state, d_o, d_final_state,
+                          dq, dk_, dv_, dalpha, db, dw, d_initial_state, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDN2_ERR_MISALIGNED;
+    if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return GDN2_ERR_MISALIGNED;
+
+    const BwdWorkspace ws = bwd_workspace(B, T, H, dk, dv, cu_seqlens != nullptr, N);
+    if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return GDN2_ERR_WORKSPACE;
+
+    const int64_t tokens = int64_t(B) * T * H;
+    const int eb = element_bytes(dtype);
+    const int64_t state_bytes = int64_t(N) * H * dk * dv * 4;
+    const Span in[] = {span(q, tokens * dk * eb), span(k, tokens * dk * eb), span(v, tokens * dv * eb),
+                       span(alpha, tokens * dk * 4), span(b, tokens * dk * eb), span(w, tokens * dv * eb),
+                       span(initial_state, initial_state ? state_bytes : 0), span(d_o, tokens * dv * eb),
+                       span(d_final_state, d_final_state ? state_bytes : 0),
+                       span(cu_seqlens, cu_seqlens ? int64_t(N + 1) * 4 : 0)};
+    const Span out[] = {span(dq, tokens * dk * eb), span(dk_, tokens * dk * eb), span(dv_, tokens * dv * eb),
+                        span(dalpha, tokens * dk * 4), span(db, tokens * dk * eb), span(dw, tokens * dv * eb),
+                        span(d_initial_state, d_initial_state ? state_bytes : 0),
+                        span(workspace, ws.total > 0 ? int64_t(ws.total) : 0)};
+    constexpr int kDInit = 6;
+    for (int i = 0; i < 8; ++i) {
+        for (const Span& x : in) {
+            // the initial-state gradient may replace the final-state gradient in place
+            if (i == kDInit && d_initial_state == d_final_state && x.lo == in[8].lo) continue;
+            if (overlap(out[i], x)) return GDN2_ERR_ALIAS;
+        }
+        for (int j = 0; j < i; ++j)
+            if (overlap(out[i], out[j])) return GDN2_ERR_ALIAS;
+    }
+
+    gdn2::BwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.b = b; a.w = w;
+    a.initial_state = initial_state; a.d_o = d_o; a.d_final_state = d_final_state;
+    a.dq = dq; a.dk = dk_; a.dv = dv_; a.dalpha = dalpha; a.db = db; a.dw = dw;
+    a.d_initial_state = d_initial_state; a.cu_seqlens = cu_seqlens;
+    a.B = B; a.T = T; a.H = H; a.dk_ = dk; a.dv_ = dv; a.N = N;
+    a.slots = ws.slots;
+    unsigned char* base = static_cast<unsigned char*>(workspace);
+    a.ws_states = ws.total ? reinterpret_cast<float*>(base) : nullptr;
+    a.ws_dstates = ws.total ? reinterpret_cast<float*>(base + ws.states) : nullptr;
+    a.ws_u = ws.total ? reinterpret_cast<float*>(base + 2 * ws.states) : nullptr;
+    a.ws_dx = ws.total ? reinterpret_cast<float*>(base + 2 * ws.states + ws.rows) : nullptr;
+    const hipError_t e = gdn2::launch_chunk_bwd(a, dtype == GDN2_DTYPE_BF16, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -217,6 +298,26 @@ gdn2_status gdn2_recurrent_fwd(const void* q, const void* k, const void* v, cons
                                int32_t dv, gdn2_dtype dtype, int32_t gates, void* stream)
 {
     return recurrent(q, k, v, alpha, b, w, state, o, N, T, H, dk, dv, dtype, gates, stream);
+}
+
+gdn2_status gdn2_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha, const void* b,
+                           const void* w, const float* initial_state, const void* d_o, const float* d_final_state,
+                           void* dq, void* dk, void* dv, float* dalpha, void* db, void* dw, float* d_initial_state,
+                           const int32_t* cu_seqlens, int32_t B, int32_t T, int32_t H, int32_t dk_size,
+                           int32_t dv_size, int32_t num_seqs, gdn2_dtype dtype, void* workspace,
+                           size_t workspace_bytes, void* stream)
+{
+    return chunk_bwd(q, k, v, alpha, b, w, initial_state, d_o, d_final_state, dq, dk, dv, dalpha, db, dw,
+                     d_initial_state, cu_seqlens, B, T, H, dk_size, dv_size, num_seqs, dtype, workspace,
+                     workspace_bytes, stream);
+}
+
+size_t gdn2_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv, int32_t num_seqs,
+                                      gdn2_dtype dtype)
+{
+    (void)dtype;
+    if (B <= 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return 0;
+    return bwd_workspace(B, T, H, dk, dv, num_seqs > 0, num_seqs).total;
 }
 
 }  // extern "C"

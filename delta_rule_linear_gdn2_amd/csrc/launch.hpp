@@ -39,7 +39,40 @@ struct StepArgs {
     int32_t T;      // tokens per sequence: inputs [N, T, H, .], o [N, T, H, dv]
 };
 
+// Chunkwise backward.  Chunk-start states and chunk-end state gradients sit
+// in "slots": slot m of batch row n for packed-free input, and for packed
+// sequences slot (bos + m * kBwdChunk) / kBwdChunk + n of row 0 (distinct
+// for distinct chunks, fewer than ceil(T / kBwdChunk) + N).
+constexpr int kBwdChunk = 32;
+
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const void* b;
+    const void* w;
+    const float* initial_state;
+    const void* d_o;
+    const float* d_final_state;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dalpha;
+    void* db;
+    void* dw;
+    float* d_initial_state;
+    const int32_t* cu_seqlens;
+    int32_t B, T, H, dk_, dv_, N;
+    int64_t slots;       // chunk slots per batch row
+    float* ws_states;    // [B][slots][H][dk][dv] state at each chunk start
+    float* ws_dstates;   // [B][slots][H][dk][dv] gradient of the state at each chunk end
+    float* ws_u;         // [B * T * H][dv] U rows
+    float* ws_dx;        // [B * T * H][dv] dX rows
+};
+
 // Each returns hipSuccess or the launch error; bf16 selects the input dtype.
+hipError_t launch_chunk_bwd(const BwdArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_recurrent(const StepArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_chunk_fwd_simple(const ChunkArgs& a, bool bf16, hipStream_t stream);
 

@@ -198,6 +198,45 @@ gdn2_status gdn2_recurrent_fwd(const void* q, const void* k, const void* v,
                                int32_t N, int32_t T, int32_t H, int32_t dk, int32_t dv,
                                gdn2_dtype dtype, int32_t gates, void* stream);
 
+/*
+ * Chunkwise backward pass: the gradients of gdn2_chunk_fwd (full gate layout)
+ * for the loss <d_o, o> + <d_final_state, final_state>, accumulated through
+ * the gated keys and values with the channel-wise decay inside the sums
+ * ("Token processing and parallel training": the backward pass cannot pull
+ * the channel-wise factors out as it could a scalar beta).  FP32 arithmetic;
+ * alpha is clamped to [2^-15, 1] as in the forward pass, and dalpha is zero
+ * where the clamp is active.
+ *
+ *   q, k, v, alpha, b, w, initial_state, cu_seqlens, B, T, H, dk, dv,
+ *   num_seqs, dtype: the forward call's arguments (initial_state may be NULL).
+ *   d_o           : [B, T, H, dv] dtype, the gradient of o.
+ *   d_final_state : [N, H, dk, dv] FP32, or NULL for zero.
+ *   dq, dk, db    : [B, T, H, dk] dtype      dv, dw : [B, T, H, dv] dtype
+ *   dalpha        : [B, T, H, dk] FP32
+ *   d_initial_state : [N, H, dk, dv] FP32, or NULL if not wanted; may be the
+ *                   same pointer as d_final_state (replaced in place).
+ *   workspace     : device memory of at least gdn2_chunk_bwd_workspace_bytes
+ *                   (same sizes; num_seqs = the packed sequence count with
+ *                   cu_seqlens, else 0), 16-byte aligned; its contents on
+ *                   entry do not matter.  Too small or NULL: GDN2_ERR_WORKSPACE.
+ * Every output, and the workspace, must not overlap an input or another
+ * output (GDN2_ERR_ALIAS).  Results are bitwise reproducible.
+ */
+gdn2_status gdn2_chunk_bwd(const void* q, const void* k, const void* v,
+                           const float* alpha, const void* b, const void* w,
+                           const float* initial_state, const void* d_o, const float* d_final_state,
+                           void* dq, void* dk, void* dv, float* dalpha, void* db, void* dw,
+                           float* d_initial_state, const int32_t* cu_seqlens,
+                           int32_t B, int32_t T, int32_t H, int32_t dk_size, int32_t dv_size,
+                           int32_t num_seqs, gdn2_dtype dtype,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace needed by gdn2_chunk_bwd: 2 x B x (ceil(T / 32) + num_seqs) x H x
+ * dk x dv x 4 bytes of states plus 2 x B x T x H x dv x 4 bytes of rows (0 when
+ * T = 0).  Returns 0 for invalid sizes. */
+size_t gdn2_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t dk_size, int32_t dv_size,
+                                      int32_t num_seqs, gdn2_dtype dtype);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* gdn2_status_string(gdn2_status status);
 

@@ -209,3 +209,52 @@ def recurrent_fwd_call(lib, gates=0, **kw):
 ])
 def test_recurrent_fwd_rejects(lib, gates, kw, expected):
     assert recurrent_fwd_call(lib, gates, **kw) == expected
+
+
+def bwd_call(lib, **kw):
+    # B=2, T=64, H=4, dk=dv=64 bf16: token tensors 64 KiB, states 128 KiB
+    args = dict(q=fake(0), k=fake(1), v=fake(2), alpha=fake(3), b=fake(4), w=fake(5), s0=fake(6),
+                d_o=fake(7), dsf=fake(8), dq=fake(9), dk=fake(10), dv=fake(11), dalpha=fake(12),
+                db=fake(13), dw=fake(14), ds0=fake(15), cu=None, B=2, T=64, H=4, dk_=64, dv_=64,
+                num_seqs=0, dtype=1, ws=fake(16), ws_bytes=1 << 30)
+    args.update(kw)
+    a = args
+    return lib.gdn2_chunk_bwd(a["q"], a["k"], a["v"], a["alpha"], a["b"], a["w"], a["s0"], a["d_o"], a["dsf"],
+                              a["dq"], a["dk"], a["dv"], a["dalpha"], a["db"], a["dw"], a["ds0"], a["cu"],
+                              a["B"], a["T"], a["H"], a["dk_"], a["dv_"], a["num_seqs"], a["dtype"],
+                              a["ws"], a["ws_bytes"], None)
+
+
+def test_bwd_workspace_query(lib):
+    # 2 x B x ceil(T/32) x H x dk x dv x 4 + 2 x B x T x H x dv x 4
+    assert binding.gdn2_chunk_bwd_workspace_bytes(8, 4096, 16, 128, 128, 0, 1) == \
+        2 * 8 * 128 * 16 * 128 * 128 * 4 + 2 * 8 * 4096 * 16 * 128 * 4
+    assert binding.gdn2_chunk_bwd_workspace_bytes(1, 0, 4, 64, 64, 3, 1) == 0
+    assert binding.gdn2_chunk_bwd_workspace_bytes(1, 100, 2, 32, 32, 3, 0) == \
+        2 * (4 + 3) * 2 * 32 * 32 * 4 + 2 * 100 * 2 * 32 * 4
+    assert binding.gdn2_chunk_bwd_workspace_bytes(0, 100, 2, 32, 32, 0, 0) == 0
+
+
+# Every case must be rejected before launch.
+@pytest.mark.parametrize("kw,expected", [
+    (dict(dtype=2), DTYPE),
+    (dict(B=0), SHAPE),
+    (dict(T=-3), SHAPE),
+    (dict(cu=fake(17), B=2, num_seqs=2), SHAPE),
+    (dict(dk_=48), UNSUP),
+    (dict(d_o=None), NULLP),
+    (dict(dalpha=None), NULLP),
+    (dict(w=None), NULLP),
+    (dict(dalpha=fake(12, 4)), MISAL),
+    (dict(ws=fake(16, 8)), MISAL),
+    (dict(ws=None), WS),
+    (dict(ws_bytes=4096), WS),
+    (dict(dq=fake(0, 1024)), ALIAS),                  # dq inside q
+    (dict(dk=fake(9, 512)), ALIAS),                   # dk inside dq
+    (dict(ws=fake(1)), ALIAS),                        # workspace over k
+    (dict(ds0=fake(6)), ALIAS),                       # d_initial_state == initial_state
+    (dict(dalpha=fake(7, 2048)), ALIAS),              # dalpha inside d_o
+    (dict(ds0=fake(8, 1024)), ALIAS),                 # partial overlap with d_final_state
+])
+def test_chunk_bwd_rejects(lib, kw, expected):
+    assert bwd_call(lib, **kw) == expected

@@ -1,0 +1,152 @@
+"""GPU parity of gdn2_chunk_bwd (the gate-aware backward pass) against the
+FP64 oracle's reverse-mode gradients O5 (needs an MI355X).
+
+Bar: relative L2 error of each gradient tensor (dq, dk, dv, dalpha, db, dw,
+dS0), at most 1e-4 for FP32 inputs and 1e-2 for bf16 inputs, the same bar as
+the forward pass.  The seeds d_o and d_final_state are N(0, 1), rounded to the
+input dtype, and the oracle sees exactly the values the kernels see."""
+import numpy as np
+import pytest
+
+import gpu_util as G
+import oracle
+from delta_rule_linear_gdn2_amd import binding
+from delta_rule_linear_gdn2_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ("dq", "dk", "dv", "dalpha", "db", "dw")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    yield
+
+
+def _seeds(x, dtype, seed, with_dsf=True):
+    rng = np.random.default_rng(seed)
+    B, T, H, _ = x["q"].shape
+    dv = x["v"].shape[-1]
+    dk = x["q"].shape[-1]
+    N = B if x.get("cu_seqlens") is None else len(x["cu_seqlens"]) - 1
+    g = rng.standard_normal((B, T, H, dv)).astype(np.float32)
+    if dtype == "bf16":
+        g = W.round_bf16(g)
+    gs = rng.standard_normal((N, H, dk, dv)).astype(np.float32) if with_dsf else None
+    return g, gs
+
+
+def gpu_bwd(x, dtype, g, gs, **kw):
+    import torch
+
+    d = G.to_dev(x, dtype)
+    dg = W.to_torch(g, dtype, "cuda")
+    dgs = None if gs is None else torch.from_numpy(gs).cuda()
+    out = binding.gdn2_chunk_bwd(d["q"], d["k"], d["v"], d["alpha"], d["b"], d["w"], dg, d["initial_state"], dgs,
+                                 cu_seqlens=d["cu_seqlens"], **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_bwd(x, g, gs, chains=None, threads=0):
+    return oracle.backward(x["q"], x["k"], x["v"], x["alpha"], x["b"], x["w"], g, x.get("initial_state"), gs,
+                           x.get("cu_seqlens"), chains=chains, threads=threads)
+
+
+def _compare(out, ref, dtype, what, d_init=True):
+    for name in GRADS:
+        G.assert_rel(G.f64(out[name]), ref[name], G.TOL[dtype], f"{what} {name}")
+    if d_init:
+        G.assert_rel(G.f64(out["d_initial_state"]), ref["d_initial_state"], G.TOL[dtype], f"{what} dS0")
+
+
+@pytest.mark.parametrize("dtype,dk,dv", [("f32", 32, 32), ("f32", 64, 128), ("f32", 128, 64), ("f32", 128, 128),
+                                         ("bf16", 128, 128), ("bf16", 64, 32)])
+def test_backward_shapes(dtype, dk, dv):
+    """B=2, T=100 (three 32-token chunks and a ragged 4), H=3, random initial state and seeds."""
+    x = W.make("batched_bf16", seed=201, B=2, T=100, H=3, dk=dk, dv=dv, dtype=dtype)
+    g, gs = _seeds(x, dtype, 202)
+    _compare(gpu_bwd(x, dtype, g, gs), oracle_bwd(x, g, gs), dtype, f"bwd {dtype} dk={dk} dv={dv}")
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
+def test_backward_varlen_edges(dtype, d):
+    """Zero-length, one-token, chunk-boundary and ragged sequences packed together."""
+    lens = [0, 1, 31, 32, 33, 70, 0, 7, 100]
+    cu = W.cu_from_lengths(lens)
+    x = W.make("batched_bf16", seed=203, B=1, T=int(cu[-1]), H=2, dk=d, dv=d, dtype=dtype)
+    x["cu_seqlens"] = cu
+    x["initial_state"] = 0.1 * np.random.default_rng(204).standard_normal((len(lens), 2, d, d)).astype(np.float32)
+    g, gs = _seeds(x, dtype, 205)
+    out = gpu_bwd(x, dtype, g, gs)
+    ref = oracle_bwd(x, g, gs)
+    _compare(out, ref, dtype, f"bwd varlen {dtype} d={d}")
+    # zero-length sequences pass the final-state seed through unchanged
+    np.testing.assert_array_equal(G.f64(out["d_initial_state"])[0], gs[0])
+    np.testing.assert_array_equal(G.f64(out["d_initial_state"])[6], gs[6])
+
+
+def test_backward_without_state_seed_or_initial_state():
+    """No initial state, no final-state seed, no initial-state gradient wanted."""
+    x = W.make("tiny_f32", seed=206, T=90)
+    g, _ = _seeds(x, "f32", 207, with_dsf=False)
+    out = gpu_bwd(x, "f32", g, None, output_d_initial_state=False)
+    assert out["d_initial_state"] is None
+    _compare(out, oracle_bwd(x, g, None), "f32", "bwd no state", d_init=False)
+
+
+def test_backward_in_place_state_gradient():
+    """d_initial_state may replace d_final_state in place."""
+    import torch
+
+    x = W.make("batched_bf16", seed=208, B=2, T=70, H=2, dk=64, dv=64, dtype="f32")
+    g, gs = _seeds(x, "f32", 209)
+    ref = gpu_bwd(x, "f32", g, gs)
+    d = G.to_dev(x, "f32")
+    buf = torch.from_numpy(gs).cuda()
+    out = binding.gdn2_chunk_bwd(d["q"], d["k"], d["v"], d["alpha"], d["b"], d["w"], W.to_torch(g, "f32", "cuda"),
+                                 d["initial_state"], buf, d_initial_state=buf)
+    torch.cuda.synchronize()
+    assert out["d_initial_state"].data_ptr() == buf.data_ptr()
+    assert torch.equal(buf, ref["d_initial_state"])
+    for name in GRADS:
+        assert torch.equal(out[name], ref[name]), name
+
+
+def test_backward_bitwise_deterministic():
+    import torch
+
+    x = W.make("batched_bf16", seed=210, B=2, T=150, H=4)
+    g, gs = _seeds(x, "bf16", 211)
+    o1 = gpu_bwd(x, "bf16", g, gs)
+    o2 = gpu_bwd(x, "bf16", g, gs)
+    for name in GRADS + ("d_initial_state",):
+        assert torch.equal(o1[name], o2[name]), name
+
+
+@pytest.mark.parametrize("mode", ["kda", "gdn"])
+def test_backward_reduced_gate_inputs(mode):
+    """Inputs with tied scalar gates (broadcast): the same bar."""
+    x = W.make("batched_bf16", gate_mode=mode, seed=212, B=2, T=96, H=2, dk=128, dv=128)
+    g, gs = _seeds(x, "bf16", 213)
+    _compare(gpu_bwd(x, "bf16", g, gs), oracle_bwd(x, g, gs), "bf16", f"bwd {mode} inputs")
+
+
+def test_backward_batched_bf16_sampled():
+    """B=8, H=16, T=4096, d=128, bf16 (the headline forward shape): sampled chains."""
+    x = W.make("batched_bf16")
+    g, gs = _seeds(x, "bf16", 214)
+    out = gpu_bwd(x, "bf16", g, gs)
+    chains = [(0, 0), (7, 15), (3, 9)]
+    ids = [n * 16 + h for n, h in chains]
+    ref = oracle_bwd(x, g, gs, chains=ids)
+    for name in GRADS:
+        got = np.concatenate([G.f64(out[name][n, :, h]).ravel() for n, h in chains])
+        exp = np.concatenate([ref[name][n, :, h].ravel() for n, h in chains])
+        G.assert_rel(got, exp, G.TOL["bf16"], f"batched bwd {name} (sampled)")
+    got = np.concatenate([G.f64(out["d_initial_state"][n, h]).ravel() for n, h in chains])
+    exp = np.concatenate([ref["d_initial_state"][n, h].ravel() for n, h in chains])
+    G.assert_rel(got, exp, G.TOL["bf16"], "batched bwd dS0 (sampled)")
