@@ -29,14 +29,19 @@
 // nothing overflows.  alpha is clamped to [2^-15, 1] as in the forward
 // kernels; the gradient is zero where the clamp is active.
 //
-// Three kernels, 32-token chunks (the same mathematics as any chunk size):
-//   bwd_states  (chain x value tile, chunks in order)   recompute the forward,
-//               store every chunk-start state;
-//   bwd_dstate  (chain x value tile, chunks in reverse) U, dX and the state
-//               gradient recurrence; dv, dw and dS0; store U and dX rows and
-//               each chunk-end state gradient;
+// Four kernels, 32-token chunks (the same mathematics as any chunk size):
+//   bwd_prep    (chunk x head, all parallel)            A, P, Tm = (I + A)^-1,
+//               Et, Qt, Kb and 2^G_L of every chunk, once, into the workspace;
+//   bwd_states  (chain x value tile, chunks in order)   X, U = Tm X and the
+//               state update; stores every chunk-start state;
+//   bwd_dstate  (chain x value tile, chunks in reverse) U, dU, dX = Tm^T dU and
+//               the state-gradient recurrence; dv, dw and dS0; stores U and dX
+//               rows and each chunk-end state gradient;
 //   bwd_keys    (chunk x head x channel block)          dA, dP, dEt, dQt, dKb
 //               over all value columns, then dq, dk, db and dalpha.
+// The two sequential kernels only multiply: all of a chunk's triangular
+// algebra is done in parallel beforehand.  Each thread owns several outputs
+// of every product so that one LDS read feeds several FMAs.
 #include "gdn2_device.hpp"
 #include "launch.hpp"
 
@@ -45,6 +50,8 @@ namespace {
 
 constexpr int kBwdThreads = 256;
 constexpr int CH = kBwdChunk;
+constexpr int kTile = 32;  // value columns per workgroup of the sequential kernels
+static_assert(kBwdThreads == 8 * kTile && CH == 32, "thread layouts below assume 8 groups of 32 lanes");
 
 __device__ __forceinline__ int64_t slot_of(const BwdArgs& a, int n, int64_t bos, int m)
 {
@@ -57,26 +64,78 @@ __device__ __forceinline__ int64_t slot_base(const BwdArgs& a, int64_t row, int6
     return ((row * a.slots + slot) * a.H + h) * int64_t(a.dk_) * a.dv_;
 }
 
-// The forward quantities of one chunk shared by the first two kernels.
+// Per-chunk prepared block (floats): Tm [CH][CH], Pm [CH][CH], Et, Qt, Kb [CH][dk], gamma [dk].
+__host__ __device__ constexpr int64_t prep_floats(int dk) { return 2 * CH * CH + 3 * int64_t(CH) * dk + dk; }
+constexpr int kPrepT = 0, kPrepP = CH * CH, kPrepE = 2 * CH * CH;
+__device__ __forceinline__ int64_t prep_base(const BwdArgs& a, int64_t row, int64_t slot, int h)
+{
+    return ((row * a.slots + slot) * a.H + h) * prep_floats(a.dk_);
+}
+
+// The chunk that owns a slot (false for an unused slot).
+__device__ bool chunk_of_slot(const BwdArgs& a, int64_t row, int64_t slot, int& n, int& m, int64_t& bos,
+                              int64_t& eos, int64_t& brow)
+{
+    if (!a.cu_seqlens) {
+        n = int(row);
+        m = int(slot);
+        sequence_bounds(nullptr, n, a.T, bos, eos, brow);
+        return int64_t(m) * CH < eos;
+    }
+    // first slot of sequence s: bos_s / CH + s, strictly increasing in s; take
+    // the last sequence whose first slot is <= slot
+    int lo = 0, hi = a.N - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        int64_t mb, me, mr;
+        sequence_bounds(a.cu_seqlens, mid, a.T, mb, me, mr);
+        if (mb / CH + mid <= slot) lo = mid; else hi = mid - 1;
+    }
+    n = lo;
+    sequence_bounds(a.cu_seqlens, n, a.T, bos, eos, brow);
+    const int64_t first = bos / CH + n;
+    if (slot < first) return false;
+    m = int(slot - first);
+    return bos + int64_t(m) * CH < eos && slot_of(a, n, bos, m) == slot;
+}
+
+// The forward quantities of one chunk.  Rows are padded by one float: lanes
+// that walk different rows of the same column then fall in different banks.
 template <int DK>
 struct ChunkRows {
-    float Q[CH][DK];  // q, then Qt = q 2^G
-    float K[CH][DK];  // k, then Kb = k 2^(G_L - G)
-    float E[CH][DK];  // e = b k, then Et = e 2^G
-    float G[CH][DK];  // log2 alpha, then its running sum
+    float Q[CH][DK + 1];  // q, then Qt = q 2^G
+    float K[CH][DK + 1];  // k, then Kb = k 2^(G_L - G)
+    float E[CH][DK + 1];  // e = b k, then Et = e 2^G
+    float G[CH][DK + 1];  // log2 alpha, then its running sum
     float A[CH][CH + 1];
     float P[CH][CH + 1];
 };
 
-// Stage rows row0 + H * i (i < L) and form A, P and the absorbed factors.
+// ---------------------------------------------------------------------------
+// bwd_prep: everything of a chunk that does not involve the state.
 template <typename T, int DK>
-__device__ void chunk_prologue(ChunkRows<DK>& c, const BwdArgs& a, int64_t row0, int L, int tid)
+__global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdArgs a)
 {
+    __shared__ ChunkRows<DK> c;
+    __shared__ float Tm[CH][CH + 1];
+
+    const int tid = threadIdx.x;
+    int64_t idx = blockIdx.x;
+    const int h = int(idx % a.H);
+    idx /= a.H;
+    const int64_t slot = idx % a.slots, row = idx / a.slots;
+    int n, m;
+    int64_t bos, eos, brow;
+    if (!chunk_of_slot(a, row, slot, n, m, bos, eos, brow)) return;
+    const int64_t t0 = bos + int64_t(m) * CH;
+    const int L = int(eos - t0 < CH ? eos - t0 : CH);
+    const int64_t row0 = (brow * a.T + t0) * a.H + h;
     const T* q = static_cast<const T*>(a.q);
     const T* k = static_cast<const T*>(a.k);
     const T* b = static_cast<const T*>(a.b);
-    for (int idx = tid; idx < CH * DK; idx += kBwdThreads) {
-        const int i = idx / DK, ch = idx % DK;
+
+    for (int i2 = tid; i2 < CH * DK; i2 += kBwdThreads) {
+        const int i = i2 / DK, ch = i2 % DK;
         if (i < L) {
             const int64_t off = (row0 + int64_t(i) * a.H) * DK + ch;
             const float kk = load_as_f32(k, off);
@@ -85,10 +144,7 @@ __device__ void chunk_prologue(ChunkRows<DK>& c, const BwdArgs& a, int64_t row0,
             c.E[i][ch] = load_as_f32(b, off) * kk;
             c.G[i][ch] = log2_decay(a.alpha[off]);
         } else {
-            c.Q[i][ch] = 0.f;
-            c.K[i][ch] = 0.f;
-            c.E[i][ch] = 0.f;
-            c.G[i][ch] = 0.f;
+            c.Q[i][ch] = c.K[i][ch] = c.E[i][ch] = c.G[i][ch] = 0.f;
         }
     }
     __syncthreads();
@@ -100,8 +156,9 @@ __device__ void chunk_prologue(ChunkRows<DK>& c, const BwdArgs& a, int64_t row0,
         }
     }
     __syncthreads();
-    for (int idx = tid; idx < CH * CH; idx += kBwdThreads) {
-        const int i = idx / CH, j = idx % CH;
+    // A and P with every pairwise decay factor formed exactly (exponent <= 0)
+    for (int i2 = tid; i2 < CH * CH; i2 += kBwdThreads) {
+        const int i = i2 / CH, j = i2 % CH;
         float acc_a = 0.f, acc_p = 0.f;
         if (j <= i && i < L) {
             for (int ch = 0; ch < DK; ++ch) {
@@ -114,223 +171,315 @@ __device__ void chunk_prologue(ChunkRows<DK>& c, const BwdArgs& a, int64_t row0,
         c.P[i][j] = acc_p;
     }
     __syncthreads();
-    for (int idx = tid; idx < L * DK; idx += kBwdThreads) {
-        const int i = idx / DK, ch = idx % DK;
+    // Tm = (I + A)^-1 by columns (lane j owns column j; no lane reads another's)
+    if (tid < CH) {
+        const int j = tid;
+        for (int i = 0; i < CH; ++i) Tm[i][j] = i == j ? 1.f : 0.f;
+        for (int i = 1; i < L; ++i) {
+            float acc = 0.f;
+            for (int mm = 0; mm < i; ++mm) acc += c.A[i][mm] * Tm[mm][j];
+            if (j < i) Tm[i][j] = -acc;
+        }
+    }
+    // absorb the decay into the row and column factors
+    for (int i2 = tid; i2 < L * DK; i2 += kBwdThreads) {
+        const int i = i2 / DK, ch = i2 % DK;
         const float g = c.G[i][ch], up = exp2f(g);
         c.E[i][ch] *= up;
         c.Q[i][ch] *= up;
         c.K[i][ch] *= exp2f(c.G[L - 1][ch] - g);
     }
     __syncthreads();
+    float* dst = a.ws_prep + prep_base(a, row, slot, h);
+    for (int i2 = tid; i2 < CH * CH; i2 += kBwdThreads) {
+        const int i = i2 / CH, j = i2 % CH;
+        dst[kPrepT + i2] = Tm[i][j];
+        dst[kPrepP + i2] = c.P[i][j];
+    }
+    for (int i2 = tid; i2 < CH * DK; i2 += kBwdThreads) {
+        const int i = i2 / DK, ch = i2 % DK;
+        dst[kPrepE + i2] = c.E[i][ch];
+        dst[kPrepE + CH * DK + i2] = c.Q[i][ch];
+        dst[kPrepE + 2 * CH * DK + i2] = c.K[i][ch];
+    }
+    for (int ch = tid; ch < DK; ch += kBwdThreads) dst[kPrepE + 3 * CH * DK + ch] = exp2f(c.G[L - 1][ch]);
 }
 
-// X = Z - Et S into U, then U = (I + A)^-1 X (column-oriented forward substitution).
-template <typename T, int DK, int DVT>
-__device__ void chunk_solve(const ChunkRows<DK>& c, const float (*S)[DVT], float (*U)[DVT], const BwdArgs& a,
-                            int64_t row0, int L, int j0, int tid)
+// Thread layout of the sequential kernels: lane column jj = tid % 32 of the
+// tile; chunk rows i0 + 8 r (r < 4) and state rows c0 + 8 r (r < DK / 8), with
+// i0 = c0 = tid / 32.  The rows a wavefront reads at one time are two, so the
+// row operand is a broadcast and the column operand is contiguous.
+
+// Prepared rows of one chunk into LDS (rows past the chunk are zero in the block).
+template <int DK, bool kQ>
+__device__ __forceinline__ void load_prep(const float* src, float (*Et)[DK + 1], float (*Qt)[DK + 1],
+                                          float (*Kb)[DK + 1], float (*Tm)[CH + 1], float (*Pm)[CH + 1],
+                                          float* gam, int tid)
 {
-    const T* v = static_cast<const T*>(a.v);
-    const T* w = static_cast<const T*>(a.w);
-    for (int idx = tid; idx < L * DVT; idx += kBwdThreads) {
-        const int i = idx / DVT, jj = idx % DVT;
-        float acc = 0.f;
-        for (int ch = 0; ch < DK; ++ch) acc += c.E[i][ch] * S[ch][jj];
-        const int64_t off = (row0 + int64_t(i) * a.H) * a.dv_ + j0 + jj;
-        U[i][jj] = load_as_f32(w, off) * load_as_f32(v, off) - acc;
+    for (int i2 = tid; i2 < CH * CH; i2 += kBwdThreads) {
+        Tm[i2 / CH][i2 % CH] = src[kPrepT + i2];
+        if (kQ) Pm[i2 / CH][i2 % CH] = src[kPrepP + i2];
     }
-    __syncthreads();
-    for (int i = 0; i + 1 < L; ++i) {
-        for (int idx = tid; idx < (L - 1 - i) * DVT; idx += kBwdThreads) {
-            const int m = i + 1 + idx / DVT, jj = idx % DVT;
-            U[m][jj] -= c.A[m][i] * U[i][jj];
-        }
-        __syncthreads();
+    for (int i2 = tid; i2 < CH * DK; i2 += kBwdThreads) {
+        const int i = i2 / DK, ch = i2 % DK;
+        Et[i][ch] = src[kPrepE + i2];
+        if (kQ) Qt[i][ch] = src[kPrepE + CH * DK + i2];
+        Kb[i][ch] = src[kPrepE + 2 * CH * DK + i2];
     }
+    for (int ch = tid; ch < DK; ch += kBwdThreads) gam[ch] = src[kPrepE + 3 * CH * DK + ch];
 }
 
 // ---------------------------------------------------------------------------
 // bwd_states: the forward again, storing the state at every chunk start.
-template <typename T, int DK, int DVT>
+template <typename T, int DK>
 __global__ __launch_bounds__(kBwdThreads) void bwd_states_kernel(BwdArgs a)
 {
-    __shared__ ChunkRows<DK> c;
-    __shared__ float Ss[DK][DVT];
-    __shared__ float Us[CH][DVT];
+    constexpr int RS = DK / 8;  // state rows per thread
+    __shared__ float Et[CH][DK + 1], Kb[CH][DK + 1];
+    __shared__ float Tm[CH][CH + 1];
+    __shared__ float gam[DK];
+    __shared__ float Ss[DK][kTile];
+    __shared__ float Xs[CH][kTile], Us[CH][kTile];
 
     const int tid = threadIdx.x;
-    const int ntiles = a.dv_ / DVT;
+    const int jj = tid % kTile, i0 = tid / kTile;
+    const int ntiles = a.dv_ / kTile;
     const int chain = blockIdx.x / ntiles, tile = blockIdx.x % ntiles;
     const int n = chain / a.H, h = chain % a.H;
-    const int j0 = tile * DVT;
+    const int j0 = tile * kTile;
     const int64_t dv = a.dv_;
     int64_t bos, eos, brow;
     sequence_bounds(a.cu_seqlens, n, a.T, bos, eos, brow);
-    const int64_t s_off = (int64_t(n) * a.H + h) * DK * dv + j0;
+    const T* v = static_cast<const T*>(a.v);
+    const T* w = static_cast<const T*>(a.w);
 
-    for (int idx = tid; idx < DK * DVT; idx += kBwdThreads) {
-        const int ch = idx / DVT, jj = idx % DVT;
-        Ss[ch][jj] = a.initial_state ? a.initial_state[s_off + int64_t(ch) * dv + jj] : 0.f;
-    }
-    __syncthreads();
+    const int64_t s_off = (int64_t(n) * a.H + h) * DK * dv + j0 + jj;
+#pragma unroll
+    for (int r = 0; r < RS; ++r)
+        Ss[i0 + 8 * r][jj] = a.initial_state ? a.initial_state[s_off + int64_t(i0 + 8 * r) * dv] : 0.f;
+
     int m = 0;
     for (int64_t t0 = bos; t0 < eos; t0 += CH, ++m) {
         const int L = int(eos - t0 < CH ? eos - t0 : CH);
         const int64_t row0 = (brow * a.T + t0) * a.H + h;
-        float* dst = a.ws_states + slot_base(a, brow, slot_of(a, n, bos, m), h) + j0;
-        for (int idx = tid; idx < DK * DVT; idx += kBwdThreads) {
-            const int ch = idx / DVT, jj = idx % DVT;
-            dst[int64_t(ch) * dv + jj] = Ss[ch][jj];
-        }
-        chunk_prologue<T, DK>(c, a, row0, L, tid);
-        chunk_solve<T, DK, DVT>(c, Ss, Us, a, row0, L, j0, tid);
-        for (int idx = tid; idx < DK * DVT; idx += kBwdThreads) {
-            const int ch = idx / DVT, jj = idx % DVT;
-            float acc = exp2f(c.G[L - 1][ch]) * Ss[ch][jj];
-            for (int i = 0; i < L; ++i) acc += c.K[i][ch] * Us[i][jj];
-            Ss[ch][jj] = acc;
+        const int64_t slot = slot_of(a, n, bos, m);
+        float* dst = a.ws_states + slot_base(a, brow, slot, h) + j0 + jj;
+#pragma unroll
+        for (int r = 0; r < RS; ++r) dst[int64_t(i0 + 8 * r) * dv] = Ss[i0 + 8 * r][jj];
+        __syncthreads();  // the previous chunk is done with Et, Kb, Tm, Xs, Us and Ss
+        load_prep<DK, false>(a.ws_prep + prep_base(a, brow, slot, h), Et, nullptr, Kb, Tm, nullptr, gam, tid);
+        float z[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = i0 + 8 * r;
+            const int64_t off = (row0 + int64_t(i) * a.H) * dv + j0 + jj;
+            z[r] = i < L ? load_as_f32(w, off) * load_as_f32(v, off) : 0.f;
         }
         __syncthreads();
+        // X = Z - Et S
+        {
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+            for (int ch = 0; ch < DK; ++ch) {
+                const float sv = Ss[ch][jj];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] += Et[i0 + 8 * r][ch] * sv;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Xs[i0 + 8 * r][jj] = z[r] - acc[r];
+        }
+        __syncthreads();
+        // U = Tm X  (Tm is unit lower triangular; rows past the chunk give zero)
+        {
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+            for (int mm = 0; mm < CH; ++mm) {
+                const float xv = Xs[mm][jj];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] += Tm[i0 + 8 * r][mm] * xv;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Us[i0 + 8 * r][jj] = acc[r];
+        }
+        __syncthreads();
+        // S <- 2^G_L S + Kb^T U  (each thread its own elements)
+        {
+            float acc[RS];
+#pragma unroll
+            for (int r = 0; r < RS; ++r) acc[r] = gam[i0 + 8 * r] * Ss[i0 + 8 * r][jj];
+            for (int i = 0; i < L; ++i) {
+                const float uv = Us[i][jj];
+#pragma unroll
+                for (int r = 0; r < RS; ++r) acc[r] += Kb[i][i0 + 8 * r] * uv;
+            }
+#pragma unroll
+            for (int r = 0; r < RS; ++r) Ss[i0 + 8 * r][jj] = acc[r];
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
 // bwd_dstate: chunks in reverse, carrying the state gradient.
-template <typename T, int DK, int DVT>
+template <typename T, int DK>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dstate_kernel(BwdArgs a)
 {
-    __shared__ ChunkRows<DK> c;
-    __shared__ float Ss[DK][DVT];   // chunk-start state
-    __shared__ float dSs[DK][DVT];  // gradient of the chunk-end state, then of its start
-    __shared__ float Us[CH][DVT];
-    __shared__ float dXs[CH][DVT];  // dU, then dX
-    __shared__ float dOs[CH][DVT];
+    constexpr int RS = DK / 8;
+    __shared__ float Et[CH][DK + 1], Qt[CH][DK + 1], Kb[CH][DK + 1];
+    __shared__ float Tm[CH][CH + 1], Pm[CH][CH + 1];
+    __shared__ float gam[DK];
+    __shared__ float Ss[DK][kTile];    // chunk-start state
+    __shared__ float dSs[DK][kTile];   // gradient of the chunk-end state, then of its start
+    __shared__ float Xs[CH][kTile], dUs[CH][kTile], dOs[CH][kTile], Us[CH][kTile], dXs[CH][kTile];
 
     const int tid = threadIdx.x;
-    const int ntiles = a.dv_ / DVT;
+    const int jj = tid % kTile, i0 = tid / kTile;
+    const int ntiles = a.dv_ / kTile;
     const int chain = blockIdx.x / ntiles, tile = blockIdx.x % ntiles;
     const int n = chain / a.H, h = chain % a.H;
-    const int j0 = tile * DVT;
+    const int j0 = tile * kTile;
     const int64_t dv = a.dv_;
     int64_t bos, eos, brow;
     sequence_bounds(a.cu_seqlens, n, a.T, bos, eos, brow);
-    const int64_t s_off = (int64_t(n) * a.H + h) * DK * dv + j0;
     const T* dO = static_cast<const T*>(a.d_o);
     const T* v = static_cast<const T*>(a.v);
     const T* w = static_cast<const T*>(a.w);
     T* dv_out = static_cast<T*>(a.dv);
     T* dw_out = static_cast<T*>(a.dw);
 
-    for (int idx = tid; idx < DK * DVT; idx += kBwdThreads) {
-        const int ch = idx / DVT, jj = idx % DVT;
-        dSs[ch][jj] = a.d_final_state ? a.d_final_state[s_off + int64_t(ch) * dv + jj] : 0.f;
-    }
-    __syncthreads();
+    const int64_t s_off = (int64_t(n) * a.H + h) * DK * dv + j0 + jj;
+#pragma unroll
+    for (int r = 0; r < RS; ++r)
+        dSs[i0 + 8 * r][jj] = a.d_final_state ? a.d_final_state[s_off + int64_t(i0 + 8 * r) * dv] : 0.f;
+
     const int M = int((eos - bos + CH - 1) / CH);
     for (int m = M - 1; m >= 0; --m) {
         const int64_t t0 = bos + int64_t(m) * CH;
         const int L = int(eos - t0 < CH ? eos - t0 : CH);
         const int64_t row0 = (brow * a.T + t0) * a.H + h;
-        const int64_t sb = slot_base(a, brow, slot_of(a, n, bos, m), h) + j0;
-        for (int idx = tid; idx < DK * DVT; idx += kBwdThreads) {
-            const int ch = idx / DVT, jj = idx % DVT;
-            a.ws_dstates[sb + int64_t(ch) * dv + jj] = dSs[ch][jj];
-            Ss[ch][jj] = a.ws_states[sb + int64_t(ch) * dv + jj];
+        const int64_t slot = slot_of(a, n, bos, m);
+        const int64_t sb = slot_base(a, brow, slot, h) + j0 + jj;
+#pragma unroll
+        for (int r = 0; r < RS; ++r) {
+            a.ws_dstates[sb + int64_t(i0 + 8 * r) * dv] = dSs[i0 + 8 * r][jj];
+            Ss[i0 + 8 * r][jj] = a.ws_states[sb + int64_t(i0 + 8 * r) * dv];
         }
-        for (int idx = tid; idx < CH * DVT; idx += kBwdThreads) {
-            const int i = idx / DVT, jj = idx % DVT;
-            dOs[i][jj] = i < L ? load_as_f32(dO, (row0 + int64_t(i) * a.H) * dv + j0 + jj) : 0.f;
-        }
-        chunk_prologue<T, DK>(c, a, row0, L, tid);  // begins and ends with a barrier
-        chunk_solve<T, DK, DVT>(c, Ss, Us, a, row0, L, j0, tid);
-        // dU = Kb dS' + P^T dO
-        for (int idx = tid; idx < L * DVT; idx += kBwdThreads) {
-            const int i = idx / DVT, jj = idx % DVT;
-            float acc = 0.f;
-            for (int ch = 0; ch < DK; ++ch) acc += c.K[i][ch] * dSs[ch][jj];
-            for (int r = i; r < L; ++r) acc += c.P[r][i] * dOs[r][jj];
-            dXs[i][jj] = acc;
-        }
-        __syncthreads();
-        // dX = (I + A)^-T dU: backward substitution, row i final once rows > i are done
-        for (int i = L - 1; i >= 1; --i) {
-            for (int idx = tid; idx < i * DVT; idx += kBwdThreads) {
-                const int r = idx / DVT, jj = idx % DVT;
-                dXs[r][jj] -= c.A[i][r] * dXs[i][jj];
-            }
-            __syncthreads();
-        }
-        for (int idx = tid; idx < L * DVT; idx += kBwdThreads) {
-            const int i = idx / DVT, jj = idx % DVT;
+        __syncthreads();  // the previous chunk is done with the prepared rows and the row buffers
+        load_prep<DK, true>(a.ws_prep + prep_base(a, brow, slot, h), Et, Qt, Kb, Tm, Pm, gam, tid);
+        float z[4], vv[4], ww[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = i0 + 8 * r;
+            const bool live = i < L;
             const int64_t off = (row0 + int64_t(i) * a.H) * dv + j0 + jj;
-            const float dx = dXs[i][jj];
-            a.ws_u[off] = Us[i][jj];
-            a.ws_dx[off] = dx;
-            store_from_f32(dw_out, off, dx * load_as_f32(v, off));
-            store_from_f32(dv_out, off, dx * load_as_f32(w, off));
-        }
-        // dS = 2^G_L dS' + Qt^T dO - Et^T dX (each element read and written by one thread)
-        for (int idx = tid; idx < DK * DVT; idx += kBwdThreads) {
-            const int ch = idx / DVT, jj = idx % DVT;
-            float acc = exp2f(c.G[L - 1][ch]) * dSs[ch][jj];
-            for (int i = 0; i < L; ++i) acc += c.Q[i][ch] * dOs[i][jj] - c.E[i][ch] * dXs[i][jj];
-            dSs[ch][jj] = acc;
+            vv[r] = live ? load_as_f32(v, off) : 0.f;
+            ww[r] = live ? load_as_f32(w, off) : 0.f;
+            z[r] = ww[r] * vv[r];
+            dOs[i][jj] = live ? load_as_f32(dO, off) : 0.f;
         }
         __syncthreads();
+        // X = Z - Et S and dU = Kb dS' + Pm^T dO
+        {
+            float ax[4] = {0.f, 0.f, 0.f, 0.f}, au[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+            for (int ch = 0; ch < DK; ++ch) {
+                const float sv = Ss[ch][jj], dsv = dSs[ch][jj];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    ax[r] += Et[i0 + 8 * r][ch] * sv;
+                    au[r] += Kb[i0 + 8 * r][ch] * dsv;
+                }
+            }
+#pragma unroll 4
+            for (int rr = 0; rr < CH; ++rr) {  // Pm is lower triangular: only rr >= i contributes
+                const float ov = dOs[rr][jj];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) au[r] += Pm[rr][i0 + 8 * r] * ov;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                Xs[i0 + 8 * r][jj] = z[r] - ax[r];
+                dUs[i0 + 8 * r][jj] = au[r];
+            }
+        }
+        __syncthreads();
+        // U = Tm X,  dX = Tm^T dU
+        {
+            float au[4] = {0.f, 0.f, 0.f, 0.f}, ad[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+            for (int mm = 0; mm < CH; ++mm) {
+                const float xv = Xs[mm][jj], dv_ = dUs[mm][jj];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    au[r] += Tm[i0 + 8 * r][mm] * xv;
+                    ad[r] += Tm[mm][i0 + 8 * r] * dv_;
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = i0 + 8 * r;
+                Us[i][jj] = au[r];
+                dXs[i][jj] = i < L ? ad[r] : 0.f;
+                if (i < L) {
+                    const int64_t off = (row0 + int64_t(i) * a.H) * dv + j0 + jj;
+                    a.ws_u[off] = au[r];
+                    a.ws_dx[off] = ad[r];
+                    store_from_f32(dw_out, off, ad[r] * vv[r]);
+                    store_from_f32(dv_out, off, ad[r] * ww[r]);
+                }
+            }
+        }
+        __syncthreads();
+        // dS = 2^G_L dS' + Qt^T dO - Et^T dX  (each thread its own elements)
+        {
+            float acc[RS];
+#pragma unroll
+            for (int r = 0; r < RS; ++r) acc[r] = gam[i0 + 8 * r] * dSs[i0 + 8 * r][jj];
+            for (int i = 0; i < L; ++i) {
+                const float ov = dOs[i][jj], xv = dXs[i][jj];
+#pragma unroll
+                for (int r = 0; r < RS; ++r) acc[r] += Qt[i][i0 + 8 * r] * ov - Et[i][i0 + 8 * r] * xv;
+            }
+#pragma unroll
+            for (int r = 0; r < RS; ++r) dSs[i0 + 8 * r][jj] = acc[r];
+        }
     }
     if (a.d_initial_state)
-        for (int idx = tid; idx < DK * DVT; idx += kBwdThreads) {
-            const int ch = idx / DVT, jj = idx % DVT;
-            a.d_initial_state[s_off + int64_t(ch) * dv + jj] = dSs[ch][jj];
-        }
+#pragma unroll
+        for (int r = 0; r < RS; ++r) a.d_initial_state[s_off + int64_t(i0 + 8 * r) * dv] = dSs[i0 + 8 * r][jj];
 }
 
 // ---------------------------------------------------------------------------
-// bwd_keys: one chunk of one head, channels c0 .. c0 + CB - 1.
-template <typename T, int DK, int DV, int CB>
+// bwd_keys: one chunk of one head, channels c0 .. c0 + 31.  Thread layout:
+// column (token j or channel cc) = tid % 32, rows i0 + 8 r with i0 = tid / 32.
+template <typename T, int DK, int DV>
 __global__ __launch_bounds__(kBwdThreads) void bwd_keys_kernel(BwdArgs a)
 {
-    __shared__ float Us[CH][DV], dXs[CH][DV], dOs[CH][DV];
-    __shared__ float Sb[CB][DV], dSb[CB][DV];   // rows c0.. of the chunk-start state and end gradient
+    constexpr int CB = 32;                // channels per block
+    constexpr int DH = DV < 64 ? DV : 64; // value columns per pass
+    static_assert(DK % CB == 0 && DV % DH == 0 && DH >= CB, "block shapes");
+    // per pass: U, dX, dO rows and the block's S and dS' rows; afterwards dg and Kb dKb
+    __shared__ float buf[5][CH][DH + 1];
     __shared__ float dA[CH][CH + 1], dP[CH][CH + 1];
-    __shared__ float qb[CH][CB], kb[CH][CB], eb[CH][CB], bb[CH][CB], ab[CH][CB], Gb[CH][CB];
-    __shared__ float dEt[CH][CB], dQt[CH][CB], dKb[CH][CB], dg[CH][CB];
+    __shared__ float qb[CH][CB + 1], kb[CH][CB + 1], eb[CH][CB + 1], bb[CH][CB + 1], ab[CH][CB + 1], Gb[CH][CB + 1];
     __shared__ float rs[CB];
+    float (*Us)[DH + 1] = buf[0];
+    float (*dXs)[DH + 1] = buf[1];
+    float (*dOs)[DH + 1] = buf[2];
+    float (*Sb)[DH + 1] = buf[3];
+    float (*dSb)[DH + 1] = buf[4];
 
     const int tid = threadIdx.x;
+    const int col = tid % 32, i0 = tid / 32;
     constexpr int nblk = DK / CB;
     int64_t idx = blockIdx.x;
     const int cblk = int(idx % nblk);
     idx /= nblk;
     const int h = int(idx % a.H);
     idx /= a.H;
-    const int64_t slot = idx % a.slots;
-    const int64_t row = idx / a.slots;
-
-    // which chunk of which sequence owns this slot
+    const int64_t slot = idx % a.slots, row = idx / a.slots;
     int n, m;
     int64_t bos, eos, brow;
-    if (!a.cu_seqlens) {
-        n = int(row);
-        m = int(slot);
-        sequence_bounds(nullptr, n, a.T, bos, eos, brow);
-        if (int64_t(m) * CH >= eos) return;
-    } else {
-        // first slot of sequence s: bos_s / CH + s, strictly increasing in s;
-        // take the last sequence whose first slot is <= slot
-        int lo = 0, hi = a.N - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) / 2;
-            int64_t mb, me, mr;
-            sequence_bounds(a.cu_seqlens, mid, a.T, mb, me, mr);
-            if (mb / CH + mid <= slot) lo = mid; else hi = mid - 1;
-        }
-        n = lo;
-        sequence_bounds(a.cu_seqlens, n, a.T, bos, eos, brow);
-        const int64_t first = bos / CH + n;
-        if (slot < first) return;
-        m = int(slot - first);
-        if (bos + int64_t(m) * CH >= eos || slot_of(a, n, bos, m) != slot) return;
-    }
+    if (!chunk_of_slot(a, row, slot, n, m, bos, eos, brow)) return;
     const int64_t t0 = bos + int64_t(m) * CH;
     const int L = int(eos - t0 < CH ? eos - t0 : CH);
     const int64_t row0 = (brow * a.T + t0) * a.H + h;
@@ -341,100 +490,105 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_keys_kernel(BwdArgs a)
     const T* b = static_cast<const T*>(a.b);
     const T* dO = static_cast<const T*>(a.d_o);
 
-    for (int i2 = tid; i2 < CH * DV; i2 += kBwdThreads) {
-        const int i = i2 / DV, j = i2 % DV;
-        const bool live = i < L;
-        const int64_t off = (row0 + int64_t(i) * a.H) * DV + j;
-        Us[i][j] = live ? a.ws_u[off] : 0.f;
-        dXs[i][j] = live ? a.ws_dx[off] : 0.f;
-        dOs[i][j] = live ? load_as_f32(dO, off) : 0.f;
-    }
-    for (int i2 = tid; i2 < CB * DV; i2 += kBwdThreads) {
-        const int cc = i2 / DV, j = i2 % DV;
-        const int64_t off = sbase + int64_t(c0 + cc) * DV + j;
-        Sb[cc][j] = a.ws_states[off];
-        dSb[cc][j] = a.ws_dstates[off];
-    }
-    for (int i2 = tid; i2 < CH * CB; i2 += kBwdThreads) {
-        const int i = i2 / CB, cc = i2 % CB;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {  // the block's token inputs, thread (i0 + 8 r, col)
+        const int i = i0 + 8 * r;
         if (i < L) {
-            const int64_t off = (row0 + int64_t(i) * a.H) * DK + c0 + cc;
+            const int64_t off = (row0 + int64_t(i) * a.H) * DK + c0 + col;
             const float kk = load_as_f32(k, off), bv = load_as_f32(b, off);
-            qb[i][cc] = load_as_f32(q, off);
-            kb[i][cc] = kk;
-            bb[i][cc] = bv;
-            eb[i][cc] = bv * kk;
-            ab[i][cc] = a.alpha[off];
-            Gb[i][cc] = log2_decay(a.alpha[off]);
+            qb[i][col] = load_as_f32(q, off);
+            kb[i][col] = kk;
+            bb[i][col] = bv;
+            eb[i][col] = bv * kk;
+            ab[i][col] = a.alpha[off];
+            Gb[i][col] = log2_decay(a.alpha[off]);
         } else {
-            qb[i][cc] = kb[i][cc] = bb[i][cc] = eb[i][cc] = Gb[i][cc] = 0.f;
-            ab[i][cc] = 1.f;
+            qb[i][col] = kb[i][col] = bb[i][col] = eb[i][col] = Gb[i][col] = 0.f;
+            ab[i][col] = 1.f;
         }
     }
-    __syncthreads();
-    for (int cc = tid; cc < CB; cc += kBwdThreads) {
+
+    // dA, dP (row i, column j = col) and dEt, dQt, dKb (row i, channel col), over all value columns
+    float xa[4] = {0.f, 0.f, 0.f, 0.f}, xp[4] = {0.f, 0.f, 0.f, 0.f};
+    float xe[4] = {0.f, 0.f, 0.f, 0.f}, xq[4] = {0.f, 0.f, 0.f, 0.f}, xk[4] = {0.f, 0.f, 0.f, 0.f};
+    float xr = 0.f;
+    for (int jh = 0; jh < DV; jh += DH) {
+        for (int i2 = tid; i2 < CH * DH; i2 += kBwdThreads) {
+            const int i = i2 / DH, j = i2 % DH;
+            const bool live = i < L;
+            const int64_t off = (row0 + int64_t(i) * a.H) * DV + jh + j;
+            Us[i][j] = live ? a.ws_u[off] : 0.f;
+            dXs[i][j] = live ? a.ws_dx[off] : 0.f;
+            dOs[i][j] = live ? load_as_f32(dO, off) : 0.f;
+            const int64_t soff = sbase + int64_t(c0 + i) * DV + jh + j;  // i doubles as the channel (CB == CH)
+            Sb[i][j] = a.ws_states[soff];
+            dSb[i][j] = a.ws_dstates[soff];
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int j = 0; j < DH; ++j) {
+            const float uc = Us[col][j], sc = Sb[col][j], dsc = dSb[col][j];
+            if (i0 == 0) xr += dsc * sc;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = i0 + 8 * r;
+                const float dx = dXs[i][j], dov = dOs[i][j];
+                xa[r] += dx * uc;
+                xp[r] += dov * uc;
+                xe[r] += dx * sc;
+                xq[r] += dov * sc;
+                xk[r] += Us[i][j] * dsc;
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int i = i0 + 8 * r, j = col;
+        dA[i][j] = j < i ? -xa[r] : 0.f;
+        dP[i][j] = j <= i ? xp[r] : 0.f;
+    }
+    if (i0 == 0) rs[col] = xr;
+    for (int cc = tid; cc < CB; cc += kBwdThreads) {  // running sums of the block's decay
         float g = 0.f;
         for (int i = 0; i < L; ++i) {
             g += Gb[i][cc];
             Gb[i][cc] = g;
         }
     }
-    // dA = -strict_lower(dX U^T), dP = lower(dO U^T) over every value column
-    for (int i2 = tid; i2 < CH * CH; i2 += kBwdThreads) {
-        const int i = i2 / CH, j = i2 % CH;
-        float xa = 0.f, xp = 0.f;
-        if (j <= i && i < L)
-            for (int jj = 0; jj < DV; ++jj) {
-                xa += dXs[i][jj] * Us[j][jj];
-                xp += dOs[i][jj] * Us[j][jj];
-            }
-        dA[i][j] = j < i ? -xa : 0.f;
-        dP[i][j] = j <= i ? xp : 0.f;
-    }
-    // dEt = -dX S^T, dQt = dO S^T, dKb = U dS'^T (this block's channels)
-    for (int i2 = tid; i2 < CH * CB; i2 += kBwdThreads) {
-        const int i = i2 / CB, cc = i2 % CB;
-        float xe = 0.f, xq = 0.f, xk = 0.f;
-        if (i < L)
-            for (int jj = 0; jj < DV; ++jj) {
-                xe += dXs[i][jj] * Sb[cc][jj];
-                xq += dOs[i][jj] * Sb[cc][jj];
-                xk += Us[i][jj] * dSb[cc][jj];
-            }
-        dEt[i][cc] = -xe;
-        dQt[i][cc] = xq;
-        dKb[i][cc] = xk;
-    }
-    for (int cc = tid; cc < CB; cc += kBwdThreads) {
-        float acc = 0.f;
-        for (int jj = 0; jj < DV; ++jj) acc += dSb[cc][jj] * Sb[cc][jj];
-        rs[cc] = acc;
-    }
     __syncthreads();
 
+    // pairwise and absorbed-factor gradients, thread (i0 + 8 r, channel col)
+    float (*dg)[DH + 1] = buf[0];
+    float (*kbd)[DH + 1] = buf[1];
     T* dq_out = static_cast<T*>(a.dq);
     T* dk_out = static_cast<T*>(a.dk);
     T* db_out = static_cast<T*>(a.db);
-    for (int i2 = tid; i2 < L * CB; i2 += kBwdThreads) {
-        const int i = i2 / CB, cc = i2 % CB;
+    const int cc = col;
+    const float gl = Gb[L - 1][cc];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int i = i0 + 8 * r;
+        if (i >= L) continue;
         const float gi = Gb[i][cc];
         float de_a = 0.f, dq_p = 0.f, dk_ap = 0.f;
         for (int j = 0; j <= i; ++j) {
             const float kf = kb[j][cc] * exp2f(gi - Gb[j][cc]);
-            if (j < i) de_a += dA[i][j] * kf;
+            de_a += dA[i][j] * kf;  // dA is zero on the diagonal
             dq_p += dP[i][j] * kf;
         }
-        for (int r = i; r < L; ++r) {
-            const float f = exp2f(Gb[r][cc] - gi);
-            if (r > i) dk_ap += dA[r][i] * eb[r][cc] * f;
-            dk_ap += dP[r][i] * qb[r][cc] * f;
+        for (int rr = i; rr < L; ++rr) {
+            const float f = exp2f(Gb[rr][cc] - gi);
+            dk_ap += (dA[rr][i] * eb[rr][cc] + dP[rr][i] * qb[rr][cc]) * f;
         }
-        const float up = exp2f(gi), down = exp2f(Gb[L - 1][cc] - gi);
-        const float de = de_a + dEt[i][cc] * up;
-        const float dq = dq_p + dQt[i][cc] * up;
-        const float dkk = dk_ap + dKb[i][cc] * down;
-        dg[i][cc] = eb[i][cc] * de_a + qb[i][cc] * dq_p - kb[i][cc] * dk_ap
-                    + eb[i][cc] * up * dEt[i][cc] + qb[i][cc] * up * dQt[i][cc] - kb[i][cc] * down * dKb[i][cc];
+        const float up = exp2f(gi), down = exp2f(gl - gi);
+        const float dEt = -xe[r], dQt = xq[r], dKb = xk[r];
+        const float de = de_a + dEt * up;
+        const float dq = dq_p + dQt * up;
+        const float dkk = dk_ap + dKb * down;
+        dg[i][cc] = eb[i][cc] * de_a + qb[i][cc] * dq_p - kb[i][cc] * dk_ap + eb[i][cc] * up * dEt
+                    + qb[i][cc] * up * dQt - kb[i][cc] * down * dKb;
+        kbd[i][cc] = kb[i][cc] * down * dKb;
         const int64_t off = (row0 + int64_t(i) * a.H) * DK + c0 + cc;
         store_from_f32(dq_out, off, dq);
         store_from_f32(db_out, off, de * kb[i][cc]);
@@ -442,10 +596,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_keys_kernel(BwdArgs a)
     }
     __syncthreads();
     // the chunk-end terms, then the reverse running sum over the chunk's tokens
-    for (int cc = tid; cc < CB; cc += kBwdThreads) {
-        const float gl = Gb[L - 1][cc];
+    if (tid < CB) {
         float acc = exp2f(gl) * rs[cc];
-        for (int j = 0; j < L; ++j) acc += kb[j][cc] * exp2f(gl - Gb[j][cc]) * dKb[j][cc];
+        for (int j = 0; j < L; ++j) acc += kbd[j][cc];
         for (int i = L - 1; i >= 0; --i) {
             acc += dg[i][cc];
             const float al = ab[i][cc];
@@ -457,34 +610,39 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_keys_kernel(BwdArgs a)
     }
 }
 
-template <typename T, int DK, int DVT>
-hipError_t launch_chain_kernels(const BwdArgs& a, hipStream_t stream)
+template <typename T, int DK>
+hipError_t launch_chain(const BwdArgs& a, hipStream_t stream)
 {
-    const int64_t blocks = int64_t(a.N) * a.H * (a.dv_ / DVT);
-    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_states_kernel<T, DK, DVT>), dim3(unsigned(blocks)), dim3(kBwdThreads), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dstate_kernel<T, DK, DVT>), dim3(unsigned(blocks)), dim3(kBwdThreads), 0, stream, a);
+    const int64_t chains = int64_t(a.N) * a.H * (a.dv_ / kTile);
+    const int64_t chunks = int64_t(a.B) * a.slots * a.H;
+    if (chains > 0x7fffffff || chunks * (DK / 32) > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (chunks > 0) {
+        hipLaunchKernelGGL((bwd_prep_kernel<T, DK>), dim3(unsigned(chunks)), dim3(kBwdThreads), 0, stream, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((bwd_states_kernel<T, DK>), dim3(unsigned(chains)), dim3(kBwdThreads), 0, stream, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    // runs for T = 0 as well: it passes the final-state gradient through
+    hipLaunchKernelGGL((bwd_dstate_kernel<T, DK>), dim3(unsigned(chains)), dim3(kBwdThreads), 0, stream, a);
     return hipGetLastError();
 }
 
 template <typename T, int DK, int DV>
 hipError_t launch_keys(const BwdArgs& a, hipStream_t stream)
 {
-    constexpr int CB = DK < 32 ? DK : 32;
-    const int64_t blocks = int64_t(a.B) * a.slots * a.H * (DK / CB);
-    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const int64_t blocks = int64_t(a.B) * a.slots * a.H * (DK / 32);
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_keys_kernel<T, DK, DV, CB>), dim3(unsigned(blocks)), dim3(kBwdThreads), 0, stream, a);
+    hipLaunchKernelGGL((bwd_keys_kernel<T, DK, DV>), dim3(unsigned(blocks)), dim3(kBwdThreads), 0, stream, a);
     return hipGetLastError();
 }
 
 template <typename T, int DK>
 hipError_t launch_dk(const BwdArgs& a, hipStream_t stream)
 {
-    if (a.dv_ % 32 != 0) return hipErrorInvalidValue;
-    hipError_t e = launch_chain_kernels<T, DK, 32>(a, stream);
+    if (a.dv_ % kTile != 0) return hipErrorInvalidValue;
+    hipError_t e = launch_chain<T, DK>(a, stream);
     if (e != hipSuccess) return e;
     switch (a.dv_) {
         case 32: return launch_keys<T, DK, 32>(a, stream);
@@ -506,6 +664,8 @@ hipError_t launch_typed(const BwdArgs& a, hipStream_t stream)
 }
 
 }  // namespace
+
+int64_t chunk_bwd_prep_floats(int dk) { return prep_floats(dk); }
 
 hipError_t launch_chunk_bwd(const BwdArgs& a, bool bf16, hipStream_t stream)
 {

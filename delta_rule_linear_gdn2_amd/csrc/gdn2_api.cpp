@@ -170,10 +170,11 @@ gdn2_status recurrent(const void* q, const void* k, const void* v, const float* 
 
 // Workspace regions of the backward pass: chunk-start states, chunk-end
 // state gradients (slots x H x dk x dv FP32 each, per batch row), U and dX
-// rows (B x T x H x dv FP32 each), each region 256-byte aligned.
+// rows (B x T x H x dv FP32 each) and each chunk's prepared triangular
+// algebra (slots x H per batch row), each region 256-byte aligned.
 struct BwdWorkspace {
     int64_t slots;
-    size_t states, rows, total;
+    size_t states, rows, prep, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -184,7 +185,8 @@ BwdWorkspace bwd_workspace(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t 
     w.slots = T == 0 ? 0 : (int64_t(T) + gdn2::kBwdChunk - 1) / gdn2::kBwdChunk + (varlen ? N : 0);
     w.states = align256(size_t(B) * size_t(w.slots) * size_t(H) * size_t(dk) * size_t(dv) * 4);
     w.rows = align256(size_t(B) * size_t(T) * size_t(H) * size_t(dv) * 4);
-    w.total = 2 * w.states + 2 * w.rows;
+    w.prep = align256(size_t(B) * size_t(w.slots) * size_t(H) * size_t(gdn2::chunk_bwd_prep_floats(dk)) * 4);
+    w.total = 2 * w.states + 2 * w.rows + w.prep;
     return w;
 }
 
@@ -245,6 +247,7 @@ gdn2_status chunk_bwd(const void* q, const void* k, const void* v, const float* 
     a.ws_dstates = ws.total ? reinterpret_cast<float*>(base + ws.states) : nullptr;
     a.ws_u = ws.total ? reinterpret_cast<float*>(base + 2 * ws.states) : nullptr;
     a.ws_dx = ws.total ? reinterpret_cast<float*>(base + 2 * ws.states + ws.rows) : nullptr;
+    a.ws_prep = ws.total ? reinterpret_cast<float*>(base + 2 * ws.states + 2 * ws.rows) : nullptr;
     const hipError_t e = gdn2::launch_chunk_bwd(a, dtype == GDN2_DTYPE_BF16, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }

@@ -69,7 +69,11 @@ struct BwdArgs {
     float* ws_dstates;   // [B][slots][H][dk][dv] gradient of the state at each chunk end
     float* ws_u;         // [B * T * H][dv] U rows
     float* ws_dx;        // [B * T * H][dv] dX rows
+    float* ws_prep;      // [B][slots][H][chunk_bwd_prep_floats(dk)] per-chunk triangular algebra
 };
+
+// Floats of one chunk's prepared block in ws_prep.
+int64_t chunk_bwd_prep_floats(int dk);
 
 // Each returns hipSuccess or the launch error; bf16 selects the input dtype.
 hipError_t launch_chunk_bwd(const BwdArgs& a, bool bf16, hipStream_t stream);

@@ -231,9 +231,11 @@ gdn2_status gdn2_chunk_bwd(const void* q, const void* k, const void* v,
                            int32_t num_seqs, gdn2_dtype dtype,
                            void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace needed by gdn2_chunk_bwd: 2 x B x (ceil(T / 32) + num_seqs) x H x
- * dk x dv x 4 bytes of states plus 2 x B x T x H x dv x 4 bytes of rows (0 when
- * T = 0).  Returns 0 for invalid sizes. */
+/* Workspace needed by gdn2_chunk_bwd.  With C = B x (ceil(T / 32) + num_seqs)
+ * x H chunk slots: 2 x C x dk x dv x 4 bytes of states, 2 x B x T x H x dv x 4
+ * bytes of rows and C x (2048 + 97 dk) x 4 bytes of per-chunk triangular
+ * algebra, each rounded up to 256 bytes (0 when T = 0).  Returns 0 for
+ * invalid sizes. */
 size_t gdn2_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t dk_size, int32_t dv_size,
                                       int32_t num_seqs, gdn2_dtype dtype);
 

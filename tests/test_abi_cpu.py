@@ -225,13 +225,17 @@ def bwd_call(lib, **kw):
                               a["ws"], a["ws_bytes"], None)
 
 
+def _bwd_ws(B, T, H, dk, dv, slots):
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    prep = 2 * 32 * 32 + 3 * 32 * dk + dk  # Tm, Pm, Et, Qt, Kb, 2^G_L per chunk
+    return (2 * al(B * slots * H * dk * dv * 4) + 2 * al(B * T * H * dv * 4) + al(B * slots * H * prep * 4))
+
+
 def test_bwd_workspace_query(lib):
-    # 2 x B x ceil(T/32) x H x dk x dv x 4 + 2 x B x T x H x dv x 4
-    assert binding.gdn2_chunk_bwd_workspace_bytes(8, 4096, 16, 128, 128, 0, 1) == \
-        2 * 8 * 128 * 16 * 128 * 128 * 4 + 2 * 8 * 4096 * 16 * 128 * 4
+    # states and state gradients per chunk slot, U and dX rows, prepared chunk algebra
+    assert binding.gdn2_chunk_bwd_workspace_bytes(8, 4096, 16, 128, 128, 0, 1) == _bwd_ws(8, 4096, 16, 128, 128, 128)
     assert binding.gdn2_chunk_bwd_workspace_bytes(1, 0, 4, 64, 64, 3, 1) == 0
-    assert binding.gdn2_chunk_bwd_workspace_bytes(1, 100, 2, 32, 32, 3, 0) == \
-        2 * (4 + 3) * 2 * 32 * 32 * 4 + 2 * 100 * 2 * 32 * 4
+    assert binding.gdn2_chunk_bwd_workspace_bytes(1, 100, 2, 32, 32, 3, 0) == _bwd_ws(1, 100, 2, 32, 32, 4 + 3)
     assert binding.gdn2_chunk_bwd_workspace_bytes(0, 100, 2, 32, 32, 0, 0) == 0
 
 
