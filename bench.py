@@ -28,6 +28,9 @@ if ROOT not in sys.path:
 METRIC = "GDN-2 fwd tokens/s (H16,d128,T4K,B8) + decode state GB/s; % of roofline"
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak
+# FP32 vector ALU without packed FP32 (which this build leaves off): 256 CUs x
+# 4 SIMDs x 16 lanes x 2 flops (FMA) x 2.4 GHz
+FP32_VALU_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 NAMES = ("q", "k", "v", "alpha", "b", "w")
 
 
@@ -59,6 +62,29 @@ def chunk_flops(lengths, H, dk, dv, C=64):
         for L, cnt in ((C, full), (tail, 1 if tail else 0)):
             per = (dk * L * (L - 1) + dk * L * (L + 1) + L ** 3 / 3 + (dk + dv) * L * (L + 1)
                    + 3 * 2 * L * dk * dv + dv * L * (L + 1))
+            total += cnt * per
+    return total * H
+
+
+def bwd_bytes(B, T, H, dk, dv, N, eb=2):
+    """Algorithmic HBM bytes of one backward call: q, k, b, v, w, d_o read and
+    dq, dk, db, dv, dw written in the input dtype, alpha read and dalpha
+    written in FP32, the initial state and the final-state seed read and the
+    initial-state gradient written in FP32 (workspace traffic not counted)."""
+    tok = B * T * H
+    return tok * (6 * dk * eb + 5 * dv * eb + 2 * dk * 4) + 3 * N * H * dk * dv * 4
+
+
+def bwd_flops(lengths, H, dk, dv, C=32):
+    """FLOPs of the chunkwise backward as built (32-token chunks), summed over
+    chunks: the forward recompute (X, U = Tm X, the state update), the reverse
+    pass (X, U, dU, dX, the state-gradient update), the key-side products
+    (dA, dP, dEt, dQt, dKb) and the per-chunk algebra (A, P, Tm, pairwise)."""
+    total = 0
+    for n in lengths:
+        full, tail = divmod(int(n), C)
+        for L, cnt in ((C, full), (tail, 1 if tail else 0)):
+            per = (18 * L * dk * dv + 5 * L * L * dv + 5 * L * L * dk + L ** 3 / 3 + 2 * dk * dv)
             total += cnt * per
     return total * H
 
@@ -201,11 +227,47 @@ def cpu_baseline(x, wl, chains_rows=4):
                       f"{wall:.1f} s wall"}
 
 
+def bench_bwd(args):
+    """The gate-aware backward pass on batched_bf16 (B=8, T=4096, H=16, d=128):
+    median HIP-event time per call, with a final-state seed and the
+    initial-state gradient."""
+    import torch
+
+    from delta_rule_linear_gdn2_amd import binding
+    from delta_rule_linear_gdn2_amd import workloads as W
+
+    x = W.make("batched_bf16")
+    wl = x["workload"]
+    d = to_dev(x, "bf16")
+    s0 = torch.from_numpy(x["initial_state"]).cuda()
+    rng = np.random.default_rng(7)
+    g = W.to_torch(rng.standard_normal(x["v"].shape).astype(np.float32), "bf16", "cuda")
+    gs = torch.from_numpy(rng.standard_normal(x["initial_state"].shape).astype(np.float32)).cuda()
+    B, T, H, dk, dv = wl.B, wl.T, wl.H, wl.dk, wl.dv
+    ws = torch.empty(binding.gdn2_chunk_bwd_workspace_bytes(B, T, H, dk, dv, 0, 1), dtype=torch.uint8,
+                     device="cuda")
+
+    def call():
+        binding.gdn2_chunk_bwd(d["q"], d["k"], d["v"], d["alpha"], d["b"], d["w"], g, s0, gs, workspace=ws)
+
+    per, _, _ = time_events(call, args.warmup, args.steps)
+    ms = float(np.median(per))
+    nbytes = bwd_bytes(B, T, H, dk, dv, B)
+    flops = bwd_flops([T] * B, H, dk, dv)
+    log(f"backward: {ms:.2f} ms per call, {B * T / (ms / 1e3) / 1e6:.2f} M tokens/s, "
+        f"{flops / (ms / 1e3) / 1e12:.1f} TFLOP/s FP32")
+    return dict(x=x, wl=wl, ms=ms, bytes=nbytes, flops=flops, ws_bytes=ws.numel())
+
+
 def run_only(args):
     """One part alone (for rocprofv3 runs); prints one JSON line."""
     import torch
 
-    if args.only == "chunk":
+    if args.only == "bwd":
+        bw = bench_bwd(args)
+        res = {"part": "bwd", "workload": bw["wl"].name, "median_call_ms": bw["ms"],
+               "algorithmic_bytes": bw["bytes"], "flops": bw["flops"], "launches": args.steps + args.warmup}
+    elif args.only == "chunk":
         ch = bench_chunk(args)
         res = {"part": "chunk", "workload": ch["wl"].name, "avg_launch_ms": ch["kern_ms"],
                "algorithmic_bytes": ch["bytes"], "launches": args.steps + args.warmup}
@@ -312,6 +374,28 @@ def run_configs(args):
             f"{row['hbm_frac'] * 100:.1f}% HBM")
         print(json.dumps(row), flush=True)
         del d, x
+    # the gate-aware backward on the headline shape, and the oracle's reverse mode beside it
+    bw = bench_bwd(args)
+    t0 = time.perf_counter()
+    xb = bw["x"]
+    sub = {n: np.ascontiguousarray(xb[n][:1, :1024, :1]) for n in NAMES}
+    rng = np.random.default_rng(8)
+    oracle.backward(sub["q"], sub["k"], sub["v"], sub["alpha"], sub["b"], sub["w"],
+                    rng.standard_normal(sub["v"].shape), np.ascontiguousarray(xb["initial_state"][:1, :1]),
+                    rng.standard_normal((1, 1, 128, 128)), threads=1)
+    one_bwd = time.perf_counter() - t0
+    wlb = bw["wl"]
+    print(json.dumps({"report": "config", "workload": "batched_bf16 backward (gdn2_chunk_bwd)",
+                      "ms_per_call": bw["ms"], "tokens_per_s": wlb.B * wlb.T / (bw["ms"] / 1e3),
+                      "GBps": bw["bytes"] / (bw["ms"] / 1e3) / 1e9,
+                      "hbm_frac": bw["bytes"] / (bw["ms"] / 1e3) / 1e9 / HBM_PEAK_GBPS,
+                      "TFLOPs": bw["flops"] / (bw["ms"] / 1e3) / 1e12,
+                      "fp32_alu_frac": bw["flops"] / (bw["ms"] / 1e3) / 1e12 / FP32_VALU_TFLOPS,
+                      "workspace_bytes": bw["ws_bytes"],
+                      "oracle_one_core": {"value": 1024 / one_bwd, "unit": "token-heads/s",
+                                          "sample": f"1 sequence x 1 head x 1024 tokens, {one_bwd:.2f} s"}}),
+          flush=True)
+    del bw, xb
     # the oracle: all cores on four sequences of the headline workload, one core on one (sequence, head)
     x = W.make("batched_bf16")
     wl = x["workload"]
@@ -345,7 +429,7 @@ def main():
     ap.add_argument("--workload", default="batched_bf16",
                     choices=["batched_bf16", "layer_bf16", "varlen32_bf16", "tiny_f32"])
     ap.add_argument("--no-decode", action="store_true", help="skip the decode half")
-    ap.add_argument("--only", choices=["chunk", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["chunk", "decode", "copy", "bwd"], default=None,
                     help="profiling aid: run one part only and print its timing line "
                          "(copy = a plain 1 GiB device copy, the reference for HBM byte counters)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
