@@ -374,6 +374,41 @@ def run_configs(args):
             f"{row['hbm_frac'] * 100:.1f}% HBM")
         print(json.dumps(row), flush=True)
         del d, x
+    # the token mixer around the recurrence on the headline shape (HBM-bound passes)
+    x = W.make("batched_bf16")
+    B, T, H, dk, dv, K = 8, 4096, 16, 128, 128, 4
+    rng = np.random.default_rng(9)
+    d = to_dev(x, "bf16")
+    conv = [torch.from_numpy((0.5 * rng.standard_normal((H * dd, K))).astype(np.float32)).cuda() for dd in (dk, dk, dv)]
+    state = torch.zeros((B, H * (2 * dk + dv), K - 1), dtype=torch.float32, device="cuda")
+    outs = {}
+
+    def call_pro():
+        outs["p"] = binding.gdn2_mixer_prologue(d["q"], d["k"], d["v"], conv[0], conv[1], conv[2], d["b"], d["w"],
+                                                conv_state=state, q_scale=dk ** -0.5)
+
+    per, _, _ = time_events(call_pro, args.warmup, args.steps)
+    ms = float(np.median(per))
+    nbytes = B * T * H * (3 * dk * 2 + 2 * dv * 2) * 2  # xq, xk, b_logit, xv, w_logit in; q, k, b, v, w out
+    log(f"mixer prologue: {ms * 1e3:.1f} us, {nbytes / (ms / 1e3) / 1e9:.0f} GB/s")
+    print(json.dumps({"report": "config", "workload": "batched_bf16 token-mixer prologue (K=4)",
+                      "us_per_call": ms * 1e3, "GBps": nbytes / (ms / 1e3) / 1e9,
+                      "hbm_frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, "algorithmic_bytes": nbytes}), flush=True)
+    gate = d["w"]
+    wgt = torch.ones(dv, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(d["v"])
+
+    def call_epi():
+        binding.gdn2_mixer_epilogue(d["v"], gate, wgt, out=y)
+
+    per, _, _ = time_events(call_epi, args.warmup, args.steps)
+    ms = float(np.median(per))
+    nbytes = B * T * H * 3 * dv * 2  # o, gate in; y out
+    log(f"mixer epilogue: {ms * 1e3:.1f} us, {nbytes / (ms / 1e3) / 1e9:.0f} GB/s")
+    print(json.dumps({"report": "config", "workload": "batched_bf16 token-mixer epilogue",
+                      "us_per_call": ms * 1e3, "GBps": nbytes / (ms / 1e3) / 1e9,
+                      "hbm_frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, "algorithmic_bytes": nbytes}), flush=True)
+    del d, x, outs, y
     # the gate-aware backward on the headline shape, and the oracle's reverse mode beside it
     bw = bench_bwd(args)
     t0 = time.perf_counter()

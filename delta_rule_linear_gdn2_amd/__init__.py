@@ -7,6 +7,8 @@ Two entry points, both hand-written HIP behind the C ABI in include/gdn2.h:
 * ``gdn2_recurrent_step`` fused single-token decode step, state updated in place
 * ``gdn2_recurrent_fwd``  the fused recurrent form over T tokens per sequence
 * ``gdn2_chunk_bwd``      gradients of the chunkwise forward (gate-aware backward)
+* ``gdn2_mixer_prologue`` / ``gdn2_mixer_epilogue``: the token mixer around the
+  recurrence (convolution, SiLU, L2 norm, gate sigmoids; RMS norm and output gate)
 * ``gdn2_chunk_fwd_gates`` / ``gdn2_recurrent_step_gates``: the same with a gate
   layout (``GATES_*`` flags: scalar erase, write or decay gates, tied write gate)
 
@@ -26,6 +28,8 @@ from .binding import (  # noqa: F401
     gdn2_chunk_fwd,
     gdn2_chunk_fwd_gates,
     gdn2_chunk_fwd_workspace_bytes,
+    gdn2_mixer_epilogue,
+    gdn2_mixer_prologue,
     gdn2_recurrent_fwd,
     gdn2_recurrent_step,
     gdn2_recurrent_step_gates,
@@ -47,6 +51,8 @@ __all__ = [
     "gdn2_chunk_fwd",
     "gdn2_chunk_fwd_gates",
     "gdn2_chunk_fwd_workspace_bytes",
+    "gdn2_mixer_epilogue",
+    "gdn2_mixer_prologue",
     "gdn2_recurrent_fwd",
     "gdn2_recurrent_step",
     "gdn2_recurrent_step_gates",

@@ -24,8 +24,8 @@ DTYPE_BF16 = 1
 
 EXPORTS = ("gdn2_chunk_bwd", "gdn2_chunk_bwd_workspace_bytes", "gdn2_chunk_fwd", "gdn2_chunk_fwd_gates",
            "gdn2_chunk_fwd_workspace_bytes",
-           "gdn2_recurrent_fwd", "gdn2_recurrent_step", "gdn2_recurrent_step_gates", "gdn2_status_string",
-           "gdn2_version")
+           "gdn2_mixer_epilogue", "gdn2_mixer_prologue", "gdn2_recurrent_fwd", "gdn2_recurrent_step",
+           "gdn2_recurrent_step_gates", "gdn2_status_string", "gdn2_version")
 
 # gdn2_gate_flags: layout of the gates (b, w, alpha), OR-ed together
 GATES_FULL, GATES_SCALAR_ERASE, GATES_SCALAR_WRITE, GATES_TIED, GATES_SCALAR_DECAY = 0, 1, 2, 4, 8
@@ -84,6 +84,11 @@ def load(path: str = LIB_PATH):
     lib.gdn2_chunk_bwd.restype = ctypes.c_int
     lib.gdn2_chunk_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     lib.gdn2_chunk_bwd_workspace_bytes.restype = Z
+    F = ctypes.c_float
+    lib.gdn2_mixer_prologue.argtypes = [P] * 16 + [I] * 7 + [F, F, I, P]
+    lib.gdn2_mixer_prologue.restype = ctypes.c_int
+    lib.gdn2_mixer_epilogue.argtypes = [P, P, P, P, ctypes.c_int64, I, F, I, I, P]
+    lib.gdn2_mixer_epilogue.restype = ctypes.c_int
     lib.gdn2_status_string.argtypes = [ctypes.c_int]
     lib.gdn2_status_string.restype = ctypes.c_char_p
     lib.gdn2_version.argtypes = []
@@ -350,4 +355,83 @@ def gdn2_chunk_bwd(q, k, v, alpha, b, w, d_o, initial_state=None, d_final_state=
                             0 if workspace is None else workspace.numel(), _stream(stream))
     if rc != GDN2_OK:
         raise Gdn2Error(rc, "gdn2_chunk_bwd")
+    return out
+
+
+GATE_ACTS = {"sigmoid": 0, "silu": 1}
+
+
+def gdn2_mixer_prologue(xq, xk, xv, conv_q, conv_k, conv_v, b_logit, w_logit, *, conv_state=None,
+                        output_conv_state=True, conv_state_out=None, cu_seqlens=None, q_scale=1.0, eps_l2=1e-6,
+                        stream=None):
+    """q, k, v, b, w of the recurrence from the projection outputs (one pass).
+
+    xq, xk, b_logit: [B, T, H, dk]; xv, w_logit: [B, T, H, dv] (float32 or
+    bfloat16); conv_q, conv_k: [H * dk, K], conv_v: [H * dv, K] float32;
+    conv_state: [N, H * (2 dk + dv), K - 1] float32 or None (zeros).  Returns
+    dict(q, k, v, b, w, conv_state) with the final convolution state (None if
+    not wanted; pass conv_state_out=conv_state for an in-place decode step).
+    """
+    import torch
+
+    lib = load()
+    B, T, H, dk = xq.shape
+    dv = xv.shape[-1]
+    K = conv_q.shape[-1]
+    dev, dt = xq.device, xq.dtype
+    code = _dtype_code(dt)
+    N = B if cu_seqlens is None else int(cu_seqlens.shape[0]) - 1
+    for name, t, width in (("xq", xq, dk), ("xk", xk, dk), ("b_logit", b_logit, dk), ("xv", xv, dv),
+                           ("w_logit", w_logit, dv)):
+        _check(name, t, (B, T, H, width), dt, dev)
+    for name, t, width in (("conv_q", conv_q, dk), ("conv_k", conv_k, dk), ("conv_v", conv_v, dv)):
+        _check(name, t, (H * width, K), torch.float32, dev)
+    st_shape = (N, H * (2 * dk + dv), K - 1)
+    if conv_state is not None:
+        _check("conv_state", conv_state, st_shape, torch.float32, dev)
+    if conv_state_out is not None:
+        _check("conv_state_out", conv_state_out, st_shape, torch.float32, dev)
+    elif output_conv_state:
+        conv_state_out = torch.empty(st_shape, dtype=torch.float32, device=dev)
+    if cu_seqlens is not None:
+        _check("cu_seqlens", cu_seqlens, (N + 1,), torch.int32, dev)
+    out = {name: torch.empty((B, T, H, width), dtype=dt, device=dev)
+           for name, width in (("q", dk), ("k", dk), ("b", dk), ("v", dv), ("w", dv))}
+    rc = lib.gdn2_mixer_prologue(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(conv_q), _ptr(conv_k), _ptr(conv_v),
+                                 _ptr(b_logit), _ptr(w_logit), _ptr(conv_state), _ptr(conv_state_out),
+                                 _ptr(out["q"]), _ptr(out["k"]), _ptr(out["v"]), _ptr(out["b"]), _ptr(out["w"]),
+                                 _ptr(cu_seqlens), B, T, H, dk, dv, K, N, float(q_scale), float(eps_l2), code,
+                                 _stream(stream))
+    if rc != GDN2_OK:
+        raise Gdn2Error(rc, "gdn2_mixer_prologue")
+    out["conv_state"] = conv_state_out
+    return out
+
+
+def gdn2_mixer_epilogue(o, gate, weight, *, eps=1e-5, act="sigmoid", out=None, stream=None):
+    """RMS-normalised o times weight times act(gate), over the last axis (dv).
+
+    o, gate: [..., dv] (float32 or bfloat16, same shape); weight: [dv] float32;
+    act: "sigmoid" or "silu"."""
+    import torch
+
+    lib = load()
+    dv = o.shape[-1]
+    dev, dt = o.device, o.dtype
+    code = _dtype_code(dt)
+    _check("gate", gate, tuple(o.shape), dt, dev)
+    _check("weight", weight, (dv,), torch.float32, dev)
+    if not o.is_contiguous():
+        raise ValueError("o: must be contiguous")
+    if out is None:
+        out = torch.empty_like(o)
+    else:
+        _check("out", out, tuple(o.shape), dt, dev)
+    if act not in GATE_ACTS:
+        raise ValueError(f"act must be one of {tuple(GATE_ACTS)}")
+    rows = o.numel() // dv
+    rc = lib.gdn2_mixer_epilogue(_ptr(o), _ptr(gate), _ptr(weight), _ptr(out), rows, dv, float(eps),
+                                 GATE_ACTS[act], code, _stream(stream))
+    if rc != GDN2_OK:
+        raise Gdn2Error(rc, "gdn2_mixer_epilogue")
     return out

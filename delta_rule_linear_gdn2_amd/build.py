@@ -24,6 +24,7 @@ SOURCES = [
     "chunk_fwd_simple.hip",
     "chunk_fwd_mfma.hip",
     "chunk_bwd.hip",
+    "mixer.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

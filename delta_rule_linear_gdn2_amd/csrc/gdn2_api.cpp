@@ -168,6 +168,75 @@ gdn2_status recurrent(const void* q, const void* k, const void* v, const float* 
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 
+gdn2_status mixer_prologue(const void* xq, const void* xk, const void* xv, const float* conv_q,
+                           const float* conv_k, const float* conv_v, const void* b_logit, const void* w_logit,
+                           const float* conv_state_in, float* conv_state_out, void* q, void* k, void* v, void* b,
+                           void* w, const int32_t* cu_seqlens, int32_t B, int32_t T, int32_t H, int32_t dk,
+                           int32_t dv, int32_t K, int32_t num_seqs, float q_scale, float eps_l2, gdn2_dtype dtype,
+                           void* stream)
+{
+    if (dtype != GDN2_DTYPE_F32 && dtype != GDN2_DTYPE_BF16) return GDN2_ERR_BAD_DTYPE;
+    if (B <= 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0 || K < 1 || K > 16) return GDN2_ERR_BAD_SHAPE;
+    if (cu_seqlens && (B != 1 || num_seqs <= 0)) return GDN2_ERR_BAD_SHAPE;
+    if (!(eps_l2 >= 0.f)) return GDN2_ERR_BAD_SHAPE;
+    if (!supported_head(dk) || !supported_head(dv)) return GDN2_ERR_UNSUPPORTED;
+    const int32_t N = cu_seqlens ? num_seqs : B;
+    if (T > 0 && (!xq || !xk || !xv || !conv_q || !conv_k || !conv_v || !b_logit || !w_logit || !q || !k || !v ||
+                  !b || !w))
+        return GDN2_ERR_NULL_POINTER;
+    const void* ptrs[] = {xq, xk, xv, conv_q, conv_k, conv_v, b_logit, w_logit, conv_state_in, conv_state_out,
+                          q, k, v, b, w};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDN2_ERR_MISALIGNED;
+    if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return GDN2_ERR_MISALIGNED;
+    const int64_t tokens = int64_t(B) * T * H;
+    const int eb = element_bytes(dtype);
+    const int64_t st_bytes = int64_t(N) * H * (2 * dk + dv) * (K - 1) * 4;
+    const Span s_in = span(conv_state_in, conv_state_in ? st_bytes : 0);
+    const Span in[] = {span(xq, tokens * dk * eb), span(xk, tokens * dk * eb), span(xv, tokens * dv * eb),
+                       span(conv_q, int64_t(H) * dk * K * 4), span(conv_k, int64_t(H) * dk * K * 4),
+                       span(conv_v, int64_t(H) * dv * K * 4), span(b_logit, tokens * dk * eb),
+                       span(w_logit, tokens * dv * eb), s_in,
+                       span(cu_seqlens, cu_seqlens ? int64_t(N + 1) * 4 : 0)};
+    const Span out[] = {span(q, tokens * dk * eb), span(k, tokens * dk * eb), span(v, tokens * dv * eb),
+                        span(b, tokens * dk * eb), span(w, tokens * dv * eb),
+                        span(conv_state_out, conv_state_out ? st_bytes : 0)};
+    // The state may be updated in place only when each sequence is one token
+    // (a decode step): then one wavefront reads and writes each state row.
+    const bool in_place_ok = !cu_seqlens && T == 1 && conv_state_out == conv_state_in;
+    for (int i = 0; i < 6; ++i) {
+        for (const Span& x : in) {
+            if (i == 5 && in_place_ok && x.lo == s_in.lo) continue;
+            if (overlap(out[i], x)) return GDN2_ERR_ALIAS;
+        }
+        for (int j = 0; j < i; ++j)
+            if (overlap(out[i], out[j])) return GDN2_ERR_ALIAS;
+    }
+    gdn2::MixerArgs a{xq, xk, xv, conv_q, conv_k, conv_v, b_logit, w_logit, conv_state_in, conv_state_out,
+                      q, k, v, b, w, cu_seqlens, B, T, H, dk, dv, K, N, q_scale, eps_l2};
+    const hipError_t e = gdn2::launch_mixer_prologue(a, dtype == GDN2_DTYPE_BF16, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
+gdn2_status mixer_epilogue(const void* o, const void* gate, const float* weight, void* y, int64_t rows, int32_t dv,
+                           float eps, int32_t act, gdn2_dtype dtype, void* stream)
+{
+    if (dtype != GDN2_DTYPE_F32 && dtype != GDN2_DTYPE_BF16) return GDN2_ERR_BAD_DTYPE;
+    if (rows < 0 || dv <= 0 || (act != 0 && act != 1) || !(eps > 0.f)) return GDN2_ERR_BAD_SHAPE;
+    if (!supported_head(dv)) return GDN2_ERR_UNSUPPORTED;
+    if (rows > 0 && (!o || !gate || !weight || !y)) return GDN2_ERR_NULL_POINTER;
+    const void* ptrs[] = {o, gate, weight, y};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDN2_ERR_MISALIGNED;
+    const int eb = element_bytes(dtype);
+    const Span sy = span(y, rows * dv * eb);
+    for (Span x : {span(o, rows * dv * eb), span(gate, rows * dv * eb), span(weight, int64_t(dv) * 4)})
+        if (overlap(sy, x)) return GDN2_ERR_ALIAS;
+    gdn2::EpilogueArgs a{o, gate, weight, y, rows, dv, eps, act};
+    const hipError_t e = gdn2::launch_mixer_epilogue(a, dtype == GDN2_DTYPE_BF16, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
 // Workspace regions of the backward pass: chunk-start states, chunk-end
 // state gradients (slots x H x dk x dv FP32 each, per batch row), U and dX
 // rows (B x T x H x dv FP32 each) and each chunk's prepared triangular
@@ -321,6 +390,24 @@ size_t gdn2_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d
     (void)dtype;
     if (B <= 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return 0;
     return bwd_workspace(B, T, H, dk, dv, num_seqs > 0, num_seqs).total;
+}
+
+gdn2_status gdn2_mixer_prologue(const void* xq, const void* xk, const void* xv, const float* conv_q,
+                                const float* conv_k, const float* conv_v, const void* b_logit, const void* w_logit,
+                                const float* conv_state_in, float* conv_state_out, void* q, void* k, void* v,
+                                void* b, void* w, const int32_t* cu_seqlens, int32_t B, int32_t T, int32_t H,
+                                int32_t dk, int32_t dv, int32_t kernel_size, int32_t num_seqs, float q_scale,
+                                float eps_l2, gdn2_dtype dtype, void* stream)
+{
+    return mixer_prologue(xq, xk, xv, conv_q, conv_k, conv_v, b_logit, w_logit, conv_state_in, conv_state_out, q, k,
+                          v, b, w, cu_seqlens, B, T, H, dk, dv, kernel_size, num_seqs, q_scale, eps_l2, dtype,
+                          stream);
+}
+
+gdn2_status gdn2_mixer_epilogue(const void* o, const void* gate, const float* weight, void* y, int64_t rows,
+                                int32_t dv, float eps, int32_t gate_act, gdn2_dtype dtype, void* stream)
+{
+    return mixer_epilogue(o, gate, weight, y, rows, dv, eps, gate_act, dtype, stream);
 }
 
 }  // extern "C"

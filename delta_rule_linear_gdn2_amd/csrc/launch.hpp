@@ -75,7 +75,43 @@ struct BwdArgs {
 // Floats of one chunk's prepared block in ws_prep.
 int64_t chunk_bwd_prep_floats(int dk);
 
+// Token-mixer prologue: q, k, v, b, w from projection outputs.
+struct MixerArgs {
+    const void* xq;
+    const void* xk;
+    const void* xv;
+    const float* conv_q;  // [H * dk][K]
+    const float* conv_k;  // [H * dk][K]
+    const float* conv_v;  // [H * dv][K]
+    const void* b_logit;
+    const void* w_logit;
+    const float* conv_state_in;  // [N][H * (2 dk + dv)][K - 1] or null (zeros)
+    float* conv_state_out;       // same layout, or null
+    void* q;
+    void* k;
+    void* v;
+    void* b;
+    void* w;
+    const int32_t* cu_seqlens;
+    int32_t B, T, H, dk, dv, K, N;
+    float q_scale, eps_l2;
+};
+
+// Token-mixer epilogue: RMS norm times weight times act(gate), per row of dv.
+struct EpilogueArgs {
+    const void* o;
+    const void* gate;
+    const float* weight;  // [dv]
+    void* y;
+    int64_t rows;
+    int32_t dv;
+    float eps;
+    int32_t act;  // 0 sigmoid, 1 SiLU
+};
+
 // Each returns hipSuccess or the launch error; bf16 selects the input dtype.
+hipError_t launch_mixer_prologue(const MixerArgs& a, bool bf16, hipStream_t stream);
+hipError_t launch_mixer_epilogue(const EpilogueArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_chunk_bwd(const BwdArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_recurrent(const StepArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_chunk_fwd_simple(const ChunkArgs& a, bool bf16, hipStream_t stream);

@@ -239,6 +239,55 @@ gdn2_status gdn2_chunk_bwd(const void* q, const void* k, const void* v,
 size_t gdn2_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t dk_size, int32_t dv_size,
                                       int32_t num_seqs, gdn2_dtype dtype);
 
+/*
+ * Token-mixer prologue: q, k, v, b, w for the recurrence from the projection
+ * outputs, in one pass ("Token processing and parallel training": short
+ * causal convolution, SiLU and L2 normalisation on the query and key paths,
+ * convolution and SiLU on the value path; "Independent decisions on two
+ * axes": sigmoid erase and write gates).  Per channel c of head h and token t
+ * of a sequence starting at bos:
+ *     y_t = sum_{i<K} W[h d + c][i] x_{t-K+1+i}   (inputs before bos come from
+ *                                                  the carried state)
+ *     q = q_scale * y_q' / sqrt(|y_q'|^2 + eps_l2) with y_q' = SiLU(y_q)
+ *     k = y_k' / sqrt(|y_k'|^2 + eps_l2)            with y_k' = SiLU(y_k)
+ *     v = SiLU(y_v),  b = sigmoid(b_logit),  w = sigmoid(w_logit)
+ * (the norms over the head's dk channels).
+ *
+ *   xq, xk, b_logit : [B, T, H, dk] dtype     xv, w_logit : [B, T, H, dv] dtype
+ *   conv_q, conv_k  : [H * dk][K] FP32        conv_v      : [H * dv][K] FP32
+ *                     (tap K - 1 multiplies the current token)
+ *   conv_state_in   : [N, H * (2 dk + dv), K - 1] FP32, the K - 1 inputs before
+ *                     each sequence, oldest first (channels: q, then k, then v);
+ *                     NULL = zeros
+ *   conv_state_out  : same layout, each sequence's last K - 1 inputs, or NULL.
+ *                     It may equal conv_state_in only when every sequence is
+ *                     one token (T = 1 without cu_seqlens: a decode step).
+ *   q, k, b         : [B, T, H, dk] dtype      v, w : [B, T, H, dv] dtype
+ *   cu_seqlens, num_seqs: as for gdn2_chunk_fwd (the convolution restarts at
+ *                     every sequence).  1 <= kernel_size <= 16, eps_l2 >= 0.
+ * Outputs must not overlap inputs or each other (GDN2_ERR_ALIAS).
+ */
+gdn2_status gdn2_mixer_prologue(const void* xq, const void* xk, const void* xv,
+                                const float* conv_q, const float* conv_k, const float* conv_v,
+                                const void* b_logit, const void* w_logit,
+                                const float* conv_state_in, float* conv_state_out,
+                                void* q, void* k, void* v, void* b, void* w,
+                                const int32_t* cu_seqlens,
+                                int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                                int32_t kernel_size, int32_t num_seqs, float q_scale, float eps_l2,
+                                gdn2_dtype dtype, void* stream);
+
+/*
+ * Token-mixer epilogue, after the recurrence (same section: RMS
+ * normalisation, then an output gate distinct from the write gate):
+ *     y = o / sqrt(mean(o^2) + eps) * weight * act(gate)
+ * per row of dv values.  o, gate, y: [rows, dv] dtype; weight: [dv] FP32;
+ * gate_act 0 = sigmoid, 1 = SiLU; eps > 0.  y must not overlap an input.
+ */
+gdn2_status gdn2_mixer_epilogue(const void* o, const void* gate, const float* weight, void* y,
+                                int64_t rows, int32_t dv, float eps, int32_t gate_act,
+                                gdn2_dtype dtype, void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* gdn2_status_string(gdn2_status status);
 

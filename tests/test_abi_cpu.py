@@ -262,3 +262,56 @@ def test_bwd_workspace_query(lib):
 ])
 def test_chunk_bwd_rejects(lib, kw, expected):
     assert bwd_call(lib, **kw) == expected
+
+
+def pro_call(lib, **kw):
+    # B=2, T=64, H=4, dk=dv=64, K=4 bf16: token tensors 64 KiB; filters 4 KiB; state 2 x 768 x 3 x 4 B
+    args = dict(xq=fake(0), xk=fake(1), xv=fake(2), cq=fake(3), ck=fake(4), cv=fake(5), bl=fake(6), wl=fake(7),
+                si=fake(8), so=fake(9), q=fake(10), k=fake(11), v=fake(12), b=fake(13), w=fake(14), cu=None,
+                B=2, T=64, H=4, dk_=64, dv_=64, K=4, num_seqs=0, scale=1.0, eps=1e-6, dtype=1)
+    args.update(kw)
+    a = args
+    return lib.gdn2_mixer_prologue(a["xq"], a["xk"], a["xv"], a["cq"], a["ck"], a["cv"], a["bl"], a["wl"],
+                                   a["si"], a["so"], a["q"], a["k"], a["v"], a["b"], a["w"], a["cu"], a["B"],
+                                   a["T"], a["H"], a["dk_"], a["dv_"], a["K"], a["num_seqs"], a["scale"], a["eps"],
+                                   a["dtype"], None)
+
+
+# Every case must be rejected before launch.
+@pytest.mark.parametrize("kw,expected", [
+    (dict(dtype=7), DTYPE),
+    (dict(K=0), SHAPE),
+    (dict(K=17), SHAPE),
+    (dict(eps=-1.0), SHAPE),
+    (dict(T=-1), SHAPE),
+    (dict(dk_=96), UNSUP),
+    (dict(cq=None), NULLP),
+    (dict(w=None), NULLP),
+    (dict(xv=fake(2, 8)), MISAL),
+    (dict(q=fake(0, 512)), ALIAS),                    # q inside xq
+    (dict(k=fake(10, 4096)), ALIAS),                  # k inside q
+    (dict(so=fake(8)), ALIAS),                        # in-place state with T > 1
+    (dict(so=fake(8), T=1, cu=fake(15), B=1, num_seqs=2), ALIAS),  # in place with packed sequences
+    (dict(v=fake(3, 1024)), ALIAS),                   # v over the q filters
+])
+def test_mixer_prologue_rejects(lib, kw, expected):
+    assert pro_call(lib, **kw) == expected
+
+
+@pytest.mark.parametrize("kw,expected", [
+    (dict(dtype=3), DTYPE),
+    (dict(act=2), SHAPE),
+    (dict(eps=0.0), SHAPE),
+    (dict(rows=-1), SHAPE),
+    (dict(dv_=80), UNSUP),
+    (dict(gate=None), NULLP),
+    (dict(weight=fake(2, 4)), MISAL),
+    (dict(y=fake(0, 256)), ALIAS),                    # y inside o
+    (dict(y=fake(2)), ALIAS),                         # y over the weight
+])
+def test_mixer_epilogue_rejects(lib, kw, expected):
+    args = dict(o=fake(0), gate=fake(1), weight=fake(2), y=fake(3), rows=100, dv_=64, eps=1e-5, act=0, dtype=1)
+    args.update(kw)
+    a = args
+    assert lib.gdn2_mixer_epilogue(a["o"], a["gate"], a["weight"], a["y"], a["rows"], a["dv_"], a["eps"], a["act"],
+                                   a["dtype"], None) == expected
