@@ -95,23 +95,48 @@ def step_bytes(N, H, dk, dv, eb=2):
     return N * H * (2 * dk * dv * 4 + 3 * dk * eb + 2 * dv * eb + dk * 4 + dv * eb)
 
 
+# What the recorded HBM counters of a kernel depend on: its source file and
+# the device helpers, and the argument struct it takes (comments and blank
+# lines do not count).
+KERNEL_SOURCES = {"chunk": ("chunk_fwd_mfma.hip", "ChunkArgs"), "decode": ("recurrent_step.hip", "StepArgs")}
+
+
+def _strip_comments(text):
+    import re
+
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
+def source_digest(part):
+    """sha256 of the code a kernel's counters depend on."""
+    import hashlib
+    import re
+
+    csrc = os.path.join(ROOT, "delta_rule_linear_gdn2_amd", "csrc")
+    src, struct = KERNEL_SOURCES[part]
+    h = hashlib.sha256()
+    for name in (src, "gdn2_device.hpp"):
+        with open(os.path.join(csrc, name)) as f:
+            h.update(_strip_comments(f.read()).encode())
+    with open(os.path.join(csrc, "launch.hpp")) as f:
+        m = re.search(r"struct %s \{.*?\};" % struct, _strip_comments(f.read()), flags=re.S)
+    h.update(m.group(0).encode())
+    return h.hexdigest()
+
+
 def pmc_traffic(part):
     """HBM bytes per launch measured by rocprofv3 FETCH_SIZE + WRITE_SIZE
     (scaled by the copy-kernel factors) as recorded in profiles/pmc_traffic.json,
-    or None when the kernel's sources have changed since the counters were taken."""
-    import hashlib
-
+    or None when the kernel's code has changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)["kernels"][part]
     except (OSError, KeyError, ValueError):
         return None
-    h = hashlib.sha256()
-    for name in rec["sources"]:
-        with open(os.path.join(ROOT, "delta_rule_linear_gdn2_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
-    return rec["traffic_bytes"] if h.hexdigest() == rec["source_sha256"] else None
+    return rec["traffic_bytes"] if rec.get("source_digest") == source_digest(part) else None
 
 
 def to_dev(x, dtype):

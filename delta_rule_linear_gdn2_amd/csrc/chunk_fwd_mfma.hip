@@ -2,10 +2,10 @@
 // tiles of 64 columns).
 //
 // The chunkwise WY form (Gated DeltaNet-2 analysis, iplexlaw.co.kr, "Token
-// processing and parallel training"): per chunk the cumulative channel-wise
-// decay is absorbed into asymmetric factors, leaving a lower-triangular solve
-// and dense products; FP32 is kept for the decay, the solve and the carried
-// state.  With incoming state S, per key channel the running decay
+// processing and parallel training"): inside a chunk the running product of
+// each key channel's decay is folded into the row factors and, inverted, into
+// the column factors, so one lower-triangular solve and a few dense products
+// remain; the decay, the solve and the carried state stay in FP32.  With incoming state S, per key channel the running decay
 // c_i = prod_{m<=i} alpha_m inside the chunk, e = b k and z = w v:
 //     Et_i = e_i c_i     Qt_i = q_i c_i     Kt_j = k_j / c_j     gamma = c_last
 //     A = strict_lower(Et Kt^T)     P = lower(Qt Kt^T)

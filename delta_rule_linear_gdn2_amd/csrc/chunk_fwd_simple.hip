@@ -3,8 +3,8 @@
 //
 // Within a chunk of L tokens with incoming state S0 (Gated DeltaNet-2
 // analysis, iplexlaw.co.kr, "Token processing and parallel training": the
-// cumulative channel-wise decay is absorbed into asymmetric erase factors,
-// leaving a triangular solve and dense products per chunk), with
+// running per-channel decay is folded into unequal row and column factors,
+// so a triangular solve and dense products per chunk remain), with
 // G_i = sum_{m<=i} log2 alpha_m per key channel:
 //     A_ij = sum_c e_ic k_jc 2^(G_ic - G_jc)   (j < i)      strictly lower
 //     P_ij = sum_c q_ic k_jc 2^(G_ic - G_jc)   (j <= i)     lower incl. diagonal

@@ -3,10 +3,10 @@
 // recurrence.
 //
 // The Gated DeltaNet-2 analysis (iplexlaw.co.kr, "Token processing and
-// parallel training") puts a short causal convolution, SiLU and L2
-// normalisation on the query and key paths, a convolution and SiLU on the
-// value path, and RMS normalisation with a separate output gate after the
-// recurrence.  The erase and write gates pass through a sigmoid ("Independent
+// parallel training") passes the query and key projections through a causal
+// convolution of a few taps, SiLU and an L2 norm, the value projection
+// through a convolution and SiLU, and follows the recurrence with an RMS norm
+// and an output gate of its own.  The erase and write gates pass through a sigmoid ("Independent
 // decisions on two axes").  Per channel c of head h and token t of a
 // sequence that starts at bos:
 //     y_t = sum_{i<K} W[h d + c][i] x_{t-K+1+i}     (x before bos: the carried state)

@@ -10,7 +10,7 @@
  *     Sbar = Diag(alpha_t) S_{t-1}          (decay on key channels)
  *     r_t = Sbar^T e_t                      (old read through the erase key)
  *     S_t = Sbar + k_t (z_t - r_t)^T        (delta update)
- *     o_t = S_t^T q_t                       (query reads the UPDATED state)
+ *     o_t = S_t^T q_t                       (output from the state AFTER the update)
  * The same page, section "Token processing and parallel training", gives the
  * chunkwise WY form with 64-token chunks used for long inputs
  * (gdn2_chunk_fwd); the "DeltaNet" entity trail at mindpattern.ai (finding
@@ -98,9 +98,10 @@ typedef enum gdn2_gate_flags {
 
 /*
  * Chunkwise forward over whole sequences ("Token processing and parallel
- * training": 64-token chunks, cumulative channel-wise decay in FP32 absorbed
- * into asymmetric erase factors, a per-chunk lower-triangular solve and dense
- * products; the state is carried between chunks in FP32).
+ * training": chunks of 64 tokens; inside a chunk the running per-channel
+ * decay, in FP32, is folded into unequal row and column factors, leaving a
+ * lower-triangular solve and dense products; the state passes from chunk to
+ * chunk in FP32).
  *
  *   q, k, b : [B, T, H, dk]  dtype          v, w, o : [B, T, H, dv]  dtype
  *   alpha   : [B, T, H, dk]  FP32

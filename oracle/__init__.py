@@ -11,9 +11,11 @@ only marshals numpy arrays.  Sources, cited by page title and section:
 * "Gated DeltaNet-2: Decoupling Erase and Write in Linear Attention" analysis
   (iplexlaw.co.kr), "Independent decisions on two axes": the update
   e = b*k, z = w*v, Sbar = Diag(alpha) S, r = Sbar^T e, S = Sbar + k (z - r)^T,
-  and the query reads the updated state.  -> ``recurrent`` (THE oracle).
+  and the output is read from the state after the update.  -> ``recurrent``
+  (THE oracle).
 * Same page, "Token processing and parallel training": 64-token chunkwise WY
-  form with cumulative channel-wise decay absorbed into asymmetric factors.
+  form, the running per-channel decay folded into unequal row and column
+  factors.
   -> ``chunked`` (any chunk size; a self-consistency pin).
 * "DeltaNet" entity trail (mindpattern.ai), "You Could Have Come Up With Kimi
   Delta Attention": each token's transition is a diagonal decay composed with

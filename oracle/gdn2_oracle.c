@@ -24,7 +24,7 @@
  *     Sbar = Diag(alpha_t) S_{t-1}       channel-wise decay on key channels
  *     r_t  = Sbar^T e_t                  old read
  *     S_t  = Sbar + k_t (z_t - r_t)^T    delta update
- *     o_t  = S_t^T q_t                   query reads the UPDATED state
+ *     o_t  = S_t^T q_t                   output from the state AFTER the update
  *
  * Functions:
  *   gdn2_oracle_recurrent   O1  the definition, token by token  (THE oracle)
@@ -157,8 +157,8 @@ static void recurrent_chain(const shape_t* s, int32_t n, int32_t h,
 
 /* ------------------------------------------------------------------------
  * O2: the chunkwise form [IPX, "Token processing and parallel training"]:
- * within a chunk the cumulative channel-wise decay is absorbed into
- * asymmetric factors (row side e * exp(+G), column side k * exp(-G)), which
+ * within a chunk the running per-channel decay is folded into unequal row
+ * and column factors (row side e * exp(+G), column side k * exp(-G)), which
  * leaves a unit-lower-triangular solve and dense products:
  *   G_i  = sum_{m<=i} log alpha_m                 (per key channel)
  *   Et_i = e_i exp(G_i),  Kh_j = k_j exp(-G_j),  Qt_i = q_i exp(G_i),

@@ -2,9 +2,9 @@
 
 The "Gated DeltaNet-2: Decoupling Erase and Write in Linear Attention"
 analysis (iplexlaw.co.kr), section "Token processing and parallel training",
-lists the layer around the recurrence.  The query and key paths each apply a
-linear projection, a short causal convolution, SiLU and L2 normalisation.
-The value path applies a projection, a convolution and SiLU.  The erase and
+lists the layer around the recurrence.  Queries and keys go through a linear
+projection, a causal convolution of a few taps, SiLU and an L2 norm; values
+through a projection, a convolution and SiLU.  The erase and
 write gates come from their own projections through a sigmoid (section
 "Independent decisions on two axes").  After the recurrence, an RMS
 normalisation and a separate output gate precede the output projection.  The
