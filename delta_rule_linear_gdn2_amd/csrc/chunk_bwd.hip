@@ -48,10 +48,13 @@
 namespace gdn2 {
 namespace {
 
-constexpr int kBwdThreads = 256;
+constexpr int kBwdThreads = 256;  // the parallel kernels
 constexpr int CH = kBwdChunk;
-constexpr int kTile = 32;  // value columns per workgroup of the sequential kernels
-static_assert(kBwdThreads == 8 * kTile && CH == 32, "thread layouts below assume 8 groups of 32 lanes");
+constexpr int kTile = 32;          // value columns per workgroup of the sequential kernels
+constexpr int kSeqThreads = 512;   // the sequential kernels: two wavefronts per SIMD
+constexpr int NG = kSeqThreads / kTile;  // lane groups of the sequential kernels
+constexpr int RR = CH / NG;              // chunk rows per thread
+static_assert(kBwdThreads == 8 * kTile && CH == 32 && CH % NG == 0, "thread layouts below");
 
 __device__ __forceinline__ int64_t slot_of(const BwdArgs& a, int n, int64_t bos, int m)
 {
@@ -206,35 +209,35 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdArgs a)
 }
 
 // Thread layout of the sequential kernels: lane column jj = tid % 32 of the
-// tile; chunk rows i0 + 8 r (r < 4) and state rows c0 + 8 r (r < DK / 8), with
-// i0 = c0 = tid / 32.  The rows a wavefront reads at one time are two, so the
-// row operand is a broadcast and the column operand is contiguous.
+// tile; chunk rows i0 + NG r (r < RR) and state rows c0 + NG r (r < DK / NG),
+// with i0 = c0 = tid / 32.  The rows a wavefront reads at one time are two,
+// so the row operand is a broadcast and the column operand is contiguous.
 
 // Prepared rows of one chunk into LDS (rows past the chunk are zero in the block).
-template <int DK, bool kQ>
+template <int DK, bool kQ, int NT>
 __device__ __forceinline__ void load_prep(const float* src, float (*Et)[DK + 1], float (*Qt)[DK + 1],
                                           float (*Kb)[DK + 1], float (*Tm)[CH + 1], float (*Pm)[CH + 1],
                                           float* gam, int tid)
 {
-    for (int i2 = tid; i2 < CH * CH; i2 += kBwdThreads) {
+    for (int i2 = tid; i2 < CH * CH; i2 += NT) {
         Tm[i2 / CH][i2 % CH] = src[kPrepT + i2];
         if (kQ) Pm[i2 / CH][i2 % CH] = src[kPrepP + i2];
     }
-    for (int i2 = tid; i2 < CH * DK; i2 += kBwdThreads) {
+    for (int i2 = tid; i2 < CH * DK; i2 += NT) {
         const int i = i2 / DK, ch = i2 % DK;
         Et[i][ch] = src[kPrepE + i2];
         if (kQ) Qt[i][ch] = src[kPrepE + CH * DK + i2];
         Kb[i][ch] = src[kPrepE + 2 * CH * DK + i2];
     }
-    for (int ch = tid; ch < DK; ch += kBwdThreads) gam[ch] = src[kPrepE + 3 * CH * DK + ch];
+    for (int ch = tid; ch < DK; ch += NT) gam[ch] = src[kPrepE + 3 * CH * DK + ch];
 }
 
 // ---------------------------------------------------------------------------
 // bwd_states: the forward again, storing the state at every chunk start.
 template <typename T, int DK>
-__global__ __launch_bounds__(kBwdThreads) void bwd_states_kernel(BwdArgs a)
+__global__ __launch_bounds__(kSeqThreads) void bwd_states_kernel(BwdArgs a)
 {
-    constexpr int RS = DK / 8;  // state rows per thread
+    constexpr int RS = DK / NG;  // state rows per thread
     __shared__ float Et[CH][DK + 1], Kb[CH][DK + 1];
     __shared__ float Tm[CH][CH + 1];
     __shared__ float gam[DK];
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_states_kernel(BwdArgs a)
     const int64_t s_off = (int64_t(n) * a.H + h) * DK * dv + j0 + jj;
 #pragma unroll
     for (int r = 0; r < RS; ++r)
-        Ss[i0 + 8 * r][jj] = a.initial_state ? a.initial_state[s_off + int64_t(i0 + 8 * r) * dv] : 0.f;
+        Ss[i0 + NG * r][jj] = a.initial_state ? a.initial_state[s_off + int64_t(i0 + NG * r) * dv] : 0.f;
 
     int m = 0;
     for (int64_t t0 = bos; t0 < eos; t0 += CH, ++m) {
@@ -265,55 +268,55 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_states_kernel(BwdArgs a)
         const int64_t slot = slot_of(a, n, bos, m);
         float* dst = a.ws_states + slot_base(a, brow, slot, h) + j0 + jj;
 #pragma unroll
-        for (int r = 0; r < RS; ++r) dst[int64_t(i0 + 8 * r) * dv] = Ss[i0 + 8 * r][jj];
+        for (int r = 0; r < RS; ++r) dst[int64_t(i0 + NG * r) * dv] = Ss[i0 + NG * r][jj];
         __syncthreads();  // the previous chunk is done with Et, Kb, Tm, Xs, Us and Ss
-        load_prep<DK, false>(a.ws_prep + prep_base(a, brow, slot, h), Et, nullptr, Kb, Tm, nullptr, gam, tid);
-        float z[4];
+        load_prep<DK, false, kSeqThreads>(a.ws_prep + prep_base(a, brow, slot, h), Et, nullptr, Kb, Tm, nullptr, gam, tid);
+        float z[RR];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = i0 + 8 * r;
+        for (int r = 0; r < RR; ++r) {
+            const int i = i0 + NG * r;
             const int64_t off = (row0 + int64_t(i) * a.H) * dv + j0 + jj;
             z[r] = i < L ? load_as_f32(w, off) * load_as_f32(v, off) : 0.f;
         }
         __syncthreads();
         // X = Z - Et S
         {
-            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+            float acc[RR] = {};
 #pragma unroll 4
             for (int ch = 0; ch < DK; ++ch) {
                 const float sv = Ss[ch][jj];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[r] += Et[i0 + 8 * r][ch] * sv;
+                for (int r = 0; r < RR; ++r) acc[r] += Et[i0 + NG * r][ch] * sv;
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Xs[i0 + 8 * r][jj] = z[r] - acc[r];
+            for (int r = 0; r < RR; ++r) Xs[i0 + NG * r][jj] = z[r] - acc[r];
         }
         __syncthreads();
         // U = Tm X  (Tm is unit lower triangular; rows past the chunk give zero)
         {
-            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+            float acc[RR] = {};
 #pragma unroll 4
             for (int mm = 0; mm < CH; ++mm) {
                 const float xv = Xs[mm][jj];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[r] += Tm[i0 + 8 * r][mm] * xv;
+                for (int r = 0; r < RR; ++r) acc[r] += Tm[i0 + NG * r][mm] * xv;
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Us[i0 + 8 * r][jj] = acc[r];
+            for (int r = 0; r < RR; ++r) Us[i0 + NG * r][jj] = acc[r];
         }
         __syncthreads();
         // S <- 2^G_L S + Kb^T U  (each thread its own elements)
         {
             float acc[RS];
 #pragma unroll
-            for (int r = 0; r < RS; ++r) acc[r] = gam[i0 + 8 * r] * Ss[i0 + 8 * r][jj];
+            for (int r = 0; r < RS; ++r) acc[r] = gam[i0 + NG * r] * Ss[i0 + NG * r][jj];
             for (int i = 0; i < L; ++i) {
                 const float uv = Us[i][jj];
 #pragma unroll
-                for (int r = 0; r < RS; ++r) acc[r] += Kb[i][i0 + 8 * r] * uv;
+                for (int r = 0; r < RS; ++r) acc[r] += Kb[i][i0 + NG * r] * uv;
             }
 #pragma unroll
-            for (int r = 0; r < RS; ++r) Ss[i0 + 8 * r][jj] = acc[r];
+            for (int r = 0; r < RS; ++r) Ss[i0 + NG * r][jj] = acc[r];
         }
     }
 }
@@ -321,9 +324,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_states_kernel(BwdArgs a)
 // ---------------------------------------------------------------------------
 // bwd_dstate: chunks in reverse, carrying the state gradient.
 template <typename T, int DK>
-__global__ __launch_bounds__(kBwdThreads) void bwd_dstate_kernel(BwdArgs a)
+__global__ __launch_bounds__(kSeqThreads) void bwd_dstate_kernel(BwdArgs a)
 {
-    constexpr int RS = DK / 8;
+    constexpr int RS = DK / NG;
     __shared__ float Et[CH][DK + 1], Qt[CH][DK + 1], Kb[CH][DK + 1];
     __shared__ float Tm[CH][CH + 1], Pm[CH][CH + 1];
     __shared__ float gam[DK];
@@ -349,7 +352,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dstate_kernel(BwdArgs a)
     const int64_t s_off = (int64_t(n) * a.H + h) * DK * dv + j0 + jj;
 #pragma unroll
     for (int r = 0; r < RS; ++r)
-        dSs[i0 + 8 * r][jj] = a.d_final_state ? a.d_final_state[s_off + int64_t(i0 + 8 * r) * dv] : 0.f;
+        dSs[i0 + NG * r][jj] = a.d_final_state ? a.d_final_state[s_off + int64_t(i0 + NG * r) * dv] : 0.f;
 
     const int M = int((eos - bos + CH - 1) / CH);
     for (int m = M - 1; m >= 0; --m) {
@@ -360,15 +363,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dstate_kernel(BwdArgs a)
         const int64_t sb = slot_base(a, brow, slot, h) + j0 + jj;
 #pragma unroll
         for (int r = 0; r < RS; ++r) {
-            a.ws_dstates[sb + int64_t(i0 + 8 * r) * dv] = dSs[i0 + 8 * r][jj];
-            Ss[i0 + 8 * r][jj] = a.ws_states[sb + int64_t(i0 + 8 * r) * dv];
+            a.ws_dstates[sb + int64_t(i0 + NG * r) * dv] = dSs[i0 + NG * r][jj];
+            Ss[i0 + NG * r][jj] = a.ws_states[sb + int64_t(i0 + NG * r) * dv];
         }
         __syncthreads();  // the previous chunk is done with the prepared rows and the row buffers
-        load_prep<DK, true>(a.ws_prep + prep_base(a, brow, slot, h), Et, Qt, Kb, Tm, Pm, gam, tid);
-        float z[4], vv[4], ww[4];
+        load_prep<DK, true, kSeqThreads>(a.ws_prep + prep_base(a, brow, slot, h), Et, Qt, Kb, Tm, Pm, gam, tid);
+        float z[RR], vv[RR], ww[RR];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = i0 + 8 * r;
+        for (int r = 0; r < RR; ++r) {
+            const int i = i0 + NG * r;
             const bool live = i < L;
             const int64_t off = (row0 + int64_t(i) * a.H) * dv + j0 + jj;
             vv[r] = live ? load_as_f32(v, off) : 0.f;
@@ -379,44 +382,44 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dstate_kernel(BwdArgs a)
         __syncthreads();
         // X = Z - Et S and dU = Kb dS' + Pm^T dO
         {
-            float ax[4] = {0.f, 0.f, 0.f, 0.f}, au[4] = {0.f, 0.f, 0.f, 0.f};
+            float ax[RR] = {}, au[RR] = {};
 #pragma unroll 4
             for (int ch = 0; ch < DK; ++ch) {
                 const float sv = Ss[ch][jj], dsv = dSs[ch][jj];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    ax[r] += Et[i0 + 8 * r][ch] * sv;
-                    au[r] += Kb[i0 + 8 * r][ch] * dsv;
+                for (int r = 0; r < RR; ++r) {
+                    ax[r] += Et[i0 + NG * r][ch] * sv;
+                    au[r] += Kb[i0 + NG * r][ch] * dsv;
                 }
             }
 #pragma unroll 4
             for (int rr = 0; rr < CH; ++rr) {  // Pm is lower triangular: only rr >= i contributes
                 const float ov = dOs[rr][jj];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) au[r] += Pm[rr][i0 + 8 * r] * ov;
+                for (int r = 0; r < RR; ++r) au[r] += Pm[rr][i0 + NG * r] * ov;
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                Xs[i0 + 8 * r][jj] = z[r] - ax[r];
-                dUs[i0 + 8 * r][jj] = au[r];
+            for (int r = 0; r < RR; ++r) {
+                Xs[i0 + NG * r][jj] = z[r] - ax[r];
+                dUs[i0 + NG * r][jj] = au[r];
             }
         }
         __syncthreads();
         // U = Tm X,  dX = Tm^T dU
         {
-            float au[4] = {0.f, 0.f, 0.f, 0.f}, ad[4] = {0.f, 0.f, 0.f, 0.f};
+            float au[RR] = {}, ad[RR] = {};
 #pragma unroll 4
             for (int mm = 0; mm < CH; ++mm) {
                 const float xv = Xs[mm][jj], dv_ = dUs[mm][jj];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    au[r] += Tm[i0 + 8 * r][mm] * xv;
-                    ad[r] += Tm[mm][i0 + 8 * r] * dv_;
+                for (int r = 0; r < RR; ++r) {
+                    au[r] += Tm[i0 + NG * r][mm] * xv;
+                    ad[r] += Tm[mm][i0 + NG * r] * dv_;
                 }
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = i0 + 8 * r;
+            for (int r = 0; r < RR; ++r) {
+                const int i = i0 + NG * r;
                 Us[i][jj] = au[r];
                 dXs[i][jj] = i < L ? ad[r] : 0.f;
                 if (i < L) {
@@ -433,19 +436,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dstate_kernel(BwdArgs a)
         {
             float acc[RS];
 #pragma unroll
-            for (int r = 0; r < RS; ++r) acc[r] = gam[i0 + 8 * r] * dSs[i0 + 8 * r][jj];
+            for (int r = 0; r < RS; ++r) acc[r] = gam[i0 + NG * r] * dSs[i0 + NG * r][jj];
             for (int i = 0; i < L; ++i) {
                 const float ov = dOs[i][jj], xv = dXs[i][jj];
 #pragma unroll
-                for (int r = 0; r < RS; ++r) acc[r] += Qt[i][i0 + 8 * r] * ov - Et[i][i0 + 8 * r] * xv;
+                for (int r = 0; r < RS; ++r) acc[r] += Qt[i][i0 + NG * r] * ov - Et[i][i0 + NG * r] * xv;
             }
 #pragma unroll
-            for (int r = 0; r < RS; ++r) dSs[i0 + 8 * r][jj] = acc[r];
+            for (int r = 0; r < RS; ++r) dSs[i0 + NG * r][jj] = acc[r];
         }
     }
     if (a.d_initial_state)
 #pragma unroll
-        for (int r = 0; r < RS; ++r) a.d_initial_state[s_off + int64_t(i0 + 8 * r) * dv] = dSs[i0 + 8 * r][jj];
+        for (int r = 0; r < RS; ++r) a.d_initial_state[s_off + int64_t(i0 + NG * r) * dv] = dSs[i0 + NG * r][jj];
 }
 
 // ---------------------------------------------------------------------------
@@ -620,12 +623,12 @@ hipError_t launch_chain(const BwdArgs& a, hipStream_t stream)
         hipLaunchKernelGGL((bwd_prep_kernel<T, DK>), dim3(unsigned(chunks)), dim3(kBwdThreads), 0, stream, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((bwd_states_kernel<T, DK>), dim3(unsigned(chains)), dim3(kBwdThreads), 0, stream, a);
+        hipLaunchKernelGGL((bwd_states_kernel<T, DK>), dim3(unsigned(chains)), dim3(kSeqThreads), 0, stream, a);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     // runs for T = 0 as well: it passes the final-state gradient through
-    hipLaunchKernelGGL((bwd_dstate_kernel<T, DK>), dim3(unsigned(chains)), dim3(kBwdThreads), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dstate_kernel<T, DK>), dim3(unsigned(chains)), dim3(kSeqThreads), 0, stream, a);
     return hipGetLastError();
 }
 
