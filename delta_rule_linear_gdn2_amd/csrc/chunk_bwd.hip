@@ -56,6 +56,19 @@ constexpr int NG = kSeqThreads / kTile;  // lane groups of the sequential kernel
 constexpr int RR = CH / NG;              // chunk rows per thread
 static_assert(kBwdThreads == 8 * kTile && CH == 32 && CH % NG == 0, "thread layouts below");
 
+// XCD-aware block order: workgroups that read the same data (the channel
+// blocks of one chunk, the value tiles of one chain) get the same blockIdx
+// mod 8, so they run on one XCD and share its L2.  Group `group` member
+// `member` of G is block ((group / 8) * G + member) * 8 + group % 8; the grid
+// is padded to a multiple of 8 G and blocks past the last group exit.
+__device__ __forceinline__ void xcd_group(int64_t bid, int G, int64_t& group, int& member)
+{
+    const int64_t q = bid >> 3;
+    member = int(q % G);
+    group = (q / G) * 8 + (bid & 7);
+}
+__host__ __device__ inline int64_t xcd_grid(int64_t groups, int G) { return (groups + 7) / 8 * 8 * G; }
+
 __device__ __forceinline__ int64_t slot_of(const BwdArgs& a, int n, int64_t bos, int m)
 {
     return a.cu_seqlens ? (bos + int64_t(m) * CH) / CH + n : int64_t(m);
@@ -100,6 +113,22 @@ __device__ bool chunk_of_slot(const BwdArgs& a, int64_t row, int64_t slot, int& 
     if (slot < first) return false;
     m = int(slot - first);
     return bos + int64_t(m) * CH < eos && slot_of(a, n, bos, m) == slot;
+}
+
+// Four consecutive values as FP32 (16-byte FP32 or 8-byte bf16 loads).
+__device__ __forceinline__ float4 load4(const float* p, int64_t i) { return *reinterpret_cast<const float4*>(p + i); }
+__device__ __forceinline__ float4 load4(const bf16raw* p, int64_t i)
+{
+    const uint2 u = *reinterpret_cast<const uint2*>(p + i);
+    return make_float4(bf16_to_f32(bf16raw(u.x & 0xffffu)), bf16_to_f32(bf16raw(u.x >> 16)),
+                       bf16_to_f32(bf16raw(u.y & 0xffffu)), bf16_to_f32(bf16raw(u.y >> 16)));
+}
+__device__ __forceinline__ void st4(float* row, int j, float4 v)
+{
+    row[j] = v.x;
+    row[j + 1] = v.y;
+    row[j + 2] = v.z;
+    row[j + 3] = v.w;
 }
 
 // The forward quantities of one chunk.  Rows are padded by one float: lanes
@@ -213,23 +242,47 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdArgs a)
 // with i0 = c0 = tid / 32.  The rows a wavefront reads at one time are two,
 // so the row operand is a broadcast and the column operand is contiguous.
 
-// Prepared rows of one chunk into LDS (rows past the chunk are zero in the block).
+// Prepared rows of one chunk into LDS (rows past the chunk are zero in the
+// block).  Sixteen-byte loads, all issued before the first LDS store so that
+// they are in flight together.
 template <int DK, bool kQ, int NT>
 __device__ __forceinline__ void load_prep(const float* src, float (*Et)[DK + 1], float (*Qt)[DK + 1],
                                           float (*Kb)[DK + 1], float (*Tm)[CH + 1], float (*Pm)[CH + 1],
                                           float* gam, int tid)
 {
-    for (int i2 = tid; i2 < CH * CH; i2 += NT) {
-        Tm[i2 / CH][i2 % CH] = src[kPrepT + i2];
-        if (kQ) Pm[i2 / CH][i2 % CH] = src[kPrepP + i2];
+    constexpr int QR = CH * DK / 4;              // quads per row array
+    constexpr int NQ = (QR + NT - 1) / NT;       // quads per thread and array
+    constexpr int QT = CH * CH / 4;              // quads of Tm (and Pm)
+    static_assert(QT <= NT && DK / 4 <= NT, "one quad of Tm, Pm and gamma per thread at most");
+    const float4* s4 = reinterpret_cast<const float4*>(src);
+    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 ve[NQ], vq[NQ], vk[NQ], vt, vp, vg;
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd) {
+        const int i4 = tid + NT * qd;
+        const bool in = i4 < QR;
+        ve[qd] = in ? s4[kPrepE / 4 + i4] : z4;
+        vq[qd] = in && kQ ? s4[kPrepE / 4 + QR + i4] : z4;
+        vk[qd] = in ? s4[kPrepE / 4 + 2 * QR + i4] : z4;
     }
-    for (int i2 = tid; i2 < CH * DK; i2 += NT) {
-        const int i = i2 / DK, ch = i2 % DK;
-        Et[i][ch] = src[kPrepE + i2];
-        if (kQ) Qt[i][ch] = src[kPrepE + CH * DK + i2];
-        Kb[i][ch] = src[kPrepE + 2 * CH * DK + i2];
+    vt = tid < QT ? s4[kPrepT / 4 + tid] : z4;
+    vp = tid < QT && kQ ? s4[kPrepP / 4 + tid] : z4;
+    vg = tid < DK / 4 ? s4[kPrepE / 4 + 3 * QR + tid] : z4;
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd) {
+        const int i4 = tid + NT * qd;
+        if (i4 >= QR) continue;
+        const int i = i4 / (DK / 4), c = (i4 % (DK / 4)) * 4;
+        st4(Et[i], c, ve[qd]);
+        if (kQ) st4(Qt[i], c, vq[qd]);
+        st4(Kb[i], c, vk[qd]);
     }
-    for (int ch = tid; ch < DK; ch += NT) gam[ch] = src[kPrepE + 3 * CH * DK + ch];
+    if (tid < QT) {
+        const int i = tid / (CH / 4), c = (tid % (CH / 4)) * 4;
+        st4(Tm[i], c, vt);
+        if (kQ) st4(Pm[i], c, vp);
+    }
+    if (tid < DK / 4) st4(gam, 4 * tid, vg);
 }
 
 // ---------------------------------------------------------------------------
@@ -247,7 +300,11 @@ __global__ __launch_bounds__(kSeqThreads) void bwd_states_kernel(BwdArgs a)
     const int tid = threadIdx.x;
     const int jj = tid % kTile, i0 = tid / kTile;
     const int ntiles = a.dv_ / kTile;
-    const int chain = blockIdx.x / ntiles, tile = blockIdx.x % ntiles;
+    int64_t chain64;
+    int tile;
+    xcd_group(blockIdx.x, ntiles, chain64, tile);
+    if (chain64 >= int64_t(a.N) * a.H) return;
+    const int chain = int(chain64);
     const int n = chain / a.H, h = chain % a.H;
     const int j0 = tile * kTile;
     const int64_t dv = a.dv_;
@@ -337,7 +394,11 @@ __global__ __launch_bounds__(kSeqThreads) void bwd_dstate_kernel(BwdArgs a)
     const int tid = threadIdx.x;
     const int jj = tid % kTile, i0 = tid / kTile;
     const int ntiles = a.dv_ / kTile;
-    const int chain = blockIdx.x / ntiles, tile = blockIdx.x % ntiles;
+    int64_t chain64;
+    int tile;
+    xcd_group(blockIdx.x, ntiles, chain64, tile);
+    if (chain64 >= int64_t(a.N) * a.H) return;
+    const int chain = int(chain64);
     const int n = chain / a.H, h = chain % a.H;
     const int j0 = tile * kTile;
     const int64_t dv = a.dv_;
@@ -474,9 +535,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_keys_kernel(BwdArgs a)
     const int tid = threadIdx.x;
     const int col = tid % 32, i0 = tid / 32;
     constexpr int nblk = DK / CB;
-    int64_t idx = blockIdx.x;
-    const int cblk = int(idx % nblk);
-    idx /= nblk;
+    int64_t idx;
+    int cblk;
+    xcd_group(blockIdx.x, nblk, idx, cblk);
+    if (idx >= int64_t(a.B) * a.slots * a.H) return;
     const int h = int(idx % a.H);
     idx /= a.H;
     const int64_t slot = idx % a.slots, row = idx / a.slots;
@@ -516,16 +578,34 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_keys_kernel(BwdArgs a)
     float xe[4] = {0.f, 0.f, 0.f, 0.f}, xq[4] = {0.f, 0.f, 0.f, 0.f}, xk[4] = {0.f, 0.f, 0.f, 0.f};
     float xr = 0.f;
     for (int jh = 0; jh < DV; jh += DH) {
-        for (int i2 = tid; i2 < CH * DH; i2 += kBwdThreads) {
-            const int i = i2 / DH, j = i2 % DH;
+        // four consecutive columns per thread; every load of the pass is
+        // issued before the first LDS store, so they are all in flight together
+        constexpr int NQ = CH * DH / 4 / kBwdThreads;  // quads per thread
+        static_assert(NQ >= 1 && CH * DH % (4 * kBwdThreads) == 0, "staging layout");
+        float4 vu[NQ], vx[NQ], vo[NQ], vs[NQ], vd[NQ];
+#pragma unroll
+        for (int qd = 0; qd < NQ; ++qd) {
+            const int i4 = tid + kBwdThreads * qd;
+            const int i = i4 / (DH / 4), j = (i4 % (DH / 4)) * 4;
             const bool live = i < L;
             const int64_t off = (row0 + int64_t(i) * a.H) * DV + jh + j;
-            Us[i][j] = live ? a.ws_u[off] : 0.f;
-            dXs[i][j] = live ? a.ws_dx[off] : 0.f;
-            dOs[i][j] = live ? load_as_f32(dO, off) : 0.f;
+            const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+            vu[qd] = live ? load4(a.ws_u, off) : z4;
+            vx[qd] = live ? load4(a.ws_dx, off) : z4;
+            vo[qd] = live ? load4(dO, off) : z4;
             const int64_t soff = sbase + int64_t(c0 + i) * DV + jh + j;  // i doubles as the channel (CB == CH)
-            Sb[i][j] = a.ws_states[soff];
-            dSb[i][j] = a.ws_dstates[soff];
+            vs[qd] = load4(a.ws_states, soff);
+            vd[qd] = load4(a.ws_dstates, soff);
+        }
+#pragma unroll
+        for (int qd = 0; qd < NQ; ++qd) {
+            const int i4 = tid + kBwdThreads * qd;
+            const int i = i4 / (DH / 4), j = (i4 % (DH / 4)) * 4;
+            st4(Us[i], j, vu[qd]);
+            st4(dXs[i], j, vx[qd]);
+            st4(dOs[i], j, vo[qd]);
+            st4(Sb[i], j, vs[qd]);
+            st4(dSb[i], j, vd[qd]);
         }
         __syncthreads();
 #pragma unroll 4
@@ -616,9 +696,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_keys_kernel(BwdArgs a)
 template <typename T, int DK>
 hipError_t launch_chain(const BwdArgs& a, hipStream_t stream)
 {
-    const int64_t chains = int64_t(a.N) * a.H * (a.dv_ / kTile);
+    const int64_t chains = xcd_grid(int64_t(a.N) * a.H, a.dv_ / kTile);
     const int64_t chunks = int64_t(a.B) * a.slots * a.H;
-    if (chains > 0x7fffffff || chunks * (DK / 32) > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (chains > 0x7fffffff || xcd_grid(chunks, DK / 32) > 0x7fffffff) return hipErrorInvalidConfiguration;
     if (chunks > 0) {
         hipLaunchKernelGGL((bwd_prep_kernel<T, DK>), dim3(unsigned(chunks)), dim3(kBwdThreads), 0, stream, a);
         hipError_t e = hipGetLastError();
@@ -635,8 +715,9 @@ hipError_t launch_chain(const BwdArgs& a, hipStream_t stream)
 template <typename T, int DK, int DV>
 hipError_t launch_keys(const BwdArgs& a, hipStream_t stream)
 {
-    const int64_t blocks = int64_t(a.B) * a.slots * a.H * (DK / 32);
-    if (blocks == 0) return hipSuccess;
+    const int64_t groups = int64_t(a.B) * a.slots * a.H;
+    if (groups == 0) return hipSuccess;
+    const int64_t blocks = xcd_grid(groups, DK / 32);
     hipLaunchKernelGGL((bwd_keys_kernel<T, DK, DV>), dim3(unsigned(blocks)), dim3(kBwdThreads), 0, stream, a);
     return hipGetLastError();
 }
