@@ -394,6 +394,7 @@ def run_configs(args):
         row = {"report": "config", "workload": f"recurrent_fwd N={N} H={H} d=128 bf16 T={T}",
                "us_per_call": kern_ms * 1e3, "tokens_per_s": N * T / (kern_ms / 1e3),
                "GBps": nbytes / (kern_ms / 1e3) / 1e9, "hbm_frac": nbytes / (kern_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
+               "kernel": "recurrent" if T < 24 else "chunkwise (long calls are dispatched to it)",
                "timing": f"median of {args.steps} launches after {args.warmup}"}
         log(f"recurrent_fwd T={T}: {row['us_per_call']:.1f} us, {row['tokens_per_s'] / 1e6:.2f} M tokens/s, "
             f"{row['hbm_frac'] * 100:.1f}% HBM")

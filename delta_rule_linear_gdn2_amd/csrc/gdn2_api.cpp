@@ -14,6 +14,10 @@ namespace {
 
 constexpr int32_t kVersion = 10000;  // 1.0.0
 
+// Tokens per sequence from which gdn2_recurrent_fwd runs the chunkwise kernel
+// (measured crossover on MI355X at N = 256, H = 16, d = 128: about 20).
+constexpr int32_t kRecurrentChunkMinT = 24;
+
 bool supported_head(int32_t d) { return d == 32 || d == 64 || d == 128; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -163,6 +167,17 @@ gdn2_status recurrent(const void* q, const void* k, const void* v, const float* 
         if (overlap(ss, in)) return GDN2_ERR_ALIAS;
     if (T == 0) return GDN2_OK;  // nothing to do: the state is unchanged
 
+    // From about 20 tokens per sequence the chunkwise matrix-core kernel is
+    // faster (the same mathematics, the [N, T, H, .] inputs taken as a batch,
+    // the state updated in place): hand the call to it where it applies.
+    const bool bf16 = dtype == GDN2_DTYPE_BF16;
+    if (T >= kRecurrentChunkMinT) {
+        gdn2::ChunkArgs c{q, k, v, alpha, b, w, state, state, o, nullptr, N, T, H, dk, dv, N, device_cus(), gates};
+        if (gdn2::chunk_fwd_mfma_supported(c, bf16)) {
+            const hipError_t e = gdn2::launch_chunk_fwd_mfma(c, static_cast<hipStream_t>(stream));
+            return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+        }
+    }
     gdn2::StepArgs a{q, k, v, alpha, b, w, state, o, N, H, dk, dv, gates, T};
     const hipError_t e = gdn2::launch_recurrent(a, dtype == GDN2_DTYPE_BF16, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;

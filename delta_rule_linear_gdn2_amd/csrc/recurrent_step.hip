@@ -5,7 +5,8 @@
 // the updated state (Gated DeltaNet-2 analysis, iplexlaw.co.kr, "Independent
 // decisions on two axes") are fused, and the FP32 state stays in registers
 // across the call's tokens: it is streamed from HBM once and written back
-// once per call.  With ae = alpha (.) e and aq = alpha (.) q:
+// once per call.  alpha is clamped to [2^-15, 1] as in the chunkwise kernels.
+// With ae = alpha (.) e and aq = alpha (.) q:
 //     r = S^T ae,  s = S^T aq,  u = z - r,  o = s + (k . q) u,
 //     S <- Diag(alpha) S + k u^T
 // (o = S_new^T q expands to S^T (alpha (.) q) + u (k^T q)).
@@ -42,7 +43,7 @@ __device__ __forceinline__ void load_token(TokenRegs& x, const StepArgs& a, int6
         x.q = load_as_f32(static_cast<const T*>(a.q), row * DK + tid);
         x.k = load_as_f32(static_cast<const T*>(a.k), row * DK + tid);
         x.b = load_as_f32(static_cast<const T*>(a.b), sb ? row : row * DK + tid);
-        x.a = a.alpha[sa ? row : row * DK + tid];
+        x.a = __builtin_amdgcn_fmed3f(a.alpha[sa ? row : row * DK + tid], 0x1p-15f, 1.0f);  // as the chunk kernels
     }
     if (tid < DV) {
         x.v = load_as_f32(static_cast<const T*>(a.v), row * DV + tid);

@@ -27,9 +27,8 @@
  *    bf16 inputs feed bf16 matrix-core products with FP32 accumulation.
  *  - Inputs are gate VALUES, not logits: 0 <= alpha <= 1; b, w are used as
  *    given (no clamp, so an erase gate in [0, 2] works).  There is no query
- *    scale: callers pre-scale q.  The chunkwise entry points clamp alpha per
- *    token and key channel to [2^-15, 1] (alpha below 2^-15 acts as 2^-15);
- *    the recurrent step uses alpha as given.
+ *    scale: callers pre-scale q.  Every entry point clamps alpha per token
+ *    and key channel to [2^-15, 1] (alpha below 2^-15 acts as 2^-15).
  *  - Pointers to q, k, v, b, w, o, alpha and states must be 16-byte aligned.
  *  - Calls enqueue work on `stream` (a hipStream_t; NULL = the null stream)
  *    and return without synchronising.  Argument errors are reported
@@ -180,9 +179,11 @@ gdn2_status gdn2_recurrent_step_gates(const void* q, const void* k, const void* 
  * recurrence token by token, each (sequence, head) state read once and
  * written once, in place.  The same mathematics as gdn2_chunk_fwd ("DeltaNet"
  * entity trail at mindpattern.ai, finding "You Could Have Come Up With Kimi
- * Delta Attention"), so a final state of gdn2_chunk_fwd continues here; alpha
- * is used as given (no clamp).  Cost grows with T (one token at a time):
- * meant for T up to a few chunks, with gdn2_chunk_fwd for long inputs.
+ * Delta Attention"), so a final state of gdn2_chunk_fwd continues here.  For
+ * T >= 24 with bf16 inputs, dk = 128 and dv a multiple of 64 the call runs the
+ * chunkwise matrix-core kernel on the [N, T, H, .] inputs (the same
+ * mathematics; it is faster from about 20 tokens on); otherwise one token at
+ * a time with the state in registers.
  *
  *   q, k, b : [N, T, H, dk] dtype     v, w, o : [N, T, H, dv] dtype
  *   alpha   : [N, T, H, dk] FP32
