@@ -242,6 +242,41 @@ def make(name: str, gate_mode: str = "gdn2", seed: int | None = None, **override
     return out
 
 
+def device_token_tensors(lead: tuple, H: int, dk: int, dv: int, dtype: str, seed: int, device="cuda",
+                         tokens_per_draw: int = 65536) -> dict:
+    """q, k, v, alpha, b, w of leading shape ``lead`` drawn on ``device``.
+
+    For sizes too large to draw on the host (tens of GB): torch's seeded
+    generator on the device, with the distributions of ``token_tensors`` (the
+    values differ from it).  Tests that use it overwrite the chains they check
+    with host inputs from ``token_tensors``, so every value the oracle sees
+    comes from the host recipe.  q, k, v, b, w are rounded to ``dtype``; alpha
+    is FP32.  Drawn ``tokens_per_draw`` tokens at a time (bounded scratch).
+    """
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    widths = dict(q=dk, k=dk, v=dv, alpha=dk, b=dk, w=dv)
+    ntok = int(np.prod(lead)) if lead else 1
+    out = {n: torch.empty((ntok, H, d), dtype=torch.float32 if n == "alpha" else tdt, device=device)
+           for n, d in widths.items()}
+    for t0 in range(0, ntok, tokens_per_draw):
+        t1 = min(ntok, t0 + tokens_per_draw)
+        for n, d in widths.items():
+            x = torch.randn((t1 - t0, H, d), generator=g, device=device)
+            if n in ("q", "k"):
+                x /= x.norm(dim=-1, keepdim=True).clamp_min(1e-12)
+            elif n == "alpha":
+                x = torch.sigmoid(x + 3.0)
+            elif n in ("b", "w"):
+                x = torch.sigmoid(x)
+            out[n][t0:t1] = x
+            del x
+    return {n: t.view(tuple(lead) + (H, widths[n])) for n, t in out.items()}
+
+
 def to_torch(arr: np.ndarray, dtype: str, device="cpu"):
     """float32 numpy array (values exact in ``dtype``) -> torch tensor on ``device``."""
     import torch
