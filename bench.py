@@ -235,6 +235,43 @@ def bench_decode(args):
                 achieved=nbytes / (step_ms / 1e3) / 1e9, bytes=nbytes)
 
 
+def bench_decode_flushed(args, reps=20, warm=3):
+    """decode_b256 one step at a time, each after a 1 GiB device write that
+    evicts the state from the 256 MB Infinity Cache: the cold-cache figure
+    beside the 64-step in-place headline."""
+    import torch
+
+    from delta_rule_linear_gdn2_amd import binding
+    from delta_rule_linear_gdn2_amd import workloads as W
+
+    x = W.make("decode_b256")
+    wl = x["workload"]
+    steps_in = x["q"].shape[0]
+    N, H, dk = x["q"].shape[1:]
+    dv = x["v"].shape[-1]
+    slices = [to_dev({n: x[n][t] for n in NAMES}, wl.dtype) for t in range(steps_in)]
+    state = torch.from_numpy(x["initial_state"]).cuda()
+    out = torch.empty((N, H, dv), dtype=slices[0]["q"].dtype, device="cuda")
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for i in range(warm + reps):
+        flush.fill_(float(i))
+        s = slices[i % steps_in]
+        e0.record()
+        binding.gdn2_recurrent_step(s["q"], s["k"], s["v"], s["alpha"], s["b"], s["w"], state, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= warm:
+            times.append(e0.elapsed_time(e1))
+    step_ms = float(np.median(times))
+    state_bytes = 2 * N * H * dk * dv * 4
+    nbytes = step_bytes(N, H, dk, dv)
+    log(f"decode flushed: {step_ms * 1e3:.1f} us/step, state {state_bytes / (step_ms / 1e3) / 1e9:.0f} GB/s")
+    return dict(step_ms=step_ms, state_gbps=state_bytes / (step_ms / 1e3) / 1e9,
+                achieved=nbytes / (step_ms / 1e3) / 1e9, timing=f"median of {reps} single steps after {warm}")
+
+
 def cpu_baseline(x, wl, chains_rows=4):
     """The FP64 oracle on the first ``chains_rows`` batch rows (all heads, full length)."""
     import oracle
@@ -375,8 +412,12 @@ def run_configs(args):
             del sets
     dec = bench_decode(args)
     print(json.dumps({"report": "config", "workload": "decode_b256", "us_per_step": dec["step_ms"] * 1e3,
-                      "state_GBps": dec["state_gbps"], "hbm_frac": dec["achieved"] / HBM_PEAK_GBPS}),
-          flush=True)
+                      "state_GBps": dec["state_gbps"], "hbm_frac": dec["achieved"] / HBM_PEAK_GBPS,
+                      "timing": "64 consecutive in-place steps, per step"}), flush=True)
+    fl = bench_decode_flushed(args)
+    print(json.dumps({"report": "config", "workload": "decode_b256, Infinity Cache flushed before each step",
+                      "us_per_step": fl["step_ms"] * 1e3, "state_GBps": fl["state_gbps"],
+                      "hbm_frac": fl["achieved"] / HBM_PEAK_GBPS, "timing": fl["timing"]}), flush=True)
     # several tokens per sequence in one recurrent call (verification steps, short prompts)
     for T in (4, 16, 64):
         N, H, dk, dv = 256, 16, 128, 128

@@ -16,13 +16,18 @@ constexpr float kLog2AlphaFloor = -15.0f;
 
 __device__ __forceinline__ float bf16_to_f32(bf16raw x) { return __uint_as_float(uint32_t(x) << 16); }
 
-// Round to nearest even; NaN stays NaN.
-__device__ __forceinline__ bf16raw f32_to_bf16(float f)
+// Round to nearest even (gfx950's bf16 conversion instruction, which rounds
+// as the mode register says: nearest even by default); NaN stays NaN.
+__device__ __forceinline__ bf16raw f32_to_bf16(float f) { return __builtin_bit_cast(bf16raw, static_cast<__bf16>(f)); }
+
+// Two values packed as one 32-bit word, the first in the low half.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return bf16raw((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return bf16raw(u >> 16);
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    bf16x2_t v;
+    v[0] = static_cast<__bf16>(a);
+    v[1] = static_cast<__bf16>(b);
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ float load_as_f32(const float* p, int64_t i) { return p[i]; }

@@ -80,7 +80,7 @@ __device__ __forceinline__ void load_ch(const float* p, int64_t i, float* v, int
 __device__ __forceinline__ void store_ch(bf16raw* p, int64_t i, const float* v, int n)
 {
     if (n == 2)
-        *reinterpret_cast<uint32_t*>(p + i) = uint32_t(f32_to_bf16(v[0])) | (uint32_t(f32_to_bf16(v[1])) << 16);
+        *reinterpret_cast<uint32_t*>(p + i) = f32x2_to_bf16x2(v[0], v[1]);
     else
         p[i] = f32_to_bf16(v[0]);
 }
@@ -329,7 +329,7 @@ __device__ __forceinline__ void store8(bf16raw* p, int64_t i, const float* v)
 {
     uint32_t w[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = uint32_t(f32_to_bf16(v[2 * j])) | (uint32_t(f32_to_bf16(v[2 * j + 1])) << 16);
+    for (int j = 0; j < 4; ++j) w[j] = f32x2_to_bf16x2(v[2 * j], v[2 * j + 1]);
     *reinterpret_cast<uint4*>(p + i) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 __device__ __forceinline__ void store8(float* p, int64_t i, const float* v)
