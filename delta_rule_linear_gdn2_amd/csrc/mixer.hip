@@ -338,6 +338,249 @@ __device__ __forceinline__ void store8(float* p, int64_t i, const float* v)
     *reinterpret_cast<float4*>(p + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
 
+// ---------------------------------------------------------------------------
+// Prologue for filters of at most four taps (the usual short convolution): one
+// wavefront per (output, batch row, group of heads, run of kRun tokens).  An
+// output is one of q, k, v (convolution, SiLU; L2 norm for q and k) or b, w
+// (sigmoid).  A lane takes eight channels (16-byte bf16 accesses) and a head
+// D / 8 lanes, so one load of a wavefront is 64 / (D / 8) adjacent heads of one
+// token, contiguous in memory; every lane walks the same tokens, so sequence
+// starts of packed input are the same for the whole wavefront.  The three
+// inputs before the current token stay in registers; tokens go kStep at a time
+// with the next step's loads in flight.
+
+constexpr int kRun = 64;  // tokens per wavefront
+constexpr int kStep = 4;  // tokens per unrolled step
+constexpr int kWin = 3;   // window rows: the inputs before the current token, for up to four taps
+
+// Eight channels of one token row, as loaded (bf16 stays packed until used).
+template <typename T>
+struct Raw8;
+template <>
+struct Raw8<bf16raw> {
+    uint4 u;
+    __device__ void load(const bf16raw* p, int64_t i) { u = *reinterpret_cast<const uint4*>(p + i); }
+    __device__ void get(float* v) const
+    {
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = __uint_as_float(w[j] << 16);
+            v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+        }
+    }
+};
+template <>
+struct Raw8<float> {
+    float4 a, b;
+    __device__ void load(const float* p, int64_t i)
+    {
+        a = *reinterpret_cast<const float4*>(p + i);
+        b = *reinterpret_cast<const float4*>(p + i + 4);
+    }
+    __device__ void get(float* v) const
+    {
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+};
+
+// Sigmoid with the hardware reciprocal (about one ulp; the outputs are FP32 or bf16).
+__device__ __forceinline__ float sigmoid_r(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+
+// Where wavefront wid of an output of head width D sits; false past the last.
+template <int D>
+struct PathPos {
+    static constexpr int LPH = D / 8;      // lanes per head
+    static constexpr int HPW = 64 / LPH;   // heads per wavefront
+    int h, c0;
+    int64_t brow, t_begin, t_end;
+    __device__ bool init(const MixerArgs& a, int64_t wid, int lane)
+    {
+        const int ng = (a.H + HPW - 1) / HPW;
+        const int64_t nruns = (int64_t(a.T) + kRun - 1) / kRun;
+        if (wid >= int64_t(a.B) * nruns * ng) return false;
+        const int g = int(wid % ng);
+        const int64_t run = (wid / ng) % nruns;
+        brow = wid / ng / nruns;
+        h = g * HPW + lane / LPH;
+        c0 = (lane % LPH) * 8;
+        t_begin = run * kRun;
+        t_end = t_begin + kRun < a.T ? t_begin + kRun : a.T;
+        return h < a.H;  // lanes past the last head stop (they share no reduction with live lanes)
+    }
+};
+
+template <typename T, int D>
+__device__ void gate_path(const T* x, T* y, const MixerArgs& a, int64_t wid, int lane)
+{
+    PathPos<D> p;
+    if (!p.init(a, wid, lane)) return;
+    const int64_t stride = int64_t(a.H) * D;  // elements per token
+    const int64_t base = ((p.brow * a.T + p.t_begin) * a.H + p.h) * D + p.c0;
+    const int n = int(p.t_end - p.t_begin);
+    for (int t0 = 0; t0 < n; t0 += 8) {
+        Raw8<T> r[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) r[j].load(x, base + int64_t(t0 + j < n ? t0 + j : n - 1) * stride);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (t0 + j < n) {
+                float v[8];
+                r[j].get(v);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) v[c] = sigmoid_r(v[c]);
+                store8(y, base + int64_t(t0 + j) * stride, v);
+            }
+        }
+    }
+}
+
+// Convolution output KIND 0 (q: SiLU, L2 norm, q_scale), 1 (k: SiLU, L2 norm)
+// or 2 (v: SiLU) of head width D; its convolution-state channels start at
+// state_ch0.
+template <typename T, int D, int KIND>
+__device__ void conv_path(const T* x, const float* wgt, T* y, const MixerArgs& a, int state_ch0, int64_t wid,
+                          int lane)
+{
+    PathPos<D> p;
+    if (!p.init(a, wid, lane)) return;
+    const int K = a.K;
+    const int64_t stride = int64_t(a.H) * D;
+    const int64_t nch = int64_t(a.H) * (2 * a.dk + a.dv);
+    const int64_t row_base = (p.brow * a.T * a.H + p.h) * D + p.c0;  // token 0 of this row and head
+    // wt[j]: the taps for the input kWin - j tokens before the current one (j = kWin: the current token);
+    // zero for the j < 4 - K that a shorter filter does not reach
+    float wt[kWin + 1][8];
+#pragma unroll
+    for (int j = 0; j <= kWin; ++j)
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            wt[j][c] = j >= kWin + 1 - K ? wgt[(int64_t(p.h) * D + p.c0 + c) * K + (j - (kWin + 1 - K))] : 0.f;
+
+    int n;
+    int64_t bos, eos;
+    if (a.cu_seqlens) {
+        n = seq_of(a.cu_seqlens, a.N, a.T, p.t_begin);
+        int64_t b2;
+        sequence_bounds(a.cu_seqlens, n, a.T, bos, eos, b2);
+    } else {
+        n = int(p.brow);
+        bos = 0;
+        eos = a.T;
+    }
+    // xr[j] for j < kWin: the input kWin - j tokens before the step's token 0;
+    // xr[kWin + i]: the step's token i
+    float xr[kWin + kStep][8];
+    // the K - 1 inputs before token t (of sequence n from bos) into xr[j0 .. j0 + kWin - 1]
+    auto window = [&](int64_t t, float (*w)[8]) {
+#pragma unroll
+        for (int j = 0; j < kWin; ++j) {
+            const int64_t s = t - kWin + j;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) w[j][c] = 0.f;
+            if (j < kWin + 1 - K) continue;  // beyond the filter: stays zero
+            if (s >= bos) {
+                Raw8<T> r;
+                r.load(x, row_base + s * stride);
+                r.get(w[j]);
+            } else if (a.conv_state_in) {
+                const int64_t js = (K - 1) - (bos - s);  // position in the state, oldest first
+                if (js >= 0) {
+#pragma unroll
+                    for (int c = 0; c < 8; ++c)
+                        w[j][c] = a.conv_state_in[(int64_t(n) * nch + state_ch0 + int64_t(p.h) * D + p.c0 + c) * (K - 1) + js];
+                }
+            }
+        }
+    };
+    window(p.t_begin, xr);
+
+    Raw8<T> nx[kStep];
+    auto load_step = [&](int64_t t0) {
+#pragma unroll
+        for (int i = 0; i < kStep; ++i) nx[i].load(x, row_base + (t0 + i < p.t_end ? t0 + i : p.t_end - 1) * stride);
+    };
+    load_step(p.t_begin);
+    for (int64_t t0 = p.t_begin; t0 < p.t_end; t0 += kStep) {
+#pragma unroll
+        for (int i = 0; i < kStep; ++i) nx[i].get(xr[kWin + i]);
+        if (t0 + kStep < p.t_end) load_step(t0 + kStep);
+#pragma unroll
+        for (int j = 0; j < kStep; ++j) {
+            const int64_t t = t0 + j;
+            if (t >= p.t_end) continue;
+            if (t >= eos) {  // the next non-empty sequence starts here (packed input only)
+                n = seq_of(a.cu_seqlens, a.N, a.T, t);
+                int64_t b2;
+                sequence_bounds(a.cu_seqlens, n, a.T, bos, eos, b2);
+                window(t, xr + j);  // rows j .. j + kWin - 1 hold tokens already used
+            }
+            float v[8];
+            float ss = 0.f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                float acc = 0.f;
+#pragma unroll
+                for (int i = 0; i <= kWin; ++i)
+                    if (i >= kWin + 1 - K) acc = fmaf(wt[i][c], xr[j + i][c], acc);
+                v[c] = acc * sigmoid_r(acc);
+                ss = fmaf(v[c], v[c], ss);
+            }
+            if (KIND < 2) {
+#pragma unroll
+                for (int off = PathPos<D>::LPH / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+                const float r = (KIND == 0 ? a.q_scale : 1.0f) * __builtin_amdgcn_rsqf(ss + a.eps_l2);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) v[c] *= r;
+            }
+            store8(y, row_base + t * stride, v);
+            if (a.conv_state_out && t == eos - 1 && K > 1) {
+                // the K - 1 inputs up to and including t, oldest first: rows j + 1 + m hold token t - 2 + m
+#pragma unroll
+                for (int m = 0; m < kWin; ++m) {
+                    const int js = m + K - 1 - kWin;
+                    if (js >= 0) {
+#pragma unroll
+                        for (int c = 0; c < 8; ++c)
+                            a.conv_state_out[(int64_t(n) * nch + state_ch0 + int64_t(p.h) * D + p.c0 + c) * (K - 1) + js] =
+                                xr[j + 1 + m][c];
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kWin; ++j)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) xr[j][c] = xr[kStep + j][c];
+    }
+}
+
+// blockIdx.y selects the output: 0 q, 1 k, 2 v, 3 b, 4 w.
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(kMixThreads) void mixer_prologue_short_kernel(MixerArgs a)
+{
+    const int lane = threadIdx.x % 64;
+    const int64_t wid = int64_t(blockIdx.x) * (kMixThreads / 64) + threadIdx.x / 64;
+    const int hk = a.H * DK;
+    switch (blockIdx.y) {
+        case 0:
+            conv_path<T, DK, 0>(static_cast<const T*>(a.xq), a.conv_q, static_cast<T*>(a.q), a, 0, wid, lane);
+            break;
+        case 1:
+            conv_path<T, DK, 1>(static_cast<const T*>(a.xk), a.conv_k, static_cast<T*>(a.k), a, hk, wid, lane);
+            break;
+        case 2:
+            conv_path<T, DV, 2>(static_cast<const T*>(a.xv), a.conv_v, static_cast<T*>(a.v), a, 2 * hk, wid, lane);
+            break;
+        case 3:
+            gate_path<T, DK>(static_cast<const T*>(a.b_logit), static_cast<T*>(a.b), a, wid, lane);
+            break;
+        default:
+            gate_path<T, DV>(static_cast<const T*>(a.w_logit), static_cast<T*>(a.w), a, wid, lane);
+            break;
+    }
+}
+
 // A group of DV / 8 lanes per row (eight channels each), 64 / (DV / 8) rows
 // per wavefront; the mean square is a reduction inside the lane group.
 template <typename T, int DV>
@@ -376,14 +619,25 @@ __global__ __launch_bounds__(kMixThreads) void mixer_epilogue_kernel(EpilogueArg
 template <typename T, int DK, int DV>
 hipError_t launch_pro(const MixerArgs& a, hipStream_t stream)
 {
+    if (a.K <= 4) {
+        // wavefronts of the output with the narrowest heads (the most head groups)
+        const int64_t nruns = (int64_t(a.T) + kRun - 1) / kRun;
+        const int hpw = 64 / ((DK < DV ? DK : DV) / 8);
+        const int64_t waves = int64_t(a.B) * nruns * ((a.H + hpw - 1) / hpw);
+        const int64_t blocks = (waves + 3) / 4;
+        if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+        if (blocks > 0) {
+            hipLaunchKernelGGL((mixer_prologue_short_kernel<T, DK, DV>), dim3(unsigned(blocks), 5), dim3(kMixThreads),
+                               0, stream, a);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    }
     const int64_t waves = int64_t(a.B) * ((a.T + kTokBlock - 1) / kTokBlock) * a.H;
     const int64_t blocks = (waves + 3) / 4;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    if (blocks > 0) {
-        if (a.K <= 4)
-            hipLaunchKernelGGL((mixer_prologue_kernel<T, DK, DV, 4>), dim3(unsigned(blocks)), dim3(kMixThreads), 0,
-                               stream, a);
-        else if (a.K <= 8)
+    if (blocks > 0 && a.K > 4) {
+        if (a.K <= 8)
             hipLaunchKernelGGL((mixer_prologue_kernel<T, DK, DV, 8>), dim3(unsigned(blocks)), dim3(kMixThreads), 0,
                                stream, a);
         else

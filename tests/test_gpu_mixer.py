@@ -79,7 +79,8 @@ def _compare(out, ref, dtype, what):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("dk,dv,K", [(32, 32, 4), (64, 128, 4), (128, 64, 2), (128, 128, 4), (64, 64, 1)])
+@pytest.mark.parametrize("dk,dv,K", [(32, 32, 4), (64, 128, 4), (128, 64, 2), (128, 128, 4), (64, 64, 1), (64, 32, 3),
+                                     (32, 64, 7), (128, 32, 16)])
 def test_prologue(dtype, dk, dv, K):
     x = _inputs(300 + dk + dv + K, B=2, T=37, H=3, dk=dk, dv=dv, K=K, dtype=dtype)
     _compare(_gpu_prologue(x, dtype, q_scale=0.125), _oracle_prologue(x, q_scale=0.125), dtype,
@@ -87,12 +88,14 @@ def test_prologue(dtype, dk, dv, K):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_prologue_packed(dtype):
+@pytest.mark.parametrize("K", [2, 4, 8])
+def test_prologue_packed(dtype, K):
     """Packed sequences: empty ones (state passed through), ones shorter than the
-    filter, and longer ones; the convolution restarts at each."""
-    lens = [0, 1, 2, 9, 0, 40, 3]
+    filter, and longer ones, some crossing the token runs of a wavefront; the
+    convolution restarts at each."""
+    lens = [0, 1, 2, 9, 0, 40, 3, 33, 1, 70]
     cu = W.cu_from_lengths(lens)
-    x = _inputs(320, B=1, T=int(cu[-1]), H=2, dk=64, dv=64, K=4, dtype=dtype, N=len(lens))
+    x = _inputs(320 + K, B=1, T=int(cu[-1]), H=2, dk=64, dv=64, K=K, dtype=dtype, N=len(lens))
     _compare(_gpu_prologue(x, dtype, cu=cu), _oracle_prologue(x, cu=cu), dtype, f"prologue packed {dtype}")
 
 
