@@ -35,7 +35,8 @@ __device__ __forceinline__ float wave_sum(float x)
     for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
     return x;
 }
-__device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// Sigmoid with the hardware reciprocal (about one ulp; the outputs are FP32 or bf16).
+__device__ __forceinline__ float sigmoid_f(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 __device__ __forceinline__ float silu_f(float x) { return x * sigmoid_f(x); }
 
 // Sequence of packed position t: the last n with cu[n] <= t (its sequence is
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(kMixThreads) void mixer_prologue_kernel(MixerArgs a
         }
         sq = wave_sum(sq);
         sk = wave_sum(sk);
-        const float rq = a.q_scale / sqrtf(sq + a.eps_l2), rk = 1.0f / sqrtf(sk + a.eps_l2);
+        const float rq = a.q_scale * __builtin_amdgcn_rsqf(sq + a.eps_l2), rk = __builtin_amdgcn_rsqf(sk + a.eps_l2);
         if (lq.live) {
             float o[CK], g[CK];
 #pragma unroll
@@ -384,9 +385,6 @@ struct Raw8<float> {
     }
 };
 
-// Sigmoid with the hardware reciprocal (about one ulp; the outputs are FP32 or bf16).
-__device__ __forceinline__ float sigmoid_r(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
-
 // Where wavefront wid of an output of head width D sits; false past the last.
 template <int D>
 struct PathPos {
@@ -428,7 +426,7 @@ __device__ void gate_path(const T* x, T* y, const MixerArgs& a, int64_t wid, int
                 float v[8];
                 r[j].get(v);
 #pragma unroll
-                for (int c = 0; c < 8; ++c) v[c] = sigmoid_r(v[c]);
+                for (int c = 0; c < 8; ++c) v[c] = sigmoid_f(v[c]);
                 store8(y, base + int64_t(t0 + j) * stride, v);
             }
         }
@@ -523,7 +521,7 @@ __device__ void conv_path(const T* x, const float* wgt, T* y, const MixerArgs& a
 #pragma unroll
                 for (int i = 0; i <= kWin; ++i)
                     if (i >= kWin + 1 - K) acc = fmaf(wt[i][c], xr[j + i][c], acc);
-                v[c] = acc * sigmoid_r(acc);
+                v[c] = acc * sigmoid_f(acc);
                 ss = fmaf(v[c], v[c], ss);
             }
             if (KIND < 2) {
@@ -605,7 +603,7 @@ __global__ __launch_bounds__(kMixThreads) void mixer_epilogue_kernel(EpilogueArg
     for (int c = 0; c < 8; ++c) ss += ov[c] * ov[c];
 #pragma unroll
     for (int off = G / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);  // within the row's lane group
-    const float rr = 1.0f / sqrtf(ss / DV + a.eps);
+    const float rr = __builtin_amdgcn_rsqf(ss * (1.0f / DV) + a.eps);
     if (!live) return;
     float out[8];
 #pragma unroll
