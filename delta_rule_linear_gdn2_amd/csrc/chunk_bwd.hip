@@ -48,6 +48,11 @@
 namespace gdn2 {
 namespace {
 
+// 2^x with the hardware exponential (about one ulp; results below 2^-126 flush
+// to zero, which only drops terms far below FP32 resolution: every factor here
+// is at most 1 and multiplies values of order one).
+__device__ __forceinline__ float pow2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 constexpr int kBwdThreads = 256;  // the parallel kernels
 constexpr int CH = kBwdChunk;
 constexpr int kTile = 32;          // value columns per workgroup of the sequential kernels
@@ -194,7 +199,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdArgs a)
         float acc_a = 0.f, acc_p = 0.f;
         if (j <= i && i < L) {
             for (int ch = 0; ch < DK; ++ch) {
-                const float kf = c.K[j][ch] * exp2f(c.G[i][ch] - c.G[j][ch]);
+                const float kf = c.K[j][ch] * pow2(c.G[i][ch] - c.G[j][ch]);
                 acc_a += c.E[i][ch] * kf;
                 acc_p += c.Q[i][ch] * kf;
             }
@@ -216,10 +221,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdArgs a)
     // absorb the decay into the row and column factors
     for (int i2 = tid; i2 < L * DK; i2 += kBwdThreads) {
         const int i = i2 / DK, ch = i2 % DK;
-        const float g = c.G[i][ch], up = exp2f(g);
+        const float g = c.G[i][ch], up = pow2(g);
         c.E[i][ch] *= up;
         c.Q[i][ch] *= up;
-        c.K[i][ch] *= exp2f(c.G[L - 1][ch] - g);
+        c.K[i][ch] *= pow2(c.G[L - 1][ch] - g);
     }
     __syncthreads();
     float* dst = a.ws_prep + prep_base(a, row, slot, h);
@@ -234,7 +239,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdArgs a)
         dst[kPrepE + CH * DK + i2] = c.Q[i][ch];
         dst[kPrepE + 2 * CH * DK + i2] = c.K[i][ch];
     }
-    for (int ch = tid; ch < DK; ch += kBwdThreads) dst[kPrepE + 3 * CH * DK + ch] = exp2f(c.G[L - 1][ch]);
+    for (int ch = tid; ch < DK; ch += kBwdThreads) dst[kPrepE + 3 * CH * DK + ch] = pow2(c.G[L - 1][ch]);
 }
 
 // Thread layout of the sequential kernels: lane column jj = tid % 32 of the
@@ -656,15 +661,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_keys_kernel(BwdArgs a)
         const float gi = Gb[i][cc];
         float de_a = 0.f, dq_p = 0.f, dk_ap = 0.f;
         for (int j = 0; j <= i; ++j) {
-            const float kf = kb[j][cc] * exp2f(gi - Gb[j][cc]);
+            const float kf = kb[j][cc] * pow2(gi - Gb[j][cc]);
             de_a += dA[i][j] * kf;  // dA is zero on the diagonal
             dq_p += dP[i][j] * kf;
         }
         for (int rr = i; rr < L; ++rr) {
-            const float f = exp2f(Gb[rr][cc] - gi);
+            const float f = pow2(Gb[rr][cc] - gi);
             dk_ap += (dA[rr][i] * eb[rr][cc] + dP[rr][i] * qb[rr][cc]) * f;
         }
-        const float up = exp2f(gi), down = exp2f(gl - gi);
+        const float up = pow2(gi), down = pow2(gl - gi);
         const float dEt = -xe[r], dQt = xq[r], dKb = xk[r];
         const float de = de_a + dEt * up;
         const float dq = dq_p + dQt * up;
@@ -680,7 +685,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_keys_kernel(BwdArgs a)
     __syncthreads();
     // the chunk-end terms, then the reverse running sum over the chunk's tokens
     if (tid < CB) {
-        float acc = exp2f(gl) * rs[cc];
+        float acc = pow2(gl) * rs[cc];
         for (int j = 0; j < L; ++j) acc += kbd[j][cc];
         for (int i = L - 1; i >= 0; --i) {
             acc += dg[i][cc];
