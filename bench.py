@@ -321,6 +321,51 @@ def bench_bwd(args):
     return dict(x=x, wl=wl, ms=ms, bytes=nbytes, flops=flops, ws_bytes=ws.numel())
 
 
+def bench_mixer(args):
+    """The token-mixer prologue (K = 4) and epilogue on batched_bf16's shape
+    (B=8, T=4096, H=16, d=128, bf16): one report row each."""
+    import torch
+
+    from delta_rule_linear_gdn2_amd import binding
+    from delta_rule_linear_gdn2_amd import workloads as W
+
+    x = W.make("batched_bf16")
+    B, T, H, dk, dv, K = 8, 4096, 16, 128, 128, 4
+    rng = np.random.default_rng(9)
+    d = to_dev(x, "bf16")
+    conv = [torch.from_numpy((0.5 * rng.standard_normal((H * dd, K))).astype(np.float32)).cuda() for dd in (dk, dk, dv)]
+    state = torch.zeros((B, H * (2 * dk + dv), K - 1), dtype=torch.float32, device="cuda")
+    outs = {}
+    rows = []
+
+    def call_pro():
+        outs["p"] = binding.gdn2_mixer_prologue(d["q"], d["k"], d["v"], conv[0], conv[1], conv[2], d["b"], d["w"],
+                                                conv_state=state, q_scale=dk ** -0.5)
+
+    per, _, _ = time_events(call_pro, args.warmup, args.steps)
+    ms = float(np.median(per))
+    nbytes = B * T * H * (3 * dk * 2 + 2 * dv * 2) * 2  # xq, xk, b_logit, xv, w_logit in; q, k, b, v, w out
+    log(f"mixer prologue: {ms * 1e3:.1f} us, {nbytes / (ms / 1e3) / 1e9:.0f} GB/s")
+    rows.append({"report": "config", "workload": "batched_bf16 token-mixer prologue (K=4)",
+                 "us_per_call": ms * 1e3, "GBps": nbytes / (ms / 1e3) / 1e9,
+                 "hbm_frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, "algorithmic_bytes": nbytes})
+    gate = d["w"]
+    wgt = torch.ones(dv, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(d["v"])
+
+    def call_epi():
+        binding.gdn2_mixer_epilogue(d["v"], gate, wgt, out=y)
+
+    per, _, _ = time_events(call_epi, args.warmup, args.steps)
+    ms = float(np.median(per))
+    nbytes = B * T * H * 3 * dv * 2  # o, gate in; y out
+    log(f"mixer epilogue: {ms * 1e3:.1f} us, {nbytes / (ms / 1e3) / 1e9:.0f} GB/s")
+    rows.append({"report": "config", "workload": "batched_bf16 token-mixer epilogue",
+                 "us_per_call": ms * 1e3, "GBps": nbytes / (ms / 1e3) / 1e9,
+                 "hbm_frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, "algorithmic_bytes": nbytes})
+    return rows
+
+
 def run_only(args):
     """One part alone (for rocprofv3 runs); prints one JSON line."""
     import torch
@@ -336,6 +381,8 @@ def run_only(args):
     elif args.only == "decode":
         dec = bench_decode(args)
         res = {"part": "decode", "us_per_step": dec["step_ms"] * 1e3, "algorithmic_bytes": dec["bytes"]}
+    elif args.only == "mixer":
+        res = {"part": "mixer", "rows": bench_mixer(args), "launches": args.steps + args.warmup}
     else:
         nbytes = 1 << 30
         src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -442,40 +489,8 @@ def run_configs(args):
         print(json.dumps(row), flush=True)
         del d, x
     # the token mixer around the recurrence on the headline shape (HBM-bound passes)
-    x = W.make("batched_bf16")
-    B, T, H, dk, dv, K = 8, 4096, 16, 128, 128, 4
-    rng = np.random.default_rng(9)
-    d = to_dev(x, "bf16")
-    conv = [torch.from_numpy((0.5 * rng.standard_normal((H * dd, K))).astype(np.float32)).cuda() for dd in (dk, dk, dv)]
-    state = torch.zeros((B, H * (2 * dk + dv), K - 1), dtype=torch.float32, device="cuda")
-    outs = {}
-
-    def call_pro():
-        outs["p"] = binding.gdn2_mixer_prologue(d["q"], d["k"], d["v"], conv[0], conv[1], conv[2], d["b"], d["w"],
-                                                conv_state=state, q_scale=dk ** -0.5)
-
-    per, _, _ = time_events(call_pro, args.warmup, args.steps)
-    ms = float(np.median(per))
-    nbytes = B * T * H * (3 * dk * 2 + 2 * dv * 2) * 2  # xq, xk, b_logit, xv, w_logit in; q, k, b, v, w out
-    log(f"mixer prologue: {ms * 1e3:.1f} us, {nbytes / (ms / 1e3) / 1e9:.0f} GB/s")
-    print(json.dumps({"report": "config", "workload": "batched_bf16 token-mixer prologue (K=4)",
-                      "us_per_call": ms * 1e3, "GBps": nbytes / (ms / 1e3) / 1e9,
-                      "hbm_frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, "algorithmic_bytes": nbytes}), flush=True)
-    gate = d["w"]
-    wgt = torch.ones(dv, dtype=torch.float32, device="cuda")
-    y = torch.empty_like(d["v"])
-
-    def call_epi():
-        binding.gdn2_mixer_epilogue(d["v"], gate, wgt, out=y)
-
-    per, _, _ = time_events(call_epi, args.warmup, args.steps)
-    ms = float(np.median(per))
-    nbytes = B * T * H * 3 * dv * 2  # o, gate in; y out
-    log(f"mixer epilogue: {ms * 1e3:.1f} us, {nbytes / (ms / 1e3) / 1e9:.0f} GB/s")
-    print(json.dumps({"report": "config", "workload": "batched_bf16 token-mixer epilogue",
-                      "us_per_call": ms * 1e3, "GBps": nbytes / (ms / 1e3) / 1e9,
-                      "hbm_frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, "algorithmic_bytes": nbytes}), flush=True)
-    del d, x, outs, y
+    for row in bench_mixer(args):
+        print(json.dumps(row), flush=True)
     # the gate-aware backward on the headline shape, and the oracle's reverse mode beside it
     bw = bench_bwd(args)
     t0 = time.perf_counter()
@@ -531,7 +546,7 @@ def main():
     ap.add_argument("--workload", default="batched_bf16",
                     choices=["batched_bf16", "layer_bf16", "varlen32_bf16", "tiny_f32"])
     ap.add_argument("--no-decode", action="store_true", help="skip the decode half")
-    ap.add_argument("--only", choices=["chunk", "decode", "copy", "bwd"], default=None,
+    ap.add_argument("--only", choices=["chunk", "decode", "copy", "bwd", "mixer"], default=None,
                     help="profiling aid: run one part only and print its timing line "
                          "(copy = a plain 1 GiB device copy, the reference for HBM byte counters)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
