@@ -48,6 +48,19 @@
 namespace gdn2 {
 namespace {
 
+// Barrier for the sequential kernels, whose workgroups share data through LDS
+// alone: a wave waits for its own LDS accesses (lgkmcnt = 0) and meets the
+// others at s_barrier, while its global loads (the next chunk's) stay in
+// flight; __syncthreads() would wait for them too.  The empty asm statements
+// keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_sync()
+{
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63, expcnt 7, lgkmcnt 0
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
 // 2^x with the hardware exponential (about one ulp; results below 2^-126 flush
 // to zero, which only drops terms far below FP32 resolution: every factor here
 // is at most 1 and multiplies values of order one).
@@ -247,48 +260,54 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdArgs a)
 // with i0 = c0 = tid / 32.  The rows a wavefront reads at one time are two,
 // so the row operand is a broadcast and the column operand is contiguous.
 
-// Prepared rows of one chunk into LDS (rows past the chunk are zero in the
-// block).  Sixteen-byte loads, all issued before the first LDS store so that
-// they are in flight together.
+// A chunk's prepared rows (rows past the chunk are zero in the block), loaded
+// with sixteen-byte loads into registers by issue() and written to LDS by
+// store(): the sequential kernels issue the next chunk's loads while they
+// compute the current one.
 template <int DK, bool kQ, int NT>
-__device__ __forceinline__ void load_prep(const float* src, float (*Et)[DK + 1], float (*Qt)[DK + 1],
-                                          float (*Kb)[DK + 1], float (*Tm)[CH + 1], float (*Pm)[CH + 1],
-                                          float* gam, int tid)
-{
-    constexpr int QR = CH * DK / 4;              // quads per row array
-    constexpr int NQ = (QR + NT - 1) / NT;       // quads per thread and array
-    constexpr int QT = CH * CH / 4;              // quads of Tm (and Pm)
+struct PrepRegs {
+    static constexpr int QR = CH * DK / 4;           // quads per row array
+    static constexpr int NQ = (QR + NT - 1) / NT;    // quads per thread and array
+    static constexpr int QT = CH * CH / 4;           // quads of Tm (and Pm)
     static_assert(QT <= NT && DK / 4 <= NT, "one quad of Tm, Pm and gamma per thread at most");
-    const float4* s4 = reinterpret_cast<const float4*>(src);
-    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
     float4 ve[NQ], vq[NQ], vk[NQ], vt, vp, vg;
+
+    __device__ void issue(const float* src, int tid)
+    {
+        const float4* s4 = reinterpret_cast<const float4*>(src);
+        const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int qd = 0; qd < NQ; ++qd) {
-        const int i4 = tid + NT * qd;
-        const bool in = i4 < QR;
-        ve[qd] = in ? s4[kPrepE / 4 + i4] : z4;
-        vq[qd] = in && kQ ? s4[kPrepE / 4 + QR + i4] : z4;
-        vk[qd] = in ? s4[kPrepE / 4 + 2 * QR + i4] : z4;
+        for (int qd = 0; qd < NQ; ++qd) {
+            const int i4 = tid + NT * qd;
+            const bool in = i4 < QR;
+            ve[qd] = in ? s4[kPrepE / 4 + i4] : z4;
+            vq[qd] = in && kQ ? s4[kPrepE / 4 + QR + i4] : z4;
+            vk[qd] = in ? s4[kPrepE / 4 + 2 * QR + i4] : z4;
+        }
+        vt = tid < QT ? s4[kPrepT / 4 + tid] : z4;
+        vp = tid < QT && kQ ? s4[kPrepP / 4 + tid] : z4;
+        vg = tid < DK / 4 ? s4[kPrepE / 4 + 3 * QR + tid] : z4;
     }
-    vt = tid < QT ? s4[kPrepT / 4 + tid] : z4;
-    vp = tid < QT && kQ ? s4[kPrepP / 4 + tid] : z4;
-    vg = tid < DK / 4 ? s4[kPrepE / 4 + 3 * QR + tid] : z4;
+    __device__ void store(float (*Et)[DK + 1], float (*Qt)[DK + 1], float (*Kb)[DK + 1], float (*Tm)[CH + 1],
+                          float (*Pm)[CH + 1], float* gam, int tid) const
+    {
 #pragma unroll
-    for (int qd = 0; qd < NQ; ++qd) {
-        const int i4 = tid + NT * qd;
-        if (i4 >= QR) continue;
-        const int i = i4 / (DK / 4), c = (i4 % (DK / 4)) * 4;
-        st4(Et[i], c, ve[qd]);
-        if (kQ) st4(Qt[i], c, vq[qd]);
-        st4(Kb[i], c, vk[qd]);
+        for (int qd = 0; qd < NQ; ++qd) {
+            const int i4 = tid + NT * qd;
+            if (i4 >= QR) continue;
+            const int i = i4 / (DK / 4), c = (i4 % (DK / 4)) * 4;
+            st4(Et[i], c, ve[qd]);
+            if (kQ) st4(Qt[i], c, vq[qd]);
+            st4(Kb[i], c, vk[qd]);
+        }
+        if (tid < QT) {
+            const int i = tid / (CH / 4), c = (tid % (CH / 4)) * 4;
+            st4(Tm[i], c, vt);
+            if (kQ) st4(Pm[i], c, vp);
+        }
+        if (tid < DK / 4) st4(gam, 4 * tid, vg);
     }
-    if (tid < QT) {
-        const int i = tid / (CH / 4), c = (tid % (CH / 4)) * 4;
-        st4(Tm[i], c, vt);
-        if (kQ) st4(Pm[i], c, vp);
-    }
-    if (tid < DK / 4) st4(gam, 4 * tid, vg);
-}
+};
 
 // ---------------------------------------------------------------------------
 // bwd_states: the forward again, storing the state at every chunk start.
@@ -323,24 +342,38 @@ __global__ __launch_bounds__(kSeqThreads) void bwd_states_kernel(BwdArgs a)
     for (int r = 0; r < RS; ++r)
         Ss[i0 + NG * r][jj] = a.initial_state ? a.initial_state[s_off + int64_t(i0 + NG * r) * dv] : 0.f;
 
-    int m = 0;
-    for (int64_t t0 = bos; t0 < eos; t0 += CH, ++m) {
+    // chunk m's prepared rows and v, w rows, loaded one chunk ahead
+    const int M = int((eos - bos + CH - 1) / CH);
+    PrepRegs<DK, false, kSeqThreads> pf;
+    float pv[RR], pw[RR];
+    auto issue = [&](int m) {
+        const int64_t t0 = bos + int64_t(m) * CH;
         const int L = int(eos - t0 < CH ? eos - t0 : CH);
         const int64_t row0 = (brow * a.T + t0) * a.H + h;
-        const int64_t slot = slot_of(a, n, bos, m);
-        float* dst = a.ws_states + slot_base(a, brow, slot, h) + j0 + jj;
-#pragma unroll
-        for (int r = 0; r < RS; ++r) dst[int64_t(i0 + NG * r) * dv] = Ss[i0 + NG * r][jj];
-        __syncthreads();  // the previous chunk is done with Et, Kb, Tm, Xs, Us and Ss
-        load_prep<DK, false, kSeqThreads>(a.ws_prep + prep_base(a, brow, slot, h), Et, nullptr, Kb, Tm, nullptr, gam, tid);
-        float z[RR];
+        pf.issue(a.ws_prep + prep_base(a, brow, slot_of(a, n, bos, m), h), tid);
 #pragma unroll
         for (int r = 0; r < RR; ++r) {
             const int i = i0 + NG * r;
             const int64_t off = (row0 + int64_t(i) * a.H) * dv + j0 + jj;
-            z[r] = i < L ? load_as_f32(w, off) * load_as_f32(v, off) : 0.f;
+            pv[r] = i < L ? load_as_f32(v, off) : 0.f;
+            pw[r] = i < L ? load_as_f32(w, off) : 0.f;
         }
-        __syncthreads();
+    };
+    if (M > 0) issue(0);
+    for (int m = 0; m < M; ++m) {
+        const int64_t t0 = bos + int64_t(m) * CH;
+        const int L = int(eos - t0 < CH ? eos - t0 : CH);
+        const int64_t slot = slot_of(a, n, bos, m);
+        float* dst = a.ws_states + slot_base(a, brow, slot, h) + j0 + jj;
+#pragma unroll
+        for (int r = 0; r < RS; ++r) dst[int64_t(i0 + NG * r) * dv] = Ss[i0 + NG * r][jj];
+        lds_sync();  // the previous chunk is done with Et, Kb, Tm, Xs, Us and Ss
+        pf.store(Et, nullptr, Kb, Tm, nullptr, gam, tid);
+        float z[RR];
+#pragma unroll
+        for (int r = 0; r < RR; ++r) z[r] = pw[r] * pv[r];
+        if (m + 1 < M) issue(m + 1);  // in flight while this chunk is computed
+        lds_sync();
         // X = Z - Et S
         {
             float acc[RR] = {};
@@ -353,7 +386,7 @@ __global__ __launch_bounds__(kSeqThreads) void bwd_states_kernel(BwdArgs a)
 #pragma unroll
             for (int r = 0; r < RR; ++r) Xs[i0 + NG * r][jj] = z[r] - acc[r];
         }
-        __syncthreads();
+        lds_sync();
         // U = Tm X  (Tm is unit lower triangular; rows past the chunk give zero)
         {
             float acc[RR] = {};
@@ -366,7 +399,7 @@ __global__ __launch_bounds__(kSeqThreads) void bwd_states_kernel(BwdArgs a)
 #pragma unroll
             for (int r = 0; r < RR; ++r) Us[i0 + NG * r][jj] = acc[r];
         }
-        __syncthreads();
+        lds_sync();
         // S <- 2^G_L S + Kb^T U  (each thread its own elements)
         {
             float acc[RS];
@@ -420,7 +453,30 @@ __global__ __launch_bounds__(kSeqThreads) void bwd_dstate_kernel(BwdArgs a)
     for (int r = 0; r < RS; ++r)
         dSs[i0 + NG * r][jj] = a.d_final_state ? a.d_final_state[s_off + int64_t(i0 + NG * r) * dv] : 0.f;
 
+    // chunk m's prepared rows, chunk-start state and v, w, dO rows, loaded one chunk ahead
     const int M = int((eos - bos + CH - 1) / CH);
+    PrepRegs<DK, true, kSeqThreads> pf;
+    float pv[RR], pw[RR], po[RR], ps[RS];
+    auto issue = [&](int m) {
+        const int64_t t0 = bos + int64_t(m) * CH;
+        const int L = int(eos - t0 < CH ? eos - t0 : CH);
+        const int64_t row0 = (brow * a.T + t0) * a.H + h;
+        const int64_t slot = slot_of(a, n, bos, m);
+        pf.issue(a.ws_prep + prep_base(a, brow, slot, h), tid);
+        const int64_t sb = slot_base(a, brow, slot, h) + j0 + jj;
+#pragma unroll
+        for (int r = 0; r < RS; ++r) ps[r] = a.ws_states[sb + int64_t(i0 + NG * r) * dv];
+#pragma unroll
+        for (int r = 0; r < RR; ++r) {
+            const int i = i0 + NG * r;
+            const bool live = i < L;
+            const int64_t off = (row0 + int64_t(i) * a.H) * dv + j0 + jj;
+            pv[r] = live ? load_as_f32(v, off) : 0.f;
+            pw[r] = live ? load_as_f32(w, off) : 0.f;
+            po[r] = live ? load_as_f32(dO, off) : 0.f;
+        }
+    };
+    if (M > 0) issue(M - 1);
     for (int m = M - 1; m >= 0; --m) {
         const int64_t t0 = bos + int64_t(m) * CH;
         const int L = int(eos - t0 < CH ? eos - t0 : CH);
@@ -430,22 +486,20 @@ __global__ __launch_bounds__(kSeqThreads) void bwd_dstate_kernel(BwdArgs a)
 #pragma unroll
         for (int r = 0; r < RS; ++r) {
             a.ws_dstates[sb + int64_t(i0 + NG * r) * dv] = dSs[i0 + NG * r][jj];
-            Ss[i0 + NG * r][jj] = a.ws_states[sb + int64_t(i0 + NG * r) * dv];
+            Ss[i0 + NG * r][jj] = ps[r];
         }
-        __syncthreads();  // the previous chunk is done with the prepared rows and the row buffers
-        load_prep<DK, true, kSeqThreads>(a.ws_prep + prep_base(a, brow, slot, h), Et, Qt, Kb, Tm, Pm, gam, tid);
+        lds_sync();  // the previous chunk is done with the prepared rows and the row buffers
+        pf.store(Et, Qt, Kb, Tm, Pm, gam, tid);
         float z[RR], vv[RR], ww[RR];
 #pragma unroll
         for (int r = 0; r < RR; ++r) {
-            const int i = i0 + NG * r;
-            const bool live = i < L;
-            const int64_t off = (row0 + int64_t(i) * a.H) * dv + j0 + jj;
-            vv[r] = live ? load_as_f32(v, off) : 0.f;
-            ww[r] = live ? load_as_f32(w, off) : 0.f;
+            vv[r] = pv[r];
+            ww[r] = pw[r];
             z[r] = ww[r] * vv[r];
-            dOs[i][jj] = live ? load_as_f32(dO, off) : 0.f;
+            dOs[i0 + NG * r][jj] = po[r];
         }
-        __syncthreads();
+        if (m > 0) issue(m - 1);  // in flight while this chunk is computed
+        lds_sync();
         // X = Z - Et S and dU = Kb dS' + Pm^T dO
         {
             float ax[RR] = {}, au[RR] = {};
@@ -470,7 +524,7 @@ __global__ __launch_bounds__(kSeqThreads) void bwd_dstate_kernel(BwdArgs a)
                 dUs[i0 + NG * r][jj] = au[r];
             }
         }
-        __syncthreads();
+        lds_sync();
         // U = Tm X,  dX = Tm^T dU
         {
             float au[RR] = {}, ad[RR] = {};
@@ -497,7 +551,7 @@ __global__ __launch_bounds__(kSeqThreads) void bwd_dstate_kernel(BwdArgs a)
                 }
             }
         }
-        __syncthreads();
+        lds_sync();
         // dS = 2^G_L dS' + Qt^T dO - Et^T dX  (each thread its own elements)
         {
             float acc[RS];
