@@ -288,8 +288,9 @@ struct PrepRegs {
         vp = tid < QT && kQ ? s4[kPrepP / 4 + tid] : z4;
         vg = tid < DK / 4 ? s4[kPrepE / 4 + 3 * QR + tid] : z4;
     }
-    __device__ void store(float (*Et)[DK + 1], float (*Qt)[DK + 1], float (*Kb)[DK + 1], float (*Tm)[CH + 1],
-                          float (*Pm)[CH + 1], float* gam, int tid) const
+    template <int RSD, int RST>  // row strides of the [CH][DK] and [CH][CH] arrays
+    __device__ void store(float (*Et)[RSD], float (*Qt)[RSD], float (*Kb)[RSD], float (*Tm)[RST],
+                          float (*Pm)[RST], float* gam, int tid) const
     {
 #pragma unroll
         for (int qd = 0; qd < NQ; ++qd) {
@@ -310,18 +311,35 @@ struct PrepRegs {
 };
 
 // ---------------------------------------------------------------------------
+// The sequential kernels' products on the FP32 matrix cores
+// (v_mfma_f32_16x16x4_f32, one 16 x 16 output block per instruction group).
+// Lane l of a wavefront supplies A[row l % 16][k l / 16] and B[k l / 16][column
+// l % 16] of a K = 4 step, and holds D[rows 4 (l / 16) .. + 3][column l % 16].
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4_t mfma4(float a, float b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+constexpr int kPad = 4;  // row padding of the LDS operands: the b32 operand reads stay free of bank conflicts
+
+// ---------------------------------------------------------------------------
 // bwd_states: the forward again, storing the state at every chunk start.
+// Wavefront w owns the state blocks w, w + 8, ... (block t: rows 16 (t / 2),
+// columns 16 (t % 2) of the 32-column tile) in accumulator registers;
+// wavefronts 0..3 form the four blocks of X and U.
 template <typename T, int DK>
 __global__ __launch_bounds__(kSeqThreads) void bwd_states_kernel(BwdArgs a)
 {
-    constexpr int RS = DK / NG;  // state rows per thread
-    __shared__ float Et[CH][DK + 1], Kb[CH][DK + 1];
-    __shared__ float Tm[CH][CH + 1];
+    constexpr int NTS = (DK / 16) * (kTile / 16);  // 16 x 16 blocks of the state tile
+    constexpr int TPW = (NTS + 7) / 8;             // per wavefront
+    __shared__ float Et[CH][DK + kPad], Kb[CH][DK + kPad];
+    __shared__ float Tm[CH][CH + kPad];
     __shared__ float gam[DK];
-    __shared__ float Ss[DK][kTile];
-    __shared__ float Xs[CH][kTile], Us[CH][kTile];
+    __shared__ float Ss[DK][kTile];  // chunk-start state
+    __shared__ float Zs[CH][kTile], Xs[CH][kTile], Us[CH][kTile];
 
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ln = lane & 15, lk = lane >> 4;
     const int jj = tid % kTile, i0 = tid / kTile;
     const int ntiles = a.dv_ / kTile;
     int64_t chain64;
@@ -337,10 +355,19 @@ __global__ __launch_bounds__(kSeqThreads) void bwd_states_kernel(BwdArgs a)
     const T* v = static_cast<const T*>(a.v);
     const T* w = static_cast<const T*>(a.w);
 
-    const int64_t s_off = (int64_t(n) * a.H + h) * DK * dv + j0 + jj;
+    f32x4_t st[TPW];
+    const int64_t s_off = (int64_t(n) * a.H + h) * DK * dv + j0;
 #pragma unroll
-    for (int r = 0; r < RS; ++r)
-        Ss[i0 + NG * r][jj] = a.initial_state ? a.initial_state[s_off + int64_t(i0 + NG * r) * dv] : 0.f;
+    for (int u = 0; u < TPW; ++u) {
+        const int t = wave + 8 * u;
+        if (t >= NTS) continue;
+        const int r0 = 16 * (t >> 1) + 4 * lk, c = 16 * (t & 1) + ln;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            st[u][i] = a.initial_state ? a.initial_state[s_off + int64_t(r0 + i) * dv + c] : 0.f;
+            Ss[r0 + i][c] = st[u][i];
+        }
+    }
 
     // chunk m's prepared rows and v, w rows, loaded one chunk ahead
     const int M = int((eos - bos + CH - 1) / CH);
@@ -361,75 +388,80 @@ __global__ __launch_bounds__(kSeqThreads) void bwd_states_kernel(BwdArgs a)
     };
     if (M > 0) issue(0);
     for (int m = 0; m < M; ++m) {
-        const int64_t t0 = bos + int64_t(m) * CH;
-        const int L = int(eos - t0 < CH ? eos - t0 : CH);
         const int64_t slot = slot_of(a, n, bos, m);
-        float* dst = a.ws_states + slot_base(a, brow, slot, h) + j0 + jj;
+        float* dst = a.ws_states + slot_base(a, brow, slot, h) + j0;
 #pragma unroll
-        for (int r = 0; r < RS; ++r) dst[int64_t(i0 + NG * r) * dv] = Ss[i0 + NG * r][jj];
-        lds_sync();  // the previous chunk is done with Et, Kb, Tm, Xs, Us and Ss
-        pf.store(Et, nullptr, Kb, Tm, nullptr, gam, tid);
-        float z[RR];
+        for (int u = 0; u < TPW; ++u) {
+            const int t = wave + 8 * u;
+            if (t >= NTS) continue;
+            const int r0 = 16 * (t >> 1) + 4 * lk, c = 16 * (t & 1) + ln;
 #pragma unroll
-        for (int r = 0; r < RR; ++r) z[r] = pw[r] * pv[r];
+            for (int i = 0; i < 4; ++i) dst[int64_t(r0 + i) * dv + c] = st[u][i];
+        }
+        lds_sync();  // the previous chunk is done with Et, Kb, Tm, Zs, Xs and Us
+        pf.template store<DK + kPad, CH + kPad>(Et, nullptr, Kb, Tm, nullptr, gam, tid);
+#pragma unroll
+        for (int r = 0; r < RR; ++r) Zs[i0 + NG * r][jj] = pw[r] * pv[r];
         if (m + 1 < M) issue(m + 1);  // in flight while this chunk is computed
         lds_sync();
-        // X = Z - Et S
-        {
-            float acc[RR] = {};
-#pragma unroll 4
-            for (int ch = 0; ch < DK; ++ch) {
-                const float sv = Ss[ch][jj];
+        // X = Z - Et S  (rows past the chunk: zero rows of Et and Z give zero)
+        if (wave < 4) {
+            const int r0 = 16 * (wave >> 1), c = 16 * (wave & 1) + ln;
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+            for (int k0 = 0; k0 < DK; k0 += 4) acc = mfma4(Et[r0 + ln][k0 + lk], Ss[k0 + lk][c], acc);
 #pragma unroll
-                for (int r = 0; r < RR; ++r) acc[r] += Et[i0 + NG * r][ch] * sv;
-            }
-#pragma unroll
-            for (int r = 0; r < RR; ++r) Xs[i0 + NG * r][jj] = z[r] - acc[r];
+            for (int i = 0; i < 4; ++i) Xs[r0 + 4 * lk + i][c] = Zs[r0 + 4 * lk + i][c] - acc[i];
         }
         lds_sync();
-        // U = Tm X  (Tm is unit lower triangular; rows past the chunk give zero)
-        {
-            float acc[RR] = {};
-#pragma unroll 4
-            for (int mm = 0; mm < CH; ++mm) {
-                const float xv = Xs[mm][jj];
+        // U = Tm X
+        if (wave < 4) {
+            const int r0 = 16 * (wave >> 1), c = 16 * (wave & 1) + ln;
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int r = 0; r < RR; ++r) acc[r] += Tm[i0 + NG * r][mm] * xv;
-            }
+            for (int k0 = 0; k0 < CH; k0 += 4) acc = mfma4(Tm[r0 + ln][k0 + lk], Xs[k0 + lk][c], acc);
 #pragma unroll
-            for (int r = 0; r < RR; ++r) Us[i0 + NG * r][jj] = acc[r];
+            for (int i = 0; i < 4; ++i) Us[r0 + 4 * lk + i][c] = acc[i];
         }
         lds_sync();
-        // S <- 2^G_L S + Kb^T U  (each thread its own elements)
-        {
-            float acc[RS];
+        // S <- 2^G_L S + Kb^T U  (Kb and U are zero past the chunk)
 #pragma unroll
-            for (int r = 0; r < RS; ++r) acc[r] = gam[i0 + NG * r] * Ss[i0 + NG * r][jj];
-            for (int i = 0; i < L; ++i) {
-                const float uv = Us[i][jj];
+        for (int u = 0; u < TPW; ++u) {
+            const int t = wave + 8 * u;
+            if (t >= NTS) continue;
+            const int r0 = 16 * (t >> 1), c = 16 * (t & 1) + ln;
+            f32x4_t acc;
 #pragma unroll
-                for (int r = 0; r < RS; ++r) acc[r] += Kb[i][i0 + NG * r] * uv;
-            }
+            for (int i = 0; i < 4; ++i) acc[i] = gam[r0 + 4 * lk + i] * st[u][i];
 #pragma unroll
-            for (int r = 0; r < RS; ++r) Ss[i0 + NG * r][jj] = acc[r];
+            for (int k0 = 0; k0 < CH; k0 += 4) acc = mfma4(Kb[k0 + lk][r0 + ln], Us[k0 + lk][c], acc);
+            st[u] = acc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Ss[r0 + 4 * lk + i][c] = acc[i];
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// bwd_dstate: chunks in reverse, carrying the state gradient.
+// bwd_dstate: chunks in reverse, carrying the state gradient.  Wavefront w
+// owns the gradient blocks w, w + 8, ... in accumulator registers;
+// wavefronts 0..3 form the blocks of X and U, wavefronts 4..7 those of dU
+// and dX.
 template <typename T, int DK>
 __global__ __launch_bounds__(kSeqThreads) void bwd_dstate_kernel(BwdArgs a)
 {
-    constexpr int RS = DK / NG;
-    __shared__ float Et[CH][DK + 1], Qt[CH][DK + 1], Kb[CH][DK + 1];
-    __shared__ float Tm[CH][CH + 1], Pm[CH][CH + 1];
+    constexpr int NTS = (DK / 16) * (kTile / 16);
+    constexpr int TPW = (NTS + 7) / 8;
+    __shared__ float Et[CH][DK + kPad], Qt[CH][DK + kPad], Kb[CH][DK + kPad];
+    __shared__ float Tm[CH][CH + kPad], Pm[CH][CH + kPad];
     __shared__ float gam[DK];
-    __shared__ float Ss[DK][kTile];    // chunk-start state
-    __shared__ float dSs[DK][kTile];   // gradient of the chunk-end state, then of its start
-    __shared__ float Xs[CH][kTile], dUs[CH][kTile], dOs[CH][kTile], Us[CH][kTile], dXs[CH][kTile];
+    __shared__ float Ss[DK][kTile];   // chunk-start state
+    __shared__ float dSs[DK][kTile];  // gradient of the chunk-end state
+    __shared__ float Zs[CH][kTile], Xs[CH][kTile], dUs[CH][kTile], dOs[CH][kTile], dXs[CH][kTile];
+    __shared__ float Vs[CH][kTile], Ws[CH][kTile];
 
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ln = lane & 15, lk = lane >> 4;
     const int jj = tid % kTile, i0 = tid / kTile;
     const int ntiles = a.dv_ / kTile;
     int64_t chain64;
@@ -448,13 +480,23 @@ __global__ __launch_bounds__(kSeqThreads) void bwd_dstate_kernel(BwdArgs a)
     T* dv_out = static_cast<T*>(a.dv);
     T* dw_out = static_cast<T*>(a.dw);
 
-    const int64_t s_off = (int64_t(n) * a.H + h) * DK * dv + j0 + jj;
+    f32x4_t ds[TPW];
+    const int64_t s_off = (int64_t(n) * a.H + h) * DK * dv + j0;
 #pragma unroll
-    for (int r = 0; r < RS; ++r)
-        dSs[i0 + NG * r][jj] = a.d_final_state ? a.d_final_state[s_off + int64_t(i0 + NG * r) * dv] : 0.f;
+    for (int u = 0; u < TPW; ++u) {
+        const int t = wave + 8 * u;
+        if (t >= NTS) continue;
+        const int r0 = 16 * (t >> 1) + 4 * lk, c = 16 * (t & 1) + ln;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ds[u][i] = a.d_final_state ? a.d_final_state[s_off + int64_t(r0 + i) * dv + c] : 0.f;
+            dSs[r0 + i][c] = ds[u][i];
+        }
+    }
 
     // chunk m's prepared rows, chunk-start state and v, w, dO rows, loaded one chunk ahead
     const int M = int((eos - bos + CH - 1) / CH);
+    constexpr int RS = DK / NG;
     PrepRegs<DK, true, kSeqThreads> pf;
     float pv[RR], pw[RR], po[RR], ps[RS];
     auto issue = [&](int m) {
@@ -482,93 +524,107 @@ __global__ __launch_bounds__(kSeqThreads) void bwd_dstate_kernel(BwdArgs a)
         const int L = int(eos - t0 < CH ? eos - t0 : CH);
         const int64_t row0 = (brow * a.T + t0) * a.H + h;
         const int64_t slot = slot_of(a, n, bos, m);
-        const int64_t sb = slot_base(a, brow, slot, h) + j0 + jj;
+        float* dsd = a.ws_dstates + slot_base(a, brow, slot, h) + j0;
 #pragma unroll
-        for (int r = 0; r < RS; ++r) {
-            a.ws_dstates[sb + int64_t(i0 + NG * r) * dv] = dSs[i0 + NG * r][jj];
-            Ss[i0 + NG * r][jj] = ps[r];
+        for (int u = 0; u < TPW; ++u) {
+            const int t = wave + 8 * u;
+            if (t >= NTS) continue;
+            const int r0 = 16 * (t >> 1) + 4 * lk, c = 16 * (t & 1) + ln;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dsd[int64_t(r0 + i) * dv + c] = ds[u][i];
         }
-        lds_sync();  // the previous chunk is done with the prepared rows and the row buffers
-        pf.store(Et, Qt, Kb, Tm, Pm, gam, tid);
-        float z[RR], vv[RR], ww[RR];
+        lds_sync();  // the previous chunk is done with the prepared rows, the state and the row buffers
+        pf.template store<DK + kPad, CH + kPad>(Et, Qt, Kb, Tm, Pm, gam, tid);
+#pragma unroll
+        for (int r = 0; r < RS; ++r) Ss[i0 + NG * r][jj] = ps[r];
 #pragma unroll
         for (int r = 0; r < RR; ++r) {
-            vv[r] = pv[r];
-            ww[r] = pw[r];
-            z[r] = ww[r] * vv[r];
-            dOs[i0 + NG * r][jj] = po[r];
+            const int i = i0 + NG * r;
+            Vs[i][jj] = pv[r];
+            Ws[i][jj] = pw[r];
+            Zs[i][jj] = pw[r] * pv[r];
+            dOs[i][jj] = po[r];
         }
         if (m > 0) issue(m - 1);  // in flight while this chunk is computed
         lds_sync();
-        // X = Z - Et S and dU = Kb dS' + Pm^T dO
-        {
-            float ax[RR] = {}, au[RR] = {};
-#pragma unroll 4
-            for (int ch = 0; ch < DK; ++ch) {
-                const float sv = Ss[ch][jj], dsv = dSs[ch][jj];
+        if (wave < 4) {  // X = Z - Et S
+            const int r0 = 16 * (wave >> 1), c = 16 * (wave & 1) + ln;
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+            for (int k0 = 0; k0 < DK; k0 += 4) acc = mfma4(Et[r0 + ln][k0 + lk], Ss[k0 + lk][c], acc);
 #pragma unroll
-                for (int r = 0; r < RR; ++r) {
-                    ax[r] += Et[i0 + NG * r][ch] * sv;
-                    au[r] += Kb[i0 + NG * r][ch] * dsv;
-                }
-            }
-#pragma unroll 4
-            for (int rr = 0; rr < CH; ++rr) {  // Pm is lower triangular: only rr >= i contributes
-                const float ov = dOs[rr][jj];
+            for (int i = 0; i < 4; ++i) Xs[r0 + 4 * lk + i][c] = Zs[r0 + 4 * lk + i][c] - acc[i];
+        } else {  // dU = Kb dS' + Pm^T dO
+            const int r0 = 16 * ((wave - 4) >> 1), c = 16 * (wave & 1) + ln;
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+            for (int k0 = 0; k0 < DK; k0 += 4) acc = mfma4(Kb[r0 + ln][k0 + lk], dSs[k0 + lk][c], acc);
 #pragma unroll
-                for (int r = 0; r < RR; ++r) au[r] += Pm[rr][i0 + NG * r] * ov;
-            }
+            for (int k0 = 0; k0 < CH; k0 += 4) acc = mfma4(Pm[k0 + lk][r0 + ln], dOs[k0 + lk][c], acc);
 #pragma unroll
-            for (int r = 0; r < RR; ++r) {
-                Xs[i0 + NG * r][jj] = z[r] - ax[r];
-                dUs[i0 + NG * r][jj] = au[r];
-            }
+            for (int i = 0; i < 4; ++i) dUs[r0 + 4 * lk + i][c] = acc[i];
         }
         lds_sync();
-        // U = Tm X,  dX = Tm^T dU
-        {
-            float au[RR] = {}, ad[RR] = {};
-#pragma unroll 4
-            for (int mm = 0; mm < CH; ++mm) {
-                const float xv = Xs[mm][jj], dv_ = dUs[mm][jj];
+        if (wave < 4) {  // U = Tm X (to the workspace for the key kernel)
+            const int r0 = 16 * (wave >> 1), c = 16 * (wave & 1) + ln;
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int r = 0; r < RR; ++r) {
-                    au[r] += Tm[i0 + NG * r][mm] * xv;
-                    ad[r] += Tm[mm][i0 + NG * r] * dv_;
-                }
+            for (int k0 = 0; k0 < CH; k0 += 4) acc = mfma4(Tm[r0 + ln][k0 + lk], Xs[k0 + lk][c], acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = r0 + 4 * lk + i;
+                if (row < L) a.ws_u[(row0 + int64_t(row) * a.H) * dv + j0 + c] = acc[i];
             }
+        } else {  // dX = Tm^T dU (zero past the chunk), dw = dX v, dv = dX w
+            const int r0 = 16 * ((wave - 4) >> 1), c = 16 * (wave & 1) + ln;
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < RR; ++r) {
-                const int i = i0 + NG * r;
-                Us[i][jj] = au[r];
-                dXs[i][jj] = i < L ? ad[r] : 0.f;
-                if (i < L) {
-                    const int64_t off = (row0 + int64_t(i) * a.H) * dv + j0 + jj;
-                    a.ws_u[off] = au[r];
-                    a.ws_dx[off] = ad[r];
-                    store_from_f32(dw_out, off, ad[r] * vv[r]);
-                    store_from_f32(dv_out, off, ad[r] * ww[r]);
+            for (int k0 = 0; k0 < CH; k0 += 4) acc = mfma4(Tm[k0 + lk][r0 + ln], dUs[k0 + lk][c], acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = r0 + 4 * lk + i;
+                const float dx = row < L ? acc[i] : 0.f;
+                dXs[row][c] = dx;
+                if (row < L) {
+                    const int64_t off = (row0 + int64_t(row) * a.H) * dv + j0 + c;
+                    a.ws_dx[off] = dx;
+                    store_from_f32(dw_out, off, dx * Vs[row][c]);
+                    store_from_f32(dv_out, off, dx * Ws[row][c]);
                 }
             }
         }
         lds_sync();
-        // dS = 2^G_L dS' + Qt^T dO - Et^T dX  (each thread its own elements)
-        {
-            float acc[RS];
+        // dS = 2^G_L dS' + Qt^T dO - Et^T dX  (the gradient of the chunk-start state)
 #pragma unroll
-            for (int r = 0; r < RS; ++r) acc[r] = gam[i0 + NG * r] * dSs[i0 + NG * r][jj];
-            for (int i = 0; i < L; ++i) {
-                const float ov = dOs[i][jj], xv = dXs[i][jj];
+        for (int u = 0; u < TPW; ++u) {
+            const int t = wave + 8 * u;
+            if (t >= NTS) continue;
+            const int r0 = 16 * (t >> 1), c = 16 * (t & 1) + ln;
+            f32x4_t acc, sub = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int r = 0; r < RS; ++r) acc[r] += Qt[i][i0 + NG * r] * ov - Et[i][i0 + NG * r] * xv;
+            for (int i = 0; i < 4; ++i) acc[i] = gam[r0 + 4 * lk + i] * ds[u][i];
+#pragma unroll
+            for (int k0 = 0; k0 < CH; k0 += 4) {
+                acc = mfma4(Qt[k0 + lk][r0 + ln], dOs[k0 + lk][c], acc);
+                sub = mfma4(Et[k0 + lk][r0 + ln], dXs[k0 + lk][c], sub);
             }
 #pragma unroll
-            for (int r = 0; r < RS; ++r) dSs[i0 + NG * r][jj] = acc[r];
+            for (int i = 0; i < 4; ++i) {
+                ds[u][i] = acc[i] - sub[i];
+                dSs[r0 + 4 * lk + i][c] = ds[u][i];
+            }
         }
     }
-    if (a.d_initial_state)
+    if (a.d_initial_state) {
 #pragma unroll
-        for (int r = 0; r < RS; ++r) a.d_initial_state[s_off + int64_t(i0 + NG * r) * dv] = dSs[i0 + NG * r][jj];
+        for (int u = 0; u < TPW; ++u) {
+            const int t = wave + 8 * u;
+            if (t >= NTS) continue;
+            const int r0 = 16 * (t >> 1) + 4 * lk, c = 16 * (t & 1) + ln;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a.d_initial_state[s_off + int64_t(r0 + i) * dv + c] = ds[u][i];
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
