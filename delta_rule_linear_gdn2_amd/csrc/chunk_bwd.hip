@@ -637,17 +637,18 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_keys_kernel(BwdArgs a)
     constexpr int DH = DV < 64 ? DV : 64; // value columns per pass
     static_assert(DK % CB == 0 && DV % DH == 0 && DH >= CB, "block shapes");
     // per pass: U, dX, dO rows and the block's S and dS' rows; afterwards dg and Kb dKb
-    __shared__ float buf[5][CH][DH + 1];
+    __shared__ float buf[5][CH][DH + kPad];
     __shared__ float dA[CH][CH + 1], dP[CH][CH + 1];
     __shared__ float qb[CH][CB + 1], kb[CH][CB + 1], eb[CH][CB + 1], bb[CH][CB + 1], ab[CH][CB + 1], Gb[CH][CB + 1];
     __shared__ float rs[CB];
-    float (*Us)[DH + 1] = buf[0];
-    float (*dXs)[DH + 1] = buf[1];
-    float (*dOs)[DH + 1] = buf[2];
-    float (*Sb)[DH + 1] = buf[3];
-    float (*dSb)[DH + 1] = buf[4];
+    float (*Us)[DH + kPad] = buf[0];
+    float (*dXs)[DH + kPad] = buf[1];
+    float (*dOs)[DH + kPad] = buf[2];
+    float (*Sb)[DH + kPad] = buf[3];
+    float (*dSb)[DH + kPad] = buf[4];
 
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ln = lane & 15, lk = lane >> 4;
     const int col = tid % 32, i0 = tid / 32;
     constexpr int nblk = DK / CB;
     int64_t idx;
@@ -688,9 +689,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_keys_kernel(BwdArgs a)
         }
     }
 
-    // dA, dP (row i, column j = col) and dEt, dQt, dKb (row i, channel col), over all value columns
-    float xa[4] = {0.f, 0.f, 0.f, 0.f}, xp[4] = {0.f, 0.f, 0.f, 0.f};
-    float xe[4] = {0.f, 0.f, 0.f, 0.f}, xq[4] = {0.f, 0.f, 0.f, 0.f}, xk[4] = {0.f, 0.f, 0.f, 0.f};
+    // Over all value columns, on the matrix cores: dX U^T, dO U^T (-> dA, dP),
+    // dX S^T, dO S^T, U dS'^T (-> dEt, dQt, dKb); wavefront w forms the 16 x 16
+    // block (rows 16 (w / 2), columns 16 (w % 2)) of each.  The row sums of
+    // dS' . S go with the first 32 threads.
+    static_assert(kBwdThreads == 256 && CH == 32, "four wavefronts, one block of each 32 x 32 product");
+    const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t ma = zero4, mp = zero4, me = zero4, mq = zero4, mk = zero4;
     float xr = 0.f;
     for (int jh = 0; jh < DV; jh += DH) {
         // four consecutive columns per thread; every load of the pass is
@@ -723,30 +728,39 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_keys_kernel(BwdArgs a)
             st4(dSb[i], j, vd[qd]);
         }
         __syncthreads();
+        {
+            const int ra = 16 * (wave >> 1) + ln, rb = 16 * (wave & 1) + ln;  // A rows (tokens), B rows (tokens or channels)
 #pragma unroll 4
-        for (int j = 0; j < DH; ++j) {
-            const float uc = Us[col][j], sc = Sb[col][j], dsc = dSb[col][j];
-            if (i0 == 0) xr += dsc * sc;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = i0 + 8 * r;
-                const float dx = dXs[i][j], dov = dOs[i][j];
-                xa[r] += dx * uc;
-                xp[r] += dov * uc;
-                xe[r] += dx * sc;
-                xq[r] += dov * sc;
-                xk[r] += Us[i][j] * dsc;
+            for (int k0 = 0; k0 < DH; k0 += 4) {
+                const int kk = k0 + lk;
+                const float ax = dXs[ra][kk], ao = dOs[ra][kk], au = Us[ra][kk];
+                const float bu = Us[rb][kk], bs = Sb[rb][kk], bd = dSb[rb][kk];
+                ma = mfma4(ax, bu, ma);
+                mp = mfma4(ao, bu, mp);
+                me = mfma4(ax, bs, me);
+                mq = mfma4(ao, bs, mq);
+                mk = mfma4(au, bd, mk);
             }
+            if (tid < CB)
+                for (int j = 0; j < DH; ++j) xr += dSb[tid][j] * Sb[tid][j];
         }
         __syncthreads();
     }
+    // block results: row 16 (w / 2) + 4 lk + e, column 16 (w % 2) + ln; dEt, dQt, dKb go to
+    // LDS (over the staging rows, free now) for the thread layout of the pairwise part
+    float (*Xe)[DH + kPad] = buf[2];
+    float (*Xq)[DH + kPad] = buf[3];
+    float (*Xk)[DH + kPad] = buf[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int i = i0 + 8 * r, j = col;
-        dA[i][j] = j < i ? -xa[r] : 0.f;
-        dP[i][j] = j <= i ? xp[r] : 0.f;
+    for (int e = 0; e < 4; ++e) {
+        const int i = 16 * (wave >> 1) + 4 * lk + e, j = 16 * (wave & 1) + ln;
+        dA[i][j] = j < i ? -ma[e] : 0.f;
+        dP[i][j] = j <= i ? mp[e] : 0.f;
+        Xe[i][j] = me[e];
+        Xq[i][j] = mq[e];
+        Xk[i][j] = mk[e];
     }
-    if (i0 == 0) rs[col] = xr;
+    if (tid < CB) rs[tid] = xr;
     for (int cc = tid; cc < CB; cc += kBwdThreads) {  // running sums of the block's decay
         float g = 0.f;
         for (int i = 0; i < L; ++i) {
@@ -757,8 +771,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_keys_kernel(BwdArgs a)
     __syncthreads();
 
     // pairwise and absorbed-factor gradients, thread (i0 + 8 r, channel col)
-    float (*dg)[DH + 1] = buf[0];
-    float (*kbd)[DH + 1] = buf[1];
+    float (*dg)[DH + kPad] = buf[0];
+    float (*kbd)[DH + kPad] = buf[1];
     T* dq_out = static_cast<T*>(a.dq);
     T* dk_out = static_cast<T*>(a.dk);
     T* db_out = static_cast<T*>(a.db);
@@ -780,7 +794,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_keys_kernel(BwdArgs a)
             dk_ap += (dA[rr][i] * eb[rr][cc] + dP[rr][i] * qb[rr][cc]) * f;
         }
         const float up = pow2(gi), down = pow2(gl - gi);
-        const float dEt = -xe[r], dQt = xq[r], dKb = xk[r];
+        const float dEt = -Xe[i][cc], dQt = Xq[i][cc], dKb = Xk[i][cc];
         const float de = de_a + dEt * up;
         const float dq = dq_p + dQt * up;
         const float dkk = dk_ap + dKb * down;
