@@ -206,11 +206,22 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdArgs a)
         }
     }
     __syncthreads();
-    // A and P with every pairwise decay factor formed exactly (exponent <= 0)
+    // A and P with every pairwise decay factor formed exactly (exponent <= 0):
+    // zeros above the diagonal, then the CH (CH + 1) / 2 pairs j <= i spread
+    // evenly over the threads (pair p: row i with i (i + 1) / 2 <= p, column
+    // p - i (i + 1) / 2)
     for (int i2 = tid; i2 < CH * CH; i2 += kBwdThreads) {
         const int i = i2 / CH, j = i2 % CH;
+        if (j > i) c.A[i][j] = c.P[i][j] = 0.f;
+    }
+    constexpr int kPairs = CH * (CH + 1) / 2;
+    for (int p = tid; p < kPairs; p += kBwdThreads) {
+        int i = int((sqrtf(8.f * float(p) + 1.f) - 1.f) * 0.5f);
+        while ((i + 1) * (i + 2) / 2 <= p) ++i;
+        while (i * (i + 1) / 2 > p) --i;
+        const int j = p - i * (i + 1) / 2;
         float acc_a = 0.f, acc_p = 0.f;
-        if (j <= i && i < L) {
+        if (i < L) {
             for (int ch = 0; ch < DK; ++ch) {
                 const float kf = c.K[j][ch] * pow2(c.G[i][ch] - c.G[j][ch]);
                 acc_a += c.E[i][ch] * kf;
@@ -221,15 +232,25 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdArgs a)
         c.P[i][j] = acc_p;
     }
     __syncthreads();
-    // Tm = (I + A)^-1 by columns (lane j owns column j; no lane reads another's)
+    // Tm = (I + A)^-1 by columns: lane j keeps column j in registers
+    // (substitution row by row, the same operations in the same order as a
+    // column in memory)
     if (tid < CH) {
         const int j = tid;
-        for (int i = 0; i < CH; ++i) Tm[i][j] = i == j ? 1.f : 0.f;
-        for (int i = 1; i < L; ++i) {
-            float acc = 0.f;
-            for (int mm = 0; mm < i; ++mm) acc += c.A[i][mm] * Tm[mm][j];
-            if (j < i) Tm[i][j] = -acc;
+        float t[CH];
+#pragma unroll
+        for (int i = 0; i < CH; ++i) t[i] = i == j ? 1.f : 0.f;
+#pragma unroll
+        for (int i = 1; i < CH; ++i) {
+            if (i < L) {
+                float acc = 0.f;
+#pragma unroll
+                for (int mm = 0; mm < i; ++mm) acc += c.A[i][mm] * t[mm];
+                if (j < i) t[i] = -acc;
+            }
         }
+#pragma unroll
+        for (int i = 0; i < CH; ++i) Tm[i][j] = t[i];
     }
     // absorb the decay into the row and column factors
     for (int i2 = tid; i2 < L * DK; i2 += kBwdThreads) {
