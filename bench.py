@@ -31,6 +31,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak
 # FP32 vector ALU without packed FP32 (which this build leaves off): 256 CUs x
 # 4 SIMDs x 16 lanes x 2 flops (FMA) x 2.4 GHz
 FP32_VALU_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+MFMA_FP32_PEAK_TFLOPS = 157.3  # dense FP32 matrix-core peak
 NAMES = ("q", "k", "v", "alpha", "b", "w")
 
 
@@ -508,6 +509,7 @@ def run_configs(args):
                       "hbm_frac": bw["bytes"] / (bw["ms"] / 1e3) / 1e9 / HBM_PEAK_GBPS,
                       "TFLOPs": bw["flops"] / (bw["ms"] / 1e3) / 1e12,
                       "fp32_alu_frac": bw["flops"] / (bw["ms"] / 1e3) / 1e12 / FP32_VALU_TFLOPS,
+                      "fp32_mfma_frac": bw["flops"] / (bw["ms"] / 1e3) / 1e12 / MFMA_FP32_PEAK_TFLOPS,
                       "workspace_bytes": bw["ws_bytes"],
                       "oracle_one_core": {"value": 1024 / one_bwd, "unit": "token-heads/s",
                                           "sample": f"1 sequence x 1 head x 1024 tokens, {one_bwd:.2f} s"}}),
