@@ -692,6 +692,29 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_keys_kernel(BwdArgs a)
     const T* b = static_cast<const T*>(a.b);
     const T* dO = static_cast<const T*>(a.d_o);
 
+    // the passes' rows: four consecutive columns per thread, the next pass's
+    // loads issued before this pass's products (the barriers wait on LDS only)
+    constexpr int NQ = CH * DH / 4 / kBwdThreads;  // quads per thread
+    static_assert(NQ >= 1 && CH * DH % (4 * kBwdThreads) == 0, "staging layout");
+    float4 vu[NQ], vx[NQ], vo[NQ], vs[NQ], vd[NQ];
+    auto issue = [&](int jh) {
+#pragma unroll
+        for (int qd = 0; qd < NQ; ++qd) {
+            const int i4 = tid + kBwdThreads * qd;
+            const int i = i4 / (DH / 4), j = (i4 % (DH / 4)) * 4;
+            const bool live = i < L;
+            const int64_t off = (row0 + int64_t(i) * a.H) * DV + jh + j;
+            const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+            vu[qd] = live ? load4(a.ws_u, off) : z4;
+            vx[qd] = live ? load4(a.ws_dx, off) : z4;
+            vo[qd] = live ? load4(dO, off) : z4;
+            const int64_t soff = sbase + int64_t(c0 + i) * DV + jh + j;  // i doubles as the channel (CB == CH)
+            vs[qd] = load4(a.ws_states, soff);
+            vd[qd] = load4(a.ws_dstates, soff);
+        }
+    };
+    issue(0);  // in flight with the token inputs below
+
 #pragma unroll
     for (int r = 0; r < 4; ++r) {  // the block's token inputs, thread (i0 + 8 r, col)
         const int i = i0 + 8 * r;
@@ -719,25 +742,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_keys_kernel(BwdArgs a)
     f32x4_t ma = zero4, mp = zero4, me = zero4, mq = zero4, mk = zero4;
     float xr = 0.f;
     for (int jh = 0; jh < DV; jh += DH) {
-        // four consecutive columns per thread; every load of the pass is
-        // issued before the first LDS store, so they are all in flight together
-        constexpr int NQ = CH * DH / 4 / kBwdThreads;  // quads per thread
-        static_assert(NQ >= 1 && CH * DH % (4 * kBwdThreads) == 0, "staging layout");
-        float4 vu[NQ], vx[NQ], vo[NQ], vs[NQ], vd[NQ];
-#pragma unroll
-        for (int qd = 0; qd < NQ; ++qd) {
-            const int i4 = tid + kBwdThreads * qd;
-            const int i = i4 / (DH / 4), j = (i4 % (DH / 4)) * 4;
-            const bool live = i < L;
-            const int64_t off = (row0 + int64_t(i) * a.H) * DV + jh + j;
-            const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-            vu[qd] = live ? load4(a.ws_u, off) : z4;
-            vx[qd] = live ? load4(a.ws_dx, off) : z4;
-            vo[qd] = live ? load4(dO, off) : z4;
-            const int64_t soff = sbase + int64_t(c0 + i) * DV + jh + j;  // i doubles as the channel (CB == CH)
-            vs[qd] = load4(a.ws_states, soff);
-            vd[qd] = load4(a.ws_dstates, soff);
-        }
 #pragma unroll
         for (int qd = 0; qd < NQ; ++qd) {
             const int i4 = tid + kBwdThreads * qd;
@@ -748,7 +752,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_keys_kernel(BwdArgs a)
             st4(Sb[i], j, vs[qd]);
             st4(dSb[i], j, vd[qd]);
         }
-        __syncthreads();
+        if (jh + DH < DV) issue(jh + DH);
+        lds_sync();
         {
             const int ra = 16 * (wave >> 1) + ln, rb = 16 * (wave & 1) + ln;  // A rows (tokens), B rows (tokens or channels)
 #pragma unroll 4
@@ -765,7 +770,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_keys_kernel(BwdArgs a)
             if (tid < CB)
                 for (int j = 0; j < DH; ++j) xr += dSb[tid][j] * Sb[tid][j];
         }
-        __syncthreads();
+        lds_sync();
     }
     // block results: row 16 (w / 2) + 4 lk + e, column 16 (w % 2) + ln; dEt, dQt, dKb go to
     // LDS (over the staging rows, free now) for the thread layout of the pairwise part
