@@ -772,19 +772,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_keys_kernel(BwdArgs a)
         }
         lds_sync();
     }
-    // block results: row 16 (w / 2) + 4 lk + e, column 16 (w % 2) + ln; dEt, dQt, dKb go to
-    // LDS (over the staging rows, free now) for the thread layout of the pairwise part
-    float (*Xe)[DH + kPad] = buf[2];
-    float (*Xq)[DH + kPad] = buf[3];
-    float (*Xk)[DH + kPad] = buf[4];
+    // block results: row 16 (w / 2) + 4 lk + e, column 16 (w % 2) + ln
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int i = 16 * (wave >> 1) + 4 * lk + e, j = 16 * (wave & 1) + ln;
         dA[i][j] = j < i ? -ma[e] : 0.f;
         dP[i][j] = j <= i ? mp[e] : 0.f;
-        Xe[i][j] = me[e];
-        Xq[i][j] = mq[e];
-        Xk[i][j] = mk[e];
     }
     if (tid < CB) rs[tid] = xr;
     for (int cc = tid; cc < CB; cc += kBwdThreads) {  // running sums of the block's decay
@@ -796,45 +789,91 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_keys_kernel(BwdArgs a)
     }
     __syncthreads();
 
-    // pairwise and absorbed-factor gradients, thread (i0 + 8 r, channel col)
+    // The pairwise sums as products.  With the decay split as
+    // 2^(G_i - G_j) = 2^G_i 2^-G_j:
+    //   de_a  = 2^G (.) (dA (K (.) 2^-G)),   dq_p = 2^G (.) (dP (K (.) 2^-G)),
+    //   dk_ap = 2^-G (.) (dA^T (E (.) 2^G) + dP^T (Q (.) 2^G)).
+    // Scaling by a power of two is exact, so this equals the pairwise form
+    // wherever nothing overflows: for channels whose decay over the chunk stays
+    // above 2^kSplitMin (then 2^-G <= 2^-kSplitMin).  Other channels take the
+    // pairwise loops below.  Rows past the chunk are zero in every factor.
+    constexpr float kSplitMin = -64.f;
+    float (*K2)[DH + kPad] = buf[2];
+    float (*E2)[DH + kPad] = buf[3];
+    float (*Q2)[DH + kPad] = buf[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {  // thread (i0 + 8 r, col)
+        const int i = i0 + 8 * r;
+        const float g = Gb[i][col], up = pow2(g);
+        K2[i][col] = Gb[L - 1][col] >= kSplitMin ? kb[i][col] * pow2(-g) : 0.f;
+        E2[i][col] = eb[i][col] * up;
+        Q2[i][col] = qb[i][col] * up;
+    }
+    __syncthreads();
+    f32x4_t y1 = zero4, y2 = zero4, y3 = zero4;
+    {
+        const int ra = 16 * (wave >> 1) + ln, cn = 16 * (wave & 1) + ln;
+#pragma unroll
+        for (int k0 = 0; k0 < CH; k0 += 4) {
+            const int kk = k0 + lk;
+            const float bk = K2[kk][cn];
+            y1 = mfma4(dA[ra][kk], bk, y1);
+            y2 = mfma4(dP[ra][kk], bk, y2);
+            y3 = mfma4(dA[kk][ra], E2[kk][cn], y3);
+            y3 = mfma4(dP[kk][ra], Q2[kk][cn], y3);
+        }
+    }
+
+    // pairwise and absorbed-factor gradients, in the block layout: token
+    // 16 (w / 2) + 4 lk + e, channel cw
     float (*dg)[DH + kPad] = buf[0];
     float (*kbd)[DH + kPad] = buf[1];
     T* dq_out = static_cast<T*>(a.dq);
     T* dk_out = static_cast<T*>(a.dk);
     T* db_out = static_cast<T*>(a.db);
-    const int cc = col;
-    const float gl = Gb[L - 1][cc];
+    const int cw = 16 * (wave & 1) + ln;
+    const float glw = Gb[L - 1][cw];
+    const bool split = glw >= kSplitMin;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int i = i0 + 8 * r;
+    for (int e = 0; e < 4; ++e) {
+        const int i = 16 * (wave >> 1) + 4 * lk + e;
         if (i >= L) continue;
-        const float gi = Gb[i][cc];
-        float de_a = 0.f, dq_p = 0.f, dk_ap = 0.f;
-        for (int j = 0; j <= i; ++j) {
-            const float kf = kb[j][cc] * pow2(gi - Gb[j][cc]);
-            de_a += dA[i][j] * kf;  // dA is zero on the diagonal
-            dq_p += dP[i][j] * kf;
+        const float gi = Gb[i][cw];
+        const float up = pow2(gi), down = pow2(glw - gi);
+        float de_a, dq_p, dk_ap;
+        if (split) {
+            de_a = up * y1[e];
+            dq_p = up * y2[e];
+            dk_ap = pow2(-gi) * y3[e];
+        } else {
+            de_a = dq_p = dk_ap = 0.f;
+            for (int j = 0; j <= i; ++j) {
+                const float kf = kb[j][cw] * pow2(gi - Gb[j][cw]);
+                de_a += dA[i][j] * kf;  // dA is zero on the diagonal
+                dq_p += dP[i][j] * kf;
+            }
+            for (int rr = i; rr < L; ++rr) {
+                const float f = pow2(Gb[rr][cw] - gi);
+                dk_ap += (dA[rr][i] * eb[rr][cw] + dP[rr][i] * qb[rr][cw]) * f;
+            }
         }
-        for (int rr = i; rr < L; ++rr) {
-            const float f = pow2(Gb[rr][cc] - gi);
-            dk_ap += (dA[rr][i] * eb[rr][cc] + dP[rr][i] * qb[rr][cc]) * f;
-        }
-        const float up = pow2(gi), down = pow2(gl - gi);
-        const float dEt = -Xe[i][cc], dQt = Xq[i][cc], dKb = Xk[i][cc];
+        const float dEt = -me[e], dQt = mq[e], dKb = mk[e];
         const float de = de_a + dEt * up;
         const float dq = dq_p + dQt * up;
         const float dkk = dk_ap + dKb * down;
-        dg[i][cc] = eb[i][cc] * de_a + qb[i][cc] * dq_p - kb[i][cc] * dk_ap + eb[i][cc] * up * dEt
-                    + qb[i][cc] * up * dQt - kb[i][cc] * down * dKb;
-        kbd[i][cc] = kb[i][cc] * down * dKb;
-        const int64_t off = (row0 + int64_t(i) * a.H) * DK + c0 + cc;
+        dg[i][cw] = eb[i][cw] * de_a + qb[i][cw] * dq_p - kb[i][cw] * dk_ap + eb[i][cw] * up * dEt
+                    + qb[i][cw] * up * dQt - kb[i][cw] * down * dKb;
+        kbd[i][cw] = kb[i][cw] * down * dKb;
+        const int64_t off = (row0 + int64_t(i) * a.H) * DK + c0 + cw;
         store_from_f32(dq_out, off, dq);
-        store_from_f32(db_out, off, de * kb[i][cc]);
-        store_from_f32(dk_out, off, dkk + de * bb[i][cc]);
+        store_from_f32(db_out, off, de * kb[i][cw]);
+        store_from_f32(dk_out, off, dkk + de * bb[i][cw]);
     }
     __syncthreads();
     // the chunk-end terms, then the reverse running sum over the chunk's tokens
     if (tid < CB) {
+        const int cc = tid;
+        const float gl = Gb[L - 1][cc];
         float acc = pow2(gl) * rs[cc];
         for (int j = 0; j < L; ++j) acc += kbd[j][cc];
         for (int i = L - 1; i >= 0; --i) {

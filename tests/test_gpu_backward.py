@@ -72,6 +72,21 @@ def test_backward_shapes(dtype, dk, dv):
     _compare(gpu_bwd(x, dtype, g, gs), oracle_bwd(x, g, gs), dtype, f"bwd {dtype} dk={dk} dv={dv}")
 
 
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("f32", 128), ("bf16", 128)])
+def test_backward_strong_decay(dtype, d):
+    """Half of the key channels decay strongly (alpha in [0.05, 0.2]: over a
+    32-token chunk far below 2^-64), half as in the workload recipe; both
+    ways of forming the pairwise sums run in one call (the split products for
+    mild channels, the pairwise loops for strong ones).  alpha stays above the
+    clamp so that the oracle, which uses alpha as given, sees the same values."""
+    x = W.make("batched_bf16", seed=206, B=2, T=100, H=2, dk=d, dv=d, dtype=dtype)
+    rng = np.random.default_rng(207)
+    strong = rng.uniform(0.05, 0.2, x["alpha"][..., : d // 2].shape).astype(np.float32)
+    x["alpha"] = np.ascontiguousarray(np.concatenate([strong, x["alpha"][..., d // 2:]], axis=-1))
+    g, gs = _seeds(x, dtype, 208)
+    _compare(gpu_bwd(x, dtype, g, gs), oracle_bwd(x, g, gs), dtype, f"bwd strong decay {dtype} d={d}")
+
+
 @pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
 def test_backward_varlen_edges(dtype, d):
     """Zero-length, one-token, chunk-boundary and ragged sequences packed together."""
