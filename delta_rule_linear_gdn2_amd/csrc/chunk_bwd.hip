@@ -149,6 +149,21 @@ __device__ __forceinline__ void st4(float* row, int j, float4 v)
     row[j + 3] = v.w;
 }
 
+// ---------------------------------------------------------------------------
+// Products on the FP32 matrix cores
+// (v_mfma_f32_16x16x4_f32, one 16 x 16 output block per instruction group).
+// Lane l of a wavefront supplies A[row l % 16][k l / 16] and B[k l / 16][column
+// l % 16] of a K = 4 step, and holds D[rows 4 (l / 16) .. + 3][column l % 16].
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4_t mfma4(float a, float b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+constexpr int kPad = 4;  // row padding of the LDS operands: the b32 operand reads stay free of bank conflicts
+// Decay over a chunk (log2) above which a channel's pairwise factors
+// 2^(G_i - G_j) may be split into 2^G_i 2^-G_j without overflow.
+constexpr float kSplitMinPrep = -64.f;
+
 // The forward quantities of one chunk.  Rows are padded by one float: lanes
 // that walk different rows of the same column then fall in different banks.
 template <int DK>
@@ -168,6 +183,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdArgs a)
 {
     __shared__ ChunkRows<DK> c;
     __shared__ float Tm[CH][CH + 1];
+    __shared__ float glv[DK];  // G at the chunk's last token
+    __shared__ int split;      // every channel's decay over the chunk above 2^kSplitMinPrep
 
     const int tid = threadIdx.x;
     int64_t idx = blockIdx.x;
@@ -198,38 +215,75 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdArgs a)
         }
     }
     __syncthreads();
+    if (tid == 0) split = 1;
     for (int ch = tid; ch < DK; ch += kBwdThreads) {
         float g = 0.f;
         for (int i = 0; i < L; ++i) {
             g += c.G[i][ch];
             c.G[i][ch] = g;
         }
+        glv[ch] = g;
     }
     __syncthreads();
-    // A and P with every pairwise decay factor formed exactly (exponent <= 0):
-    // zeros above the diagonal, then the CH (CH + 1) / 2 pairs j <= i spread
-    // evenly over the threads (pair p: row i with i (i + 1) / 2 <= p, column
-    // p - i (i + 1) / 2)
-    for (int i2 = tid; i2 < CH * CH; i2 += kBwdThreads) {
-        const int i = i2 / CH, j = i2 % CH;
-        if (j > i) c.A[i][j] = c.P[i][j] = 0.f;
-    }
-    constexpr int kPairs = CH * (CH + 1) / 2;
-    for (int p = tid; p < kPairs; p += kBwdThreads) {
-        int i = int((sqrtf(8.f * float(p) + 1.f) - 1.f) * 0.5f);
-        while ((i + 1) * (i + 2) / 2 <= p) ++i;
-        while (i * (i + 1) / 2 > p) --i;
-        const int j = p - i * (i + 1) / 2;
-        float acc_a = 0.f, acc_p = 0.f;
-        if (i < L) {
-            for (int ch = 0; ch < DK; ++ch) {
-                const float kf = c.K[j][ch] * pow2(c.G[i][ch] - c.G[j][ch]);
-                acc_a += c.E[i][ch] * kf;
-                acc_p += c.Q[i][ch] * kf;
-            }
+    for (int ch = tid; ch < DK; ch += kBwdThreads)
+        if (glv[ch] < kSplitMinPrep) split = 0;  // every writer stores the same value
+    __syncthreads();
+    const int lane = tid & 63, wave = tid >> 6, ln = lane & 15, lk = lane >> 4;
+    if (split) {
+        // A = strict_lower(Et Kd^T), P = lower(Qt Kd^T) with Et = E 2^G, Qt = Q 2^G
+        // (the absorbed factors stored below) and Kd = K 2^-G: the pairwise
+        // factor 2^(G_i - G_j) split into two.  Scaling by a power of two is
+        // exact, and with every decay above 2^kSplitMinPrep nothing overflows.
+        // Kd goes where G was; Kb = Kd 2^G_L below.
+        for (int i2 = tid; i2 < CH * DK; i2 += kBwdThreads) {
+            const int i = i2 / DK, ch = i2 % DK;
+            const float g = c.G[i][ch], up = pow2(g);
+            c.E[i][ch] *= up;
+            c.Q[i][ch] *= up;
+            c.G[i][ch] = c.K[i][ch] * pow2(-g);
         }
-        c.A[i][j] = j < i ? acc_a : 0.f;
-        c.P[i][j] = acc_p;
+        __syncthreads();
+        static_assert(kBwdThreads == 256 && CH == 32, "four wavefronts, one 16 x 16 block of A and of P each");
+        const int r0 = 16 * (wave >> 1), cn = 16 * (wave & 1);
+        f32x4_t aa = {0.f, 0.f, 0.f, 0.f}, pp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+        for (int k0 = 0; k0 < DK; k0 += 4) {
+            const float kd = c.G[cn + ln][k0 + lk];
+            aa = mfma4(c.E[r0 + ln][k0 + lk], kd, aa);
+            pp = mfma4(c.Q[r0 + ln][k0 + lk], kd, pp);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = r0 + 4 * lk + e, j = cn + ln;
+            c.A[i][j] = j < i ? aa[e] : 0.f;
+            c.P[i][j] = j <= i ? pp[e] : 0.f;
+        }
+    } else {
+        // A and P with every pairwise decay factor formed exactly (exponent <= 0):
+        // zeros above the diagonal, then the CH (CH + 1) / 2 pairs j <= i spread
+        // evenly over the threads (pair p: row i with i (i + 1) / 2 <= p, column
+        // p - i (i + 1) / 2)
+        for (int i2 = tid; i2 < CH * CH; i2 += kBwdThreads) {
+            const int i = i2 / CH, j = i2 % CH;
+            if (j > i) c.A[i][j] = c.P[i][j] = 0.f;
+        }
+        constexpr int kPairs = CH * (CH + 1) / 2;
+        for (int p = tid; p < kPairs; p += kBwdThreads) {
+            int i = int((sqrtf(8.f * float(p) + 1.f) - 1.f) * 0.5f);
+            while ((i + 1) * (i + 2) / 2 <= p) ++i;
+            while (i * (i + 1) / 2 > p) --i;
+            const int j = p - i * (i + 1) / 2;
+            float acc_a = 0.f, acc_p = 0.f;
+            if (i < L) {
+                for (int ch = 0; ch < DK; ++ch) {
+                    const float kf = c.K[j][ch] * pow2(c.G[i][ch] - c.G[j][ch]);
+                    acc_a += c.E[i][ch] * kf;
+                    acc_p += c.Q[i][ch] * kf;
+                }
+            }
+            c.A[i][j] = j < i ? acc_a : 0.f;
+            c.P[i][j] = acc_p;
+        }
     }
     __syncthreads();
     // Tm = (I + A)^-1 by columns: lane j keeps column j in registers
@@ -252,13 +306,18 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdArgs a)
 #pragma unroll
         for (int i = 0; i < CH; ++i) Tm[i][j] = t[i];
     }
-    // absorb the decay into the row and column factors
+    // absorb the decay into the row and column factors (already done for Et, Qt
+    // on the split path)
     for (int i2 = tid; i2 < L * DK; i2 += kBwdThreads) {
         const int i = i2 / DK, ch = i2 % DK;
-        const float g = c.G[i][ch], up = pow2(g);
-        c.E[i][ch] *= up;
-        c.Q[i][ch] *= up;
-        c.K[i][ch] *= pow2(c.G[L - 1][ch] - g);
+        if (split) {
+            c.K[i][ch] = c.G[i][ch] * pow2(glv[ch]);
+        } else {
+            const float g = c.G[i][ch], up = pow2(g);
+            c.E[i][ch] *= up;
+            c.Q[i][ch] *= up;
+            c.K[i][ch] *= pow2(glv[ch] - g);
+        }
     }
     __syncthreads();
     float* dst = a.ws_prep + prep_base(a, row, slot, h);
@@ -273,7 +332,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdArgs a)
         dst[kPrepE + CH * DK + i2] = c.Q[i][ch];
         dst[kPrepE + 2 * CH * DK + i2] = c.K[i][ch];
     }
-    for (int ch = tid; ch < DK; ch += kBwdThreads) dst[kPrepE + 3 * CH * DK + ch] = pow2(c.G[L - 1][ch]);
+    for (int ch = tid; ch < DK; ch += kBwdThreads) dst[kPrepE + 3 * CH * DK + ch] = pow2(glv[ch]);
 }
 
 // Thread layout of the sequential kernels: lane column jj = tid % 32 of the
@@ -330,18 +389,6 @@ struct PrepRegs {
         if (tid < DK / 4) st4(gam, 4 * tid, vg);
     }
 };
-
-// ---------------------------------------------------------------------------
-// The sequential kernels' products on the FP32 matrix cores
-// (v_mfma_f32_16x16x4_f32, one 16 x 16 output block per instruction group).
-// Lane l of a wavefront supplies A[row l % 16][k l / 16] and B[k l / 16][column
-// l % 16] of a K = 4 step, and holds D[rows 4 (l / 16) .. + 3][column l % 16].
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ f32x4_t mfma4(float a, float b, f32x4_t c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-constexpr int kPad = 4;  // row padding of the LDS operands: the b32 operand reads stay free of bank conflicts
 
 // ---------------------------------------------------------------------------
 // bwd_states: the forward again, storing the state at every chunk start.
