@@ -26,8 +26,12 @@
 //             db = de k,  dk += de b,  dw = dZ v,  dv = dZ w
 // (dg is the gradient with respect to the natural-log cumulative decay.)
 // Every decay factor is a power of two with a non-positive exponent, so
-// nothing overflows.  alpha is clamped to [2^-15, 1] as in the forward
-// kernels; the gradient is zero where the clamp is active.
+// nothing overflows.  Where a channel's decay over a chunk stays above 2^-64,
+// the pairwise sums use the factor split as 2^G_i 2^-G_j, which turns them
+// into matrix products; a power-of-two scale is exact, so the sums are the
+// same up to rounding, and below that bound the pairwise form is kept.  alpha
+// is clamped to [2^-15, 1] as in the forward kernels; the gradient is zero
+// where the clamp is active.
 //
 // Four kernels, 32-token chunks (the same mathematics as any chunk size):
 //   bwd_prep    (chunk x head, all parallel)            A, P, Tm = (I + A)^-1,
@@ -40,8 +44,9 @@
 //   bwd_keys    (chunk x head x channel block)          dA, dP, dEt, dQt, dKb
 //               over all value columns, then dq, dk, db and dalpha.
 // The two sequential kernels only multiply: all of a chunk's triangular
-// algebra is done in parallel beforehand.  Each thread owns several outputs
-// of every product so that one LDS read feeds several FMAs.
+// algebra is done in parallel beforehand.  The products run on the FP32
+// matrix cores (full FP32 arithmetic), one 16 x 16 output block per
+// wavefront and instruction group.
 #include "gdn2_device.hpp"
 #include "launch.hpp"
 
