@@ -701,28 +701,36 @@ __global__ __launch_bounds__(kSeqThreads) void bwd_dstate_kernel(BwdArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// bwd_keys: one chunk of one head, channels c0 .. c0 + 31.  Thread layout:
-// column (token j or channel cc) = tid % 32, rows i0 + 8 r with i0 = tid / 32.
+// bwd_keys: one chunk of one head, channels c0 .. c0 + CB - 1 (CB = 64 when
+// both head sizes are at least 64, else 32), 8 CB threads.  Thread layout of the
+// loads and elementwise steps: column (token j or channel cc) = tid % CB, rows
+// i0 + 8 r with i0 = tid / CB.
+template <int DK, int DV>
+constexpr int keys_cb() { return DK >= 64 && DV >= 64 ? 64 : 32; }
+
 template <typename T, int DK, int DV>
-__global__ __launch_bounds__(kBwdThreads) void bwd_keys_kernel(BwdArgs a)
+__global__ __launch_bounds__((8 * keys_cb<DK, DV>())) void bwd_keys_kernel(BwdArgs a)
 {
-    constexpr int CB = 32;                // channels per block
+    constexpr int CB = keys_cb<DK, DV>(); // channels per block
+    constexpr int NT = 8 * CB;            // threads: CB / 8 wavefronts
     constexpr int DH = DV < 64 ? DV : 64; // value columns per pass
-    static_assert(DK % CB == 0 && DV % DH == 0 && DH >= CB, "block shapes");
-    // per pass: U, dX, dO rows and the block's S and dS' rows; afterwards dg and Kb dKb
-    __shared__ float buf[5][CH][DH + kPad];
+    static_assert(DK % CB == 0 && DV % DH == 0 && DH >= CB && CH == 32, "block shapes");
+    // per pass: U, dX, dO rows and the block's S and dS' rows; afterwards the
+    // split factors (rows) and dg, Kb dKb (channel rows)
+    __shared__ float rowbuf[3][CH][DH + kPad];
+    __shared__ float sbuf[2][CB][DH + kPad];
     __shared__ float dA[CH][CH + 1], dP[CH][CH + 1];
     __shared__ float qb[CH][CB + 1], kb[CH][CB + 1], eb[CH][CB + 1], bb[CH][CB + 1], ab[CH][CB + 1], Gb[CH][CB + 1];
     __shared__ float rs[CB];
-    float (*Us)[DH + kPad] = buf[0];
-    float (*dXs)[DH + kPad] = buf[1];
-    float (*dOs)[DH + kPad] = buf[2];
-    float (*Sb)[DH + kPad] = buf[3];
-    float (*dSb)[DH + kPad] = buf[4];
+    float (*Us)[DH + kPad] = rowbuf[0];
+    float (*dXs)[DH + kPad] = rowbuf[1];
+    float (*dOs)[DH + kPad] = rowbuf[2];
+    float (*Sb)[DH + kPad] = sbuf[0];
+    float (*dSb)[DH + kPad] = sbuf[1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 15, lk = lane >> 4;
-    const int col = tid % 32, i0 = tid / 32;
+    const int col = tid % CB, i0 = tid / CB;
     constexpr int nblk = DK / CB;
     int64_t idx;
     int cblk;
@@ -746,21 +754,27 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_keys_kernel(BwdArgs a)
 
     // the passes' rows: four consecutive columns per thread, the next pass's
     // loads issued before this pass's products (the barriers wait on LDS only)
-    constexpr int NQ = CH * DH / 4 / kBwdThreads;  // quads per thread
-    static_assert(NQ >= 1 && CH * DH % (4 * kBwdThreads) == 0, "staging layout");
-    float4 vu[NQ], vx[NQ], vo[NQ], vs[NQ], vd[NQ];
+    constexpr int NQR = CH * DH / 4 / NT;  // quads per thread of the token rows
+    constexpr int NQS = CB * DH / 4 / NT;  // and of the channel rows
+    static_assert(NQR >= 1 && NQS >= 1 && CH * DH % (4 * NT) == 0 && CB * DH % (4 * NT) == 0, "staging layout");
+    float4 vu[NQR], vx[NQR], vo[NQR], vs[NQS], vd[NQS];
     auto issue = [&](int jh) {
+        const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-        for (int qd = 0; qd < NQ; ++qd) {
-            const int i4 = tid + kBwdThreads * qd;
+        for (int qd = 0; qd < NQR; ++qd) {
+            const int i4 = tid + NT * qd;
             const int i = i4 / (DH / 4), j = (i4 % (DH / 4)) * 4;
             const bool live = i < L;
             const int64_t off = (row0 + int64_t(i) * a.H) * DV + jh + j;
-            const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
             vu[qd] = live ? load4(a.ws_u, off) : z4;
             vx[qd] = live ? load4(a.ws_dx, off) : z4;
             vo[qd] = live ? load4(dO, off) : z4;
-            const int64_t soff = sbase + int64_t(c0 + i) * DV + jh + j;  // i doubles as the channel (CB == CH)
+        }
+#pragma unroll
+        for (int qd = 0; qd < NQS; ++qd) {
+            const int i4 = tid + NT * qd;
+            const int c = i4 / (DH / 4), j = (i4 % (DH / 4)) * 4;
+            const int64_t soff = sbase + int64_t(c0 + c) * DV + jh + j;
             vs[qd] = load4(a.ws_states, soff);
             vd[qd] = load4(a.ws_dstates, soff);
         }
@@ -786,35 +800,47 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_keys_kernel(BwdArgs a)
     }
 
     // Over all value columns, on the matrix cores: dX U^T, dO U^T (-> dA, dP),
-    // dX S^T, dO S^T, U dS'^T (-> dEt, dQt, dKb); wavefront w forms the 16 x 16
-    // block (rows 16 (w / 2), columns 16 (w % 2)) of each.  The row sums of
-    // dS' . S go with the first 32 threads.
-    static_assert(kBwdThreads == 256 && CH == 32, "four wavefronts, one block of each 32 x 32 product");
+    // dX S^T, dO S^T, U dS'^T (-> dEt, dQt, dKb).  Wavefront w forms the 16 x 16
+    // blocks (tokens 16 tb, channels 16 cb) of the last three, and of dA, dP
+    // (tokens 16 tb, tokens 16 jb) the ones given by:
+    //   CB = 32 (4 wavefronts): tb = w / 2, cb = jb = w % 2, both dA and dP;
+    //   CB = 64 (8 wavefronts): tb = w % 2, cb = w / 2, jb = (w / 2) % 2, dA for
+    //   w < 4 and dP for w >= 4.
+    // The row sums of dS' . S go with the first CB threads.
+    const int tb = CB == 32 ? wave >> 1 : wave & 1;
+    const int cb = CB == 32 ? wave & 1 : wave >> 1;
+    const int jb = CB == 32 ? wave & 1 : (wave >> 1) & 1;
+    const bool do_a = CB == 32 || wave < 4, do_p = CB == 32 || wave >= 4;
     const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
     f32x4_t ma = zero4, mp = zero4, me = zero4, mq = zero4, mk = zero4;
     float xr = 0.f;
     for (int jh = 0; jh < DV; jh += DH) {
 #pragma unroll
-        for (int qd = 0; qd < NQ; ++qd) {
-            const int i4 = tid + kBwdThreads * qd;
+        for (int qd = 0; qd < NQR; ++qd) {
+            const int i4 = tid + NT * qd;
             const int i = i4 / (DH / 4), j = (i4 % (DH / 4)) * 4;
             st4(Us[i], j, vu[qd]);
             st4(dXs[i], j, vx[qd]);
             st4(dOs[i], j, vo[qd]);
-            st4(Sb[i], j, vs[qd]);
-            st4(dSb[i], j, vd[qd]);
+        }
+#pragma unroll
+        for (int qd = 0; qd < NQS; ++qd) {
+            const int i4 = tid + NT * qd;
+            const int c = i4 / (DH / 4), j = (i4 % (DH / 4)) * 4;
+            st4(Sb[c], j, vs[qd]);
+            st4(dSb[c], j, vd[qd]);
         }
         if (jh + DH < DV) issue(jh + DH);
         lds_sync();
         {
-            const int ra = 16 * (wave >> 1) + ln, rb = 16 * (wave & 1) + ln;  // A rows (tokens), B rows (tokens or channels)
+            const int ra = 16 * tb + ln, rc = 16 * cb + ln, rj = 16 * jb + ln;
 #pragma unroll 4
             for (int k0 = 0; k0 < DH; k0 += 4) {
                 const int kk = k0 + lk;
                 const float ax = dXs[ra][kk], ao = dOs[ra][kk], au = Us[ra][kk];
-                const float bu = Us[rb][kk], bs = Sb[rb][kk], bd = dSb[rb][kk];
-                ma = mfma4(ax, bu, ma);
-                mp = mfma4(ao, bu, mp);
+                const float bs = Sb[rc][kk], bd = dSb[rc][kk], bu = Us[rj][kk];
+                if (do_a) ma = mfma4(ax, bu, ma);
+                if (do_p) mp = mfma4(ao, bu, mp);
                 me = mfma4(ax, bs, me);
                 mq = mfma4(ao, bs, mq);
                 mk = mfma4(au, bd, mk);
@@ -824,15 +850,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_keys_kernel(BwdArgs a)
         }
         lds_sync();
     }
-    // block results: row 16 (w / 2) + 4 lk + e, column 16 (w % 2) + ln
+    // dA, dP blocks: token 16 tb + 4 lk + e, token 16 jb + ln
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const int i = 16 * (wave >> 1) + 4 * lk + e, j = 16 * (wave & 1) + ln;
-        dA[i][j] = j < i ? -ma[e] : 0.f;
-        dP[i][j] = j <= i ? mp[e] : 0.f;
+        const int i = 16 * tb + 4 * lk + e, j = 16 * jb + ln;
+        if (do_a) dA[i][j] = j < i ? -ma[e] : 0.f;
+        if (do_p) dP[i][j] = j <= i ? mp[e] : 0.f;
     }
     if (tid < CB) rs[tid] = xr;
-    for (int cc = tid; cc < CB; cc += kBwdThreads) {  // running sums of the block's decay
+    for (int cc = tid; cc < CB; cc += NT) {  // running sums of the block's decay
         float g = 0.f;
         for (int i = 0; i < L; ++i) {
             g += Gb[i][cc];
@@ -850,9 +876,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_keys_kernel(BwdArgs a)
     // above 2^kSplitMin (then 2^-G <= 2^-kSplitMin).  Other channels take the
     // pairwise loops below.  Rows past the chunk are zero in every factor.
     constexpr float kSplitMin = -64.f;
-    float (*K2)[DH + kPad] = buf[2];
-    float (*E2)[DH + kPad] = buf[3];
-    float (*Q2)[DH + kPad] = buf[4];
+    float (*K2)[DH + kPad] = rowbuf[0];
+    float (*E2)[DH + kPad] = rowbuf[1];
+    float (*Q2)[DH + kPad] = rowbuf[2];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {  // thread (i0 + 8 r, col)
         const int i = i0 + 8 * r;
@@ -864,7 +890,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_keys_kernel(BwdArgs a)
     __syncthreads();
     f32x4_t y1 = zero4, y2 = zero4, y3 = zero4;
     {
-        const int ra = 16 * (wave >> 1) + ln, cn = 16 * (wave & 1) + ln;
+        const int ra = 16 * tb + ln, cn = 16 * cb + ln;
 #pragma unroll
         for (int k0 = 0; k0 < CH; k0 += 4) {
             const int kk = k0 + lk;
@@ -877,18 +903,18 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_keys_kernel(BwdArgs a)
     }
 
     // pairwise and absorbed-factor gradients, in the block layout: token
-    // 16 (w / 2) + 4 lk + e, channel cw
-    float (*dg)[DH + kPad] = buf[0];
-    float (*kbd)[DH + kPad] = buf[1];
+    // 16 tb + 4 lk + e, channel cw
+    float (*dg)[DH + kPad] = sbuf[0];
+    float (*kbd)[DH + kPad] = sbuf[1];
     T* dq_out = static_cast<T*>(a.dq);
     T* dk_out = static_cast<T*>(a.dk);
     T* db_out = static_cast<T*>(a.db);
-    const int cw = 16 * (wave & 1) + ln;
+    const int cw = 16 * cb + ln;
     const float glw = Gb[L - 1][cw];
     const bool split = glw >= kSplitMin;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const int i = 16 * (wave >> 1) + 4 * lk + e;
+        const int i = 16 * tb + 4 * lk + e;
         if (i >= L) continue;
         const float gi = Gb[i][cw];
         const float up = pow2(gi), down = pow2(glw - gi);
@@ -963,8 +989,9 @@ hipError_t launch_keys(const BwdArgs& a, hipStream_t stream)
 {
     const int64_t groups = int64_t(a.B) * a.slots * a.H;
     if (groups == 0) return hipSuccess;
-    const int64_t blocks = xcd_grid(groups, DK / 32);
-    hipLaunchKernelGGL((bwd_keys_kernel<T, DK, DV>), dim3(unsigned(blocks)), dim3(kBwdThreads), 0, stream, a);
+    constexpr int CB = keys_cb<DK, DV>();
+    const int64_t blocks = xcd_grid(groups, DK / CB);
+    hipLaunchKernelGGL((bwd_keys_kernel<T, DK, DV>), dim3(unsigned(blocks)), dim3(8 * CB), 0, stream, a);
     return hipGetLastError();
 }
 
