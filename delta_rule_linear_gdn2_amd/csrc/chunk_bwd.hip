@@ -461,6 +461,9 @@ __global__ __launch_bounds__(kSeqThreads) void bwd_states_kernel(BwdArgs a)
     };
     if (M > 0) issue(0);
     for (int m = 0; m < M; ++m) {
+        const int64_t t0 = bos + int64_t(m) * CH;
+        const int L = int(eos - t0 < CH ? eos - t0 : CH);
+        const int64_t row0 = (brow * a.T + t0) * a.H + h;
         const int64_t slot = slot_of(a, n, bos, m);
         float* dst = a.ws_states + slot_base(a, brow, slot, h) + j0;
 #pragma unroll
@@ -487,14 +490,18 @@ __global__ __launch_bounds__(kSeqThreads) void bwd_states_kernel(BwdArgs a)
             for (int i = 0; i < 4; ++i) Xs[r0 + 4 * lk + i][c] = Zs[r0 + 4 * lk + i][c] - acc[i];
         }
         lds_sync();
-        // U = Tm X
+        // U = Tm X (also to the workspace, for the key kernel)
         if (wave < 4) {
             const int r0 = 16 * (wave >> 1), c = 16 * (wave & 1) + ln;
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int k0 = 0; k0 < CH; k0 += 4) acc = mfma4(Tm[r0 + ln][k0 + lk], Xs[k0 + lk][c], acc);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Us[r0 + 4 * lk + i][c] = acc[i];
+            for (int i = 0; i < 4; ++i) {
+                const int r = r0 + 4 * lk + i;
+                Us[r][c] = acc[i];
+                if (r < L) a.ws_u[(row0 + int64_t(r) * a.H) * dv + j0 + c] = acc[i];
+            }
         }
         lds_sync();
         // S <- 2^G_L S + Kb^T U  (Kb and U are zero past the chunk)
@@ -516,10 +523,10 @@ __global__ __launch_bounds__(kSeqThreads) void bwd_states_kernel(BwdArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// bwd_dstate: chunks in reverse, carrying the state gradient.  Wavefront w
-// owns the gradient blocks w, w + 8, ... in accumulator registers;
-// wavefronts 0..3 form the blocks of X and U, wavefronts 4..7 those of dU
-// and dX.
+// bwd_dstate: chunks in reverse, carrying the state gradient (U comes from
+// bwd_states through the workspace).  Wavefront w owns the gradient blocks
+// w, w + 8, ... in accumulator registers; wavefronts 0..3 form the blocks of
+// dU and dX.
 template <typename T, int DK>
 __global__ __launch_bounds__(kSeqThreads) void bwd_dstate_kernel(BwdArgs a)
 {
@@ -528,9 +535,8 @@ __global__ __launch_bounds__(kSeqThreads) void bwd_dstate_kernel(BwdArgs a)
     __shared__ float Et[CH][DK + kPad], Qt[CH][DK + kPad], Kb[CH][DK + kPad];
     __shared__ float Tm[CH][CH + kPad], Pm[CH][CH + kPad];
     __shared__ float gam[DK];
-    __shared__ float Ss[DK][kTile];   // chunk-start state
     __shared__ float dSs[DK][kTile];  // gradient of the chunk-end state
-    __shared__ float Zs[CH][kTile], Xs[CH][kTile], dUs[CH][kTile], dOs[CH][kTile], dXs[CH][kTile];
+    __shared__ float dUs[CH][kTile], dOs[CH][kTile], dXs[CH][kTile];
     __shared__ float Vs[CH][kTile], Ws[CH][kTile];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -567,20 +573,16 @@ __global__ __launch_bounds__(kSeqThreads) void bwd_dstate_kernel(BwdArgs a)
         }
     }
 
-    // chunk m's prepared rows, chunk-start state and v, w, dO rows, loaded one chunk ahead
+    // chunk m's prepared rows and v, w, dO rows, loaded one chunk ahead
     const int M = int((eos - bos + CH - 1) / CH);
-    constexpr int RS = DK / NG;
     PrepRegs<DK, true, kSeqThreads> pf;
-    float pv[RR], pw[RR], po[RR], ps[RS];
+    float pv[RR], pw[RR], po[RR];
     auto issue = [&](int m) {
         const int64_t t0 = bos + int64_t(m) * CH;
         const int L = int(eos - t0 < CH ? eos - t0 : CH);
         const int64_t row0 = (brow * a.T + t0) * a.H + h;
         const int64_t slot = slot_of(a, n, bos, m);
         pf.issue(a.ws_prep + prep_base(a, brow, slot, h), tid);
-        const int64_t sb = slot_base(a, brow, slot, h) + j0 + jj;
-#pragma unroll
-        for (int r = 0; r < RS; ++r) ps[r] = a.ws_states[sb + int64_t(i0 + NG * r) * dv];
 #pragma unroll
         for (int r = 0; r < RR; ++r) {
             const int i = i0 + NG * r;
@@ -606,29 +608,19 @@ __global__ __launch_bounds__(kSeqThreads) void bwd_dstate_kernel(BwdArgs a)
 #pragma unroll
             for (int i = 0; i < 4; ++i) dsd[int64_t(r0 + i) * dv + c] = ds[u][i];
         }
-        lds_sync();  // the previous chunk is done with the prepared rows, the state and the row buffers
+        lds_sync();  // the previous chunk is done with the prepared rows and the row buffers
         pf.template store<DK + kPad, CH + kPad>(Et, Qt, Kb, Tm, Pm, gam, tid);
-#pragma unroll
-        for (int r = 0; r < RS; ++r) Ss[i0 + NG * r][jj] = ps[r];
 #pragma unroll
         for (int r = 0; r < RR; ++r) {
             const int i = i0 + NG * r;
             Vs[i][jj] = pv[r];
             Ws[i][jj] = pw[r];
-            Zs[i][jj] = pw[r] * pv[r];
             dOs[i][jj] = po[r];
         }
         if (m > 0) issue(m - 1);  // in flight while this chunk is computed
         lds_sync();
-        if (wave < 4) {  // X = Z - Et S
+        if (wave < 4) {  // dU = Kb dS' + Pm^T dO
             const int r0 = 16 * (wave >> 1), c = 16 * (wave & 1) + ln;
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-            for (int k0 = 0; k0 < DK; k0 += 4) acc = mfma4(Et[r0 + ln][k0 + lk], Ss[k0 + lk][c], acc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Xs[r0 + 4 * lk + i][c] = Zs[r0 + 4 * lk + i][c] - acc[i];
-        } else {  // dU = Kb dS' + Pm^T dO
-            const int r0 = 16 * ((wave - 4) >> 1), c = 16 * (wave & 1) + ln;
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
             for (int k0 = 0; k0 < DK; k0 += 4) acc = mfma4(Kb[r0 + ln][k0 + lk], dSs[k0 + lk][c], acc);
@@ -638,18 +630,8 @@ __global__ __launch_bounds__(kSeqThreads) void bwd_dstate_kernel(BwdArgs a)
             for (int i = 0; i < 4; ++i) dUs[r0 + 4 * lk + i][c] = acc[i];
         }
         lds_sync();
-        if (wave < 4) {  // U = Tm X (to the workspace for the key kernel)
+        if (wave < 4) {  // dX = Tm^T dU (zero past the chunk), dw = dX v, dv = dX w
             const int r0 = 16 * (wave >> 1), c = 16 * (wave & 1) + ln;
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int k0 = 0; k0 < CH; k0 += 4) acc = mfma4(Tm[r0 + ln][k0 + lk], Xs[k0 + lk][c], acc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = r0 + 4 * lk + i;
-                if (row < L) a.ws_u[(row0 + int64_t(row) * a.H) * dv + j0 + c] = acc[i];
-            }
-        } else {  // dX = Tm^T dU (zero past the chunk), dw = dX v, dv = dX w
-            const int r0 = 16 * ((wave - 4) >> 1), c = 16 * (wave & 1) + ln;
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int k0 = 0; k0 < CH; k0 += 4) acc = mfma4(Tm[k0 + lk][r0 + ln], dUs[k0 + lk][c], acc);
