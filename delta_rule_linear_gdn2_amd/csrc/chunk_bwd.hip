@@ -37,9 +37,9 @@
 //   bwd_prep    (chunk x head, all parallel)            A, P, Tm = (I + A)^-1,
 //               Et, Qt, Kb and 2^G_L of every chunk, once, into the workspace;
 //   bwd_states  (chain x value tile, chunks in order)   X, U = Tm X and the
-//               state update; stores every chunk-start state;
-//   bwd_dstate  (chain x value tile, chunks in reverse) U, dU, dX = Tm^T dU and
-//               the state-gradient recurrence; dv, dw and dS0; stores U and dX
+//               state update; stores every chunk-start state and the U rows;
+//   bwd_dstate  (chain x value tile, chunks in reverse) dU, dX = Tm^T dU and
+//               the state-gradient recurrence; dv, dw and dS0; stores the dX
 //               rows and each chunk-end state gradient;
 //   bwd_keys    (chunk x head x channel block)          dA, dP, dEt, dQt, dKb
 //               over all value columns, then dq, dk, db and dalpha.
