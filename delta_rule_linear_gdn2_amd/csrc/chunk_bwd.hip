@@ -528,16 +528,23 @@ __global__ __launch_bounds__(kSeqThreads) void bwd_states_kernel(BwdArgs a)
 // w, w + 8, ... in accumulator registers; wavefronts 0..3 form the blocks of
 // dU and dX.
 template <typename T, int DK>
-__global__ __launch_bounds__(kSeqThreads) void bwd_dstate_kernel(BwdArgs a)
+__global__ __launch_bounds__(kSeqThreads, 4) void bwd_dstate_kernel(BwdArgs a)
 {
     constexpr int NTS = (DK / 16) * (kTile / 16);
     constexpr int TPW = (NTS + 7) / 8;
     __shared__ float Et[CH][DK + kPad], Qt[CH][DK + kPad], Kb[CH][DK + kPad];
-    __shared__ float Tm[CH][CH + kPad], Pm[CH][CH + kPad];
+    __shared__ float Tm[CH][CH + 1], Pm[CH][CH + 1];  // read transposed: stride 33 keeps them conflict-free
     __shared__ float gam[DK];
     __shared__ float dSs[DK][kTile];  // gradient of the chunk-end state
-    __shared__ float dUs[CH][kTile], dOs[CH][kTile], dXs[CH][kTile];
-    __shared__ float Vs[CH][kTile], Ws[CH][kTile];
+    __shared__ float dOs[CH][kTile];
+    // dU and dX live in Kb's space, which is free once dU is formed (about 80 KB
+    // of LDS in all at dk = 128, so that two workgroups share a CU); with the
+    // smallest heads Kb is too small and they get their own
+    constexpr bool kInKb = 2 * CH * kTile <= CH * (DK + kPad);
+    __shared__ float ux_own[kInKb ? 1 : 2 * CH * kTile];
+    float* ux = kInKb ? &Kb[0][0] : ux_own;
+    float (*dUs)[kTile] = reinterpret_cast<float (*)[kTile]>(ux);
+    float (*dXs)[kTile] = reinterpret_cast<float (*)[kTile]>(ux + CH * kTile);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 15, lk = lane >> 4;
@@ -573,10 +580,12 @@ __global__ __launch_bounds__(kSeqThreads) void bwd_dstate_kernel(BwdArgs a)
         }
     }
 
-    // chunk m's prepared rows and v, w, dO rows, loaded one chunk ahead
+    // chunk m's prepared rows, dO rows, and (wavefronts 0..3, in the layout of
+    // their dX block) v and w; loaded at the chunk's start (the other
+    // workgroup on the CU covers their latency)
     const int M = int((eos - bos + CH - 1) / CH);
     PrepRegs<DK, true, kSeqThreads> pf;
-    float pv[RR], pw[RR], po[RR];
+    float po[RR], pv[4], pw[4];
     auto issue = [&](int m) {
         const int64_t t0 = bos + int64_t(m) * CH;
         const int L = int(eos - t0 < CH ? eos - t0 : CH);
@@ -586,14 +595,20 @@ __global__ __launch_bounds__(kSeqThreads) void bwd_dstate_kernel(BwdArgs a)
 #pragma unroll
         for (int r = 0; r < RR; ++r) {
             const int i = i0 + NG * r;
-            const bool live = i < L;
             const int64_t off = (row0 + int64_t(i) * a.H) * dv + j0 + jj;
-            pv[r] = live ? load_as_f32(v, off) : 0.f;
-            pw[r] = live ? load_as_f32(w, off) : 0.f;
-            po[r] = live ? load_as_f32(dO, off) : 0.f;
+            po[r] = i < L ? load_as_f32(dO, off) : 0.f;
+        }
+        if (wave < 4) {
+            const int r0 = 16 * (wave >> 1) + 4 * lk, c = 16 * (wave & 1) + ln;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = r0 + e;
+                const int64_t off = (row0 + int64_t(i) * a.H) * dv + j0 + c;
+                pv[e] = i < L ? load_as_f32(v, off) : 0.f;
+                pw[e] = i < L ? load_as_f32(w, off) : 0.f;
+            }
         }
     };
-    if (M > 0) issue(M - 1);
     for (int m = M - 1; m >= 0; --m) {
         const int64_t t0 = bos + int64_t(m) * CH;
         const int L = int(eos - t0 < CH ? eos - t0 : CH);
@@ -608,26 +623,31 @@ __global__ __launch_bounds__(kSeqThreads) void bwd_dstate_kernel(BwdArgs a)
 #pragma unroll
             for (int i = 0; i < 4; ++i) dsd[int64_t(r0 + i) * dv + c] = ds[u][i];
         }
+        issue(m);
         lds_sync();  // the previous chunk is done with the prepared rows and the row buffers
-        pf.template store<DK + kPad, CH + kPad>(Et, Qt, Kb, Tm, Pm, gam, tid);
+        pf.template store<DK + kPad, CH + 1>(Et, Qt, Kb, Tm, Pm, gam, tid);
 #pragma unroll
-        for (int r = 0; r < RR; ++r) {
-            const int i = i0 + NG * r;
-            Vs[i][jj] = pv[r];
-            Ws[i][jj] = pw[r];
-            dOs[i][jj] = po[r];
+        for (int r = 0; r < RR; ++r) dOs[i0 + NG * r][jj] = po[r];
+        float vv[4], ww[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            vv[e] = pv[e];
+            ww[e] = pw[e];
         }
-        if (m > 0) issue(m - 1);  // in flight while this chunk is computed
         lds_sync();
+        f32x4_t du = {0.f, 0.f, 0.f, 0.f};
         if (wave < 4) {  // dU = Kb dS' + Pm^T dO
             const int r0 = 16 * (wave >> 1), c = 16 * (wave & 1) + ln;
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
-            for (int k0 = 0; k0 < DK; k0 += 4) acc = mfma4(Kb[r0 + ln][k0 + lk], dSs[k0 + lk][c], acc);
+            for (int k0 = 0; k0 < DK; k0 += 4) du = mfma4(Kb[r0 + ln][k0 + lk], dSs[k0 + lk][c], du);
 #pragma unroll
-            for (int k0 = 0; k0 < CH; k0 += 4) acc = mfma4(Pm[k0 + lk][r0 + ln], dOs[k0 + lk][c], acc);
+            for (int k0 = 0; k0 < CH; k0 += 4) du = mfma4(Pm[k0 + lk][r0 + ln], dOs[k0 + lk][c], du);
+        }
+        lds_sync();  // Kb is read: its space takes dU and dX
+        if (wave < 4) {
+            const int r0 = 16 * (wave >> 1), c = 16 * (wave & 1) + ln;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dUs[r0 + 4 * lk + i][c] = acc[i];
+            for (int i = 0; i < 4; ++i) dUs[r0 + 4 * lk + i][c] = du[i];
         }
         lds_sync();
         if (wave < 4) {  // dX = Tm^T dU (zero past the chunk), dw = dX v, dv = dX w
@@ -643,8 +663,8 @@ __global__ __launch_bounds__(kSeqThreads) void bwd_dstate_kernel(BwdArgs a)
                 if (row < L) {
                     const int64_t off = (row0 + int64_t(row) * a.H) * dv + j0 + c;
                     a.ws_dx[off] = dx;
-                    store_from_f32(dw_out, off, dx * Vs[row][c]);
-                    store_from_f32(dv_out, off, dx * Ws[row][c]);
+                    store_from_f32(dw_out, off, dx * vv[i]);
+                    store_from_f32(dv_out, off, dx * ww[i]);
                 }
             }
         }
