@@ -715,20 +715,24 @@ __global__ __launch_bounds__((8 * keys_cb<DK, DV>())) void bwd_keys_kernel(BwdAr
 {
     constexpr int CB = keys_cb<DK, DV>(); // channels per block
     constexpr int NT = 8 * CB;            // threads: CB / 8 wavefronts
-    constexpr int DH = DV < 64 ? DV : 64; // value columns per pass
-    static_assert(DK % CB == 0 && DV % DH == 0 && DH >= CB && CH == 32, "block shapes");
-    // per pass: U, dX, dO rows and the block's S and dS' rows; afterwards the
-    // split factors (rows) and dg, Kb dKb (channel rows)
-    __shared__ float rowbuf[3][CH][DH + kPad];
-    __shared__ float sbuf[2][CB][DH + kPad];
+    constexpr int DH = 32;                // value columns per pass
+    static_assert(DK % CB == 0 && DV % DH == 0 && CH == 32, "block shapes");
+    // One region, used in turn for: each pass's U, dX, dO rows and the block's
+    // S, dS' rows; the split factors K2, E2, Q2; dg and Kb dKb.  With alpha and
+    // b read again where they are used, the kernel fits in about 74 KB of LDS
+    // at CB = 64, so that two workgroups share a CU.
+    constexpr int RP = DH + kPad, RC = CB + kPad;  // row strides: pass rows, channel-wide rows
+    constexpr int kPassF = 3 * CH * RP + 2 * CB * RP, kSplitF = 3 * CH * RC, kGradF = 2 * CH * RC;
+    constexpr int kFlat = kPassF > kSplitF ? (kPassF > kGradF ? kPassF : kGradF) : (kSplitF > kGradF ? kSplitF : kGradF);
+    __shared__ __align__(16) float flat[kFlat];
     __shared__ float dA[CH][CH + 1], dP[CH][CH + 1];
-    __shared__ float qb[CH][CB + 1], kb[CH][CB + 1], eb[CH][CB + 1], bb[CH][CB + 1], ab[CH][CB + 1], Gb[CH][CB + 1];
+    __shared__ float qb[CH][CB + 1], kb[CH][CB + 1], eb[CH][CB + 1], Gb[CH][CB + 1];
     __shared__ float rs[CB];
-    float (*Us)[DH + kPad] = rowbuf[0];
-    float (*dXs)[DH + kPad] = rowbuf[1];
-    float (*dOs)[DH + kPad] = rowbuf[2];
-    float (*Sb)[DH + kPad] = sbuf[0];
-    float (*dSb)[DH + kPad] = sbuf[1];
+    float (*Us)[RP] = reinterpret_cast<float (*)[RP]>(flat);
+    float (*dXs)[RP] = reinterpret_cast<float (*)[RP]>(flat + CH * RP);
+    float (*dOs)[RP] = reinterpret_cast<float (*)[RP]>(flat + 2 * CH * RP);
+    float (*Sb)[RP] = reinterpret_cast<float (*)[RP]>(flat + 3 * CH * RP);
+    float (*dSb)[RP] = reinterpret_cast<float (*)[RP]>(flat + 3 * CH * RP + CB * RP);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 15, lk = lane >> 4;
@@ -756,9 +760,8 @@ __global__ __launch_bounds__((8 * keys_cb<DK, DV>())) void bwd_keys_kernel(BwdAr
 
     // the passes' rows: four consecutive columns per thread, the next pass's
     // loads issued before this pass's products (the barriers wait on LDS only)
-    constexpr int NQR = CH * DH / 4 / NT;  // quads per thread of the token rows
-    constexpr int NQS = CB * DH / 4 / NT;  // and of the channel rows
-    static_assert(NQR >= 1 && NQS >= 1 && CH * DH % (4 * NT) == 0 && CB * DH % (4 * NT) == 0, "staging layout");
+    constexpr int QR = CH * DH / 4, QS = CB * DH / 4;      // quads of the token rows and channel rows
+    constexpr int NQR = (QR + NT - 1) / NT, NQS = (QS + NT - 1) / NT;  // per thread (the last partly idle)
     float4 vu[NQR], vx[NQR], vo[NQR], vs[NQS], vd[NQS];
     auto issue = [&](int jh) {
         const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -766,7 +769,7 @@ __global__ __launch_bounds__((8 * keys_cb<DK, DV>())) void bwd_keys_kernel(BwdAr
         for (int qd = 0; qd < NQR; ++qd) {
             const int i4 = tid + NT * qd;
             const int i = i4 / (DH / 4), j = (i4 % (DH / 4)) * 4;
-            const bool live = i < L;
+            const bool live = i4 < QR && i < L;
             const int64_t off = (row0 + int64_t(i) * a.H) * DV + jh + j;
             vu[qd] = live ? load4(a.ws_u, off) : z4;
             vx[qd] = live ? load4(a.ws_dx, off) : z4;
@@ -777,8 +780,8 @@ __global__ __launch_bounds__((8 * keys_cb<DK, DV>())) void bwd_keys_kernel(BwdAr
             const int i4 = tid + NT * qd;
             const int c = i4 / (DH / 4), j = (i4 % (DH / 4)) * 4;
             const int64_t soff = sbase + int64_t(c0 + c) * DV + jh + j;
-            vs[qd] = load4(a.ws_states, soff);
-            vd[qd] = load4(a.ws_dstates, soff);
+            vs[qd] = i4 < QS ? load4(a.ws_states, soff) : z4;
+            vd[qd] = i4 < QS ? load4(a.ws_dstates, soff) : z4;
         }
     };
     issue(0);  // in flight with the token inputs below
@@ -791,13 +794,10 @@ __global__ __launch_bounds__((8 * keys_cb<DK, DV>())) void bwd_keys_kernel(BwdAr
             const float kk = load_as_f32(k, off), bv = load_as_f32(b, off);
             qb[i][col] = load_as_f32(q, off);
             kb[i][col] = kk;
-            bb[i][col] = bv;
             eb[i][col] = bv * kk;
-            ab[i][col] = a.alpha[off];
             Gb[i][col] = log2_decay(a.alpha[off]);
         } else {
-            qb[i][col] = kb[i][col] = bb[i][col] = eb[i][col] = Gb[i][col] = 0.f;
-            ab[i][col] = 1.f;
+            qb[i][col] = kb[i][col] = eb[i][col] = Gb[i][col] = 0.f;
         }
     }
 
@@ -821,16 +821,20 @@ __global__ __launch_bounds__((8 * keys_cb<DK, DV>())) void bwd_keys_kernel(BwdAr
         for (int qd = 0; qd < NQR; ++qd) {
             const int i4 = tid + NT * qd;
             const int i = i4 / (DH / 4), j = (i4 % (DH / 4)) * 4;
-            st4(Us[i], j, vu[qd]);
-            st4(dXs[i], j, vx[qd]);
-            st4(dOs[i], j, vo[qd]);
+            if (i4 < QR) {
+                st4(Us[i], j, vu[qd]);
+                st4(dXs[i], j, vx[qd]);
+                st4(dOs[i], j, vo[qd]);
+            }
         }
 #pragma unroll
         for (int qd = 0; qd < NQS; ++qd) {
             const int i4 = tid + NT * qd;
             const int c = i4 / (DH / 4), j = (i4 % (DH / 4)) * 4;
-            st4(Sb[c], j, vs[qd]);
-            st4(dSb[c], j, vd[qd]);
+            if (i4 < QS) {
+                st4(Sb[c], j, vs[qd]);
+                st4(dSb[c], j, vd[qd]);
+            }
         }
         if (jh + DH < DV) issue(jh + DH);
         lds_sync();
@@ -878,9 +882,9 @@ __global__ __launch_bounds__((8 * keys_cb<DK, DV>())) void bwd_keys_kernel(BwdAr
     // above 2^kSplitMin (then 2^-G <= 2^-kSplitMin).  Other channels take the
     // pairwise loops below.  Rows past the chunk are zero in every factor.
     constexpr float kSplitMin = -64.f;
-    float (*K2)[DH + kPad] = rowbuf[0];
-    float (*E2)[DH + kPad] = rowbuf[1];
-    float (*Q2)[DH + kPad] = rowbuf[2];
+    float (*K2)[RC] = reinterpret_cast<float (*)[RC]>(flat);
+    float (*E2)[RC] = reinterpret_cast<float (*)[RC]>(flat + CH * RC);
+    float (*Q2)[RC] = reinterpret_cast<float (*)[RC]>(flat + 2 * CH * RC);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {  // thread (i0 + 8 r, col)
         const int i = i0 + 8 * r;
@@ -904,10 +908,11 @@ __global__ __launch_bounds__((8 * keys_cb<DK, DV>())) void bwd_keys_kernel(BwdAr
         }
     }
 
+    lds_sync();  // the split factors are read: their space takes dg and Kb dKb
     // pairwise and absorbed-factor gradients, in the block layout: token
     // 16 tb + 4 lk + e, channel cw
-    float (*dg)[DH + kPad] = sbuf[0];
-    float (*kbd)[DH + kPad] = sbuf[1];
+    float (*dg)[RC] = reinterpret_cast<float (*)[RC]>(flat);
+    float (*kbd)[RC] = reinterpret_cast<float (*)[RC]>(flat + CH * RC);
     T* dq_out = static_cast<T*>(a.dq);
     T* dk_out = static_cast<T*>(a.dk);
     T* db_out = static_cast<T*>(a.db);
@@ -947,7 +952,7 @@ __global__ __launch_bounds__((8 * keys_cb<DK, DV>())) void bwd_keys_kernel(BwdAr
         const int64_t off = (row0 + int64_t(i) * a.H) * DK + c0 + cw;
         store_from_f32(dq_out, off, dq);
         store_from_f32(db_out, off, de * kb[i][cw]);
-        store_from_f32(dk_out, off, dkk + de * bb[i][cw]);
+        store_from_f32(dk_out, off, dkk + de * load_as_f32(b, off));
     }
     __syncthreads();
     // the chunk-end terms, then the reverse running sum over the chunk's tokens
@@ -958,7 +963,7 @@ __global__ __launch_bounds__((8 * keys_cb<DK, DV>())) void bwd_keys_kernel(BwdAr
         for (int j = 0; j < L; ++j) acc += kbd[j][cc];
         for (int i = L - 1; i >= 0; --i) {
             acc += dg[i][cc];
-            const float al = ab[i][cc];
+            const float al = a.alpha[(row0 + int64_t(i) * a.H) * DK + c0 + cc];
             const float lg = __log2f(al);
             const bool clamped = !(lg >= kLog2AlphaFloor && lg <= 0.f);
             const int64_t off = (row0 + int64_t(i) * a.H) * DK + c0 + cc;
