@@ -200,7 +200,8 @@ def bench_chunk(args):
     eb = 2 if wl.dtype == "bf16" else 4
     nbytes = chunk_bytes(B, T, H, dk, dv, N, eb)
     tokens = B * T
-    log(f"chunk: {ms * 1e3:.1f} us/step (event avg {kern_ms * 1e3:.1f} us), "
+    log(f"chunk: {ms * 1e3:.1f} us/step (event avg {kern_ms * 1e3:.1f} us, median {np.median(per) * 1e3:.1f}, "
+        f"min {min(per) * 1e3:.1f}, max {max(per) * 1e3:.1f} over {len(per)} launches), "
         f"{tokens / (ms / 1e3) / 1e6:.2f} M tokens/s, {nbytes / (kern_ms / 1e3) / 1e9:.0f} GB/s")
     return dict(x=x, wl=wl, tokens=tokens, ms=ms, kern_ms=kern_ms, wall=wall, bytes=nbytes,
                 per=per, dims=(B, T, H, dk, dv, N))
@@ -234,6 +235,44 @@ def bench_decode(args):
     log(f"decode: {step_ms * 1e3:.1f} us/step, state {state_bytes / (step_ms / 1e3) / 1e9:.0f} GB/s")
     return dict(step_ms=step_ms, state_gbps=state_bytes / (step_ms / 1e3) / 1e9,
                 achieved=nbytes / (step_ms / 1e3) / 1e9, bytes=nbytes)
+
+
+def bench_decode_rotated(args, nstates=4):
+    """decode_b256 with ``nstates`` distinct 268 MB states in rotation: step t
+    updates state t mod nstates in place, so a state was last touched
+    nstates - 1 steps (and (nstates - 1) x 537 MB of other traffic) earlier and
+    cannot still sit in the 256 MB Infinity Cache.  64 steps timed as one
+    region, per step."""
+    import torch
+
+    from delta_rule_linear_gdn2_amd import binding
+    from delta_rule_linear_gdn2_amd import workloads as W
+
+    x = W.make("decode_b256")
+    wl = x["workload"]
+    steps_in = x["q"].shape[0]
+    N, H, dk = x["q"].shape[1:]
+    dv = x["v"].shape[-1]
+    slices = [to_dev({n: x[n][t] for n in NAMES}, wl.dtype) for t in range(steps_in)]
+    s0 = torch.from_numpy(x["initial_state"]).cuda()
+    states = [s0.clone() for _ in range(nstates)]
+    outs = [torch.empty((N, H, dv), dtype=slices[0]["q"].dtype, device="cuda") for _ in range(steps_in)]
+
+    def call():
+        for t in range(steps_in):
+            s = slices[t]
+            binding.gdn2_recurrent_step(s["q"], s["k"], s["v"], s["alpha"], s["b"], s["w"], states[t % nstates],
+                                        out=outs[t])
+
+    per, total_ms, _ = time_events(call, max(1, args.warmup), max(1, args.steps // 4))
+    step_ms = total_ms / max(1, args.steps // 4) / steps_in
+    state_bytes = 2 * N * H * dk * dv * 4
+    nbytes = step_bytes(N, H, dk, dv)
+    log(f"decode, {nstates} states in rotation: {step_ms * 1e3:.1f} us/step, "
+        f"state {state_bytes / (step_ms / 1e3) / 1e9:.0f} GB/s")
+    return dict(step_ms=step_ms, state_gbps=state_bytes / (step_ms / 1e3) / 1e9,
+                achieved=nbytes / (step_ms / 1e3) / 1e9, bytes=nbytes,
+                timing=f"{steps_in} consecutive steps over {nstates} states in rotation, per step")
 
 
 def bench_decode_flushed(args, reps=20, warm=3):
@@ -462,6 +501,10 @@ def run_configs(args):
     print(json.dumps({"report": "config", "workload": "decode_b256", "us_per_step": dec["step_ms"] * 1e3,
                       "state_GBps": dec["state_gbps"], "hbm_frac": dec["achieved"] / HBM_PEAK_GBPS,
                       "timing": "64 consecutive in-place steps, per step"}), flush=True)
+    rot = bench_decode_rotated(args)
+    print(json.dumps({"report": "config", "workload": "decode_b256, four states in rotation (cache-clean)",
+                      "us_per_step": rot["step_ms"] * 1e3, "state_GBps": rot["state_gbps"],
+                      "hbm_frac": rot["achieved"] / HBM_PEAK_GBPS, "timing": rot["timing"]}), flush=True)
     fl = bench_decode_flushed(args)
     print(json.dumps({"report": "config", "workload": "decode_b256, Infinity Cache flushed before each step",
                       "us_per_step": fl["step_ms"] * 1e3, "state_GBps": fl["state_gbps"],
@@ -573,6 +616,7 @@ def main():
         return run_configs(args)
     ch = bench_chunk(args)
     dec = None if args.no_decode else bench_decode(args)
+    rot = None if args.no_decode else bench_decode_rotated(args)
     cpu = None
     if not args.no_cpu and ch["wl"].kind == "chunk":
         cpu = cpu_baseline(ch["x"], ch["wl"], chains_rows=ch["wl"].B)
@@ -608,6 +652,8 @@ def main():
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE)",
                      "kernel": "gdn2 chunk forward", "algorithmic_bytes": ch["bytes"],
                      "avg_launch_ms": ch["kern_ms"],
+                     "launch_ms": {"median": float(np.median(ch["per"])), "min": float(min(ch["per"])),
+                                   "max": float(max(ch["per"])), "launches": len(ch["per"])},
                      "mfma": {"achieved": mfma_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
                               "unit": "TFLOP/s", "frac": mfma_tflops / MFMA_BF16_PEAK_TFLOPS,
                               "flops": flops, "counting": "triangle-aware algorithmic FLOPs"}},
@@ -622,6 +668,10 @@ def main():
                          "traffic": pmc_traffic("decode"),
                          "traffic_unit": "HBM bytes per step (rocprofv3 FETCH_SIZE+WRITE_SIZE)",
                          "algorithmic_bytes": dec["bytes"]},
+            "rotated": {"workload": "the same steps over four distinct states in rotation: each state last "
+                                    "touched four steps earlier, so none is still in the 256 MB Infinity Cache",
+                        "state_GBps": rot["state_gbps"], "us_per_step": rot["step_ms"] * 1e3,
+                        "hbm_frac": rot["achieved"] / HBM_PEAK_GBPS},
         }
     print(json.dumps(out), flush=True)
 

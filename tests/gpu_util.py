@@ -83,6 +83,34 @@ def gpu_chain_view(o_gpu: np.ndarray, s_gpu: np.ndarray, x: dict, n: int, h: int
     return o_gpu[n, :, h], s_gpu[n, h]
 
 
+def chain_sq_sums(x: np.ndarray, cu=None):
+    """Sum of squares per (sequence, head) chain of an output [B, T, H, d]
+    (batched) or [1, T_total, H, d] (packed by ``cu``): returns [N, H]."""
+    per_tok = np.einsum("bthd,bthd->bth", x, x)
+    if cu is None:
+        return per_tok.sum(axis=1)
+    c = np.concatenate([np.zeros((1, per_tok.shape[2])), np.cumsum(per_tok[0], axis=0)])
+    cu = np.asarray(cu, dtype=np.int64)
+    return c[cu[1:]] - c[cu[:-1]]
+
+
+def assert_chains(o, s, ro, rs, tol, what, cu=None):
+    """Whole-tensor relative L2 of the outputs and of the final states against
+    the oracle, plus the worst (sequence, head) chain of each as a log line."""
+    eo = assert_rel(o, ro, tol, f"{what} o")
+    es = assert_rel(s, rs, tol, f"{what} final state")
+    num_o = chain_sq_sums(o - ro, cu)
+    den_o = chain_sq_sums(ro, cu)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        per_o = np.sqrt(np.where(den_o > 0, num_o / den_o, num_o))
+        per_s = np.sqrt(((s - rs) ** 2).sum(axis=(2, 3)) / np.maximum((rs ** 2).sum(axis=(2, 3)), 1e-300))
+    wo = np.unravel_index(int(np.argmax(per_o)), per_o.shape)
+    ws = np.unravel_index(int(np.argmax(per_s)), per_s.shape)
+    log(f"{what}: {per_o.size} chains; worst o chain (n={wo[0]}, h={wo[1]}) rel L2 {per_o[wo]:.3e}; "
+        f"worst state chain (n={ws[0]}, h={ws[1]}) rel L2 {per_s[ws]:.3e}")
+    return eo, es
+
+
 def assert_rel(x, ref, tol, what):
     err = oracle.rel_l2(x, ref)
     log(f"{what}: rel L2 = {err:.3e} (tol {tol:.0e})")

@@ -51,26 +51,20 @@ def test_tiny_f32_stepped():
     G.assert_rel(G.f64(state), rs, G.TOL["f32"], "tiny stepped state")
 
 
-def test_decode_b256_sampled():
-    """256 sequences x 16 heads, d=128, bf16, 64 consecutive in-place steps."""
+def test_decode_b256():
+    """256 sequences x 16 heads, d=128, bf16, 64 consecutive in-place steps:
+    all 4,096 chains, every step's output and the state after the last."""
     import torch
 
     x = W.make("decode_b256")
     state = torch.from_numpy(x["initial_state"]).cuda()
-    o = G.f64(_step_all(x, "bf16", state))
+    o = G.f64(_step_all(x, "bf16", state)).swapaxes(0, 1)  # [N, steps, H, dv]
     sg = G.f64(state)
     assert np.isfinite(o).all() and np.isfinite(sg).all()
     seqs = _as_sequences(x)
-    H = x["q"].shape[2]
-    chains = [0, 17, 255 * H + 15, 100 * H + 7, 200 * H + 3, 31 * H + 11]
     ro, rs = oracle.recurrent(seqs["q"], seqs["k"], seqs["v"], seqs["alpha"], seqs["b"], seqs["w"],
-                              x["initial_state"], chains=chains)
-    go = [o[:, c // H, c % H].ravel() for c in chains]
-    rr = [ro[c // H, :, c % H].ravel() for c in chains]
-    G.assert_rel(np.concatenate(go), np.concatenate(rr), G.TOL["bf16"], "decode o (sampled)")
-    G.assert_rel(np.concatenate([sg[c // H, c % H].ravel() for c in chains]),
-                 np.concatenate([rs[c // H, c % H].ravel() for c in chains]), G.TOL["bf16"],
-                 "decode state (sampled)")
+                              x["initial_state"])
+    G.assert_chains(o, sg, ro, rs, G.TOL["bf16"], "decode_b256")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

@@ -97,9 +97,12 @@ def test_chunk_gates_varlen_edges(mode, dtype, d):
 
 
 @pytest.mark.parametrize("mode", ["kda", "gdn"])
-def test_chunk_gates_varlen32_sampled(mode):
-    """32 packed sequences, lengths U{256..8192}, H=16, d=128, bf16: bitwise equal to
-    the full layout everywhere, and the oracle on sampled chains."""
+def test_chunk_gates_varlen32(mode):
+    """32 packed sequences, lengths U{256..8192}, H=16, d=128, bf16, compact
+    layout: bitwise equal to the full layout everywhere; the oracle's
+    recurrence on the broadcast gates over all 512 chains; and its separately
+    written reduced form (a dk x dk matrix per token, too slow for every
+    chain) on one head of every fourth sequence and of the longest."""
     import torch
 
     x = W.make("varlen32_bf16", gate_mode=mode)
@@ -107,19 +110,24 @@ def test_chunk_gates_varlen32_sampled(mode):
     fo, fs = G.gpu_chunk(d)
     assert torch.equal(o, fo) and torch.equal(sf, fs), f"varlen32 {mode}: compact and full layouts differ"
     og, sg = G.f64(o), G.f64(sf)
+    G.log(f"varlen32 {mode}: oracle recurrence on all chains")
+    ro, rs = G.oracle_full(x)
+    G.assert_chains(og, sg, ro, rs, G.TOL["bf16"], f"varlen32 {mode} compact", x["cu_seqlens"])
     beta, alpha = compact(x, mode)
+    H = x["q"].shape[2]
+    N = len(x["cu_seqlens"]) - 1
     lens = np.diff(x["cu_seqlens"])
-    chains = [(int(np.argmax(lens)), 2), (int(np.argmin(lens)), 11), (13, 6)]
-    os_, ors, ss_, srs = [], [], [], []
-    for n, h in chains:
-        lo, hi = int(x["cu_seqlens"][n]), int(x["cu_seqlens"][n + 1])
-        sl = lambda a: a[0:1, lo:hi, h:h + 1]  # noqa: E731
-        ro, rs = oracle_compact(mode, sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(alpha), sl(beta),
-                                x["initial_state"][n:n + 1, h:h + 1], None)
-        go, gs = G.gpu_chain_view(og, sg, x, n, h)
-        os_.append(go.ravel()); ors.append(ro[0, :, 0].ravel()); ss_.append(gs.ravel()); srs.append(rs[0, 0].ravel())
-    G.assert_rel(np.concatenate(os_), np.concatenate(ors), G.TOL["bf16"], f"varlen32 {mode} o (sampled)")
-    G.assert_rel(np.concatenate(ss_), np.concatenate(srs), G.TOL["bf16"], f"varlen32 {mode} state (sampled)")
+    seqs = sorted(set(range(0, N, 4)) | {int(np.argmax(lens))})
+    chains = [n * H + (n % H) for n in seqs]
+    G.log(f"varlen32 {mode}: oracle {mode} form on {len(chains)} chains")
+    fn = oracle.kda if mode == "kda" else oracle.gdn
+    ro, rs = fn(x["q"], x["k"], x["v"], alpha, beta, x["initial_state"], x["cu_seqlens"], chains=chains)
+    cu = x["cu_seqlens"]
+    go = np.concatenate([og[0, cu[n]:cu[n + 1], n % H].ravel() for n in seqs])
+    eo = np.concatenate([ro[0, cu[n]:cu[n + 1], n % H].ravel() for n in seqs])
+    G.assert_rel(go, eo, G.TOL["bf16"], f"varlen32 {mode} o vs the {mode} form ({len(seqs)} chains)")
+    G.assert_rel(np.stack([sg[n, n % H] for n in seqs]), np.stack([rs[n, n % H] for n in seqs]),
+                 G.TOL["bf16"], f"varlen32 {mode} state vs the {mode} form ({len(seqs)} chains)")
 
 
 @pytest.mark.parametrize("mode", ["kda", "gdn"])
