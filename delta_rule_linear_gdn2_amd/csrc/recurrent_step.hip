@@ -11,12 +11,27 @@
 //     S <- Diag(alpha) S + k u^T
 // (o = S_new^T q expands to S^T (alpha (.) q) + u (k^T q)).
 //
-// Work split: one 256-thread workgroup per (sequence, head).  Thread t owns
-// four adjacent value columns (one float4) in rows t / (DV/4) + RPP * i, so a
-// wavefront reads whole contiguous rows (coalesced dwordx4).  The tile stays
-// in VGPRs between the two column reductions and the write-back: no re-read.
-// The token vectors go through LDS in two buffers (token parity), and the
-// next token's are loaded into registers while the current one is computed.
+// Work split: column j of the state evolves with column j of z, r and s
+// alone, so a (sequence, head) splits into independent 32-column quarters.
+// One wavefront (a one-wave workgroup) owns one quarter: lane l holds the
+// four columns 4 (l & 7) .. + 3 of the rows g NP .. g NP + NP - 1, g = l >> 3,
+// NP = dk / 8, in VGPRs.  The column sums over dk are a register sum over the
+// lane's NP rows and three shuffle steps across the eight row groups: no
+// workgroup barrier and no cross-wave exchange, so a wavefront never waits
+// for another.  The token vectors go through the wave's own LDS (two buffers,
+// token parity); the next token's are loaded into registers while the current
+// one is computed.  The quarters of one head share blockIdx mod 8, hence one
+// XCD, so the token vectors that every quarter reads come from that XCD's L2.
+//
+// The state is streamed: the loads carry the non-temporal hint and the stores
+// the non-temporal and system-scope hints.  On MI355X with 256 sequences x 16
+// heads of 128 x 128 FP32 state (268 MB, beyond the 256 MB Infinity Cache),
+// that policy measured 95-96 us per step both in place and with the state
+// last touched several steps earlier; the default policy took 82 us in place
+// (partly served from the cache) but 108 us on a cold state.  A decode loop
+// over a model's layers touches every layer's state between two steps of one
+// layer, so the cold figure is the one that matters.
+//
 // There is no matrix work here (0.75 flop per state byte per token), so no
 // MFMA.
 #include "gdn2_device.hpp"
@@ -25,143 +40,183 @@
 namespace gdn2 {
 namespace {
 
-constexpr int kStepThreads = 256;
+constexpr int kCols = 32;          // value columns per wavefront
+constexpr int kAuxLoad = 2;        // buffer cache policy of the state loads: nt
+constexpr int kAuxStore = 2 | 16;  // of the state stores: nt, sc1
 
-// One token's inputs as loaded by this thread: key channel c = tid (q, k, b,
-// alpha; tid < DK) and value column j = tid (v, w; tid < DV).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), 0x00020000);
+}
+__device__ __forceinline__ float4 ld_state(rsrc_t r, uint32_t off)
+{
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, kAuxLoad);
+    return make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]), __uint_as_float(x[3]));
+}
+__device__ __forceinline__ void st_state(rsrc_t r, uint32_t off, float4 v)
+{
+    const u32x4 x = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
+    __builtin_amdgcn_raw_buffer_store_b128(x, r, int(off), 0, kAuxStore);
+}
+
+__device__ __forceinline__ void store_o4(float* o, float4 x) { *reinterpret_cast<float4*>(o) = x; }
+__device__ __forceinline__ void store_o4(bf16raw* o, float4 x)
+{
+    *reinterpret_cast<uint2*>(o) = make_uint2(f32x2_to_bf16x2(x.x, x.y), f32x2_to_bf16x2(x.z, x.w));
+}
+
+// One token's inputs as loaded by a lane: key channels lane + 64 i (q, k, b,
+// alpha) and value column lane of the quarter (v, w; lanes < 32).  A scalar
+// gate (one value per token and head) is read with stride 0 over its
+// channels; a tied write gate is the scalar erase gate.
+template <int DK>
 struct TokenRegs {
-    float q, k, b, a, v, w;
+    static constexpr int KI = (DK + 63) / 64;
+    float q[KI], k[KI], b[KI], a[KI];
+    float v, w;
 };
 
 template <typename T, int DK, int DV>
-__device__ __forceinline__ void load_token(TokenRegs& x, const StepArgs& a, int64_t row, int tid)
+__device__ __forceinline__ void load_token(TokenRegs<DK>& x, const StepArgs& a, int64_t row, int col0, int lane)
 {
-    // A scalar gate (one value per token and head) is read with stride 0 over
-    // its channels; a tied write gate is the scalar erase gate.
     const bool sb = a.gates & kScalarErase, sa = a.gates & kScalarDecay;
-    if (tid < DK) {
-        x.q = load_as_f32(static_cast<const T*>(a.q), row * DK + tid);
-        x.k = load_as_f32(static_cast<const T*>(a.k), row * DK + tid);
-        x.b = load_as_f32(static_cast<const T*>(a.b), sb ? row : row * DK + tid);
-        x.a = __builtin_amdgcn_fmed3f(a.alpha[sa ? row : row * DK + tid], 0x1p-15f, 1.0f);  // as the chunk kernels
+#pragma unroll
+    for (int i = 0; i < TokenRegs<DK>::KI; ++i) {
+        const int c = lane + 64 * i;
+        if (c < DK) {
+            x.q[i] = load_as_f32(static_cast<const T*>(a.q), row * DK + c);
+            x.k[i] = load_as_f32(static_cast<const T*>(a.k), row * DK + c);
+            x.b[i] = load_as_f32(static_cast<const T*>(a.b), sb ? row : row * DK + c);
+            x.a[i] = a.alpha[sa ? row : row * DK + c];
+        }
     }
-    if (tid < DV) {
-        x.v = load_as_f32(static_cast<const T*>(a.v), row * DV + tid);
+    if (lane < kCols) {
+        const int64_t j = row * DV + col0 + lane;
+        x.v = load_as_f32(static_cast<const T*>(a.v), j);
         x.w = a.gates & kTied         ? load_as_f32(static_cast<const T*>(a.b), row)
               : a.gates & kScalarWrite ? load_as_f32(static_cast<const T*>(a.w), row)
-                                       : load_as_f32(static_cast<const T*>(a.w), row * DV + tid);
+                                       : load_as_f32(static_cast<const T*>(a.w), j);
     }
 }
 
-template <typename T, int DK, int DV>
-__global__ __launch_bounds__(kStepThreads) void recurrent_kernel(StepArgs a)
+// The wave's own LDS writes are complete (it is the only wave of its
+// workgroup, so no s_barrier); global loads stay in flight.
+__device__ __forceinline__ void wave_lds_fence()
 {
-    constexpr int TPR = DV / 4;               // threads per state row
-    constexpr int RPP = kStepThreads / TPR;   // rows per pass
-    constexpr int NP = DK / RPP;              // float4s per thread
-    static_assert(DK % RPP == 0 && NP >= 1, "tile does not divide the state");
-    static_assert(TPR <= 64 && 64 % TPR == 0, "row must fit in a wavefront");
-    static_assert(DK <= kStepThreads && DV <= kStepThreads, "one thread per channel");
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63, expcnt 7, lgkmcnt 0
+    __asm__ volatile("" ::: "memory");
+}
 
-    __shared__ float s_alpha[2][DK], s_ae[2][DK], s_aq[2][DK], s_k[2][DK], s_q[2][DK];
-    __shared__ float s_z[2][DV];
-    __shared__ float4 s_red[2][kStepThreads / 64][TPR];
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(64) void recurrent_kernel(StepArgs a)
+{
+    constexpr int NQ = DV / kCols;   // quarters per head
+    constexpr int NP = DK / 8;       // rows per lane
+    static_assert(DV % kCols == 0 && NP % 4 == 0, "tile does not divide the state");
 
-    const int head = blockIdx.x;  // n * H + h
-    const int tid = threadIdx.x;
-    const int col4 = tid % TPR;
-    const int row0 = tid / TPR;
-    const int wave = tid / 64, lane = tid % 64;
+    __shared__ __attribute__((aligned(16))) float s_al[2][DK], s_ae[2][DK], s_aq[2][DK], s_k[2][DK];
+    __shared__ __attribute__((aligned(16))) float s_z[2][kCols];
+
+    // blockIdx -> (head, quarter): the NQ quarters of a head are 8 blocks apart
+    const int blk = blockIdx.x;
+    const int quarter = (blk % (8 * NQ)) / 8;
+    const int64_t head = int64_t(blk / (8 * NQ)) * 8 + (blk & 7);  // n * H + h
+    if (head >= int64_t(a.N) * a.H) return;
+    const int lane = threadIdx.x;
+    const int col4 = lane & 7, g = lane >> 3;
     const int64_t n = head / a.H, h = head % a.H;
-    float* S = a.state + int64_t(head) * DK * DV;
+    const int col0 = quarter * kCols;
+    const int c0 = col0 + 4 * col4;  // this lane's first column
 
+    // token 0's inputs first: they land before the state and are staged while
+    // the state is still in flight
+    TokenRegs<DK> x;
+    if (a.T > 0) load_token<T, DK, DV>(x, a, n * a.T * a.H + h, col0, lane);
+
+    const rsrc_t rs = make_rsrc(a.state + head * DK * DV, DK * DV * 4);
     float4 st[NP];
 #pragma unroll
-    for (int i = 0; i < NP; ++i)
-        st[i] = reinterpret_cast<const float4*>(S + int64_t(row0 + RPP * i) * DV)[col4];
+    for (int i = 0; i < NP; ++i) st[i] = ld_state(rs, uint32_t((g * NP + i) * DV + c0) * 4);
 
-    TokenRegs x;
-    if (a.T > 0) load_token<T, DK, DV>(x, a, n * a.T * a.H + h, tid);
     for (int t = 0; t < a.T; ++t) {
         const int buf = t & 1;
         const int64_t row = (n * a.T + t) * a.H + h;  // token t of this (sequence, head)
-        if (tid < DK) {
-            s_alpha[buf][tid] = x.a;
-            s_ae[buf][tid] = x.a * (x.b * x.k);
-            s_aq[buf][tid] = x.a * x.q;
-            s_k[buf][tid] = x.k;
-            s_q[buf][tid] = x.q;
-        }
-        if (tid < DV) s_z[buf][tid] = x.w * x.v;
-        if (t + 1 < a.T) load_token<T, DK, DV>(x, a, row + a.H, tid);  // in flight during this token
-        __syncthreads();
-
-        // k . q, computed redundantly by every wavefront
         float kq = 0.f;
-        for (int c = lane; c < DK; c += 64) kq += s_k[buf][c] * s_q[buf][c];
+#pragma unroll
+        for (int i = 0; i < TokenRegs<DK>::KI; ++i) {
+            const int c = lane + 64 * i;
+            if (c < DK) {
+                const float al = __builtin_amdgcn_fmed3f(x.a[i], 0x1p-15f, 1.0f);
+                s_al[buf][c] = al;
+                s_ae[buf][c] = al * (x.b[i] * x.k[i]);
+                s_aq[buf][c] = al * x.q[i];
+                s_k[buf][c] = x.k[i];
+                kq += x.k[i] * x.q[i];
+            }
+        }
+        if (lane < kCols) s_z[buf][lane] = x.w * x.v;
+        if (t + 1 < a.T) load_token<T, DK, DV>(x, a, row + a.H, col0, lane);  // in flight during this token
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) kq += __shfl_xor(kq, off, 64);
+        wave_lds_fence();
 
         float4 r = make_float4(0.f, 0.f, 0.f, 0.f), s = r;
 #pragma unroll
-        for (int i = 0; i < NP; ++i) {
-            const int c = row0 + RPP * i;
-            const float ae = s_ae[buf][c], aq = s_aq[buf][c];
-            r.x += st[i].x * ae; r.y += st[i].y * ae; r.z += st[i].z * ae; r.w += st[i].w * ae;
-            s.x += st[i].x * aq; s.y += st[i].y * aq; s.z += st[i].z * aq; s.w += st[i].w * aq;
-        }
-        // reduce over the row groups inside the wavefront ...
+        for (int i4 = 0; i4 < NP / 4; ++i4) {
+            const float4 ae = *reinterpret_cast<const float4*>(&s_ae[buf][g * NP + 4 * i4]);
+            const float4 aq = *reinterpret_cast<const float4*>(&s_aq[buf][g * NP + 4 * i4]);
+            const float aev[4] = {ae.x, ae.y, ae.z, ae.w}, aqv[4] = {aq.x, aq.y, aq.z, aq.w};
 #pragma unroll
-        for (int off = TPR; off < 64; off <<= 1) {
+            for (int j = 0; j < 4; ++j) {
+                const float4 y = st[4 * i4 + j];
+                r.x += y.x * aev[j]; r.y += y.y * aev[j]; r.z += y.z * aev[j]; r.w += y.w * aev[j];
+                s.x += y.x * aqv[j]; s.y += y.y * aqv[j]; s.z += y.z * aqv[j]; s.w += y.w * aqv[j];
+            }
+        }
+        // sum over the eight row groups (lanes 8 apart)
+#pragma unroll
+        for (int off = 8; off < 64; off <<= 1) {
             r.x += __shfl_xor(r.x, off, 64); r.y += __shfl_xor(r.y, off, 64);
             r.z += __shfl_xor(r.z, off, 64); r.w += __shfl_xor(r.w, off, 64);
             s.x += __shfl_xor(s.x, off, 64); s.y += __shfl_xor(s.y, off, 64);
             s.z += __shfl_xor(s.z, off, 64); s.w += __shfl_xor(s.w, off, 64);
         }
-        // ... and across wavefronts through LDS
-        if (lane < TPR) {
-            s_red[0][wave][lane] = r;
-            s_red[1][wave][lane] = s;
-        }
-        __syncthreads();
-        r = s_red[0][0][col4];
-        s = s_red[1][0][col4];
+        const float4 z = *reinterpret_cast<const float4*>(&s_z[buf][4 * col4]);
+        const float4 u = make_float4(z.x - r.x, z.y - r.y, z.z - r.z, z.w - r.w);
+        if (g == 0)
+            store_o4(static_cast<T*>(a.o) + row * DV + c0,
+                     make_float4(s.x + kq * u.x, s.y + kq * u.y, s.z + kq * u.z, s.w + kq * u.w));
 #pragma unroll
-        for (int wv = 1; wv < kStepThreads / 64; ++wv) {
-            const float4 r2 = s_red[0][wv][col4], s2 = s_red[1][wv][col4];
-            r.x += r2.x; r.y += r2.y; r.z += r2.z; r.w += r2.w;
-            s.x += s2.x; s.y += s2.y; s.z += s2.z; s.w += s2.w;
-        }
-        const float* z = s_z[buf] + 4 * col4;
-        const float4 u = make_float4(z[0] - r.x, z[1] - r.y, z[2] - r.z, z[3] - r.w);
-        if (row0 == 0) {
-            T* o = static_cast<T*>(a.o) + row * DV + 4 * col4;
-            store_from_f32(o, 0, s.x + kq * u.x);
-            store_from_f32(o, 1, s.y + kq * u.y);
-            store_from_f32(o, 2, s.z + kq * u.z);
-            store_from_f32(o, 3, s.w + kq * u.w);
-        }
+        for (int i4 = 0; i4 < NP / 4; ++i4) {
+            const float4 al = *reinterpret_cast<const float4*>(&s_al[buf][g * NP + 4 * i4]);
+            const float4 kk = *reinterpret_cast<const float4*>(&s_k[buf][g * NP + 4 * i4]);
+            const float alv[4] = {al.x, al.y, al.z, al.w}, kv[4] = {kk.x, kk.y, kk.z, kk.w};
 #pragma unroll
-        for (int i = 0; i < NP; ++i) {
-            const int c = row0 + RPP * i;
-            const float aa = s_alpha[buf][c], kk = s_k[buf][c];
-            st[i].x = aa * st[i].x + kk * u.x;
-            st[i].y = aa * st[i].y + kk * u.y;
-            st[i].z = aa * st[i].z + kk * u.z;
-            st[i].w = aa * st[i].w + kk * u.w;
+            for (int j = 0; j < 4; ++j) {
+                float4& y = st[4 * i4 + j];
+                y.x = alv[j] * y.x + kv[j] * u.x;
+                y.y = alv[j] * y.y + kv[j] * u.y;
+                y.z = alv[j] * y.z + kv[j] * u.z;
+                y.w = alv[j] * y.w + kv[j] * u.w;
+            }
         }
     }
 #pragma unroll
-    for (int i = 0; i < NP; ++i) reinterpret_cast<float4*>(S + int64_t(row0 + RPP * i) * DV)[col4] = st[i];
+    for (int i = 0; i < NP; ++i) st_state(rs, uint32_t((g * NP + i) * DV + c0) * 4, st[i]);
 }
 
 template <typename T, int DK, int DV>
 hipError_t launch_dkdv(const StepArgs& a, hipStream_t stream)
 {
-    const int64_t blocks = int64_t(a.N) * a.H;
+    constexpr int NQ = DV / kCols;
+    const int64_t heads = int64_t(a.N) * a.H;
+    const int64_t blocks = (heads + 7) / 8 * 8 * NQ;  // padded to whole groups of eight heads
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((recurrent_kernel<T, DK, DV>), dim3(unsigned(blocks)), dim3(kStepThreads),
-                       0, stream, a);
+    hipLaunchKernelGGL((recurrent_kernel<T, DK, DV>), dim3(unsigned(blocks)), dim3(64), 0, stream, a);
     return hipGetLastError();
 }
 
