@@ -171,7 +171,10 @@ def time_events(fn, warmup, steps):
     return per, t_all0.elapsed_time(t_all1), wall
 
 
-def bench_chunk(args):
+def bench_chunk(args, pre=None):
+    """Time the chunkwise forward.  ``pre`` (optional) runs after the inputs
+    are on the device and before the warmup launches; its result is returned
+    under "pre"."""
     import torch
 
     from delta_rule_linear_gdn2_amd import binding
@@ -194,9 +197,11 @@ def bench_chunk(args):
         binding.gdn2_chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["b"], d["w"], s0,
                                final_state=sf, out=o, cu_seqlens=cu)
 
+    pre_res = pre() if pre is not None else None
     per, total_ms, wall = time_events(call, args.warmup, args.steps)
     ms = total_ms / args.steps
     kern_ms = float(np.mean(per))
+    log("chunk per-launch us: " + " ".join(f"{p * 1e3:.0f}" for p in per))
     eb = 2 if wl.dtype == "bf16" else 4
     nbytes = chunk_bytes(B, T, H, dk, dv, N, eb)
     tokens = B * T
@@ -204,16 +209,16 @@ def bench_chunk(args):
         f"min {min(per) * 1e3:.1f}, max {max(per) * 1e3:.1f} over {len(per)} launches), "
         f"{tokens / (ms / 1e3) / 1e6:.2f} M tokens/s, {nbytes / (kern_ms / 1e3) / 1e9:.0f} GB/s")
     return dict(x=x, wl=wl, tokens=tokens, ms=ms, kern_ms=kern_ms, wall=wall, bytes=nbytes,
-                per=per, dims=(B, T, H, dk, dv, N))
+                per=per, dims=(B, T, H, dk, dv, N), pre=pre_res)
 
 
-def bench_decode(args):
+def bench_decode(args, x=None):
     import torch
 
     from delta_rule_linear_gdn2_amd import binding
     from delta_rule_linear_gdn2_amd import workloads as W
 
-    x = W.make("decode_b256")
+    x = W.make("decode_b256") if x is None else x
     wl = x["workload"]
     steps_in = x["q"].shape[0]
     N, H, dk = x["q"].shape[1:]
@@ -237,7 +242,7 @@ def bench_decode(args):
                 achieved=nbytes / (step_ms / 1e3) / 1e9, bytes=nbytes)
 
 
-def bench_decode_rotated(args, nstates=4):
+def bench_decode_rotated(args, nstates=4, x=None):
     """decode_b256 with ``nstates`` distinct 268 MB states in rotation: step t
     updates state t mod nstates in place, so a state was last touched
     nstates - 1 steps (and (nstates - 1) x 537 MB of other traffic) earlier and
@@ -248,7 +253,7 @@ def bench_decode_rotated(args, nstates=4):
     from delta_rule_linear_gdn2_amd import binding
     from delta_rule_linear_gdn2_amd import workloads as W
 
-    x = W.make("decode_b256")
+    x = W.make("decode_b256") if x is None else x
     wl = x["workload"]
     steps_in = x["q"].shape[0]
     N, H, dk = x["q"].shape[1:]
@@ -614,9 +619,21 @@ def main():
         return run_only(args)
     if args.configs:
         return run_configs(args)
-    ch = bench_chunk(args)
-    dec = None if args.no_decode else bench_decode(args)
-    rot = None if args.no_decode else bench_decode_rotated(args)
+    # The decode half runs first, right before the chunkwise warmup: the GPU's
+    # clocks take tens of milliseconds of sustained load to settle (launches of
+    # the chunkwise kernel on an idle GPU run up to a third slower at first),
+    # so the chunkwise timing then starts on settled clocks.
+    from delta_rule_linear_gdn2_amd import workloads as W
+
+    xd = None if args.no_decode else W.make("decode_b256")
+
+    def decode_first():
+        if xd is None:
+            return None, None
+        return bench_decode(args, xd), bench_decode_rotated(args, x=xd)
+
+    ch = bench_chunk(args, pre=decode_first)
+    dec, rot = ch["pre"]
     cpu = None
     if not args.no_cpu and ch["wl"].kind == "chunk":
         cpu = cpu_baseline(ch["x"], ch["wl"], chains_rows=ch["wl"].B)
