@@ -22,7 +22,8 @@ STATUS_NAMES = {
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 
-EXPORTS = ("gdn2_chunk_bwd", "gdn2_chunk_bwd_workspace_bytes", "gdn2_chunk_fwd", "gdn2_chunk_fwd_gates",
+EXPORTS = ("gdn2_chunk_bwd", "gdn2_chunk_bwd_noalloc", "gdn2_chunk_bwd_noalloc_max_workspace_bytes",
+           "gdn2_chunk_bwd_workspace_bytes", "gdn2_chunk_fwd", "gdn2_chunk_fwd_gates",
            "gdn2_chunk_fwd_workspace_bytes",
            "gdn2_mixer_epilogue", "gdn2_mixer_prologue", "gdn2_recurrent_fwd", "gdn2_recurrent_step",
            "gdn2_recurrent_step_gates", "gdn2_status_string", "gdn2_version")
@@ -82,6 +83,10 @@ def load(path: str = LIB_PATH):
     lib.gdn2_recurrent_fwd.restype = ctypes.c_int
     lib.gdn2_chunk_bwd.argtypes = [P] * 17 + [I, I, I, I, I, I, I, P, Z, P]
     lib.gdn2_chunk_bwd.restype = ctypes.c_int
+    lib.gdn2_chunk_bwd_noalloc.argtypes = [P] * 17 + [I, I, I, I, I, I, I, P]
+    lib.gdn2_chunk_bwd_noalloc.restype = ctypes.c_int
+    lib.gdn2_chunk_bwd_noalloc_max_workspace_bytes.argtypes = []
+    lib.gdn2_chunk_bwd_noalloc_max_workspace_bytes.restype = Z
     lib.gdn2_chunk_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     lib.gdn2_chunk_bwd_workspace_bytes.restype = Z
     F = ctypes.c_float
@@ -355,6 +360,48 @@ def gdn2_chunk_bwd(q, k, v, alpha, b, w, d_o, initial_state=None, d_final_state=
                             0 if workspace is None else workspace.numel(), _stream(stream))
     if rc != GDN2_OK:
         raise Gdn2Error(rc, "gdn2_chunk_bwd")
+    return out
+
+
+def gdn2_chunk_bwd_noalloc_max_workspace_bytes() -> int:
+    return int(load().gdn2_chunk_bwd_noalloc_max_workspace_bytes())
+
+
+def gdn2_chunk_bwd_noalloc(q, k, v, alpha, b, w, d_o, initial_state=None, d_final_state=None, *, out,
+                           cu_seqlens=None, stream=None):
+    """gdn2_chunk_bwd on the library's own workspace (the call allocates nothing).
+
+    ``out``: dict of preallocated outputs dq, dk, db [B, T, H, dk] and dv, dw
+    [B, T, H, dv] (input dtype), dalpha [B, T, H, dk] float32 and
+    d_initial_state [N, H, dk, dv] float32 or None; filled in place and
+    returned."""
+    import torch
+
+    lib = load()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(dt)
+    N = B if cu_seqlens is None else int(cu_seqlens.shape[0]) - 1
+    for name, t, width in (("q", q, dk), ("k", k, dk), ("b", b, dk), ("v", v, dv), ("w", w, dv),
+                           ("d_o", d_o, dv), ("dq", out["dq"], dk), ("dk", out["dk"], dk), ("db", out["db"], dk),
+                           ("dv", out["dv"], dv), ("dw", out["dw"], dv)):
+        _check(name, t, (B, T, H, width), dt, dev)
+    _check("alpha", alpha, (B, T, H, dk), torch.float32, dev)
+    _check("dalpha", out["dalpha"], (B, T, H, dk), torch.float32, dev)
+    for name, t in (("initial_state", initial_state), ("d_final_state", d_final_state),
+                    ("d_initial_state", out.get("d_initial_state"))):
+        if t is not None:
+            _check(name, t, (N, H, dk, dv), torch.float32, dev)
+    if cu_seqlens is not None:
+        _check("cu_seqlens", cu_seqlens, (N + 1,), torch.int32, dev)
+    rc = lib.gdn2_chunk_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(initial_state),
+                                    _ptr(d_o), _ptr(d_final_state), _ptr(out["dq"]), _ptr(out["dk"]),
+                                    _ptr(out["dv"]), _ptr(out["dalpha"]), _ptr(out["db"]), _ptr(out["dw"]),
+                                    _ptr(out.get("d_initial_state")), _ptr(cu_seqlens), B, T, H, dk, dv, N, code,
+                                    _stream(stream))
+    if rc != GDN2_OK:
+        raise Gdn2Error(rc, "gdn2_chunk_bwd_noalloc")
     return out
 
 

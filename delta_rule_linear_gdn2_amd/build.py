@@ -25,6 +25,7 @@ SOURCES = [
     "chunk_fwd_mfma.hip",
     "chunk_bwd.hip",
     "mixer.hip",
+    "scratch.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -274,12 +274,21 @@ BwdWorkspace bwd_workspace(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t 
     return w;
 }
 
-gdn2_status chunk_bwd(const void* q, const void* k, const void* v, const float* alpha, const void* b, const void* w,
-                      const float* initial_state, const void* d_o, const float* d_final_state, void* dq, void* dk_,
-                      void* dv_, float* dalpha, void* db, void* dw, float* d_initial_state,
-                      const int32_t* cu_seqlens, int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
-                      int32_t num_seqs, gdn2_dtype dtype, void* workspace, size_t workspace_bytes, void* stream)
+// Host-side checks of a backward call (no HIP call): sizes, pointers,
+// alignment, workspace size and overlaps.  ws receives the workspace layout.
+// With own_workspace the library supplies the workspace itself: the caller's
+// workspace arguments are ignored and no workspace check is made here.
+gdn2_status chunk_bwd_check(const void* q, const void* k, const void* v, const float* alpha, const void* b,
+                            const void* w, const float* initial_state, const void* d_o, const float* d_final_state,
+                            void* dq, void* dk_, void* dv_, float* dalpha, void* db, void* dw,
+                            float* d_initial_state, const int32_t* cu_seqlens, int32_t B, int32_t T, int32_t H,
+                            int32_t dk, int32_t dv, int32_t num_seqs, gdn2_dtype dtype, const void* workspace,
+                            size_t workspace_bytes, bool own_workspace, BwdWorkspace& ws)
 {
+    if (own_workspace) {
+        workspace = nullptr;
+        workspace_bytes = 0;
+    }
     if (dtype != GDN2_DTYPE_F32 && dtype != GDN2_DTYPE_BF16) return GDN2_ERR_BAD_DTYPE;
     if (B <= 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return GDN2_ERR_BAD_SHAPE;
     if (cu_seqlens && (B != 1 || num_seqs <= 0)) return GDN2_ERR_BAD_SHAPE;
@@ -293,8 +302,8 @@ gdn2_status chunk_bwd(const void* q, const void* k, const void* v, const float* 
         if (p && !aligned16(p)) return GDN2_ERR_MISALIGNED;
     if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return GDN2_ERR_MISALIGNED;
 
-    const BwdWorkspace ws = bwd_workspace(B, T, H, dk, dv, cu_seqlens != nullptr, N);
-    if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return GDN2_ERR_WORKSPACE;
+    ws = bwd_workspace(B, T, H, dk, dv, cu_seqlens != nullptr, N);
+    if (!own_workspace && ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return GDN2_ERR_WORKSPACE;
 
     const int64_t tokens = int64_t(B) * T * H;
     const int eb = element_bytes(dtype);
@@ -307,7 +316,7 @@ gdn2_status chunk_bwd(const void* q, const void* k, const void* v, const float* 
     const Span out[] = {span(dq, tokens * dk * eb), span(dk_, tokens * dk * eb), span(dv_, tokens * dv * eb),
                         span(dalpha, tokens * dk * 4), span(db, tokens * dk * eb), span(dw, tokens * dv * eb),
                         span(d_initial_state, d_initial_state ? state_bytes : 0),
-                        span(workspace, ws.total > 0 ? int64_t(ws.total) : 0)};
+                        span(workspace, ws.total > 0 && !own_workspace ? int64_t(ws.total) : 0)};
     constexpr int kDInit = 6;
     for (int i = 0; i < 8; ++i) {
         for (const Span& x : in) {
@@ -318,7 +327,18 @@ gdn2_status chunk_bwd(const void* q, const void* k, const void* v, const float* 
         for (int j = 0; j < i; ++j)
             if (overlap(out[i], out[j])) return GDN2_ERR_ALIAS;
     }
+    return GDN2_OK;
+}
 
+// Launches a checked backward call on the given workspace.
+gdn2_status chunk_bwd_launch(const void* q, const void* k, const void* v, const float* alpha, const void* b,
+                             const void* w, const float* initial_state, const void* d_o, const float* d_final_state,
+                             void* dq, void* dk_, void* dv_, float* dalpha, void* db, void* dw,
+                             float* d_initial_state, const int32_t* cu_seqlens, int32_t B, int32_t T, int32_t H,
+                             int32_t dk, int32_t dv, int32_t num_seqs, gdn2_dtype dtype, void* workspace,
+                             const BwdWorkspace& ws, void* stream)
+{
+    const int32_t N = cu_seqlens ? num_seqs : B;
     gdn2::BwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.b = b; a.w = w;
     a.initial_state = initial_state; a.d_o = d_o; a.d_final_state = d_final_state;
@@ -334,6 +354,44 @@ gdn2_status chunk_bwd(const void* q, const void* k, const void* v, const float* 
     a.ws_prep = ws.total ? reinterpret_cast<float*>(base + 2 * ws.states + 2 * ws.rows) : nullptr;
     const hipError_t e = gdn2::launch_chunk_bwd(a, dtype == GDN2_DTYPE_BF16, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
+gdn2_status chunk_bwd(const void* q, const void* k, const void* v, const float* alpha, const void* b, const void* w,
+                      const float* initial_state, const void* d_o, const float* d_final_state, void* dq, void* dk_,
+                      void* dv_, float* dalpha, void* db, void* dw, float* d_initial_state,
+                      const int32_t* cu_seqlens, int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                      int32_t num_seqs, gdn2_dtype dtype, void* workspace, size_t workspace_bytes, void* stream)
+{
+    BwdWorkspace ws{};
+    const gdn2_status st = chunk_bwd_check(q, k, v, alpha, b, w, initial_state, d_o, d_final_state, dq, dk_, dv_,
+                                           dalpha, db, dw, d_initial_state, cu_seqlens, B, T, H, dk, dv, num_seqs,
+                                           dtype, workspace, workspace_bytes, false, ws);
+    if (st != GDN2_OK) return st;
+    return chunk_bwd_launch(q, k, v, alpha, b, w, initial_state, d_o, d_final_state, dq, dk_, dv_, dalpha, db, dw,
+                            d_initial_state, cu_seqlens, B, T, H, dk, dv, num_seqs, dtype, workspace, ws, stream);
+}
+
+// The same on the library's own scratch array: the host checks run first
+// (the array cannot overlap caller memory), then the workspace size against
+// the array's capacity (larger: GDN2_ERR_WORKSPACE); then the array's device
+// address on the current device is looked up (once per device) and the
+// kernels run on it.  Nothing is allocated.
+gdn2_status chunk_bwd_noalloc(const void* q, const void* k, const void* v, const float* alpha, const void* b,
+                              const void* w, const float* initial_state, const void* d_o,
+                              const float* d_final_state, void* dq, void* dk_, void* dv_, float* dalpha, void* db,
+                              void* dw, float* d_initial_state, const int32_t* cu_seqlens, int32_t B, int32_t T,
+                              int32_t H, int32_t dk, int32_t dv, int32_t num_seqs, gdn2_dtype dtype, void* stream)
+{
+    BwdWorkspace ws{};
+    const gdn2_status st = chunk_bwd_check(q, k, v, alpha, b, w, initial_state, d_o, d_final_state, dq, dk_, dv_,
+                                           dalpha, db, dw, d_initial_state, cu_seqlens, B, T, H, dk, dv, num_seqs,
+                                           dtype, nullptr, 0, true, ws);
+    if (st != GDN2_OK) return st;
+    if (ws.total > gdn2::kScratchBytes) return GDN2_ERR_WORKSPACE;
+    void* scratch = nullptr;
+    if (ws.total > 0 && gdn2::scratch_pointer(&scratch) != hipSuccess) return GDN2_ERR_HIP;
+    return chunk_bwd_launch(q, k, v, alpha, b, w, initial_state, d_o, d_final_state, dq, dk_, dv_, dalpha, db, dw,
+                            d_initial_state, cu_seqlens, B, T, H, dk, dv, num_seqs, dtype, scratch, ws, stream);
 }
 
 }  // namespace
@@ -398,6 +456,19 @@ gdn2_status gdn2_chunk_bwd(const void* q, const void* k, const void* v, const fl
                      d_initial_state, cu_seqlens, B, T, H, dk_size, dv_size, num_seqs, dtype, workspace,
                      workspace_bytes, stream);
 }
+
+gdn2_status gdn2_chunk_bwd_noalloc(const void* q, const void* k, const void* v, const float* alpha, const void* b,
+                                   const void* w, const float* initial_state, const void* d_o,
+                                   const float* d_final_state, void* dq, void* dk, void* dv, float* dalpha, void* db,
+                                   void* dw, float* d_initial_state, const int32_t* cu_seqlens, int32_t B, int32_t T,
+                                   int32_t H, int32_t dk_size, int32_t dv_size, int32_t num_seqs, gdn2_dtype dtype,
+                                   void* stream)
+{
+    return chunk_bwd_noalloc(q, k, v, alpha, b, w, initial_state, d_o, d_final_state, dq, dk, dv, dalpha, db, dw,
+                             d_initial_state, cu_seqlens, B, T, H, dk_size, dv_size, num_seqs, dtype, stream);
+}
+
+size_t gdn2_chunk_bwd_noalloc_max_workspace_bytes(void) { return gdn2::kScratchBytes; }
 
 size_t gdn2_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv, int32_t num_seqs,
                                       gdn2_dtype dtype)

@@ -116,6 +116,11 @@ hipError_t launch_chunk_bwd(const BwdArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_recurrent(const StepArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_chunk_fwd_simple(const ChunkArgs& a, bool bf16, hipStream_t stream);
 
+// Library-owned device scratch (scratch.hip): its capacity, and its device
+// address on the current device (looked up once per device).
+constexpr size_t kScratchBytes = size_t(256) << 20;
+hipError_t scratch_pointer(void** out);
+
 // Matrix-core chunk kernel: bf16 inputs, dk = 128, dv a multiple of 64.
 bool chunk_fwd_mfma_supported(const ChunkArgs& a, bool bf16);
 hipError_t launch_chunk_fwd_mfma(const ChunkArgs& a, hipStream_t stream);

@@ -242,6 +242,41 @@ size_t gdn2_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d
                                       int32_t num_seqs, gdn2_dtype dtype);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * gdn2_chunk_bwd with its workspace taken from a fixed device array that the
+ * library owns, so the call allocates nothing (no hipMalloc, no hipFree, no
+ * allocating library routine).  Arguments, outputs, checks and results are
+ * those of gdn2_chunk_bwd (bitwise the same), without the workspace
+ * arguments.
+ *
+ * Limit: the workspace gdn2_chunk_bwd_workspace_bytes reports for the call
+ * must not exceed gdn2_chunk_bwd_noalloc_max_workspace_bytes() (256 MiB),
+ * else GDN2_ERR_WORKSPACE, before anything is enqueued.  For example
+ * B = 1, T = 2048, H = 16, dk = dv = 128 fits; the B = 8, T = 4096 training
+ * shape (3.4 GB) does not.
+ *
+ * The array: each GPU the library runs on holds its own 256 MiB copy from the
+ * moment the library's code is loaded there until the process ends; its
+ * address is looked up on the call's current device at the first call there.
+ * Every call on one GPU shares that GPU's array and nothing in it needs to
+ * start at zero.  Calls that overlap on one GPU (two streams, two host
+ * threads) race on the array: serialise them.  A failed address lookup
+ * returns GDN2_ERR_HIP.
+ */
+gdn2_status gdn2_chunk_bwd_noalloc(const void* q, const void* k, const void* v,
+                                   const float* alpha, const void* b, const void* w,
+                                   const float* initial_state, const void* d_o,
+                                   const float* d_final_state,
+                                   void* dq, void* dk, void* dv, float* dalpha, void* db, void* dw,
+                                   float* d_initial_state, const int32_t* cu_seqlens,
+                                   int32_t B, int32_t T, int32_t H, int32_t dk_size, int32_t dv_size,
+                                   int32_t num_seqs, gdn2_dtype dtype, void* stream);
+
+/* Capacity of the library-owned workspace of gdn2_chunk_bwd_noalloc, in bytes. */
+size_t gdn2_chunk_bwd_noalloc_max_workspace_bytes(void);
+
+/*
  * Token-mixer prologue: q, k, v, b, w for the recurrence from the projection
  * outputs, in one pass ("Token processing and parallel training": short
  * causal convolution, SiLU and L2 normalisation on the query and key paths,

@@ -264,6 +264,43 @@ def test_chunk_bwd_rejects(lib, kw, expected):
     assert bwd_call(lib, **kw) == expected
 
 
+def bwd_noalloc_call(lib, **kw):
+    # as bwd_call, without the workspace arguments
+    args = dict(q=fake(0), k=fake(1), v=fake(2), alpha=fake(3), b=fake(4), w=fake(5), s0=fake(6),
+                d_o=fake(7), dsf=fake(8), dq=fake(9), dk=fake(10), dv=fake(11), dalpha=fake(12),
+                db=fake(13), dw=fake(14), ds0=fake(15), cu=None, B=2, T=64, H=4, dk_=64, dv_=64,
+                num_seqs=0, dtype=1)
+    args.update(kw)
+    a = args
+    return lib.gdn2_chunk_bwd_noalloc(a["q"], a["k"], a["v"], a["alpha"], a["b"], a["w"], a["s0"], a["d_o"],
+                                      a["dsf"], a["dq"], a["dk"], a["dv"], a["dalpha"], a["db"], a["dw"], a["ds0"],
+                                      a["cu"], a["B"], a["T"], a["H"], a["dk_"], a["dv_"], a["num_seqs"],
+                                      a["dtype"], None)
+
+
+def test_bwd_noalloc_capacity(lib):
+    assert binding.gdn2_chunk_bwd_noalloc_max_workspace_bytes() == 256 << 20
+    # the documented examples: B=1 T=2048 H=16 d=128 fits, the B=8 T=4096 training shape does not
+    assert binding.gdn2_chunk_bwd_workspace_bytes(1, 2048, 16, 128, 128, 0, 1) <= 256 << 20
+    assert binding.gdn2_chunk_bwd_workspace_bytes(8, 4096, 16, 128, 128, 0, 1) > 256 << 20
+
+
+# Every case must be rejected on the host, before the library's array is looked up.
+@pytest.mark.parametrize("kw,expected", [
+    (dict(dtype=2), DTYPE),
+    (dict(B=0), SHAPE),
+    (dict(dk_=48), UNSUP),
+    (dict(d_o=None), NULLP),
+    (dict(dalpha=fake(12, 4)), MISAL),
+    (dict(dq=fake(0, 1024)), ALIAS),                  # dq inside q
+    (dict(ds0=fake(6)), ALIAS),                       # d_initial_state == initial_state
+    (dict(B=8, T=4096, H=16, dk_=128, dv_=128), WS),  # workspace of 3.4 GB > 256 MiB
+    (dict(B=1, T=4096, H=16, dk_=128, dv_=128), WS),  # 335 MB > 256 MiB
+])
+def test_chunk_bwd_noalloc_rejects(lib, kw, expected):
+    assert bwd_noalloc_call(lib, **kw) == expected
+
+
 def pro_call(lib, **kw):
     # B=2, T=64, H=4, dk=dv=64, K=4 bf16: token tensors 64 KiB; filters 4 KiB; state 2 x 768 x 3 x 4 B
     args = dict(xq=fake(0), xk=fake(1), xv=fake(2), cq=fake(3), ck=fake(4), cv=fake(5), bl=fake(6), wl=fake(7),
