@@ -11,7 +11,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libgdn2.so")
+# GDN2_LIBRARY names another build of the library to load (the sanitizer
+# check loads a build whose host code carries AddressSanitizer).
+LIB_PATH = os.environ.get("GDN2_LIBRARY") or os.path.join(PKG, "libgdn2.so")
 
 GDN2_OK = 0
 STATUS_NAMES = {

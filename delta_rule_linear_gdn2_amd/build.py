@@ -64,6 +64,48 @@ def build(extra: list[str] | None = None, jobs: int | None = None) -> str:
     return LIB
 
 
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer for the C ABI's
+# argument checking (gdn2_api.cpp holds no device code; every sanitizer flag
+# is host-only).
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-sanitize-recover=all"]
+SAN_RUNTIME = "libclang_rt.asan-x86_64.so"
+
+
+def sanitizer_runtime_dir() -> str:
+    """Directory of the clang sanitizer runtime the sanitized build links."""
+    r = subprocess.run([HIPCC, "-print-resource-dir"], capture_output=True, text=True, check=True)
+    return os.path.join(r.stdout.strip(), "lib", "linux")
+
+
+def build_sanitized(out_dir: str) -> str:
+    """``libgdn2_asan.so`` in out_dir: gdn2_api.cpp built with the host
+    sanitizers, linked with the kernels' regular objects (built here if
+    missing).  Load it with the clang sanitizer runtime preloaded."""
+    os.makedirs(out_dir, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        if src == "gdn2_api.cpp":
+            obj = os.path.join(out_dir, "gdn2_api_asan.o")
+            cmd = [HIPCC, "-O1", "-g", "-std=c++17", "-fPIC", "-fno-omit-frame-pointer", "-Wall", *SAN_FLAGS,
+                   f"-I{os.path.join(ROOT, 'include')}", "-c", os.path.join(CSRC, src), "-o", obj]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"sanitized build of {src} failed:\n{' '.join(cmd)}\n{r.stderr}")
+            objs.append(obj)
+        else:
+            obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+            if not os.path.exists(obj):
+                os.makedirs(BUILD, exist_ok=True)
+                obj = _compile(src, [])
+            objs.append(obj)
+    lib = os.path.join(out_dir, "libgdn2_asan.so")
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *SAN_FLAGS, "-shared-libsan", "-o", lib, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized link failed:\n{' '.join(cmd)}\n{r.stderr}")
+    return lib
+
+
 def clean() -> None:
     shutil.rmtree(BUILD, ignore_errors=True)
     if os.path.exists(LIB):

@@ -69,6 +69,7 @@ const char* gdn2_status_string(gdn2_status s)
         case GDN2_ERR_ALIAS: return "GDN2_ERR_ALIAS: an output overlaps an input";
         case GDN2_ERR_WORKSPACE: return "GDN2_ERR_WORKSPACE: workspace too small";
         case GDN2_ERR_HIP: return "GDN2_ERR_HIP: the HIP runtime reported an error";
+        default: break;
     }
     return "GDN2: unknown status";
 }

@@ -56,12 +56,20 @@ typedef enum gdn2_status {
     GDN2_ERR_MISALIGNED = 5,   /* a tensor pointer is not 16-byte aligned            */
     GDN2_ERR_ALIAS = 6,        /* an output overlaps an input it may not overlap     */
     GDN2_ERR_WORKSPACE = 7,    /* workspace smaller than the query function's answer */
-    GDN2_ERR_HIP = 8           /* the HIP runtime reported an error at launch        */
+    GDN2_ERR_HIP = 8,          /* the HIP runtime reported an error at launch        */
+    /* not statuses: with these every int32 value is a valid gdn2_status, so
+       unknown codes are safe to pass */
+    GDN2_STATUS_MIN_ENUM = -0x7fffffff - 1,
+    GDN2_STATUS_MAX_ENUM = 0x7fffffff
 } gdn2_status;
 
 typedef enum gdn2_dtype {
     GDN2_DTYPE_F32 = 0,
-    GDN2_DTYPE_BF16 = 1
+    GDN2_DTYPE_BF16 = 1,
+    /* not dtypes (GDN2_ERR_BAD_DTYPE): with these every int32 value is a valid
+       gdn2_dtype, so bad codes are safe to pass */
+    GDN2_DTYPE_MIN_ENUM = -0x7fffffff - 1,
+    GDN2_DTYPE_MAX_ENUM = 0x7fffffff
 } gdn2_dtype;
 
 /*

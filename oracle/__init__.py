@@ -40,8 +40,16 @@ _LIB = None
 
 
 def load(path: str | None = None):
-    """Load (building first if stale) the oracle shared library."""
+    """Load (building first if stale) the oracle shared library.  The
+    environment variable GDN2_ORACLE_LIB names another build of the same
+    source to load instead (the sanitizer check uses it)."""
     global _LIB
+    if path is None and os.environ.get("GDN2_ORACLE_LIB"):
+        path = os.environ["GDN2_ORACLE_LIB"]
+        if _LIB is None:
+            _LIB = ctypes.CDLL(path)
+            _declare(_LIB)
+        return _LIB
     if path is not None:
         lib = ctypes.CDLL(path)
         _declare(lib)
