@@ -15,12 +15,23 @@
 //     out = o / sqrt(mean(o^2) + eps) * weight * act(gate)      (epilogue)
 // with L2norm(x) = x / sqrt(sum x^2 + eps_l2).
 //
-// Each is one pass over HBM with lanes over channels (channel pairs for
-// 128-wide heads) and the norms as wave reductions.  A prologue wavefront
-// walks 16 consecutive tokens of one (sequence, head), holding the filter taps
-// and the window of the last K - 1 inputs in registers, so every input is
-// read once; an epilogue row takes a group of dv / 8 lanes with 16-byte
-// accesses (four 128-wide rows per wavefront).
+// Each is one pass over HBM, with the norms as reductions inside lane groups.
+//   * Prologue, filters of up to four taps (the usual short convolution): one
+//     wavefront per (output, batch row, group of heads, run of 64 tokens),
+//     where an output is one of q, k, v (convolution, SiLU, and the L2 norm
+//     for q and k) or b, w (sigmoid).  A lane takes eight channels with
+//     16-byte accesses and a head takes d / 8 lanes, so one load of the
+//     wavefront covers 64 / (d / 8) adjacent heads of one token.  The three
+//     inputs before the current token stay in registers; tokens go four at a
+//     time with the next four's loads in flight.  At a sequence start the
+//     window restarts from the carried state; the token that ends a sequence
+//     writes the new state, and a small pass carries the state through empty
+//     sequences.
+//   * Prologue, longer filters (5 to 16 taps): a wavefront walks 16
+//     consecutive tokens of one (sequence, head) with two channels per lane,
+//     holding the taps and the window of the last K - 1 inputs in registers.
+//   * Epilogue: a group of dv / 8 lanes per (token, head) row with 16-byte
+//     accesses (four 128-wide rows per wavefront).
 #include "gdn2_device.hpp"
 #include "launch.hpp"
 
