@@ -454,7 +454,7 @@ def run_configs(args):
     full, tied, scalar = binding.GATES_FULL, binding.GATES_KDA, binding.GATES_GDN
     # (gate mode of the inputs, layout passed): the reduced-gate inputs run once
     # broadcast through the full layout and once in their compact layout
-    for name, modes, rotate in (("layer_bf16", (("gdn2", full),), 3),
+    for name, modes, rotate in (("layer_bf16", (("gdn2", full),), 3), ("long16k_bf16", (("gdn2", full),), 1),
                                 ("batched_bf16", (("gdn2", full), ("kda", tied), ("gdn", scalar)), 1),
                                 ("varlen32_bf16", (("gdn2", full), ("kda", full), ("kda", tied), ("gdn", full),
                                                    ("gdn", scalar)), 1)):
@@ -481,12 +481,19 @@ def run_configs(args):
             sf = torch.empty((N, H, dk, dv), dtype=torch.float32, device="cuda")
             idx = [0]
 
-            def call():
+            few = binding.gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, 0 if x["cu_seqlens"] is None else N,
+                                                         binding.DTYPE_BF16 if wl.dtype == "bf16" else 0) > 0
+
+            def call(segmented=True):
                 d = sets[idx[0] % rotate]
                 idx[0] += 1
                 binding.gdn2_chunk_fwd_gates(d["q"], d["k"], d["v"], d["alpha"], d["b"], d["w"], gates, d["s0"],
-                                             final_state=sf, out=o, cu_seqlens=d["cu"])
+                                             final_state=sf, out=o, cu_seqlens=d["cu"], segmented=segmented)
 
+            if few:  # the single pass beside the segmented path the call takes
+                per1, _, _ = time_events(lambda: call(False), args.warmup, args.steps)
+                single_ms = float(np.median(per1))
+                log(f"{name}: single pass {single_ms * 1e3:.1f} us")
             per, _, _ = time_events(call, args.warmup, args.steps)
             kern_ms = float(np.median(per))
             nbytes = chunk_bytes(B, T, H, dk, dv, N, 2 if wl.dtype == "bf16" else 4, gates)
@@ -498,6 +505,9 @@ def run_configs(args):
                    "GBps": nbytes / (kern_ms / 1e3) / 1e9,
                    "hbm_frac": nbytes / (kern_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
                    "input_sets": rotate, "timing": f"median of {args.steps} launches after {args.warmup}"}
+            if few:
+                row["path"] = "segmented (few chains)"
+                row["single_pass_us"] = single_ms * 1e3
             log(f"{name}/{mode}/{layout}: {row['us_per_call']:.1f} us, {row['tokens_per_s'] / 1e6:.1f} M tokens/s, "
                 f"{row['hbm_frac'] * 100:.1f}% HBM")
             print(json.dumps(row), flush=True)
@@ -594,7 +604,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="batched_bf16",
-                    choices=["batched_bf16", "layer_bf16", "varlen32_bf16", "tiny_f32"])
+                    choices=["batched_bf16", "layer_bf16", "long16k_bf16", "varlen32_bf16", "tiny_f32"])
     ap.add_argument("--no-decode", action="store_true", help="skip the decode half")
     ap.add_argument("--only", choices=["chunk", "decode", "copy", "bwd", "mixer"], default=None,
                     help="profiling aid: run one part only and print its timing line "

@@ -159,7 +159,7 @@ def _gate_widths(gates, dk, dv):
 
 
 def _chunk_fwd(q, k, v, alpha, b, w, gates, initial_state, output_final_state, final_state, out,
-               cu_seqlens, stream):
+               cu_seqlens, stream, segmented=True):
     import torch
 
     lib = load()
@@ -189,7 +189,9 @@ def _chunk_fwd(q, k, v, alpha, b, w, gates, initial_state, output_final_state, f
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     elif final_state is not None:
         _check("final_state", final_state, (N, H, dk, dv), torch.float32, dev)
-    ws_bytes = gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, code)
+    ws_bytes = gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N if cu_seqlens is not None else 0, code)
+    if not segmented:
+        ws_bytes = 0
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(initial_state), _ptr(final_state),
             _ptr(out), _ptr(cu_seqlens), B, T, H, dk, dv, N, code)
@@ -204,7 +206,7 @@ def _chunk_fwd(q, k, v, alpha, b, w, gates, initial_state, output_final_state, f
 
 
 def gdn2_chunk_fwd(q, k, v, alpha, b, w, initial_state=None, *, output_final_state=True,
-                   final_state=None, out=None, cu_seqlens=None, stream=None):
+                   final_state=None, out=None, cu_seqlens=None, stream=None, segmented=True):
     """Chunkwise GDN-2 forward.  Returns ``(o, final_state)`` (final_state may be None).
 
     q, k, b: [B, T, H, dk]; v, w: [B, T, H, dv] (float32 or bfloat16, all the
@@ -212,20 +214,23 @@ def gdn2_chunk_fwd(q, k, v, alpha, b, w, initial_state=None, *, output_final_sta
     or None; cu_seqlens: int32 [N + 1] on the device or None (then B must be 1).
     ``final_state`` may be passed (e.g. the initial_state tensor itself for an
     in-place update); otherwise it is allocated when ``output_final_state``.
+    The workspace gdn2_chunk_fwd_workspace_bytes asks for is allocated, which
+    selects the segmented path for few-chain shapes; ``segmented=False``
+    passes none (the single pass).
     """
     return _chunk_fwd(q, k, v, alpha, b, w, GATES_FULL, initial_state, output_final_state, final_state, out,
-                      cu_seqlens, stream)
+                      cu_seqlens, stream, segmented)
 
 
 def gdn2_chunk_fwd_gates(q, k, v, alpha, b, w, gates, initial_state=None, *, output_final_state=True,
-                         final_state=None, out=None, cu_seqlens=None, stream=None):
+                         final_state=None, out=None, cu_seqlens=None, stream=None, segmented=True):
     """gdn2_chunk_fwd with a gate layout, an OR of the GATES_* flags:
     SCALAR_ERASE takes b as [B, T, H]; SCALAR_WRITE takes w as [B, T, H];
     TIED (with SCALAR_ERASE) uses b as the write gate too (w ignored, may be
     None); SCALAR_DECAY takes alpha as [B, T, H] float32.  GATES_FULL is
     gdn2_chunk_fwd; GATES_KDA and GATES_GDN are the two reductions."""
     return _chunk_fwd(q, k, v, alpha, b, w, gates, initial_state, output_final_state, final_state, out,
-                      cu_seqlens, stream)
+                      cu_seqlens, stream, segmented)
 
 
 def _recurrent_step(q, k, v, alpha, b, w, gates, state, out, stream):

@@ -26,6 +26,7 @@ SOURCES = [
     "chunk_bwd.hip",
     "mixer.hip",
     "scratch.hip",
+    "segments.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -399,17 +399,20 @@ __device__ __forceinline__ void load_alpha(RawK& R, const RawSrc& s, int t, cons
     R.a[t][1] = ld_b128(s.a, off + 16);
 }
 
-template <int G>
+template <int G, bool SEG>
 __device__ __forceinline__ void load_vk(RawVK& V, const ChunkArgs& a, int64_t row0, int L, int j0, int kw, int lane)
 {
-    const uint32_t vstride = uint32_t(a.H) * uint32_t(a.dv) * 2;
-    const uint32_t win = L > 0 ? uint32_t(L - 1) * vstride + kDVT * 2 : 0u;
-    const int64_t base = row0 * a.dv + j0;
+    const int dvio = SEG && a.dv_io > 0 ? a.dv_io : a.dv;
+    const bool real = !SEG || j0 < dvio;
+    const uint32_t vstride = uint32_t(a.H) * uint32_t(dvio) * 2;
+    // map columns (j0 >= dv_io) have no v, w: an empty window reads zeros, so z = 0
+    const uint32_t win = L > 0 && real ? uint32_t(L - 1) * vstride + kDVT * 2 : 0u;
+    const int64_t base = row0 * dvio + (real ? j0 : 0);
     const uint32_t tok = uint32_t(16 * (kw & 3) + (lane & 15));
     const rsrc_t rv = make_rsrc(static_cast<const bf16raw*>(a.v) + base, win);
     const uint32_t off = tok * vstride + 2 * (8 * (lane >> 4));
     if (G & (kTied | kScalarWrite)) {  // the token's scalar write gate (tied: its erase gate)
-        const uint32_t rows = L > 0 ? uint32_t(L - 1) * uint32_t(a.H) + 1 : 0u;
+        const uint32_t rows = L > 0 && real ? uint32_t(L - 1) * uint32_t(a.H) + 1 : 0u;
         const rsrc_t rg = make_rsrc(static_cast<const bf16raw*>(G & kTied ? a.b : a.w) + row0, 2 * rows);
 #pragma unroll
         for (int u = 0; u < 2; ++u) V.v[u] = ld_b128(rv, off + 64 * u);
@@ -851,7 +854,7 @@ __device__ __forceinline__ void value_chunk(const unsigned char* lds, const Lane
     }
 }
 
-template <int G>
+template <int G, bool SEG>
 __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, int ntiles, int nchains)
 {
     extern __shared__ __align__(16) unsigned char lds[];
@@ -870,10 +873,23 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
     if (chain >= nchains) return;
     const int n = chain / a.H, h = chain % a.H;
     const int j0 = tile * kDVT;
-    const int64_t dv = a.dv;
+    const int64_t dv = a.dv;  // columns of the carried state
+    // segment mode (SEG): columns of v, w, o and the caller's states, and
+    // whether this tile holds state-map columns (identity start, z = 0, no output)
+    const int64_t dvio = SEG && a.dv_io > 0 ? a.dv_io : a.dv;
+    const bool map_tile = SEG && j0 >= dvio;
 
     int64_t bos, eos, brow;
-    sequence_bounds(a.cu_seqlens, n, a.T, bos, eos, brow);
+    int seg = 0;  // segment of the row (segment mode)
+    if (SEG) {
+        brow = n / a.seg_count;
+        seg = a.seg_first + n % a.seg_count;
+        bos = int64_t(seg) * a.seg_len;
+        eos = bos + a.seg_len < a.T ? bos + a.seg_len : a.T;
+        if (bos > eos) bos = eos;
+    } else {
+        sequence_bounds(a.cu_seqlens, n, a.T, bos, eos, brow);
+    }
 
     // The blocks the solve and the output read as zero (A on the diagonal, P
     // right of it) are never written: clear Aneg and P once.
@@ -893,23 +909,39 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
     if (vwave) {
         // state slice of a value wavefront: channels 16 cb + 4 g + i, column j0 + 16 wave + r
         f32x4 S[8];
-        const int64_t sbase = (int64_t(n) * a.H + h) * kDK * dv + j0;
-        const uint32_t sbytes = uint32_t(kDK * dv * 4);
-        const int s_vo = ((4 * g0) * int(dv) + 16 * wave + r0) * 4;
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb) S[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (a.initial_state) {
-            const rsrc_t rs = make_rsrc(a.initial_state + sbase, sbytes);
+        // the initial state: a [..][dk][dv_io] FP32 array, columns j0 .. j0 + 63
+        const float* sin = nullptr;
+        if (map_tile) {  // identity: column j0 + 16 wave + r holds e_(j0 - dv_io + 16 wave + r)
+            const int d = int(j0 - dvio) + 16 * wave + r0;
+#pragma unroll
+            for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[cb][i] = 16 * cb + 4 * g0 + i == d ? 1.f : 0.f;
+        } else if (SEG && a.seg_states_in) {
+            sin = a.seg_states_in + ((int64_t(brow) * a.seg_total + seg) * a.H + h) * kDK * dvio + j0;
+        } else if (!SEG || seg == 0) {
+            sin = a.initial_state ? a.initial_state + (int64_t(SEG ? brow : n) * a.H + h) * kDK * dvio + j0 : nullptr;
+        }
+        if (sin) {
+            const int win = int(dvio);
+            const rsrc_t rs = make_rsrc(sin, uint32_t(kDK * win * 4));
+            const int s_vo = ((4 * g0) * win + 16 * wave + r0) * 4;
 #pragma unroll
             for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     S[cb][i] = __uint_as_float(
-                        __builtin_amdgcn_raw_buffer_load_b32(rs, s_vo, (16 * cb + i) * int(dv) * 4, 0));
+                        __builtin_amdgcn_raw_buffer_load_b32(rs, s_vo, (16 * cb + i) * win * 4, 0));
         }
 
+        // outputs: real columns only, and in segment mode per seg_o_all; token
+        // tv of this (row, head) at obase + tv * H * dv_io
+        const bool store_o = !SEG || (!map_tile && (a.seg_o_all || seg == 0));
         bf16raw* o = static_cast<bf16raw*>(a.o);
-        const int ostride = a.H * int(dv) * 2;
+        const int ostride = a.H * int(dvio) * 2;
+        const uint32_t o_on = store_o ? ~0u : 0u;
         int lv = 0;  // length of chunk tv
         while (tk < eos || tv >= 0) {
             const bool has_k = tk < eos, has_v = tv >= 0;
@@ -920,8 +952,9 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
             if (has_k && wave == 0) value_gamma(lds, step, kbuf, lane);  // read by the next period's update
 
             if (has_v) {
-                const rsrc_t ro = make_rsrc(o + token_row(a, brow, tv, h) * dv + j0,
-                                            uint32_t(lv - 1) * uint32_t(ostride) + kDVT * 2);
+                const rsrc_t ro = make_rsrc(o + token_row(a, brow, tv, h) * dvio + j0,
+                                            SEG ? o_on & (uint32_t(lv - 1) * uint32_t(ostride) + kDVT * 2)
+                                                : uint32_t(lv - 1) * uint32_t(ostride) + kDVT * 2);
                 value_chunk(lds, lane_offsets(r, g), S, lv, kbuf ^ 1, ro, ostride, wave, r, g);
             }
             const int64_t tn = tk + step;
@@ -940,14 +973,23 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
             tk = has_k ? tn : eos;
             kbuf ^= 1;
         }
-        if (a.final_state) {
-            const rsrc_t rs = make_rsrc(a.final_state + sbase, sbytes);
+        float* sout = nullptr;
+        int wout = int(dvio);
+        if (SEG && a.seg_states_out) {
+            sout = a.seg_states_out + ((int64_t(brow) * a.seg_total + seg) * a.H + h) * kDK * dv + j0;
+            wout = int(dv);
+        } else if (!map_tile && a.final_state && (!SEG || seg == a.seg_total - 1)) {
+            sout = a.final_state + (int64_t(SEG ? brow : n) * a.H + h) * kDK * dvio + j0;
+        }
+        if (sout) {
+            const rsrc_t rs = make_rsrc(sout, uint32_t(kDK * wout * 4));
+            const int s_vo = ((4 * g0) * wout + 16 * wave + r0) * 4;
 #pragma unroll
             for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(S[cb][i]), rs, s_vo,
-                                                          (16 * cb + i) * int(dv) * 4, 0);
+                                                          (16 * cb + i) * wout * 4, 0);
         }
     } else {
         // Key side.  The decay products of a chunk are formed after B1 of the
@@ -974,7 +1016,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
                 load_q(R, src, t, K);
                 load_kb<G>(R, src, t, K);
             }
-            if (K.ch == 0) load_vk<G>(V, a, token_row(a, brow, tk, h), L, j0, kw, lane0);
+            if (K.ch == 0) load_vk<G, SEG>(V, a, token_row(a, brow, tk, h), L, j0, kw, lane0);
             decay_pass1<G>(lds, R, al, ex, L, K, lane0);
         }
         while (tk < eos || tv >= 0) {
@@ -1008,7 +1050,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
                 // z of chunk tk (read by the value side next period), then v, w of the next chunk
                 if (K.ch == 0) {
                     store_z<G>(lds, V, kbuf, kw, lane);
-                    load_vk<G>(V, a, token_row(a, brow, Ln > 0 ? tn : tk, h), Ln, j0, kw, lane);
+                    load_vk<G, SEG>(V, a, token_row(a, brow, Ln > 0 ? tn : tk, h), Ln, j0, kw, lane);
                 }
             }
             if (Ln > 0) decay_pass1<G>(lds, R, al, ex, Ln, K, lane);
@@ -1029,20 +1071,27 @@ bool chunk_fwd_mfma_supported(const ChunkArgs& a, bool bf16)
 
 namespace {
 
-template <int G>
-hipError_t launch_gates(const ChunkArgs& a, hipStream_t stream)
+template <int G, bool SEG>
+hipError_t launch_mode(const ChunkArgs& a, hipStream_t stream)
 {
     // Allow the kernel its > 64 KiB of dynamic LDS (thread-safe one-time call).
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fwd_mfma_kernel<G>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    static const hipError_t attr =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fwd_mfma_kernel<G, SEG>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (attr != hipSuccess) return attr;
     const int ntiles = a.dv / kDVT;
     const int64_t chains = int64_t(a.N) * a.H;
     const int64_t blocks = (chains + 7) / 8 * 8 * ntiles;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(chunk_fwd_mfma_kernel<G>, dim3(unsigned(blocks)), dim3(kThreads), kLdsBytes, stream, a,
-                       ntiles, int(chains));
+    hipLaunchKernelGGL((chunk_fwd_mfma_kernel<G, SEG>), dim3(unsigned(blocks)), dim3(kThreads), kLdsBytes, stream,
+                       a, ntiles, int(chains));
     return hipGetLastError();
+}
+
+template <int G>
+hipError_t launch_gates(const ChunkArgs& a, hipStream_t stream)
+{
+    return a.seg_len > 0 ? launch_mode<G, true>(a, stream) : launch_mode<G, false>(a, stream);
 }
 
 }  // namespace

@@ -53,6 +53,49 @@ int32_t device_cus()
     return cus;
 }
 
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Sequence segments for chunkwise calls with few (sequence, head) chains: the
+// plan and its workspace.  The matrix-core kernel runs one workgroup per
+// (chain, 64-column value tile), one per CU, walking the sequence chunk by
+// chunk, so B x H x dv / 64 workgroups leave most of the GPU idle when that
+// is small.  Cutting each row into P segments gives P-fold parallelism for
+// the cost of a second pass (see segments.hip):
+//   pass 1: segments 0 .. P - 2 of every row, each with dv + dk columns (the
+//           real ones from a zero state, segment 0 from the caller's; dk map
+//           columns from the identity), final states into the workspace;
+//           outputs of segment 0 only;
+//   combine: the true incoming state of segments 1 .. P - 1;
+//   pass 2: segments 1 .. P - 1 from those states, outputs and the final
+//           state.
+// P is chosen so that pass 1 fills the GPU once (at most one workgroup per
+// CU); segments are whole chunks of at least 256 tokens, at least three are
+// needed for a gain, and rows shorter than 1024 tokens keep the single pass.
+struct SegPlan {
+    int32_t P = 0, len = 0;
+    size_t out_bytes = 0, in_bytes = 0, total = 0;
+};
+
+SegPlan seg_plan(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv, bool packed, bool bf16, int32_t cus)
+{
+    SegPlan sp;
+    if (!bf16 || dk != 128 || dv % 64 != 0 || packed || B <= 0 || H <= 0 || T < 1024) return sp;
+    const int64_t per_seg = int64_t(B) * H * ((dv + dk) / 64);  // pass-1 workgroups per segment
+    const int64_t fit = cus / per_seg;                          // segments pass 1 can hold at once
+    if (fit < 2) return sp;
+    int64_t P = fit + 1;
+    int64_t len = ((T + P - 1) / P + 63) / 64 * 64;
+    if (len < 256) len = 256;
+    P = (T + len - 1) / len;
+    if (P < 3) return sp;
+    sp.P = int32_t(P);
+    sp.len = int32_t(len);
+    sp.out_bytes = align256(size_t(B) * P * H * dk * (dv + dk) * 4);
+    sp.in_bytes = align256(size_t(B) * P * H * dk * dv * 4);
+    sp.total = sp.out_bytes + sp.in_bytes;
+    return sp;
+}
+
 }  // namespace
 
 extern "C" {
@@ -76,9 +119,10 @@ const char* gdn2_status_string(gdn2_status s)
 
 int32_t gdn2_version(void) { return kVersion; }
 
-size_t gdn2_chunk_fwd_workspace_bytes(int32_t, int32_t, int32_t, int32_t, int32_t, int32_t, gdn2_dtype)
+size_t gdn2_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv, int32_t num_seqs,
+                                      gdn2_dtype dtype)
 {
-    return 0;
+    return seg_plan(B, T, H, dk, dv, num_seqs > 0, dtype == GDN2_DTYPE_BF16, device_cus()).total;
 }
 
 }  // extern "C"
@@ -98,7 +142,7 @@ bool valid_gates(int32_t g)
 gdn2_status chunk_fwd(const void* q, const void* k, const void* v, const float* alpha, const void* b, const void* w,
                       const float* initial_state, float* final_state, void* o, const int32_t* cu_seqlens, int32_t B,
                       int32_t T, int32_t H, int32_t dk, int32_t dv, int32_t num_seqs, gdn2_dtype dtype,
-                      int32_t gates, void* stream)
+                      int32_t gates, void* workspace, size_t workspace_bytes, void* stream)
 {
     if (dtype != GDN2_DTYPE_F32 && dtype != GDN2_DTYPE_BF16) return GDN2_ERR_BAD_DTYPE;
     if (!valid_gates(gates)) return GDN2_ERR_BAD_SHAPE;
@@ -109,10 +153,14 @@ gdn2_status chunk_fwd(const void* q, const void* k, const void* v, const float* 
     if (tied) w = nullptr;  // ignored
     const int32_t N = cu_seqlens ? num_seqs : B;
     if (T > 0 && (!q || !k || !v || !alpha || !b || (!tied && !w) || !o)) return GDN2_ERR_NULL_POINTER;
-    const void* ptrs[] = {q, k, v, alpha, b, w, o, initial_state, final_state};
+    const void* ptrs[] = {q, k, v, alpha, b, w, o, initial_state, final_state, workspace};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return GDN2_ERR_MISALIGNED;
     if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return GDN2_ERR_MISALIGNED;
+    const bool bf16 = dtype == GDN2_DTYPE_BF16;
+    // the segmented path runs when the caller passes the workspace it needs
+    const SegPlan sp = workspace ? seg_plan(B, T, H, dk, dv, cu_seqlens != nullptr, bf16, device_cus()) : SegPlan{};
+    if (sp.P > 0 && workspace_bytes < sp.total) return GDN2_ERR_WORKSPACE;
 
     const int64_t tokens = int64_t(B) * T * H;
     const int eb = element_bytes(dtype);
@@ -130,11 +178,40 @@ gdn2_status chunk_fwd(const void* q, const void* k, const void* v, const float* 
     for (Span in : {sq, sk, sv, sa, sb, sw, sc, so})
         if (overlap(sf, in)) return GDN2_ERR_ALIAS;
     if (overlap(sf, si) && final_state != initial_state) return GDN2_ERR_ALIAS;
+    const Span sws = span(workspace, int64_t(sp.total));
+    for (Span x : {sq, sk, sv, sa, sb, sw, si, sc, so, sf})
+        if (overlap(sws, x)) return GDN2_ERR_ALIAS;
 
     gdn2::ChunkArgs a{q, k, v, alpha, b, w, initial_state, final_state, o, cu_seqlens,
                       B, T, H, dk, dv, N, device_cus(), gates};
-    const bool bf16 = dtype == GDN2_DTYPE_BF16;
     const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (sp.P > 0 && T > 0) {
+        float* seg_out = static_cast<float*>(workspace);
+        float* seg_in = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + sp.out_bytes);
+        gdn2::ChunkArgs p1 = a;  // pass 1: segments 0 .. P - 2, real and map columns
+        p1.dv = dv + dk;
+        p1.dv_io = dv;
+        p1.N = B * (sp.P - 1);
+        p1.seg_len = sp.len;
+        p1.seg_total = sp.P;
+        p1.seg_first = 0;
+        p1.seg_count = sp.P - 1;
+        p1.seg_o_all = 0;
+        p1.seg_states_out = seg_out;
+        gdn2::ChunkArgs p2 = a;  // pass 2: segments 1 .. P - 1 from their true incoming states
+        p2.dv_io = dv;
+        p2.N = B * (sp.P - 1);
+        p2.seg_len = sp.len;
+        p2.seg_total = sp.P;
+        p2.seg_first = 1;
+        p2.seg_count = sp.P - 1;
+        p2.seg_o_all = 1;
+        p2.seg_states_in = seg_in;
+        hipError_t e = gdn2::launch_chunk_fwd_mfma(p1, st);
+        if (e == hipSuccess) e = gdn2::launch_segment_combine(seg_out, seg_in, B, H, dk, dv, sp.P, st);
+        if (e == hipSuccess) e = gdn2::launch_chunk_fwd_mfma(p2, st);
+        return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+    }
     const hipError_t e = gdn2::chunk_fwd_mfma_supported(a, bf16) ? gdn2::launch_chunk_fwd_mfma(a, st)
                                                                  : gdn2::launch_chunk_fwd_simple(a, bf16, st);
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
@@ -261,8 +338,6 @@ struct BwdWorkspace {
     int64_t slots;
     size_t states, rows, prep, total;
 };
-
-size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 BwdWorkspace bwd_workspace(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv, bool varlen, int32_t N)
 {
@@ -405,10 +480,8 @@ gdn2_status gdn2_chunk_fwd(const void* q, const void* k, const void* v, const fl
                            int32_t T, int32_t H, int32_t dk, int32_t dv, int32_t num_seqs,
                            gdn2_dtype dtype, void* workspace, size_t workspace_bytes, void* stream)
 {
-    (void)workspace;
-    (void)workspace_bytes;
     return chunk_fwd(q, k, v, alpha, b, w, initial_state, final_state, o, cu_seqlens, B, T, H, dk, dv, num_seqs,
-                     dtype, GDN2_GATES_FULL, stream);
+                     dtype, GDN2_GATES_FULL, workspace, workspace_bytes, stream);
 }
 
 gdn2_status gdn2_chunk_fwd_gates(const void* q, const void* k, const void* v, const float* alpha,
@@ -418,10 +491,8 @@ gdn2_status gdn2_chunk_fwd_gates(const void* q, const void* k, const void* v, co
                                  gdn2_dtype dtype, int32_t gates, void* workspace,
                                  size_t workspace_bytes, void* stream)
 {
-    (void)workspace;
-    (void)workspace_bytes;
     return chunk_fwd(q, k, v, alpha, b, w, initial_state, final_state, o, cu_seqlens, B, T, H, dk, dv, num_seqs,
-                     dtype, gates, stream);
+                     dtype, gates, workspace, workspace_bytes, stream);
 }
 
 gdn2_status gdn2_recurrent_step(const void* q, const void* k, const void* v, const float* alpha,

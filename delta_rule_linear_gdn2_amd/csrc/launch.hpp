@@ -23,6 +23,23 @@ struct ChunkArgs {
     int32_t B, T, H, dk, dv, N;
     int32_t cus;    // compute units of the device
     int32_t gates;  // gdn2_gate_flags, validated: 1 scalar erase, 2 scalar write, 4 write tied to erase, 8 scalar decay
+    // Sequence segments (matrix-core kernel only; seg_len = 0: off).  Each
+    // batch row (no cu_seqlens) is cut into seg_total segments of seg_len
+    // tokens (the last may be shorter); launch sequence n is segment
+    // seg_first + n % seg_count of row n / seg_count, and N = B * seg_count.
+    // Value columns j >= dv_io are map columns: they start from the identity
+    // (column j holds e_{j - dv_io}), take z = 0 and write no output, so they
+    // carry the segment's state map.  Initial state of a segment: from
+    // seg_states_in ([B][seg_total][H][dk][dv_io]) if given, else the
+    // caller's initial_state for segment 0 and zero otherwise.  Final state:
+    // into seg_states_out ([B][seg_total][H][dk][dv], every column) if given,
+    // else the caller's final_state for the row's last segment.  o (dv_io
+    // columns) is written for every segment when seg_o_all, else for segment
+    // 0 only.
+    int32_t seg_len, seg_total, seg_first, seg_count, seg_o_all;
+    int32_t dv_io;  // columns of v, w, o and the caller's states (0: dv)
+    const float* seg_states_in;
+    float* seg_states_out;
 };
 
 struct StepArgs {
@@ -120,6 +137,12 @@ hipError_t launch_chunk_fwd_simple(const ChunkArgs& a, bool bf16, hipStream_t st
 // address on the current device (looked up once per device).
 constexpr size_t kScratchBytes = size_t(256) << 20;
 hipError_t scratch_pointer(void** out);
+
+// Segment combine (segments.hip): S_in(1) = S_out(0), S_in(p + 1) = M_p
+// S_in(p) + N_p for the layouts of ChunkArgs::seg_states_out (dv + dk
+// columns) and ::seg_states_in (dv columns).
+hipError_t launch_segment_combine(const float* seg_out, float* seg_in, int B, int H, int dk, int dv, int P,
+                                  hipStream_t stream);
 
 // Matrix-core chunk kernel: bf16 inputs, dk = 128, dv a multiple of 64.
 bool chunk_fwd_mfma_supported(const ChunkArgs& a, bool bf16);

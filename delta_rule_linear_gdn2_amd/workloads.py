@@ -66,6 +66,9 @@ WORKLOADS = {
     "varlen32_bf16": Workload("varlen32_bf16", 4, "varlen", "bf16", B=1, H=16, init_state=True,
                               num_seqs=32, min_len=256, max_len=8192,
                               gate_modes=("gdn2", "kda", "gdn")),
+    # one long row: the 16K x 1 end of the pages' training sweep (16 heads,
+    # 128 x 128 state); chunkwise, N(0, 0.1^2) initial state
+    "long16k_bf16": Workload("long16k_bf16", 5, "chunk", "bf16", B=1, T=16384, H=16, init_state=True),
 }
 
 

@@ -125,10 +125,26 @@ typedef enum gdn2_gate_flags {
  *                   a malformed array cannot make the kernel read or write
  *                   outside the tensors; it only gives meaningless results.
  *   T may be 0 (then only final_state = initial_state is written).
- *   workspace / workspace_bytes: device scratch of at least
- *                   gdn2_chunk_fwd_workspace_bytes(...) bytes (may be NULL when
- *                   that is 0).
+ *   workspace / workspace_bytes: NULL, or device scratch of at least
+ *                   gdn2_chunk_fwd_workspace_bytes(...) bytes, 16-byte aligned,
+ *                   contents on entry irrelevant.  With it, calls with few
+ *                   (sequence, head) chains run the segmented path below;
+ *                   with NULL they run the single pass.  Smaller than
+ *                   required: GDN2_ERR_WORKSPACE.  It must not overlap any
+ *                   argument (GDN2_ERR_ALIAS).
  * o must not overlap any input.
+ *
+ * Segmented path (bf16, dk = 128, dv a multiple of 64, no cu_seqlens, few
+ * chains).  The single pass runs one workgroup per (chain, 64 value
+ * columns), walking its chain chunk by chunk, so B x H x dv / 64 small
+ * leaves most of the GPU idle.  Each batch row is then cut into P segments
+ * of whole chunks.  Over a segment the state map is affine, S_out = M S_in +
+ * N (the same fact that carries the state from chunk to chunk), so: pass 1
+ * runs segments 0 .. P - 2 in parallel, each from a zero state (segment 0
+ * from initial_state) with dk extra columns that start from the identity and
+ * take no writes, giving N and M; a combine step forms the true incoming
+ * state of every later segment; pass 2 runs segments 1 .. P - 1 from those.
+ * The result is the same mathematics, rounded differently.
  */
 gdn2_status gdn2_chunk_fwd(const void* q, const void* k, const void* v,
                            const float* alpha, const void* b, const void* w,
@@ -152,7 +168,13 @@ gdn2_status gdn2_chunk_fwd_gates(const void* q, const void* k, const void* v,
                                  int32_t num_seqs, gdn2_dtype dtype, int32_t gates,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace needed by gdn2_chunk_fwd for these sizes (currently always 0). */
+/* Workspace for the segmented path of gdn2_chunk_fwd / _gates: 0 when that
+ * path does not apply to these sizes (then the call needs no workspace).
+ * num_seqs: the packed sequence count with cu_seqlens, else 0 (the
+ * segmented path takes no packed input; it needs T >= 1024).  P segments of
+ * L tokens (L a multiple of 64, at least 256; P at least 3 and small enough
+ * that pass 1 fills the device's compute units once) need B x P x H x dk x (dv + dk) +
+ * B x P x H x dk x dv FP32 values, each part rounded up to 256 bytes. */
 size_t gdn2_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
                                       int32_t num_seqs, gdn2_dtype dtype);
 

@@ -44,7 +44,19 @@ def test_status_strings(lib):
 
 
 def test_workspace_query(lib):
-    assert binding.gdn2_chunk_fwd_workspace_bytes(8, 4096, 16, 128, 128, 8, 1) == 0
+    # the segmented path: bf16, dk = 128, no packed input, few chains (plans for 256 compute units here)
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    seg = lambda B, P, H, dk, dv: al(B * P * H * dk * (dv + dk) * 4) + al(B * P * H * dk * dv * 4)  # noqa: E731
+    # B=1 H=16: 64 pass-1 workgroups per segment, 4 fit, P = 5 segments of 832 tokens
+    assert binding.gdn2_chunk_fwd_workspace_bytes(1, 4096, 16, 128, 128, 0, 1) == seg(1, 5, 16, 128, 128)
+    assert binding.gdn2_chunk_fwd_workspace_bytes(1, 16384, 16, 128, 128, 0, 1) == seg(1, 5, 16, 128, 128)
+    assert binding.gdn2_chunk_fwd_workspace_bytes(2, 4096, 16, 128, 128, 0, 1) == seg(2, 3, 16, 128, 128)
+    assert binding.gdn2_chunk_fwd_workspace_bytes(8, 4096, 16, 128, 128, 0, 1) == 0    # enough chains already
+    assert binding.gdn2_chunk_fwd_workspace_bytes(1, 4096, 16, 128, 128, 3, 1) == 0    # packed input
+    assert binding.gdn2_chunk_fwd_workspace_bytes(1, 4096, 16, 128, 128, 0, 0) == 0    # FP32
+    assert binding.gdn2_chunk_fwd_workspace_bytes(1, 4096, 16, 64, 64, 0, 1) == 0      # dk = 64
+    assert binding.gdn2_chunk_fwd_workspace_bytes(1, 1000, 16, 128, 128, 0, 1) == 0    # rows under 1024 tokens
+    assert binding.gdn2_chunk_fwd_workspace_bytes(1, 1024, 16, 128, 128, 0, 1) == seg(1, 4, 16, 128, 128)
 
 
 # Fake, well-separated, 256-byte aligned device addresses: validation must
@@ -101,6 +113,7 @@ def step_call(lib, **kw):
     (dict(sf=fake(3, 64)), ALIAS),                    # final state inside alpha
     (dict(sf=fake(8)), ALIAS),                        # final state == o
     (dict(sf=fake(6, 1024)), ALIAS),                  # partial overlap with initial state
+    (dict(ws=fake(10, 8)), MISAL),                    # workspace not 16-byte aligned
 ])
 def test_chunk_fwd_rejects(lib, kw, expected):
     assert chunk_call(lib, **kw) == expected
