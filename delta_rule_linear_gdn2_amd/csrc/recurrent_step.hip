@@ -16,11 +16,12 @@
 // One wavefront (a one-wave workgroup) owns one quarter: lane l holds the
 // four columns 4 (l & 7) .. + 3 of the rows g NP .. g NP + NP - 1, g = l >> 3,
 // NP = dk / 8, in VGPRs.  The column sums over dk are a register sum over the
-// lane's NP rows and three shuffle steps across the eight row groups: no
-// workgroup barrier and no cross-wave exchange, so a wavefront never waits
-// for another.  The token vectors go through the wave's own LDS (two buffers,
-// token parity); the next token's are loaded into registers while the current
-// one is computed.  The quarters of one head share blockIdx mod 8, hence one
+// lane's NP rows and three lane-exchange steps across the eight row groups
+// (on the vector ALU: a DPP rotate and two lane swaps): no workgroup barrier,
+// no LDS and no cross-wave exchange, so a wavefront never waits for another.
+// The token vectors go through the wave's own LDS (two buffers, token
+// parity); the next token's are loaded into registers while the current one
+// is computed.  The quarters of one head share blockIdx mod 8, hence one
 // XCD, so the token vectors that every quarter reads come from that XCD's L2.
 //
 // The state is streamed: the loads carry the non-temporal hint and the stores
@@ -102,6 +103,40 @@ __device__ __forceinline__ void load_token(TokenRegs<DK>& x, const StepArgs& a, 
     }
 }
 
+// Cross-lane sums on the vector ALU (no LDS traffic): every lane receives x
+// plus the value of lane ^ 8 (DPP rotate by 8 inside each row of 16 lanes),
+// lane ^ 16 and lane ^ 32.  A lane-swap instruction given the same register
+// twice returns the two halves exchanged; their sum is the pairwise sum in
+// every lane.
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128;
+__device__ __forceinline__ float sum_xor8(float x) { return x + dpp_row<kRowRor8>(x); }
+__device__ __forceinline__ float sum_xor16(float x)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+// Sum over the whole wavefront, in every lane.
+__device__ __forceinline__ float wave_sum(float x)
+{
+    x += dpp_row<kRowRor8>(x);
+    x += dpp_row<kRowRor4>(x);
+    x += dpp_row<kRowRor2>(x);
+    x += dpp_row<kRowRor1>(x);
+    return sum_xor32(sum_xor16(x));
+}
+// Sum over the eight row groups (lanes 8 apart), in every lane.
+__device__ __forceinline__ float rowgroup_sum(float x) { return sum_xor32(sum_xor16(sum_xor8(x))); }
+
 // The wave's own LDS writes are complete (it is the only wave of its
 // workgroup, so no s_barrier); global loads stay in flight.
 __device__ __forceinline__ void wave_lds_fence()
@@ -160,8 +195,7 @@ __global__ __launch_bounds__(64) void recurrent_kernel(StepArgs a)
         }
         if (lane < kCols) s_z[buf][lane] = x.w * x.v;
         if (t + 1 < a.T) load_token<T, DK, DV>(x, a, row + a.H, col0, lane);  // in flight during this token
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) kq += __shfl_xor(kq, off, 64);
+        kq = wave_sum(kq);
         wave_lds_fence();
 
         float4 r = make_float4(0.f, 0.f, 0.f, 0.f), s = r;
@@ -178,13 +212,8 @@ __global__ __launch_bounds__(64) void recurrent_kernel(StepArgs a)
             }
         }
         // sum over the eight row groups (lanes 8 apart)
-#pragma unroll
-        for (int off = 8; off < 64; off <<= 1) {
-            r.x += __shfl_xor(r.x, off, 64); r.y += __shfl_xor(r.y, off, 64);
-            r.z += __shfl_xor(r.z, off, 64); r.w += __shfl_xor(r.w, off, 64);
-            s.x += __shfl_xor(s.x, off, 64); s.y += __shfl_xor(s.y, off, 64);
-            s.z += __shfl_xor(s.z, off, 64); s.w += __shfl_xor(s.w, off, 64);
-        }
+        r = make_float4(rowgroup_sum(r.x), rowgroup_sum(r.y), rowgroup_sum(r.z), rowgroup_sum(r.w));
+        s = make_float4(rowgroup_sum(s.x), rowgroup_sum(s.y), rowgroup_sum(s.z), rowgroup_sum(s.w));
         const float4 z = *reinterpret_cast<const float4*>(&s_z[buf][4 * col4]);
         const float4 u = make_float4(z.x - r.x, z.y - r.y, z.z - r.z, z.w - r.w);
         if (g == 0)
