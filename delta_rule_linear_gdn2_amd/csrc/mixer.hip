@@ -337,17 +337,25 @@ __device__ __forceinline__ void load8(const float* p, int64_t i, float* v)
     const float4 a = *reinterpret_cast<const float4*>(p + i), b = *reinterpret_cast<const float4*>(p + i + 4);
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
+// Outputs are written once and not read again by the writing kernel, so the
+// stores are streaming (nontemporal): on MI355X this took the epilogue from 75
+// to 60 us and the prologue from 318 to 311 us on B=8, T=4096, H=16, d=128.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void store8(bf16raw* p, int64_t i, const float* v)
 {
-    uint32_t w[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = f32x2_to_bf16x2(v[2 * j], v[2 * j + 1]);
-    *reinterpret_cast<uint4*>(p + i) = make_uint4(w[0], w[1], w[2], w[3]);
+    u32x4 w;
+    w.x = f32x2_to_bf16x2(v[0], v[1]);
+    w.y = f32x2_to_bf16x2(v[2], v[3]);
+    w.z = f32x2_to_bf16x2(v[4], v[5]);
+    w.w = f32x2_to_bf16x2(v[6], v[7]);
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p + i));
 }
 __device__ __forceinline__ void store8(float* p, int64_t i, const float* v)
 {
-    *reinterpret_cast<float4*>(p + i) = make_float4(v[0], v[1], v[2], v[3]);
-    *reinterpret_cast<float4*>(p + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    const f32x4 a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
+    __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(p + i));
+    __builtin_nontemporal_store(b, reinterpret_cast<f32x4*>(p + i + 4));
 }
 
 // ---------------------------------------------------------------------------
