@@ -77,10 +77,11 @@ def bwd_bytes(B, T, H, dk, dv, N, eb=2):
 
 
 def bwd_flops(lengths, H, dk, dv, C=32):
-    """FLOPs of the chunkwise backward as built (32-token chunks), summed over
-    chunks: the forward recompute (X, U = Tm X, the state update), the reverse
-    pass (X, U, dU, dX, the state-gradient update), the key-side products
-    (dA, dP, dEt, dQt, dKb) and the per-chunk algebra (A, P, Tm, pairwise)."""
+    """FLOPs of the chunkwise backward at C-token chunks (32 on the FP32 path,
+    64 on the matrix-core path), summed over chunks: the forward recompute
+    (X, U = Tm X, the state update), the reverse pass (dU, dX, the
+    state-gradient update), the key-side products (dA, dP, dEt, dQt, dKb) and
+    the per-chunk algebra (A, P, Tm, pairwise)."""
     total = 0
     for n in lengths:
         full, tail = divmod(int(n), C)
@@ -359,11 +360,15 @@ def bench_bwd(args):
 
     per, _, _ = time_events(call, args.warmup, args.steps)
     ms = float(np.median(per))
+    # 0: the bf16 matrix-core path ran; 1: a chunk was out of its range and the FP32 path ran
+    path = "bf16 matrix-core" if int(ws[:4].view(torch.int32).item()) == 0 else "FP32 (range fallback)"
     nbytes = bwd_bytes(B, T, H, dk, dv, B)
-    flops = bwd_flops([T] * B, H, dk, dv)
-    log(f"backward: {ms:.2f} ms per call, {B * T / (ms / 1e3) / 1e6:.2f} M tokens/s, "
-        f"{flops / (ms / 1e3) / 1e12:.1f} TFLOP/s FP32")
-    return dict(x=x, wl=wl, ms=ms, bytes=nbytes, flops=flops, ws_bytes=ws.numel())
+    flops = bwd_flops([T] * B, H, dk, dv, C=64 if path.startswith("bf16") else 32)
+    peak = MFMA_BF16_PEAK_TFLOPS if path.startswith("bf16") else MFMA_FP32_PEAK_TFLOPS
+    log(f"backward ({path} path): {ms:.2f} ms per call, {B * T / (ms / 1e3) / 1e6:.2f} M tokens/s, "
+        f"{flops / (ms / 1e3) / 1e12:.1f} TFLOP/s ({flops / (ms / 1e3) / 1e12 / peak * 100:.1f}% of the "
+        f"{peak:.0f} TFLOP/s matrix peak), {nbytes / (ms / 1e3) / 1e9:.0f} GB/s of algorithmic bytes")
+    return dict(x=x, wl=wl, ms=ms, bytes=nbytes, flops=flops, ws_bytes=ws.numel(), path=path, peak=peak)
 
 
 def bench_mixer(args):
@@ -565,9 +570,10 @@ def run_configs(args):
                       "ms_per_call": bw["ms"], "tokens_per_s": wlb.B * wlb.T / (bw["ms"] / 1e3),
                       "GBps": bw["bytes"] / (bw["ms"] / 1e3) / 1e9,
                       "hbm_frac": bw["bytes"] / (bw["ms"] / 1e3) / 1e9 / HBM_PEAK_GBPS,
+                      "path": bw["path"],
                       "TFLOPs": bw["flops"] / (bw["ms"] / 1e3) / 1e12,
-                      "fp32_alu_frac": bw["flops"] / (bw["ms"] / 1e3) / 1e12 / FP32_VALU_TFLOPS,
-                      "fp32_mfma_frac": bw["flops"] / (bw["ms"] / 1e3) / 1e12 / MFMA_FP32_PEAK_TFLOPS,
+                      "mfma_frac": bw["flops"] / (bw["ms"] / 1e3) / 1e12 / bw["peak"],
+                      "mfma_peak_TFLOPs": bw["peak"],
                       "workspace_bytes": bw["ws_bytes"],
                       "oracle_one_core": {"value": 1024 / one_bwd, "unit": "token-heads/s",
                                           "sample": f"1 sequence x 1 head x 1024 tokens, {one_bwd:.2f} s"}}),

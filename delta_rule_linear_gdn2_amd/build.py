@@ -24,6 +24,7 @@ SOURCES = [
     "chunk_fwd_simple.hip",
     "chunk_fwd_mfma.hip",
     "chunk_bwd.hip",
+    "chunk_bwd_mfma.hip",
     "mixer.hip",
     "scratch.hip",
     "segments.hip",

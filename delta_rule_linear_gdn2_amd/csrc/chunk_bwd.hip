@@ -186,6 +186,7 @@ struct ChunkRows {
 template <typename T, int DK>
 __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdArgs a)
 {
+    if (a.gate && *a.gate == 0) return;  // the matrix-core path covers this call
     __shared__ ChunkRows<DK> c;
     __shared__ float Tm[CH][CH + 1];
     __shared__ float glv[DK];  // G at the chunk's last token
@@ -403,6 +404,7 @@ struct PrepRegs {
 template <typename T, int DK>
 __global__ __launch_bounds__(kSeqThreads) void bwd_states_kernel(BwdArgs a)
 {
+    if (a.gate && *a.gate == 0) return;  // the matrix-core path covers this call
     constexpr int NTS = (DK / 16) * (kTile / 16);  // 16 x 16 blocks of the state tile
     constexpr int TPW = (NTS + 7) / 8;             // per wavefront
     __shared__ float Et[CH][DK + kPad], Kb[CH][DK + kPad];
@@ -530,6 +532,7 @@ __global__ __launch_bounds__(kSeqThreads) void bwd_states_kernel(BwdArgs a)
 template <typename T, int DK>
 __global__ __launch_bounds__(kSeqThreads, 4) void bwd_dstate_kernel(BwdArgs a)
 {
+    if (a.gate && *a.gate == 0) return;  // the matrix-core path covers this call
     constexpr int NTS = (DK / 16) * (kTile / 16);
     constexpr int TPW = (NTS + 7) / 8;
     __shared__ float Et[CH][DK + kPad], Qt[CH][DK + kPad], Kb[CH][DK + kPad];
@@ -713,6 +716,7 @@ constexpr int keys_cb() { return DK >= 64 && DV >= 64 ? 64 : 32; }
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__((8 * keys_cb<DK, DV>())) void bwd_keys_kernel(BwdArgs a)
 {
+    if (a.gate && *a.gate == 0) return;  // the matrix-core path covers this call
     constexpr int CB = keys_cb<DK, DV>(); // channels per block
     constexpr int NT = 8 * CB;            // threads: CB / 8 wavefronts
     constexpr int DH = 32;                // value columns per pass

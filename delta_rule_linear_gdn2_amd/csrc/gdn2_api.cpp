@@ -4,6 +4,7 @@
 // errors come back synchronously and never reach the device.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdint>
 
@@ -330,16 +331,22 @@ gdn2_status mixer_epilogue(const void* o, const void* gate, const float* weight,
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 
-// Workspace regions of the backward pass: chunk-start states, chunk-end
-// state gradients (slots x H x dk x dv FP32 each, per batch row), U and dX
-// rows (B x T x H x dv FP32 each) and each chunk's prepared triangular
-// algebra (slots x H per batch row), each region 256-byte aligned.
+// Workspace regions of the backward pass.  FP32 path: chunk-start states,
+// chunk-end state gradients (slots x H x dk x dv FP32 each, per batch row), U
+// and dX rows (B x T x H x dv FP32 each) and each chunk's prepared triangular
+// algebra (slots x H per batch row), each region 256-byte aligned.  The
+// matrix-core path (bf16, dk = dv = 128, T > 0) puts its range flag in the
+// first 256 bytes; after it, its own regions (bf16 states and state gradients
+// per 64-token slot, bf16 U and dX rows per slot) and the FP32 path's, which
+// runs instead when the flag is raised, share the same memory.
 struct BwdWorkspace {
-    int64_t slots;
-    size_t states, rows, prep, total;
+    int64_t slots, slots64;
+    size_t states, rows, prep, states16, rows16, total;
+    bool mfma;
 };
 
-BwdWorkspace bwd_workspace(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv, bool varlen, int32_t N)
+BwdWorkspace bwd_workspace(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv, bool varlen, int32_t N,
+                           gdn2_dtype dtype)
 {
     BwdWorkspace w;
     w.slots = T == 0 ? 0 : (int64_t(T) + gdn2::kBwdChunk - 1) / gdn2::kBwdChunk + (varlen ? N : 0);
@@ -347,6 +354,11 @@ BwdWorkspace bwd_workspace(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t 
     w.rows = align256(size_t(B) * size_t(T) * size_t(H) * size_t(dv) * 4);
     w.prep = align256(size_t(B) * size_t(w.slots) * size_t(H) * size_t(gdn2::chunk_bwd_prep_floats(dk)) * 4);
     w.total = 2 * w.states + 2 * w.rows + w.prep;
+    w.mfma = T > 0 && gdn2::chunk_bwd_mfma_shape(dtype == GDN2_DTYPE_BF16, dk, dv);
+    w.slots64 = T == 0 ? 0 : (int64_t(T) + 63) / 64 + (varlen ? N : 0);
+    w.states16 = align256(size_t(B) * size_t(w.slots64) * size_t(H) * size_t(dk) * size_t(dv) * 2);
+    w.rows16 = align256(size_t(B) * size_t(w.slots64) * size_t(H) * 64 * size_t(dv) * 2);
+    if (w.mfma) w.total = 256 + std::max(w.total, 2 * w.states16 + 2 * w.rows16);
     return w;
 }
 
@@ -378,7 +390,7 @@ gdn2_status chunk_bwd_check(const void* q, const void* k, const void* v, const f
         if (p && !aligned16(p)) return GDN2_ERR_MISALIGNED;
     if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return GDN2_ERR_MISALIGNED;
 
-    ws = bwd_workspace(B, T, H, dk, dv, cu_seqlens != nullptr, N);
+    ws = bwd_workspace(B, T, H, dk, dv, cu_seqlens != nullptr, N, dtype);
     if (!own_workspace && ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return GDN2_ERR_WORKSPACE;
 
     const int64_t tokens = int64_t(B) * T * H;
@@ -423,12 +435,22 @@ gdn2_status chunk_bwd_launch(const void* q, const void* k, const void* v, const 
     a.B = B; a.T = T; a.H = H; a.dk_ = dk; a.dv_ = dv; a.N = N;
     a.slots = ws.slots;
     unsigned char* base = static_cast<unsigned char*>(workspace);
+    if (ws.mfma) {
+        a.range_flag = reinterpret_cast<int32_t*>(base);
+        base += 256;
+        a.slots64 = ws.slots64;
+        a.ws_s16 = reinterpret_cast<uint16_t*>(base);
+        a.ws_ds16 = reinterpret_cast<uint16_t*>(base + ws.states16);
+        a.ws_u16 = reinterpret_cast<uint16_t*>(base + 2 * ws.states16);
+        a.ws_dx16 = reinterpret_cast<uint16_t*>(base + 2 * ws.states16 + ws.rows16);
+    }
     a.ws_states = ws.total ? reinterpret_cast<float*>(base) : nullptr;
     a.ws_dstates = ws.total ? reinterpret_cast<float*>(base + ws.states) : nullptr;
     a.ws_u = ws.total ? reinterpret_cast<float*>(base + 2 * ws.states) : nullptr;
     a.ws_dx = ws.total ? reinterpret_cast<float*>(base + 2 * ws.states + ws.rows) : nullptr;
     a.ws_prep = ws.total ? reinterpret_cast<float*>(base + 2 * ws.states + 2 * ws.rows) : nullptr;
-    const hipError_t e = gdn2::launch_chunk_bwd(a, dtype == GDN2_DTYPE_BF16, static_cast<hipStream_t>(stream));
+    const hipError_t e = ws.mfma ? gdn2::launch_chunk_bwd_mfma(a, static_cast<hipStream_t>(stream))
+                                 : gdn2::launch_chunk_bwd(a, dtype == GDN2_DTYPE_BF16, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 
@@ -547,7 +569,7 @@ size_t gdn2_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t d
 {
     (void)dtype;
     if (B <= 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return 0;
-    return bwd_workspace(B, T, H, dk, dv, num_seqs > 0, num_seqs).total;
+    return bwd_workspace(B, T, H, dk, dv, num_seqs > 0, num_seqs, dtype).total;
 }
 
 gdn2_status gdn2_mixer_prologue(const void* xq, const void* xk, const void* xv, const float* conv_q,

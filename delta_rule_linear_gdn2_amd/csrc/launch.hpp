@@ -87,7 +87,20 @@ struct BwdArgs {
     float* ws_u;         // [B * T * H][dv] U rows
     float* ws_dx;        // [B * T * H][dv] dX rows
     float* ws_prep;      // [B][slots][H][chunk_bwd_prep_floats(dk)] per-chunk triangular algebra
+    // The matrix-core path (bf16, dk = dv = 128, 64-token chunks), whose
+    // workspace shares the memory above:
+    int64_t slots64;     // 64-token chunk slots per batch row
+    uint16_t* ws_s16;     // [B][slots64][H][dk][dv] state at each chunk start
+    uint16_t* ws_ds16;    // [B][slots64][H][dk][dv] gradient of the state at each chunk end
+    uint16_t* ws_u16;     // [B][slots64][H][64][dv] U rows of each chunk
+    uint16_t* ws_dx16;    // [B][slots64][H][64][dv] dX rows of each chunk
+    int32_t* range_flag; // set when some chunk decays below the split range: the FP32 path then runs
+    const int32_t* gate; // FP32 path kernels do nothing when this is set and *gate == 0
 };
+
+// Whether a backward call takes the matrix-core path.
+inline bool chunk_bwd_mfma_shape(bool bf16, int dk, int dv) { return bf16 && dk == 128 && dv == 128; }
+hipError_t launch_chunk_bwd_mfma(const BwdArgs& a, hipStream_t stream);
 
 // Floats of one chunk's prepared block in ws_prep.
 int64_t chunk_bwd_prep_floats(int dk);

@@ -235,9 +235,21 @@ gdn2_status gdn2_recurrent_fwd(const void* q, const void* k, const void* v,
  * for the loss <d_o, o> + <d_final_state, final_state>, accumulated through
  * the gated keys and values with the channel-wise decay inside the sums
  * ("Token processing and parallel training": the backward pass cannot pull
- * the channel-wise factors out as it could a scalar beta).  FP32 arithmetic;
- * alpha is clamped to [2^-15, 1] as in the forward pass, and dalpha is zero
- * where the clamp is active.
+ * the channel-wise factors out as it could a scalar beta).  alpha is clamped
+ * to [2^-15, 1] as in the forward pass, and dalpha is zero where the clamp is
+ * active.
+ *
+ * Two paths.  bf16 inputs with dk = dv = 128 (T > 0) take the matrix-core
+ * path: 64-token chunks, bf16 products with FP32 accumulation, FP32 decay,
+ * states and state gradients (stored in bf16 between its kernels).  It needs
+ * every key channel to decay by at least 2^-64 over every 64-token chunk
+ * (the split of the pairwise decay factors stays in range); when some chunk
+ * decays faster, the FP32 path below runs instead, on the same workspace,
+ * decided on the device without a host round trip.  All other calls take the
+ * FP32 path: 32-token chunks, FP32 arithmetic throughout, exact pairwise
+ * factors where the split would leave the FP32 range.  After a matrix-core
+ * shaped call the first int32 of the workspace is 0 when the matrix-core path
+ * produced the results and 1 when the FP32 path did.
  *
  *   q, k, v, alpha, b, w, initial_state, cu_seqlens, B, T, H, dk, dv,
  *   num_seqs, dtype: the forward call's arguments (initial_state may be NULL).
@@ -263,11 +275,14 @@ gdn2_status gdn2_chunk_bwd(const void* q, const void* k, const void* v,
                            int32_t num_seqs, gdn2_dtype dtype,
                            void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace needed by gdn2_chunk_bwd.  With C = B x (ceil(T / 32) + num_seqs)
- * x H chunk slots: 2 x C x dk x dv x 4 bytes of states, 2 x B x T x H x dv x 4
- * bytes of rows and C x (2048 + 97 dk) x 4 bytes of per-chunk triangular
- * algebra, each rounded up to 256 bytes (0 when T = 0).  Returns 0 for
- * invalid sizes. */
+/* Workspace needed by gdn2_chunk_bwd.  FP32 path, with C = B x (ceil(T / 32)
+ * + num_seqs) x H chunk slots: 2 x C x dk x dv x 4 bytes of states,
+ * 2 x B x T x H x dv x 4 bytes of rows and C x (2048 + 97 dk) x 4 bytes of
+ * per-chunk triangular algebra, each rounded up to 256 bytes (0 when T = 0).
+ * Matrix-core shaped calls (bf16, dk = dv = 128, T > 0): 256 bytes more than
+ * the larger of that and, with C64 = B x (ceil(T / 64) + num_seqs) x H,
+ * 2 x C64 x 128 x 128 x 2 bytes of states plus 2 x C64 x 64 x 128 x 2 bytes of
+ * rows (each rounded up to 256 bytes).  Returns 0 for invalid sizes. */
 size_t gdn2_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t dk_size, int32_t dv_size,
                                       int32_t num_seqs, gdn2_dtype dtype);
 

@@ -244,9 +244,20 @@ def _bwd_ws(B, T, H, dk, dv, slots):
     return (2 * al(B * slots * H * dk * dv * 4) + 2 * al(B * T * H * dv * 4) + al(B * slots * H * prep * 4))
 
 
+def _bwd_ws_mfma(B, T, H, slots, slots64):
+    # the range flag, then the larger of the FP32 path's regions and the
+    # matrix-core path's bf16 states, state gradients, U and dX rows per 64-token slot
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    own = 2 * al(B * slots64 * H * 128 * 128 * 2) + 2 * al(B * slots64 * H * 64 * 128 * 2)
+    return 256 + max(_bwd_ws(B, T, H, 128, 128, slots), own)
+
+
 def test_bwd_workspace_query(lib):
     # states and state gradients per chunk slot, U and dX rows, prepared chunk algebra
-    assert binding.gdn2_chunk_bwd_workspace_bytes(8, 4096, 16, 128, 128, 0, 1) == _bwd_ws(8, 4096, 16, 128, 128, 128)
+    assert binding.gdn2_chunk_bwd_workspace_bytes(8, 4096, 16, 128, 128, 0, 0) == _bwd_ws(8, 4096, 16, 128, 128, 128)
+    assert binding.gdn2_chunk_bwd_workspace_bytes(8, 4096, 16, 128, 128, 0, 1) == _bwd_ws_mfma(8, 4096, 16, 128, 64)
+    assert binding.gdn2_chunk_bwd_workspace_bytes(1, 300, 2, 128, 128, 3, 1) == _bwd_ws_mfma(1, 300, 2, 10 + 3, 5 + 3)
+    assert binding.gdn2_chunk_bwd_workspace_bytes(1, 300, 2, 128, 64, 3, 1) == _bwd_ws(1, 300, 2, 128, 64, 10 + 3)
     assert binding.gdn2_chunk_bwd_workspace_bytes(1, 0, 4, 64, 64, 3, 1) == 0
     assert binding.gdn2_chunk_bwd_workspace_bytes(1, 100, 2, 32, 32, 3, 0) == _bwd_ws(1, 100, 2, 32, 32, 4 + 3)
     assert binding.gdn2_chunk_bwd_workspace_bytes(0, 100, 2, 32, 32, 0, 0) == 0

@@ -3,7 +3,9 @@ FP64 oracle's reverse-mode gradients O5 (needs an MI355X).
 
 Bar: relative L2 error of each gradient tensor (dq, dk, dv, dalpha, db, dw,
 dS0), at most 1e-4 for FP32 inputs and 1e-2 for bf16 inputs, the same bar as
-the forward pass.  The seeds d_o and d_final_state are N(0, 1), rounded to the
+the forward pass.  bf16 inputs with dk = dv = 128 take the matrix-core path
+(bf16 products); the tests read which path ran from the workspace's first
+int32 (0: matrix-core path, 1: the FP32 path after the range check).  The seeds d_o and d_final_state are N(0, 1), rounded to the
 input dtype, and the oracle sees exactly the values the kernels see."""
 import numpy as np
 import pytest
@@ -43,11 +45,18 @@ def gpu_bwd(x, dtype, g, gs, **kw):
     import torch
 
     d = G.to_dev(x, dtype)
+    if kw.pop("want_path", False):
+        B, T, H, dk = x["q"].shape
+        N = 0 if x.get("cu_seqlens") is None else len(x["cu_seqlens"]) - 1
+        n = binding.gdn2_chunk_bwd_workspace_bytes(B, T, H, dk, x["v"].shape[-1], N, 1 if dtype == "bf16" else 0)
+        kw["workspace"] = torch.empty(n, dtype=torch.uint8, device="cuda")
     dg = W.to_torch(g, dtype, "cuda")
     dgs = None if gs is None else torch.from_numpy(gs).cuda()
     out = binding.gdn2_chunk_bwd(d["q"], d["k"], d["v"], d["alpha"], d["b"], d["w"], dg, d["initial_state"], dgs,
                                  cu_seqlens=d["cu_seqlens"], **kw)
     torch.cuda.synchronize()
+    if "workspace" in kw:
+        out["path_flag"] = int(kw["workspace"][:4].view(torch.int32).item())
     return out
 
 
@@ -69,7 +78,10 @@ def test_backward_shapes(dtype, dk, dv):
     """B=2, T=100 (three 32-token chunks and a ragged 4), H=3, random initial state and seeds."""
     x = W.make("batched_bf16", seed=201, B=2, T=100, H=3, dk=dk, dv=dv, dtype=dtype)
     g, gs = _seeds(x, dtype, 202)
-    _compare(gpu_bwd(x, dtype, g, gs), oracle_bwd(x, g, gs), dtype, f"bwd {dtype} dk={dk} dv={dv}")
+    out = gpu_bwd(x, dtype, g, gs, want_path=True)
+    _compare(out, oracle_bwd(x, g, gs), dtype, f"bwd {dtype} dk={dk} dv={dv}")
+    if dtype == "bf16" and dk == dv == 128:
+        assert out["path_flag"] == 0, "the matrix-core path must produce these results"
 
 
 @pytest.mark.parametrize("dtype,d", [("f32", 64), ("f32", 128), ("bf16", 128)])
@@ -84,7 +96,10 @@ def test_backward_strong_decay(dtype, d):
     strong = rng.uniform(0.05, 0.2, x["alpha"][..., : d // 2].shape).astype(np.float32)
     x["alpha"] = np.ascontiguousarray(np.concatenate([strong, x["alpha"][..., d // 2:]], axis=-1))
     g, gs = _seeds(x, dtype, 208)
-    _compare(gpu_bwd(x, dtype, g, gs), oracle_bwd(x, g, gs), dtype, f"bwd strong decay {dtype} d={d}")
+    out = gpu_bwd(x, dtype, g, gs, want_path=True)
+    _compare(out, oracle_bwd(x, g, gs), dtype, f"bwd strong decay {dtype} d={d}")
+    if dtype == "bf16" and d == 128:
+        assert out["path_flag"] == 1, "strong decay must fall back to the FP32 path"
 
 
 @pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
@@ -155,6 +170,42 @@ def test_backward_batched_bf16():
     gradient over all 128 chains."""
     x = W.make("batched_bf16")
     g, gs = _seeds(x, "bf16", 214)
-    out = gpu_bwd(x, "bf16", g, gs)
+    out = gpu_bwd(x, "bf16", g, gs, want_path=True)
+    assert out["path_flag"] == 0, "the matrix-core path must produce these results"
     ref = oracle_bwd(x, g, gs)
     _compare(out, ref, "bf16", "batched bwd")
+
+
+@pytest.mark.parametrize("case", ["ragged", "no_decay", "slow_decay", "erase_0_2", "one_steep_chunk"])
+def test_backward_matrix_core_cases(case):
+    """The matrix-core path (bf16, d = 128) over several 64-token chunks and a
+    ragged tail (B=2, T=300, H=2): the workload's gates; alpha = 1 (state
+    carried unchanged); slow decay sigmoid(N(6, 0.5)); erase gate widened to
+    [0, 2]; and one channel of one head decaying by 2^-2 per token over tokens
+    130..200 only: that chunk spans 2^-128, so the whole call falls back to the
+    FP32 path, which must give the same bar."""
+    x = W.make("batched_bf16", seed=215, B=2, T=300, H=2)
+    rng = np.random.default_rng(216)
+    if case == "no_decay":
+        x["alpha"][:] = 1.0
+    elif case == "slow_decay":
+        x["alpha"][:] = (1.0 / (1.0 + np.exp(-rng.normal(6.0, 0.5, x["alpha"].shape)))).astype(np.float32)
+    elif case == "erase_0_2":
+        x["b"] = W.round_bf16(2.0 * x["b"])
+    elif case == "one_steep_chunk":
+        x["alpha"][1, 130:200, 1, 17] = 0.25
+    g, gs = _seeds(x, "bf16", 217)
+    out = gpu_bwd(x, "bf16", g, gs, want_path=True)
+    assert out["path_flag"] == (1 if case == "one_steep_chunk" else 0), out["path_flag"]
+    _compare(out, oracle_bwd(x, g, gs), "bf16", f"bwd matrix-core {case}")
+
+
+def test_backward_matrix_core_long_horizon():
+    """B=1, H=4, T=4096 with alpha = 1: the state gradient carried over 64
+    chunks, every chain compared whole."""
+    x = W.make("batched_bf16", seed=218, B=1, T=4096, H=4)
+    x["alpha"][:] = 1.0
+    g, gs = _seeds(x, "bf16", 219)
+    out = gpu_bwd(x, "bf16", g, gs, want_path=True)
+    assert out["path_flag"] == 0
+    _compare(out, oracle_bwd(x, g, gs), "bf16", "bwd matrix-core long horizon")
