@@ -178,6 +178,23 @@ __device__ __forceinline__ float wave_scan(float x, int lane)
     return x + ((rw >= 1 ? t0 : 0.f) + (rw >= 2 ? t1 : 0.f) + (rw >= 3 ? t2 : 0.f));
 }
 
+// Inclusive suffix sum over the 64 lanes (lane l gets the sum over lanes >= l).
+template <int N>
+__device__ __forceinline__ float row_shl(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x100 + N, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float wave_rscan(float x, int lane)
+{
+    x += row_shl<1>(x);
+    x += row_shl<2>(x);
+    x += row_shl<4>(x);
+    x += row_shl<8>(x);
+    const float t1 = readlane_f(x, 16), t2 = readlane_f(x, 32), t3 = readlane_f(x, 48);
+    const int rw = lane >> 4;
+    return x + ((rw <= 2 ? t3 : 0.f) + (rw <= 1 ? t2 : 0.f) + (rw <= 0 ? t1 : 0.f));
+}
+
 // XCD-aware block order: the two value tiles of a chain get the same blockIdx
 // mod 8, so they run on one XCD and share its L2.
 __device__ __forceinline__ void xcd_pair(int64_t bid, int64_t& group, int& member)
@@ -247,24 +264,43 @@ __device__ __forceinline__ bool decay_scan(const KeyIn<NC>& x, int lane, float* 
     return ok;
 }
 
-// T = (I + Ad)^-1 for a strictly lower 16 x 16 block Ad (FP32, at ad), by
-// forward substitution, column j = lane % 16 in the lane's registers; lanes
-// 0..15 write T.
-__device__ __forceinline__ void diag_inverse(unsigned char* lds, int ad, int t, int lane)
+// T = (I + L)^-1 for a strictly lower 16 x 16 FP32 block L on the FP32
+// matrix cores: L is nilpotent (L^16 = 0), so
+//     (I + L)^-1 = (I - L)(I + L^2)(I + L^4)(I + L^8).
+// An accumulator block holding a matrix P (lane rows 4g..4g+3, column r)
+// serves as the A operand of P^T (K index 4g + s in step s) and as the B
+// operand of P, so mm(P, Q) = P^T Q needs no data movement; the chain keeps L
+// and L^T (both read from the block's FP32 copy at ad, rows padded) and works
+// on T^T.  Each product reads accumulators of the one before: the explicit
+// wait covers that on gfx950.  Lanes write T (rows i, columns j) at t.
+__device__ __forceinline__ f32x4 mm(f32x4 p, f32x4 q)
 {
-    const int j = lane & 15;
-    float x[16];
+    mfma_src_wait(p);
+    mfma_src_wait(q);
+    f32x4 d = zero4();
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        float s = (i == j) ? 1.f : 0.f;
+    for (int s = 0; s < 4; ++s) d = mma4(p[s], q[s], d);
+    return d;
+}
+__device__ __forceinline__ void diag_inverse(unsigned char* lds, int ad, int t, int g, int r)
+{
+    f32x4 L, LT;
 #pragma unroll
-        for (int k = 0; k < i; ++k) s -= ldsr<float>(lds, ad + (i * kTRow + k) * 4) * x[k];
-        x[i] = s;
+    for (int e = 0; e < 4; ++e) {
+        L[e] = ldsr<float>(lds, ad + ((4 * g + e) * kTRow + r) * 4);   // L[4g + e][r]
+        LT[e] = ldsr<float>(lds, ad + (r * kTRow + 4 * g + e) * 4);   // L^T[4g + e][r]
     }
-    if (lane < 16) {
+    const f32x4 L2 = mm(LT, L), L2T = mm(L, LT);
+    const f32x4 L4 = mm(L2T, L2), L4T = mm(L2, L2T);
+    const f32x4 L8 = mm(L4T, L4);
+    f32x4 M = -LT;  // (I - L)^T
 #pragma unroll
-        for (int i = 0; i < 16; ++i) ldsw<float>(lds, t + (i * kTRow + j) * 4, x[i]);
-    }
+    for (int e = 0; e < 4; ++e) M[e] += (4 * g + e == r) ? 1.f : 0.f;
+    M += mm(L2, M);
+    M += mm(L4, M);
+    M += mm(L8, M);  // T^T: lane holds T[r][4g + e]
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ldsw<float>(lds, t + (r * kTRow + 4 * g + e) * 4, M[e]);
 }
 
 // Stage an accumulator tile set (NB blocks of 16 rows x 16 columns, lane rows
@@ -297,8 +333,8 @@ constexpr int kF_KBT = 49152;                // [128][64] bf16 Kb^T
 constexpr int kF_AN = 65536;                 // [64][64] bf16 -A (rows i), blocks below the diagonal
 constexpr int kF_T = 73728;                  // [4] FP32 blocks T_m = (I + A_mm)^-1
 constexpr int kF_AD = kF_T + 4 * kTBlk;      // [4] FP32 blocks A_mm (preparation)
-constexpr int kF_GL = kF_AD + 4 * kTBlk;     // [128] f32 2^G_L
-constexpr int kF_Z = kF_GL + 512;            // [4 value waves][16 columns][64 tokens] f32, z = w v
+constexpr int kF_GL = kF_AD + 4 * kTBlk;     // [2][128] f32 2^G_L (chunk in work, chunk in preparation)
+constexpr int kF_Z = kF_GL + 1024;           // [4 value waves][16 columns][64 tokens] f32, z = w v
 constexpr int kF_STG = kF_Z + 4 * 4096;      // [4 value waves][128][48 B] staging
 constexpr int kF_Bytes = kF_STG + 4 * 128 * 48;
 static_assert(kF_Bytes <= 160 * 1024, "LDS budget");
@@ -313,7 +349,6 @@ __device__ __forceinline__ int zoff(int col, int tok)
 struct FPrep {
     KeyIn<32> in;
     uint32_t kb[16];  // Kb of the lane's token, 32 channels, bf16 pairs
-    float gl[32];
 };
 
 __global__ __launch_bounds__(kThreads) void bwd_fstate_kernel(BwdArgs a)
@@ -374,7 +409,6 @@ __global__ __launch_bounds__(kThreads) void bwd_fstate_kernel(BwdArgs a)
                     ldsw<float>(lds, zw + zoff(2 * j + 1, lane), hi_f(vv[j]) * hi_f(ww[j]));
                 }
             }
-            if (c + 1 < nch) load_z(c + 1);
             const int64_t tl = tile64(a, n, bos, c);
             // the chunk-start state, bf16, [dk][dv]
             stage_store<8>(lds, stg, S, g, r, lane, a.ws_s16 + (tl * a.H + h) * kD * kD + col0, kD);
@@ -408,13 +442,14 @@ __global__ __launch_bounds__(kThreads) void bwd_fstate_kernel(BwdArgs a)
                 for (int s = 0; s < 2; ++s) ub[s] = pk_pair(U[2 * s], U[2 * s + 1]);
 #pragma unroll
                 for (int cb = 0; cb < 8; ++cb) {
-                    const float4 gl = ldsr<float4>(lds, kF_GL + (16 * cb + 4 * g) * 4);
+                    const float4 gl = ldsr<float4>(lds, kF_GL + 512 * (c & 1) + (16 * cb + 4 * g) * 4);
                     f32x4 acc = S[cb] * f32x4{gl.x, gl.y, gl.z, gl.w};
 #pragma unroll
                     for (int s = 0; s < 2; ++s) acc = mma32(op_split<128>(lds, kF_KBT, 16 * cb + r, s, g), ub[s], acc);
                     S[cb] = acc;
                 }
             }
+            if (c + 1 < nch) load_z(c + 1);  // completes while the key waves finish the next chunk
             lds_sync();  // B1: the key waves prepared the next chunk's first half
             lds_sync();  // B0: and its second half
         }
@@ -428,22 +463,27 @@ __global__ __launch_bounds__(kThreads) void bwd_fstate_kernel(BwdArgs a)
         };
         // first half: scan, Et and Kd tiles, Kb and 2^G_L in registers
         auto half1 = [&](int c) {
-            float G[32];
-            if (!decay_scan<32>(pr.in, lane, G, pr.gl) && lane == 0) atomicOr(a.range_flag, 1);
             const int eb = kF_E + (c & 1) * 16384;
+            bool ok = true;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
+                // eight channels at a time: running decay, its chunk total, the factor tiles
                 uint32_t et[4], kd[4];
+                float gl8[8];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float ev[2], kdv[2], kbv[2];
 #pragma unroll
                     for (int h2 = 0; h2 < 2; ++h2) {
                         const int ch = 8 * j + 2 * i + h2;
+                        const float G = wave_scan(log2_decay(pr.in.al[ch]), lane);
+                        const float GL = readlane_f(G, 63);
+                        ok = ok && GL >= kRangeLog2;
+                        gl8[2 * i + h2] = GL;
                         const float kf = kv<32>(pr.in.k, ch), bf = kv<32>(pr.in.b, ch);
-                        ev[h2] = bf * kf * pow2(G[ch]);
-                        kdv[h2] = kf * pow2(-G[ch]);
-                        kbv[h2] = kf * pow2(pr.gl[ch] - G[ch]);
+                        ev[h2] = bf * kf * pow2(G);
+                        kdv[h2] = kf * pow2(-G);
+                        kbv[h2] = kf * pow2(GL - G);
                     }
                     et[i] = pk2(ev[0], ev[1]);
                     kd[i] = pk2(kdv[0], kdv[1]);
@@ -451,7 +491,14 @@ __global__ __launch_bounds__(kThreads) void bwd_fstate_kernel(BwdArgs a)
                 }
                 ldsw<uint4>(lds, eb + toff<256>(lane, c0 + 8 * j), make_uint4(et[0], et[1], et[2], et[3]));
                 ldsw<uint4>(lds, kF_KD + toff<256>(lane, c0 + 8 * j), make_uint4(kd[0], kd[1], kd[2], kd[3]));
+                if (lane == 63) {
+                    ldsw<float4>(lds, kF_GL + 512 * (c & 1) + (c0 + 8 * j) * 4,
+                                 make_float4(pow2(gl8[0]), pow2(gl8[1]), pow2(gl8[2]), pow2(gl8[3])));
+                    ldsw<float4>(lds, kF_GL + 512 * (c & 1) + (c0 + 8 * j + 4) * 4,
+                                 make_float4(pow2(gl8[4]), pow2(gl8[5]), pow2(gl8[6]), pow2(gl8[7])));
+                }
             }
+            if (!ok && lane == 0) atomicOr(a.range_flag, 1);
         };
         // second half: A^T blocks of row block p (-A below the diagonal, the
         // diagonal block inverted), Kb^T and 2^G_L
@@ -474,18 +521,11 @@ __global__ __launch_bounds__(kThreads) void bwd_fstate_kernel(BwdArgs a)
                 }
             }
             wave_lds_fence();
-            diag_inverse(lds, kF_AD + m * kTBlk, kF_T + m * kTBlk, lane);
+            diag_inverse(lds, kF_AD + m * kTBlk, kF_T + m * kTBlk, g, r);
 #pragma unroll
             for (int ch = 0; ch < 32; ++ch) {
                 const uint32_t w = pr.kb[ch >> 1];
                 ldsw<bf16raw>(lds, kF_KBT + toff<128>(c0 + ch, lane), bf16raw((ch & 1) ? (w >> 16) : (w & 0xffffu)));
-            }
-            if (lane == 63) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    ldsw<float4>(lds, kF_GL + (c0 + 4 * j) * 4,
-                                 make_float4(pow2(pr.gl[4 * j]), pow2(pr.gl[4 * j + 1]), pow2(pr.gl[4 * j + 2]),
-                                             pow2(pr.gl[4 * j + 3])));
             }
         };
         load(0);
@@ -638,7 +678,6 @@ __global__ __launch_bounds__(kThreads) void bwd_bstate_kernel(BwdArgs a)
                     ldsw<bf16raw>(lds, dw_ + toff<128>(2 * j + 1, lane), bf16raw(d8[j] >> 16));
                 }
             }
-            if (c > 0) load_rows_b(a, nxt, dop, wp, vp, rowbase, h, col0, c - 1, L, lane);
             const int64_t tl = tile64(a, n, bos, c);
             // the chunk-end state gradient, bf16, [dk][dv]
             stage_store<8>(lds, stg, S, g, r, lane, a.ws_ds16 + (tl * a.H + h) * kD * kD + col0, kD);
@@ -683,7 +722,6 @@ __global__ __launch_bounds__(kThreads) void bwd_bstate_kernel(BwdArgs a)
             store_dvdw(a, lds, stg, lane, tl, h, col0, c, L, rowbase, cur.w0, cur.v0, 0);
             store_dvdw(a, lds, stg, lane, tl, h, col0, c, L, rowbase, cur.w1, cur.v1, 1);
             wave_lds_fence();
-            cur = nxt;
             // dS = 2^G_L dS' + Qt^T dO - Et^T dX
             const bf16x8 xb0 = pk_pair(dx0, dx1), xb1 = pk_pair(dx2, dx3);
 #pragma unroll
@@ -696,8 +734,12 @@ __global__ __launch_bounds__(kThreads) void bwd_bstate_kernel(BwdArgs a)
                 acc = mma32(op_split<128>(lds, kB_ET, 16 * cb + r, 1, g), xb1, acc);
                 S[cb] = acc;
             }
+            // the next chunk's rows: the loads complete while the key waves
+            // finish its preparation
+            if (c > 0) load_rows_b(a, nxt, dop, wp, vp, rowbase, h, col0, c - 1, L, lane);
             lds_sync();
             lds_sync();
+            if (c > 0) cur = nxt;
         }
         if (a.d_initial_state) {
 #pragma unroll
@@ -717,23 +759,25 @@ __global__ __launch_bounds__(kThreads) void bwd_bstate_kernel(BwdArgs a)
         // first half: scan, the Et, Qt, Kd tiles (rows = tokens), Kb in
         // registers, 2^G_L into the buffer of chunk c
         auto half1 = [&](int c) {
-            float G[32], GL[32];
-            decay_scan<32>(pr.in, lane, G, GL);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 uint32_t kd[4], et[4], qt[4];
+                float gl8[8];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float ev[2], kdv[2], kbv[2], qv[2];
 #pragma unroll
                     for (int h2 = 0; h2 < 2; ++h2) {
                         const int ch = 8 * j + 2 * i + h2;
+                        const float G = wave_scan(log2_decay(pr.in.al[ch]), lane);
+                        const float GL = readlane_f(G, 63);
+                        gl8[2 * i + h2] = GL;
                         const float kf = kv<32>(pr.in.k, ch), bf = kv<32>(pr.in.b, ch), qf = kv<32>(pr.in.q, ch);
-                        const float up = pow2(G[ch]);
+                        const float up = pow2(G);
                         ev[h2] = bf * kf * up;
                         qv[h2] = qf * up;
-                        kdv[h2] = kf * pow2(-G[ch]);
-                        kbv[h2] = kf * pow2(GL[ch] - G[ch]);
+                        kdv[h2] = kf * pow2(-G);
+                        kbv[h2] = kf * pow2(GL - G);
                     }
                     et[i] = pk2(ev[0], ev[1]);
                     qt[i] = pk2(qv[0], qv[1]);
@@ -743,13 +787,12 @@ __global__ __launch_bounds__(kThreads) void bwd_bstate_kernel(BwdArgs a)
                 ldsw<uint4>(lds, kB_SE + toff<256>(lane, c0 + 8 * j), make_uint4(et[0], et[1], et[2], et[3]));
                 ldsw<uint4>(lds, kB_SQ + toff<256>(lane, c0 + 8 * j), make_uint4(qt[0], qt[1], qt[2], qt[3]));
                 ldsw<uint4>(lds, kB_SKD + toff<256>(lane, c0 + 8 * j), make_uint4(kd[0], kd[1], kd[2], kd[3]));
-            }
-            if (lane == 63) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    ldsw<float4>(lds, kB_GL + 512 * (c & 1) + (c0 + 4 * j) * 4,
-                                 make_float4(pow2(GL[4 * j]), pow2(GL[4 * j + 1]), pow2(GL[4 * j + 2]),
-                                             pow2(GL[4 * j + 3])));
+                if (lane == 63) {
+                    ldsw<float4>(lds, kB_GL + 512 * (c & 1) + (c0 + 8 * j) * 4,
+                                 make_float4(pow2(gl8[0]), pow2(gl8[1]), pow2(gl8[2]), pow2(gl8[3])));
+                    ldsw<float4>(lds, kB_GL + 512 * (c & 1) + (c0 + 8 * j + 4) * 4,
+                                 make_float4(pow2(gl8[4]), pow2(gl8[5]), pow2(gl8[6]), pow2(gl8[7])));
+                }
             }
         };
         auto half2 = [&](int c) {
@@ -782,7 +825,7 @@ __global__ __launch_bounds__(kThreads) void bwd_bstate_kernel(BwdArgs a)
                 }
             }
             wave_lds_fence();
-            diag_inverse(lds, kB_AD + m * kTBlk, kB_T + m * kTBlk, lane);
+            diag_inverse(lds, kB_AD + m * kTBlk, kB_T + m * kTBlk, g, r);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 ldsw<uint4>(lds, kB_KB + toff<256>(lane, c0 + 8 * j),
@@ -831,18 +874,31 @@ constexpr int kG_DX = 16384;    // [64][128] bf16 dX
 constexpr int kG_DO = 32768;    // [64][128] bf16 dO
 constexpr int kG_S = 49152;     // [128][128] bf16 S
 constexpr int kG_DS = 81920;    // [128][128] bf16 dS'
-// phases 2 and 3 (the products over tokens and the epilogue), over the same memory:
-constexpr int kGRow = 65;                   // floats per row of the [channel][token] FP32 arrays
+// phases 2 to 4 (the products over tokens and the epilogue), over the same memory:
+constexpr int kGRow = 65;                   // floats per row of the [channel][token] FP32 array
 constexpr int kG_G = 0;                     // [128][65] f32 G
 constexpr int kG_KDT = 33280;               // [128][64] bf16 Kd^T
 constexpr int kG_ETT = kG_KDT + 16384;      // [128][64] bf16 Et^T
 constexpr int kG_QTT = kG_ETT + 16384;      // [128][64] bf16 Qt^T
-constexpr int kG_DG = kG_QTT + 16384;       // [128][65] f32 dg
-constexpr int kG_KBD = kG_DG + 33280;       // [128][65] f32 Kb dKb
-constexpr int kG_RS = kG_KBD + 33280;       // [128] f32 rowsum(dS' . S)
+constexpr int kG_RQ = kG_QTT + 16384;       // [64][128] bf16 q (rows tokens)
+constexpr int kG_RK = kG_RQ + 16384;        // [64][128] bf16 k
+constexpr int kG_RB = kG_RK + 16384;        // [64][128] bf16 b
+constexpr int kG_CL = kG_RB + 16384;        // [128][64] u8: alpha outside [2^-15, 1]
+constexpr int kG_BT = kG_CL + 8192;         // [2][4][128] f32: per 16-token block, sums of dg and of Kb dKb
+constexpr int kG_RS = kG_BT + 4096;         // [128] f32 rowsum(dS' . S)
 constexpr int kG_GL = kG_RS + 512;          // [128] f32 G_L
 constexpr int kG_Bytes = kG_GL + 512;
 static_assert(kG_Bytes <= 160 * 1024 && kG_DS + 32768 <= kG_RS, "LDS budget");
+
+// Suffix sums within each row of 16 lanes (lane r gets the sum over r' >= r).
+__device__ __forceinline__ float row_rscan16(float x)
+{
+    x += row_shl<1>(x);
+    x += row_shl<2>(x);
+    x += row_shl<4>(x);
+    x += row_shl<8>(x);
+    return x;
+}
 
 // The chunk that owns workspace tile `tile` (false for an unused slot).
 __device__ bool chunk_of_tile(const BwdArgs& a, int64_t tile, int& n, int& m, int64_t& bos, int64_t& eos,
@@ -934,13 +990,16 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdArgs a)
     f32x4 dAt[4], dA[4], dPt[4], dP[4], dEt[4], dQt[4], dKb[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) dAt[b] = dA[b] = dPt[b] = dP[b] = dEt[b] = dQt[b] = dKb[b] = zero4();
+    // block by block, the K steps inside (the shared operands are read again
+    // per block: that keeps the live registers to the accumulators)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        const bf16x8 xt = op_nat<256>(lds, kG_DX, 16 * tb + r, s, g);
-        const bf16x8 ut = op_nat<256>(lds, kG_U, 16 * tb + r, s, g);
-        const bf16x8 ot = op_nat<256>(lds, kG_DO, 16 * tb + r, s, g);
+    for (int b = 0; b < 4; ++b) {
+        const int cb = 4 * cq + b;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+        for (int s = 0; s < 4; ++s) {
+            const bf16x8 xt = op_nat<256>(lds, kG_DX, 16 * tb + r, s, g);
+            const bf16x8 ut = op_nat<256>(lds, kG_U, 16 * tb + r, s, g);
+            const bf16x8 ot = op_nat<256>(lds, kG_DO, 16 * tb + r, s, g);
             if (b <= tb) {
                 const bf16x8 ub = op_nat<256>(lds, kG_U, 16 * b + r, s, g);
                 dAt[b] = mma32(ub, xt, dAt[b]);
@@ -950,12 +1009,12 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdArgs a)
                 dA[b] = mma32(op_nat<256>(lds, kG_DX, 16 * b + r, s, g), ut, dA[b]);
                 dP[b] = mma32(op_nat<256>(lds, kG_DO, 16 * b + r, s, g), ut, dP[b]);
             }
-            const int cb = 4 * cq + b;
             const bf16x8 sr = op_nat<256>(lds, kG_S, 16 * cb + r, s, g);
             dEt[b] = mma32(sr, xt, dEt[b]);
             dQt[b] = mma32(sr, ot, dQt[b]);
             dKb[b] = mma32(op_nat<256>(lds, kG_DS, 16 * cb + r, s, g), ut, dKb[b]);
         }
+        __builtin_amdgcn_sched_barrier(0);  // one block at a time: bounds the live operands
     }
     // masks and signs: dA = -strict_lower(dX U^T), dP = lower(dO U^T), dEt = -dX S^T
 #pragma unroll
@@ -969,9 +1028,19 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdArgs a)
             dP[b][e] = lr >= lc ? dP[b][e] : 0.f;
             dEt[b][e] = -dEt[b][e];
         }
+    // dA, dP and their transposes as bf16 B operands over tokens (half the registers)
+    bf16x8 bAt[2], bPt[2], bA[2], bP[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        bAt[s] = pk_pair(dAt[2 * s], dAt[2 * s + 1]);
+        bPt[s] = pk_pair(dPt[2 * s], dPt[2 * s + 1]);
+        bA[s] = pk_pair(dA[2 * s], dA[2 * s + 1]);
+        bP[s] = pk_pair(dP[2 * s], dP[2 * s + 1]);
+    }
     __syncthreads();
 
-    // ---- phase 2: the key side of this chunk, [channel][token]
+    // ---- phase 2: the key side of this chunk: G, the factor tiles and the
+    // clamp flags [channel][token], the raw q, k, b [token][channel]
     {
         float G[16], GL[16];
         decay_scan<16>(kin, lane, G, GL);
@@ -984,40 +1053,31 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdArgs a)
             ldsw<bf16raw>(lds, kG_KDT + toff<128>(ch, lane), f32_to_bf16(kf * pow2(-G[c])));
             ldsw<bf16raw>(lds, kG_ETT + toff<128>(ch, lane), f32_to_bf16(bf * kf * up));
             ldsw<bf16raw>(lds, kG_QTT + toff<128>(ch, lane), f32_to_bf16(qf * up));
+            const float lg = __log2f(kin.al[c]);
+            ldsw<unsigned char>(lds, kG_CL + ch * 64 + lane, (lg >= kLog2AlphaFloor && lg <= 0.f) ? 0 : 1);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            ldsw<uint4>(lds, kG_RQ + toff<256>(lane, c0 + 8 * j),
+                        make_uint4(kin.q[4 * j], kin.q[4 * j + 1], kin.q[4 * j + 2], kin.q[4 * j + 3]));
+            ldsw<uint4>(lds, kG_RK + toff<256>(lane, c0 + 8 * j),
+                        make_uint4(kin.k[4 * j], kin.k[4 * j + 1], kin.k[4 * j + 2], kin.k[4 * j + 3]));
+            ldsw<uint4>(lds, kG_RB + toff<256>(lane, c0 + 8 * j),
+                        make_uint4(kin.b[4 * j], kin.b[4 * j + 1], kin.b[4 * j + 2], kin.b[4 * j + 3]));
         }
         if (lane == 63) {
 #pragma unroll
             for (int c = 0; c < 16; ++c) ldsw<float>(lds, kG_GL + 4 * (c0 + c), GL[c]);
         }
     }
-    // the raw inputs the epilogue needs: q, k, b at (token 16 tb + r, channels 16 cb + 4g .. + 3)
     const int tok = 16 * tb + r;
-    uint2 rq[4], rk[4], rb[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        if (tok < L) {
-            const int64_t off = ((rowbase + tok) * a.H + h) * kD + 16 * (4 * cq + b) + 4 * g;
-            rq[b] = *reinterpret_cast<const uint2*>(static_cast<const bf16raw*>(a.q) + off);
-            rk[b] = *reinterpret_cast<const uint2*>(static_cast<const bf16raw*>(a.k) + off);
-            rb[b] = *reinterpret_cast<const uint2*>(static_cast<const bf16raw*>(a.b) + off);
-        } else {
-            rq[b] = rk[b] = rb[b] = make_uint2(0, 0);
-        }
-    }
     __syncthreads();
 
     // ---- phase 3: products over tokens and the epilogue
-    bf16x8 bAt[2], bPt[2], bA[2], bP[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        bAt[s] = pk_pair(dAt[2 * s], dAt[2 * s + 1]);
-        bPt[s] = pk_pair(dPt[2 * s], dPt[2 * s + 1]);
-        bA[s] = pk_pair(dA[2 * s], dA[2 * s + 1]);
-        bP[s] = pk_pair(dP[2 * s], dP[2 * s + 1]);
-    }
     bf16raw* dq_out = static_cast<bf16raw*>(a.dq);
     bf16raw* dk_out = static_cast<bf16raw*>(a.dk);
     bf16raw* db_out = static_cast<bf16raw*>(a.db);
+    f32x4 dgs[4];  // dg summed over this and the later tokens of the lane's 16-token block
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
         const int cb = 4 * cq + b;
@@ -1030,7 +1090,10 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdArgs a)
             dk = mma32(op_split<128>(lds, kG_ETT, 16 * cb + r, s, g), bA[s], dk);
             dk = mma32(op_split<128>(lds, kG_QTT, 16 * cb + r, s, g), bP[s], dk);
         }
-        const uint32_t qw[2] = {rq[b].x, rq[b].y}, kw[2] = {rk[b].x, rk[b].y}, bw[2] = {rb[b].x, rb[b].y};
+        const uint2 rq = ldsr<uint2>(lds, kG_RQ + toff<256>(tok, 16 * cb + 4 * g));
+        const uint2 rk = ldsr<uint2>(lds, kG_RK + toff<256>(tok, 16 * cb + 4 * g));
+        const uint2 rb = ldsr<uint2>(lds, kG_RB + toff<256>(tok, 16 * cb + 4 * g));
+        const uint32_t qw[2] = {rq.x, rq.y}, kw[2] = {rk.x, rk.y}, bw[2] = {rb.x, rb.y};
         float oq[4], ok[4], ob[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -1050,8 +1113,13 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdArgs a)
             ob[e] = dev * kf;
             const float kbd = kf * kbf * dKbv;
             const float dg = ef * dep + qf * dqp - kf * dkp + ef * up * dEtv + qf * up * dQtv - kbd;
-            ldsw<float>(lds, kG_DG + (ch * kGRow + tok) * 4, dg);
-            ldsw<float>(lds, kG_KBD + (ch * kGRow + tok) * 4, kbd);
+            // sums over the block's tokens: lane r = 0 of the row holds the block's total
+            dgs[b][e] = row_rscan16(dg);
+            const float kbs = row_rscan16(kbd);
+            if (r == 0) {
+                ldsw<float>(lds, kG_BT + (tb * 128 + ch) * 4, dgs[b][e]);
+                ldsw<float>(lds, kG_BT + 2048 + (tb * 128 + ch) * 4, kbs);
+            }
         }
         if (tok < L) {
             const int64_t off = ((rowbase + tok) * a.H + h) * kD + 16 * cb + 4 * g;
@@ -1059,23 +1127,38 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdArgs a)
             *reinterpret_cast<uint2*>(dk_out + off) = make_uint2(pk2(ok[0], ok[1]), pk2(ok[2], ok[3]));
             *reinterpret_cast<uint2*>(db_out + off) = make_uint2(pk2(ob[0], ob[1]), pk2(ob[2], ob[3]));
         }
+        __builtin_amdgcn_sched_barrier(0);  // one tile at a time: bounds the live registers
     }
     __syncthreads();
 
-    // ---- phase 4: the chunk-end terms and the reverse running sum per channel
-    if (tid < kD) {
-        const int ch = tid;
-        const float gl = ldsr<float>(lds, kG_GL + 4 * ch);
-        float acc = pow2(gl) * ldsr<float>(lds, kG_RS + 4 * ch);
-        for (int j = 0; j < L; ++j) acc += ldsr<float>(lds, kG_KBD + (ch * kGRow + j) * 4);
-        for (int i = L - 1; i >= 0; --i) {
-            acc += ldsr<float>(lds, kG_DG + (ch * kGRow + i) * 4);
-            const int64_t off = ((rowbase + i) * a.H + h) * kD + ch;
-            const float al = a.alpha[off];
-            const float lg = __log2f(al);
-            const bool clamped = !(lg >= kLog2AlphaFloor && lg <= 0.f);
-            a.dalpha[off] = clamped ? 0.f : acc / al;
+    // ---- phase 4: dlog(alpha_m) = the sum of dg over tokens >= m plus the
+    // chunk-end terms (2^G_L rowsum(dS' . S) and the sum of Kb dKb);
+    // dalpha = dlog(alpha) / alpha, with alpha = 2^(G_m - G_(m-1)) (zero
+    // where the clamp is active)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int cb = 4 * cq + b;
+        float da[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int ch = 16 * cb + 4 * g + e;
+            float later = 0.f, kbsum = 0.f;
+#pragma unroll
+            for (int t2 = 0; t2 < 4; ++t2) {
+                const float bt = ldsr<float>(lds, kG_BT + (t2 * 128 + ch) * 4);
+                later += t2 > tb ? bt : 0.f;
+                kbsum += ldsr<float>(lds, kG_BT + 2048 + (t2 * 128 + ch) * 4);
+            }
+            const float end = pow2(ldsr<float>(lds, kG_GL + 4 * ch)) * ldsr<float>(lds, kG_RS + 4 * ch) + kbsum;
+            const float G = ldsr<float>(lds, kG_G + (ch * kGRow + tok) * 4);
+            const float Gp = tok > 0 ? ldsr<float>(lds, kG_G + (ch * kGRow + tok - 1) * 4) : 0.f;
+            const float dl = dgs[b][e] + later + end;
+            da[e] = ldsr<unsigned char>(lds, kG_CL + ch * 64 + tok) ? 0.f : dl / pow2(G - Gp);
         }
+        if (tok < L)
+            *reinterpret_cast<float4*>(a.dalpha + ((rowbase + tok) * a.H + h) * kD + 16 * cb + 4 * g) =
+                make_float4(da[0], da[1], da[2], da[3]);
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
