@@ -867,28 +867,33 @@ __global__ __launch_bounds__(kThreads) void bwd_bstate_kernel(BwdArgs a)
 }
 
 // =============================================================================
-// bwd_grads: per (chunk, head), everything that needs S, dS', U and dX.
+// bwd_grads: per (chunk, head, half of the key channels), everything that
+// needs S, dS', U and dX.  A workgroup takes 64 key channels, so that its LDS
+// stays at 80 KB and two workgroups share a CU: one's loads overlap the
+// other's products.  The products over value columns that do not involve the
+// key channels (dA, dP and their transposes) are formed by both halves.
 // LDS map (bytes).  Phase 1 (the products over value columns):
 constexpr int kG_U = 0;         // [64][128] bf16 U
 constexpr int kG_DX = 16384;    // [64][128] bf16 dX
 constexpr int kG_DO = 32768;    // [64][128] bf16 dO
-constexpr int kG_S = 49152;     // [128][128] bf16 S
-constexpr int kG_DS = 81920;    // [128][128] bf16 dS'
+constexpr int kG_S = 49152;     // [64][128] bf16 S, the half's key channels
+constexpr int kG_DS = 65536;    // [64][128] bf16 dS'
+constexpr int kG_Phase1 = 81920;
 // phases 2 to 4 (the products over tokens and the epilogue), over the same memory:
 constexpr int kGRow = 65;                   // floats per row of the [channel][token] FP32 array
-constexpr int kG_G = 0;                     // [128][65] f32 G
-constexpr int kG_KDT = 33280;               // [128][64] bf16 Kd^T
-constexpr int kG_ETT = kG_KDT + 16384;      // [128][64] bf16 Et^T
-constexpr int kG_QTT = kG_ETT + 16384;      // [128][64] bf16 Qt^T
-constexpr int kG_RQ = kG_QTT + 16384;       // [64][128] bf16 q (rows tokens)
-constexpr int kG_RK = kG_RQ + 16384;        // [64][128] bf16 k
-constexpr int kG_RB = kG_RK + 16384;        // [64][128] bf16 b
-constexpr int kG_CL = kG_RB + 16384;        // [128][64] u8: alpha outside [2^-15, 1]
-constexpr int kG_BT = kG_CL + 8192;         // [2][4][128] f32: per 16-token block, sums of dg and of Kb dKb
-constexpr int kG_RS = kG_BT + 4096;         // [128] f32 rowsum(dS' . S)
-constexpr int kG_GL = kG_RS + 512;          // [128] f32 G_L
-constexpr int kG_Bytes = kG_GL + 512;
-static_assert(kG_Bytes <= 160 * 1024 && kG_DS + 32768 <= kG_RS, "LDS budget");
+constexpr int kG_G = 0;                     // [64][65] f32 G
+constexpr int kG_KDT = 16640;               // [64][64] bf16 Kd^T
+constexpr int kG_ETT = kG_KDT + 8192;       // [64][64] bf16 Et^T
+constexpr int kG_QTT = kG_ETT + 8192;       // [64][64] bf16 Qt^T
+constexpr int kG_RQ = kG_QTT + 8192;        // [64][64] bf16 q (rows tokens)
+constexpr int kG_RK = kG_RQ + 8192;         // [64][64] bf16 k
+constexpr int kG_RB = kG_RK + 8192;         // [64][64] bf16 b
+constexpr int kG_CL = kG_RB + 8192;         // [64][64] u8: alpha outside [2^-15, 1]
+constexpr int kG_BT = kG_CL + 4096;         // [2][4][64] f32: per 16-token block, sums of dg and of Kb dKb
+constexpr int kG_RS = kG_BT + 2048;         // [64] f32 rowsum(dS' . S)
+constexpr int kG_GL = kG_RS + 256;          // [64] f32 G_L
+constexpr int kG_Bytes = kG_Phase1;
+static_assert(kG_GL + 256 <= kG_Bytes && 2 * kG_Bytes <= 160 * 1024, "LDS budget: two workgroups per CU");
 
 // Suffix sums within each row of 16 lanes (lane r gets the sum over r' >= r).
 __device__ __forceinline__ float row_rscan16(float x)
@@ -926,12 +931,16 @@ __device__ bool chunk_of_tile(const BwdArgs& a, int64_t tile, int& n, int& m, in
     return bos + int64_t(m) * kC < eos && tile64(a, n, bos, m) == tile;
 }
 
-__global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdArgs a)
+__global__ __launch_bounds__(kThreads, 4) void bwd_grads_kernel(BwdArgs a)
 {
     extern __shared__ __align__(16) unsigned char lds[];
     if (*a.range_flag != 0) return;
-    const int h = int(blockIdx.x % a.H);
-    const int64_t tile = blockIdx.x / a.H;
+    int64_t ch_idx;  // (tile, head)
+    int half;
+    xcd_pair(blockIdx.x, ch_idx, half);
+    if (ch_idx >= int64_t(a.B) * a.slots64 * a.H) return;
+    const int h = int(ch_idx % a.H);
+    const int64_t tile = ch_idx / a.H;
     int n, m;
     int64_t bos, eos, brow;
     if (!chunk_of_tile(a, tile, n, m, bos, eos, brow)) return;
@@ -939,14 +948,16 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdArgs a)
     const int64_t t0 = bos + int64_t(m) * kC;  // first token of the chunk
     const int L = int(eos - t0 < kC ? eos - t0 : kC);
     const int64_t rowbase = brow * a.T + t0;
+    const int hc = 64 * half;                  // first key channel of this workgroup
     const bf16raw* dop = static_cast<const bf16raw*>(a.d_o);
 
-    // ---- phase 0: U, dX, dO, S and dS' into LDS; the key inputs into registers
+    // ---- phase 0: U, dX, dO and the half's rows of S and dS' into LDS; the
+    // key inputs (one token per lane, eight channels per wave) into registers
     {
         const bf16raw* us = a.ws_u16 + (tile * a.H + h) * kC * kD;
         const bf16raw* xs = a.ws_dx16 + (tile * a.H + h) * kC * kD;
-        const bf16raw* ss = a.ws_s16 + (tile * a.H + h) * kD * kD;
-        const bf16raw* ds = a.ws_ds16 + (tile * a.H + h) * kD * kD;
+        const bf16raw* ss = a.ws_s16 + ((tile * a.H + h) * kD + hc) * kD;
+        const bf16raw* ds = a.ws_ds16 + ((tile * a.H + h) * kD + hc) * kD;
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
             const int p = tid + kThreads * it, row = p >> 4, gr = p & 15;
@@ -954,47 +965,49 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdArgs a)
             const uint4 x = reinterpret_cast<const uint4*>(xs)[p];
             uint4 d = make_uint4(0, 0, 0, 0);
             if (row < L) d = *reinterpret_cast<const uint4*>(dop + ((rowbase + row) * a.H + h) * kD + 8 * gr);
+            const uint4 sv = reinterpret_cast<const uint4*>(ss)[p];
+            const uint4 dv4 = reinterpret_cast<const uint4*>(ds)[p];
             ldsw<uint4>(lds, kG_U + toff<256>(row, 8 * gr), u);
             ldsw<uint4>(lds, kG_DX + toff<256>(row, 8 * gr), x);
             ldsw<uint4>(lds, kG_DO + toff<256>(row, 8 * gr), d);
-        }
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int p = tid + kThreads * it, row = p >> 4, gr = p & 15;
-            ldsw<uint4>(lds, kG_S + toff<256>(row, 8 * gr), reinterpret_cast<const uint4*>(ss)[p]);
-            ldsw<uint4>(lds, kG_DS + toff<256>(row, 8 * gr), reinterpret_cast<const uint4*>(ds)[p]);
+            ldsw<uint4>(lds, kG_S + toff<256>(row, 8 * gr), sv);
+            ldsw<uint4>(lds, kG_DS + toff<256>(row, 8 * gr), dv4);
         }
     }
-    KeyIn<16> kin;
-    const int c0 = 16 * wave;
-    load_keys<16, true>(kin, a, ((rowbase + lane) * a.H + h) * kD + c0, lane < L);
+    KeyIn<8> kin;
+    const int c0 = 8 * wave;  // the wave's key channels within the half
+    load_keys<8, true>(kin, a, ((rowbase + lane) * a.H + h) * kD + hc + c0, lane < L);
     __syncthreads();
 
-    // ---- phase 1: rowsum(dS' . S) and the products over value columns
+    // ---- phase 1: rowsum(dS' . S) (kept in a register until phase 4) and the
+    // products over value columns
+    float rs_val;
     {
-        const int ch = tid >> 2, qq = tid & 3;
+        const int ch = tid >> 3, qq = tid & 7;  // 8 threads per channel, 16 columns each
         float acc = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint4 s4 = ldsr<uint4>(lds, kG_S + toff<256>(ch, 32 * qq + 8 * j));
-            const uint4 d4 = ldsr<uint4>(lds, kG_DS + toff<256>(ch, 32 * qq + 8 * j));
+        for (int j = 0; j < 2; ++j) {
+            const uint4 s4 = ldsr<uint4>(lds, kG_S + toff<256>(ch, 16 * qq + 8 * j));
+            const uint4 d4 = ldsr<uint4>(lds, kG_DS + toff<256>(ch, 16 * qq + 8 * j));
             const uint32_t sw[4] = {s4.x, s4.y, s4.z, s4.w}, dw[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc += lo_f(sw[i]) * lo_f(dw[i]) + hi_f(sw[i]) * hi_f(dw[i]);
         }
         acc += __shfl_xor(acc, 1);
         acc += __shfl_xor(acc, 2);
-        if (qq == 0) ldsw<float>(lds, kG_RS + 4 * ch, acc);
+        acc += __shfl_xor(acc, 4);
+        rs_val = acc;  // lanes with qq == 0 hold channel ch's sum
     }
-    const int tb = wave & 3, cq = wave >> 2;
-    f32x4 dAt[4], dA[4], dPt[4], dP[4], dEt[4], dQt[4], dKb[4];
+    const int tb = wave & 3, cq = wave >> 2;  // token block; pair of channel blocks (2 cq, 2 cq + 1)
+    f32x4 dAt[4], dA[4], dPt[4], dP[4], dEt[2], dQt[2], dKb[2];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) dAt[b] = dA[b] = dPt[b] = dP[b] = dEt[b] = dQt[b] = dKb[b] = zero4();
-    // block by block, the K steps inside (the shared operands are read again
-    // per block: that keeps the live registers to the accumulators)
+    for (int b = 0; b < 4; ++b) dAt[b] = dA[b] = dPt[b] = dP[b] = zero4();
+#pragma unroll
+    for (int b = 0; b < 2; ++b) dEt[b] = dQt[b] = dKb[b] = zero4();
+    // block by block, the K steps inside (shared operands are read again per
+    // block: that keeps the live registers to the accumulators)
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-        const int cb = 4 * cq + b;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const bf16x8 xt = op_nat<256>(lds, kG_DX, 16 * tb + r, s, g);
@@ -1009,10 +1022,13 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdArgs a)
                 dA[b] = mma32(op_nat<256>(lds, kG_DX, 16 * b + r, s, g), ut, dA[b]);
                 dP[b] = mma32(op_nat<256>(lds, kG_DO, 16 * b + r, s, g), ut, dP[b]);
             }
-            const bf16x8 sr = op_nat<256>(lds, kG_S, 16 * cb + r, s, g);
-            dEt[b] = mma32(sr, xt, dEt[b]);
-            dQt[b] = mma32(sr, ot, dQt[b]);
-            dKb[b] = mma32(op_nat<256>(lds, kG_DS, 16 * cb + r, s, g), ut, dKb[b]);
+            if (b < 2) {
+                const int cb = 2 * cq + b;  // channel block within the half
+                const bf16x8 sr = op_nat<256>(lds, kG_S, 16 * cb + r, s, g);
+                dEt[b] = mma32(sr, xt, dEt[b]);
+                dQt[b] = mma32(sr, ot, dQt[b]);
+                dKb[b] = mma32(op_nat<256>(lds, kG_DS, 16 * cb + r, s, g), ut, dKb[b]);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);  // one block at a time: bounds the live operands
     }
@@ -1026,8 +1042,9 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdArgs a)
             dPt[b][e] = lr <= lc ? dPt[b][e] : 0.f;
             dA[b][e] = lr > lc ? -dA[b][e] : 0.f;     // rows i, columns j: i > j
             dP[b][e] = lr >= lc ? dP[b][e] : 0.f;
-            dEt[b][e] = -dEt[b][e];
         }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) dEt[b] = -dEt[b];
     // dA, dP and their transposes as bf16 B operands over tokens (half the registers)
     bf16x8 bAt[2], bPt[2], bA[2], bP[2];
 #pragma unroll
@@ -1042,12 +1059,12 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdArgs a)
     // ---- phase 2: the key side of this chunk: G, the factor tiles and the
     // clamp flags [channel][token], the raw q, k, b [token][channel]
     {
-        float G[16], GL[16];
-        decay_scan<16>(kin, lane, G, GL);
+        float G[8], GL[8];
+        decay_scan<8>(kin, lane, G, GL);
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            const int ch = c0 + c;
-            const float kf = kv<16>(kin.k, c), bf = kv<16>(kin.b, c), qf = kv<16>(kin.q, c);
+        for (int c = 0; c < 8; ++c) {
+            const int ch = c0 + c;  // within the half
+            const float kf = kv<8>(kin.k, c), bf = kv<8>(kin.b, c), qf = kv<8>(kin.q, c);
             const float up = pow2(G[c]);
             ldsw<float>(lds, kG_G + (ch * kGRow + lane) * 4, G[c]);
             ldsw<bf16raw>(lds, kG_KDT + toff<128>(ch, lane), f32_to_bf16(kf * pow2(-G[c])));
@@ -1056,19 +1073,14 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdArgs a)
             const float lg = __log2f(kin.al[c]);
             ldsw<unsigned char>(lds, kG_CL + ch * 64 + lane, (lg >= kLog2AlphaFloor && lg <= 0.f) ? 0 : 1);
         }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            ldsw<uint4>(lds, kG_RQ + toff<256>(lane, c0 + 8 * j),
-                        make_uint4(kin.q[4 * j], kin.q[4 * j + 1], kin.q[4 * j + 2], kin.q[4 * j + 3]));
-            ldsw<uint4>(lds, kG_RK + toff<256>(lane, c0 + 8 * j),
-                        make_uint4(kin.k[4 * j], kin.k[4 * j + 1], kin.k[4 * j + 2], kin.k[4 * j + 3]));
-            ldsw<uint4>(lds, kG_RB + toff<256>(lane, c0 + 8 * j),
-                        make_uint4(kin.b[4 * j], kin.b[4 * j + 1], kin.b[4 * j + 2], kin.b[4 * j + 3]));
-        }
+        ldsw<uint4>(lds, kG_RQ + toff<128>(lane, c0), make_uint4(kin.q[0], kin.q[1], kin.q[2], kin.q[3]));
+        ldsw<uint4>(lds, kG_RK + toff<128>(lane, c0), make_uint4(kin.k[0], kin.k[1], kin.k[2], kin.k[3]));
+        ldsw<uint4>(lds, kG_RB + toff<128>(lane, c0), make_uint4(kin.b[0], kin.b[1], kin.b[2], kin.b[3]));
         if (lane == 63) {
 #pragma unroll
-            for (int c = 0; c < 16; ++c) ldsw<float>(lds, kG_GL + 4 * (c0 + c), GL[c]);
+            for (int c = 0; c < 8; ++c) ldsw<float>(lds, kG_GL + 4 * (c0 + c), GL[c]);
         }
+        if ((tid & 7) == 0) ldsw<float>(lds, kG_RS + 4 * (tid >> 3), rs_val);
     }
     const int tok = 16 * tb + r;
     __syncthreads();
@@ -1077,10 +1089,10 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdArgs a)
     bf16raw* dq_out = static_cast<bf16raw*>(a.dq);
     bf16raw* dk_out = static_cast<bf16raw*>(a.dk);
     bf16raw* db_out = static_cast<bf16raw*>(a.db);
-    f32x4 dgs[4];  // dg summed over this and the later tokens of the lane's 16-token block
+    f32x4 dgs[2];  // dg summed over this and the later tokens of the lane's 16-token block
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const int cb = 4 * cq + b;
+    for (int b = 0; b < 2; ++b) {
+        const int cb = 2 * cq + b;
         f32x4 de = zero4(), dq = zero4(), dk = zero4();
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
@@ -1090,14 +1102,14 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdArgs a)
             dk = mma32(op_split<128>(lds, kG_ETT, 16 * cb + r, s, g), bA[s], dk);
             dk = mma32(op_split<128>(lds, kG_QTT, 16 * cb + r, s, g), bP[s], dk);
         }
-        const uint2 rq = ldsr<uint2>(lds, kG_RQ + toff<256>(tok, 16 * cb + 4 * g));
-        const uint2 rk = ldsr<uint2>(lds, kG_RK + toff<256>(tok, 16 * cb + 4 * g));
-        const uint2 rb = ldsr<uint2>(lds, kG_RB + toff<256>(tok, 16 * cb + 4 * g));
+        const uint2 rq = ldsr<uint2>(lds, kG_RQ + toff<128>(tok, 16 * cb + 4 * g));
+        const uint2 rk = ldsr<uint2>(lds, kG_RK + toff<128>(tok, 16 * cb + 4 * g));
+        const uint2 rb = ldsr<uint2>(lds, kG_RB + toff<128>(tok, 16 * cb + 4 * g));
         const uint32_t qw[2] = {rq.x, rq.y}, kw[2] = {rk.x, rk.y}, bw[2] = {rb.x, rb.y};
         float oq[4], ok[4], ob[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int ch = 16 * cb + 4 * g + e;
+            const int ch = 16 * cb + 4 * g + e;  // within the half
             const float G = ldsr<float>(lds, kG_G + (ch * kGRow + tok) * 4);
             const float gl = ldsr<float>(lds, kG_GL + 4 * ch);
             const float up = pow2(G), dn = pow2(-G), kbf = pow2(gl - G);
@@ -1117,12 +1129,12 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdArgs a)
             dgs[b][e] = row_rscan16(dg);
             const float kbs = row_rscan16(kbd);
             if (r == 0) {
-                ldsw<float>(lds, kG_BT + (tb * 128 + ch) * 4, dgs[b][e]);
-                ldsw<float>(lds, kG_BT + 2048 + (tb * 128 + ch) * 4, kbs);
+                ldsw<float>(lds, kG_BT + (tb * 64 + ch) * 4, dgs[b][e]);
+                ldsw<float>(lds, kG_BT + 1024 + (tb * 64 + ch) * 4, kbs);
             }
         }
         if (tok < L) {
-            const int64_t off = ((rowbase + tok) * a.H + h) * kD + 16 * cb + 4 * g;
+            const int64_t off = ((rowbase + tok) * a.H + h) * kD + hc + 16 * cb + 4 * g;
             *reinterpret_cast<uint2*>(dq_out + off) = make_uint2(pk2(oq[0], oq[1]), pk2(oq[2], oq[3]));
             *reinterpret_cast<uint2*>(dk_out + off) = make_uint2(pk2(ok[0], ok[1]), pk2(ok[2], ok[3]));
             *reinterpret_cast<uint2*>(db_out + off) = make_uint2(pk2(ob[0], ob[1]), pk2(ob[2], ob[3]));
@@ -1136,8 +1148,8 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdArgs a)
     // dalpha = dlog(alpha) / alpha, with alpha = 2^(G_m - G_(m-1)) (zero
     // where the clamp is active)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const int cb = 4 * cq + b;
+    for (int b = 0; b < 2; ++b) {
+        const int cb = 2 * cq + b;
         float da[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -1145,9 +1157,9 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdArgs a)
             float later = 0.f, kbsum = 0.f;
 #pragma unroll
             for (int t2 = 0; t2 < 4; ++t2) {
-                const float bt = ldsr<float>(lds, kG_BT + (t2 * 128 + ch) * 4);
+                const float bt = ldsr<float>(lds, kG_BT + (t2 * 64 + ch) * 4);
                 later += t2 > tb ? bt : 0.f;
-                kbsum += ldsr<float>(lds, kG_BT + 2048 + (t2 * 128 + ch) * 4);
+                kbsum += ldsr<float>(lds, kG_BT + 1024 + (t2 * 64 + ch) * 4);
             }
             const float end = pow2(ldsr<float>(lds, kG_GL + 4 * ch)) * ldsr<float>(lds, kG_RS + 4 * ch) + kbsum;
             const float G = ldsr<float>(lds, kG_G + (ch * kGRow + tok) * 4);
@@ -1156,7 +1168,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(BwdArgs a)
             da[e] = ldsr<unsigned char>(lds, kG_CL + ch * 64 + tok) ? 0.f : dl / pow2(G - Gp);
         }
         if (tok < L)
-            *reinterpret_cast<float4*>(a.dalpha + ((rowbase + tok) * a.H + h) * kD + 16 * cb + 4 * g) =
+            *reinterpret_cast<float4*>(a.dalpha + ((rowbase + tok) * a.H + h) * kD + hc + 16 * cb + 4 * g) =
                 make_float4(da[0], da[1], da[2], da[3]);
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -1197,7 +1209,9 @@ hipError_t launch_chunk_bwd_mfma(const BwdArgs& a, hipStream_t stream)
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (tiles > 0) {
-        hipLaunchKernelGGL(bwd_grads_kernel, dim3(unsigned(tiles)), dim3(kThreads), kG_Bytes, stream, a);
+        const int64_t gblocks = xcd_pair_grid(tiles);  // the two channel halves of a (chunk, head) share an XCD
+        if (gblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(bwd_grads_kernel, dim3(unsigned(gblocks)), dim3(kThreads), kG_Bytes, stream, a);
         e = hipGetLastError();
     }
     return e;
