@@ -95,7 +95,8 @@ constexpr int kZsBuf = kValueWaves * kZsWave;
 constexpr int kLdsBytes = kOffZs + 2 * kZsBuf;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 static_assert(kOffP == kOffAneg + 8192 && kOffT == kOffP + 8192, "Aneg and P are cleared as one range");
-static_assert(kOffZs % 16 == 0 && kZsWave % 16 == 0, "16-byte aligned z rows");
+static_assert(kOffZs % 16 == 0 && kZsWave % 256 == 0 && kZsBuf % 256 == 0 && (kOffZs & 0xF0) == 0,
+              "16-byte aligned z rows; granule bits of the z base clear (store_z)");
 
 // [64][128] bf16 tiles Et, Qt, Kt.  Channels are stored permuted within each
 // group of 32 so that the split K groups of the matrix products, channels
@@ -296,9 +297,16 @@ __device__ __forceinline__ void lds_barrier()
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcFlags = 0x00020000;  // 32-bit raw buffer, gfx9 family
 
+// Every window in this kernel is the same in all lanes of a wavefront (it
+// depends on the chain, the chunk and the wavefront's role only); taking the
+// first lane's value keeps the descriptor in scalar registers, where the
+// buffer instructions need it, instead of a per-lane loop over descriptors.
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes)
 {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), kRsrcFlags);
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(p)), hi = __builtin_amdgcn_readfirstlane(uint32_t(p >> 32));
+    void* pu = reinterpret_cast<void*>((uint64_t(hi) << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(pu, (short)0, int(__builtin_amdgcn_readfirstlane(bytes)), kRsrcFlags);
 }
 __device__ __forceinline__ uint4 ld_b128(rsrc_t r, uint32_t off)
 {
@@ -314,16 +322,17 @@ __device__ __forceinline__ uint4 ld_b128(rsrc_t r, uint32_t off)
 // Gate layouts (template parameter G, gdn2_gate_flags): a scalar gate is one
 // value per token and head, read once per token and applied to every channel
 // of its axis.  A scalar erase gate sits in b[t].x (bf16 bits), a scalar or
-// tied write gate in w[0].x of RawVK, a scalar decay in a[t][0].x.
+// tied write gate in w.x of RawVK, a scalar decay in a[t][0].x.
 struct RawK {
     uint4 q[2], k[2], b[2];  // 8 bf16 channels per token
     uint4 a[2][2];           // alpha, 8 FP32 channels per token
 };
-// v and w of the workgroup's 64 value columns, loaded by the key wavefronts of
-// channel half 0 (the others run behind them on their SIMDs): tokens
-// 16 tb + (l & 15), columns 8 (l >> 4) + 32 u .. + 7 of the tile.
+// v and w of 32 of the workgroup's 64 value columns, loaded by every key
+// wavefront (its channel half ch picks the 32-column block u = ch, so that the
+// two key wavefronts of a SIMD carry the same work and issue the same loads):
+// tokens 16 tb + (l & 15), columns 32 u + 8 (l >> 4) .. + 7 of the tile.
 struct RawVK {
-    uint4 v[2], w[2];
+    uint4 v, w;
 };
 struct KeyLane {
     int tb, ch, tp, cg;
@@ -402,6 +411,7 @@ __device__ __forceinline__ void load_alpha(RawK& R, const RawSrc& s, int t, cons
 template <int G, bool SEG>
 __device__ __forceinline__ void load_vk(RawVK& V, const ChunkArgs& a, int64_t row0, int L, int j0, int kw, int lane)
 {
+    const int u = kw >> 2;  // 32-column block
     const int dvio = SEG && a.dv_io > 0 ? a.dv_io : a.dv;
     const bool real = !SEG || j0 < dvio;
     const uint32_t vstride = uint32_t(a.H) * uint32_t(dvio) * 2;
@@ -410,43 +420,43 @@ __device__ __forceinline__ void load_vk(RawVK& V, const ChunkArgs& a, int64_t ro
     const int64_t base = row0 * dvio + (real ? j0 : 0);
     const uint32_t tok = uint32_t(16 * (kw & 3) + (lane & 15));
     const rsrc_t rv = make_rsrc(static_cast<const bf16raw*>(a.v) + base, win);
-    const uint32_t off = tok * vstride + 2 * (8 * (lane >> 4));
+    const uint32_t off = tok * vstride + 2 * (8 * (lane >> 4)) + 64 * u;
     if (G & (kTied | kScalarWrite)) {  // the token's scalar write gate (tied: its erase gate)
         const uint32_t rows = L > 0 && real ? uint32_t(L - 1) * uint32_t(a.H) + 1 : 0u;
         const rsrc_t rg = make_rsrc(static_cast<const bf16raw*>(G & kTied ? a.b : a.w) + row0, 2 * rows);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) V.v[u] = ld_b128(rv, off + 64 * u);
-        V.w[0].x = __builtin_amdgcn_raw_buffer_load_b16(rg, int(tok * uint32_t(a.H) * 2), 0, 0);
+        V.v = ld_b128(rv, off);
+        V.w.x = __builtin_amdgcn_raw_buffer_load_b16(rg, int(tok * uint32_t(a.H) * 2), 0, 0);
     } else {
         const rsrc_t rw = make_rsrc(static_cast<const bf16raw*>(a.w) + base, win);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            V.v[u] = ld_b128(rv, off + 64 * u);
-            V.w[u] = ld_b128(rw, off + 64 * u);
-        }
+        V.v = ld_b128(rv, off);
+        V.w = ld_b128(rw, off);
     }
 }
 // z = w v of this key lane's eight columns into buffer buf of the z of the
 // value wavefront that owns them (rows past the chunk are masked when read).
+//
+// The lane's columns are c8 + m (c8 = 0 or 8, m < 8), so zs_off(c8 + m, tok)
+// = base + 256 m + (((tok >> 2) ^ c8 ^ m) << 4) with base free of bits 4..7:
+// one XOR with a constant per store, the column step in the offset field.
 template <int G>
 __device__ __forceinline__ void store_z(unsigned char* lds, const RawVK& V, int buf, int kw, int lane)
 {
     const int tok = 16 * (kw & 3) + (lane & 15);
+    const int c8 = 8 * ((lane >> 4) & 1);
+    // zs_off(c8, tok) in the z of value wavefront 2 u + (lane >> 5), the owner
+    // of columns 32 u + 8 (lane >> 4) .. + 7
+    const int base = kOffZs + buf * kZsBuf + (2 * (kw >> 2) + (lane >> 5)) * kZsWave + c8 * 256 +
+                     ((tok & 3) << 2) + ((((tok >> 2) ^ c8) & 15) << 4);
+    float v[8], w[8];
+    unpack8(V.v, v);
+    if (G & (kTied | kScalarWrite)) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int col = 32 * u + 8 * (lane >> 4);
-        unsigned char* zs = lds + kOffZs + buf * kZsBuf + (col >> 4) * kZsWave;
-        float v[8], w[8];
-        unpack8(V.v[u], v);
-        if (G & (kTied | kScalarWrite)) {
-#pragma unroll
-            for (int m = 0; m < 8; ++m) w[m] = lo_f(V.w[0].x);
-        } else {
-            unpack8(V.w[u], w);
-        }
-#pragma unroll
-        for (int m = 0; m < 8; ++m) lds_st<float>(zs, zs_off((col & 15) + m, tok), v[m] * w[m]);
+        for (int m = 0; m < 8; ++m) w[m] = lo_f(V.w.x);
+    } else {
+        unpack8(V.w, w);
     }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) lds_st<float>(lds + 256 * m, base ^ (m << 4), v[m] * w[m]);
 }
 
 // Alpha of channel c of token t of this lane, as loaded.
@@ -527,7 +537,9 @@ __device__ __forceinline__ int chunk_step(const unsigned char* lds, int L)
                 m3 = fminf(pm[6], pm[7]);
     const float g16 = m0, g32 = g16 * m1, g64 = g32 * m2 * m3;
     const int leff = g64 >= kRangeMin ? 64 : g32 >= kRangeMin ? 32 : g16 >= kRangeMin ? 16 : 8;
-    return leff < L ? leff : L;
+    // every lane read the same values: a scalar, so that the buffer windows
+    // built from it stay scalar too
+    return __builtin_amdgcn_readfirstlane(leff < L ? leff : L);
 }
 
 // Store offsets of the key prep for one lane (tokens tok0, tok0 + 1 with tok0
@@ -681,6 +693,9 @@ __device__ __forceinline__ void ap_block(unsigned char* lds, const LaneOffs& o, 
 // them, over value wavefronts 0..2 (grouped by shared operands).
 __device__ __forceinline__ void ap_work(unsigned char* lds, const LaneOffs& o, int ebuf, int slot, int r, int g)
 {
+    // the store offsets are formed here each period, not held across the
+    // loop (register budget of the value side's merged chunk sequence)
+    __asm__ volatile("" : "+v"(r), "+v"(g));
     switch (slot) {
         case 0:
             ap_block<1, 3, 3>(lds, o, ebuf, r, g);
@@ -740,27 +755,32 @@ __device__ __forceinline__ void t_work(unsigned char* lds, const LaneOffs& o, in
     float t[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) t[i] = i == r ? 1.f : 0.f;
-    // Column j + 1 is read during step j; its byte offset is made opaque per
-    // step so that no read moves further ahead (register budget).
-    float4 c0[4];
+    // Step j needs rows j + 1 .. 15 of column j (the 16-byte pieces from
+    // (j + 1) / 4 on).  Column j + kAhead is requested at step j, once t[j]
+    // is final (its byte offset is made opaque there), so that kAhead columns
+    // are in flight and none is read earlier (register budget).
+    constexpr int kAhead = 2;
+    float4 cb[kAhead + 1][4];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) c0[q4] = lds_ld<float4>(adc, 16 * q4);
+    for (int j = 0; j < kAhead; ++j)
+#pragma unroll
+        for (int q4 = (j + 1) >> 2; q4 < 4; ++q4) cb[j][q4] = lds_ld<float4>(adc, j * kT16 * 4 + 16 * q4);
 #pragma unroll
     for (int j = 0; j < 15; ++j) {
-        float4 c1[4];
-        if (j < 14) {
-            int off = (j + 1) * kT16 * 4;
+        if (j + kAhead < 15) {
+            const int jn = j + kAhead;
+            int off = jn * kT16 * 4;
             __asm__ volatile("" : "+v"(off) : "v"(t[j]) : "memory");  // after t[j] is final
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) c1[q4] = lds_ld<float4>(adc, off + 16 * q4);
+            for (int q4 = (jn + 1) >> 2; q4 < 4; ++q4) cb[jn % (kAhead + 1)][q4] = lds_ld<float4>(adc, off + 16 * q4);
         }
-        const float col[16] = {c0[0].x, c0[0].y, c0[0].z, c0[0].w, c0[1].x, c0[1].y, c0[1].z, c0[1].w,
-                               c0[2].x, c0[2].y, c0[2].z, c0[2].w, c0[3].x, c0[3].y, c0[3].z, c0[3].w};
+        const float4* c = cb[j % (kAhead + 1)];
 #pragma unroll
-        for (int i = j + 1; i < 16; ++i) t[i] -= col[i] * t[j];
-        if (j < 14)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) c0[q4] = c1[q4];
+        for (int i = j + 1; i < 16; ++i) {
+            const float4 c4 = c[i >> 2];
+            const float a = (i & 3) == 0 ? c4.x : (i & 3) == 1 ? c4.y : (i & 3) == 2 ? c4.z : c4.w;
+            t[i] -= a * t[j];
+        }
     }
     float* T = reinterpret_cast<float*>(lds + kOffT) + g * kTBlk;
 #pragma unroll
@@ -834,7 +854,9 @@ __device__ __forceinline__ void value_chunk(const unsigned char* lds, const Lane
         if (I == 3) ub[1] = pack_acc_pair_hi(ub[1], u);
         f32x4 acc2 = mfma_bf16(ub[0], pa[0], xq);
         if (I >= 2) acc2 = mfma_bf16(ub[1], pa[1], acc2);
-        if (16 * I + r < lv) {  // lane holds token 16 I + r, columns 4g..4g+3
+        {  // lane holds token 16 I + r, columns 4g..4g+3; tokens past the chunk
+           // lie past the window ro (their offset is at least lv rows), so the
+           // store drops them, with no branch splitting the block sequence
             u32x2 pk;
             pk[0] = pack2(acc2[0], acc2[1]);
             pk[1] = pack2(acc2[2], acc2[3]);
@@ -1016,7 +1038,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
                 load_q(R, src, t, K);
                 load_kb<G>(R, src, t, K);
             }
-            if (K.ch == 0) load_vk<G, SEG>(V, a, token_row(a, brow, tk, h), L, j0, kw, lane0);
+            load_vk<G, SEG>(V, a, token_row(a, brow, tk, h), L, j0, kw, lane0);
             decay_pass1<G>(lds, R, al, ex, L, K, lane0);
         }
         while (tk < eos || tv >= 0) {
@@ -1048,10 +1070,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
                 for (int t = 0; t < 2; ++t) load_kb<G>(R, nxt, t, K);
                 store_kbt(lds, kbp, K);
                 // z of chunk tk (read by the value side next period), then v, w of the next chunk
-                if (K.ch == 0) {
-                    store_z<G>(lds, V, kbuf, kw, lane);
-                    load_vk<G, SEG>(V, a, token_row(a, brow, Ln > 0 ? tn : tk, h), Ln, j0, kw, lane);
-                }
+                store_z<G>(lds, V, kbuf, kw, lane);
+                load_vk<G, SEG>(V, a, token_row(a, brow, Ln > 0 ? tn : tk, h), Ln, j0, kw, lane);
             }
             if (Ln > 0) decay_pass1<G>(lds, R, al, ex, Ln, K, lane);
             tv = has_k ? tk : -1;
