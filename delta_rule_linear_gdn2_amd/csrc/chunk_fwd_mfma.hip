@@ -31,10 +31,11 @@
 // block by block (X = Z - Et S, the blocked solve, the output rows, (Qt S)^T)
 // and update the state, while the key waves form the tiles Et, Qt, Kt of chunk
 // c; after B1 the value waves form the A and P blocks of chunk c and the
-// inverses of its diagonal blocks, while the key waves store its Kt^T and its
-// z = w v and form the decay products of chunk c + 1, so that its length is
-// known at the next B0.  Et, Qt, z and gamma are double-buffered; A, P, T, Kt
-// and Kt^T are written and read in different halves of the period and stay
+// inverses of its diagonal blocks, while the key waves store its z = w v and
+// form the decay products of chunk c + 1, so that its length is known at the
+// next B0.  Et, Qt, Kt, z and gamma are double-buffered (the state update
+// reads the previous chunk's Kt as Kt^T, through the transposing LDS load);
+// A, P and T are written and read in different halves of the period and stay
 // single.  Global loads go out in both halves so that the memory pipe stays
 // busy: alpha and q of the next chunk during the prep, as registers free up,
 // and its k, b, v and w after B1.  Workgroups of one chain share an XCD, so
@@ -61,6 +62,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;  // four 16-bit values in LDS
 
 constexpr int kDK = 128;          // key head size
 constexpr int kC = 64;            // chunk
@@ -76,8 +79,7 @@ constexpr float kRangeMin = 0x1p-64f;
 // ---- LDS map (bytes) -------------------------------------------------------
 constexpr int kOffEt = 0;          // [2][64][128] bf16
 constexpr int kOffQt = 32768;      // [2][64][128] bf16
-constexpr int kOffKt = 65536;      // [64][128] bf16
-constexpr int kOffKbT = 81920;     // [128][64] bf16
+constexpr int kOffKt = 65536;      // [2][64][128] bf16
 constexpr int kOffAneg = 98304;    // [64][64] bf16 (-A below the diagonal blocks)
 constexpr int kOffP = 106496;      // [64][64] bf16
 constexpr int kT16 = 20;            // floats per row of a 16 x 16 FP32 block (padded)
@@ -112,7 +114,6 @@ __device__ __forceinline__ int chan_pos(int ch)
 {
     return (ch & ~31) | ((ch & 12) << 1) | ((ch & 16) >> 2) | (ch & 3);
 }
-__device__ __forceinline__ int parity(int x) { return __builtin_popcount(x) & 1; }
 __device__ __forceinline__ int tile_swz(int row)
 {
     return (row ^ (((row >> 2) ^ (row >> 3)) & 1)) & 15;
@@ -125,17 +126,6 @@ __device__ __forceinline__ int off_t128(int row, int pos)  // pos: permuted posi
 __device__ __forceinline__ int off_rc64(int row, int col)
 {
     return row * 128 + ((((col >> 2) ^ row) & 15) << 3) + ((col & 3) << 1);
-}
-// [128][64] bf16 tile Kt^T (channel rows, token columns): 8-byte pieces
-// XOR-swizzled by a linear map of the row bits (prep stores hit 16 channels
-// eight apart, reads 16 consecutive channels).
-__device__ __forceinline__ int kbt_swz(int row)
-{
-    return parity(row & 40) | (parity(row & 6) << 1) | (parity(row & 20) << 2) | (parity(row & 9) << 3);
-}
-__device__ __forceinline__ int off_kbt(int row, int col)
-{
-    return row * 128 + ((((col >> 2) ^ kbt_swz(row)) & 15) << 3) + ((col & 3) << 1);
 }
 
 // Byte offset of (column, token) in a value wavefront's z: the 16-byte token
@@ -179,13 +169,13 @@ __device__ __forceinline__ void lds_st(unsigned char* lds, int off, V v)
 
 // Per-lane byte offsets of the operand reads.  For a tile row 16 k + r the
 // swizzle terms depend on r only, so every read is one of these plus a
-// compile-time constant (tile base and 16 k rows) -- except in Kt^T, whose
-// swizzle also takes the block index (a constant XOR, see ld_kbt).
+// compile-time constant (tile base and 16 k rows) -- except in the transposed
+// reads of Kt, whose granule also takes the channel block (a constant XOR,
+// see ld_ktr).
 struct LaneOffs {
     int c128[4];     // [64][128] tile, positions 32 s + 8 g .. + 7 (16 bytes)
     int s64[2][2];   // [64][64] tile, columns 32 s + 16 h + 4 g .. + 3 (8 bytes)
-    int kbt_row;     // Kt^T: r * 128
-    int kbt_sl;      // Kt^T: 8-byte slot g ^ swizzle(r)
+    int ktr;         // Kt read transposed: row 4 g + (r >> 2), piece r & 3 (see ld_ktr)
 };
 
 __device__ __forceinline__ LaneOffs lane_offsets(int r, int g)
@@ -198,8 +188,10 @@ __device__ __forceinline__ LaneOffs lane_offsets(int r, int g)
         o.s64[s][0] = off_rc64(r, 32 * s + 4 * g);
         o.s64[s][1] = off_rc64(r, 32 * s + 16 + 4 * g);
     }
-    o.kbt_row = r * 128;
-    o.kbt_sl = (g ^ kbt_swz(r)) & 15;
+    {
+        const int row = 4 * g + (r >> 2);
+        o.ktr = row * 256 + ((((r & 3) ^ tile_swz(row)) & 15) << 4);
+    }
     return o;
 }
 
@@ -215,15 +207,22 @@ __device__ __forceinline__ bf16x8 ld_s64(const unsigned char* lds, const LaneOff
     const uint2 hi = lds_ld<uint2>(lds, base + 16 * k * 128 + o.s64[s][1]);
     return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
-// Split K groups, channel row 16 cb + r of Kt^T (tokens 32 s + 4 g .. + 3 and
-// 32 s + 16 + 4 g .. + 3): slot (8 s + 4 h + g) ^ swizzle(16 cb + r), and the
-// swizzle is linear, so the block part is a constant.
-__device__ __forceinline__ bf16x8 ld_kbt(const unsigned char* lds, const LaneOffs& o, int base, int cb, int s)
+// Split K groups of Kt^T, channel row 16 cb + r (tokens 32 s + 4 g .. + 3 and
+// 32 s + 16 + 4 g .. + 3), read straight from the token-major Kt tile with
+// gfx950's transposing LDS load (ds_read_b64_tr_b16): in each group of 16
+// lanes, lane 4 j + q reads the eight bytes of row t0 + j that hold
+// channels 16 cb + 4 q .. + 3, and lane r receives channel 16 cb + r of those
+// four rows (lane layout checked on the GPU with an in-bounds probe).  Those
+// four channels sit at positions 32 (cb >> 1) + 8 q + 4 (cb & 1) .. + 3, in
+// granule (4 (cb >> 1) + q) ^ tile_swz(row), and tile_swz(row) depends only
+// on row & 15 = 4 g + j: the channel block enters as a constant XOR on the
+// granule bits.
+__device__ __forceinline__ bf16x8 ld_ktr(const unsigned char* lds, const LaneOffs& o, int base, int cb, int s)
 {
-    const int c0 = ((8 * s) ^ kbt_swz(16 * cb)) & 15, c1 = ((8 * s + 4) ^ kbt_swz(16 * cb)) & 15;
-    const uint2 lo = lds_ld<uint2>(lds, base + 16 * cb * 128 + o.kbt_row + ((o.kbt_sl ^ c0) << 3));
-    const uint2 hi = lds_ld<uint2>(lds, base + 16 * cb * 128 + o.kbt_row + ((o.kbt_sl ^ c1) << 3));
-    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+    const int off = base + (o.ktr ^ ((cb >> 1) << 6)) + 8 * (cb & 1) + 32 * s * 256;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds + off));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds + off + 16 * 256));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 // Operand from two accumulator blocks held by this lane (rows 4g..4g+3 of
 // blocks 2s and 2s+1), rounded to bf16.
@@ -543,20 +542,18 @@ __device__ __forceinline__ int chunk_step(const unsigned char* lds, int L)
 }
 
 // Store offsets of the key prep for one lane (tokens tok0, tok0 + 1 with tok0
-// even, channels c0 .. c0 + 7 with c0 a multiple of 8).  Both swizzles are
+// even, channels c0 .. c0 + 7 with c0 a multiple of 8).  The swizzle is
 // linear in the row bits over GF(2), so row tok0 + t of a [64][128] tile lies
-// at (base ^ (tile_swz(t) << 4)) + 256 t and channel row c0 + c of Kt^T at
-// (base ^ (kbt_swz(c) << 3)) + 128 c: the XOR only touches the granule bits.
+// at (base ^ (tile_swz(t) << 4)) + 256 t: the XOR only touches the granule
+// bits.
 struct PrepOffs {
     int t128[2];  // row tok0 of a [64][128] tile, channels c0 .. + 3 and c0 + 4 .. + 7
-    int kbt;      // Kt^T, channel row c0, tokens tok0, tok0 + 1
 };
 __device__ __forceinline__ PrepOffs prep_offsets(int tok0, int c0)
 {
     PrepOffs o;
     o.t128[0] = off_t128(tok0, chan_pos(c0));
     o.t128[1] = off_t128(tok0, chan_pos(c0 + 4));
-    o.kbt = kOffKbT + off_kbt(c0, tok0);
     return o;
 }
 // Channels 8 cg .. 8 cg + 7 of row tok0 + t of the tile at byte offset tile.
@@ -568,8 +565,7 @@ __device__ __forceinline__ void st_tok(unsigned char* lds, const PrepOffs& o, in
 }
 
 // Key prep of a chunk, after its decay products (decay_pass1) and length
-// (chunk_step) are known: the rows of Et, Qt (buffer ebuf) and Kt, and in kbp
-// this lane's columns of Kt^T (stored after B1, see store_kbt).  Token by
+// (chunk_step) are known: the rows of Et, Qt and Kt (buffer ebuf).  Token by
 // token, as their registers are consumed, the inputs of the next chunk are
 // loaded into R.
 //
@@ -580,7 +576,7 @@ __device__ __forceinline__ void st_tok(unsigned char* lds, const PrepOffs& o, in
 // read as zero and alpha as 1, which gives zero rows as well.
 template <int G, bool kAllLive>
 __device__ __forceinline__ void prep_tiles(unsigned char* lds, RawK& R, const RawSrc& nxt, const float (*al)[8],
-                                           const float* ex, uint32_t* kbp, int step, int ebuf, const KeyLane& K)
+                                           const float* ex, int step, int ebuf, const KeyLane& K)
 {
     const bool live = kAllLive || K.tok0 < step;
     // decay before this lane's tokens: blocks 0 .. tb - 1 (the row of ones
@@ -635,28 +631,13 @@ __device__ __forceinline__ void prep_tiles(unsigned char* lds, RawK& R, const Ra
                                                pack2(et[6], et[7])));
         st_tok(lds, po, qt_base, t, make_uint4(pack2(qt[0], qt[1]), pack2(qt[2], qt[3]), pack2(qt[4], qt[5]),
                                                pack2(qt[6], qt[7])));
-        st_tok(lds, po, kOffKt, t, make_uint4(pack2(kt[0], kt[1]), pack2(kt[2], kt[3]), pack2(kt[4], kt[5]),
-                                              pack2(kt[6], kt[7])));
-        if (t == 1) {
-#pragma unroll
-            for (int c = 0; c < 8; ++c) kbp[c] = pack2(__uint_as_float(kbp[c]), kt[c]);
-        } else {
-#pragma unroll
-            for (int c = 0; c < 8; ++c) kbp[c] = __float_as_uint(kt[c]);
-        }
+        st_tok(lds, po, kOffKt + ebuf * 16384, t, make_uint4(pack2(kt[0], kt[1]), pack2(kt[2], kt[3]),
+                                                             pack2(kt[4], kt[5]), pack2(kt[6], kt[7])));
         load_q(R, nxt, t, K);  // q of token t of the next chunk (k and b follow after B1)
         __builtin_amdgcn_sched_barrier(0);  // one token's temporaries at a time
     }
 }
 
-// Columns of Kt^T for this lane's two tokens, after B1 (the value side reads
-// the previous chunk's until then).
-__device__ __forceinline__ void store_kbt(unsigned char* lds, const uint32_t* kbp, const KeyLane& K)
-{
-    const PrepOffs po = prep_offsets(K.tok0, K.c0);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) lds_st<uint32_t>(lds, (po.kbt ^ (kbt_swz(c) << 3)) + 128 * c, kbp[c]);
-}
 
 // One block of A or P (16 x 16 over K = 128 channels), formed transposed:
 // D = Kt_J Row_I^T, which leaves row 16 I + r, columns 16 J + 4 g .. + 3 in
@@ -669,7 +650,7 @@ __device__ __forceinline__ void ap_block(unsigned char* lds, const LaneOffs& o, 
     bf16x8 ka[4], ra[4];  // operands issued together so that their latency overlaps
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        ka[s] = ld_c128(lds, o, kOffKt, J, s);
+        ka[s] = ld_c128(lds, o, kOffKt + ebuf * 16384, J, s);
         ra[s] = ld_c128(lds, o, rows, I, s);
     }
 #pragma unroll
@@ -735,7 +716,7 @@ __device__ __forceinline__ void t_work(unsigned char* lds, const LaneOffs& o, in
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             ea[s] = ld_c128(lds, o, kOffEt + ebuf * 16384, I, s);
-            ka[s] = ld_c128(lds, o, kOffKt, I, s);
+            ka[s] = ld_c128(lds, o, kOffKt + ebuf * 16384, I, s);
         }
 #pragma unroll
         for (int s = 0; s < 4; ++s) acc = mfma_bf16(ea[s], ka[s], acc);
@@ -869,8 +850,8 @@ __device__ __forceinline__ void value_chunk(const unsigned char* lds, const Lane
     for (int cb = 0; cb < 8; ++cb) {
         const float4 gm = *reinterpret_cast<const float4*>(gam + 16 * cb + 4 * g);
         f32x4 acc3 = S[cb];
-        acc3 = mfma_bf16(ld_kbt(lds, o, kOffKbT, cb, 0), ub[0], acc3);
-        acc3 = mfma_bf16(ld_kbt(lds, o, kOffKbT, cb, 1), ub[1], acc3);
+        acc3 = mfma_bf16(ld_ktr(lds, o, kOffKt + ebuf * 16384, cb, 0), ub[0], acc3);
+        acc3 = mfma_bf16(ld_ktr(lds, o, kOffKt + ebuf * 16384, cb, 1), ub[1], acc3);
         S[cb] = f32x4{acc3[0] * gm.x, acc3[1] * gm.y, acc3[2] * gm.z, acc3[3] * gm.w};
         if (cb & 1) __builtin_amdgcn_sched_barrier(0);
     }
@@ -981,7 +962,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
             }
             const int64_t tn = tk + step;
 
-            lds_barrier();  // B1: tiles of chunk tk visible; A, P, T and Kt^T of chunk tv consumed
+            lds_barrier();  // B1: tiles of chunk tk visible; A, P and T of chunk tv consumed
             if (has_k) {
 
                 const LaneOffs lk = lane_offsets(r, g);
@@ -1016,10 +997,10 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
     } else {
         // Key side.  The decay products of a chunk are formed after B1 of the
         // period before the one that prepares it, so its length is known at
-        // B0; its tiles are formed between B0 and B1 (Et and Qt into the
-        // buffer the value side does not read this period) and its Kt^T
-        // columns after B1.  The next chunk's inputs are loaded during the
-        // prep and stay in flight until its decay products and prep.
+        // B0; its tiles are formed between B0 and B1 (Et, Qt and Kt into the
+        // buffers the value side does not read this period) and its z after
+        // B1.  The next chunk's inputs are loaded during the prep and stay in
+        // flight until its decay products and prep.
         if (kw == 0) {  // the row of ones of the decay products
             const float4 one = make_float4(1.f, 1.f, 1.f, 1.f);
             if (lane0 < 32) reinterpret_cast<float4*>(lds + kOffPh)[kPhOnes * 32 + lane0] = one;
@@ -1054,12 +1035,11 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
             const int Ln = has_k && tn < eos ? int(eos - tn < kC ? eos - tn : kC) : 0;
             // the next chunk's window (empty past the sequence end: loads read zero)
             const RawSrc nxt = raw_src<G>(a, token_row(a, brow, Ln > 0 ? tn : tk, h), Ln);
-            uint32_t kbp[8];
             if (has_k) {
                 if (16 * K.tb + 16 <= step)
-                    prep_tiles<G, true>(lds, R, nxt, al, ex, kbp, step, kbuf, K);
+                    prep_tiles<G, true>(lds, R, nxt, al, ex, step, kbuf, K);
                 else
-                    prep_tiles<G, false>(lds, R, nxt, al, ex, kbp, step, kbuf, K);
+                    prep_tiles<G, false>(lds, R, nxt, al, ex, step, kbuf, K);
             }
             lds_barrier();  // B1
             if (kw >= 4) __builtin_amdgcn_s_setprio(0);
@@ -1068,7 +1048,6 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_mfma_kernel(ChunkArgs a, i
                 // stays busy in this half of the period as well
 #pragma unroll
                 for (int t = 0; t < 2; ++t) load_kb<G>(R, nxt, t, K);
-                store_kbt(lds, kbp, K);
                 // z of chunk tk (read by the value side next period), then v, w of the next chunk
                 store_z<G>(lds, V, kbuf, kw, lane);
                 load_vk<G, SEG>(V, a, token_row(a, brow, Ln > 0 ? tn : tk, h), Ln, j0, kw, lane);
