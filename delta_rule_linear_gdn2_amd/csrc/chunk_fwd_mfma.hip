@@ -61,6 +61,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) f32x4 lds_f4;  // four floats in LDS
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;  // four 16-bit values in LDS
@@ -262,18 +263,26 @@ __device__ __forceinline__ float dpp(float x)
 constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128;
 constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114;  // lane i <- lane i - k of its row of 16
 
-// Minimum over the wavefront, returned as a wave-uniform value.
+// The smaller of two decay products.  These are non-negative and finite (the
+// clamped alpha and products of it, possibly denormal or zero), and for such
+// floats the order of the bit patterns as unsigned integers is the numeric
+// order: one integer minimum, without the NaN canonicalisation of fminf.
+__device__ __forceinline__ float min_decay(float a, float b)
+{
+    return __uint_as_float(min(__float_as_uint(a), __float_as_uint(b)));
+}
+// Minimum of decay products over the wavefront, returned as a wave-uniform
+// value (integer minima as in min_decay; the last four on the scalar unit).
 __device__ __forceinline__ float wave_min(float x)
 {
-    x = fminf(x, dpp<kRowRor8>(x));
-    x = fminf(x, dpp<kRowRor4>(x));
-    x = fminf(x, dpp<kRowRor2>(x));
-    x = fminf(x, dpp<kRowRor1>(x));
-    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
-    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
-    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
-    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
-    return fminf(fminf(r0, r1), fminf(r2, r3));
+    uint32_t u = __float_as_uint(x);
+    u = min(u, uint32_t(__builtin_amdgcn_mov_dpp(int(u), kRowRor8, 0xF, 0xF, true)));
+    u = min(u, uint32_t(__builtin_amdgcn_mov_dpp(int(u), kRowRor4, 0xF, 0xF, true)));
+    u = min(u, uint32_t(__builtin_amdgcn_mov_dpp(int(u), kRowRor2, 0xF, 0xF, true)));
+    u = min(u, uint32_t(__builtin_amdgcn_mov_dpp(int(u), kRowRor1, 0xF, 0xF, true)));
+    const uint32_t r0 = __builtin_amdgcn_readlane(int(u), 0), r1 = __builtin_amdgcn_readlane(int(u), 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane(int(u), 32), r3 = __builtin_amdgcn_readlane(int(u), 48);
+    return __uint_as_float(min(min(r0, r1), min(r2, r3)));
 }
 
 // Workgroup barrier for LDS traffic only.  The waves exchange data through
@@ -517,7 +526,7 @@ __device__ __forceinline__ void decay_pass1(unsigned char* lds, const RawK& R, f
     float m = 1.0f;
     if (tp == 7) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) m = fminf(m, inc[c]);
+        for (int c = 0; c < 8; ++c) m = min_decay(m, inc[c]);
     }
     m = wave_min(m);
     if (lane == 0) ph[5 * 128 + 2 * K.tb + K.ch] = m;
@@ -532,8 +541,8 @@ __device__ __forceinline__ void decay_pass1(unsigned char* lds, const RawK& R, f
 __device__ __forceinline__ int chunk_step(const unsigned char* lds, int L)
 {
     const float* pm = reinterpret_cast<const float*>(lds + kOffPh) + 5 * 128;
-    const float m0 = fminf(pm[0], pm[1]), m1 = fminf(pm[2], pm[3]), m2 = fminf(pm[4], pm[5]),
-                m3 = fminf(pm[6], pm[7]);
+    const float m0 = min_decay(pm[0], pm[1]), m1 = min_decay(pm[2], pm[3]), m2 = min_decay(pm[4], pm[5]),
+                m3 = min_decay(pm[6], pm[7]);
     const float g16 = m0, g32 = g16 * m1, g64 = g32 * m2 * m3;
     const int leff = g64 >= kRangeMin ? 64 : g32 >= kRangeMin ? 32 : g16 >= kRangeMin ? 16 : 8;
     // every lane read the same values: a scalar, so that the buffer windows
@@ -720,46 +729,45 @@ __device__ __forceinline__ void t_work(unsigned char* lds, const LaneOffs& o, in
         }
 #pragma unroll
         for (int s = 0; s < 4; ++s) acc = mfma_bf16(ea[s], ka[s], acc);
-        // acc[i] = A_II[4g + i][r]: column r, rows 4g..4g+3, strictly lower part
-        float4 v;
-        v.x = 4 * g + 0 > r ? acc[0] : 0.f;
-        v.y = 4 * g + 1 > r ? acc[1] : 0.f;
-        v.z = 4 * g + 2 > r ? acc[2] : 0.f;
-        v.w = 4 * g + 3 > r ? acc[3] : 0.f;
-        lds_st<float4>(lds, kOffAd + (I * kTBlk + r * kT16 + 4 * g) * 4, v);
+        // acc[i] = (Et Kt^T)_II[4g + i][r]: column r, rows 4g..4g+3.  Only the
+        // part below the diagonal, A_II, is read back (step j of the
+        // substitution reads rows j + 1 .. 15 of column j), so the rest needs
+        // no masking.
+        lds_st<float4>(lds, kOffAd + (I * kTBlk + r * kT16 + 4 * g) * 4, make_float4(acc[0], acc[1], acc[2], acc[3]));
         __builtin_amdgcn_sched_barrier(0);
     }
     // Other lanes of this wavefront read the columns back: LDS accesses of one
     // wavefront complete in order; this keeps the compiler from reordering.
     __asm__ volatile("" ::: "memory");
-    const unsigned char* adc = lds + kOffAd + g * kTBlk * 4;  // column j at byte j * kT16 * 4
+    // column 0 of this lane group's block, as a local-memory pointer so that
+    // it can be made opaque without leaving LDS addressing; column j at + j * kT16 / 4
+    lds_f4* adc = (lds_f4*)(lds + kOffAd + g * kTBlk * 4);
     float t[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) t[i] = i == r ? 1.f : 0.f;
     // Step j needs rows j + 1 .. 15 of column j (the 16-byte pieces from
     // (j + 1) / 4 on).  Column j + kAhead is requested at step j, once t[j]
-    // is final (its byte offset is made opaque there), so that kAhead columns
-    // are in flight and none is read earlier (register budget).
+    // is final (the column pointer is made opaque there; the column offset is
+    // the instruction's constant), so that kAhead columns are in flight and
+    // none is read earlier (register budget).
     constexpr int kAhead = 2;
-    float4 cb[kAhead + 1][4];
+    f32x4 cb[kAhead + 1][4];
 #pragma unroll
     for (int j = 0; j < kAhead; ++j)
 #pragma unroll
-        for (int q4 = (j + 1) >> 2; q4 < 4; ++q4) cb[j][q4] = lds_ld<float4>(adc, j * kT16 * 4 + 16 * q4);
+        for (int q4 = (j + 1) >> 2; q4 < 4; ++q4) cb[j][q4] = adc[j * kT16 / 4 + q4];
 #pragma unroll
     for (int j = 0; j < 15; ++j) {
         if (j + kAhead < 15) {
             const int jn = j + kAhead;
-            int off = jn * kT16 * 4;
-            __asm__ volatile("" : "+v"(off) : "v"(t[j]) : "memory");  // after t[j] is final
+            __asm__ volatile("" : "+v"(adc) : "v"(t[j]) : "memory");  // after t[j] is final
 #pragma unroll
-            for (int q4 = (jn + 1) >> 2; q4 < 4; ++q4) cb[jn % (kAhead + 1)][q4] = lds_ld<float4>(adc, off + 16 * q4);
+            for (int q4 = (jn + 1) >> 2; q4 < 4; ++q4) cb[jn % (kAhead + 1)][q4] = adc[jn * kT16 / 4 + q4];
         }
-        const float4* c = cb[j % (kAhead + 1)];
+        const f32x4* c = cb[j % (kAhead + 1)];
 #pragma unroll
         for (int i = j + 1; i < 16; ++i) {
-            const float4 c4 = c[i >> 2];
-            const float a = (i & 3) == 0 ? c4.x : (i & 3) == 1 ? c4.y : (i & 3) == 2 ? c4.z : c4.w;
+            const float a = c[i >> 2][i & 3];
             t[i] -= a * t[j];
         }
     }
