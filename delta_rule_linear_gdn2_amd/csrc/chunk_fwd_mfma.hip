@@ -261,7 +261,26 @@ __device__ __forceinline__ float dpp(float x)
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128;
-constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114;  // lane i <- lane i - k of its row of 16
+
+// x <- x * x[lane - K] within the row of 16 lanes; a lane whose source lies
+// outside its row keeps x (bound control off: the DPP result is not written
+// there).  A DPP operand that a vector instruction has just written needs two
+// wait states.
+template <int K>
+__device__ __forceinline__ void scan_mul(float& x)
+{
+    static_assert(K == 2 || K == 4 || K == 8, "row shift");
+    if (K == 2) __asm__ volatile("s_nop 1\n\tv_mul_f32_dpp %0, %0, %0 row_shr:2 row_mask:0xf bank_mask:0xf" : "+v"(x));
+    if (K == 4) __asm__ volatile("s_nop 1\n\tv_mul_f32_dpp %0, %0, %0 row_shr:4 row_mask:0xf bank_mask:0xf" : "+v"(x));
+    if (K == 8) __asm__ volatile("s_nop 1\n\tv_mul_f32_dpp %0, %0, %0 row_shr:8 row_mask:0xf bank_mask:0xf" : "+v"(x));
+}
+// x[lane - 2] within the row of 16 lanes, or 1 where that lies outside it.
+__device__ __forceinline__ float scan_prev(float x)
+{
+    float e = 1.0f;
+    __asm__ volatile("s_nop 1\n\tv_mov_b32_dpp %0, %1 row_shr:2 row_mask:0xf bank_mask:0xf" : "+v"(e) : "v"(x));
+    return e;
+}
 
 // The smaller of two decay products.  These are non-negative and finite (the
 // clamped alpha and products of it, possibly denormal or zero), and for such
@@ -324,8 +343,12 @@ __device__ __forceinline__ uint4 ld_b128(rsrc_t r, uint32_t off)
 
 // One key wavefront's share of a chunk's inputs: key wavefront kw prepares
 // tokens 16 tb .. 16 tb + 15 (tb = kw & 3) in channels 64 ch .. 64 ch + 63
-// (ch = kw >> 2); lane l takes tokens 16 tb + 2 (l & 7) + {0, 1} and channels
-// 64 ch + 8 (l >> 3) .. + 7 (eight consecutive lanes hold the block's 16 tokens).
+// (ch = kw >> 2); lane l takes tokens 16 tb + 2 tp + {0, 1} and channels
+// 64 ch + 8 cg .. + 7 with tp = (l >> 1) & 7 and cg = (l & 1) + 2 (l >> 4):
+// each row of 16 lanes holds the block's 16 tokens of two channel groups,
+// interleaved (see decay_pass1), and each half-wavefront the same tokens and
+// channel groups as with consecutive lanes, so the loads and the prep's LDS
+// stores touch the same addresses per half-wavefront.
 //
 // Gate layouts (template parameter G, gdn2_gate_flags): a scalar gate is one
 // value per token and head, read once per token and applied to every channel
@@ -352,8 +375,8 @@ __device__ __forceinline__ KeyLane key_lane(int kw, int lane)
     KeyLane k;
     k.tb = kw & 3;
     k.ch = kw >> 2;
-    k.tp = lane & 7;
-    k.cg = lane >> 3;
+    k.tp = (lane >> 1) & 7;                   // the two channel groups of a
+    k.cg = (lane & 1) | ((lane >> 4) << 1);   // row of 16 lanes interleave
     k.tok0 = 16 * k.tb + 2 * k.tp;
     k.c0 = 64 * k.ch + 8 * k.cg;
     return k;
@@ -486,36 +509,34 @@ template <int G>
 __device__ __forceinline__ void decay_pass1(unsigned char* lds, const RawK& R, float (*al)[8], float* ex, int L,
                                             const KeyLane& K, int lane)
 {
-    // alpha clamped to [2^-15, 1], and 1 past the sequence end
-    if (L == kC) {
+    // alpha clamped to [2^-15, 1], and 1 past the sequence end: the lower
+    // clamp bound is 1 for a token past it (med3(x, 1, 1) = 1), so a chunk
+    // of any length takes the same instructions
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t) {
+        const float lo = K.tok0 + t < L ? kAlphaMin : 1.0f;
 #pragma unroll
-            for (int c = 0; c < 8; ++c) al[t][c] = __builtin_amdgcn_fmed3f(raw_alpha<G>(R, t, c), kAlphaMin, 1.0f);
-    } else {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const bool live = K.tok0 + t < L;
-#pragma unroll
-            for (int c = 0; c < 8; ++c)
-                al[t][c] = live ? __builtin_amdgcn_fmed3f(raw_alpha<G>(R, t, c), kAlphaMin, 1.0f) : 1.0f;
-        }
+        for (int c = 0; c < 8; ++c) al[t][c] = __builtin_amdgcn_fmed3f(raw_alpha<G>(R, t, c), lo, 1.0f);
     }
     const int tp = K.tp;
     float inc[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        float x = al[0][c] * al[1][c];
-        float y = dpp<kRowShr1>(x);
-        x = tp >= 1 ? x * y : x;
-        y = dpp<kRowShr2>(x);
-        x = tp >= 2 ? x * y : x;
-        y = dpp<kRowShr4>(x);
-        x = tp >= 4 ? x * y : x;
-        inc[c] = x;  // tokens 16 tb .. 16 tb + 2 tp + 1
-        const float e = dpp<kRowShr1>(x);
-        ex[c] = tp >= 1 ? e : 1.0f;  // tokens 16 tb .. 16 tb + 2 tp - 1
-    }
+    for (int c = 0; c < 8; ++c) inc[c] = al[0][c] * al[1][c];
+    // The eight lanes of a channel group sit two apart in their row of 16, so
+    // a row shift by 2 k reaches position tp - k of the same group, and
+    // positions tp < k read from outside the row: with bound control off such
+    // a lane is not written by the DPP multiply, which leaves its partial
+    // product as it is (lane layout and result checked on the GPU with an
+    // in-bounds probe).  Three in-place multiplies per channel form the
+    // inclusive scan.
+#pragma unroll
+    for (int c = 0; c < 8; ++c) scan_mul<2>(inc[c]);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) scan_mul<4>(inc[c]);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) scan_mul<8>(inc[c]);  // tokens 16 tb .. 16 tb + 2 tp + 1
+#pragma unroll
+    for (int c = 0; c < 8; ++c) ex[c] = scan_prev(inc[c]);  // tokens 16 tb .. 16 tb + 2 tp - 1
     float* ph = reinterpret_cast<float*>(lds + kOffPh);
     if (tp == 7 || (K.tb == 0 && tp == 3)) {
         float* dst = ph + (tp == 7 ? K.tb : 4) * 128 + K.c0;
