@@ -5,9 +5,11 @@ shape B=8, T=4096, H=16, dk=dv=128 (bf16 q/k/v/b/w, FP32 alpha and state,
 N(0, 0.1^2) initial state).  ``value`` is its throughput in tokens/s (B*T
 tokens per call), inputs resident in HBM.  The decode half of the metric --
 gdn2_recurrent_step over N=256 sequences x 16 heads with 128 x 128 FP32
-states, 64 consecutive in-place steps -- is timed right after and reported as
-state GB/s under "decode".  Both carry their roofline; the FP64 CPU oracle is
-timed on a bounded sample of the same chunkwise workload as ``cpu_baseline``.
+states, 64 consecutive in-place steps -- is timed before it and reported as
+state GB/s under "decode".  The chunkwise timing starts after --settle untimed
+launches (the shader clock's dip after a heavy kernel starts) and the W
+warm-up ones.  Both carry their roofline; the FP64 CPU oracle is timed on a
+bounded sample of the same chunkwise workload as ``cpu_baseline``.
 
 Prints exactly one JSON line.
 """
@@ -147,6 +149,19 @@ def to_dev(x, dtype):
     return {n: W.to_torch(x[n], "f32" if n == "alpha" else dtype, "cuda") for n in NAMES}
 
 
+def settle(fn, launches):
+    """Untimed launches that hold the GPU under the workload's own load until
+    the shader clock has settled.  The power management lowers the clock for
+    a few tens of milliseconds after a heavy kernel starts (launch times rise
+    by up to a fifth, then fall back), so without this the first few dozen
+    launches measure the clock's transient rather than the kernel."""
+    import torch
+
+    for _ in range(launches):
+        fn()
+    torch.cuda.synchronize()
+
+
 def time_events(fn, warmup, steps):
     """Per-call HIP-event durations (ms) on the current stream, plus total."""
     import torch
@@ -199,6 +214,7 @@ def bench_chunk(args, pre=None):
                                final_state=sf, out=o, cu_seqlens=cu)
 
     pre_res = pre() if pre is not None else None
+    settle(call, getattr(args, "settle", 0))
     per, total_ms, wall = time_events(call, args.warmup, args.steps)
     ms = total_ms / args.steps
     kern_ms = float(np.mean(per))
@@ -495,6 +511,7 @@ def run_configs(args):
                 binding.gdn2_chunk_fwd_gates(d["q"], d["k"], d["v"], d["alpha"], d["b"], d["w"], gates, d["s0"],
                                              final_state=sf, out=o, cu_seqlens=d["cu"], segmented=segmented)
 
+            settle(call, args.settle)
             if few:  # the single pass beside the segmented path the call takes
                 per1, _, _ = time_events(lambda: call(False), args.warmup, args.steps)
                 single_ms = float(np.median(per1))
@@ -509,7 +526,9 @@ def run_configs(args):
                    "sequences": N, "us_per_call": kern_ms * 1e3, "tokens_per_s": B * T / (kern_ms / 1e3),
                    "GBps": nbytes / (kern_ms / 1e3) / 1e9,
                    "hbm_frac": nbytes / (kern_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
-                   "input_sets": rotate, "timing": f"median of {args.steps} launches after {args.warmup}"}
+                   "input_sets": rotate,
+                   "timing": f"median of {args.steps} launches after {args.settle} settling and {args.warmup} "
+                             f"warm-up launches"}
             if few:
                 row["path"] = "segmented (few chains)"
                 row["single_pass_us"] = single_ms * 1e3
@@ -611,6 +630,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="batched_bf16",
                     choices=["batched_bf16", "layer_bf16", "long16k_bf16", "varlen32_bf16", "tiny_f32"])
+    ap.add_argument("--settle", type=int, default=150,
+                    help="untimed chunkwise launches before the warm-up ones, so that the timed launches run on a "
+                         "settled shader clock (headline line and --configs; --only parts take none)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode half")
     ap.add_argument("--only", choices=["chunk", "decode", "copy", "bwd", "mixer"], default=None,
                     help="profiling aid: run one part only and print its timing line "
@@ -632,13 +654,14 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     binding.load()
     if args.only:
+        args.settle = 0
         return run_only(args)
     if args.configs:
         return run_configs(args)
-    # The decode half runs first, right before the chunkwise warmup: the GPU's
-    # clocks take tens of milliseconds of sustained load to settle (launches of
-    # the chunkwise kernel on an idle GPU run up to a third slower at first),
-    # so the chunkwise timing then starts on settled clocks.
+    # The decode half runs first.  The chunkwise launches that follow it still
+    # ride a dip of the shader clock (the power management lowers it for a few
+    # tens of milliseconds once the heavier chunkwise kernel starts), so
+    # --settle untimed chunkwise launches precede the W warm-up and K timed ones.
     from delta_rule_linear_gdn2_amd import workloads as W
 
     xd = None if args.no_decode else W.make("decode_b256")
@@ -670,6 +693,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_launches": args.settle,
         "ms_per_step": ch["ms"],
         "higher_is_better": True,
         "scaling": "weak",
