@@ -163,26 +163,36 @@ def settle(fn, launches):
 
 
 def time_events(fn, warmup, steps):
-    """Per-call HIP-event durations (ms) on the current stream, plus total."""
+    """Time ``steps`` calls of fn after ``warmup`` untimed ones.
+
+    The timed region is the ``steps`` calls back to back between one pair of
+    HIP events on the current stream (bracketed by device synchronisations);
+    its total (ms) and host wall time are returned.  A second, instrumented
+    pass of ``steps`` calls then records an event pair around each call for
+    the spread of single calls (``per``, ms each).  It is kept out of the
+    timed region because each event record between launches adds a few
+    microseconds of dispatch gap that is not kernel work."""
     import torch
 
     for _ in range(warmup):
         fn()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
     t_all0 = torch.cuda.Event(enable_timing=True)
     t_all1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_all0.record()
+    for _ in range(steps):
+        fn()
+    t_all1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
     for e0, e1 in ev:
         e0.record()
         fn()
         e1.record()
-    t_all1.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
     per = [e0.elapsed_time(e1) for e0, e1 in ev]
     return per, t_all0.elapsed_time(t_all1), wall
 
@@ -216,14 +226,15 @@ def bench_chunk(args, pre=None):
     pre_res = pre() if pre is not None else None
     settle(call, getattr(args, "settle", 0))
     per, total_ms, wall = time_events(call, args.warmup, args.steps)
-    ms = total_ms / args.steps
-    kern_ms = float(np.mean(per))
-    log("chunk per-launch us: " + " ".join(f"{p * 1e3:.0f}" for p in per))
+    ms = total_ms / args.steps  # one launch per step: also the average launch duration
+    kern_ms = ms
+    log("chunk per-launch us (instrumented pass): " + " ".join(f"{p * 1e3:.0f}" for p in per))
     eb = 2 if wl.dtype == "bf16" else 4
     nbytes = chunk_bytes(B, T, H, dk, dv, N, eb)
     tokens = B * T
-    log(f"chunk: {ms * 1e3:.1f} us/step (event avg {kern_ms * 1e3:.1f} us, median {np.median(per) * 1e3:.1f}, "
-        f"min {min(per) * 1e3:.1f}, max {max(per) * 1e3:.1f} over {len(per)} launches), "
+    log(f"chunk: {ms * 1e3:.1f} us/step over {args.steps} back-to-back launches (instrumented pass: "
+        f"mean {np.mean(per) * 1e3:.1f}, median {np.median(per) * 1e3:.1f}, min {min(per) * 1e3:.1f}, "
+        f"max {max(per) * 1e3:.1f} us per launch), "
         f"{tokens / (ms / 1e3) / 1e6:.2f} M tokens/s, {nbytes / (kern_ms / 1e3) / 1e9:.0f} GB/s")
     return dict(x=x, wl=wl, tokens=tokens, ms=ms, kern_ms=kern_ms, wall=wall, bytes=nbytes,
                 per=per, dims=(B, T, H, dk, dv, N), pre=pre_res)
@@ -447,6 +458,11 @@ def run_only(args):
     elif args.only == "decode":
         dec = bench_decode(args)
         res = {"part": "decode", "us_per_step": dec["step_ms"] * 1e3, "algorithmic_bytes": dec["bytes"]}
+    elif args.only == "segmented":  # layer_bf16 (16 chains) through the few-chain segmented path
+        args.workload = "layer_bf16"
+        ch = bench_chunk(args)
+        res = {"part": "segmented", "workload": ch["wl"].name, "avg_launch_ms": ch["kern_ms"],
+               "median_launch_ms": float(np.median(ch["per"])), "launches": args.steps + args.warmup}
     elif args.only == "mixer":
         res = {"part": "mixer", "rows": bench_mixer(args), "launches": args.steps + args.warmup}
     else:
@@ -634,9 +650,10 @@ def main():
                     help="untimed chunkwise launches before the warm-up ones, so that the timed launches run on a "
                          "settled shader clock (headline line and --configs; --only parts take none)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode half")
-    ap.add_argument("--only", choices=["chunk", "decode", "copy", "bwd", "mixer"], default=None,
+    ap.add_argument("--only", choices=["chunk", "decode", "copy", "bwd", "mixer", "segmented"], default=None,
                     help="profiling aid: run one part only and print its timing line "
-                         "(copy = a plain 1 GiB device copy, the reference for HBM byte counters)")
+                         "(copy = a plain 1 GiB device copy, the reference for HBM byte counters; "
+                         "segmented = layer_bf16 through the few-chain segmented path)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--configs", action="store_true",
                     help="report every configuration (chunkwise workloads, gate modes, decode, oracle) "
@@ -709,8 +726,11 @@ def main():
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE)",
                      "kernel": "gdn2 chunk forward", "algorithmic_bytes": ch["bytes"],
                      "avg_launch_ms": ch["kern_ms"],
-                     "launch_ms": {"median": float(np.median(ch["per"])), "min": float(min(ch["per"])),
-                                   "max": float(max(ch["per"])), "launches": len(ch["per"])},
+                     "launch_ms": {"median": float(np.median(ch["per"])), "mean": float(np.mean(ch["per"])),
+                                   "min": float(min(ch["per"])), "max": float(max(ch["per"])),
+                                   "launches": len(ch["per"]),
+                                   "from": "a pass of as many launches after the timed region, each "
+                                           "between its own pair of HIP events"},
                      "mfma": {"achieved": mfma_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
                               "unit": "TFLOP/s", "frac": mfma_tflops / MFMA_BF16_PEAK_TFLOPS,
                               "flops": flops, "counting": "triangle-aware algorithmic FLOPs"}},
