@@ -119,3 +119,13 @@ def test_segmented_deterministic():
     o1, s1 = G.gpu_chunk(d)
     o2, s2 = G.gpu_chunk(d)
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+@pytest.mark.parametrize("T", [1024, 1025, 1089])
+def test_segmented_threshold(T):
+    """B=1, H=16 at the shortest rows the segmented path takes: T = 1024 gives
+    four segments of 256 tokens, T = 1025 five (the last a single token),
+    T = 1089 five (the last one chunk and one token); random initial state."""
+    x = W.make("layer_bf16", seed=1330 + T, T=T)
+    x["initial_state"] = 0.1 * np.random.default_rng(1331 + T).standard_normal((1, 16, 128, 128)).astype(np.float32)
+    _both(x, f"segmented T={T}")
