@@ -110,3 +110,35 @@ def test_chunk_equals_stepped(dtype):
     G.assert_rel(G.f64(os_), ro, G.TOL[dtype], f"stepped {dtype} o")
     G.assert_rel(G.f64(oc), G.f64(os_), G.TOL[dtype], f"chunk vs stepped {dtype} o")
     G.assert_rel(G.f64(sc), G.f64(state), G.TOL[dtype], f"chunk vs stepped {dtype} state")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("case", ["no_decay", "zero_alpha", "steep_3", "erase_0_2"])
+def test_decode_gate_edges(dtype, d, case):
+    """The decode step over 48 consecutive steps with the gate edge cases of
+    the chunkwise tests: alpha = 1 (nothing decays, so the state keeps every
+    write), alpha = 0 in some channels (acts as 2^-15), one channel decaying
+    by 2^-3 per step, and the erase gate widened to [0, 2]; a random initial
+    state.  Every step's output and the final state against the oracle."""
+    import torch
+
+    x = W.make("decode_b256", seed=50, B=6, H=3, dk=d, dv=d, steps=48, dtype=dtype)
+    rng = np.random.default_rng(51)
+    if case == "no_decay":
+        x["alpha"][:] = 1.0
+    elif case == "zero_alpha":
+        x["alpha"][..., ::7] = 0.0
+    elif case == "steep_3":
+        x["alpha"][..., 5] = 2.0 ** -3
+    else:
+        b = 2.0 / (1.0 + np.exp(-rng.standard_normal(x["b"].shape)))
+        x["b"] = W.round_bf16(b.astype(np.float32)) if dtype == "bf16" else b.astype(np.float32)
+    state = torch.from_numpy(x["initial_state"]).cuda()
+    o = G.f64(_step_all(x, dtype, state))
+    seqs = _as_sequences(x)
+    ro, rs = oracle.recurrent(seqs["q"], seqs["k"], seqs["v"], seqs["alpha"], seqs["b"], seqs["w"],
+                              x["initial_state"])
+    what = f"decode gate edge {case} {dtype} d={d}"
+    G.assert_rel(o.swapaxes(0, 1), ro, G.TOL[dtype], f"{what} o")
+    G.assert_rel(G.f64(state), rs, G.TOL[dtype], f"{what} state")
