@@ -82,16 +82,22 @@ static_assert(kCombLoads * kCombThreads * 4 == kCombDK * kCombDK, "every element
 // columns < dv, M_p in columns dv .. dv + dk - 1); in: [B][P][H][dk][dv]
 // receives S_in(p) for p = 1 .. P - 1.
 __global__ __launch_bounds__(kCombThreads) void segment_combine_kernel(const float* __restrict__ out,
-                                                                       float* __restrict__ in, int H, int dv, int P)
+                                                                       float* __restrict__ in, int B, int H, int dv,
+                                                                       int P)
 {
     constexpr int DK = kCombDK;
     extern __shared__ __align__(16) unsigned char comb_lds[];
     float* s_m = reinterpret_cast<float*>(comb_lds);                          // [DK][kCombPad]
     float4* s_state = reinterpret_cast<float4*>(comb_lds + DK * kCombPad * 4);  // [DK][kCombCols / 4]
+    // XCD-aware mapping: the column slices of one (row, head) share blockIdx
+    // mod 8, hence an XCD, so its maps come from HBM once and from that XCD's
+    // L2 for the other slices
     const int slices = dv / kCombCols;
     const int blk = blockIdx.x;
-    const int slice = blk % slices;
-    const int bh = blk / slices;  // b * H + h
+    const int xcd = blk & 7, slot = blk >> 3;
+    const int slice = slot % slices;
+    const int bh = (slot / slices) * 8 + xcd;  // b * H + h
+    if (bh >= B * H) return;
     const int64_t b = bh / H, h = bh % H;
     const int tid = threadIdx.x;
     const int r = tid % DK, g = tid / DK;  // state row, group of four columns
@@ -150,10 +156,10 @@ hipError_t launch_segment_combine(const float* seg_out, float* seg_in, int B, in
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(segment_combine_kernel),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, kCombLds);
     if (attr != hipSuccess) return attr;
-    const int64_t blocks = int64_t(B) * H * (dv / kCombCols);
+    const int64_t blocks = (int64_t(B) * H + 7) / 8 * 8 * (dv / kCombCols);  // whole groups of eight (row, head)
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(segment_combine_kernel, dim3(unsigned(blocks)), dim3(kCombThreads), kCombLds, stream, seg_out,
-                       seg_in, H, dv, P);
+                       seg_in, B, H, dv, P);
     return hipGetLastError();
 }
 
